@@ -1,0 +1,117 @@
+"""Planted mistakes: every plausible slip in the oracle must fail at least one pin.
+
+Each case copies the oracle's source, applies one textual mutation (a flipped
+sign, a dropped term, a swapped operand), builds or loads the copy in a
+temporary directory, and runs the pins of ``test_oracle_pins`` against it.
+The committed oracle itself is never modified.
+"""
+import ctypes
+import importlib.util
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ORACLE_DIR = os.path.join(os.path.dirname(HERE), "oracle")
+
+C_MUTATIONS = {
+    "delta_sign": ("d[j] = bt * (vt[j] - acc);", "d[j] = bt * (vt[j] + acc);"),
+    "no_decay": ("S[(int64_t)i * V + j] *= a;", "S[(int64_t)i * V + j] *= 1.0;"),
+    "exp_not_exp2": ("g_is_log2 ? exp2(gt[i]) : exp(gt[i])", "exp(gt[i])"),
+    "key_for_query": ("acc += S[(int64_t)i * V + j] * qt[i];", "acc += S[(int64_t)i * V + j] * kt[i];"),
+    "no_scale": ("ot[j] = acc * scale;", "ot[j] = acc;"),
+    "no_beta": ("d[j] = bt * (vt[j] - acc);", "d[j] = (vt[j] - acc);"),
+    "sigmoid_sign": ("(1.0 / (1.0 + exp(-a)))", "(1.0 / (1.0 + exp(a)))"),
+    "softplus_log": ("? z : log1p(exp(z))", "? z : log(exp(z) + 0.5)"),
+    "no_dt_bias": ("x[idx] + (dt_bias ? dt_bias[(int64_t)h * K + i] : 0.0)", "x[idx]"),
+    "transposed_state_read": ("acc += S[(int64_t)i * V + j] * kt[i];",
+                              "acc += S[(int64_t)(j % K) * V + (i % V)] * kt[i];"),
+}
+
+PY_MUTATIONS = {
+    "diag_in_Akk": ("Akk = np.tril(Akk, -1) * bc[:, None]", "Akk = np.tril(Akk) * bc[:, None]"),
+    "no_state_decay": ("h_next = np.exp2(bL)[:, None] * h +", "h_next = h +"),
+    "vnew_sign": ("vnew = u - w @ h", "vnew = u + w @ h"),
+    "w_without_gamma": ("w = Tm @ (bc[:, None] * kc * gam)", "w = Tm @ (bc[:, None] * kc)"),
+    "q_without_gamma": ("o = scale * (qc * gam) @ h", "o = scale * qc @ h"),
+    "beta_in_columns": ("Akk = np.tril(Akk, -1) * bc[:, None]", "Akk = np.tril(Akk, -1) * bc[None, :]"),
+    "offdiag_anchor_wrong_side": ("col = np.exp2(a - b[S])", "col = np.exp2(b[S] - a)"),
+    "k_tilde_direction": ("(kc * np.exp2(bL - b)).T @ vnew", "(kc * np.exp2(b - bL)).T @ vnew"),
+}
+
+RECURRENCE_PINS = [
+    ("test_exact_bruteforce_dyadic", dict(K=4, V=4, T=6, seed=0)),
+    ("test_scalar_closed_form", {}),
+    ("test_zero_gate_is_plain_delta_rule", {}),
+    ("test_zero_beta_pure_decay", {}),
+    ("test_small_beta_limit_is_gated_linear_attention", {}),
+    ("test_unit_beta_query_equals_key", {}),
+    ("test_axis_aligned_keys_decouple_rows", {}),
+    ("test_gate_activations", {}),
+]
+
+CHUNKED_PINS = [
+    ("test_chunked_matches_recurrence", dict(C=64, anchored=True, mid=8, gate="safe")),
+    ("test_chunked_matches_recurrence", dict(C=32, anchored=False, mid=8, gate="softplus")),
+    ("test_chunked_packed_and_intermediates", {}),
+    ("test_chunked_gram_matches_pairwise_definition", {}),
+]
+
+
+def _fails_some_pin(pin_list):
+    for name, kw in pin_list:
+        try:
+            getattr(pins, name)(oracle, **kw)
+        except (AssertionError, FloatingPointError, ValueError, np_linalg_error()):
+            return True
+    return False
+
+
+def np_linalg_error():
+    import numpy as np
+
+    return np.linalg.LinAlgError
+
+
+@pytest.mark.parametrize("name", sorted(C_MUTATIONS))
+def test_c_mutation_is_caught(oracle_mod, tmp_path, name):
+    src = open(os.path.join(ORACLE_DIR, "kda_oracle.c")).read()
+    old, new = C_MUTATIONS[name]
+    assert src.count(old) == 1, "mutation anchor missing or ambiguous: " + old
+    mutated = tmp_path / "m.c"
+    mutated.write_text(src.replace(old, new, 1))
+    so = tmp_path / "libm.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", str(mutated), "-o", str(so), "-lm"],
+                   check=True)
+    good = oracle._lib()
+    lib = ctypes.CDLL(str(so))
+    lib.kda_oracle_gate.argtypes = good.kda_oracle_gate.argtypes
+    lib.kda_oracle_recurrent.argtypes = good.kda_oracle_recurrent.argtypes
+    saved = oracle._LIB
+    oracle._LIB = lib
+    try:
+        assert _fails_some_pin(RECURRENCE_PINS), "mutation %s survived every pin" % name
+    finally:
+        oracle._LIB = saved
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTATIONS))
+def test_chunked_mutation_is_caught(oracle_mod, tmp_path, name):
+    src = open(os.path.join(ORACLE_DIR, "chunked.py")).read()
+    old, new = PY_MUTATIONS[name]
+    assert src.count(old) == 1, "mutation anchor missing or ambiguous: " + old
+    path = tmp_path / "chunked_mut.py"
+    path.write_text(src.replace(old, new, 1))
+    spec = importlib.util.spec_from_file_location("chunked_mut_%s" % name, str(path))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    saved = pins.chunked_forward
+    pins.chunked_forward = mod.chunked_forward
+    try:
+        assert _fails_some_pin(CHUNKED_PINS), "mutation %s survived every pin" % name
+    finally:
+        pins.chunked_forward = saved
