@@ -1,0 +1,180 @@
+"""ctypes binding of libkda.so (include/kda.h): argument marshalling only.
+
+Every step of the computation runs in the HIP library. PyTorch supplies device
+memory and the current stream. When the library has not been built, every
+entry point raises: there is no fallback path.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_build", "libkda.so")
+
+KDA_BF16, KDA_F32 = 0, 1
+GATE_KINDS = {"loge": 0, "safe": 1, "softplus": 2, "log2": 4}
+SCHEDULES = {"auto": 0, "staged": 1, "fused": 2}
+
+_LIB = None
+
+
+class KdaError(RuntimeError):
+    """A status code other than KDA_OK returned by the library."""
+
+
+class KdaArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("K", ctypes.c_int),
+                ("V", ctypes.c_int), ("N", ctypes.c_int), ("chunk_size", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("scale", ctypes.c_float), ("gate_kind", ctypes.c_int), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("lower_bound", ctypes.c_float), ("schedule", ctypes.c_int)]
+
+
+def lib():
+    """Loads libkda.so (raises if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libkda.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ap = ctypes.c_void_p, ctypes.POINTER(KdaArgs)
+        L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_last_error.argtypes = []
+        L.kda_last_error.restype = ctypes.c_char_p
+        L.kda_recurrent_fwd.argtypes = [ap] + [vp] * 10
+        L.kda_recurrent_fwd.restype = ctypes.c_int
+        if hasattr(L, "kda_chunk_fwd"):
+            L.kda_chunk_workspace_bytes.argtypes = [ap]
+            L.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
+            L.kda_chunk_fwd.argtypes = [ap] + [vp] * 10 + [ctypes.c_size_t, vp]
+            L.kda_chunk_fwd.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def check(status):
+    if status != 0:
+        L = lib()
+        msg = L.kda_status_string(status).decode()
+        if status == 9:
+            msg += " (" + L.kda_last_error().decode() + ")"
+        raise KdaError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensors(named, device):
+    for name, t in named.items():
+        if t is None:
+            continue
+        _require(t.is_cuda and t.device == device, "%s must be on %s" % (name, device))
+        _require(t.is_contiguous(), "%s must be contiguous" % name)
+        if t.requires_grad:
+            raise RuntimeError("%s requires grad: this forward-only op does not track gradients; "
+                               "use a training implementation of chunk_kda for backward" % name)
+
+
+def make_args(q, v, H, N, gate_kind, chunk_size=64, scale=None, A_log=None, dt_bias=None, lower_bound=-5.0,
+              schedule="auto"):
+    B, T, _, K = q.shape
+    V = v.shape[-1]
+    a = KdaArgs()
+    a.B, a.T, a.H, a.K, a.V, a.N = B, T, H, K, V, N
+    a.chunk_size = int(chunk_size)
+    a.dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
+    a.scale = float(scale) if scale is not None else 0.0
+    a.gate_kind = GATE_KINDS[gate_kind] if isinstance(gate_kind, str) else int(gate_kind)
+    a.A_log = A_log.data_ptr() if A_log is not None else None
+    a.dt_bias = dt_bias.data_ptr() if dt_bias is not None else None
+    a.lower_bound = float(lower_bound) if lower_bound is not None else 0.0
+    a.schedule = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
+    return a
+
+
+def _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias):
+    _require(q.dim() == 4 and k.shape == q.shape, "q, k must be [B, T, H, K] of one shape")
+    _require(v.dim() == 4 and v.shape[:3] == q.shape[:3], "v must be [B, T, H, V]")
+    _require(q.dtype in (torch.bfloat16, torch.float32) and k.dtype == q.dtype and v.dtype == q.dtype,
+             "q, k, v must share dtype bf16 or fp32")
+    _require(g.shape == q.shape and g.dtype == torch.float32, "g must be fp32 [B, T, H, K]")
+    _require(beta.shape == q.shape[:3] and beta.dtype == torch.float32, "beta must be fp32 [B, T, H]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if cu_seqlens is not None:
+        _require(B == 1, "packed inputs (cu_seqlens) need batch 1")
+        _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1, "cu_seqlens must be int32 [N+1]")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _require(initial_state.shape == (N, H, K, V) and initial_state.dtype == torch.float32,
+                 "initial_state must be fp32 [N, H, K, V]")
+    _check_tensors(dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state, cu_seqlens=cu_seqlens,
+                        A_log=A_log, dt_bias=dt_bias), q.device)
+    return B, T, H, K, V, N
+
+
+def recurrent_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_final_state=False,
+                  gate_kind="log2", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None, final_state=None,
+                  out=None):
+    """Fused token-sequential KDA forward. Returns (o, ht); ht is None unless requested.
+
+    g is the per-token decay (log2 units by default; ``gate_kind`` "loge", "safe"
+    or "softplus" select the other gate contracts). ``final_state`` may be a
+    preallocated fp32 [N, H, K, V] output, including ``initial_state`` itself for
+    an in-place state update. ``out`` may preallocate o; rows outside the
+    packed contract are left as they are.
+    """
+    B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
+    o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
+    ht = final_state
+    if ht is None and output_final_state:
+        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
+    if ht is not None:
+        _require(ht.shape == (N, H, K, V) and ht.dtype == torch.float32 and ht.is_contiguous(),
+                 "final_state must be fp32 [N, H, K, V]")
+    a = make_args(q, v, H, N, gate_kind, scale=scale, A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound)
+    check(lib().kda_recurrent_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(ht), _stream()))
+    return o, ht
+
+
+def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_final_state=False,
+              chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None,
+              schedule="auto", final_state=None, out=None):
+    """Chunked KDA prefill forward. Returns (o, ht); ht is None unless requested.
+
+    g is the raw gate input for ``gate_kind`` "safe" / "softplus" (activation in
+    the kernel) or the natural-log decay for "loge". ``out`` may preallocate o.
+    """
+    B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
+    o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
+    ht = final_state
+    if ht is None and output_final_state:
+        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
+    a = make_args(q, v, H, N, gate_kind, chunk_size=chunk_size, scale=scale, A_log=A_log, dt_bias=dt_bias,
+                  lower_bound=lower_bound, schedule=schedule)
+    L = lib()
+    ws_bytes = L.kda_chunk_workspace_bytes(ctypes.byref(a))
+    ws = torch.empty((max(int(ws_bytes), 256),), dtype=torch.uint8, device=q.device)
+    check(L.kda_chunk_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                          _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))
+    return o, ht
+
+
+def workspace_bytes(q, v, H, N, chunk_size=64, schedule="auto"):
+    a = make_args(q, v, H, N, "safe", chunk_size=chunk_size, schedule=schedule)
+    return int(lib().kda_chunk_workspace_bytes(ctypes.byref(a)))

@@ -1,0 +1,88 @@
+// Device-side helpers shared by the gfx950 kernels of the KDA library:
+// storage-type loads/stores, the gate activations in log2 units, and the
+// 16x16 MFMA tile conventions used by every contraction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;  // 1 / ln 2 (the RCP_LN2 conversion)
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Gate kinds (values match kda_gate_kind in include/kda.h).
+enum GateKind : int { kGateLogE = 0, kGateSafe = 1, kGateSoftplus = 2, kGateLog2 = 4 };
+
+// ---------------------------------------------------------------------------------------------
+// Storage types: bf16 (round-to-nearest-even on store) or fp32.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return static_cast<float>(x); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return static_cast<bf16_t>(x); }
+
+// Hardware base-2 exponential / logarithm / reciprocal (v_exp_f32, v_log_f32, v_rcp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// log(1 + x) for x >= 0 by Goldberg's correction ("What Every Computer Scientist Should
+// Know About Floating-Point Arithmetic", 1991, Theorem 4): with u = fl(1 + x),
+// log1p(x) = log(u) * x / (u - 1), exact to a few ulps even when x is tiny.
+__device__ __forceinline__ float log1p_pos(float x) {
+  float u = 1.0f + x;
+  if (u == 1.0f) return x;
+  return fast_log2(u) * kLn2 * (x / (u - 1.0f));
+}
+
+// Per-token decay in log2 units from the gate input of one channel.
+//   kGateLog2:     g is already log2
+//   kGateLogE:     g * log2(e)
+//   kGateSafe:     lower_bound * sigmoid(expA * (x + dt)) * log2(e)
+//   kGateSoftplus: -expA * softplus(x + dt) * log2(e)
+// The activations follow "FLA KDA Skill", section "Gate modes".
+__device__ __forceinline__ float gate_log2(int kind, float x, float dt, float expA, float lower_bound) {
+  if (kind == kGateLog2) return x;
+  if (kind == kGateLogE) return x * kLog2e;
+  float z = x + dt;
+  if (kind == kGateSafe) {
+    float a = expA * z;
+    float sig = fast_rcp(1.0f + fast_exp2(-a * kLog2e));
+    return lower_bound * sig * kLog2e;
+  }
+  float sp = fmaxf(z, 0.0f) + log1p_pos(fast_exp2(-fabsf(z) * kLog2e));
+  return -expA * sp * kLog2e;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Slot / chunk location for packed (cu_seqlens) and dense batches.
+// ---------------------------------------------------------------------------------------------
+struct SlotRange {
+  int64_t t0;  // first token (flattened B*T axis)
+  int len;     // tokens in the slot
+};
+
+__device__ __forceinline__ SlotRange slot_range(const int32_t *cu, int n, int T) {
+  SlotRange r;
+  if (cu) {
+    int a = cu[n], b = cu[n + 1];
+    r.t0 = a;
+    r.len = b - a;
+  } else {
+    r.t0 = (int64_t)n * T;
+    r.len = T;
+  }
+  return r;
+}
+
+}  // namespace kda

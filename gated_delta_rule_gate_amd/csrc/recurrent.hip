@@ -1,0 +1,182 @@
+// Fused token-sequential KDA recurrence (decode and inference prefill).
+//
+// One workgroup of 256 threads owns a (sequence, head, value-block) and scans
+// its tokens with the [K, BV] FP32 state held in registers, computing in FP32
+// whatever the input dtype ("Add fused recurrent_kda for decode and inference
+// prefill", section "Agent note"). Per token, with S' = Diag(2^g) S:
+//
+//   delta = beta (v - S'^T k)
+//   o     = scale S_t^T q = scale (S'^T q + (k . q) delta)
+//   S     = S' + k delta^T
+//
+// so both column reductions (S'^T k and S'^T q) happen in one pass over the
+// state, and o needs no second pass after the rank-1 update.
+//
+// Thread layout: thread = (column group cg of 4 adjacent columns, row group rg);
+// it holds RPT rows x 4 columns. A wave's 16-byte loads of the state cover whole
+// 512-byte rows, so the state streams through HBM fully coalesced.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <int K, int BV>
+struct RecCfg {
+  static constexpr int kThreads = 256;
+  static constexpr int kCG = BV / 4;             // column groups
+  static constexpr int kRG = kThreads / kCG;     // row groups
+  static constexpr int kRPT = K / kRG;           // rows per thread
+  static_assert(kThreads % kCG == 0 && K % kRG == 0, "tile");
+};
+
+template <typename Tin, int K, int BV>
+__global__ __launch_bounds__(256) void recurrent_kernel(RecurrentParams p) {
+  using Cfg = RecCfg<K, BV>;
+  constexpr int RPT = Cfg::kRPT, CG = Cfg::kCG, RG = Cfg::kRG;
+  const int nvb = p.V / BV;
+  const int vb = blockIdx.x % nvb;
+  const int nh = blockIdx.x / nvb;
+  const int n = nh / p.H, h = nh % p.H;
+  const int tid = threadIdx.x;
+  const int cg = tid % CG, rg = tid / CG;
+  const int row0 = rg * RPT;
+  const int col0 = vb * BV + cg * 4;
+
+  const SlotRange sr = slot_range(p.cu, n, p.T);
+  const int64_t sbase = ((int64_t)(n * p.H + h) * K) * p.V;
+
+  // ---- state load (FP32, registers) ----
+  f32x4_t S[RPT];
+  if (p.h0) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+      S[r] = *reinterpret_cast<const f32x4_t *>(p.h0 + sbase + (int64_t)(row0 + r) * p.V + col0);
+  } else {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) S[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  __shared__ float s_k[2][K], s_q[2][K], s_a[2][K];
+  __shared__ float s_v[2][BV];
+  __shared__ float s_red[2][RG][BV];
+  __shared__ float s_d[BV];
+  __shared__ float s_kq[2][4];
+  __shared__ float s_beta[2];
+
+  const float expA = (p.gate_kind == kGateSafe || p.gate_kind == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
+  const float dt = (p.dt_bias && tid < K) ? p.dt_bias[h * K + tid] : 0.f;
+
+  const Tin *qp = reinterpret_cast<const Tin *>(p.q);
+  const Tin *kp = reinterpret_cast<const Tin *>(p.k);
+  const Tin *vp = reinterpret_cast<const Tin *>(p.v);
+  Tin *op = reinterpret_cast<Tin *>(p.o);
+
+  // registers holding the next token's raw inputs
+  float nk = 0.f, nq = 0.f, ng = 0.f, nv = 0.f, nb = 0.f;
+  auto fetch = [&](int i) {
+    const int64_t t = sr.t0 + i;
+    const int64_t th = t * p.H + h;
+    if (tid < K) {
+      nk = to_f32(kp[th * K + tid]);
+      nq = to_f32(qp[th * K + tid]);
+      ng = p.g[th * K + tid];
+    }
+    if (tid < BV) nv = to_f32(vp[th * p.V + vb * BV + tid]);
+    if (tid == 0) nb = p.beta[th];
+  };
+  if (sr.len > 0) fetch(0);
+
+  for (int i = 0; i < sr.len; ++i) {
+    const int buf = i & 1;
+    // ---- phase A: stage this token's inputs in LDS, prefetch the next ----
+    float kq = 0.f;
+    if (tid < K) {
+      s_k[buf][tid] = nk;
+      s_q[buf][tid] = nq;
+      s_a[buf][tid] = fast_exp2(gate_log2(p.gate_kind, ng, dt, expA, p.lower_bound));
+      kq = nk * nq;
+    }
+    if (tid < BV) s_v[buf][tid] = nv;
+    if (tid == 0) s_beta[buf] = nb;
+    // k . q : wave reduction, one partial per wave
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
+    if ((tid & 63) == 0) s_kq[buf][tid >> 6] = kq;
+    if (i + 1 < sr.len) fetch(i + 1);
+    __syncthreads();
+
+    // ---- phase B: decay and the two column reductions ----
+    f32x4_t pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const float a = s_a[buf][row0 + r];
+      const float kr = s_k[buf][row0 + r];
+      const float qr = s_q[buf][row0 + r];
+      S[r] *= a;
+      pk += S[r] * kr;
+      pq += S[r] * qr;
+    }
+    *reinterpret_cast<f32x4_t *>(&s_red[0][rg][cg * 4]) = pk;
+    *reinterpret_cast<f32x4_t *>(&s_red[1][rg][cg * 4]) = pq;
+    __syncthreads();
+
+    // ---- phase C: delta and the output ----
+    if (tid < BV) {
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < RG; ++g2) {
+        sk += s_red[0][g2][tid];
+        sq += s_red[1][g2][tid];
+      }
+      const float kqs = s_kq[buf][0] + s_kq[buf][1] + s_kq[buf][2] + s_kq[buf][3];
+      const float d = s_beta[buf] * (s_v[buf][tid] - sk);
+      s_d[tid] = d;
+      const int64_t th = (sr.t0 + i) * p.H + h;
+      op[th * p.V + vb * BV + tid] = from_f32<Tin>(p.scale * (sq + kqs * d));
+    }
+    __syncthreads();
+
+    // ---- phase D: rank-1 update ----
+    const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(&s_d[cg * 4]);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) S[r] += s_k[buf][row0 + r] * d4;
+  }
+
+  // ---- state store ----
+  if (p.ht && !(sr.len == 0 && p.ht == p.h0)) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+      *reinterpret_cast<f32x4_t *>(p.ht + sbase + (int64_t)(row0 + r) * p.V + col0) = S[r];
+  }
+}
+
+template <typename Tin, int K, int BV>
+static hipError_t launch_rec(const RecurrentParams &p, hipStream_t st) {
+  const int grid = p.N * p.H * (p.V / BV);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((recurrent_kernel<Tin, K, BV>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename Tin, int K>
+static hipError_t launch_rec_k(const RecurrentParams &p, hipStream_t st) {
+  // value block: 128 columns when V allows (one 64 KB contiguous state block at K = 128)
+  if (p.V % 128 == 0) return launch_rec<Tin, K, 128>(p, st);
+  return launch_rec<Tin, K, 64>(p, st);
+}
+
+template <typename Tin>
+static hipError_t launch_rec_t(const RecurrentParams &p, hipStream_t st) {
+  switch (p.K) {
+    case 64: return launch_rec_k<Tin, 64>(p, st);
+    case 128: return launch_rec_k<Tin, 128>(p, st);
+    case 256: return launch_rec_k<Tin, 256>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_recurrent(const RecurrentParams &p, hipStream_t st) {
+  return p.is_bf16 ? launch_rec_t<bf16_t>(p, st) : launch_rec_t<float>(p, st);
+}
+
+}  // namespace kda

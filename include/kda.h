@@ -1,0 +1,156 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * KDA is a gated delta rule with a per-channel decay. Per (sequence, head) it
+ * keeps an FP32 state S in R^{K x V} and, token by token,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T (q_t * scale),        scale = 1/sqrt(K) unless given.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer. Every call is asynchronous on
+ *     `stream` (a hipStream_t; NULL is the default stream), never synchronises
+ *     the host, never allocates, and never reads `cu_seqlens` on the host, so
+ *     calls can be captured in a HIP graph and replayed with new offsets.
+ *     This contract (device-resident int32 offsets, graph replay with mutated
+ *     boundaries) follows "Add fused recurrent_kda for decode and inference
+ *     prefill" (attention-gym PR #317), sections "Agent note" and "Test Plan".
+ *   - The caller owns every buffer, including the workspace.
+ *   - Layouts are contiguous, row-major:
+ *       q, k [B, T, H, K]   v, o [B, T, H, V]   (dtype: bf16 or fp32)
+ *       g    [B, T, H, K]   fp32 (meaning set by gate_kind)
+ *       beta [B, T, H]      fp32, post-sigmoid
+ *       h0, ht [N, H, K, V] fp32, one entry per logical sequence
+ *       cu_seqlens [N + 1]  int32, device-resident
+ *   - Packed (variable-length) batches pass B == 1, T == physical capacity and
+ *     N + 1 offsets. A repeated offset is an empty slot: its final state is h0
+ *     bit for bit (zeros when h0 is NULL). Rows at or beyond cu_seqlens[N] are
+ *     outside the contract: they are neither read nor written. Dense batches
+ *     pass cu_seqlens == NULL and N == B.
+ *   - q and k arrive l2-normalised per row; the library does not normalise
+ *     them ("Add fused recurrent_kda ...", PR #345 text: k keeps an explicit
+ *     l2norm; inference callers normalise q before the op).
+ *   - ht may alias h0 (in-place state update). ht == NULL skips the final state.
+ *   - Errors: arguments that the host can check return a status code and
+ *     launch nothing. Device-side contract violations (offsets that decrease,
+ *     cu_seqlens[N] > T) are undefined behaviour. A failed launch returns
+ *     KDA_ERR_HIP; kda_last_error() then names the HIP error.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  KDA_ERR_SHAPE = 2,       /* B, T, H, N, K or V out of range or inconsistent      */
+  KDA_ERR_DTYPE = 3,       /* unknown dtype                                        */
+  KDA_ERR_CHUNK = 4,       /* chunk size not in {32, 64} (cumsum: {1, 32, 64})     */
+  KDA_ERR_GATE = 5,        /* gate kind unknown, A_log missing, lower bound range  */
+  KDA_ERR_ALIGN = 6,       /* a tensor pointer is not 16-byte aligned              */
+  KDA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the query says        */
+  KDA_ERR_UNSUPPORTED = 8, /* valid but not implemented (e.g. K not in {64,128,256}) */
+  KDA_ERR_HIP = 9          /* a HIP launch failed                                  */
+} kda_status;
+
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+/*
+ * Gate input contracts ("FLA KDA Skill", section "Gate modes"; the log2 forms
+ * follow "Add fused recurrent_kda ...", section "Agent note").
+ */
+typedef enum {
+  KDA_GATE_LOGE = 0,     /* g is the per-token natural-log decay (pre-gated), g <= 0        */
+  KDA_GATE_SAFE = 1,     /* g is raw x: lower_bound * sigmoid(exp(A_log) * (x + dt_bias)),
+                            requires A_log and -5 <= lower_bound < 0                       */
+  KDA_GATE_SOFTPLUS = 2, /* g is raw x: -exp(A_log) * softplus(x + dt_bias), requires A_log */
+  KDA_GATE_LOG2 = 4      /* g is the per-token log2 decay (recurrent entry point only)      */
+} kda_gate_kind;
+
+/* Execution schedule of kda_chunk_fwd. All schedules compute the same function. */
+typedef enum {
+  KDA_SCHED_AUTO = 0,   /* pick per shape                                                   */
+  KDA_SCHED_STAGED = 1, /* six kernels, one per step, intermediates in the workspace        */
+  KDA_SCHED_FUSED = 2   /* one persistent kernel per (sequence, head); state kept on chip   */
+} kda_schedule;
+
+typedef struct {
+  int B, T, H, K, V;       /* dense: tensors [B, T, H, *]; packed: B == 1, T = capacity         */
+  int N;                   /* sequences (slots); cu_seqlens has N + 1 entries (dense: N == B)   */
+  int chunk_size;          /* chunk path: 32 or 64 (sub-chunk fixed at 16 rows)                 */
+  kda_dtype dtype;         /* dtype of q, k, v and o                                            */
+  float scale;             /* query scale; <= 0 selects 1/sqrt(K)                               */
+  kda_gate_kind gate_kind; /* meaning of g                                                      */
+  const float *A_log;      /* [H] device pointer (SAFE, SOFTPLUS)                               */
+  const float *dt_bias;    /* [H, K] device pointer or NULL (SAFE, SOFTPLUS)                    */
+  float lower_bound;       /* SAFE only                                                         */
+  kda_schedule schedule;   /* kda_chunk_fwd only                                                */
+} kda_args;
+
+/* Human-readable name of a status code. */
+const char *kda_status_string(kda_status s);
+
+/* Text of the last KDA_ERR_HIP (thread-local); "" if none. */
+const char *kda_last_error(void);
+
+/*
+ * Bytes of device workspace that kda_chunk_fwd needs for these arguments
+ * (0 when the arguments are invalid). Depends on B, T, H, K, V, N, chunk_size
+ * and schedule only.
+ */
+size_t kda_chunk_workspace_bytes(const kda_args *args);
+
+/*
+ * Chunked prefill (chunk_kda forward). Steps, per (sequence, head, chunk):
+ *  (1) gate activation and chunk-local cumsum in base 2 ("FLA KDA Skill",
+ *      section "Safe gate numerical note": RCP_LN2 conversion);
+ *  (2) the intra-chunk grams A_kk and A_qk over causal 16-row blocks only
+ *      ("[examples] Read only the causal columns in chunk_fwd_A_diag_anchored",
+ *      description), midpoint offsets on diagonal blocks and paired
+ *      non-positive offsets off-diagonal for the safe gate, per-pair
+ *      exponents on diagonal blocks otherwise ("FLA KDA Skill", sections
+ *      "Safe gate numerical note" and "Safe vs non-safe intra path");
+ *  (3) T = (I + A_kk)^-1 by blocked forward substitution;
+ *  (4) w = T (beta k 2^b), u = T (beta v);
+ *  (5) the inter-chunk state scan; (6) o = scale (q 2^b) h + A_qk (u - w h).
+ * Arguments:
+ *   q, k, v, o   see the layout conventions; dtype args->dtype
+ *   g            fp32 [B, T, H, K]; gate_kind LOGE, SAFE or SOFTPLUS
+ *   beta         fp32 [B, T, H]
+ *   h0           fp32 [N, H, K, V] or NULL (zero initial state)
+ *   cu_seqlens   int32 [N + 1] or NULL (dense)
+ *   ht           fp32 [N, H, K, V] or NULL; may alias h0
+ *   workspace    device buffer of ws_bytes >= kda_chunk_workspace_bytes(args),
+ *                256-byte aligned; contents on entry are ignored
+ * Supported: K == V in {64, 128, 256}; chunk_size in {32, 64}; dtype bf16 or fp32.
+ */
+kda_status kda_chunk_fwd(const kda_args *args, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *h0, const int32_t *cu_seqlens, void *o, float *ht,
+                         void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Fused token-sequential recurrence (recurrent_kda forward), for decode and
+ * inference prefill ("Add fused recurrent_kda ...", section "Agent note"):
+ * one kernel; each workgroup owns a (sequence, head, value-block) and scans its
+ * tokens with the [K, BV] FP32 state held in registers, computing in FP32
+ * whatever the input dtype.
+ * Same arguments and layouts as kda_chunk_fwd, with no workspace; g is the
+ * per-token decay of gate_kind LOG2 (log2 units, as the recurrent contract
+ * has it), LOGE, SAFE or SOFTPLUS. args->chunk_size and args->schedule are ignored.
+ * Supported: K in {64, 128, 256}, V in {64, 128, 256}.
+ */
+kda_status kda_recurrent_fwd(const kda_args *args, const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *h0, const int32_t *cu_seqlens, void *o, float *ht,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

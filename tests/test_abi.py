@@ -1,0 +1,92 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry point,
+and rejects invalid arguments with the documented status codes before launching."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def kda_lib():
+    from gated_delta_rule_gate_amd import _binding, build
+
+    if not os.path.exists(_binding.LIB_PATH):
+        build.build()
+    return _binding.lib()
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(kda_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_headers_declare_entry_points():
+    names = _declared()
+    for required in ("kda_chunk_fwd", "kda_recurrent_fwd", "kda_chunk_workspace_bytes", "kda_status_string"):
+        assert required in names, required
+
+
+def test_every_declared_symbol_is_exported(kda_lib):
+    missing = [n for n in _declared() if not hasattr(kda_lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings(kda_lib):
+    for code in range(10):
+        s = kda_lib.kda_status_string(code).decode()
+        assert s.startswith("KDA_")
+
+
+def _args(**kw):
+    from gated_delta_rule_gate_amd._binding import KdaArgs
+
+    a = KdaArgs()
+    a.B, a.T, a.H, a.K, a.V, a.N = 1, 64, 1, 128, 128, 1
+    a.chunk_size, a.dtype, a.scale, a.gate_kind = 64, 0, 0.0, 4
+    a.lower_bound, a.schedule = -5.0, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fails before any launch
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 1),                       # NULL q
+    (dict(dtype=7), 3),
+    (dict(gate_kind=9), 5),
+    (dict(gate_kind=1), 5),            # SAFE without A_log
+    (dict(K=48), 8),
+    (dict(B=2, N=1), 2),               # dense needs N == B
+    (dict(H=0), 2),
+])
+def test_recurrent_rejects(kda_lib, kw, code):
+    a = _args(**kw)
+    null_q = not kw
+    q = None if null_q else FAKE
+    st = kda_lib.kda_recurrent_fwd(ctypes.byref(a), q, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None)
+    assert st == code, (kw, st)
+
+
+def test_misaligned_pointer_rejected(kda_lib):
+    a = _args()
+    bad = ctypes.c_void_p(0x100002)
+    st = kda_lib.kda_recurrent_fwd(ctypes.byref(a), bad, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None)
+    assert st == 6
+
+
+def test_safe_lower_bound_range(kda_lib):
+    for lb, code in ((-5.5, 5), (0.0, 5), (0.5, 5)):
+        a = _args(gate_kind=1, A_log=0x100000, lower_bound=lb)
+        st = kda_lib.kda_recurrent_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None)
+        assert st == code, lb
