@@ -50,6 +50,11 @@ def lib():
             L.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
             L.kda_chunk_fwd.argtypes = [ap] + [vp] * 10 + [ctypes.c_size_t, vp]
             L.kda_chunk_fwd.restype = ctypes.c_int
+        if hasattr(L, "kda_chunk_stage"):
+            L.kda_chunk_stage.argtypes = [ap, ctypes.c_int] + [vp] * 10 + [ctypes.c_size_t, vp]
+            L.kda_chunk_stage.restype = ctypes.c_int
+            L.kda_staged_workspace_offset.argtypes = [ap, ctypes.c_int]
+            L.kda_staged_workspace_offset.restype = ctypes.c_size_t
         _LIB = L
     return _LIB
 
@@ -178,3 +183,45 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
 def workspace_bytes(q, v, H, N, chunk_size=64, schedule="auto"):
     a = make_args(q, v, H, N, "safe", chunk_size=chunk_size, schedule=schedule)
     return int(lib().kda_chunk_workspace_bytes(ctypes.byref(a)))
+
+
+STAGES = {"index": 0, "gate": 1, "grams": 2, "solve": 3, "wy": 4, "scan": 5, "output": 6}
+WS_FIELDS = {"chunk_off": 0, "b": 1, "Akk": 2, "Aqk": 3, "T": 4, "w": 5, "u": 6, "vnew": 7, "hc": 8}
+
+
+class StagedRun:
+    """Drives the staged schedule one step at a time (include/kda_stages.h) on a
+    workspace whose intermediates are exposed as fp32 tensor views."""
+
+    def __init__(self, q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, chunk_size=64,
+                 gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None, out=None,
+                 final_state=None):
+        B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
+        self.t = dict(q=q, k=k, v=v, g=g, beta=beta, h0=initial_state, cu=cu_seqlens)
+        self.o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
+        self.ht = final_state if final_state is not None else \
+            torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
+        self.args = make_args(q, v, H, N, gate_kind, chunk_size=chunk_size, scale=scale, A_log=A_log,
+                              dt_bias=dt_bias, lower_bound=lower_bound, schedule="staged")
+        self._keep = (A_log, dt_bias)
+        L = lib()
+        nbytes = int(L.kda_chunk_workspace_bytes(ctypes.byref(self.args)))
+        self.ws = torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)
+        C = int(chunk_size)
+        rows = B * T
+        nch = max((T + C - 1) // C + N, B * ((T + C - 1) // C))
+        shapes = dict(b=(rows, H, K), Akk=(rows, H, C), Aqk=(rows, H, C), T=(rows, H, C), w=(rows, H, K),
+                      u=(rows, H, V), vnew=(rows, H, V), hc=(nch, H, K, V))
+        self.views = {}
+        for name, shp in shapes.items():
+            off = int(L.kda_staged_workspace_offset(ctypes.byref(self.args), WS_FIELDS[name]))
+            n = 1
+            for x in shp:
+                n *= x
+            self.views[name] = self.ws[off:off + 4 * n].view(torch.float32).view(shp)
+
+    def run(self, stage):
+        t = self.t
+        check(lib().kda_chunk_stage(ctypes.byref(self.args), STAGES[stage], _ptr(t["q"]), _ptr(t["k"]), _ptr(t["v"]),
+                                    _ptr(t["g"]), _ptr(t["beta"]), _ptr(t["h0"]), _ptr(t["cu"]), _ptr(self.o),
+                                    _ptr(self.ht), _ptr(self.ws), ctypes.c_size_t(self.ws.numel()), _stream()))

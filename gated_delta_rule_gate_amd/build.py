@@ -16,7 +16,7 @@ ARCH = "gfx950"
 
 # Packed FP32 vector ops are disabled: the compiler would otherwise form
 # v_pk_* FP32 instructions from ordinary float code.
-HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+HIPCC_FLAGS = ["-O3", "-std=c++20", "-fPIC", "--offload-arch=" + ARCH,
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wno-unused-result"]
 

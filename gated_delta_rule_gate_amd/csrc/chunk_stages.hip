@@ -1,0 +1,380 @@
+// The staged schedule of the chunked KDA forward: one kernel per step, with
+// the fp32 intermediates in the caller's workspace. Steps (1)-(4) and (6)
+// run one workgroup per (chunk, head); the scan (5) runs one workgroup per
+// (sequence, head, 64-column value block) and walks the chunks in order.
+// Grids are sized from capacity; workgroups past the last chunk exit at once,
+// so no launch depends on a host read of cu_seqlens.
+#include "chunk_tiles.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kNT = 256;  // threads per workgroup in every chunk kernel
+
+struct ChunkLoc {
+  int n, c, gci, L;
+  int64_t t0;
+};
+
+// Maps a global chunk index to (slot, chunk in slot, first token, rows).
+__device__ __forceinline__ bool locate_chunk(const ChunkParams &p, int gc, ChunkLoc &lc) {
+  if (!p.cu) {
+    const int nt = (p.T + p.C - 1) / p.C;
+    if (gc >= p.B * nt) return false;
+    lc.n = gc / nt;
+    lc.c = gc % nt;
+    lc.t0 = (int64_t)lc.n * p.T + (int64_t)lc.c * p.C;
+    lc.L = min(p.C, p.T - lc.c * p.C);
+    lc.gci = gc;
+    return true;
+  }
+  if (gc >= p.chunk_off[p.N]) return false;
+  int lo = 0, hi = p.N;  // largest n with chunk_off[n] <= gc
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.chunk_off[mid] <= gc) lo = mid;
+    else hi = mid;
+  }
+  lc.n = lo;
+  lc.c = gc - p.chunk_off[lo];
+  lc.t0 = (int64_t)p.cu[lo] + (int64_t)lc.c * p.C;
+  lc.L = min((int64_t)p.C, (int64_t)p.cu[lo + 1] - lc.t0);
+  lc.gci = gc;
+  return true;
+}
+
+__device__ __forceinline__ float head_expA(const ChunkParams &p, int h) {
+  return (p.gate_kind == kGateSafe || p.gate_kind == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
+}
+
+template <int C>
+__device__ __forceinline__ void load_beta(float *sBeta, const ChunkParams &p, int64_t t0, int h, int L) {
+  for (int r = threadIdx.x; r < C; r += kNT) sBeta[r] = (r < L) ? p.beta[(t0 + r) * p.H + h] : 0.f;
+}
+
+template <int ROWS, int COLS, int LDS>
+__device__ __forceinline__ void store_rows_f32(float *g, int64_t ldg, const float *s, int L) {
+  for (int idx = threadIdx.x; idx < ROWS * COLS / 4; idx += kNT) {
+    const int r = idx / (COLS / 4), c = (idx % (COLS / 4)) * 4;
+    if (r < L) *reinterpret_cast<f32x4_t *>(g + (int64_t)r * ldg + c) = *reinterpret_cast<const f32x4_t *>(s + r * LDS + c);
+  }
+}
+
+}  // namespace
+
+// ---- chunk index: chunk_off[n] = sum_{m<n} ceil(len_m / C) ----
+__global__ __launch_bounds__(256) void chunk_index_kernel(const int32_t *cu, int N, int C, int32_t *off) {
+  __shared__ int s[256];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  if (tid == 0) off[0] = 0;
+  for (int base = 0; base < N; base += 256) {
+    const int n = base + tid;
+    int cnt = 0;
+    if (n < N) {
+      const int len = cu[n + 1] - cu[n];
+      cnt = len > 0 ? (len + C - 1) / C : 0;
+    }
+    s[tid] = cnt;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int v = tid >= o ? s[tid - o] : 0;
+      __syncthreads();
+      s[tid] += v;
+      __syncthreads();
+    }
+    if (n < N) off[n + 1] = carry + s[tid];
+    carry += s[255];
+    __syncthreads();
+  }
+}
+
+// ---- (1) gate activation + chunk-local cumsum (base 2) ----
+template <int C, int D>
+__global__ __launch_bounds__(256) void stage_gate_kernel(ChunkParams p) {
+  ChunkLoc lc;
+  if (!locate_chunk(p, blockIdx.x, lc)) return;
+  const int h = blockIdx.y;
+  using TL = Tile<float, C, D>;
+  extern __shared__ __align__(16) char smem[];
+  float *sB = reinterpret_cast<float *>(smem);
+  float *sBL = sB + C * TL::LDB;
+  float *sSeg = sBL + D;
+  const int64_t ld = (int64_t)p.H * D;
+  load_rows<float, kNT, C, D>(sB, TL::LDB, p.g + lc.t0 * ld + h * D, ld, lc.L);
+  __syncthreads();
+  gate_cumsum<kNT, C, D>(sB, TL::LDB, sBL, sSeg, lc.L, p.gate_kind, p.dt_bias ? p.dt_bias + h * D : nullptr,
+                         head_expA(p, h), p.lower_bound);
+  store_rows_f32<C, D, TL::LDB>(p.b + lc.t0 * ld + h * D, ld, sB, lc.L);
+}
+
+// ---- (2) intra-chunk grams ----
+template <typename Tin, int C, int D, bool SAFE>
+__global__ __launch_bounds__(256) void stage_grams_kernel(ChunkParams p) {
+  ChunkLoc lc;
+  if (!locate_chunk(p, blockIdx.x, lc)) return;
+  const int h = blockIdx.y;
+  using TL = Tile<Tin, C, D>;
+  extern __shared__ __align__(16) char smem[];
+  Tin *sQ = reinterpret_cast<Tin *>(smem);
+  Tin *sK = sQ + C * TL::LDT;
+  float *sB = reinterpret_cast<float *>(sK + C * TL::LDT);
+  float *sBL = sB + C * TL::LDB;
+  float *sBeta = sBL + D;
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C;
+  const int64_t off = lc.t0 * ld + h * D;
+  load_rows<Tin, kNT, C, D>(sQ, TL::LDT, reinterpret_cast<const Tin *>(p.q) + off, ld, lc.L);
+  load_rows<Tin, kNT, C, D>(sK, TL::LDT, reinterpret_cast<const Tin *>(p.k) + off, ld, lc.L);
+  load_rows<float, kNT, C, D>(sB, TL::LDB, p.b + off, ld, lc.L);
+  load_beta<C>(sBeta, p, lc.t0, h, lc.L);
+  __syncthreads();
+  pad_cumsum<kNT, C, D>(sB, TL::LDB, sBL, lc.L);
+  __syncthreads();
+  grams<Tin, kNT, C, D, SAFE>(sQ, sK, sB, sBeta, p.scale, p.Akk + lc.t0 * ldc + h * C, p.Aqk + lc.t0 * ldc + h * C,
+                             ldc, lc.L, lc.L);
+}
+
+// ---- (3) T = (I + A_kk)^-1 ----
+template <int C>
+__global__ __launch_bounds__(256) void stage_solve_kernel(ChunkParams p) {
+  ChunkLoc lc;
+  if (!locate_chunk(p, blockIdx.x, lc)) return;
+  const int h = blockIdx.y;
+  constexpr int LDA = C + 4;
+  extern __shared__ __align__(16) char smem[];
+  float *sAkk = reinterpret_cast<float *>(smem);
+  float *sT = sAkk + C * LDA;
+  const int64_t ldc = (int64_t)p.H * C;
+  load_rows<float, kNT, C, C>(sAkk, LDA, p.Akk + lc.t0 * ldc + h * C, ldc, lc.L);
+  __syncthreads();
+  solve<kNT, C>(sAkk, sT);
+  store_rows_f32<C, C, LDA>(p.Tm + lc.t0 * ldc + h * C, ldc, sT, lc.L);
+}
+
+// ---- (4) WY recompute: w = T (beta k 2^b), u = T (beta v) ----
+template <typename Tin, int C, int D>
+__global__ __launch_bounds__(256) void stage_wy_kernel(ChunkParams p) {
+  ChunkLoc lc;
+  if (!locate_chunk(p, blockIdx.x, lc)) return;
+  const int h = blockIdx.y;
+  using TL = Tile<Tin, C, D>;
+  constexpr int NC = TL::NC, DT = TL::DT, LDT = TL::LDT, LDB = TL::LDB, NW = kNT / 64;
+  extern __shared__ __align__(16) char smem[];
+  float *sT = reinterpret_cast<float *>(smem);
+  float *sB = sT + C * TL::LDA;
+  float *sBL = sB + C * LDB;
+  float *sBeta = sBL + D;
+  Tin *sK = reinterpret_cast<Tin *>(sBeta + C);
+  Tin *sV = sK + C * LDT;
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C;
+  const int64_t off = lc.t0 * ld + h * D;
+  load_rows<float, kNT, C, C>(sT, TL::LDA, p.Tm + lc.t0 * ldc + h * C, ldc, lc.L);
+  load_rows<Tin, kNT, C, D>(sK, LDT, reinterpret_cast<const Tin *>(p.k) + off, ld, lc.L);
+  load_rows<Tin, kNT, C, D>(sV, LDT, reinterpret_cast<const Tin *>(p.v) + off, ld, lc.L);
+  load_rows<float, kNT, C, D>(sB, LDB, p.b + off, ld, lc.L);
+  load_beta<C>(sBeta, p, lc.t0, h, lc.L);
+  __syncthreads();
+  pad_cumsum<kNT, C, D>(sB, LDB, sBL, lc.L);
+  __syncthreads();
+  const int wid = threadIdx.x >> 6;
+  for (int ct = wid; ct < 2 * DT; ct += NW) {
+    f32x4_t acc[NC][1];
+    if (ct < DT) {
+      tri_mm<Tin, C, 1>(sT, ct, acc, 0, [&](int c, int col) {
+        return sBeta[c] * to_f32(sK[c * LDT + col]) * fast_exp2(sB[c * LDB + col]);
+      });
+      store_strip<float, NC, 1>(p.w + off, ld, 16 * ct, lc.L, acc);
+    } else {
+      tri_mm<Tin, C, 1>(sT, ct - DT, acc, 0, [&](int c, int col) { return sBeta[c] * to_f32(sV[c * LDT + col]); });
+      store_strip<float, NC, 1>(p.u + off, ld, 16 * (ct - DT), lc.L, acc);
+    }
+  }
+}
+
+// ---- (5) inter-chunk state scan, per (sequence, head, 64-column value block) ----
+template <typename Tin, int C, int D>
+__global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
+  using TL = Tile<Tin, C, D>;
+  constexpr int BV = 64, NVW = 1, NC = TL::NC, DT = TL::DT, LDT = TL::LDT;
+  const int nvb = D / BV;
+  const int vb = blockIdx.x % nvb, nh = blockIdx.x / nvb;
+  const int n = nh / p.H, h = nh % p.H;
+  const int wid = threadIdx.x >> 6;
+  const int col0 = vb * BV + wid * 16;
+  const SlotRange sr = slot_range(p.cu, n, p.T);
+  const int nch = (sr.len + C - 1) / C;
+  const int cbase = p.cu ? p.chunk_off[n] : n * ((p.T + C - 1) / C);
+  const int64_t sbase = (int64_t)nh * D * D;
+  const int64_t ld = (int64_t)p.H * D;
+
+  extern __shared__ __align__(16) char smem[];
+  Tin *sW = reinterpret_cast<Tin *>(smem);
+  Tin *sKT = sW + C * LDT;
+  float *sBL = reinterpret_cast<float *>(sKT + D * TL::LDKT);
+  float *sDecay = sBL + D;
+
+  f32x4_t hs[DT][NVW];
+  if (p.h0) {
+    load_strip<DT, NVW>(hs, p.h0 + sbase, D, col0, D);
+  } else {
+#pragma unroll
+    for (int t = 0; t < DT; ++t) hs[t][0] = zero4();
+  }
+  for (int c = 0; c < nch; ++c) {
+    const int64_t t0 = sr.t0 + (int64_t)c * C;
+    const int L = min(C, sr.len - c * C);
+    const int64_t off = t0 * ld + h * D;
+    store_strip<float, DT, NVW>(p.hc + ((int64_t)(cbase + c) * p.H + h) * D * D, D, col0, D, hs);
+    load_rows_cvt<Tin, kNT, C, D>(sW, LDT, p.w + off, ld, L);
+    for (int i = threadIdx.x; i < D; i += kNT) {
+      const float bl = p.b[off + (int64_t)(L - 1) * ld + i];  // cumsum at the chunk's last row
+      sBL[i] = bl;
+      sDecay[i] = fast_exp2(bl);
+    }
+    __syncthreads();
+    make_ktilde_t_global<Tin, kNT, C, D>(sKT, reinterpret_cast<const Tin *>(p.k) + off, p.b + off, ld, sBL, L);
+    f32x4_t uv[NC][NVW];
+    load_strip<NC, NVW>(uv, p.u + off, ld, col0, L);
+    __syncthreads();
+    f32x4_t p1[NC][NVW];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) p1[i][0] = zero4();
+    rows_times_state<Tin, C, D, NVW, false>(p1, p1, sW, sW, hs);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) uv[i][0] = uv[i][0] - p1[i][0];
+    store_strip<float, NC, NVW>(p.vnew + off, ld, col0, L, uv);
+    state_update<Tin, C, D, NVW>(hs, sKT, TL::LDKT, uv, sDecay);
+    __syncthreads();
+  }
+  if (p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, D, col0, D, hs);
+}
+
+// ---- (6) output o = q~ h_c + A_qk v_new, per (chunk, head, 64-column value block) ----
+template <typename Tin, int C, int D>
+__global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
+  ChunkLoc lc;
+  if (!locate_chunk(p, blockIdx.x, lc)) return;
+  const int h = blockIdx.y, vb = blockIdx.z;
+  using TL = Tile<Tin, C, D>;
+  constexpr int BV = 64, NVW = 1, NC = TL::NC, DT = TL::DT, LDT = TL::LDT, LDB = TL::LDB;
+  const int wid = threadIdx.x >> 6;
+  const int col0 = vb * BV + wid * 16;
+  extern __shared__ __align__(16) char smem[];
+  Tin *sQ = reinterpret_cast<Tin *>(smem);
+  float *sB = reinterpret_cast<float *>(sQ + C * LDT);
+  float *sBL = sB + C * LDB;
+  float *sAqk = sBL + D;
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C;
+  const int64_t off = lc.t0 * ld + h * D;
+  load_rows<Tin, kNT, C, D>(sQ, LDT, reinterpret_cast<const Tin *>(p.q) + off, ld, lc.L);
+  load_rows<float, kNT, C, D>(sB, LDB, p.b + off, ld, lc.L);
+  load_rows<float, kNT, C, C>(sAqk, TL::LDA, p.Aqk + lc.t0 * ldc + h * C, ldc, lc.L);
+  __syncthreads();
+  pad_cumsum<kNT, C, D>(sB, LDB, sBL, lc.L);
+  __syncthreads();
+  make_qtilde<Tin, kNT, C, D>(sQ, sB, p.scale);
+  f32x4_t hs[DT][NVW], vn[NC][NVW], o[NC][NVW];
+  load_strip<DT, NVW>(hs, p.hc + ((int64_t)lc.gci * p.H + h) * D * D, D, col0, D);
+  load_strip<NC, NVW>(vn, p.vnew + off, ld, col0, lc.L);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) o[i][0] = zero4();
+  __syncthreads();
+  rows_times_state<Tin, C, D, NVW, false>(o, o, sQ, sQ, hs);
+  causal_times<Tin, C, NVW>(o, sAqk, vn);
+  store_strip<Tin, NC, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, lc.L, o);
+}
+
+// ---------------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+template <typename K>
+hipError_t launch_dyn(K kernel, dim3 grid, size_t smem, hipStream_t st, const ChunkParams &p) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();  // do not leave the error for the next launch to report
+      return e;
+    }
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(kNT), smem, st, p);
+  return hipGetLastError();
+}
+
+// Calls f.template operator()<Tin, C, D>() for the runtime (dtype, C, D).
+template <typename F>
+hipError_t dispatch(const ChunkParams &p, F &&f) {
+#define KDA_CASE(TIN, CC, DD) \
+  if (p.C == CC && p.D == DD) return f.template operator()<TIN, CC, DD>();
+  if (p.is_bf16) {
+    KDA_CASE(bf16_t, 64, 128) KDA_CASE(bf16_t, 64, 64) KDA_CASE(bf16_t, 64, 256)
+    KDA_CASE(bf16_t, 32, 128) KDA_CASE(bf16_t, 32, 64) KDA_CASE(bf16_t, 32, 256)
+  } else {
+    KDA_CASE(float, 64, 128) KDA_CASE(float, 64, 64) KDA_CASE(float, 64, 256)
+    KDA_CASE(float, 32, 128) KDA_CASE(float, 32, 64) KDA_CASE(float, 32, 256)
+  }
+#undef KDA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_index(const ChunkParams &p, hipStream_t st) {
+  if (!p.cu) return hipSuccess;
+  hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, st, p.cu, p.N, p.C, p.chunk_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_gate(const ChunkParams &p, hipStream_t st) {
+  return dispatch(p, [&]<typename Tin, int C, int D>() {
+    const size_t smem = sizeof(float) * ((size_t)C * (D + 4) + D + kNT);
+    return launch_dyn(stage_gate_kernel<C, D>, dim3(p.max_chunks, p.H), smem, st, p);
+  });
+}
+
+hipError_t launch_stage_grams(const ChunkParams &p, hipStream_t st) {
+  return dispatch(p, [&]<typename Tin, int C, int D>() {
+    using TL = Tile<Tin, C, D>;
+    const size_t smem = sizeof(Tin) * 2 * C * TL::LDT + sizeof(float) * (C * TL::LDB + D + C);
+    if (p.gate_kind == kGateSafe)
+      return launch_dyn(stage_grams_kernel<Tin, C, D, true>, dim3(p.max_chunks, p.H), smem, st, p);
+    return launch_dyn(stage_grams_kernel<Tin, C, D, false>, dim3(p.max_chunks, p.H), smem, st, p);
+  });
+}
+
+hipError_t launch_stage_solve(const ChunkParams &p, hipStream_t st) {
+  const size_t smem = sizeof(float) * 2 * p.C * (p.C + 4);
+  if (p.C == 64) return launch_dyn(stage_solve_kernel<64>, dim3(p.max_chunks, p.H), smem, st, p);
+  return launch_dyn(stage_solve_kernel<32>, dim3(p.max_chunks, p.H), smem, st, p);
+}
+
+hipError_t launch_stage_wy(const ChunkParams &p, hipStream_t st) {
+  return dispatch(p, [&]<typename Tin, int C, int D>() {
+    using TL = Tile<Tin, C, D>;
+    const size_t smem = sizeof(float) * (C * TL::LDA + C * TL::LDB + D + C) + sizeof(Tin) * 2 * C * TL::LDT;
+    return launch_dyn(stage_wy_kernel<Tin, C, D>, dim3(p.max_chunks, p.H), smem, st, p);
+  });
+}
+
+hipError_t launch_stage_scan(const ChunkParams &p, hipStream_t st) {
+  return dispatch(p, [&]<typename Tin, int C, int D>() {
+    using TL = Tile<Tin, C, D>;
+    const size_t smem = sizeof(Tin) * (C * TL::LDT + D * TL::LDKT) + sizeof(float) * 2 * D;
+    return launch_dyn(stage_scan_kernel<Tin, C, D>, dim3(p.N * p.H * (D / 64)), smem, st, p);
+  });
+}
+
+hipError_t launch_stage_output(const ChunkParams &p, hipStream_t st) {
+  return dispatch(p, [&]<typename Tin, int C, int D>() {
+    using TL = Tile<Tin, C, D>;
+    const size_t smem = sizeof(Tin) * C * TL::LDT + sizeof(float) * (C * TL::LDB + D + C * TL::LDA);
+    return launch_dyn(stage_output_kernel<Tin, C, D>, dim3(p.max_chunks, p.H, D / 64), smem, st, p);
+  });
+}
+
+}  // namespace kda

@@ -1,0 +1,518 @@
+// Per-chunk building blocks of the chunked KDA forward, operating on LDS tiles.
+//
+// Shared by the six standalone step kernels (chunk_stages.hip) and the fused
+// persistent kernel (chunk_fused.hip). For one (sequence, head, chunk) of
+// L <= C rows starting from state h:
+//   (1) b    = cumsum(gate) in log2 units, chunk-local          gate_cumsum
+//   (2) A_kk = beta_r sum_i k_r k_s 2^(b_r-b_s)   (s < r)         grams
+//       A_qk = scale  sum_i q_r k_s 2^(b_r-b_s)   (s <= r)
+//   (3) T    = (I + A_kk)^-1                                       solve
+//   (4) w    = T (beta k 2^b),  u = T (beta v)                     tri_mm
+//   (5) v_new = u - w h ;  h <- Diag(2^b_L) h + (k 2^(b_L-b))^T v_new
+//   (6) o    = scale (q 2^b) h + A_qk v_new                       state_step
+//
+// MFMA conventions (gfx950, wave64). A 16x16 accumulator tile ("C layout")
+// gives lane l the rows 4*(l/16)+e, e = 0..3, of column l%16. Operand A of
+// a 16x16xKS product gives lane l row l%16, operand B column l%16; lane
+// group l/16 supplies EPL contraction indices. Which contraction index each
+// (group, element) slot carries is free as long as A and B agree; we pick
+// the map kidx() under which a C-layout accumulator column is, unchanged, a
+// valid B operand. The state h and the corrected values v_new therefore stay
+// in accumulator registers across the whole chunk loop with no relayout.
+#pragma once
+
+#include <type_traits>
+
+#include "kda_device.h"
+
+namespace kda {
+
+template <typename Tin>
+struct Mma;
+
+// bf16 operands: v_mfma_f32_16x16x32_bf16, 8 contraction indices per lane.
+template <>
+struct Mma<bf16_t> {
+  static constexpr int KS = 32;
+  static constexpr int EPL = 8;
+  typedef bf16x8_t frag_t;
+  // slots 0..3 -> rows 4g..4g+3 of tile 2s; slots 4..7 -> the same rows of tile 2s+1
+  static __device__ __forceinline__ int kidx(int s, int grp, int e) {
+    return 32 * s + ((e >> 2) << 4) + 4 * grp + (e & 3);
+  }
+  static __device__ __forceinline__ void set(frag_t &f, int e, float v) { f[e] = static_cast<bf16_t>(v); }
+  static __device__ __forceinline__ f32x4_t mma(const frag_t &a, const frag_t &b, const f32x4_t &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// fp32 operands: v_mfma_f32_16x16x4_f32, one contraction index per lane.
+template <>
+struct Mma<float> {
+  static constexpr int KS = 4;
+  static constexpr int EPL = 1;
+  typedef float frag_t;
+  // step s covers rows {4g + (s&3)} of tile s>>2
+  static __device__ __forceinline__ int kidx(int s, int grp, int) { return 16 * (s >> 2) + 4 * grp + (s & 3); }
+  static __device__ __forceinline__ void set(frag_t &f, int, float v) { f = v; }
+  static __device__ __forceinline__ f32x4_t mma(const frag_t &a, const frag_t &b, const f32x4_t &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// B (or A) operand for contraction step s taken from C-layout accumulator
+// tiles of one column: tiles[t] holds rows 16t..16t+15.
+template <typename Tin, int NT_>
+__device__ __forceinline__ typename Mma<Tin>::frag_t acc_frag(const f32x4_t (&tiles)[NT_], int s) {
+  typename Mma<Tin>::frag_t f;
+  if constexpr (std::is_same<Tin, bf16_t>::value) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = static_cast<bf16_t>(tiles[2 * s][e]);
+      f[e + 4] = static_cast<bf16_t>(tiles[2 * s + 1][e]);
+    }
+  } else {
+    f = tiles[s >> 2][s & 3];
+  }
+  return f;
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// LDS geometry of one chunk.
+template <typename Tin, int C_, int D_>
+struct Tile {
+  static constexpr int C = C_, D = D_;
+  static constexpr int NC = C / 16;   // 16-row sub-chunks
+  static constexpr int DT = D / 16;   // 16-wide channel tiles
+  static constexpr int LDT = D + 8;   // row stride (elements) of q, k, v, w tiles [C][D] in Tin
+  static constexpr int LDB = D + 4;   // row stride of the fp32 cumsum b [C][D]
+  static constexpr int LDA = C + 4;   // row stride of the fp32 [C][C] matrices A_kk, T, A_qk
+  static constexpr int LDKT = C + 8;  // row stride of the transposed [D][C] tile k~^T in Tin
+  static_assert(C == 32 || C == 64, "chunk size");
+  static_assert(D == 64 || D == 128 || D == 256, "head width");
+};
+
+// Copies L rows of COLS elements (global row stride ldg elements) into an LDS
+// tile of row stride lds; rows L..ROWS-1 are zero-filled. 16-byte accesses.
+template <typename T, int NT, int ROWS, int COLS>
+__device__ __forceinline__ void load_rows(T *s, int lds, const T *g, int64_t ldg, int L) {
+  constexpr int EPV = 16 / (int)sizeof(T);
+  constexpr int VPR = COLS / EPV;
+  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
+    const int r = idx / VPR, c = (idx % VPR) * EPV;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (r < L) val = *reinterpret_cast<const uint4 *>(g + (int64_t)r * ldg + c);
+    *reinterpret_cast<uint4 *>(s + r * lds + c) = val;
+  }
+}
+
+// Same, converting fp32 global rows to the tile type T (used for the fp32
+// intermediates of the staged schedule).
+template <typename T, int NT, int ROWS, int COLS>
+__device__ __forceinline__ void load_rows_cvt(T *s, int lds, const float *g, int64_t ldg, int L) {
+  constexpr int VPR = COLS / 4;
+  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
+    const int r = idx / VPR, c = (idx % VPR) * 4;
+    f32x4_t val = zero4();
+    if (r < L) val = *reinterpret_cast<const f32x4_t *>(g + (int64_t)r * ldg + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[r * lds + c + e] = from_f32<T>(val[e]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// (1) gate activation + chunk-local inclusive cumsum in log2 units, in place.
+// On entry sB rows [0, L) hold the raw gate input; on exit sB holds b for all
+// C rows (rows >= L repeat b[L-1], i.e. they carry a zero gate) and sBL holds
+// b[C-1] == b[L-1]. sSeg is scratch of NT floats.
+// ---------------------------------------------------------------------------------------------
+template <int NT, int C, int D>
+__device__ void gate_cumsum(float *sB, int ldb, float *sBL, float *sSeg, int L, int kind, const float *dt_bias,
+                            float expA, float lower_bound) {
+  static_assert(NT % D == 0, "thread mapping: whole channels per thread group");
+  constexpr int TPC = NT / D;  // threads per channel, each owning RPS consecutive rows
+  constexpr int RPS = C / TPC;
+  const int tid = threadIdx.x, col = tid % D, seg = tid / D;
+  const float dt = dt_bias ? dt_bias[col] : 0.f;
+  float run = 0.f;
+#pragma unroll 8
+  for (int i = 0; i < RPS; ++i) {
+    const int r = seg * RPS + i;
+    const float la = (r < L) ? gate_log2(kind, sB[r * ldb + col], dt, expA, lower_bound) : 0.f;
+    run += la;
+    sB[r * ldb + col] = run;
+  }
+  if constexpr (TPC > 1) {
+    sSeg[seg * D + col] = run;
+    __syncthreads();
+    if (seg > 0) {
+      float off = 0.f;
+      for (int s2 = 0; s2 < seg; ++s2) off += sSeg[s2 * D + col];
+#pragma unroll 8
+      for (int i = 0; i < RPS; ++i) sB[(seg * RPS + i) * ldb + col] += off;
+    }
+  }
+  __syncthreads();
+  if (tid < D) sBL[tid] = sB[(C - 1) * ldb + tid];
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------------------
+// (2) intra-chunk grams over the causal 16x16 blocks (i, j <= i) only.
+// Safe gate: diagonal blocks factor 2^(b_r-b_s) through the block's midpoint
+// row, off-diagonal blocks through the first row of block i (both exponents
+// non-positive) -- "FLA KDA Skill", section "Safe gate numerical note".
+// Non-safe gate: diagonal blocks evaluate 2^(b_r-b_s) per pair (token-parallel
+// form, "FLA KDA Skill", section "Safe vs non-safe intra path"); off-diagonal
+// blocks use the same paired non-positive offsets.
+// Blocks above the diagonal are written as zeros.
+// ---------------------------------------------------------------------------------------------
+// Outputs go to Akk / Aqk with row stride ldo (LDS or global); only rows < wlim
+// are written.
+template <typename Tin, int NT, int C, int D, bool SAFE>
+__device__ void grams(const Tin *sQ, const Tin *sK, const float *sB, const float *sBeta, float scale, float *Akk,
+                      float *Aqk, int64_t ldo, int L, int wlim) {
+  using M = Mma<Tin>;
+  using TL = Tile<Tin, C, D>;
+  constexpr int NW = NT / 64, NC = TL::NC, NB = NC * (NC + 1) / 2;
+  constexpr int LDT = TL::LDT, LDB = TL::LDB;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n16 = lane & 15, grp = lane >> 4;
+
+  for (int blk = wid; blk < NB; blk += NW) {
+    int i = 0, j = blk;
+    while (j > i) {
+      j -= i + 1;
+      ++i;
+    }
+    f32x4_t accQ = zero4(), accK = zero4();
+    if (SAFE || i != j) {
+      const int a = (i == j) ? 16 * i + 8 : 16 * i;  // anchor row
+      const int rr = 16 * i + n16;                   // A-operand row
+      const int cc = 16 * j + n16;                   // B-operand column token
+#pragma unroll 2
+      for (int s = 0; s < D / M::KS; ++s) {
+        typename M::frag_t fq, fk, fc;
+#pragma unroll
+        for (int e = 0; e < M::EPL; ++e) {
+          const int kk = M::kidx(s, grp, e);
+          const float ba = sB[a * LDB + kk];
+          const float er = fast_exp2(sB[rr * LDB + kk] - ba);
+          const float ec = fast_exp2(ba - sB[cc * LDB + kk]);
+          M::set(fq, e, to_f32(sQ[rr * LDT + kk]) * er);
+          M::set(fk, e, to_f32(sK[rr * LDT + kk]) * er);
+          M::set(fc, e, to_f32(sK[cc * LDT + kk]) * ec);
+        }
+        accQ = M::mma(fq, fc, accQ);
+        accK = M::mma(fk, fc, accK);
+      }
+    } else {
+      // token-parallel diagonal block: lane owns column token sc and rows 4*grp + e
+      const int sc = 16 * i + n16;
+      for (int kk = 0; kk < D; ++kk) {
+        const float ks = to_f32(sK[sc * LDT + kk]);
+        const float bs = sB[sc * LDB + kk];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * i + 4 * grp + e;
+          const float f = (r >= sc) ? fast_exp2(sB[r * LDB + kk] - bs) : 0.f;
+          const float kf = ks * f;
+          accQ[e] += to_f32(sQ[r * LDT + kk]) * kf;
+          accK[e] += to_f32(sK[r * LDT + kk]) * kf;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * i + 4 * grp + e, s_ = 16 * j + n16;
+      if (r < wlim) {
+        Aqk[r * ldo + s_] = (s_ <= r && r < L) ? scale * accQ[e] : 0.f;
+        Akk[r * ldo + s_] = (s_ < r && r < L) ? sBeta[r] * accK[e] : 0.f;
+      }
+    }
+  }
+  for (int idx = threadIdx.x; idx < C * C; idx += NT) {
+    const int r = idx / C, c = idx % C;
+    if ((c >> 4) > (r >> 4) && r < wlim) {
+      Akk[r * ldo + c] = 0.f;
+      Aqk[r * ldo + c] = 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// (3) T = (I + A_kk)^-1 for strictly lower-triangular A_kk, blocked:
+// the 16x16 diagonal blocks by forward substitution (one lane per column),
+// then T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj level by level (i - j = 1, 2, ...)
+// with fp32 MFMA. Reads sAkk, writes all of sT (upper blocks zero).
+// ---------------------------------------------------------------------------------------------
+template <int NT, int C>
+__device__ void solve(const float *sAkk, float *sT) {
+  constexpr int NW = NT / 64, NC = C / 16, LDA = C + 4;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n16 = lane & 15, grp = lane >> 4;
+  for (int idx = threadIdx.x; idx < C * C; idx += NT) {
+    const int r = idx / C, c = idx % C;
+    if ((c >> 4) > (r >> 4)) sT[r * LDA + c] = 0.f;
+  }
+  if (wid == NW - 1 && lane < 16 * NC) {
+    const int i = lane >> 4, c = lane & 15;
+    const float *A = sAkk + 16 * i * LDA + 16 * i;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) acc -= A[r * LDA + s] * x[s];
+      x[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT[(16 * i + r) * LDA + 16 * i + c] = x[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int d = 1; d < NC; ++d) {
+    for (int blk = wid; blk < NC - d; blk += NW) {
+      const int j = blk, i = blk + d;
+      f32x4_t P = zero4();
+      for (int m = j; m < i; ++m) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = sAkk[(16 * i + n16) * LDA + 16 * m + 4 * grp + e];
+          const float b = sT[(16 * m + 4 * grp + e) * LDA + 16 * j + n16];
+          P = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, P, 0, 0, 0);
+        }
+      }
+      f32x4_t R = zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = sT[(16 * i + n16) * LDA + 16 * i + 4 * grp + e];
+        R = __builtin_amdgcn_mfma_f32_16x16x4f32(a, P[e], R, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * LDA + 16 * j + n16] = -R[e];
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// (4) acc[i][v] = sum_c T[16i + r][c] X[c][16ct + n] for one 16-wide column tile ct,
+// all row blocks i. Only the causal part of T (c <= 16i + 15) is visited.
+// xval(c, col) returns X[c][col].
+// ---------------------------------------------------------------------------------------------
+template <typename Tin, int C, int NV, typename XF>
+__device__ __forceinline__ void tri_mm(const float *sT, int ct, f32x4_t (&acc)[C / 16][NV], int v, XF xval) {
+  using M = Mma<Tin>;
+  constexpr int NC = C / 16, LDA = C + 4, NS = C / M::KS;
+  const int lane = threadIdx.x & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+  const int col = 16 * ct + n16;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) acc[i][v] = zero4();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    typename M::frag_t fb;
+#pragma unroll
+    for (int e = 0; e < M::EPL; ++e) M::set(fb, e, xval(M::kidx(s, grp, e), col));
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      if (16 * (i + 1) <= s * M::KS) continue;  // T block entirely above the diagonal
+      typename M::frag_t fa;
+#pragma unroll
+      for (int e = 0; e < M::EPL; ++e) M::set(fa, e, sT[(16 * i + n16) * LDA + M::kidx(s, grp, e)]);
+      acc[i][v] = M::mma(fa, fb, acc[i][v]);
+    }
+  }
+}
+
+// q~ = scale * q * 2^b, in place (row-major).
+template <typename Tin, int NT, int C, int D>
+__device__ __forceinline__ void make_qtilde(Tin *sQ, const float *sB, float scale) {
+  using TL = Tile<Tin, C, D>;
+  for (int idx = threadIdx.x; idx < C * D; idx += NT) {
+    const int r = idx / D, c = idx % D;
+    sQ[r * TL::LDT + c] = from_f32<Tin>(scale * to_f32(sQ[r * TL::LDT + c]) * fast_exp2(sB[r * TL::LDB + c]));
+  }
+}
+
+// k~^T [D][C] with k~[c][i] = k[c][i] * 2^(b_L[i] - b[c][i]).
+template <typename Tin, int NT, int C, int D>
+__device__ __forceinline__ void make_ktilde_t(Tin *sKT, const Tin *sK, const float *sB, const float *sBL) {
+  using TL = Tile<Tin, C, D>;
+  for (int idx = threadIdx.x; idx < C * D; idx += NT) {
+    const int c = idx % C, i = idx / C;  // consecutive threads walk the chunk rows
+    const float v = to_f32(sK[c * TL::LDT + i]) * fast_exp2(sBL[i] - sB[c * TL::LDB + i]);
+    sKT[i * TL::LDKT + c] = from_f32<Tin>(v);
+  }
+}
+
+// Fills rows L..C-1 of an fp32 cumsum tile with row L-1 (rows past the end
+// of a sequence carry a zero gate) and copies the last row to sBL.
+template <int NT, int C, int D>
+__device__ __forceinline__ void pad_cumsum(float *sB, int ldb, float *sBL, int L) {
+  for (int idx = threadIdx.x; idx < C * D; idx += NT) {
+    const int r = idx / D, c = idx % D;
+    if (r >= L) sB[r * ldb + c] = (L > 0) ? sB[(L - 1) * ldb + c] : 0.f;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += NT) sBL[c] = sB[(C - 1) * ldb + c];
+}
+
+// Same from global rows: k [L][D] (row stride ld) and the fp32 cumsum b [L][D];
+// rows >= L of k~^T are zero.
+template <typename Tin, int NT, int C, int D>
+__device__ __forceinline__ void make_ktilde_t_global(Tin *sKT, const Tin *gK, const float *gB, int64_t ld,
+                                                     const float *sBL, int L) {
+  using TL = Tile<Tin, C, D>;
+  for (int idx = threadIdx.x; idx < C * D; idx += NT) {
+    const int i = idx % D, c = idx / D;  // consecutive threads walk the channels (coalesced reads)
+    float v = 0.f;
+    if (c < L) v = to_f32(gK[(int64_t)c * ld + i]) * fast_exp2(sBL[i] - gB[(int64_t)c * ld + i]);
+    sKT[i * TL::LDKT + c] = from_f32<Tin>(v);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// (5)/(6) on one wave's strip of NVW value tiles. h [D/16][NVW] and v_new
+// [C/16][NVW] are C-layout accumulators (rows = channels / chunk rows).
+// ---------------------------------------------------------------------------------------------
+
+// out0 += A0 h and, when sA1 is given, out1 += A1 h; A0, A1: [C][D] row-major Tin
+// (w and q~). Contraction over the D channels.
+template <typename Tin, int C, int D, int NVW, bool TWO>
+__device__ __forceinline__ void rows_times_state(f32x4_t (&out0)[C / 16][NVW], f32x4_t (&out1)[C / 16][NVW],
+                                                 const Tin *sA0, const Tin *sA1, const f32x4_t (&h)[D / 16][NVW]) {
+  using M = Mma<Tin>;
+  using TL = Tile<Tin, C, D>;
+  constexpr int NC = TL::NC, DT = TL::DT, LDT = TL::LDT, SD = D / M::KS;
+  const int lane = threadIdx.x & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < SD; ++s) {
+    typename M::frag_t fh[NVW];
+#pragma unroll
+    for (int v = 0; v < NVW; ++v) {
+      f32x4_t col[DT];
+#pragma unroll
+      for (int t = 0; t < DT; ++t) col[t] = h[t][v];
+      fh[v] = acc_frag<Tin, DT>(col, s);
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      typename M::frag_t f0, f1;
+#pragma unroll
+      for (int e = 0; e < M::EPL; ++e) {
+        const int kk = M::kidx(s, grp, e);
+        M::set(f0, e, to_f32(sA0[(16 * i + n16) * LDT + kk]));
+        if (TWO) M::set(f1, e, to_f32(sA1[(16 * i + n16) * LDT + kk]));
+      }
+#pragma unroll
+      for (int v = 0; v < NVW; ++v) {
+        out0[i][v] = M::mma(f0, fh[v], out0[i][v]);
+        if (TWO) out1[i][v] = M::mma(f1, fh[v], out1[i][v]);
+      }
+    }
+  }
+}
+
+// o += A_qk v_new, A_qk: [C][C] fp32 (lower triangular; causal blocks only).
+template <typename Tin, int C, int NVW>
+__device__ __forceinline__ void causal_times(f32x4_t (&o)[C / 16][NVW], const float *sAqk,
+                                             const f32x4_t (&vn)[C / 16][NVW]) {
+  using M = Mma<Tin>;
+  constexpr int NC = C / 16, LDA = C + 4, SC = C / M::KS;
+  const int lane = threadIdx.x & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < SC; ++s) {
+    typename M::frag_t fv[NVW];
+#pragma unroll
+    for (int v = 0; v < NVW; ++v) {
+      f32x4_t col[NC];
+#pragma unroll
+      for (int t = 0; t < NC; ++t) col[t] = vn[t][v];
+      fv[v] = acc_frag<Tin, NC>(col, s);
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      if (16 * (i + 1) <= s * M::KS) continue;
+      typename M::frag_t fa;
+#pragma unroll
+      for (int e = 0; e < M::EPL; ++e) M::set(fa, e, sAqk[(16 * i + n16) * LDA + M::kidx(s, grp, e)]);
+#pragma unroll
+      for (int v = 0; v < NVW; ++v) o[i][v] = M::mma(fa, fv[v], o[i][v]);
+    }
+  }
+}
+
+// h <- Diag(2^b_L) h + k~^T v_new; sKT: [D][C] Tin with row stride ldkt; sDecay: [D].
+template <typename Tin, int C, int D, int NVW>
+__device__ __forceinline__ void state_update(f32x4_t (&h)[D / 16][NVW], const Tin *sKT, int ldkt,
+                                             const f32x4_t (&vn)[C / 16][NVW], const float *sDecay) {
+  using M = Mma<Tin>;
+  constexpr int NC = C / 16, DT = D / 16, SC = C / M::KS;
+  const int lane = threadIdx.x & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    const f32x4_t dec = *reinterpret_cast<const f32x4_t *>(sDecay + 16 * t + 4 * grp);
+#pragma unroll
+    for (int v = 0; v < NVW; ++v) h[t][v] = h[t][v] * dec;
+  }
+#pragma unroll
+  for (int s = 0; s < SC; ++s) {
+    typename M::frag_t fv[NVW];
+#pragma unroll
+    for (int v = 0; v < NVW; ++v) {
+      f32x4_t col[NC];
+#pragma unroll
+      for (int t = 0; t < NC; ++t) col[t] = vn[t][v];
+      fv[v] = acc_frag<Tin, NC>(col, s);
+    }
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      typename M::frag_t fk;
+#pragma unroll
+      for (int e = 0; e < M::EPL; ++e) M::set(fk, e, to_f32(sKT[(16 * t + n16) * ldkt + M::kidx(s, grp, e)]));
+#pragma unroll
+      for (int v = 0; v < NVW; ++v) h[t][v] = M::mma(fk, fv[v], h[t][v]);
+    }
+  }
+}
+
+// Loads / stores a [ROWS][cols] fp32 strip into C-layout accumulator tiles:
+// tile (t, v) covers rows 16t.., columns col0 + 16v... Rows >= L read as 0 /
+// are not stored.
+template <int RT, int NVW>
+__device__ __forceinline__ void load_strip(f32x4_t (&x)[RT][NVW], const float *g, int64_t ld, int col0, int L) {
+  const int lane = threadIdx.x & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int v = 0; v < NVW; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * t + 4 * grp + e;
+        x[t][v][e] = (r < L) ? g[(int64_t)r * ld + col0 + 16 * v + n16] : 0.f;
+      }
+}
+
+template <typename T, int RT, int NVW>
+__device__ __forceinline__ void store_strip(T *g, int64_t ld, int col0, int L, const f32x4_t (&x)[RT][NVW]) {
+  const int lane = threadIdx.x & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int v = 0; v < NVW; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * t + 4 * grp + e;
+        if (r < L) g[(int64_t)r * ld + col0 + 16 * v + n16] = from_f32<T>(x[t][v][e]);
+      }
+}
+
+}  // namespace kda

@@ -5,7 +5,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/kda.h"
+#include "../../include/kda_stages.h"
 #include "kda_launch.h"
 
 namespace {
@@ -117,15 +120,163 @@ extern "C" kda_status kda_recurrent_fwd(const kda_args *a, const void *q, const 
   return hip_status(kda::launch_recurrent(p, (hipStream_t)stream));
 }
 
+// ---------------------------------------------------------------------------------------------
+// chunked prefill
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool chunk_shape_ok(const kda_args *a) {
+  if (!a) return false;
+  if (a->B < 1 || a->T < 0 || a->H < 1 || a->N < 0) return false;
+  if (a->K != a->V || !width_ok(a->K)) return false;
+  if (a->chunk_size != 32 && a->chunk_size != 64) return false;
+  return true;
+}
+
+// Upper bound of the number of chunks: dense B * ceil(T/C); packed ceil(T/C) + N
+// (each slot adds at most one partial chunk).
+int64_t max_chunks(const kda_args *a, bool packed) {
+  const int64_t nt = ((int64_t)a->T + a->chunk_size - 1) / a->chunk_size;
+  return packed ? nt + a->N : (int64_t)a->B * nt;
+}
+
+struct WsLayout {
+  size_t off[9];
+  size_t total;
+};
+
+// The staged workspace is laid out for the packed bound of chunks, so one
+// layout serves dense and packed calls with the same sizes.
+WsLayout staged_layout(const kda_args *a) {
+  WsLayout L{};
+  const size_t rows = (size_t)a->B * a->T * a->H;
+  const size_t D = a->K, C = a->chunk_size;
+  const size_t nch = (size_t)std::max<int64_t>(max_chunks(a, true), max_chunks(a, false));
+  const size_t sz[9] = {sizeof(int32_t) * (a->N + 1), 4 * rows * D, 4 * rows * C, 4 * rows * C, 4 * rows * C,
+                        4 * rows * D, 4 * rows * D, 4 * rows * D, 4 * nch * a->H * D * D};
+  size_t cur = 0;
+  for (int i = 0; i < 9; ++i) {
+    L.off[i] = cur;
+    cur += align_up(sz[i]);
+  }
+  L.total = cur;
+  return L;
+}
+
+bool use_fused(const kda_args *a, const kda::ChunkParams &p) {
+  if (a->schedule == KDA_SCHED_STAGED) return false;
+  return kda::fused_supported(p);
+}
+
+kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *h0, const int32_t *cu, void *o, float *ht, void *ws,
+                         size_t ws_bytes, kda::ChunkParams &p) {
+  kda_status s = check_common(a, q, k, v, g, beta, h0, o, ht, false);
+  if (s != KDA_OK) return s;
+  if ((s = check_slots(a, cu)) != KDA_OK) return s;
+  if (a->chunk_size != 32 && a->chunk_size != 64) return KDA_ERR_CHUNK;
+  if (a->K != a->V) return KDA_ERR_UNSUPPORTED;
+  if (a->schedule != KDA_SCHED_AUTO && a->schedule != KDA_SCHED_STAGED && a->schedule != KDA_SCHED_FUSED)
+    return KDA_ERR_SHAPE;
+  p = kda::ChunkParams{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.beta = beta;
+  p.h0 = h0;
+  p.cu = cu;
+  p.o = o;
+  p.ht = ht;
+  p.A_log = a->A_log;
+  p.dt_bias = a->dt_bias;
+  p.lower_bound = a->lower_bound;
+  p.scale = resolve_scale(a);
+  p.gate_kind = (int)a->gate_kind;
+  p.B = a->B;
+  p.T = a->T;
+  p.H = a->H;
+  p.D = a->K;
+  p.N = n_slots(a, cu);
+  p.C = a->chunk_size;
+  p.is_bf16 = a->dtype == KDA_BF16;
+  p.max_chunks = (int)max_chunks(a, cu != nullptr);
+  if (a->schedule == KDA_SCHED_FUSED && !kda::fused_supported(p)) return KDA_ERR_UNSUPPORTED;
+  const size_t need = kda_chunk_workspace_bytes(a);
+  if (need > 0 && (!ws || ws_bytes < need)) return KDA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return KDA_ERR_ALIGN;
+  char *base = static_cast<char *>(ws);
+  if (use_fused(a, p)) {
+    p.chunk_off = reinterpret_cast<int32_t *>(base);
+  } else {
+    const WsLayout L = staged_layout(a);
+    p.chunk_off = reinterpret_cast<int32_t *>(base + L.off[0]);
+    p.b = reinterpret_cast<float *>(base + L.off[1]);
+    p.Akk = reinterpret_cast<float *>(base + L.off[2]);
+    p.Aqk = reinterpret_cast<float *>(base + L.off[3]);
+    p.Tm = reinterpret_cast<float *>(base + L.off[4]);
+    p.w = reinterpret_cast<float *>(base + L.off[5]);
+    p.u = reinterpret_cast<float *>(base + L.off[6]);
+    p.vnew = reinterpret_cast<float *>(base + L.off[7]);
+    p.hc = reinterpret_cast<float *>(base + L.off[8]);
+  }
+  return KDA_OK;
+}
+
+kda_status run_stage(const kda::ChunkParams &p, int stage, hipStream_t st) {
+  switch (stage) {
+    case KDA_STAGE_INDEX: return hip_status(kda::launch_chunk_index(p, st));
+    case KDA_STAGE_GATE: return hip_status(kda::launch_stage_gate(p, st));
+    case KDA_STAGE_GRAMS: return hip_status(kda::launch_stage_grams(p, st));
+    case KDA_STAGE_SOLVE: return hip_status(kda::launch_stage_solve(p, st));
+    case KDA_STAGE_WY: return hip_status(kda::launch_stage_wy(p, st));
+    case KDA_STAGE_SCAN: return hip_status(kda::launch_stage_scan(p, st));
+    case KDA_STAGE_OUTPUT: return hip_status(kda::launch_stage_output(p, st));
+  }
+  return KDA_ERR_SHAPE;
+}
+
+}  // namespace
+
 extern "C" size_t kda_chunk_workspace_bytes(const kda_args *a) {
-  (void)a;
-  return 0;
+  if (!chunk_shape_ok(a)) return 0;
+  kda::ChunkParams p{};
+  p.D = a->K;
+  p.is_bf16 = a->dtype == KDA_BF16;
+  if (a->schedule != KDA_SCHED_STAGED && kda::fused_supported(p)) return align_up(sizeof(int32_t) * (a->N + 1));
+  if (a->schedule == KDA_SCHED_FUSED) return 0;
+  return staged_layout(a).total;
+}
+
+extern "C" size_t kda_staged_workspace_offset(const kda_args *a, kda_ws_field field) {
+  if (!chunk_shape_ok(a) || (int)field < 0 || (int)field > 8) return (size_t)-1;
+  return staged_layout(a).off[(int)field];
 }
 
 extern "C" kda_status kda_chunk_fwd(const kda_args *a, const void *q, const void *k, const void *v, const float *g,
                                     const float *beta, const float *h0, const int32_t *cu_seqlens, void *o,
                                     float *ht, void *workspace, size_t ws_bytes, void *stream) {
-  (void)a; (void)q; (void)k; (void)v; (void)g; (void)beta; (void)h0; (void)cu_seqlens; (void)o; (void)ht;
-  (void)workspace; (void)ws_bytes; (void)stream;
-  return KDA_ERR_UNSUPPORTED;
+  kda::ChunkParams p;
+  kda_status s = prepare_chunk(a, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace, ws_bytes, p);
+  if (s != KDA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (use_fused(a, p)) return hip_status(kda::launch_fused(p, st));
+  for (int stage = KDA_STAGE_INDEX; stage <= KDA_STAGE_OUTPUT; ++stage)
+    if ((s = run_stage(p, stage, st)) != KDA_OK) return s;
+  return KDA_OK;
+}
+
+extern "C" kda_status kda_chunk_stage(const kda_args *a, kda_stage stage, const void *q, const void *k,
+                                      const void *v, const float *g, const float *beta, const float *h0,
+                                      const int32_t *cu_seqlens, void *o, float *ht, void *workspace,
+                                      size_t ws_bytes, void *stream) {
+  if (!a) return KDA_ERR_NULL;
+  if (a->schedule != KDA_SCHED_STAGED) return KDA_ERR_SHAPE;
+  kda::ChunkParams p;
+  kda_status s = prepare_chunk(a, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace, ws_bytes, p);
+  if (s != KDA_OK) return s;
+  return run_stage(p, (int)stage, (hipStream_t)stream);
 }

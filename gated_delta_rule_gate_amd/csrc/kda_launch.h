@@ -22,4 +22,34 @@ struct RecurrentParams {
 
 hipError_t launch_recurrent(const RecurrentParams &p, hipStream_t st);
 
+// Chunked prefill. D = K = V. Intermediates of the staged schedule are fp32,
+// token-major like the inputs: b, w, u, vnew [B*T, H, D]; Akk, Aqk, Tm
+// [B*T, H, C] (column = row within the chunk); hc [n_chunks, H, D, D], the
+// state at the start of every chunk, chunks numbered slot by slot.
+struct ChunkParams {
+  const void *q, *k, *v;
+  const float *g, *beta, *h0;
+  const int32_t *cu;
+  void *o;
+  float *ht;
+  const float *A_log, *dt_bias;
+  float lower_bound, scale;
+  int gate_kind;
+  int B, T, H, D, N, C;
+  bool is_bf16;
+  int32_t *chunk_off;  // [N + 1] chunk prefix per slot (packed batches only)
+  int max_chunks;      // upper bound of the number of chunks (grid size)
+  float *b, *Akk, *Aqk, *Tm, *w, *u, *vnew, *hc;
+};
+
+hipError_t launch_chunk_index(const ChunkParams &p, hipStream_t st);
+hipError_t launch_stage_gate(const ChunkParams &p, hipStream_t st);
+hipError_t launch_stage_grams(const ChunkParams &p, hipStream_t st);
+hipError_t launch_stage_solve(const ChunkParams &p, hipStream_t st);
+hipError_t launch_stage_wy(const ChunkParams &p, hipStream_t st);
+hipError_t launch_stage_scan(const ChunkParams &p, hipStream_t st);
+hipError_t launch_stage_output(const ChunkParams &p, hipStream_t st);
+hipError_t launch_fused(const ChunkParams &p, hipStream_t st);
+bool fused_supported(const ChunkParams &p);
+
 }  // namespace kda
