@@ -1,0 +1,205 @@
+"""Benchmark of the KDA forward on one MI355X.
+
+Headline workload: chunk_kda forward, B4 T4096 H64 K=V=128, bf16 q/k/v, fp32
+gate input / beta / state, chunk 64, safe gate (lower bound -5) activated in
+the kernel, initial state 0.1 N(0,1), final state returned. Synthetic seeded
+inputs (kda_synth), resident in HBM before timing.
+
+One JSON line on stdout:
+  value          Mtokens/s (tokens = B*T per call) from HIP events around each
+                 kda_chunk_fwd launch on its stream; the 512 MiB cache-flush
+                 write between calls sits outside the events.
+  roofline       the dominant kernel (the fused chunk kernel: one launch per
+                 call) against HBM: algorithmic bytes per launch (q, k, v, gate,
+                 beta, o, h0, ht counted once) / its mean launch time.
+  cpu_baseline   the FP64 oracle on the host cores, on two of the four
+                 sequences (all 64 heads, all 4096 tokens) incl. the gate.
+  recurrent_decode  kda_recurrent_fwd: 256 sequences x 1 token, H64 D128, bf16,
+                 log2 gate, fp32 state read and written in place.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def alg_bytes_chunk(B, T, H, D, dtype_bytes=2, N=None, with_h0=True, with_ht=True):
+    """Bytes the method must move once: q, k, v, o in dtype; gate input fp32; beta fp32; h0, ht fp32."""
+    N = B if N is None else N
+    per_token_head = dtype_bytes * (2 * D + D) + 4 * D + 4 + dtype_bytes * D
+    state = 4 * N * H * D * D
+    return B * T * H * per_token_head + state * (int(with_h0) + int(with_ht))
+
+
+def alg_flops_chunk(B, T, H, D, C=64):
+    """Block-causal flops per token-head: state products, grams, WY, A_qk v_new, solve."""
+    NC = C // 16
+    pbar = 16 * (NC + 1) / 2
+    per = 6 * D * D + 2 * (2 * D) * pbar + (2 * D + 2 * D) * pbar + 2 * D * pbar + C * C / 3
+    return B * T * H * per
+
+
+def event_time_ms(fn, steps, warmup, flush=None):
+    """Mean / median / p10 / p90 of per-call HIP event times (ms) on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    st = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        starts[i].record(st)
+        fn()
+        ends[i].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return dict(mean=float(times.mean()), median=float(np.median(times)), p10=float(np.percentile(times, 10)),
+                p90=float(np.percentile(times, 90)), wall_ms=wall * 1e3)
+
+
+def cpu_baseline(d, H, T, threads):
+    import oracle
+    from kda_synth import to_f64
+
+    nseq = 2
+    sub = {k: (v[:nseq] if k in ("q", "k", "v", "x", "beta", "h0") else v) for k, v in d.items()}
+    q, k, v, x, beta, h0 = (to_f64(sub[n]) for n in ("q", "k", "v", "x", "beta", "h0"))
+    A_log, dt = to_f64(sub["A_log"]), to_f64(sub["dt_bias"])
+    t0 = time.perf_counter()
+    g = oracle.gate(oracle.GATE_SAFE, x, A_log, dt, -5.0)
+    oracle.recurrent(q, k, v, g, beta, h0=h0, nthreads=threads)
+    dt_s = time.perf_counter() - t0
+    tokens = nseq * T
+    return dict(value=tokens / dt_s / 1e6, unit="Mtokens/s", cores=threads, kind="oracle",
+                sample="2 of 4 sequences x all %d heads x %d tokens (FP64 token recurrence + gate), %.1f s"
+                       % (H, T, dt_s))
+
+
+def bench_decode(steps, warmup):
+    import kda_synth
+    from gated_delta_rule_gate_amd import recurrent_kda
+
+    N, H, D = 256, 64, 128
+    d = kda_synth.chunk_inputs(N, 1, H, D, D, dtype=torch.bfloat16, seed=1004)
+    g2 = kda_synth.log2_gate(d["x"].numpy(), d["A_log"].numpy(), d["dt_bias"].numpy())
+    dev = {k: v.cuda() for k, v in d.items() if v is not None}
+    g2 = g2.cuda()
+    state = dev["h0"]
+    o = torch.empty((N, 1, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        recurrent_kda(dev["q"], dev["k"], dev["v"], g2, dev["beta"], state, final_state=state, out=o)
+
+    t = event_time_ms(step, steps, warmup)
+    nbytes = 2 * 4 * N * H * D * D + N * H * (2 * 3 * D + 4 * D + 4 + 2 * D)
+    gbs = nbytes / (t["median"] * 1e-3) / 1e9
+    return dict(config="256 seq x 1 token, H64 K=V=128, bf16, log2 gate, state in place", ms=t["median"],
+                GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS, Mtokens_per_s=N / (t["median"] * 1e-3) / 1e6)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--schedule", default="auto", choices=["auto", "fused", "staged"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-decode", action="store_true", help="skip the recurrent decode figure")
+    ap.add_argument("--shape", default="4,4096,64,128", help="B,T,H,D")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (the op has no cross-GPU path); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+
+    import kda_synth
+    from gated_delta_rule_gate_amd import chunk_kda, lib
+
+    lib()
+    B, T, H, D = (int(x) for x in args.shape.split(","))
+    C = 64
+    d = kda_synth.chunk_inputs(B, T, H, D, D, dtype=torch.bfloat16, seed=1002)
+    dev = {k: v.cuda() for k, v in d.items() if v is not None}
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    flush_buf = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+
+    def step():
+        chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], dev["h0"], chunk_size=C, gate_kind="safe",
+                  A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0, schedule=args.schedule, out=o,
+                  final_state=ht)
+
+    def flush():
+        flush_buf.zero_()
+
+    if args.calib_copy:
+        src = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cold = event_time_ms(step, args.steps, args.warmup, flush=flush)
+    warm = event_time_ms(step, max(5, args.steps // 2), 1)
+    ms = cold["mean"]
+    tokens = B * T
+    value = tokens / (ms * 1e-3) / 1e6
+    nbytes = alg_bytes_chunk(B, T, H, D)
+    flops = alg_flops_chunk(B, T, H, D, C)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "chunk_kda fwd Mtokens/s (B4 T4096 H64 D128 bf16) + % of roofline",
+        "value": round(value, 3),
+        "unit": "Mtokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "chunk_kda fwd B%d T%d H%d K=V=%d bf16, C=%d, safe gate lb=-5, h0+ht" % (B, T, H, D, C),
+                   "B": B, "T": T, "H": H, "D": D, "chunk": C, "schedule": args.schedule, "cache": "flushed"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "fused_chunk_kernel" if args.schedule != "staged" else "staged chain",
+                     "alg_bytes_per_launch": nbytes,
+                     "alg_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "timing_ms": {"cold_mean": round(cold["mean"], 4), "cold_p10": round(cold["p10"], 4),
+                      "cold_p90": round(cold["p90"], 4), "warm_median": round(warm["median"], 4)},
+    }
+    if not args.no_decode:
+        line["recurrent_decode"] = bench_decode(max(10, args.steps), 3)
+    if not args.no_cpu:
+        threads = min(16, os.cpu_count() or 1)
+        line["cpu_baseline"] = cpu_baseline(d, H, T, threads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void chunk_index_kernel(const int32_t *cu, int
 }
 
 // ---- (1) gate activation + chunk-local cumsum (base 2) ----
-template <int C, int D>
+template <int C, int D, int GK>
 __global__ __launch_bounds__(256) void stage_gate_kernel(ChunkParams p) {
   ChunkLoc lc;
   if (!locate_chunk(p, blockIdx.x, lc)) return;
@@ -102,11 +102,14 @@ __global__ __launch_bounds__(256) void stage_gate_kernel(ChunkParams p) {
   float *sB = reinterpret_cast<float *>(smem);
   float *sBL = sB + C * TL::LDB;
   float *sSeg = sBL + D;
+  float *sDt = sSeg + kNT;
   const int64_t ld = (int64_t)p.H * D;
+  for (int i = threadIdx.x; i < D; i += kNT) sDt[i] = p.dt_bias ? p.dt_bias[h * D + i] : 0.f;
   load_rows<float, kNT, C, D>(sB, TL::LDB, p.g + lc.t0 * ld + h * D, ld, lc.L);
   __syncthreads();
-  gate_cumsum<kNT, C, D>(sB, TL::LDB, sBL, sSeg, lc.L, p.gate_kind, p.dt_bias ? p.dt_bias + h * D : nullptr,
-                         head_expA(p, h), p.lower_bound);
+  gate_activate<kNT, C, D, GK>(sB, TL::LDB, lc.L, sDt, head_expA(p, h), p.lower_bound);
+  __syncthreads();
+  gate_cumsum<kNT, C, D>(sB, TL::LDB, sBL, sSeg);
   store_rows_f32<C, D, TL::LDB>(p.b + lc.t0 * ld + h * D, ld, sB, lc.L);
 }
 
@@ -332,8 +335,14 @@ hipError_t launch_chunk_index(const ChunkParams &p, hipStream_t st) {
 
 hipError_t launch_stage_gate(const ChunkParams &p, hipStream_t st) {
   return dispatch(p, [&]<typename Tin, int C, int D>() {
-    const size_t smem = sizeof(float) * ((size_t)C * (D + 4) + D + kNT);
-    return launch_dyn(stage_gate_kernel<C, D>, dim3(p.max_chunks, p.H), smem, st, p);
+    const size_t smem = sizeof(float) * ((size_t)C * (D + 4) + 2 * D + kNT);
+    const dim3 grid(p.max_chunks, p.H);
+    switch (p.gate_kind) {
+      case kGateSafe: return launch_dyn(stage_gate_kernel<C, D, kGateSafe>, grid, smem, st, p);
+      case kGateSoftplus: return launch_dyn(stage_gate_kernel<C, D, kGateSoftplus>, grid, smem, st, p);
+      case kGateLogE: return launch_dyn(stage_gate_kernel<C, D, kGateLogE>, grid, smem, st, p);
+    }
+    return hipErrorInvalidValue;
   });
 }
 

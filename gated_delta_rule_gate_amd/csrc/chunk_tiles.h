@@ -94,16 +94,25 @@ struct Tile {
 };
 
 // Copies L rows of COLS elements (global row stride ldg elements) into an LDS
-// tile of row stride lds; rows L..ROWS-1 are zero-filled. 16-byte accesses.
+// tile of row stride lds; rows L..ROWS-1 are zero-filled. 16-byte accesses,
+// all loads of a thread issued before its first LDS write.
 template <typename T, int NT, int ROWS, int COLS>
 __device__ __forceinline__ void load_rows(T *s, int lds, const T *g, int64_t ldg, int L) {
   constexpr int EPV = 16 / (int)sizeof(T);
-  constexpr int VPR = COLS / EPV;
-  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
+  constexpr int VPR = COLS / EPV, NV = ROWS * VPR, IT = (NV + NT - 1) / NT;
+  u32x4_t buf[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NT + tid_opaque();
     const int r = idx / VPR, c = (idx % VPR) * EPV;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (r < L) val = *reinterpret_cast<const uint4 *>(g + (int64_t)r * ldg + c);
-    *reinterpret_cast<uint4 *>(s + r * lds + c) = val;
+    buf[it] = u32x4_t{0u, 0u, 0u, 0u};
+    if ((NV % NT == 0 || idx < NV) && r < L) buf[it] = *reinterpret_cast<const u32x4_t *>(g + (int64_t)r * ldg + c);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NT + tid_opaque();
+    const int r = idx / VPR, c = (idx % VPR) * EPV;
+    if (NV % NT == 0 || idx < NV) *reinterpret_cast<u32x4_t *>(s + r * lds + c) = buf[it];
   }
 }
 
@@ -111,50 +120,74 @@ __device__ __forceinline__ void load_rows(T *s, int lds, const T *g, int64_t ldg
 // intermediates of the staged schedule).
 template <typename T, int NT, int ROWS, int COLS>
 __device__ __forceinline__ void load_rows_cvt(T *s, int lds, const float *g, int64_t ldg, int L) {
-  constexpr int VPR = COLS / 4;
-  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
-    const int r = idx / VPR, c = (idx % VPR) * 4;
-    f32x4_t val = zero4();
-    if (r < L) val = *reinterpret_cast<const f32x4_t *>(g + (int64_t)r * ldg + c);
+  constexpr int VPR = COLS / 4, NV = ROWS * VPR, IT = (NV + NT - 1) / NT;
+  f32x4_t buf[IT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s[r * lds + c + e] = from_f32<T>(val[e]);
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NT + tid_opaque();
+    const int r = idx / VPR, c = (idx % VPR) * 4;
+    buf[it] = zero4();
+    if ((NV % NT == 0 || idx < NV) && r < L) buf[it] = *reinterpret_cast<const f32x4_t *>(g + (int64_t)r * ldg + c);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NT + tid_opaque();
+    const int r = idx / VPR, c = (idx % VPR) * 4;
+    if (NV % NT == 0 || idx < NV) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[r * lds + c + e] = from_f32<T>(buf[it][e]);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// (1) gate activation + chunk-local inclusive cumsum in log2 units, in place.
-// On entry sB rows [0, L) hold the raw gate input; on exit sB holds b for all
-// C rows (rows >= L repeat b[L-1], i.e. they carry a zero gate) and sBL holds
-// b[C-1] == b[L-1]. sSeg is scratch of NT floats.
+// (1) gate activation, then the chunk-local inclusive cumsum in log2 units.
+// gate_activate: rows [0, L) of sB hold the raw gate input and become the
+// per-token log2 decay; rows >= L become 0 (a zero gate). sDt: [D] dt_bias.
+// gate_cumsum: in-place inclusive cumsum over the C rows; sBL <- b[C-1]
+// (== b[L-1]). sSeg is scratch of NT floats.
 // ---------------------------------------------------------------------------------------------
+template <int NT, int C, int D, int GK>
+__device__ __forceinline__ void gate_activate(float *sB, int ldb, int L, const float *sDt, float expA,
+                                              float lower_bound) {
+  constexpr int VPR = D / 4, NV = C * VPR, IT = NV / NT;
+  static_assert(NV % NT == 0, "tile");
+#pragma unroll 4
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NT + tid_opaque();
+    const int r = idx / VPR, c = (idx % VPR) * 4;
+    f32x4_t x = *reinterpret_cast<const f32x4_t *>(sB + r * ldb + c);
+    const f32x4_t dt = *reinterpret_cast<const f32x4_t *>(sDt + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (r < L) ? gate_log2(GK, x[e], dt[e], expA, lower_bound) : 0.f;
+    *reinterpret_cast<f32x4_t *>(sB + r * ldb + c) = x;
+  }
+}
+
 template <int NT, int C, int D>
-__device__ void gate_cumsum(float *sB, int ldb, float *sBL, float *sSeg, int L, int kind, const float *dt_bias,
-                            float expA, float lower_bound) {
+__device__ __forceinline__ void gate_cumsum(float *sB, int ldb, float *sBL, float *sSeg) {
   static_assert(NT % D == 0, "thread mapping: whole channels per thread group");
   constexpr int TPC = NT / D;  // threads per channel, each owning RPS consecutive rows
   constexpr int RPS = C / TPC;
-  const int tid = threadIdx.x, col = tid % D, seg = tid / D;
-  const float dt = dt_bias ? dt_bias[col] : 0.f;
-  float run = 0.f;
-#pragma unroll 8
-  for (int i = 0; i < RPS; ++i) {
-    const int r = seg * RPS + i;
-    const float la = (r < L) ? gate_log2(kind, sB[r * ldb + col], dt, expA, lower_bound) : 0.f;
-    run += la;
-    sB[r * ldb + col] = run;
-  }
+  const int tid = tid_opaque(), col = tid % D, seg = tid / D;
+  float vals[RPS];
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) vals[i] = sB[(seg * RPS + i) * ldb + col];
+#pragma unroll
+  for (int i = 1; i < RPS; ++i) vals[i] += vals[i - 1];
   if constexpr (TPC > 1) {
-    sSeg[seg * D + col] = run;
+    sSeg[seg * D + col] = vals[RPS - 1];
     __syncthreads();
-    if (seg > 0) {
-      float off = 0.f;
-      for (int s2 = 0; s2 < seg; ++s2) off += sSeg[s2 * D + col];
-#pragma unroll 8
-      for (int i = 0; i < RPS; ++i) sB[(seg * RPS + i) * ldb + col] += off;
-    }
+    float off = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < TPC - 1; ++s2)
+      if (s2 < seg) off += sSeg[s2 * D + col];
+#pragma unroll
+    for (int i = 0; i < RPS; ++i) vals[i] += off;
   }
-  __syncthreads();
-  if (tid < D) sBL[tid] = sB[(C - 1) * ldb + tid];
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) sB[(seg * RPS + i) * ldb + col] = vals[i];
+  if (seg == TPC - 1) sBL[col] = vals[RPS - 1];
   __syncthreads();
 }
 
@@ -177,7 +210,7 @@ __device__ void grams(const Tin *sQ, const Tin *sK, const float *sB, const float
   using TL = Tile<Tin, C, D>;
   constexpr int NW = NT / 64, NC = TL::NC, NB = NC * (NC + 1) / 2;
   constexpr int LDT = TL::LDT, LDB = TL::LDB;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = tid_opaque() & 63, wid = tid_opaque() >> 6;
   const int n16 = lane & 15, grp = lane >> 4;
 
   for (int blk = wid; blk < NB; blk += NW) {
@@ -232,9 +265,11 @@ __device__ void grams(const Tin *sQ, const Tin *sK, const float *sB, const float
       }
     }
   }
-  for (int idx = threadIdx.x; idx < C * C; idx += NT) {
+#pragma unroll
+  for (int it = 0; it < (C * C + NT - 1) / NT; ++it) {
+    const int idx = it * NT + tid_opaque();
     const int r = idx / C, c = idx % C;
-    if ((c >> 4) > (r >> 4) && r < wlim) {
+    if (idx < C * C && (c >> 4) > (r >> 4) && r < wlim) {
       Akk[r * ldo + c] = 0.f;
       Aqk[r * ldo + c] = 0.f;
     }
@@ -250,22 +285,26 @@ __device__ void grams(const Tin *sQ, const Tin *sK, const float *sB, const float
 template <int NT, int C>
 __device__ void solve(const float *sAkk, float *sT) {
   constexpr int NW = NT / 64, NC = C / 16, LDA = C + 4;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = tid_opaque() & 63, wid = tid_opaque() >> 6;
   const int n16 = lane & 15, grp = lane >> 4;
-  for (int idx = threadIdx.x; idx < C * C; idx += NT) {
+#pragma unroll
+  for (int it = 0; it < (C * C + NT - 1) / NT; ++it) {
+    const int idx = it * NT + tid_opaque();
     const int r = idx / C, c = idx % C;
-    if ((c >> 4) > (r >> 4)) sT[r * LDA + c] = 0.f;
+    if (idx < C * C && (c >> 4) > (r >> 4)) sT[r * LDA + c] = 0.f;
   }
   if (wid == NW - 1 && lane < 16 * NC) {
+    // column c of T_ii solves (I + A_ii) x = e_c; right-looking so that each
+    // step's 15 - s updates are independent
     const int i = lane >> 4, c = lane & 15;
     const float *A = sAkk + 16 * i * LDA + 16 * i;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == c) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < r; ++s) acc -= A[r * LDA + s] * x[s];
-      x[r] = acc;
+    for (int s = 0; s < 16; ++s) {
+#pragma unroll
+      for (int r = s + 1; r < 16; ++r) x[r] -= A[r * LDA + s] * x[s];
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) sT[(16 * i + r) * LDA + 16 * i + c] = x[r];
@@ -306,7 +345,7 @@ template <typename Tin, int C, int NV, typename XF>
 __device__ __forceinline__ void tri_mm(const float *sT, int ct, f32x4_t (&acc)[C / 16][NV], int v, XF xval) {
   using M = Mma<Tin>;
   constexpr int NC = C / 16, LDA = C + 4, NS = C / M::KS;
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
   const int col = 16 * ct + n16;
 #pragma unroll
@@ -331,9 +370,16 @@ __device__ __forceinline__ void tri_mm(const float *sT, int ct, f32x4_t (&acc)[C
 template <typename Tin, int NT, int C, int D>
 __device__ __forceinline__ void make_qtilde(Tin *sQ, const float *sB, float scale) {
   using TL = Tile<Tin, C, D>;
-  for (int idx = threadIdx.x; idx < C * D; idx += NT) {
-    const int r = idx / D, c = idx % D;
-    sQ[r * TL::LDT + c] = from_f32<Tin>(scale * to_f32(sQ[r * TL::LDT + c]) * fast_exp2(sB[r * TL::LDB + c]));
+  constexpr int VPR = D / 4, IT = C * VPR / NT;
+  static_assert(C * VPR % NT == 0, "tile");
+#pragma unroll 4
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NT + tid_opaque();
+    const int r = idx / VPR, c = (idx % VPR) * 4;
+    const f32x4_t b = *reinterpret_cast<const f32x4_t *>(sB + r * TL::LDB + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sQ[r * TL::LDT + c + e] = from_f32<Tin>(scale * to_f32(sQ[r * TL::LDT + c + e]) * fast_exp2(b[e]));
   }
 }
 
@@ -341,7 +387,11 @@ __device__ __forceinline__ void make_qtilde(Tin *sQ, const float *sB, float scal
 template <typename Tin, int NT, int C, int D>
 __device__ __forceinline__ void make_ktilde_t(Tin *sKT, const Tin *sK, const float *sB, const float *sBL) {
   using TL = Tile<Tin, C, D>;
-  for (int idx = threadIdx.x; idx < C * D; idx += NT) {
+  constexpr int IT = C * D / NT;
+  static_assert(C * D % NT == 0, "tile");
+#pragma unroll 4
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NT + tid_opaque();
     const int c = idx % C, i = idx / C;  // consecutive threads walk the chunk rows
     const float v = to_f32(sK[c * TL::LDT + i]) * fast_exp2(sBL[i] - sB[c * TL::LDB + i]);
     sKT[i * TL::LDKT + c] = from_f32<Tin>(v);
@@ -352,12 +402,16 @@ __device__ __forceinline__ void make_ktilde_t(Tin *sKT, const Tin *sK, const flo
 // of a sequence carry a zero gate) and copies the last row to sBL.
 template <int NT, int C, int D>
 __device__ __forceinline__ void pad_cumsum(float *sB, int ldb, float *sBL, int L) {
-  for (int idx = threadIdx.x; idx < C * D; idx += NT) {
-    const int r = idx / D, c = idx % D;
-    if (r >= L) sB[r * ldb + c] = (L > 0) ? sB[(L - 1) * ldb + c] : 0.f;
+  if (L < C) {
+#pragma unroll
+    for (int it = 0; it < C * D / NT; ++it) {
+      const int idx = it * NT + tid_opaque();
+      const int r = idx / D, c = idx % D;
+      if (r >= L) sB[r * ldb + c] = (L > 0) ? sB[(L - 1) * ldb + c] : 0.f;
+    }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < D; c += NT) sBL[c] = sB[(C - 1) * ldb + c];
+  for (int c = tid_opaque(); c < D; c += NT) sBL[c] = sB[(C - 1) * ldb + c];
 }
 
 // Same from global rows: k [L][D] (row stride ld) and the fp32 cumsum b [L][D];
@@ -366,7 +420,7 @@ template <typename Tin, int NT, int C, int D>
 __device__ __forceinline__ void make_ktilde_t_global(Tin *sKT, const Tin *gK, const float *gB, int64_t ld,
                                                      const float *sBL, int L) {
   using TL = Tile<Tin, C, D>;
-  for (int idx = threadIdx.x; idx < C * D; idx += NT) {
+  for (int idx = tid_opaque(); idx < C * D; idx += NT) {
     const int i = idx % D, c = idx / D;  // consecutive threads walk the channels (coalesced reads)
     float v = 0.f;
     if (c < L) v = to_f32(gK[(int64_t)c * ld + i]) * fast_exp2(sBL[i] - gB[(int64_t)c * ld + i]);
@@ -387,7 +441,7 @@ __device__ __forceinline__ void rows_times_state(f32x4_t (&out0)[C / 16][NVW], f
   using M = Mma<Tin>;
   using TL = Tile<Tin, C, D>;
   constexpr int NC = TL::NC, DT = TL::DT, LDT = TL::LDT, SD = D / M::KS;
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int s = 0; s < SD; ++s) {
@@ -423,7 +477,7 @@ __device__ __forceinline__ void causal_times(f32x4_t (&o)[C / 16][NVW], const fl
                                              const f32x4_t (&vn)[C / 16][NVW]) {
   using M = Mma<Tin>;
   constexpr int NC = C / 16, LDA = C + 4, SC = C / M::KS;
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int s = 0; s < SC; ++s) {
@@ -453,7 +507,7 @@ __device__ __forceinline__ void state_update(f32x4_t (&h)[D / 16][NVW], const Ti
                                              const f32x4_t (&vn)[C / 16][NVW], const float *sDecay) {
   using M = Mma<Tin>;
   constexpr int NC = C / 16, DT = D / 16, SC = C / M::KS;
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
@@ -487,7 +541,7 @@ __device__ __forceinline__ void state_update(f32x4_t (&h)[D / 16][NVW], const Ti
 // are not stored.
 template <int RT, int NVW>
 __device__ __forceinline__ void load_strip(f32x4_t (&x)[RT][NVW], const float *g, int64_t ld, int col0, int L) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int t = 0; t < RT; ++t)
@@ -502,7 +556,7 @@ __device__ __forceinline__ void load_strip(f32x4_t (&x)[RT][NVW], const float *g
 
 template <typename T, int RT, int NVW>
 __device__ __forceinline__ void store_strip(T *g, int64_t ld, int col0, int L, const f32x4_t (&x)[RT][NVW]) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int t = 0; t < RT; ++t)

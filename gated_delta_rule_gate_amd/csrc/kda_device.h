@@ -11,6 +11,7 @@ namespace kda {
 typedef __bf16 bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // raw 16-byte chunk
 
 constexpr float kLog2e = 1.4426950408889634f;  // 1 / ln 2 (the RCP_LN2 conversion)
 constexpr float kLn2 = 0.6931471805599453f;
@@ -30,6 +31,16 @@ template <>
 __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return static_cast<bf16_t>(x); }
+
+// threadIdx.x behind an empty volatile asm: values derived from it cannot be
+// hoisted out of loops, so per-thread LDS/global addresses are recomputed
+// where they are used instead of being held in registers across a whole loop
+// (which otherwise spills the chunk loop's live state).
+__device__ __forceinline__ int tid_opaque() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 // Hardware base-2 exponential / logarithm / reciprocal (v_exp_f32, v_log_f32, v_rcp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -7,6 +7,7 @@ Bounds (per tensor, over valid rows only):
 rel-RMS is ||x - y||_2 / ||y||_2 over all compared elements.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -42,6 +43,11 @@ def parity(got, want, dtype, what=""):
     max_abs = float(np.abs(diff).max()) if diff.size else 0.0
     den = float(np.sqrt(np.sum(want * want)))
     rel = float(np.sqrt(np.sum(diff * diff)) / den) if den > 0 else float(np.sqrt(np.sum(diff * diff)))
+    log = os.environ.get("KDA_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write("%s | %s | %s | max-abs %.3e | rel-RMS %.3e\n" % (
+                os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0], what, dtype, max_abs, rel))
     if dtype == "fp32":
         assert max_abs <= FP32_MAX_ABS, "%s: max-abs %.3e > %.1e" % (what, max_abs, FP32_MAX_ABS)
     else:
