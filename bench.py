@@ -18,6 +18,7 @@ One JSON line on stdout:
                  log2 gate, fp32 state read and written in place.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -48,6 +49,37 @@ def alg_flops_chunk(B, T, H, D, C=64):
     pbar = 16 * (NC + 1) / 2
     per = 6 * D * D + 2 * (2 * D) * pbar + (2 * D + 2 * D) * pbar + 2 * D * pbar + C * C / 3
     return B * T * H * per
+
+
+FUSED_SOURCES = ("chunk_fused.hip", "chunk_tiles.h", "kda_device.h", "kda_launch.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_chunk_b4t4096h64d128_traffic.txt")
+
+
+def kernel_source_sha():
+    """sha256 over the sources the fused chunk kernel is built from."""
+    h = hashlib.sha256()
+    for name in FUSED_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_gate_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            vals[key.strip()] = val.strip()
+    if vals.get("source_sha256") != kernel_source_sha():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def event_time_ms(fn, steps, warmup, flush=None):
@@ -156,9 +188,10 @@ def main():
         flush_buf.zero_()
 
     if args.calib_copy:
-        src = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")  # 1 GiB
+        # one elementwise dispatch that reads 1 GiB and writes 1 GiB (counter calibration)
+        src = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
 
     cold = event_time_ms(step, args.steps, args.warmup, flush=flush)
@@ -185,7 +218,9 @@ def main():
         "config": {"workload": "chunk_kda fwd B%d T%d H%d K=V=%d bf16, C=%d, safe gate lb=-5, h0+ht" % (B, T, H, D, C),
                    "B": B, "T": T, "H": H, "D": D, "chunk": C, "schedule": args.schedule, "cache": "flushed"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if args.schedule != "staged" and (B, T, H, D) == (4, 4096, 64, 128)
+                     else None,
                      "kernel": "fused_chunk_kernel" if args.schedule != "staged" else "staged chain",
                      "alg_bytes_per_launch": nbytes,
                      "alg_tflops": round(flops / (ms * 1e-3) / 1e12, 2),

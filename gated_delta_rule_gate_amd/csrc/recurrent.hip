@@ -18,11 +18,42 @@
 #include "kda_device.h"
 #include "kda_launch.h"
 
+// State traffic cache policy: 0 = default, 1 = non-temporal stores,
+// 2 = non-temporal loads and stores, 3 = non-temporal loads only
+// (the state is touched once per call).
+#ifndef KDA_REC_STATE_NT
+#define KDA_REC_STATE_NT 2
+#endif
+// Threads per workgroup (256 or 512).
+#ifndef KDA_REC_THREADS
+#define KDA_REC_THREADS 256
+#endif
+// Widest value block per workgroup (128 or 64 columns).
+#ifndef KDA_REC_MAX_BV
+#define KDA_REC_MAX_BV 128
+#endif
+
 namespace kda {
+
+__device__ __forceinline__ f32x4_t load_state4(const float *p) {
+#if KDA_REC_STATE_NT >= 2
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+#else
+  return *reinterpret_cast<const f32x4_t *>(p);
+#endif
+}
+
+__device__ __forceinline__ void store_state4(float *p, f32x4_t v) {
+#if KDA_REC_STATE_NT == 1 || KDA_REC_STATE_NT == 2
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(p));
+#else
+  *reinterpret_cast<f32x4_t *>(p) = v;
+#endif
+}
 
 template <int K, int BV>
 struct RecCfg {
-  static constexpr int kThreads = 256;
+  static constexpr int kThreads = KDA_REC_THREADS;
   static constexpr int kCG = BV / 4;             // column groups
   static constexpr int kRG = kThreads / kCG;     // row groups
   static constexpr int kRPT = K / kRG;           // rows per thread
@@ -30,7 +61,7 @@ struct RecCfg {
 };
 
 template <typename Tin, int K, int BV>
-__global__ __launch_bounds__(256) void recurrent_kernel(RecurrentParams p) {
+__global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentParams p) {
   using Cfg = RecCfg<K, BV>;
   constexpr int RPT = Cfg::kRPT, CG = Cfg::kCG, RG = Cfg::kRG;
   const int nvb = p.V / BV;
@@ -50,7 +81,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecurrentParams p) {
   if (p.h0) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-      S[r] = *reinterpret_cast<const f32x4_t *>(p.h0 + sbase + (int64_t)(row0 + r) * p.V + col0);
+      S[r] = load_state4(p.h0 + sbase + (int64_t)(row0 + r) * p.V + col0);
   } else {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -60,7 +91,8 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecurrentParams p) {
   __shared__ float s_v[2][BV];
   __shared__ float s_red[2][RG][BV];
   __shared__ float s_d[BV];
-  __shared__ float s_kq[2][4];
+  constexpr int NWAVE = Cfg::kThreads / 64;
+  __shared__ float s_kq[2][NWAVE];
   __shared__ float s_beta[2];
 
   const float expA = (p.gate_kind == kGateSafe || p.gate_kind == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
@@ -128,7 +160,9 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecurrentParams p) {
         sk += s_red[0][g2][tid];
         sq += s_red[1][g2][tid];
       }
-      const float kqs = s_kq[buf][0] + s_kq[buf][1] + s_kq[buf][2] + s_kq[buf][3];
+      float kqs = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) kqs += s_kq[buf][w];
       const float d = s_beta[buf] * (s_v[buf][tid] - sk);
       s_d[tid] = d;
       const int64_t th = (sr.t0 + i) * p.H + h;
@@ -146,7 +180,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecurrentParams p) {
   if (p.ht && !(sr.len == 0 && p.ht == p.h0)) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-      *reinterpret_cast<f32x4_t *>(p.ht + sbase + (int64_t)(row0 + r) * p.V + col0) = S[r];
+      store_state4(p.ht + sbase + (int64_t)(row0 + r) * p.V + col0, S[r]);
   }
 }
 
@@ -154,14 +188,14 @@ template <typename Tin, int K, int BV>
 static hipError_t launch_rec(const RecurrentParams &p, hipStream_t st) {
   const int grid = p.N * p.H * (p.V / BV);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((recurrent_kernel<Tin, K, BV>), dim3(grid), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((recurrent_kernel<Tin, K, BV>), dim3(grid), dim3(RecCfg<K, BV>::kThreads), 0, st, p);
   return hipGetLastError();
 }
 
 template <typename Tin, int K>
 static hipError_t launch_rec_k(const RecurrentParams &p, hipStream_t st) {
   // value block: 128 columns when V allows (one 64 KB contiguous state block at K = 128)
-  if (p.V % 128 == 0) return launch_rec<Tin, K, 128>(p, st);
+  if (KDA_REC_MAX_BV >= 128 && p.V % 128 == 0) return launch_rec<Tin, K, 128>(p, st);
   return launch_rec<Tin, K, 64>(p, st);
 }
 
