@@ -12,8 +12,8 @@ One JSON line on stdout:
   roofline       the dominant kernel (the fused chunk kernel: one launch per
                  call) against HBM: algorithmic bytes per launch (q, k, v, gate,
                  beta, o, h0, ht counted once) / its mean launch time.
-  cpu_baseline   the FP64 oracle on the host cores, on two of the four
-                 sequences (all 64 heads, all 4096 tokens) incl. the gate.
+  cpu_baseline   the FP64 oracle on the host cores over the same workload
+                 (4 sequences, 64 heads, 4096 tokens, gate included), 3 timed runs.
   recurrent_decode  kda_recurrent_fwd: 256 sequences x 1 token, H64 D128, bf16,
                  log2 gate, fp32 state read and written in place.
 """
@@ -106,22 +106,29 @@ def event_time_ms(fn, steps, warmup, flush=None):
                 p90=float(np.percentile(times, 90)), wall_ms=wall * 1e3)
 
 
-def cpu_baseline(d, H, T, threads):
+def cpu_baseline(d, H, T, threads, runs=3):
+    """The FP64 oracle (token recurrence + gate activation) on the whole headline
+    workload: one untimed run, then the mean of ``runs`` timed runs."""
     import oracle
     from kda_synth import to_f64
 
-    nseq = 2
-    sub = {k: (v[:nseq] if k in ("q", "k", "v", "x", "beta", "h0") else v) for k, v in d.items()}
-    q, k, v, x, beta, h0 = (to_f64(sub[n]) for n in ("q", "k", "v", "x", "beta", "h0"))
-    A_log, dt = to_f64(sub["A_log"]), to_f64(sub["dt_bias"])
+    q, k, v, x, beta, h0 = (to_f64(d[n]) for n in ("q", "k", "v", "x", "beta", "h0"))
+    A_log, dt = to_f64(d["A_log"]), to_f64(d["dt_bias"])
+
+    def once():
+        g = oracle.gate(oracle.GATE_SAFE, x, A_log, dt, -5.0)
+        oracle.recurrent(q, k, v, g, beta, h0=h0, nthreads=threads)
+
+    once()
     t0 = time.perf_counter()
-    g = oracle.gate(oracle.GATE_SAFE, x, A_log, dt, -5.0)
-    oracle.recurrent(q, k, v, g, beta, h0=h0, nthreads=threads)
-    dt_s = time.perf_counter() - t0
+    for _ in range(runs):
+        once()
+    dt_s = (time.perf_counter() - t0) / runs
+    nseq = q.shape[0]
     tokens = nseq * T
     return dict(value=tokens / dt_s / 1e6, unit="Mtokens/s", cores=threads, kind="oracle",
-                sample="2 of 4 sequences x all %d heads x %d tokens (FP64 token recurrence + gate), %.1f s"
-                       % (H, T, dt_s))
+                sample="all %d sequences x %d heads x %d tokens (FP64 token recurrence + gate), "
+                       "mean of %d runs after 1 untimed, %.2f s per run" % (nseq, H, T, runs, dt_s))
 
 
 def bench_decode(steps, warmup):

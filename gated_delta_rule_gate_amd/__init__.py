@@ -3,6 +3,6 @@
 The computation lives in the HIP library ``_build/libkda.so`` (C ABI in
 ``include/kda.h``); this package only marshals arguments to it.
 """
-from ._binding import (KdaError, chunk_kda, lib, recurrent_kda, workspace_bytes)  # noqa: F401
+from ._binding import (KdaError, chunk_kda, gate_cumsum, lib, recurrent_kda, workspace_bytes)  # noqa: F401
 
-__all__ = ["chunk_kda", "recurrent_kda", "KdaError", "lib", "workspace_bytes"]
+__all__ = ["chunk_kda", "recurrent_kda", "gate_cumsum", "KdaError", "lib", "workspace_bytes"]

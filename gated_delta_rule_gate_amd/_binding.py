@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_build", "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
-GATE_KINDS = {"loge": 0, "safe": 1, "softplus": 2, "log2": 4}
+GATE_KINDS = {"loge": 0, "safe": 1, "softplus": 2, "log2_cumsum": 3, "log2": 4}
 SCHEDULES = {"auto": 0, "staged": 1, "fused": 2}
 
 _LIB = None
@@ -45,6 +45,8 @@ def lib():
         L.kda_last_error.restype = ctypes.c_char_p
         L.kda_recurrent_fwd.argtypes = [ap] + [vp] * 10
         L.kda_recurrent_fwd.restype = ctypes.c_int
+        L.kda_gate_cumsum.argtypes = [ap, vp, vp, ctypes.c_int, vp, vp]
+        L.kda_gate_cumsum.restype = ctypes.c_int
         if hasattr(L, "kda_chunk_fwd"):
             L.kda_chunk_workspace_bytes.argtypes = [ap]
             L.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
@@ -157,13 +159,40 @@ def recurrent_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, outp
     return o, ht
 
 
+def gate_cumsum(g, *, chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0,
+                cu_seqlens=None, out=None):
+    """Step (1) alone: the gate activation and the chunk-local cumsum in log2 units.
+
+    g is fp32 [B, T, H, K]. ``chunk_size`` 1 gives the per-token log2 decay that
+    ``recurrent_kda`` takes; 32 or 64 gives the gate that ``chunk_kda`` takes with
+    ``gate_kind="log2_cumsum"`` and the same chunk size. Rows outside the packed
+    contract are left as they are in ``out``.
+    """
+    _require(g.dim() == 4 and g.dtype == torch.float32, "g must be fp32 [B, T, H, K]")
+    B, T, H, K = g.shape
+    if cu_seqlens is not None:
+        _require(B == 1, "packed inputs (cu_seqlens) need batch 1")
+        _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1, "cu_seqlens must be int32 [N+1]")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    out = out if out is not None else torch.empty_like(g)
+    _require(out.shape == g.shape and out.dtype == torch.float32, "out must be fp32 like g")
+    _check_tensors(dict(g=g, out=out, cu_seqlens=cu_seqlens, A_log=A_log, dt_bias=dt_bias), g.device)
+    a = make_args(g, g, H, N, gate_kind, chunk_size=64, A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound)
+    check(lib().kda_gate_cumsum(ctypes.byref(a), _ptr(g), _ptr(cu_seqlens), int(chunk_size), _ptr(out), _stream()))
+    return out
+
+
 def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_final_state=False,
               chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None,
               schedule="auto", final_state=None, out=None):
     """Chunked KDA prefill forward. Returns (o, ht); ht is None unless requested.
 
     g is the raw gate input for ``gate_kind`` "safe" / "softplus" (activation in
-    the kernel) or the natural-log decay for "loge". ``out`` may preallocate o.
+    the kernel), the natural-log decay for "loge", or the output of
+    ``gate_cumsum`` with the same chunk size for "log2_cumsum". ``out`` may
+    preallocate o.
     """
     B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
     o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)

@@ -174,7 +174,8 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     if (c + 1 < nch) regs.load(p, t0 + C, min(C, sr.len - (c + 1) * C), h);  // in flight during this chunk
 
     // (1)
-    gate_cumsum<NT, C, D>(sB, LDB, sBL, sSeg);
+    if constexpr (GK == kGateLog2Cumsum) gate_pad<NT, C, D>(sB, LDB, sBL, L);
+    else gate_cumsum<NT, C, D>(sB, LDB, sBL, sSeg);
     for (int i = tid_opaque(); i < D; i += NT) sDecay[i] = fast_exp2(sBL[i]);
     // (2)
     grams<Tin, NT, C, D, SAFE>(sQ, sK, sB, sBeta, p.scale, sAkk, sAqk, TL::LDA, L, C);
@@ -254,6 +255,7 @@ hipError_t launch_fused_t(const ChunkParams &p, hipStream_t st) {
     case kGateSafe: return launch_fused_g<Tin, C, D, NT, kGateSafe>(p, st);
     case kGateSoftplus: return launch_fused_g<Tin, C, D, NT, kGateSoftplus>(p, st);
     case kGateLogE: return launch_fused_g<Tin, C, D, NT, kGateLogE>(p, st);
+    case kGateLog2Cumsum: return launch_fused_g<Tin, C, D, NT, kGateLog2Cumsum>(p, st);
   }
   return hipErrorInvalidValue;
 }

@@ -334,6 +334,7 @@ hipError_t launch_chunk_index(const ChunkParams &p, hipStream_t st) {
 }
 
 hipError_t launch_stage_gate(const ChunkParams &p, hipStream_t st) {
+  if (p.gate_kind == kGateLog2Cumsum) return hipSuccess;  // g already is b (p.b points at it)
   return dispatch(p, [&]<typename Tin, int C, int D>() {
     const size_t smem = sizeof(float) * ((size_t)C * (D + 4) + 2 * D + kNT);
     const dim3 grid(p.max_chunks, p.H);

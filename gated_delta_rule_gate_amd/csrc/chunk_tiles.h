@@ -191,6 +191,18 @@ __device__ __forceinline__ void gate_cumsum(float *sB, int ldb, float *sBL, floa
   __syncthreads();
 }
 
+// gate_pad: sB already holds the chunk-local cumsum for rows [0, L); rows >= L
+// take row L-1's value (as the cumsum of a zero gate would) and sBL <- b[L-1].
+template <int NT, int C, int D>
+__device__ __forceinline__ void gate_pad(float *sB, int ldb, float *sBL, int L) {
+  for (int idx = tid_opaque(); idx < (C - L) * D; idx += NT) {
+    const int r = L + idx / D, c = idx % D;
+    sB[r * ldb + c] = sB[(L - 1) * ldb + c];
+  }
+  for (int c = tid_opaque(); c < D; c += NT) sBL[c] = sB[(L - 1) * ldb + c];
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------------------------
 // (2) intra-chunk grams over the causal 16x16 blocks (i, j <= i) only.
 // Safe gate: diagonal blocks factor 2^(b_r-b_s) through the block's midpoint

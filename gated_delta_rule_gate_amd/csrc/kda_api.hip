@@ -42,6 +42,9 @@ kda_status check_common(const kda_args *a, const void *q, const void *k, const v
     case KDA_GATE_LOG2:
       if (!recurrent) return KDA_ERR_GATE;
       break;
+    case KDA_GATE_LOG2_CUMSUM:
+      if (recurrent) return KDA_ERR_GATE;
+      break;
     case KDA_GATE_SAFE:
       if (!a->A_log) return KDA_ERR_GATE;
       if (!(a->lower_bound >= -5.0f && a->lower_bound < 0.0f)) return KDA_ERR_GATE;
@@ -88,6 +91,53 @@ extern "C" const char *kda_status_string(kda_status s) {
 }
 
 extern "C" const char *kda_last_error(void) { return g_last_error; }
+
+// ---------------------------------------------------------------------------------------------
+// step (1) on its own
+// ---------------------------------------------------------------------------------------------
+extern "C" kda_status kda_gate_cumsum(const kda_args *a, const float *g_in, const int32_t *cu_seqlens,
+                                      int chunk_size, float *g_out, void *stream) {
+  if (!a) return KDA_ERR_NULL;
+  if (a->B < 1 || a->T < 0 || a->H < 1 || a->N < 0 || a->K < 1) return KDA_ERR_SHAPE;
+  if (!g_in || !g_out) return KDA_ERR_NULL;
+  if (!aligned16(g_in) || !aligned16(g_out)) return KDA_ERR_ALIGN;
+  if (chunk_size != 1 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_CHUNK;
+  switch (a->gate_kind) {
+    case KDA_GATE_LOGE:
+    case KDA_GATE_LOG2:
+      break;
+    case KDA_GATE_SAFE:
+      if (!a->A_log) return KDA_ERR_GATE;
+      if (!(a->lower_bound >= -5.0f && a->lower_bound < 0.0f)) return KDA_ERR_GATE;
+      break;
+    case KDA_GATE_SOFTPLUS:
+      if (!a->A_log) return KDA_ERR_GATE;
+      break;
+    default:
+      return KDA_ERR_GATE;
+  }
+  if (!width_ok(a->K)) return KDA_ERR_UNSUPPORTED;
+  kda_status s = check_slots(a, cu_seqlens);
+  if (s != KDA_OK) return s;
+  const size_t bytes = sizeof(float) * (size_t)a->B * a->T * a->H * a->K;
+  const char *i0 = reinterpret_cast<const char *>(g_in), *o0 = reinterpret_cast<const char *>(g_out);
+  if (bytes > 0 && i0 < o0 + bytes && o0 < i0 + bytes) return KDA_ERR_SHAPE;  // overlapping in/out
+  kda::GateCumsumParams p{};
+  p.g = g_in;
+  p.out = g_out;
+  p.cu = cu_seqlens;
+  p.A_log = a->A_log;
+  p.dt_bias = a->dt_bias;
+  p.lower_bound = a->lower_bound;
+  p.gate_kind = (int)a->gate_kind;
+  p.B = a->B;
+  p.T = a->T;
+  p.H = a->H;
+  p.K = a->K;
+  p.N = n_slots(a, cu_seqlens);
+  p.C = chunk_size;
+  return hip_status(kda::launch_gate_cumsum(p, (hipStream_t)stream));
+}
 
 extern "C" kda_status kda_recurrent_fwd(const kda_args *a, const void *q, const void *k, const void *v,
                                         const float *g, const float *beta, const float *h0,
@@ -222,6 +272,8 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
     p.u = reinterpret_cast<float *>(base + L.off[6]);
     p.vnew = reinterpret_cast<float *>(base + L.off[7]);
     p.hc = reinterpret_cast<float *>(base + L.off[8]);
+    // a pre-cumsummed gate is b itself: the gate step is skipped and the later steps read g
+    if (a->gate_kind == KDA_GATE_LOG2_CUMSUM) p.b = const_cast<float *>(g);
   }
   return KDA_OK;
 }

@@ -17,7 +17,7 @@ constexpr float kLog2e = 1.4426950408889634f;  // 1 / ln 2 (the RCP_LN2 conversi
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Gate kinds (values match kda_gate_kind in include/kda.h).
-enum GateKind : int { kGateLogE = 0, kGateSafe = 1, kGateSoftplus = 2, kGateLog2 = 4 };
+enum GateKind : int { kGateLogE = 0, kGateSafe = 1, kGateSoftplus = 2, kGateLog2Cumsum = 3, kGateLog2 = 4 };
 
 // ---------------------------------------------------------------------------------------------
 // Storage types: bf16 (round-to-nearest-even on store) or fp32.
@@ -57,13 +57,14 @@ __device__ __forceinline__ float log1p_pos(float x) {
 }
 
 // Per-token decay in log2 units from the gate input of one channel.
-//   kGateLog2:     g is already log2
+//   kGateLog2:     g is already log2 (kGateLog2Cumsum: already the chunk-local
+//                  cumsum in log2; callers skip their own cumsum)
 //   kGateLogE:     g * log2(e)
 //   kGateSafe:     lower_bound * sigmoid(expA * (x + dt)) * log2(e)
 //   kGateSoftplus: -expA * softplus(x + dt) * log2(e)
 // The activations follow "FLA KDA Skill", section "Gate modes".
 __device__ __forceinline__ float gate_log2(int kind, float x, float dt, float expA, float lower_bound) {
-  if (kind == kGateLog2) return x;
+  if (kind == kGateLog2 || kind == kGateLog2Cumsum) return x;
   if (kind == kGateLogE) return x * kLog2e;
   float z = x + dt;
   if (kind == kGateSafe) {

@@ -22,6 +22,20 @@ struct RecurrentParams {
 
 hipError_t launch_recurrent(const RecurrentParams &p, hipStream_t st);
 
+// Step (1) on its own: gate activation and chunk-local cumsum in log2 units
+// over [B*T, H, K] rows; C in {1, 32, 64}.
+struct GateCumsumParams {
+  const float *g;
+  float *out;
+  const int32_t *cu;
+  const float *A_log, *dt_bias;
+  float lower_bound;
+  int gate_kind;
+  int B, T, H, K, N, C;
+};
+
+hipError_t launch_gate_cumsum(const GateCumsumParams &p, hipStream_t st);
+
 // Chunked prefill. D = K = V. Intermediates of the staged schedule are fp32,
 // token-major like the inputs: b, w, u, vnew [B*T, H, D]; Akk, Aqk, Tm
 // [B*T, H, C] (column = row within the chunk); hc [n_chunks, H, D, D], the

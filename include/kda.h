@@ -70,7 +70,9 @@ typedef enum {
   KDA_GATE_SAFE = 1,     /* g is raw x: lower_bound * sigmoid(exp(A_log) * (x + dt_bias)),
                             requires A_log and -5 <= lower_bound < 0                       */
   KDA_GATE_SOFTPLUS = 2, /* g is raw x: -exp(A_log) * softplus(x + dt_bias), requires A_log */
-  KDA_GATE_LOG2 = 4      /* g is the per-token log2 decay (recurrent entry point only)      */
+  KDA_GATE_LOG2_CUMSUM = 3, /* g is the chunk-local log2 cumsum that kda_gate_cumsum writes
+                               with the same chunk size (kda_chunk_fwd only)               */
+  KDA_GATE_LOG2 = 4      /* g is the per-token log2 decay (kda_recurrent_fwd, kda_gate_cumsum) */
 } kda_gate_kind;
 
 /* Execution schedule of kda_chunk_fwd. All schedules compute the same function. */
@@ -107,6 +109,32 @@ const char *kda_last_error(void);
 size_t kda_chunk_workspace_bytes(const kda_args *args);
 
 /*
+ * Step (1) of the chunked forward on its own: the gate activation and the
+ * chunk-local inclusive cumsum in base 2 ("FLA KDA Skill", sections "Gate
+ * modes" and "Safe gate numerical note": RCP_LN2 conversion),
+ *     g_out[t, h, i] = sum over s in [start of t's chunk, t] of act(g_in[s, h, i]),
+ * with chunks of chunk_size rows restarting at every sequence start.
+ * act() is the gate of args->gate_kind in log2 units: LOGE (times log2 e),
+ * SAFE, SOFTPLUS (activation of the raw input) or LOG2 (as is).
+ *   chunk_size 1      g_out is the per-token log2 decay kda_recurrent_fwd takes
+ *                     (KDA_GATE_LOG2);
+ *   chunk_size 32/64  g_out is the input of kda_chunk_fwd under
+ *                     KDA_GATE_LOG2_CUMSUM with the same chunk size (the
+ *                     pre-cumsummed gate contract of "Add fused recurrent_kda ...",
+ *                     section "Agent note").
+ * Arguments:
+ *   args        B, T, H, K, N, gate_kind, A_log, dt_bias, lower_bound are used;
+ *               V, dtype, scale, chunk_size and schedule are ignored
+ *   g_in        fp32 [B, T, H, K] device pointer
+ *   cu_seqlens  int32 [N + 1] or NULL (dense: sequences of T rows)
+ *   g_out       fp32 [B, T, H, K] device pointer; must not overlap g_in
+ *               (KDA_ERR_SHAPE). Rows at or beyond cu_seqlens[N] are not written.
+ * Supported: K in {64, 128, 256}; chunk_size in {1, 32, 64} (else KDA_ERR_CHUNK).
+ */
+kda_status kda_gate_cumsum(const kda_args *args, const float *g_in, const int32_t *cu_seqlens, int chunk_size,
+                           float *g_out, void *stream);
+
+/*
  * Chunked prefill (chunk_kda forward). Steps, per (sequence, head, chunk):
  *  (1) gate activation and chunk-local cumsum in base 2 ("FLA KDA Skill",
  *      section "Safe gate numerical note": RCP_LN2 conversion);
@@ -121,7 +149,8 @@ size_t kda_chunk_workspace_bytes(const kda_args *args);
  *  (5) the inter-chunk state scan; (6) o = scale (q 2^b) h + A_qk (u - w h).
  * Arguments:
  *   q, k, v, o   see the layout conventions; dtype args->dtype
- *   g            fp32 [B, T, H, K]; gate_kind LOGE, SAFE or SOFTPLUS
+ *   g            fp32 [B, T, H, K]; gate_kind LOGE, SAFE, SOFTPLUS or
+ *                LOG2_CUMSUM (step (1) already done by kda_gate_cumsum)
  *   beta         fp32 [B, T, H]
  *   h0           fp32 [N, H, K, V] or NULL (zero initial state)
  *   cu_seqlens   int32 [N + 1] or NULL (dense)

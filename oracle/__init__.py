@@ -25,7 +25,7 @@ import math
 import numpy as np
 
 from . import build as _build
-from .chunked import chunked_forward  # noqa: F401  (re-exported)
+from .chunked import chunk_cumsum_log2, chunked_forward  # noqa: F401  (re-exported)
 
 GATE_LOGE = 0
 GATE_SAFE = 1

@@ -140,3 +140,30 @@ def chunked_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chun
         inter[key] = inter[key].reshape((B, T) + inter[key].shape[1:])
     inter["hc"] = np.concatenate(hcs, axis=0) if hcs else np.zeros((0, H, K, V))
     return o, ht, inter
+
+
+def chunk_cumsum_log2(g, cu_seqlens=None, chunk_size=64, g_is_log2=False):
+    """Step (1) alone: b = log2(e) * (running sum of g from the start of each chunk).
+
+    g is the per-token decay [B, T, H, K] (natural log, or log2 with
+    ``g_is_log2``). Chunks of ``chunk_size`` rows restart at every sequence
+    start ("FLA KDA Skill", section "Safe gate numerical note": the RCP_LN2
+    conversion of the chunk-local cumsum). chunk_size 1 is the per-token log2
+    decay. Rows outside the packed contract are NaN.
+    """
+    g = np.asarray(g, dtype=np.float64)
+    B, T, H, K = g.shape
+    unit = 1.0 if g_is_log2 else RCP_LN2
+    cu = np.arange(B + 1) * T if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    gf = g.reshape(B * T, H, K)
+    out = np.full_like(gf, np.nan)
+    C = int(chunk_size)
+    for n in range(len(cu) - 1):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        run = np.zeros((H, K))
+        for t in range(s0, s1):
+            if (t - s0) % C == 0:
+                run = np.zeros((H, K))
+            run = run + gf[t] * unit
+            out[t] = run
+    return out.reshape(B, T, H, K)

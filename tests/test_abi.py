@@ -90,3 +90,45 @@ def test_safe_lower_bound_range(kda_lib):
         a = _args(gate_kind=1, A_log=0x100000, lower_bound=lb)
         st = kda_lib.kda_recurrent_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None)
         assert st == code, lb
+
+
+FAKE2 = ctypes.c_void_p(0x40000000)  # a second aligned address far from FAKE (no overlap)
+
+
+@pytest.mark.parametrize("kw,chunk,code", [
+    (dict(gate_kind=0), 16, 4),                 # chunk size not in {1, 32, 64}
+    (dict(gate_kind=3), 64, 5),                 # a pre-cumsummed gate is no input here
+    (dict(gate_kind=2), 64, 5),                 # SOFTPLUS without A_log
+    (dict(gate_kind=0, K=48), 64, 8),
+    (dict(gate_kind=0, B=2, N=1), 64, 2),
+])
+def test_gate_cumsum_rejects(kda_lib, kw, chunk, code):
+    a = _args(**kw)
+    st = kda_lib.kda_gate_cumsum(ctypes.byref(a), FAKE, None, chunk, FAKE2, None)
+    assert st == code, (kw, st)
+
+
+def test_gate_cumsum_rejects_overlap_and_null(kda_lib):
+    a = _args(gate_kind=0)
+    assert kda_lib.kda_gate_cumsum(ctypes.byref(a), FAKE, None, 64, FAKE, None) == 2
+    assert kda_lib.kda_gate_cumsum(ctypes.byref(a), None, None, 64, FAKE2, None) == 1
+    assert kda_lib.kda_gate_cumsum(None, FAKE, None, 64, FAKE2, None) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gate_kind=4), 5),                    # per-token log2 gate is the recurrent contract
+    (dict(gate_kind=0, chunk_size=16), 4),
+    (dict(gate_kind=0, V=64), 8),              # K != V
+    (dict(gate_kind=0, K=48, V=48), 8),
+])
+def test_chunk_rejects(kda_lib, kw, code):
+    a = _args(**kw)
+    st = kda_lib.kda_chunk_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None,
+                               FAKE2, ctypes.c_size_t(1 << 30), None)
+    assert st == code, (kw, st)
+
+
+def test_recurrent_rejects_precumsummed_gate(kda_lib):
+    a = _args(gate_kind=3)
+    st = kda_lib.kda_recurrent_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None)
+    assert st == 5

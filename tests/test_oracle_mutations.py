@@ -43,6 +43,14 @@ PY_MUTATIONS = {
     "k_tilde_direction": ("(kc * np.exp2(bL - b)).T @ vnew", "(kc * np.exp2(b - bL)).T @ vnew"),
 }
 
+CUMSUM_MUTATIONS = {
+    "no_chunk_restart": ("            if (t - s0) % C == 0:\n", "            if t == s0:\n"),
+    "restart_on_absolute_row": ("            if (t - s0) % C == 0:\n", "            if t % C == 0:\n"),
+    "exclusive_cumsum": ("            run = run + gf[t] * unit\n            out[t] = run\n",
+                         "            out[t] = run\n            run = run + gf[t] * unit\n"),
+    "natural_log_units": ("unit = 1.0 if g_is_log2 else RCP_LN2", "unit = 1.0"),
+}
+
 RECURRENCE_PINS = [
     ("test_exact_bruteforce_dyadic", dict(K=4, V=4, T=6, seed=0)),
     ("test_scalar_closed_form", {}),
@@ -115,3 +123,21 @@ def test_chunked_mutation_is_caught(oracle_mod, tmp_path, name):
         assert _fails_some_pin(CHUNKED_PINS), "mutation %s survived every pin" % name
     finally:
         pins.chunked_forward = saved
+
+
+@pytest.mark.parametrize("name", sorted(CUMSUM_MUTATIONS))
+def test_cumsum_mutation_is_caught(oracle_mod, tmp_path, name):
+    src = open(os.path.join(ORACLE_DIR, "chunked.py")).read()
+    old, new = CUMSUM_MUTATIONS[name]
+    assert src.count(old) == 1, "mutation anchor missing or ambiguous: " + old
+    path = tmp_path / "cumsum_mut.py"
+    path.write_text(src.replace(old, new, 1))
+    spec = importlib.util.spec_from_file_location("cumsum_mut_%s" % name, str(path))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    saved = pins.chunk_cumsum_log2
+    pins.chunk_cumsum_log2 = mod.chunk_cumsum_log2
+    try:
+        assert _fails_some_pin([("test_chunk_cumsum_pins", {})]), "mutation %s survived every pin" % name
+    finally:
+        pins.chunk_cumsum_log2 = saved

@@ -14,7 +14,7 @@ import pytest
 from scipy.special import expit
 
 import oracle
-from oracle import chunked_forward
+from oracle import chunk_cumsum_log2, chunked_forward
 
 
 def _l2(x):
@@ -334,3 +334,37 @@ def test_chunked_gram_matches_pairwise_definition(oracle_mod):
             e = bb[r] * np.sum(kk[r] * kk[s] * np.exp(G[r] - G[s])) if s < r else 0.0
             assert abs(it["Aqk"][0, r, 0, s] - d) <= 1e-12 * max(1, abs(d))
             assert abs(it["Akk"][0, r, 0, s] - e) <= 1e-12 * max(1, abs(e))
+
+
+# ----------------------------------------------------------------------------------------
+# Step (1) alone: the chunk-local cumsum in log2 units
+# ----------------------------------------------------------------------------------------
+
+def test_chunk_cumsum_pins(oracle_mod):
+    """C = 1 is g / ln 2; a chunk spanning the sequence is numpy's cumsum; every chunk
+    restarts; packed slots equal dense runs of their own rows; rows outside are NaN;
+    the chunked form's own b agrees."""
+    rng = np.random.default_rng(31)
+    g = -np.abs(rng.standard_normal((2, 100, 3, 8)))
+    ln2 = math.log(2.0)
+    np.testing.assert_allclose(chunk_cumsum_log2(g, chunk_size=1), g / ln2, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(chunk_cumsum_log2(g, chunk_size=128), np.cumsum(g, axis=1) / ln2, rtol=1e-13)
+    b32 = chunk_cumsum_log2(g, chunk_size=32)
+    for c0 in range(0, 100, 32):
+        np.testing.assert_allclose(b32[:, c0:c0 + 32], np.cumsum(g[:, c0:c0 + 32], axis=1) / ln2, rtol=1e-13)
+    np.testing.assert_allclose(chunk_cumsum_log2(g / ln2, chunk_size=32, g_is_log2=True), b32, rtol=1e-13)
+
+    lens = [0, 70, 5, 0, 33]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    gp = -np.abs(rng.standard_normal((1, int(cu[-1]) + 9, 2, 8)))
+    bp = chunk_cumsum_log2(gp, cu_seqlens=cu, chunk_size=32)
+    for n, L in enumerate(lens):
+        s0 = int(cu[n])
+        if L:
+            np.testing.assert_allclose(bp[:, s0:s0 + L], chunk_cumsum_log2(gp[:, s0:s0 + L], chunk_size=32),
+                                       rtol=1e-15)
+    assert np.isnan(bp[:, int(cu[-1]):]).all()
+    q, k, v, _, beta = _case(33, T=gp.shape[1], H=2, K=8, V=4)
+    _, _, it = chunked_forward(q, k, v, gp, beta, cu_seqlens=cu, chunk_size=32, emit=True)
+    valid = slice(0, int(cu[-1]))
+    np.testing.assert_allclose(bp[:, valid], it["b"][:, valid], rtol=1e-13, atol=1e-13)
