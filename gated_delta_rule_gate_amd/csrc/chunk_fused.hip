@@ -56,28 +56,34 @@ struct ChunkRegs {
   f32x4_t x[IX];
   float beta;
 
+  // The chunk's first element is a uniform base pointer; each vector is a
+  // 32-bit unsigned element offset from it, so the loads take the
+  // scalar-base + vector-offset form.
   __device__ __forceinline__ void load(const ChunkParams &p, int64_t t0, int L, int h) {
-    const int64_t ld = (int64_t)p.H * D;
-    const Tin *gq = reinterpret_cast<const Tin *>(p.q) + t0 * ld + h * D;
-    const Tin *gk = reinterpret_cast<const Tin *>(p.k) + t0 * ld + h * D;
-    const Tin *gv = reinterpret_cast<const Tin *>(p.v) + t0 * ld + h * D;
-    const float *gx = p.g + t0 * ld + h * D;
+    const unsigned ld = (unsigned)p.H * D;
+    const int64_t base = t0 * (int64_t)ld + (int64_t)h * D;
+    const Tin *gq = reinterpret_cast<const Tin *>(p.q) + base;
+    const Tin *gk = reinterpret_cast<const Tin *>(p.k) + base;
+    const Tin *gv = reinterpret_cast<const Tin *>(p.v) + base;
+    const float *gx = p.g + base;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int idx = it * NT + tid_opaque();
       const int r = idx / VPR, c = (idx % VPR) * EPV;
       const bool ok = (NVT % NT == 0 || idx < NVT) && r < L;
+      const unsigned off = (unsigned)r * ld + (unsigned)c;
       const u32x4_t z = {0u, 0u, 0u, 0u};
-      q[it] = ok ? *reinterpret_cast<const u32x4_t *>(gq + (int64_t)r * ld + c) : z;
-      k[it] = ok ? *reinterpret_cast<const u32x4_t *>(gk + (int64_t)r * ld + c) : z;
-      v[it] = ok ? *reinterpret_cast<const u32x4_t *>(gv + (int64_t)r * ld + c) : z;
+      q[it] = ok ? *reinterpret_cast<const u32x4_t *>(gq + off) : z;
+      k[it] = ok ? *reinterpret_cast<const u32x4_t *>(gk + off) : z;
+      v[it] = ok ? *reinterpret_cast<const u32x4_t *>(gv + off) : z;
     }
 #pragma unroll
     for (int it = 0; it < IX; ++it) {
       const int idx = it * NT + tid_opaque();
       const int r = idx / XPR, c = (idx % XPR) * 4;
       const bool ok = (NVX % NT == 0 || idx < NVX) && r < L;
-      x[it] = ok ? *reinterpret_cast<const f32x4_t *>(gx + (int64_t)r * ld + c) : zero4();
+      const unsigned off = (unsigned)r * ld + (unsigned)c;
+      x[it] = ok ? *reinterpret_cast<const f32x4_t *>(gx + off) : zero4();
     }
     const int r = tid_opaque();
     beta = (r < C && r < L) ? p.beta[(t0 + r) * p.H + h] : 0.f;
@@ -88,6 +94,7 @@ struct ChunkRegs {
   __device__ __forceinline__ void store(Tin *sQ, Tin *sK, Tin *sV, float *sB, float *sBeta, const float *sDt, int L,
                                         float expA, float lower_bound) const {
     using TL = Tile<Tin, C, D>;
+    wait_vmem();
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int idx = it * NT + tid_opaque();
@@ -106,7 +113,11 @@ struct ChunkRegs {
         const f32x4_t dt = *reinterpret_cast<const f32x4_t *>(sDt + c);
         f32x4_t la;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) la[e] = (r < L) ? gate_log2(GK, x[it][e], dt[e], expA, lower_bound) : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          // rows >= L were loaded as zeros, so the activation is finite there; select, no branch
+          const float a = gate_log2(GK, x[it][e], dt[e], expA, lower_bound);
+          la[e] = (r < L) ? a : 0.f;
+        }
         *reinterpret_cast<f32x4_t *>(sB + r * TL::LDB + c) = la;
       }
     }
@@ -220,7 +231,10 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
       for (int v = 0; v < NVW; ++v) uv[i][v] = uv[i][v] - p1[i][v];
     causal_times<Tin, C, NVW>(o, sAqk, uv);
     state_update<Tin, C, D, NVW>(hs, sKT, TL::LDKT, uv, sDecay);
-    store_strip<Tin, NC, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, L, o);
+    // o through the (now unused) cumsum tile, then 16-byte row stores
+    stage_strip<NC, NVW>(sB, LDB, col0, o);
+    __syncthreads();
+    store_rows_from_f32<Tin, NT, C, D>(reinterpret_cast<Tin *>(p.o) + off, ld, sB, LDB, L);
     __syncthreads();
   }
   if (p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, D, col0, D, hs);

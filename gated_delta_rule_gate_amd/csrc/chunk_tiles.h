@@ -581,4 +581,47 @@ __device__ __forceinline__ void store_strip(T *g, int64_t ld, int col0, int L, c
       }
 }
 
+// The output strip of one wave (C-layout tiles: rows 16i.., columns col0 +
+// 16v..) into an fp32 staging tile of row stride lds.
+template <int NC, int NVW>
+__device__ __forceinline__ void stage_strip(float *s, int lds, int col0, const f32x4_t (&x)[NC][NVW]) {
+  const int lane = tid_opaque() & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+#pragma unroll
+    for (int v = 0; v < NVW; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[(16 * i + 4 * grp + e) * lds + col0 + 16 * v + n16] = x[i][v][e];
+}
+
+// Rows [0, L) of an fp32 staging tile [C][D] to global rows of type T with
+// 16-byte stores (all NT threads; a thread converts 16 / sizeof(T) adjacent
+// elements of one row).
+template <typename T, int NT, int C, int D>
+__device__ __forceinline__ void store_rows_from_f32(T *g, int64_t ldg, const float *s, int lds, int L) {
+  constexpr int EPV = 16 / (int)sizeof(T), VPR = D / EPV, NV = C * VPR;
+  static_assert(NV % NT == 0, "tile");
+#pragma unroll
+  for (int it = 0; it < NV / NT; ++it) {
+    const unsigned idx = it * NT + (unsigned)tid_opaque();
+    const int r = idx / VPR, c = (idx % VPR) * EPV;
+    if (r < L) {
+      if constexpr (EPV == 8) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(s + r * lds + c);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t *>(s + r * lds + c + 4);
+        bf16x8_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = static_cast<bf16_t>(a[e]);
+          o[e + 4] = static_cast<bf16_t>(b[e]);
+        }
+        *reinterpret_cast<bf16x8_t *>(g + (int64_t)r * ldg + c) = o;
+      } else {
+        *reinterpret_cast<f32x4_t *>(g + (int64_t)r * ldg + c) = *reinterpret_cast<const f32x4_t *>(s + r * lds + c);
+      }
+    }
+  }
+}
+
 }  // namespace kda

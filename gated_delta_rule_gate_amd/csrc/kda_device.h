@@ -66,15 +66,22 @@ __device__ __forceinline__ float log1p_pos(float x) {
 __device__ __forceinline__ float gate_log2(int kind, float x, float dt, float expA, float lower_bound) {
   if (kind == kGateLog2 || kind == kGateLog2Cumsum) return x;
   if (kind == kGateLogE) return x * kLog2e;
-  float z = x + dt;
+  // the coefficients depend on per-head values only, so loops hoist them
+  const float z = x + dt;
   if (kind == kGateSafe) {
-    float a = expA * z;
-    float sig = fast_rcp(1.0f + fast_exp2(-a * kLog2e));
-    return lower_bound * sig * kLog2e;
+    const float c1 = -expA * kLog2e, c2 = lower_bound * kLog2e;
+    return c2 * fast_rcp(1.0f + fast_exp2(z * c1));
   }
-  float sp = fmaxf(z, 0.0f) + log1p_pos(fast_exp2(-fabsf(z) * kLog2e));
-  return -expA * sp * kLog2e;
+  const float c3 = -expA * kLog2e;
+  const float sp = fmaxf(z, 0.0f) + log1p_pos(fast_exp2(-fabsf(z) * kLog2e));
+  return c3 * sp;
 }
+
+// s_waitcnt vmcnt(0): every vector memory load this wave issued has returned.
+// Used where registers filled by a prefetch issued in an earlier loop
+// iteration are consumed, so the wait never depends on the compiler's
+// tracking of loop-carried loads.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------------------------------------
 // Slot / chunk location for packed (cu_seqlens) and dense batches.
