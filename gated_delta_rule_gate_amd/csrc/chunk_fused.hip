@@ -3,15 +3,27 @@
 // for each chunk entirely on chip. Inputs are read from HBM exactly once and
 // only o and the final state are written; the [D, D] FP32 state lives in MFMA
 // accumulator registers for the whole sequence (each of the NT/64 waves owns
-// a 16*NVW-column strip of it).
+// a 16*NVW-column strip of it). bf16 inputs only (fp32 inputs run the staged
+// schedule).
 //
 // The next chunk's raw inputs are loaded into registers while the current
 // chunk computes, so HBM latency overlaps the on-chip work.
 //
-// LDS per chunk (bf16, C = 64, D = 128: about 144 KB):
-//   q (-> q~ in place), k, v (-> w after the WY step), gate (-> b), A_kk and
-//   T (-> k~^T after the WY step), A_qk, beta, b_L, 2^b_L, dt_bias.
-#include "chunk_tiles.h"
+// Per chunk:
+//   store   raw q, k, v and the activated gate to LDS
+//   (1)     chunk-local cumsum of the gate (b), 2^b_L
+//   (2)     grams A_kk, A_qk (fp32 in LDS)
+//   (3)     one wave inverts the four 16x16 diagonal blocks of I + A_kk while
+//           the others form q~ = scale q 2^b, X_w = beta k 2^b and k~ = k 2^(b_L-b)
+//   (4)     each wave solves its 16-column tiles of w and u by blocked
+//           forward substitution; w goes to LDS transposed, u stays in registers
+//   (5)+(6) v_new = u - w h, o = q~ h + A_qk v_new, h <- 2^b_L h + k~^T v_new
+//   o       staged in LDS, written with 16-byte row stores
+//
+// LDS (C = 64, D = 128: about 142 KB): q (-> q~), k (-> X_w), v, gate (-> b
+// -> w^T), A_kk, k~, A_qk, the diagonal inverses, beta, b_L, 2^b_L, dt_bias;
+// o is staged over the k and v tiles.
+#include "chunk_fused_tiles.h"
 #include "kda_launch.h"
 
 // Threads per workgroup of the fused kernel (0: 512 when the state has at
@@ -22,28 +34,31 @@
 
 namespace kda {
 
-template <typename Tin, int C, int D, int NT>
+template <int C, int D, int NT>
 struct FusedSmem {
-  using TL = Tile<Tin, C, D>;
-  static constexpr size_t tin_tile = sizeof(Tin) * C * TL::LDT;
+  using TL = Tile<bf16_t, C, D>;
+  static constexpr int LDT = TL::LDT;   // q, k, v, k~ [C][LDT] bf16
+  static constexpr int LDB = TL::LDB;   // gate / b [C][LDB] fp32; o staging [C][LDB] fp32
+  static constexpr int LDA = TL::LDA;   // A_kk, A_qk [C][LDA] fp32
+  static constexpr int LDW = C + 8;     // w^T [D][LDW] bf16
+  static constexpr int LDTD = 16 + 8;   // diagonal inverses [C][LDTD] bf16
+  static constexpr size_t tile = 2 * C * LDT;
   static constexpr size_t q = 0;
-  static constexpr size_t k = q + tin_tile;
-  static constexpr size_t v = k + tin_tile;
-  static constexpr size_t b = v + tin_tile;
-  static constexpr size_t akk = b + sizeof(float) * C * TL::LDB;
-  static constexpr size_t t = akk + sizeof(float) * C * TL::LDA;
-  static constexpr size_t aqk = t + sizeof(float) * C * TL::LDA;
-  static constexpr size_t beta = aqk + sizeof(float) * C * TL::LDA;
-  static constexpr size_t bl = beta + sizeof(float) * C;
-  static constexpr size_t decay = bl + sizeof(float) * D;
-  static constexpr size_t dt = decay + sizeof(float) * D;
-  static constexpr size_t seg = dt + sizeof(float) * D;
-  static constexpr size_t end = seg + sizeof(float) * NT;
-  // k~^T [D][C] reuses the A_kk + T region once the WY step has consumed T, when it fits
-  static constexpr size_t kt_bytes = sizeof(Tin) * D * TL::LDKT;
-  static constexpr bool kt_alias = kt_bytes <= 2 * sizeof(float) * C * TL::LDA;
-  static constexpr size_t kt = kt_alias ? akk : end;
-  static constexpr size_t total = kt_alias ? end : end + kt_bytes;
+  static constexpr size_t k = q + tile;
+  static constexpr size_t v = k + tile;
+  static constexpr size_t b = v + tile;
+  static constexpr size_t akk = b + 4 * C * LDB;
+  static constexpr size_t kt = akk + 4 * C * LDA;
+  static constexpr size_t aqk = kt + tile;
+  static constexpr size_t td = aqk + 4 * C * LDA;
+  static constexpr size_t beta = td + 2 * C * LDTD;
+  static constexpr size_t bl = beta + 4 * C;
+  static constexpr size_t decay = bl + 4 * D;
+  static constexpr size_t dt = decay + 4 * D;
+  static constexpr size_t seg = dt + 4 * D;
+  static constexpr size_t total = seg + 4 * NT;
+  static_assert(2 * tile >= 4 * C * LDB, "o staging over the k and v tiles");
+  static_assert(4 * C * LDB >= 2 * D * LDW, "w^T over the b tile");
 };
 
 // One chunk's raw inputs held in registers between the HBM load and the LDS store.
@@ -125,25 +140,27 @@ struct ChunkRegs {
   }
 };
 
-template <typename Tin, int C, int D, int NT, int GK>
+template <int C, int D, int NT, int GK>
 __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
+  using Tin = bf16_t;
   using TL = Tile<Tin, C, D>;
-  using S = FusedSmem<Tin, C, D, NT>;
+  using S = FusedSmem<C, D, NT>;
   constexpr bool SAFE = (GK == kGateSafe);
-  constexpr int NW = NT / 64, NC = TL::NC, DT = TL::DT, LDT = TL::LDT, LDB = TL::LDB;
-  constexpr int NVW = DT / NW;  // value tiles per wave
-  constexpr int NWT = DT / NW;  // w column tiles per wave
+  constexpr int NW = NT / 64, NC = TL::NC, DT = TL::DT, LDT = TL::LDT, LDB = TL::LDB, LDA = TL::LDA;
+  constexpr int NVW = DT / NW;  // value tiles (and w column tiles) per wave
   static_assert(DT % NW == 0 && NVW >= 1, "strip split");
 
   extern __shared__ __align__(16) char smem[];
-  Tin *sQ = reinterpret_cast<Tin *>(smem + S::q);
-  Tin *sK = reinterpret_cast<Tin *>(smem + S::k);
-  Tin *sV = reinterpret_cast<Tin *>(smem + S::v);  // v, then w
-  float *sB = reinterpret_cast<float *>(smem + S::b);
+  Tin *sQ = reinterpret_cast<Tin *>(smem + S::q);    // q, then q~
+  Tin *sK = reinterpret_cast<Tin *>(smem + S::k);    // k, then beta k 2^b
+  Tin *sV = reinterpret_cast<Tin *>(smem + S::v);
+  float *sB = reinterpret_cast<float *>(smem + S::b);  // gate, then b
+  Tin *sWT = reinterpret_cast<Tin *>(smem + S::b);     // w^T once b is consumed
+  float *sO = reinterpret_cast<float *>(smem + S::k);  // o staging over k and v
   float *sAkk = reinterpret_cast<float *>(smem + S::akk);
-  float *sT = reinterpret_cast<float *>(smem + S::t);
-  Tin *sKT = reinterpret_cast<Tin *>(smem + S::kt);
+  Tin *sKt = reinterpret_cast<Tin *>(smem + S::kt);
   float *sAqk = reinterpret_cast<float *>(smem + S::aqk);
+  Tin *sTd = reinterpret_cast<Tin *>(smem + S::td);
   float *sBeta = reinterpret_cast<float *>(smem + S::beta);
   float *sBL = reinterpret_cast<float *>(smem + S::bl);
   float *sDecay = reinterpret_cast<float *>(smem + S::decay);
@@ -152,8 +169,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
 
   const int nh = blockIdx.x;
   const int n = nh / p.H, h = nh % p.H;
-  const int lane = tid_opaque() & 63, wid = tid_opaque() >> 6;
-  const int n16 = lane & 15, grp = lane >> 4;
+  const int wid = tid_opaque() >> 6;
   const int col0 = wid * NVW * 16;
   const SlotRange sr = slot_range(p.cu, n, p.T);
   const int nch = (sr.len + C - 1) / C;
@@ -189,31 +205,23 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     else gate_cumsum<NT, C, D>(sB, LDB, sBL, sSeg);
     for (int i = tid_opaque(); i < D; i += NT) sDecay[i] = fast_exp2(sBL[i]);
     // (2)
-    grams<Tin, NT, C, D, SAFE>(sQ, sK, sB, sBeta, p.scale, sAkk, sAqk, TL::LDA, L, C);
+    grams<Tin, NT, C, D, SAFE>(sQ, sK, sB, sBeta, p.scale, sAkk, sAqk, LDA, L, C);
     __syncthreads();
-    // (3)
-    solve<NT, C>(sAkk, sT);
-    // (4) w column tiles wid + NW*j; u on this wave's own value strip
-    f32x4_t wacc[NC][NWT], uv[NC][NVW];
-#pragma unroll
-    for (int j = 0; j < NWT; ++j)
-      tri_mm<Tin, C, NWT>(sT, wid + NW * j, wacc, j, [&](int r, int col) {
-        return sBeta[r] * to_f32(sK[r * LDT + col]) * fast_exp2(sB[r * LDB + col]);
-      });
-#pragma unroll
-    for (int v = 0; v < NVW; ++v)
-      tri_mm<Tin, C, NVW>(sT, wid * NVW + v, uv, v, [&](int r, int col) { return sBeta[r] * to_f32(sV[r * LDT + col]); });
+    // (3) diagonal inverses on the last wave; operand tiles on the others
+    if (wid == NW - 1) diag_inverse<C>(sAkk, LDA, sTd, S::LDTD);
+    else operand_pass<C, D>(sQ, sK, sKt, LDT, sB, LDB, sBL, sBeta, p.scale, NT - 64);
     __syncthreads();
-    // w -> the v tile, q~ in place, k~^T over A_kk/T
+    // (4) this wave's column tiles of w (channels) and u (values)
+    f32x4_t uv[NC][NVW];
 #pragma unroll
-    for (int j = 0; j < NWT; ++j)
+    for (int v = 0; v < NVW; ++v) {
+      f32x4_t W[NC], U[NC];
+      wy_subst<C>(sK, LDT, wid * NVW + v, nullptr, sAkk, LDA, sTd, S::LDTD, W);
+      wy_subst<C>(sV, LDT, wid * NVW + v, sBeta, sAkk, LDA, sTd, S::LDTD, U);
+      store_wT<C>(sWT, S::LDW, wid * NVW + v, W);
 #pragma unroll
-      for (int i = 0; i < NC; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sV[(16 * i + 4 * grp + e) * LDT + 16 * (wid + NW * j) + n16] = from_f32<Tin>(wacc[i][j][e]);
-    make_qtilde<Tin, NT, C, D>(sQ, sB, p.scale);
-    make_ktilde_t<Tin, NT, C, D>(sKT, sK, sB, sBL);
+      for (int i = 0; i < NC; ++i) uv[i][v] = U[i];
+    }
     __syncthreads();
     // (5) + (6)
     f32x4_t p1[NC][NVW], o[NC][NVW];
@@ -224,33 +232,30 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
         p1[i][v] = zero4();
         o[i][v] = zero4();
       }
-    rows_times_state<Tin, C, D, NVW, true>(p1, o, sV, sQ, hs);
+    wq_times_state<C, D, NVW>(p1, o, sWT, S::LDW, sQ, LDT, hs);
 #pragma unroll
     for (int i = 0; i < NC; ++i)
 #pragma unroll
       for (int v = 0; v < NVW; ++v) uv[i][v] = uv[i][v] - p1[i][v];
     causal_times<Tin, C, NVW>(o, sAqk, uv);
-    state_update<Tin, C, D, NVW>(hs, sKT, TL::LDKT, uv, sDecay);
-    // o through the (now unused) cumsum tile, then 16-byte row stores
-    stage_strip<NC, NVW>(sB, LDB, col0, o);
+    state_update_kt<C, D, NVW>(hs, sKt, LDT, uv, sDecay);
+    // o through the (now unused) k and v tiles, then 16-byte row stores
+    stage_strip<NC, NVW>(sO, LDB, col0, o);
     __syncthreads();
-    store_rows_from_f32<Tin, NT, C, D>(reinterpret_cast<Tin *>(p.o) + off, ld, sB, LDB, L);
+    store_rows_from_f32<Tin, NT, C, D>(reinterpret_cast<Tin *>(p.o) + off, ld, sO, LDB, L);
     __syncthreads();
   }
   if (p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, D, col0, D, hs);
 }
 
-bool fused_supported(const ChunkParams &p) {
-  if (p.is_bf16) return p.D == 64 || p.D == 128;
-  return p.D == 64;
-}
+bool fused_supported(const ChunkParams &p) { return p.is_bf16 && (p.D == 64 || p.D == 128); }
 
 namespace {
 
-template <typename Tin, int C, int D, int NT, int GK>
+template <int C, int D, int NT, int GK>
 hipError_t launch_fused_g(const ChunkParams &p, hipStream_t st) {
-  const size_t smem = FusedSmem<Tin, C, D, NT>::total;
-  auto kern = fused_chunk_kernel<Tin, C, D, NT, GK>;
+  const size_t smem = FusedSmem<C, D, NT>::total;
+  auto kern = fused_chunk_kernel<C, D, NT, GK>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)smem);
   if (e != hipSuccess) {
@@ -261,15 +266,15 @@ hipError_t launch_fused_g(const ChunkParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename Tin, int C, int D>
+template <int C, int D>
 hipError_t launch_fused_t(const ChunkParams &p, hipStream_t st) {
   constexpr int NT = (KDA_FUSED_THREADS > 0) ? KDA_FUSED_THREADS : ((D / 16 >= 8) ? 512 : 256);
   if (p.N * p.H == 0) return hipSuccess;
   switch (p.gate_kind) {
-    case kGateSafe: return launch_fused_g<Tin, C, D, NT, kGateSafe>(p, st);
-    case kGateSoftplus: return launch_fused_g<Tin, C, D, NT, kGateSoftplus>(p, st);
-    case kGateLogE: return launch_fused_g<Tin, C, D, NT, kGateLogE>(p, st);
-    case kGateLog2Cumsum: return launch_fused_g<Tin, C, D, NT, kGateLog2Cumsum>(p, st);
+    case kGateSafe: return launch_fused_g<C, D, NT, kGateSafe>(p, st);
+    case kGateSoftplus: return launch_fused_g<C, D, NT, kGateSoftplus>(p, st);
+    case kGateLogE: return launch_fused_g<C, D, NT, kGateLogE>(p, st);
+    case kGateLog2Cumsum: return launch_fused_g<C, D, NT, kGateLog2Cumsum>(p, st);
   }
   return hipErrorInvalidValue;
 }
@@ -277,15 +282,11 @@ hipError_t launch_fused_t(const ChunkParams &p, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_fused(const ChunkParams &p, hipStream_t st) {
-  if (p.is_bf16) {
-    if (p.C == 64 && p.D == 128) return launch_fused_t<bf16_t, 64, 128>(p, st);
-    if (p.C == 64 && p.D == 64) return launch_fused_t<bf16_t, 64, 64>(p, st);
-    if (p.C == 32 && p.D == 128) return launch_fused_t<bf16_t, 32, 128>(p, st);
-    if (p.C == 32 && p.D == 64) return launch_fused_t<bf16_t, 32, 64>(p, st);
-  } else {
-    if (p.C == 64 && p.D == 64) return launch_fused_t<float, 64, 64>(p, st);
-    if (p.C == 32 && p.D == 64) return launch_fused_t<float, 32, 64>(p, st);
-  }
+  if (!p.is_bf16) return hipErrorInvalidValue;
+  if (p.C == 64 && p.D == 128) return launch_fused_t<64, 128>(p, st);
+  if (p.C == 64 && p.D == 64) return launch_fused_t<64, 64>(p, st);
+  if (p.C == 32 && p.D == 128) return launch_fused_t<32, 128>(p, st);
+  if (p.C == 32 && p.D == 64) return launch_fused_t<32, 64>(p, st);
   return hipErrorInvalidValue;
 }
 

@@ -65,12 +65,23 @@ def oracle_pairs(d, gate, pairs):
 SCHEDULES = ["fused", "staged"]
 
 
+def expect_fused_unsupported(d, cu=None):
+    from gated_delta_rule_gate_amd import KdaError
+
+    with pytest.raises(KdaError, match="UNSUPPORTED"):
+        gpu_run(d, "safe", "fused", cu=cu)
+
+
 @pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("C", [64, 32])
 def test_fp32_small_config(schedule, C):
-    """fp32, B1 T256 H2 K=V=64, safe gate, h0 = 0, final state returned."""
+    """fp32, B1 T256 H2 K=V=64, safe gate, h0 = 0, final state returned (the fused
+    kernel takes bf16 only: fp32 runs the staged schedule, also under "auto")."""
     need_gpu()
     d = make(1, 256, 2, 64, torch.float32, 1000, with_h0=False)
+    if schedule == "fused":
+        expect_fused_unsupported(d)
+        schedule = "auto"
     o, ht = gpu_run(d, "safe", schedule, C=C)
     o_ref, ht_ref = oracle_run(d, "safe")
     parity(o, o_ref, "fp32", "o")
@@ -118,6 +129,9 @@ def test_packed_empty_slots_tail(schedule, dtype):
     cap = int(cu[-1]) + 37
     D = 64 if dtype == torch.float32 else 128
     d = make(1, cap, 2, D, dtype, 400, gate="safe", n_slots=len(lens))
+    if schedule == "fused" and dtype == torch.float32:
+        expect_fused_unsupported(d, cu)
+        schedule = "auto"
     end = int(cu[-1])
     for key in ("q", "k", "v", "g"):
         d[key][:, end:] = float("nan")
@@ -169,16 +183,17 @@ def test_recurrent_chunk_cross_check():
     need_gpu()
     from gated_delta_rule_gate_amd import recurrent_kda
 
-    d = make(2, 130, 2, 64, torch.float32, 700)
-    g = oracle.gate(oracle.GATE_SAFE, f64(d["x"]), f64(d["A_log"]), f64(d["dt_bias"]), -5.0)
-    d["g"] = torch.from_numpy(g.astype(np.float32))
-    oc, hc = gpu_run(d, "loge", "fused")
-    dd = {k: (v.cuda() if v is not None else None) for k, v in d.items()}
-    orr, hr = recurrent_kda(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["h0"], output_final_state=True,
-                            gate_kind="loge")
-    torch.cuda.synchronize()
-    parity(oc, orr.cpu().numpy(), "fp32", "o chunk vs recurrent")
-    parity(hc, hr.cpu().numpy(), "fp32", "ht chunk vs recurrent")
+    for dtype, D, schedule, name in ((torch.float32, 64, "auto", "fp32"), (torch.bfloat16, 128, "fused", "bf16")):
+        d = make(2, 130, 2, D, dtype, 700)
+        g = oracle.gate(oracle.GATE_SAFE, f64(d["x"]), f64(d["A_log"]), f64(d["dt_bias"]), -5.0)
+        d["g"] = torch.from_numpy(g.astype(np.float32))
+        oc, hc = gpu_run(d, "loge", schedule)
+        dd = {k: (v.cuda() if v is not None else None) for k, v in d.items()}
+        orr, hr = recurrent_kda(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["h0"], output_final_state=True,
+                                gate_kind="loge")
+        torch.cuda.synchronize()
+        parity(oc, orr.float().cpu().numpy(), name, "o chunk vs recurrent")
+        parity(hc, hr.cpu().numpy(), name, "ht chunk vs recurrent")
 
 
 def test_config_b4_t2048_h16_full():
