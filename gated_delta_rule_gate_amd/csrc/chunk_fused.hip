@@ -169,7 +169,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
 
   const int nh = blockIdx.x;
   const int n = nh / p.H, h = nh % p.H;
-  const int wid = tid_opaque() >> 6;
+  const int wid = wave_id();
   const int col0 = wid * NVW * 16;
   const SlotRange sr = slot_range(p.cu, n, p.T);
   const int nch = (sr.len + C - 1) / C;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     else gate_cumsum<NT, C, D>(sB, LDB, sBL, sSeg);
     for (int i = tid_opaque(); i < D; i += NT) sDecay[i] = fast_exp2(sBL[i]);
     // (2)
-    grams<Tin, NT, C, D, SAFE>(sQ, sK, sB, sBeta, p.scale, sAkk, sAqk, LDA, L, C);
+    grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, L);
     __syncthreads();
     // (3) diagonal inverses on the last wave; operand tiles on the others
     if (wid == NW - 1) diag_inverse<C>(sAkk, LDA, sTd, S::LDTD);

@@ -247,3 +247,192 @@ __device__ __forceinline__ void state_update_kt(f32x4_t (&h)[D / 16][NVW], const
 }
 
 }  // namespace kda
+
+namespace kda {
+
+// ---------------------------------------------------------------------------------------------
+// (2) grams for the fused kernel. Each wave owns one row block i of both grams
+// and a 1/HS share of the channels (HS = 1 or 2 waves per row block): it builds
+// the row operands of block i once -- q, k scaled by 2^(b_r - m_i) (midpoint
+// anchor, diagonal block) and by 2^(b_r - a_i) (first-row anchor a_i,
+// off-diagonal blocks) -- and the column operands k_s 2^(m_i - b_s)
+// (diagonal) and k_s 2^(a_i - b_s) (blocks j < i), so every exponent is a
+// midpoint or paired non-positive offset ("FLA KDA Skill", section "Safe gate
+// numerical note"). Non-safe gates take the diagonal block per pair (section
+// "Safe vs non-safe intra path"). Only causal blocks are formed ("[examples]
+// Read only the causal columns in chunk_fwd_A_diag_anchored", description).
+// With HS = 2 the second channel half stores its scaled, masked partial sums,
+// and after a barrier the first half adds its own and writes the result.
+// ---------------------------------------------------------------------------------------------
+template <int I, int NC, int NS, bool SAFE>
+__device__ __forceinline__ void gram_row_partial(const bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB,
+                                                 int ldb, int c0, f32x4_t (&accQ)[NC], f32x4_t (&accK)[NC]) {
+  using M = Mma<bf16_t>;
+  const int lane = tid_opaque() & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+  const int rr = 16 * I + n16;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int kb = c0 + 32 * s + 4 * grp;  // slots e < 4: channel kb + e; e >= 4: kb + 16 + (e - 4)
+    f32x4_t br[2], bm[2], ba[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      br[hh] = *reinterpret_cast<const f32x4_t *>(sB + rr * ldb + kb + 16 * hh);
+      bm[hh] = *reinterpret_cast<const f32x4_t *>(sB + (16 * I + 8) * ldb + kb + 16 * hh);
+      ba[hh] = *reinterpret_cast<const f32x4_t *>(sB + (16 * I) * ldb + kb + 16 * hh);
+    }
+    const bf16x4_t q0 = *reinterpret_cast<const bf16x4_t *>(sQ + rr * ldt + kb);
+    const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t *>(sQ + rr * ldt + kb + 16);
+    const bf16x4_t k0 = *reinterpret_cast<const bf16x4_t *>(sK + rr * ldt + kb);
+    const bf16x4_t k1 = *reinterpret_cast<const bf16x4_t *>(sK + rr * ldt + kb + 16);
+    bf16x8_t fqd, fkd, fqo, fko;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int hh = e >> 2, ee = e & 3;
+      const float qf = static_cast<float>(hh ? q1[ee] : q0[ee]);
+      const float kf = static_cast<float>(hh ? k1[ee] : k0[ee]);
+      if (SAFE) {
+        const float ed = fast_exp2(br[hh][ee] - bm[hh][ee]);
+        fqd[e] = static_cast<bf16_t>(qf * ed);
+        fkd[e] = static_cast<bf16_t>(kf * ed);
+      }
+      if (I > 0) {
+        const float eo = fast_exp2(br[hh][ee] - ba[hh][ee]);
+        fqo[e] = static_cast<bf16_t>(qf * eo);
+        fko[e] = static_cast<bf16_t>(kf * eo);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j <= I; ++j) {
+      if (!SAFE && j == I) continue;
+      const int cs = 16 * j + n16;
+      const bf16x4_t c0v = *reinterpret_cast<const bf16x4_t *>(sK + cs * ldt + kb);
+      const bf16x4_t c1v = *reinterpret_cast<const bf16x4_t *>(sK + cs * ldt + kb + 16);
+      bf16x8_t fc;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4_t bc = *reinterpret_cast<const f32x4_t *>(sB + cs * ldb + kb + 16 * hh);
+        const f32x4_t anc = (j == I) ? bm[hh] : ba[hh];
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) {
+          const float kf = static_cast<float>(hh ? c1v[ee] : c0v[ee]);
+          fc[4 * hh + ee] = static_cast<bf16_t>(kf * fast_exp2(anc[ee] - bc[ee]));
+        }
+      }
+      // column operand first: the accumulator holds the block transposed, so
+      // lane (row n16, group g) gets A[16I + n16][16j + 4g .. 16j + 4g + 3]
+      if (j == I) {
+        accQ[j] = M::mma(fc, fqd, accQ[j]);
+        accK[j] = M::mma(fc, fkd, accK[j]);
+      } else {
+        accQ[j] = M::mma(fc, fqo, accQ[j]);
+        accK[j] = M::mma(fc, fko, accK[j]);
+      }
+    }
+  }
+}
+
+template <int NT, int C, int D, bool SAFE>
+__device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
+                                            const float *sBeta, float scale, float *sAkk, float *sAqk, int lda,
+                                            int L) {
+  constexpr int NW = NT / 64, NC = C / 16;
+  constexpr int HS = (NW / NC >= 2) ? 2 : 1, CW = D / HS, NS = CW / 32;
+  static_assert(NW >= NC && CW % 32 == 0, "wave split of the grams");
+  const int lane = tid_opaque() & 63, w = wave_id();
+  const int n16 = lane & 15, grp = lane >> 4;
+  // row block per wave; with 8 waves and 4 row blocks, blocks 0 and 3 (and 1
+  // and 2) share a SIMD (waves w and w + 4), which evens out the per-SIMD work
+  int i, hsel;
+  if constexpr (NW == 8 && NC == 4) {
+    i = (w < 4) ? (w >> 1) : (3 - ((w - 4) >> 1));
+    hsel = w & 1;
+  } else {
+    i = w / HS;
+    hsel = w % HS;
+  }
+  const bool active = i < NC;
+  const int c0 = hsel * CW;
+
+  f32x4_t accQ[NC], accK[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    accQ[j] = zero4();
+    accK[j] = zero4();
+  }
+  if (active) {
+    switch (i) {
+      case 0: gram_row_partial<0, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, accQ, accK); break;
+      case 1: gram_row_partial<1, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, accQ, accK); break;
+      case 2:
+        if constexpr (NC > 2) gram_row_partial<2, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, accQ, accK);
+        break;
+      case 3:
+        if constexpr (NC > 3) gram_row_partial<3, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, accQ, accK);
+        break;
+    }
+    if constexpr (!SAFE) {
+      // token-parallel diagonal block over this wave's channels, in the same
+      // transposed layout: lane owns row r = 16i + n16 and columns 16i + 4*grp + e
+      const int r = 16 * i + n16;
+      for (int kk = c0; kk < c0 + CW; ++kk) {
+        const float qr = static_cast<float>(sQ[r * ldt + kk]);
+        const float kr = static_cast<float>(sK[r * ldt + kk]);
+        const float br = sB[r * ldb + kk];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sc = 16 * i + 4 * grp + e;
+          const float f = (r >= sc) ? fast_exp2(br - sB[sc * ldb + kk]) : 0.f;
+          const float kf = static_cast<float>(sK[sc * ldt + kk]) * f;
+          accQ[i][e] += qr * kf;
+          accK[i][e] += kr * kf;
+        }
+      }
+    }
+  }
+  // scale, beta and masks, then one 16-byte store per block: lane holds
+  // A[r = 16i + n16][16j + 4g .. 16j + 4g + 3]. With two channel halves the
+  // second stores first and the first adds its own after a barrier.
+  const int r = 16 * i + n16;
+  const float beta_r = active ? sBeta[r] : 0.f;
+  auto finish = [&](bool add) {
+    f32x4_t prev[NC][2];
+    if (add) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        if (j > i) continue;
+        prev[j][0] = *reinterpret_cast<const f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp);
+        prev[j][1] = *reinterpret_cast<const f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      if (j > i) continue;
+      f32x4_t aq, ak;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int sj = 16 * j + 4 * grp + e;
+        aq[e] = (sj <= r && r < L) ? scale * accQ[j][e] : 0.f;
+        ak[e] = (sj < r && r < L) ? beta_r * accK[j][e] : 0.f;
+      }
+      if (add) {
+        aq = aq + prev[j][0];
+        ak = ak + prev[j][1];
+      }
+      *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp) = aq;
+      *reinterpret_cast<f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp) = ak;
+    }
+    // the product with A_qk reads 32 columns at a time: zero the block right of
+    // an even diagonal block
+    if ((i & 1) == 0 && i + 1 < NC) *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * (i + 1) + 4 * grp) = zero4();
+  };
+  if constexpr (HS == 2) {
+    if (active && hsel == 1) finish(false);
+    __syncthreads();
+    if (active && hsel == 0) finish(true);
+  } else {
+    if (active) finish(false);
+  }
+}
+
+}  // namespace kda

@@ -222,7 +222,7 @@ __device__ void grams(const Tin *sQ, const Tin *sK, const float *sB, const float
   using TL = Tile<Tin, C, D>;
   constexpr int NW = NT / 64, NC = TL::NC, NB = NC * (NC + 1) / 2;
   constexpr int LDT = TL::LDT, LDB = TL::LDB;
-  const int lane = tid_opaque() & 63, wid = tid_opaque() >> 6;
+  const int lane = tid_opaque() & 63, wid = wave_id();
   const int n16 = lane & 15, grp = lane >> 4;
 
   for (int blk = wid; blk < NB; blk += NW) {
@@ -297,7 +297,7 @@ __device__ void grams(const Tin *sQ, const Tin *sK, const float *sB, const float
 template <int NT, int C>
 __device__ void solve(const float *sAkk, float *sT) {
   constexpr int NW = NT / 64, NC = C / 16, LDA = C + 4;
-  const int lane = tid_opaque() & 63, wid = tid_opaque() >> 6;
+  const int lane = tid_opaque() & 63, wid = wave_id();
   const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int it = 0; it < (C * C + NT - 1) / NT; ++it) {

@@ -42,6 +42,12 @@ __device__ __forceinline__ int tid_opaque() {
   return t;
 }
 
+// The wave's index within the workgroup as a wave-uniform (scalar) value.
+// Branches on it are scalar branches; a branch on a per-lane value would
+// instead run both sides under an EXEC mask, and MFMA instructions do not
+// honour an empty EXEC mask.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(tid_opaque() >> 6); }
+
 // Hardware base-2 exponential / logarithm / reciprocal (v_exp_f32, v_log_f32, v_rcp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
