@@ -75,15 +75,20 @@ struct ChunkRegs {
   // 32-bit unsigned element offset from it, so the loads take the
   // scalar-base + vector-offset form.
   __device__ __forceinline__ void load(const ChunkParams &p, int64_t t0, int L, int h) {
+    load_gate(p, t0, L, h);
+    load_qkv(p, t0, L, h);
+  }
+
+  // q, k, v of the chunk at t0
+  __device__ __forceinline__ void load_qkv(const ChunkParams &p, int64_t t0, int L, int h) {
     const unsigned ld = (unsigned)p.H * D;
     const int64_t base = t0 * (int64_t)ld + (int64_t)h * D;
     const Tin *gq = reinterpret_cast<const Tin *>(p.q) + base;
     const Tin *gk = reinterpret_cast<const Tin *>(p.k) + base;
     const Tin *gv = reinterpret_cast<const Tin *>(p.v) + base;
-    const float *gx = p.g + base;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int idx = it * NT + tid_opaque();
+      const unsigned idx = it * NT + (unsigned)tid_opaque();
       const int r = idx / VPR, c = (idx % VPR) * EPV;
       const bool ok = (NVT % NT == 0 || idx < NVT) && r < L;
       const unsigned off = (unsigned)r * ld + (unsigned)c;
@@ -92,9 +97,16 @@ struct ChunkRegs {
       k[it] = ok ? *reinterpret_cast<const u32x4_t *>(gk + off) : z;
       v[it] = ok ? *reinterpret_cast<const u32x4_t *>(gv + off) : z;
     }
+  }
+
+  // gate input and beta of the chunk at t0
+  __device__ __forceinline__ void load_gate(const ChunkParams &p, int64_t t0, int L, int h) {
+    const unsigned ld = (unsigned)p.H * D;
+    const int64_t base = t0 * (int64_t)ld + (int64_t)h * D;
+    const float *gx = p.g + base;
 #pragma unroll
     for (int it = 0; it < IX; ++it) {
-      const int idx = it * NT + tid_opaque();
+      const unsigned idx = it * NT + (unsigned)tid_opaque();
       const int r = idx / XPR, c = (idx % XPR) * 4;
       const bool ok = (NVX % NT == 0 || idx < NVX) && r < L;
       const unsigned off = (unsigned)r * ld + (unsigned)c;
@@ -198,7 +210,10 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     const int64_t off = t0 * ld + h * D;
     regs.template store<GK>(sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound);
     __syncthreads();
-    if (c + 1 < nch) regs.load(p, t0 + C, min(C, sr.len - (c + 1) * C), h);  // in flight during this chunk
+    // the next chunk's inputs are loaded in two parts while this chunk computes
+    const bool more = c + 1 < nch;
+    const int Ln = more ? min(C, sr.len - (c + 1) * C) : 0;
+    if (more) regs.load_gate(p, t0 + C, Ln, h);
 
     // (1)
     if constexpr (GK == kGateLog2Cumsum) gate_pad<NT, C, D>(sB, LDB, sBL, L);
@@ -207,6 +222,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     // (2)
     grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, L);
     __syncthreads();
+    if (more) regs.load_qkv(p, t0 + C, Ln, h);
     // (3) diagonal inverses on the last wave; operand tiles on the others
     if (wid == NW - 1) diag_inverse<C>(sAkk, LDA, sTd, S::LDTD);
     else operand_pass<C, D>(sQ, sK, sKt, LDT, sB, LDB, sBL, sBeta, p.scale, NT - 64);
@@ -216,8 +232,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
 #pragma unroll
     for (int v = 0; v < NVW; ++v) {
       f32x4_t W[NC], U[NC];
-      wy_subst<C>(sK, LDT, wid * NVW + v, nullptr, sAkk, LDA, sTd, S::LDTD, W);
-      wy_subst<C>(sV, LDT, wid * NVW + v, sBeta, sAkk, LDA, sTd, S::LDTD, U);
+      wy_subst2<C>(sK, sV, LDT, wid * NVW + v, sBeta, sAkk, LDA, sTd, S::LDTD, W, U);
       store_wT<C>(sWT, S::LDW, wid * NVW + v, W);
 #pragma unroll
       for (int i = 0; i < NC; ++i) uv[i][v] = U[i];

@@ -132,31 +132,33 @@ __device__ __forceinline__ void operand_pass(bf16_t *sQ, bf16_t *sK, bf16_t *sKt
 }
 
 // ---------------------------------------------------------------------------------------------
-// (4) One 16-column tile ct of W = (I + A_kk)^-1 X by blocked forward
-// substitution: R_i = X_i - sum_{j<i} A_ij W_j, W_i = T_ii R_i. X is a
-// row-major bf16 tile; rows are scaled by rowscale[r] when given. W comes
-// back as C-layout accumulators, one per row block.
+// (4) One 16-column tile ct of W = (I + A_kk)^-1 X for two right-hand sides at
+// once (Xa, and Xb with rows scaled by rowscale[r]), by blocked forward
+// substitution: R_i = X_i - sum_{j<i} A_ij W_j, W_i = T_ii R_i. X tiles are
+// row-major bf16; A_ij and T_ii are read once for both. W comes back as
+// C-layout accumulators, one per row block.
 // ---------------------------------------------------------------------------------------------
 template <int C>
-__device__ __forceinline__ void wy_subst(const bf16_t *sX, int ldx, int ct, const float *rowscale, const float *sAkk,
-                                         int lda, const bf16_t *sTd, int ldt, f32x4_t (&W)[C / 16]) {
+__device__ __forceinline__ void wy_subst2(const bf16_t *sXa, const bf16_t *sXb, int ldx, int ct, const float *rowscale,
+                                          const float *sAkk, int lda, const bf16_t *sTd, int ldt, f32x4_t (&Wa)[C / 16],
+                                          f32x4_t (&Wb)[C / 16]) {
   constexpr int NC = C / 16;
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    f32x4_t R = to_f32x4(load_cfrag(sX, ldx, 16 * i, 16 * ct));
-    if (rowscale) {
-      const f32x4_t rs = *reinterpret_cast<const f32x4_t *>(rowscale + 16 * i + 4 * grp);
-      R = R * rs;
-    }
+    f32x4_t Ra = to_f32x4(load_cfrag(sXa, ldx, 16 * i, 16 * ct));
+    f32x4_t Rb = to_f32x4(load_cfrag(sXb, ldx, 16 * i, 16 * ct));
+    Rb = Rb * *reinterpret_cast<const f32x4_t *>(rowscale + 16 * i + 4 * grp);
 #pragma unroll
     for (int j = 0; j < i; ++j) {
-      const f32x4_t a = *reinterpret_cast<const f32x4_t *>(sAkk + (16 * i + n16) * lda + 16 * j + 4 * grp);
-      R = mma16(to_bf16x4(-a), to_bf16x4(W[j]), R);
+      const bf16x4_t a = to_bf16x4(-*reinterpret_cast<const f32x4_t *>(sAkk + (16 * i + n16) * lda + 16 * j + 4 * grp));
+      Ra = mma16(a, to_bf16x4(Wa[j]), Ra);
+      Rb = mma16(a, to_bf16x4(Wb[j]), Rb);
     }
     const bf16x4_t t = *reinterpret_cast<const bf16x4_t *>(sTd + (16 * i + n16) * ldt + 4 * grp);
-    W[i] = mma16(t, to_bf16x4(R), zero4());
+    Wa[i] = mma16(t, to_bf16x4(Ra), zero4());
+    Wb[i] = mma16(t, to_bf16x4(Rb), zero4());
   }
 }
 
@@ -332,6 +334,50 @@ __device__ __forceinline__ void gram_row_partial(const bf16_t *sQ, const bf16_t 
   }
 }
 
+// Scale, beta and masks of row block I, then one 16-byte store per block:
+// lane holds A[r = 16I + n16][16j + 4g .. 16j + 4g + 3]. With add, the values
+// already in LDS (the other channel half) are added first.
+template <int I, int NC>
+__device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)[NC], bool add, int r, int L,
+                                            float scale, float beta_r, float *sAkk, float *sAqk, int lda) {
+  const int grp = (tid_opaque() & 63) >> 4;
+  f32x4_t prev[I + 1][2];
+  if (add) {
+#pragma unroll
+    for (int j = 0; j <= I; ++j) {
+      prev[j][0] = *reinterpret_cast<const f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp);
+      prev[j][1] = *reinterpret_cast<const f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp);
+    }
+  }
+  const bool row_ok = r < L;
+#pragma unroll
+  for (int j = 0; j <= I; ++j) {
+    f32x4_t aq = accQ[j] * scale, ak = accK[j] * beta_r;
+    if (j == I) {  // diagonal block: causal masks inside the block
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int sj = 16 * j + 4 * grp + e;
+        aq[e] = (sj <= r) ? aq[e] : 0.f;
+        ak[e] = (sj < r) ? ak[e] : 0.f;
+      }
+    }
+    if (!row_ok) {
+      aq = zero4();
+      ak = zero4();
+    }
+    if (add) {
+      aq = aq + prev[j][0];
+      ak = ak + prev[j][1];
+    }
+    *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp) = aq;
+    *reinterpret_cast<f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp) = ak;
+  }
+  // the product with A_qk reads 32 columns at a time: zero the block right of
+  // an even diagonal block
+  if constexpr ((I & 1) == 0 && I + 1 < NC)
+    *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * (I + 1) + 4 * grp) = zero4();
+}
+
 template <int NT, int C, int D, bool SAFE>
 __device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                             const float *sBeta, float scale, float *sAkk, float *sAqk, int lda,
@@ -390,41 +436,19 @@ __device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, 
       }
     }
   }
-  // scale, beta and masks, then one 16-byte store per block: lane holds
-  // A[r = 16i + n16][16j + 4g .. 16j + 4g + 3]. With two channel halves the
-  // second stores first and the first adds its own after a barrier.
   const int r = 16 * i + n16;
   const float beta_r = active ? sBeta[r] : 0.f;
   auto finish = [&](bool add) {
-    f32x4_t prev[NC][2];
-    if (add) {
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        if (j > i) continue;
-        prev[j][0] = *reinterpret_cast<const f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp);
-        prev[j][1] = *reinterpret_cast<const f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp);
-      }
+    switch (i) {
+      case 0: gram_finish<0, NC>(accQ, accK, add, r, L, scale, beta_r, sAkk, sAqk, lda); break;
+      case 1: gram_finish<1, NC>(accQ, accK, add, r, L, scale, beta_r, sAkk, sAqk, lda); break;
+      case 2:
+        if constexpr (NC > 2) gram_finish<2, NC>(accQ, accK, add, r, L, scale, beta_r, sAkk, sAqk, lda);
+        break;
+      case 3:
+        if constexpr (NC > 3) gram_finish<3, NC>(accQ, accK, add, r, L, scale, beta_r, sAkk, sAqk, lda);
+        break;
     }
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if (j > i) continue;
-      f32x4_t aq, ak;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int sj = 16 * j + 4 * grp + e;
-        aq[e] = (sj <= r && r < L) ? scale * accQ[j][e] : 0.f;
-        ak[e] = (sj < r && r < L) ? beta_r * accK[j][e] : 0.f;
-      }
-      if (add) {
-        aq = aq + prev[j][0];
-        ak = ak + prev[j][1];
-      }
-      *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp) = aq;
-      *reinterpret_cast<f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp) = ak;
-    }
-    // the product with A_qk reads 32 columns at a time: zero the block right of
-    // an even diagonal block
-    if ((i & 1) == 0 && i + 1 < NC) *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * (i + 1) + 4 * grp) = zero4();
   };
   if constexpr (HS == 2) {
     if (active && hsel == 1) finish(false);
