@@ -20,8 +20,9 @@
 //   (5)+(6) v_new = u - w h, o = q~ h + A_qk v_new, h <- 2^b_L h + k~^T v_new
 //   o       staged in LDS, written with 16-byte row stores
 //
-// LDS (C = 64, D = 128: about 142 KB): q (-> q~), k (-> X_w), v, gate (-> b
-// -> w^T), A_kk, k~, A_qk, the diagonal inverses, beta, b_L, 2^b_L, dt_bias;
+// LDS (C = 64, D = 128: about 151 KB): q (-> q~), k (-> X_w), v, gate (-> b
+// -> w^T), A_kk, k~, A_qk (fp32 partial sums and the bf16 result), the
+// diagonal inverses, beta, b_L, 2^b_L, dt_bias;
 // o is staged over the k and v tiles.
 #include "chunk_fused_tiles.h"
 #include "kda_launch.h"
@@ -50,7 +51,9 @@ struct FusedSmem {
   static constexpr size_t akk = b + 4 * C * LDB;
   static constexpr size_t kt = akk + 4 * C * LDA;
   static constexpr size_t aqk = kt + tile;
-  static constexpr size_t td = aqk + 4 * C * LDA;
+  static constexpr int LDAH = C + 8;    // A_qk [C][LDAH] bf16
+  static constexpr size_t aqh = aqk + 4 * C * LDA;
+  static constexpr size_t td = aqh + 2 * C * LDAH;
   static constexpr size_t beta = td + 2 * C * LDTD;
   static constexpr size_t bl = beta + 4 * C;
   static constexpr size_t decay = bl + 4 * D;
@@ -171,7 +174,9 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   float *sO = reinterpret_cast<float *>(smem + S::k);  // o staging over k and v
   float *sAkk = reinterpret_cast<float *>(smem + S::akk);
   Tin *sKt = reinterpret_cast<Tin *>(smem + S::kt);
-  float *sAqk = reinterpret_cast<float *>(smem + S::aqk);
+  float *sAqk = reinterpret_cast<float *>(smem + S::aqk);  // partial sums of A_qk
+  Tin *sAqh = reinterpret_cast<Tin *>(smem + S::aqh);      // A_qk
+
   Tin *sTd = reinterpret_cast<Tin *>(smem + S::td);
   float *sBeta = reinterpret_cast<float *>(smem + S::beta);
   float *sBL = reinterpret_cast<float *>(smem + S::bl);
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     else gate_cumsum<NT, C, D>(sB, LDB, sBL, sSeg);
     for (int i = tid_opaque(); i < D; i += NT) sDecay[i] = fast_exp2(sBL[i]);
     // (2)
-    grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, L);
+    grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L);
     __syncthreads();
     if (more) regs.load_qkv(p, t0 + C, Ln, h);
     // (3) diagonal inverses on the last wave; operand tiles on the others
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     for (int i = 0; i < NC; ++i)
 #pragma unroll
       for (int v = 0; v < NVW; ++v) uv[i][v] = uv[i][v] - p1[i][v];
-    causal_times<Tin, C, NVW>(o, sAqk, uv);
+    causal_times_h<C, NVW>(o, sAqh, S::LDAH, uv);
     state_update_kt<C, D, NVW>(hs, sKt, LDT, uv, sDecay);
     // o through the (now unused) k and v tiles, then 16-byte row stores
     stage_strip<NC, NVW>(sO, LDB, col0, o);

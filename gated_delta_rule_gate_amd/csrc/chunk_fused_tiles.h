@@ -24,15 +24,24 @@ namespace kda {
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-// Lane l of M (row-major bf16, row stride ld elements; ld % 4 == 0, n0 % 4 == 0):
-// {M[k0 + 4g + e][n0 + l%16]}, e = 0..3, g = (l%64)/16.
-__device__ __forceinline__ bf16x4_t load_cfrag(const bf16_t *M, int ld, int k0, int n0) {
+// The lane's part of a transposed-load address into a row-major bf16 matrix
+// of row stride ld: (4g + s/4) * ld + 4 (s % 4), g = lane / 16, s = lane % 16.
+// Computed once per phase; the tile offsets k0 * ld + n0 are then immediates.
+__device__ __forceinline__ int cfrag_lane_off(int ld) {
   const int lane = tid_opaque() & 63;
   const int g = lane >> 4, s = lane & 15;
-  const bf16_t *p = M + (k0 + 4 * g + (s >> 2)) * ld + n0 + 4 * (s & 3);
-  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (i16x4_t __attribute__((address_space(3))) *)(p));
+  return (4 * g + (s >> 2)) * ld + 4 * (s & 3);
+}
+
+// Lane l of M (row-major bf16, ld % 4 == 0, n0 % 4 == 0), with lo = cfrag_lane_off(ld):
+// {M[k0 + 4g + e][n0 + l%16]}, e = 0..3, g = (l%64)/16.
+__device__ __forceinline__ bf16x4_t load_cfrag_at(const bf16_t *M, int lo) {
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4_t __attribute__((address_space(3))) *)(M + lo));
   return __builtin_bit_cast(bf16x4_t, r);
+}
+
+__device__ __forceinline__ bf16x4_t load_cfrag(const bf16_t *M, int ld, int k0, int n0) {
+  return load_cfrag_at(M + k0 * ld + n0, cfrag_lane_off(ld));
 }
 
 __device__ __forceinline__ f32x4_t mma16(const bf16x4_t &a, const bf16x4_t &b, const f32x4_t &c) {
@@ -56,6 +65,17 @@ __device__ __forceinline__ f32x4_t to_f32x4(const bf16x4_t &x) {
 
 // Two C-layout fragments (contraction rows k0.. and k0+16..) as the 8-slot
 // operand of a 16x16x32 product under the kidx map of Mma<bf16_t>.
+__device__ __forceinline__ bf16x8_t load_frag32_at(const bf16_t *M, int ld, int lo_off) {
+  const bf16x4_t lo = load_cfrag_at(M, lo_off), hi = load_cfrag_at(M + 16 * ld, lo_off);
+  bf16x8_t f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = lo[e];
+    f[e + 4] = hi[e];
+  }
+  return f;
+}
+
 __device__ __forceinline__ bf16x8_t load_frag32(const bf16_t *M, int ld, int k0, int n0) {
   const bf16x4_t lo = load_cfrag(M, ld, k0, n0), hi = load_cfrag(M, ld, k0 + 16, n0);
   bf16x8_t f;
@@ -145,18 +165,22 @@ __device__ __forceinline__ void wy_subst2(const bf16_t *sXa, const bf16_t *sXb, 
   constexpr int NC = C / 16;
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
+  const int lx = cfrag_lane_off(ldx);
+  const float *aRow = sAkk + n16 * lda + 4 * grp;
+  const bf16_t *tRow = sTd + n16 * ldt + 4 * grp;
+  const float *rs = rowscale + 4 * grp;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    f32x4_t Ra = to_f32x4(load_cfrag(sXa, ldx, 16 * i, 16 * ct));
-    f32x4_t Rb = to_f32x4(load_cfrag(sXb, ldx, 16 * i, 16 * ct));
-    Rb = Rb * *reinterpret_cast<const f32x4_t *>(rowscale + 16 * i + 4 * grp);
+    f32x4_t Ra = to_f32x4(load_cfrag_at(sXa + 16 * i * ldx + 16 * ct, lx));
+    f32x4_t Rb = to_f32x4(load_cfrag_at(sXb + 16 * i * ldx + 16 * ct, lx));
+    Rb = Rb * *reinterpret_cast<const f32x4_t *>(rs + 16 * i);
 #pragma unroll
     for (int j = 0; j < i; ++j) {
-      const bf16x4_t a = to_bf16x4(-*reinterpret_cast<const f32x4_t *>(sAkk + (16 * i + n16) * lda + 16 * j + 4 * grp));
+      const bf16x4_t a = to_bf16x4(-*reinterpret_cast<const f32x4_t *>(aRow + 16 * i * lda + 16 * j));
       Ra = mma16(a, to_bf16x4(Wa[j]), Ra);
       Rb = mma16(a, to_bf16x4(Wb[j]), Rb);
     }
-    const bf16x4_t t = *reinterpret_cast<const bf16x4_t *>(sTd + (16 * i + n16) * ldt + 4 * grp);
+    const bf16x4_t t = *reinterpret_cast<const bf16x4_t *>(tRow + 16 * i * ldt);
     Wa[i] = mma16(t, to_bf16x4(Ra), zero4());
     Wb[i] = mma16(t, to_bf16x4(Rb), zero4());
   }
@@ -185,6 +209,8 @@ __device__ __forceinline__ void wq_times_state(f32x4_t (&p1)[C / 16][NVW], f32x4
   constexpr int NC = C / 16, DT = D / 16, SD = D / 32;
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
+  const int lw = cfrag_lane_off(ldw);
+  const bf16_t *qRow = sQ + n16 * ldt + 4 * grp;
 #pragma unroll
   for (int s = 0; s < SD; ++s) {
     bf16x8_t fh[NVW];
@@ -197,10 +223,10 @@ __device__ __forceinline__ void wq_times_state(f32x4_t (&p1)[C / 16][NVW], f32x4
     }
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const bf16x8_t fw = load_frag32(sWT, ldw, 32 * s, 16 * i);
+      const bf16x8_t fw = load_frag32_at(sWT + 32 * s * ldw + 16 * i, ldw, lw);
       bf16x8_t fq;
-      const bf16x4_t q0 = *reinterpret_cast<const bf16x4_t *>(sQ + (16 * i + n16) * ldt + 32 * s + 4 * grp);
-      const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t *>(sQ + (16 * i + n16) * ldt + 32 * s + 16 + 4 * grp);
+      const bf16x4_t q0 = *reinterpret_cast<const bf16x4_t *>(qRow + 16 * i * ldt + 32 * s);
+      const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t *>(qRow + 16 * i * ldt + 32 * s + 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         fq[e] = q0[e];
@@ -215,6 +241,42 @@ __device__ __forceinline__ void wq_times_state(f32x4_t (&p1)[C / 16][NVW], f32x4
   }
 }
 
+// o += A_qk v_new with A_qk bf16 row-major [C][ldh] (causal blocks only).
+template <int C, int NVW>
+__device__ __forceinline__ void causal_times_h(f32x4_t (&o)[C / 16][NVW], const bf16_t *sAqh, int ldh,
+                                               const f32x4_t (&vn)[C / 16][NVW]) {
+  using M = Mma<bf16_t>;
+  constexpr int NC = C / 16, SC = C / 32;
+  const int lane = tid_opaque() & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+  const bf16_t *aRow = sAqh + n16 * ldh + 4 * grp;
+#pragma unroll
+  for (int s = 0; s < SC; ++s) {
+    bf16x8_t fv[NVW];
+#pragma unroll
+    for (int v = 0; v < NVW; ++v) {
+      f32x4_t col[NC];
+#pragma unroll
+      for (int t = 0; t < NC; ++t) col[t] = vn[t][v];
+      fv[v] = acc_frag<bf16_t, NC>(col, s);
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      if (16 * (i + 1) <= s * 32) continue;
+      const bf16x4_t a0 = *reinterpret_cast<const bf16x4_t *>(aRow + 16 * i * ldh + 32 * s);
+      const bf16x4_t a1 = *reinterpret_cast<const bf16x4_t *>(aRow + 16 * i * ldh + 32 * s + 16);
+      bf16x8_t fa;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        fa[e] = a0[e];
+        fa[e + 4] = a1[e];
+      }
+#pragma unroll
+      for (int v = 0; v < NVW; ++v) o[i][v] = M::mma(fa, fv[v], o[i][v]);
+    }
+  }
+}
+
 // h <- Diag(2^b_L) h + k~^T v_new with k~ row-major [C][ldt].
 template <int C, int D, int NVW>
 __device__ __forceinline__ void state_update_kt(f32x4_t (&h)[D / 16][NVW], const bf16_t *sKt, int ldt,
@@ -223,9 +285,11 @@ __device__ __forceinline__ void state_update_kt(f32x4_t (&h)[D / 16][NVW], const
   constexpr int NC = C / 16, DT = D / 16, SC = C / 32;
   const int lane = tid_opaque() & 63;
   const int grp = lane >> 4;
+  const int lk = cfrag_lane_off(ldt);
+  const float *dRow = sDecay + 4 * grp;
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
-    const f32x4_t dec = *reinterpret_cast<const f32x4_t *>(sDecay + 16 * t + 4 * grp);
+    const f32x4_t dec = *reinterpret_cast<const f32x4_t *>(dRow + 16 * t);
 #pragma unroll
     for (int v = 0; v < NVW; ++v) h[t][v] = h[t][v] * dec;
   }
@@ -241,7 +305,7 @@ __device__ __forceinline__ void state_update_kt(f32x4_t (&h)[D / 16][NVW], const
     }
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      const bf16x8_t fk = load_frag32(sKt, ldt, 32 * s, 16 * t);
+      const bf16x8_t fk = load_frag32_at(sKt + 32 * s * ldt + 16 * t, ldt, lk);
 #pragma unroll
       for (int v = 0; v < NVW; ++v) h[t][v] = M::mma(fk, fv[v], h[t][v]);
     }
@@ -338,8 +402,9 @@ __device__ __forceinline__ void gram_row_partial(const bf16_t *sQ, const bf16_t 
 // lane holds A[r = 16I + n16][16j + 4g .. 16j + 4g + 3]. With add, the values
 // already in LDS (the other channel half) are added first.
 template <int I, int NC>
-__device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)[NC], bool add, int r, int L,
-                                            float scale, float beta_r, float *sAkk, float *sAqk, int lda) {
+__device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)[NC], bool add, bool final, int r,
+                                            int L, float scale, float beta_r, float *sAkk, float *sAqk, int lda,
+                                            bf16_t *sAqh, int ldh) {
   const int grp = (tid_opaque() & 63) >> 4;
   f32x4_t prev[I + 1][2];
   if (add) {
@@ -369,19 +434,25 @@ __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)
       aq = aq + prev[j][0];
       ak = ak + prev[j][1];
     }
-    *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp) = aq;
+    if (final)
+      *reinterpret_cast<bf16x4_t *>(sAqh + r * ldh + 16 * j + 4 * grp) = to_bf16x4(aq);
+    else
+      *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp) = aq;
     *reinterpret_cast<f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp) = ak;
   }
   // the product with A_qk reads 32 columns at a time: zero the block right of
   // an even diagonal block
-  if constexpr ((I & 1) == 0 && I + 1 < NC)
-    *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * (I + 1) + 4 * grp) = zero4();
+  if constexpr ((I & 1) == 0 && I + 1 < NC) {
+    if (final) *reinterpret_cast<bf16x4_t *>(sAqh + r * ldh + 16 * (I + 1) + 4 * grp) = to_bf16x4(zero4());
+  }
 }
 
+// A_kk comes out fp32 in sAkk; A_qk comes out bf16 in sAqh (row stride ldh),
+// with sAqk (fp32) holding the second channel half's partial sums meanwhile.
 template <int NT, int C, int D, bool SAFE>
 __device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                             const float *sBeta, float scale, float *sAkk, float *sAqk, int lda,
-                                            int L) {
+                                            bf16_t *sAqh, int ldh, int L) {
   constexpr int NW = NT / 64, NC = C / 16;
   constexpr int HS = (NW / NC >= 2) ? 2 : 1, CW = D / HS, NS = CW / 32;
   static_assert(NW >= NC && CW % 32 == 0, "wave split of the grams");
@@ -438,24 +509,24 @@ __device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, 
   }
   const int r = 16 * i + n16;
   const float beta_r = active ? sBeta[r] : 0.f;
-  auto finish = [&](bool add) {
+  auto finish = [&](bool add, bool final) {
     switch (i) {
-      case 0: gram_finish<0, NC>(accQ, accK, add, r, L, scale, beta_r, sAkk, sAqk, lda); break;
-      case 1: gram_finish<1, NC>(accQ, accK, add, r, L, scale, beta_r, sAkk, sAqk, lda); break;
+      case 0: gram_finish<0, NC>(accQ, accK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh); break;
+      case 1: gram_finish<1, NC>(accQ, accK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh); break;
       case 2:
-        if constexpr (NC > 2) gram_finish<2, NC>(accQ, accK, add, r, L, scale, beta_r, sAkk, sAqk, lda);
+        if constexpr (NC > 2) gram_finish<2, NC>(accQ, accK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh);
         break;
       case 3:
-        if constexpr (NC > 3) gram_finish<3, NC>(accQ, accK, add, r, L, scale, beta_r, sAkk, sAqk, lda);
+        if constexpr (NC > 3) gram_finish<3, NC>(accQ, accK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh);
         break;
     }
   };
   if constexpr (HS == 2) {
-    if (active && hsel == 1) finish(false);
+    if (active && hsel == 1) finish(false, false);
     __syncthreads();
-    if (active && hsel == 0) finish(true);
+    if (active && hsel == 0) finish(true, true);
   } else {
-    if (active) finish(false);
+    if (active) finish(false, true);
   }
 }
 
