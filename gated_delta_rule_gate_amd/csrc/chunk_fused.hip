@@ -18,12 +18,11 @@
 //   (4)     each wave solves its 16-column tiles of w and u by blocked
 //           forward substitution; w goes to LDS transposed, u stays in registers
 //   (5)+(6) v_new = u - w h, o = q~ h + A_qk v_new, h <- 2^b_L h + k~^T v_new
-//   o       staged in LDS, written with 16-byte row stores
+//   o       formed transposed, so each lane stores four adjacent columns
 //
 // LDS (C = 64, D = 128: about 151 KB): q (-> q~), k (-> X_w), v, gate (-> b
 // -> w^T), A_kk, k~, A_qk (fp32 partial sums and the bf16 result), the
-// diagonal inverses, beta, b_L, 2^b_L, dt_bias;
-// o is staged over the k and v tiles.
+// diagonal inverses, beta, b_L, 2^b_L, dt_bias.
 #include "chunk_fused_tiles.h"
 #include "kda_launch.h"
 
@@ -60,7 +59,6 @@ struct FusedSmem {
   static constexpr size_t dt = decay + 4 * D;
   static constexpr size_t seg = dt + 4 * D;
   static constexpr size_t total = seg + 4 * NT;
-  static_assert(2 * tile >= 4 * C * LDB, "o staging over the k and v tiles");
   static_assert(4 * C * LDB >= 2 * D * LDW, "w^T over the b tile");
 };
 
@@ -171,7 +169,6 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   Tin *sV = reinterpret_cast<Tin *>(smem + S::v);
   float *sB = reinterpret_cast<float *>(smem + S::b);  // gate, then b
   Tin *sWT = reinterpret_cast<Tin *>(smem + S::b);     // w^T once b is consumed
-  float *sO = reinterpret_cast<float *>(smem + S::k);  // o staging over k and v
   float *sAkk = reinterpret_cast<float *>(smem + S::akk);
   Tin *sKt = reinterpret_cast<Tin *>(smem + S::kt);
   float *sAqk = reinterpret_cast<float *>(smem + S::aqk);  // partial sums of A_qk
@@ -259,10 +256,8 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
       for (int v = 0; v < NVW; ++v) uv[i][v] = uv[i][v] - p1[i][v];
     causal_times_h<C, NVW>(o, sAqh, S::LDAH, uv);
     state_update_kt<C, D, NVW>(hs, sKt, LDT, uv, sDecay);
-    // o through the (now unused) k and v tiles, then 16-byte row stores
-    stage_strip<NC, NVW>(sO, LDB, col0, o);
-    __syncthreads();
-    store_rows_from_f32<Tin, NT, C, D>(reinterpret_cast<Tin *>(p.o) + off, ld, sO, LDB, L);
+    // o from registers: four adjacent value columns per lane and row
+    store_oT<C, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, L, o);
     __syncthreads();
   }
   if (p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, D, col0, D, hs);

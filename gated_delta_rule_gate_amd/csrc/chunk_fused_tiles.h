@@ -199,7 +199,9 @@ __device__ __forceinline__ void store_wT(bf16_t *sWT, int ldw, int ct, const f32
 
 // ---------------------------------------------------------------------------------------------
 // (5)/(6) on one wave's strip of NVW value tiles (h [D/16][NVW], C-layout).
-// p1 = w h with w read from w^T, o = q~ h with q~ row-major.
+// p1 = w h with w read from w^T; o is formed transposed, o^T = h^T q~^T with
+// q~ row-major, so o[i][v] holds rows 16v.. of o^T (value columns) against
+// chunk rows 16i + (lane % 16).
 // ---------------------------------------------------------------------------------------------
 template <int C, int D, int NVW>
 __device__ __forceinline__ void wq_times_state(f32x4_t (&p1)[C / 16][NVW], f32x4_t (&o)[C / 16][NVW],
@@ -235,13 +237,16 @@ __device__ __forceinline__ void wq_times_state(f32x4_t (&p1)[C / 16][NVW], f32x4
 #pragma unroll
       for (int v = 0; v < NVW; ++v) {
         p1[i][v] = M::mma(fw, fh[v], p1[i][v]);
-        o[i][v] = M::mma(fq, fh[v], o[i][v]);
+        // o transposed: h^T (the same fragment) times q~^T, so a lane ends up
+        // with four adjacent value columns of one chunk row
+        o[i][v] = M::mma(fh[v], fq, o[i][v]);
       }
     }
   }
 }
 
-// o += A_qk v_new with A_qk bf16 row-major [C][ldh] (causal blocks only).
+// o^T += v_new^T A_qk^T with A_qk bf16 row-major [C][ldh] (causal blocks only);
+// o in the transposed layout of wq_times_state.
 template <int C, int NVW>
 __device__ __forceinline__ void causal_times_h(f32x4_t (&o)[C / 16][NVW], const bf16_t *sAqh, int ldh,
                                                const f32x4_t (&vn)[C / 16][NVW]) {
@@ -272,7 +277,25 @@ __device__ __forceinline__ void causal_times_h(f32x4_t (&o)[C / 16][NVW], const 
         fa[e + 4] = a1[e];
       }
 #pragma unroll
-      for (int v = 0; v < NVW; ++v) o[i][v] = M::mma(fa, fv[v], o[i][v]);
+      for (int v = 0; v < NVW; ++v) o[i][v] = M::mma(fv[v], fa, o[i][v]);
+    }
+  }
+}
+
+// o (transposed accumulators, see wq_times_state) straight to global rows of
+// type bf16: lane writes o[16i + l%16][col0 + 16v + 4g .. + 3] as 8 bytes; rows
+// >= L are not written.
+template <int C, int NVW>
+__device__ __forceinline__ void store_oT(bf16_t *g, int64_t ldg, int col0, int L, const f32x4_t (&o)[C / 16][NVW]) {
+  const int lane = tid_opaque() & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < C / 16; ++i) {
+    const int r = 16 * i + n16;
+    if (r < L) {
+#pragma unroll
+      for (int v = 0; v < NVW; ++v)
+        *reinterpret_cast<bf16x4_t *>(g + (int64_t)r * ldg + col0 + 16 * v + 4 * grp) = to_bf16x4(o[i][v]);
     }
   }
 }
