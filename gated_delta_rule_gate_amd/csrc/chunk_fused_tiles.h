@@ -350,8 +350,8 @@ namespace kda {
 // numerical note"). Non-safe gates take the diagonal block per pair (section
 // "Safe vs non-safe intra path"). Only causal blocks are formed ("[examples]
 // Read only the causal columns in chunk_fwd_A_diag_anchored", description).
-// With HS = 2 the second channel half stores its scaled, masked partial sums,
-// and after a barrier the first half adds its own and writes the result.
+// With HS = 2 each half stores its scaled, masked partial sums of one matrix,
+// and after a barrier adds its own partial sums of the other and writes it.
 // ---------------------------------------------------------------------------------------------
 template <int I, int NC, int NS, bool SAFE>
 __device__ __forceinline__ void gram_row_partial(const bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB,
@@ -422,19 +422,21 @@ __device__ __forceinline__ void gram_row_partial(const bf16_t *sQ, const bf16_t 
 }
 
 // Scale, beta and masks of row block I, then one 16-byte store per block:
-// lane holds A[r = 16I + n16][16j + 4g .. 16j + 4g + 3]. With add, the values
-// already in LDS (the other channel half) are added first.
+// lane holds A[r = 16I + n16][16j + 4g .. 16j + 4g + 3]. doQ / doK select
+// A_qk / A_kk. With add, the other channel half's partial sums (A_qk in sAqk,
+// A_kk in sAkk) are added first. Final A_qk goes to sAqh as bf16, partial
+// A_qk to sAqk; A_kk always to sAkk.
 template <int I, int NC>
-__device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)[NC], bool add, bool final, int r,
-                                            int L, float scale, float beta_r, float *sAkk, float *sAqk, int lda,
-                                            bf16_t *sAqh, int ldh) {
+__device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)[NC], bool doQ, bool doK, bool add,
+                                            bool final, int r, int L, float scale, float beta_r, float *sAkk,
+                                            float *sAqk, int lda, bf16_t *sAqh, int ldh) {
   const int grp = (tid_opaque() & 63) >> 4;
-  f32x4_t prev[I + 1][2];
+  f32x4_t prevQ[I + 1], prevK[I + 1];
   if (add) {
 #pragma unroll
     for (int j = 0; j <= I; ++j) {
-      prev[j][0] = *reinterpret_cast<const f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp);
-      prev[j][1] = *reinterpret_cast<const f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp);
+      if (doQ) prevQ[j] = *reinterpret_cast<const f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp);
+      if (doK) prevK[j] = *reinterpret_cast<const f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp);
     }
   }
   const bool row_ok = r < L;
@@ -453,20 +455,22 @@ __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)
       aq = zero4();
       ak = zero4();
     }
-    if (add) {
-      aq = aq + prev[j][0];
-      ak = ak + prev[j][1];
+    if (doQ) {
+      if (add) aq = aq + prevQ[j];
+      if (final)
+        *reinterpret_cast<bf16x4_t *>(sAqh + r * ldh + 16 * j + 4 * grp) = to_bf16x4(aq);
+      else
+        *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp) = aq;
     }
-    if (final)
-      *reinterpret_cast<bf16x4_t *>(sAqh + r * ldh + 16 * j + 4 * grp) = to_bf16x4(aq);
-    else
-      *reinterpret_cast<f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp) = aq;
-    *reinterpret_cast<f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp) = ak;
+    if (doK) {
+      if (add) ak = ak + prevK[j];
+      *reinterpret_cast<f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp) = ak;
+    }
   }
   // the product with A_qk reads 32 columns at a time: zero the block right of
   // an even diagonal block
   if constexpr ((I & 1) == 0 && I + 1 < NC) {
-    if (final) *reinterpret_cast<bf16x4_t *>(sAqh + r * ldh + 16 * (I + 1) + 4 * grp) = to_bf16x4(zero4());
+    if (doQ && final) *reinterpret_cast<bf16x4_t *>(sAqh + r * ldh + 16 * (I + 1) + 4 * grp) = to_bf16x4(zero4());
   }
 }
 
@@ -532,24 +536,32 @@ __device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, 
   }
   const int r = 16 * i + n16;
   const float beta_r = active ? sBeta[r] : 0.f;
-  auto finish = [&](bool add, bool final) {
+  auto finish = [&](bool doQ, bool doK, bool add, bool final) {
     switch (i) {
-      case 0: gram_finish<0, NC>(accQ, accK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh); break;
-      case 1: gram_finish<1, NC>(accQ, accK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh); break;
+      case 0: gram_finish<0, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh); break;
+      case 1: gram_finish<1, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh); break;
       case 2:
-        if constexpr (NC > 2) gram_finish<2, NC>(accQ, accK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh);
+        if constexpr (NC > 2) gram_finish<2, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh);
         break;
       case 3:
-        if constexpr (NC > 3) gram_finish<3, NC>(accQ, accK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh);
+        if constexpr (NC > 3) gram_finish<3, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh);
         break;
     }
   };
   if constexpr (HS == 2) {
-    if (active && hsel == 1) finish(false, false);
+    // the two halves split the merge: half 1 finishes A_qk's partner and half 0
+    // A_kk's, so each wave stores one partial and completes the other matrix
+    if (active) {
+      if (hsel == 1) finish(true, false, false, false);
+      else finish(false, true, false, false);
+    }
     __syncthreads();
-    if (active && hsel == 0) finish(true, true);
+    if (active) {
+      if (hsel == 0) finish(true, false, true, true);
+      else finish(false, true, true, true);
+    }
   } else {
-    if (active) finish(false, true);
+    if (active) finish(true, true, false, true);
   }
 }
 
