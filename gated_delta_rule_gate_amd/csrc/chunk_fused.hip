@@ -117,7 +117,9 @@ struct ChunkRegs {
     beta = (r < C && r < L) ? p.beta[(t0 + r) * p.H + h] : 0.f;
   }
 
-  // q, k, v to their tiles; the gate input, activated, to sB (rows >= L: 0)
+  // q, k, v to their tiles; the gate input, activated, to sB (rows >= L: 0).
+  // For the safe gate sDt holds dt_bias * c1 with c1 = -exp(A_log) log2(e),
+  // so the sigmoid's exponent is one fma.
   template <int GK>
   __device__ __forceinline__ void store(Tin *sQ, Tin *sK, Tin *sV, float *sB, float *sBeta, const float *sDt, int L,
                                         float expA, float lower_bound) const {
@@ -125,27 +127,31 @@ struct ChunkRegs {
     wait_vmem();
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int idx = it * NT + tid_opaque();
-      const int r = idx / VPR, c = (idx % VPR) * EPV;
+      const unsigned idx = it * NT + (unsigned)tid_opaque();
+      const unsigned r = idx / VPR, c = (idx % VPR) * EPV;
       if (NVT % NT == 0 || idx < NVT) {
         *reinterpret_cast<u32x4_t *>(sQ + r * TL::LDT + c) = q[it];
         *reinterpret_cast<u32x4_t *>(sK + r * TL::LDT + c) = k[it];
         *reinterpret_cast<u32x4_t *>(sV + r * TL::LDT + c) = v[it];
       }
     }
+    const float c1 = -expA * kLog2e, c2 = lower_bound * kLog2e;
 #pragma unroll
     for (int it = 0; it < IX; ++it) {
-      const int idx = it * NT + tid_opaque();
-      const int r = idx / XPR, c = (idx % XPR) * 4;
+      const unsigned idx = it * NT + (unsigned)tid_opaque();
+      const unsigned r = idx / XPR, c = (idx % XPR) * 4;
       if (NVX % NT == 0 || idx < NVX) {
         const f32x4_t dt = *reinterpret_cast<const f32x4_t *>(sDt + c);
         f32x4_t la;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // rows >= L were loaded as zeros, so the activation is finite there; select, no branch
-          const float a = gate_log2(GK, x[it][e], dt[e], expA, lower_bound);
-          la[e] = (r < L) ? a : 0.f;
+          if constexpr (GK == kGateSafe)
+            la[e] = c2 * fast_rcp(1.0f + fast_exp2(fmaf(x[it][e], c1, dt[e])));
+          else
+            la[e] = gate_log2(GK, x[it][e], dt[e], expA, lower_bound);
         }
+        // rows >= L were loaded as zeros, so the activation is finite there
+        if (L < C && (int)r >= L) la = zero4();
         *reinterpret_cast<f32x4_t *>(sB + r * TL::LDB + c) = la;
       }
     }
@@ -190,7 +196,10 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   const int64_t sbase = (int64_t)nh * D * D;
   const int64_t ld = (int64_t)p.H * D;
   const float expA = (GK == kGateSafe || GK == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
-  for (int i = tid_opaque(); i < D; i += NT) sDt[i] = p.dt_bias ? p.dt_bias[h * D + i] : 0.f;
+  for (int i = tid_opaque(); i < D; i += NT) {
+    const float dt = p.dt_bias ? p.dt_bias[h * D + i] : 0.f;
+    sDt[i] = (GK == kGateSafe) ? dt * (-expA * kLog2e) : dt;
+  }
 
   f32x4_t hs[DT][NVW];
   if (p.h0) {
