@@ -12,17 +12,17 @@
 // Per chunk:
 //   store   raw q, k, v and the activated gate to LDS
 //   (1)     chunk-local cumsum of the gate (b), 2^b_L
-//   (2)     grams A_kk, A_qk (fp32 in LDS)
-//   (3)     one wave inverts the four 16x16 diagonal blocks of I + A_kk while
-//           the others form q~ = scale q 2^b, X_w = beta k 2^b and k~ = k 2^(b_L-b)
+//   (2)     grams A_kk (fp32), A_qk (bf16), and from the same exponentials
+//           q~ = scale q 2^b, X_w = beta k 2^b and k~ = k 2^(b_L-b)
+//   (3)     one wave inverts the four 16x16 diagonal blocks of I + A_kk
 //   (4)     each wave solves its 16-column tiles of w and u by blocked
 //           forward substitution; w goes to LDS transposed, u stays in registers
 //   (5)+(6) v_new = u - w h, o = q~ h + A_qk v_new, h <- 2^b_L h + k~^T v_new
 //   o       formed transposed, so each lane stores four adjacent columns
 //
-// LDS (C = 64, D = 128: about 151 KB): q (-> q~), k (-> X_w), v, gate (-> b
-// -> w^T), A_kk, k~, A_qk (fp32 partial sums and the bf16 result), the
-// diagonal inverses, beta, b_L, 2^b_L, dt_bias.
+// LDS (C = 64, D = 128: about 156 KB): q (-> q~), k, v, gate (-> b -> X_w and
+// w^T), A_kk, k~, A_qk (fp32 partial sums and the bf16 result), the diagonal
+// inverses, the midpoint tables, beta, b_L, 2^b_L, dt_bias.
 #include "chunk_fused_tiles.h"
 #include "kda_launch.h"
 
@@ -46,20 +46,24 @@ struct FusedSmem {
   static constexpr size_t q = 0;
   static constexpr size_t k = q + tile;
   static constexpr size_t v = k + tile;
+  // the b region later holds X_w = beta k 2^b ([C][LDT] bf16) and w^T after it
+  static constexpr size_t xw_off = 0, wt_off = tile;
+  static constexpr size_t breg = (4 * C * LDB > tile + 2 * D * LDW) ? 4 * C * LDB : tile + 2 * D * LDW;
   static constexpr size_t b = v + tile;
-  static constexpr size_t akk = b + 4 * C * LDB;
+  static constexpr size_t akk = b + breg;
   static constexpr size_t kt = akk + 4 * C * LDA;
   static constexpr size_t aqk = kt + tile;
   static constexpr int LDAH = C + 8;    // A_qk [C][LDAH] bf16
   static constexpr size_t aqh = aqk + 4 * C * LDA;
   static constexpr size_t td = aqh + 2 * C * LDAH;
-  static constexpr size_t beta = td + 2 * C * LDTD;
+  static constexpr size_t t1 = td + 2 * C * LDTD;     // 2^m_i per row block and channel, fp32 [C/16][D]
+  static constexpr size_t t2 = t1 + 4 * (C / 16) * D;  // 2^(b_L - m_i)
+  static constexpr size_t beta = t2 + 4 * (C / 16) * D;
   static constexpr size_t bl = beta + 4 * C;
   static constexpr size_t decay = bl + 4 * D;
   static constexpr size_t dt = decay + 4 * D;
   static constexpr size_t seg = dt + 4 * D;
   static constexpr size_t total = seg + 4 * NT;
-  static_assert(4 * C * LDB >= 2 * D * LDW, "w^T over the b tile");
 };
 
 // One chunk's raw inputs held in registers between the HBM load and the LDS store.
@@ -173,8 +177,11 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   Tin *sQ = reinterpret_cast<Tin *>(smem + S::q);    // q, then q~
   Tin *sK = reinterpret_cast<Tin *>(smem + S::k);    // k, then beta k 2^b
   Tin *sV = reinterpret_cast<Tin *>(smem + S::v);
-  float *sB = reinterpret_cast<float *>(smem + S::b);  // gate, then b
-  Tin *sWT = reinterpret_cast<Tin *>(smem + S::b);     // w^T once b is consumed
+  float *sB = reinterpret_cast<float *>(smem + S::b);            // gate, then b
+  Tin *sXw = reinterpret_cast<Tin *>(smem + S::b + S::xw_off);  // beta k 2^b once b is consumed
+  Tin *sWT = reinterpret_cast<Tin *>(smem + S::b + S::wt_off);  // w^T
+  float *sT1 = reinterpret_cast<float *>(smem + S::t1);
+  float *sT2 = reinterpret_cast<float *>(smem + S::t2);
   float *sAkk = reinterpret_cast<float *>(smem + S::akk);
   Tin *sKt = reinterpret_cast<Tin *>(smem + S::kt);
   float *sAqk = reinterpret_cast<float *>(smem + S::aqk);  // partial sums of A_qk
@@ -230,20 +237,30 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     if constexpr (GK == kGateLog2Cumsum) gate_pad<NT, C, D>(sB, LDB, sBL, L);
     else gate_cumsum<NT, C, D>(sB, LDB, sBL, sSeg);
     for (int i = tid_opaque(); i < D; i += NT) sDecay[i] = fast_exp2(sBL[i]);
-    // (2)
-    grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L);
+    if constexpr (SAFE) {
+      // per row block and channel: 2^m_i and 2^(b_L - m_i), m_i the midpoint row
+      for (int idx = tid_opaque(); idx < NC * D; idx += NT) {
+        const int i = idx / D, ch = idx % D;
+        const float m = sB[(16 * i + 8) * LDB + ch];
+        sT1[idx] = fast_exp2(m);
+        sT2[idx] = fast_exp2(sBL[ch] - m);
+      }
+      __syncthreads();
+    }
+    // (2) the grams, and q~, k~, beta k 2^b
+    grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT1, sT2,
+                                sBL, sKt, sXw);
     __syncthreads();
     if (more) regs.load_qkv(p, t0 + C, Ln, h);
-    // (3) diagonal inverses on the last wave; operand tiles on the others
+    // (3) diagonal inverses on the last wave
     if (wid == NW - 1) diag_inverse<C>(sAkk, LDA, sTd, S::LDTD);
-    else operand_pass<C, D>(sQ, sK, sKt, LDT, sB, LDB, sBL, sBeta, p.scale, NT - 64);
     __syncthreads();
     // (4) this wave's column tiles of w (channels) and u (values)
     f32x4_t uv[NC][NVW];
 #pragma unroll
     for (int v = 0; v < NVW; ++v) {
       f32x4_t W[NC], U[NC];
-      wy_subst2<C>(sK, sV, LDT, wid * NVW + v, sBeta, sAkk, LDA, sTd, S::LDTD, W, U);
+      wy_subst2<C>(sXw, sV, LDT, wid * NVW + v, sBeta, sAkk, LDA, sTd, S::LDTD, W, U);
       store_wT<C>(sWT, S::LDW, wid * NVW + v, W);
 #pragma unroll
       for (int i = 0; i < NC; ++i) uv[i][v] = U[i];

@@ -6,7 +6,8 @@
 //    and only the four 16x16 diagonal inverses are formed explicitly;
 //  - keeps w^T and k~ = k 2^(b_L - b) in LDS in the layouts their producers
 //    write with wide stores, and reads the transposed MFMA operands with
-//    ds_read_b64_tr_b16.
+//    ds_read_b64_tr_b16;
+//  - forms q~, k~ and beta k 2^b in the grams from the same exponentials.
 //
 // ds_read_b64_tr_b16 (measured lane layout): within each 16-lane group g,
 // source lane s supplies four consecutive 16-bit elements m[s][0..3] from its
@@ -110,45 +111,6 @@ __device__ __forceinline__ void diag_inverse(const float *sAkk, int lda, bf16_t 
   bf16_t *T = sTd + i * 16 * ldt;
 #pragma unroll
   for (int r = 0; r < 16; ++r) T[r * ldt + c] = static_cast<bf16_t>(x[r]);
-}
-
-// ---------------------------------------------------------------------------------------------
-// Elementwise operand pass over the chunk, 8 channels per item, on threads
-// [0, nthr): with E = 2^b,
-//   q~  = scale q E            in place of q
-//   X_w = beta k E             in place of k
-//   k~  = k 2^(b_L - b)        into sKt
-// Rows past the chunk's end hold q = k = 0 and carry the last valid b, so
-// they give zeros.
-// ---------------------------------------------------------------------------------------------
-template <int C, int D>
-__device__ __forceinline__ void operand_pass(bf16_t *sQ, bf16_t *sK, bf16_t *sKt, int ldt, const float *sB, int ldb,
-                                             const float *sBL, const float *sBeta, float scale, int nthr) {
-  constexpr int G = C * D / 8, GPR = D / 8;
-  for (int g = tid_opaque(); g < G; g += nthr) {
-    const int r = g / GPR, c = (g % GPR) * 8;
-    const bf16x8_t q = *reinterpret_cast<const bf16x8_t *>(sQ + r * ldt + c);
-    const bf16x8_t k = *reinterpret_cast<const bf16x8_t *>(sK + r * ldt + c);
-    const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(sB + r * ldb + c);
-    const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(sB + r * ldb + c + 4);
-    const f32x4_t l0 = *reinterpret_cast<const f32x4_t *>(sBL + c);
-    const f32x4_t l1 = *reinterpret_cast<const f32x4_t *>(sBL + c + 4);
-    const float beta = sBeta[r];
-    bf16x8_t qt, xw, kt;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float b = e < 4 ? b0[e] : b1[e - 4];
-      const float bl = e < 4 ? l0[e] : l1[e - 4];
-      const float E = fast_exp2(b);
-      const float kf = static_cast<float>(k[e]);
-      qt[e] = static_cast<bf16_t>(scale * static_cast<float>(q[e]) * E);
-      xw[e] = static_cast<bf16_t>(beta * kf * E);
-      kt[e] = static_cast<bf16_t>(kf * fast_exp2(bl - b));
-    }
-    *reinterpret_cast<bf16x8_t *>(sQ + r * ldt + c) = qt;
-    *reinterpret_cast<bf16x8_t *>(sK + r * ldt + c) = xw;
-    *reinterpret_cast<bf16x8_t *>(sKt + r * ldt + c) = kt;
-  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -353,9 +315,19 @@ namespace kda {
 // With HS = 2 each half stores its scaled, masked partial sums of one matrix,
 // and after a barrier adds its own partial sums of the other and writes it.
 // ---------------------------------------------------------------------------------------------
+// Row block I of the grams over channels [c0, c0 + 32 NS), plus the chunk's
+// other operand tiles for the same (token, channel) elements:
+//   q~  = scale q 2^b      written over q (this wave alone reads these q)
+//   k~  = k 2^(b_L - b)    written to sKt
+//   X_w = beta k 2^b       returned in xw (written after the grams' barrier)
+// For the safe gate these reuse the midpoint exponentials: 2^b = 2^(b - m_I) T1
+// and 2^(b_L - b) = 2^(m_I - b) T2 with the per-channel tables T1 = 2^m_I,
+// T2 = 2^(b_L - m_I); other gates take them directly.
 template <int I, int NC, int NS, bool SAFE>
-__device__ __forceinline__ void gram_row_partial(const bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB,
-                                                 int ldb, int c0, f32x4_t (&accQ)[NC], f32x4_t (&accK)[NC]) {
+__device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
+                                                 int c0, const float *sT1, const float *sT2, const float *sBL, int D,
+                                                 float scale, float beta_r, bf16_t *sKt, f32x4_t (&accQ)[NC],
+                                                 f32x4_t (&accK)[NC], bf16x4_t (&xw)[NS][2]) {
   using M = Mma<bf16_t>;
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
@@ -363,28 +335,46 @@ __device__ __forceinline__ void gram_row_partial(const bf16_t *sQ, const bf16_t 
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int kb = c0 + 32 * s + 4 * grp;  // slots e < 4: channel kb + e; e >= 4: kb + 16 + (e - 4)
-    f32x4_t br[2], bm[2], ba[2];
+    f32x4_t br[2], bm[2], ba[2], t1[2], t2[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       br[hh] = *reinterpret_cast<const f32x4_t *>(sB + rr * ldb + kb + 16 * hh);
       bm[hh] = *reinterpret_cast<const f32x4_t *>(sB + (16 * I + 8) * ldb + kb + 16 * hh);
       ba[hh] = *reinterpret_cast<const f32x4_t *>(sB + (16 * I) * ldb + kb + 16 * hh);
+      if (SAFE) {
+        t1[hh] = *reinterpret_cast<const f32x4_t *>(sT1 + I * D + kb + 16 * hh);
+        t2[hh] = *reinterpret_cast<const f32x4_t *>(sT2 + I * D + kb + 16 * hh);
+      } else {
+        t2[hh] = *reinterpret_cast<const f32x4_t *>(sBL + kb + 16 * hh);
+      }
     }
     const bf16x4_t q0 = *reinterpret_cast<const bf16x4_t *>(sQ + rr * ldt + kb);
     const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t *>(sQ + rr * ldt + kb + 16);
     const bf16x4_t k0 = *reinterpret_cast<const bf16x4_t *>(sK + rr * ldt + kb);
     const bf16x4_t k1 = *reinterpret_cast<const bf16x4_t *>(sK + rr * ldt + kb + 16);
-    bf16x8_t fqd, fkd, fqo, fko;
+    bf16x8_t fqd, fkd, fqo, fko, fcd;
+    bf16x4_t qt[2], kt[2];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int hh = e >> 2, ee = e & 3;
       const float qf = static_cast<float>(hh ? q1[ee] : q0[ee]);
       const float kf = static_cast<float>(hh ? k1[ee] : k0[ee]);
+      float E, El;  // 2^b and 2^(b_L - b) of this element
       if (SAFE) {
         const float ed = fast_exp2(br[hh][ee] - bm[hh][ee]);
+        const float ec = fast_exp2(bm[hh][ee] - br[hh][ee]);
         fqd[e] = static_cast<bf16_t>(qf * ed);
         fkd[e] = static_cast<bf16_t>(kf * ed);
+        fcd[e] = static_cast<bf16_t>(kf * ec);  // the diagonal block's column operand (same token)
+        E = ed * t1[hh][ee];
+        El = ec * t2[hh][ee];
+      } else {
+        E = fast_exp2(br[hh][ee]);
+        El = fast_exp2(t2[hh][ee] - br[hh][ee]);
       }
+      qt[hh][ee] = static_cast<bf16_t>(scale * qf * E);
+      xw[s][hh][ee] = static_cast<bf16_t>(beta_r * kf * E);
+      kt[hh][ee] = static_cast<bf16_t>(kf * El);
       if (I > 0) {
         const float eo = fast_exp2(br[hh][ee] - ba[hh][ee]);
         fqo[e] = static_cast<bf16_t>(qf * eo);
@@ -392,8 +382,16 @@ __device__ __forceinline__ void gram_row_partial(const bf16_t *sQ, const bf16_t 
       }
     }
 #pragma unroll
-    for (int j = 0; j <= I; ++j) {
-      if (!SAFE && j == I) continue;
+    for (int hh = 0; hh < 2; ++hh) {
+      *reinterpret_cast<bf16x4_t *>(sQ + rr * ldt + kb + 16 * hh) = qt[hh];
+      *reinterpret_cast<bf16x4_t *>(sKt + rr * ldt + kb + 16 * hh) = kt[hh];
+    }
+    if (SAFE) {
+      accQ[I] = M::mma(fcd, fqd, accQ[I]);
+      accK[I] = M::mma(fcd, fkd, accK[I]);
+    }
+#pragma unroll
+    for (int j = 0; j < I; ++j) {
       const int cs = 16 * j + n16;
       const bf16x4_t c0v = *reinterpret_cast<const bf16x4_t *>(sK + cs * ldt + kb);
       const bf16x4_t c1v = *reinterpret_cast<const bf16x4_t *>(sK + cs * ldt + kb + 16);
@@ -401,22 +399,16 @@ __device__ __forceinline__ void gram_row_partial(const bf16_t *sQ, const bf16_t 
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const f32x4_t bc = *reinterpret_cast<const f32x4_t *>(sB + cs * ldb + kb + 16 * hh);
-        const f32x4_t anc = (j == I) ? bm[hh] : ba[hh];
 #pragma unroll
         for (int ee = 0; ee < 4; ++ee) {
           const float kf = static_cast<float>(hh ? c1v[ee] : c0v[ee]);
-          fc[4 * hh + ee] = static_cast<bf16_t>(kf * fast_exp2(anc[ee] - bc[ee]));
+          fc[4 * hh + ee] = static_cast<bf16_t>(kf * fast_exp2(ba[hh][ee] - bc[ee]));
         }
       }
       // column operand first: the accumulator holds the block transposed, so
       // lane (row n16, group g) gets A[16I + n16][16j + 4g .. 16j + 4g + 3]
-      if (j == I) {
-        accQ[j] = M::mma(fc, fqd, accQ[j]);
-        accK[j] = M::mma(fc, fkd, accK[j]);
-      } else {
-        accQ[j] = M::mma(fc, fqo, accQ[j]);
-        accK[j] = M::mma(fc, fko, accK[j]);
-      }
+      accQ[j] = M::mma(fc, fqo, accQ[j]);
+      accK[j] = M::mma(fc, fko, accK[j]);
     }
   }
 }
@@ -476,10 +468,13 @@ __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)
 
 // A_kk comes out fp32 in sAkk; A_qk comes out bf16 in sAqh (row stride ldh),
 // with sAqk (fp32) holding the second channel half's partial sums meanwhile.
+// Besides the grams, writes q~ over q, k~ into sKt and X_w = beta k 2^b into
+// sXw (which may overlap sB: it is written after a barrier).
 template <int NT, int C, int D, bool SAFE>
-__device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
+__device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                             const float *sBeta, float scale, float *sAkk, float *sAqk, int lda,
-                                            bf16_t *sAqh, int ldh, int L) {
+                                            bf16_t *sAqh, int ldh, int L, const float *sT1, const float *sT2,
+                                            const float *sBL, bf16_t *sKt, bf16_t *sXw) {
   constexpr int NW = NT / 64, NC = C / 16;
   constexpr int HS = (NW / NC >= 2) ? 2 : 1, CW = D / HS, NS = CW / 32;
   static_assert(NW >= NC && CW % 32 == 0, "wave split of the grams");
@@ -497,6 +492,9 @@ __device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, 
   }
   const bool active = i < NC;
   const int c0 = hsel * CW;
+  const int r = 16 * i + n16;
+  const float beta_r = active ? sBeta[r] : 0.f;
+  bf16x4_t xw[NS][2];
 
   f32x4_t accQ[NC], accK[NC];
 #pragma unroll
@@ -505,20 +503,10 @@ __device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, 
     accK[j] = zero4();
   }
   if (active) {
-    switch (i) {
-      case 0: gram_row_partial<0, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, accQ, accK); break;
-      case 1: gram_row_partial<1, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, accQ, accK); break;
-      case 2:
-        if constexpr (NC > 2) gram_row_partial<2, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, accQ, accK);
-        break;
-      case 3:
-        if constexpr (NC > 3) gram_row_partial<3, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, accQ, accK);
-        break;
-    }
     if constexpr (!SAFE) {
-      // token-parallel diagonal block over this wave's channels, in the same
-      // transposed layout: lane owns row r = 16i + n16 and columns 16i + 4*grp + e
-      const int r = 16 * i + n16;
+      // token-parallel diagonal block over this wave's channels (before q is
+      // overwritten), in the transposed layout: lane owns row r = 16i + n16 and
+      // columns 16i + 4*grp + e
       for (int kk = c0; kk < c0 + CW; ++kk) {
         const float qr = static_cast<float>(sQ[r * ldt + kk]);
         const float kr = static_cast<float>(sK[r * ldt + kk]);
@@ -533,9 +521,31 @@ __device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, 
         }
       }
     }
+#define KDA_GRAM_ROW(II)                                                                                     \
+  gram_row_partial<II, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, sT1, sT2, sBL, D, scale, beta_r, sKt, accQ, accK, \
+                                     xw)
+    switch (i) {
+      case 0: KDA_GRAM_ROW(0); break;
+      case 1: KDA_GRAM_ROW(1); break;
+      case 2:
+        if constexpr (NC > 2) KDA_GRAM_ROW(2);
+        break;
+      case 3:
+        if constexpr (NC > 3) KDA_GRAM_ROW(3);
+        break;
+    }
+#undef KDA_GRAM_ROW
   }
-  const int r = 16 * i + n16;
-  const float beta_r = active ? sBeta[r] : 0.f;
+  // X_w over b once every wave is past its reads of b
+  auto store_xw = [&]() {
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          *reinterpret_cast<bf16x4_t *>(sXw + r * ldt + c0 + 32 * s + 4 * grp + 16 * hh) = xw[s][hh];
+    }
+  };
   auto finish = [&](bool doQ, bool doK, bool add, bool final) {
     switch (i) {
       case 0: gram_finish<0, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh); break;
@@ -556,12 +566,15 @@ __device__ __forceinline__ void grams_fused(const bf16_t *sQ, const bf16_t *sK, 
       else finish(false, true, false, false);
     }
     __syncthreads();
+    store_xw();
     if (active) {
       if (hsel == 0) finish(true, false, true, true);
       else finish(false, true, true, true);
     }
   } else {
     if (active) finish(true, true, false, true);
+    __syncthreads();
+    store_xw();
   }
 }
 
