@@ -51,7 +51,7 @@ def alg_flops_chunk(B, T, H, D, C=64):
     return B * T * H * per
 
 
-FUSED_SOURCES = ("chunk_fused.hip", "chunk_tiles.h", "kda_device.h", "kda_launch.h")
+FUSED_SOURCES = ("chunk_fused.hip", "chunk_fused_tiles.h", "chunk_tiles.h", "kda_device.h", "kda_launch.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_chunk_b4t4096h64d128_traffic.txt")
 
 
