@@ -153,6 +153,36 @@ def bench_decode(steps, warmup):
                 GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS, Mtokens_per_s=N / (t["median"] * 1e-3) / 1e6)
 
 
+SWEEP_SHAPES = [(1, 8192, 96, 128), (2, 16384, 16, 128), (4, 2048, 16, 128), (4, 4096, 64, 128),
+                   (8, 2048, 32, 256), (8, 1024, 8, 64)]
+
+
+def bench_shape(B, T, H, D, steps, warmup, schedule="auto", C=64):
+    """Flushed-cache HIP-event timing of kda_chunk_fwd on one synthetic shape (safe gate)."""
+    import kda_synth
+    from gated_delta_rule_gate_amd import chunk_kda
+
+    d = kda_synth.chunk_inputs(B, T, H, D, D, dtype=torch.bfloat16, seed=1002)
+    dev = {k: v.cuda() for k, v in d.items() if v is not None}
+    del d
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    flush_buf = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+
+    def step():
+        chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], dev["h0"], chunk_size=C, gate_kind="safe",
+                  A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0, schedule=schedule, out=o,
+                  final_state=ht)
+
+    t = event_time_ms(step, steps, warmup, flush=lambda: flush_buf.zero_())
+    ms = t["mean"]
+    nbytes = alg_bytes_chunk(B, T, H, D)
+    return {"shape": "B%d T%d H%d D%d" % (B, T, H, D), "ms": round(ms, 4),
+            "Mtokens_per_s": round(B * T / (ms * 1e-3) / 1e6, 3),
+            "roofline_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "schedule": "fused" if (schedule != "staged" and D <= 128) else "staged"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +194,7 @@ def main():
     ap.add_argument("--shape", default="4,4096,64,128", help="B,T,H,D")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--sweep", action="store_true", help="also time a sweep of six shapes")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -237,6 +268,10 @@ def main():
     }
     if not args.no_decode:
         line["recurrent_decode"] = bench_decode(max(10, args.steps), 3)
+    if args.sweep:
+        del dev, o, ht, flush_buf
+        torch.cuda.empty_cache()
+        line["shape_sweep"] = [bench_shape(*shp, steps=max(5, args.steps // 2), warmup=2) for shp in SWEEP_SHAPES]
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
         line["cpu_baseline"] = cpu_baseline(d, H, T, threads)

@@ -170,8 +170,8 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   using S = FusedSmem<C, D, NT>;
   constexpr bool SAFE = (GK == kGateSafe);
   constexpr int NW = NT / 64, NC = TL::NC, DT = TL::DT, LDT = TL::LDT, LDB = TL::LDB, LDA = TL::LDA;
-  constexpr int NVW = DT / NW;  // value tiles (and w column tiles) per wave
-  static_assert(DT % NW == 0 && NVW >= 1, "strip split");
+  constexpr int NVW = 1;  // value tiles (and w column tiles) per wave
+  static_assert(DT == NW, "one w column tile and at most one value tile per wave");
 
   extern __shared__ __align__(16) char smem[];
   Tin *sQ = reinterpret_cast<Tin *>(smem + S::q);    // q, then q~
@@ -194,10 +194,15 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   float *sDt = reinterpret_cast<float *>(smem + S::dt);
   float *sSeg = reinterpret_cast<float *>(smem + S::seg);
 
-  const int nh = blockIdx.x;
+  // workgroup = (sequence, head, block vb of D / vsplit value columns); waves
+  // below tpb own one 16-column tile of the state, all waves share the key side
+  const int vs = p.vsplit, tpb = DT / vs;
+  const int nh = blockIdx.x / vs, vb = blockIdx.x % vs;
   const int n = nh / p.H, h = nh % p.H;
   const int wid = wave_id();
-  const int col0 = wid * NVW * 16;
+  const bool owner = wid < tpb;
+  const int ctu = vb * tpb + wid;  // this wave's value tile (owners)
+  const int col0 = ctu * 16;
   const SlotRange sr = slot_range(p.cu, n, p.T);
   const int nch = (sr.len + C - 1) / C;
   const int64_t sbase = (int64_t)nh * D * D;
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   }
 
   f32x4_t hs[DT][NVW];
-  if (p.h0) {
+  if (p.h0 && owner) {
     load_strip<DT, NVW>(hs, p.h0 + sbase, D, col0, D);
   } else {
 #pragma unroll
@@ -257,36 +262,40 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     __syncthreads();
     // (4) this wave's column tiles of w (channels) and u (values)
     f32x4_t uv[NC][NVW];
-#pragma unroll
-    for (int v = 0; v < NVW; ++v) {
+    {
       f32x4_t W[NC], U[NC];
-      wy_subst2<C>(sXw, sV, LDT, wid * NVW + v, sBeta, sAkk, LDA, sTd, S::LDTD, W, U);
-      store_wT<C>(sWT, S::LDW, wid * NVW + v, W);
+      if (owner)
+        wy_subst2<C, true>(sXw, wid, sV, ctu, LDT, sBeta, sAkk, LDA, sTd, S::LDTD, W, U);
+      else
+        wy_subst2<C, false>(sXw, wid, sV, 0, LDT, sBeta, sAkk, LDA, sTd, S::LDTD, W, U);
+      store_wT<C>(sWT, S::LDW, wid, W);
 #pragma unroll
-      for (int i = 0; i < NC; ++i) uv[i][v] = U[i];
+      for (int i = 0; i < NC; ++i) uv[i][0] = U[i];
     }
     __syncthreads();
-    // (5) + (6)
-    f32x4_t p1[NC][NVW], o[NC][NVW];
+    // (5) + (6) on the waves that own a value tile
+    if (owner) {
+      f32x4_t p1[NC][NVW], o[NC][NVW];
 #pragma unroll
-    for (int i = 0; i < NC; ++i)
+      for (int i = 0; i < NC; ++i)
 #pragma unroll
-      for (int v = 0; v < NVW; ++v) {
-        p1[i][v] = zero4();
-        o[i][v] = zero4();
-      }
-    wq_times_state<C, D, NVW>(p1, o, sWT, S::LDW, sQ, LDT, hs);
+        for (int v = 0; v < NVW; ++v) {
+          p1[i][v] = zero4();
+          o[i][v] = zero4();
+        }
+      wq_times_state<C, D, NVW>(p1, o, sWT, S::LDW, sQ, LDT, hs);
 #pragma unroll
-    for (int i = 0; i < NC; ++i)
+      for (int i = 0; i < NC; ++i)
 #pragma unroll
-      for (int v = 0; v < NVW; ++v) uv[i][v] = uv[i][v] - p1[i][v];
-    causal_times_h<C, NVW>(o, sAqh, S::LDAH, uv);
-    state_update_kt<C, D, NVW>(hs, sKt, LDT, uv, sDecay);
-    // o from registers: four adjacent value columns per lane and row
-    store_oT<C, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, L, o);
+        for (int v = 0; v < NVW; ++v) uv[i][v] = uv[i][v] - p1[i][v];
+      causal_times_h<C, NVW>(o, sAqh, S::LDAH, uv);
+      state_update_kt<C, D, NVW>(hs, sKt, LDT, uv, sDecay);
+      // o from registers: four adjacent value columns per lane and row
+      store_oT<C, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, L, o);
+    }
     __syncthreads();
   }
-  if (p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, D, col0, D, hs);
+  if (owner && p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, D, col0, D, hs);
 }
 
 bool fused_supported(const ChunkParams &p) { return p.is_bf16 && (p.D == 64 || p.D == 128); }
@@ -303,14 +312,33 @@ hipError_t launch_fused_g(const ChunkParams &p, hipStream_t st) {
     (void)hipGetLastError();  // do not leave the error for the next launch to report
     return e;
   }
-  hipLaunchKernelGGL(kern, dim3(p.N * p.H), dim3(NT), smem, st, p);
+  hipLaunchKernelGGL(kern, dim3(p.N * p.H * p.vsplit), dim3(NT), smem, st, p);
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
 template <int C, int D>
-hipError_t launch_fused_t(const ChunkParams &p, hipStream_t st) {
+hipError_t launch_fused_t(const ChunkParams &p0, hipStream_t st) {
   constexpr int NT = (KDA_FUSED_THREADS > 0) ? KDA_FUSED_THREADS : ((D / 16 >= 8) ? 512 : 256);
-  if (p.N * p.H == 0) return hipSuccess;
+  if (p0.N * p0.H == 0) return hipSuccess;
+  // with fewer (sequence, head) pairs than compute units, split the value
+  // columns so that the workgroups still cover the chip
+  ChunkParams p = p0;
+  const int cus = device_cus();
+  p.vsplit = 1;
+  while (2 * p.vsplit <= D / 16 && (int64_t)p.N * p.H * 2 * p.vsplit <= cus) p.vsplit *= 2;
   switch (p.gate_kind) {
     case kGateSafe: return launch_fused_g<C, D, NT, kGateSafe>(p, st);
     case kGateSoftplus: return launch_fused_g<C, D, NT, kGateSoftplus>(p, st);

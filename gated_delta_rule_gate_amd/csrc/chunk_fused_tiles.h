@@ -114,16 +114,16 @@ __device__ __forceinline__ void diag_inverse(const float *sAkk, int lda, bf16_t 
 }
 
 // ---------------------------------------------------------------------------------------------
-// (4) One 16-column tile ct of W = (I + A_kk)^-1 X for two right-hand sides at
-// once (Xa, and Xb with rows scaled by rowscale[r]), by blocked forward
+// (4) A 16-column tile of W = (I + A_kk)^-1 X for one or two right-hand sides
+// (tile cta of Xa, and with TWO tile ctb of Xb with rows scaled by rowscale[r]), by blocked forward
 // substitution: R_i = X_i - sum_{j<i} A_ij W_j, W_i = T_ii R_i. X tiles are
 // row-major bf16; A_ij and T_ii are read once for both. W comes back as
 // C-layout accumulators, one per row block.
 // ---------------------------------------------------------------------------------------------
-template <int C>
-__device__ __forceinline__ void wy_subst2(const bf16_t *sXa, const bf16_t *sXb, int ldx, int ct, const float *rowscale,
-                                          const float *sAkk, int lda, const bf16_t *sTd, int ldt, f32x4_t (&Wa)[C / 16],
-                                          f32x4_t (&Wb)[C / 16]) {
+template <int C, bool TWO>
+__device__ __forceinline__ void wy_subst2(const bf16_t *sXa, int cta, const bf16_t *sXb, int ctb, int ldx,
+                                          const float *rowscale, const float *sAkk, int lda, const bf16_t *sTd,
+                                          int ldt, f32x4_t (&Wa)[C / 16], f32x4_t (&Wb)[C / 16]) {
   constexpr int NC = C / 16;
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
@@ -133,18 +133,21 @@ __device__ __forceinline__ void wy_subst2(const bf16_t *sXa, const bf16_t *sXb, 
   const float *rs = rowscale + 4 * grp;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    f32x4_t Ra = to_f32x4(load_cfrag_at(sXa + 16 * i * ldx + 16 * ct, lx));
-    f32x4_t Rb = to_f32x4(load_cfrag_at(sXb + 16 * i * ldx + 16 * ct, lx));
-    Rb = Rb * *reinterpret_cast<const f32x4_t *>(rs + 16 * i);
+    f32x4_t Ra = to_f32x4(load_cfrag_at(sXa + 16 * i * ldx + 16 * cta, lx));
+    f32x4_t Rb;
+    if (TWO) {
+      Rb = to_f32x4(load_cfrag_at(sXb + 16 * i * ldx + 16 * ctb, lx));
+      Rb = Rb * *reinterpret_cast<const f32x4_t *>(rs + 16 * i);
+    }
 #pragma unroll
     for (int j = 0; j < i; ++j) {
       const bf16x4_t a = to_bf16x4(-*reinterpret_cast<const f32x4_t *>(aRow + 16 * i * lda + 16 * j));
       Ra = mma16(a, to_bf16x4(Wa[j]), Ra);
-      Rb = mma16(a, to_bf16x4(Wb[j]), Rb);
+      if (TWO) Rb = mma16(a, to_bf16x4(Wb[j]), Rb);
     }
     const bf16x4_t t = *reinterpret_cast<const bf16x4_t *>(tRow + 16 * i * ldt);
     Wa[i] = mma16(t, to_bf16x4(Ra), zero4());
-    Wb[i] = mma16(t, to_bf16x4(Rb), zero4());
+    if (TWO) Wb[i] = mma16(t, to_bf16x4(Rb), zero4());
   }
 }
 

@@ -53,6 +53,7 @@ struct ChunkParams {
   bool is_bf16;
   int32_t *chunk_off;  // [N + 1] chunk prefix per slot (packed batches only)
   int max_chunks;      // upper bound of the number of chunks (grid size)
+  int vsplit;          // fused schedule: value-column blocks per (sequence, head), set by its launcher
   float *b, *Akk, *Aqk, *Tm, *w, *u, *vnew, *hc;
 };
 

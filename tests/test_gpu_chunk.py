@@ -224,6 +224,21 @@ def test_contract_shapes_sampled(shape):
     parity(got_h, ht_ref, "bf16", "ht")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("pairs", [144, 96, 48, 6])
+def test_value_column_split(D, pairs):
+    """The fused kernel splits the value columns over 1, 2, 4 or 8 workgroups per
+    (sequence, head) so that few pairs still cover 256 compute units: every split
+    checked in full, with an h0, a ragged tail and several chunks."""
+    need_gpu()
+    B = 3 if pairs % 3 == 0 else 2
+    d = make(B, 70, pairs // B, D, torch.bfloat16, 500 + pairs + D)
+    o, ht = gpu_run(d, "safe", "fused")
+    o_ref, ht_ref = oracle_run(d, "safe")
+    parity(o, o_ref, "bf16", "o")
+    parity(ht, ht_ref, "bf16", "ht")
+
+
 def test_config_varlen_softplus():
     """Packed capacity 16384, H16 D128, 10 slots (two empty), terminal offset 512 below
     capacity, non-safe softplus gate, h0 per slot; 4 sampled heads checked in full."""
