@@ -243,23 +243,20 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     else gate_cumsum<NT, C, D>(sB, LDB, sBL, sSeg);
     for (int i = tid_opaque(); i < D; i += NT) sDecay[i] = fast_exp2(sBL[i]);
     if constexpr (SAFE) {
-      // per row block and channel: 2^m_i and 2^(b_L - m_i), m_i the midpoint row
+      // per row block and channel: scale 2^a_i and 2^(b_L - a_i), a_i the block's first row
       for (int idx = tid_opaque(); idx < NC * D; idx += NT) {
         const int i = idx / D, ch = idx % D;
-        const float m = sB[(16 * i + 8) * LDB + ch];
-        sT1[idx] = fast_exp2(m);
-        sT2[idx] = fast_exp2(sBL[ch] - m);
+        const float a = sB[(16 * i) * LDB + ch];
+        sT1[idx] = p.scale * fast_exp2(a);
+        sT2[idx] = fast_exp2(sBL[ch] - a);
       }
       __syncthreads();
     }
-    // (2) the grams, and q~, k~, beta k 2^b
+    // (2) the grams, and q~, k~, beta k 2^b; (3) the diagonal inverses
     grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT1, sT2,
-                                sBL, sKt, sXw);
+                                sBL, sKt, sXw, sTd, S::LDTD);
     __syncthreads();
     if (more) regs.load_qkv(p, t0 + C, Ln, h);
-    // (3) diagonal inverses on the last wave
-    if (wid == NW - 1) diag_inverse<C>(sAkk, LDA, sTd, S::LDTD);
-    __syncthreads();
     // (4) this wave's column tiles of w (channels) and u (values)
     f32x4_t uv[NC][NVW];
     {

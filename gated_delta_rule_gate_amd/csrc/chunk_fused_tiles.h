@@ -51,10 +51,11 @@ __device__ __forceinline__ f32x4_t mma16(const bf16x4_t &a, const bf16x4_t &b, c
 }
 
 __device__ __forceinline__ bf16x4_t to_bf16x4(const f32x4_t &x) {
-  bf16x4_t r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = static_cast<bf16_t>(x[e]);
-  return r;
+  return __builtin_bit_cast(bf16x4_t, u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
+}
+
+__device__ __forceinline__ bf16x4_t pack_bf16x4(float a, float b, float c, float d) {
+  return __builtin_bit_cast(bf16x4_t, u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)});
 }
 
 __device__ __forceinline__ f32x4_t to_f32x4(const bf16x4_t &x) {
@@ -88,17 +89,12 @@ __device__ __forceinline__ bf16x8_t load_frag32(const bf16_t *M, int ld, int k0,
   return f;
 }
 
-// ---------------------------------------------------------------------------------------------
-// (3) the diagonal blocks T_ii = (I + A_ii)^-1, i < C/16, by forward
-// substitution in FP32 on one wave (lane = block i, column c), stored as
-// bf16 T_ii[r][c] with row stride ldt.
-// ---------------------------------------------------------------------------------------------
-template <int C>
-__device__ __forceinline__ void diag_inverse(const float *sAkk, int lda, bf16_t *sTd, int ldt) {
-  constexpr int NC = C / 16;
-  const int lane = tid_opaque() & 63;
-  if (lane >= 16 * NC) return;
-  const int i = lane >> 4, c = lane & 15;
+// (3) T_ii = (I + A_ii)^-1 of one 16 x 16 diagonal block by forward
+// substitution, one column per lane (lanes 0..15; the rest idle), written as
+// bf16 rows of sTd. -A_ii is read from sAkk (fp32, strictly lower, beta folded).
+__device__ __forceinline__ void diag_inverse_block(const float *sAkk, int lda, bf16_t *sTd, int ldt, int i) {
+  const int c = tid_opaque() & 63;
+  if (c >= 16) return;
   const float *A = sAkk + 16 * i * lda + 16 * i;
   float x[16];
 #pragma unroll
@@ -106,18 +102,20 @@ __device__ __forceinline__ void diag_inverse(const float *sAkk, int lda, bf16_t 
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
 #pragma unroll
-    for (int r = s + 1; r < 16; ++r) x[r] -= A[r * lda + s] * x[s];
+    for (int r = s + 1; r < 16; ++r) x[r] += A[r * lda + s] * x[s];
   }
   bf16_t *T = sTd + i * 16 * ldt;
 #pragma unroll
   for (int r = 0; r < 16; ++r) T[r * ldt + c] = static_cast<bf16_t>(x[r]);
 }
 
+
 // ---------------------------------------------------------------------------------------------
 // (4) A 16-column tile of W = (I + A_kk)^-1 X for one or two right-hand sides
 // (tile cta of Xa, and with TWO tile ctb of Xb with rows scaled by rowscale[r]), by blocked forward
-// substitution: R_i = X_i - sum_{j<i} A_ij W_j, W_i = T_ii R_i. X tiles are
-// row-major bf16; A_ij and T_ii are read once for both. W comes back as
+// substitution: R_i = X_i - sum_{j<i} A_ij W_j, W_i = T_ii R_i, with sAkk
+// holding -A_kk. X tiles are row-major bf16; A_ij and T_ii are read once for
+// both. W comes back as
 // C-layout accumulators, one per row block.
 // ---------------------------------------------------------------------------------------------
 template <int C, bool TWO>
@@ -141,7 +139,7 @@ __device__ __forceinline__ void wy_subst2(const bf16_t *sXa, int cta, const bf16
     }
 #pragma unroll
     for (int j = 0; j < i; ++j) {
-      const bf16x4_t a = to_bf16x4(-*reinterpret_cast<const f32x4_t *>(aRow + 16 * i * lda + 16 * j));
+      const bf16x4_t a = to_bf16x4(*reinterpret_cast<const f32x4_t *>(aRow + 16 * i * lda + 16 * j));
       Ra = mma16(a, to_bf16x4(Wa[j]), Ra);
       if (TWO) Rb = mma16(a, to_bf16x4(Wb[j]), Rb);
     }
@@ -307,25 +305,30 @@ namespace kda {
 // ---------------------------------------------------------------------------------------------
 // (2) grams for the fused kernel. Each wave owns one row block i of both grams
 // and a 1/HS share of the channels (HS = 1 or 2 waves per row block): it builds
-// the row operands of block i once -- q, k scaled by 2^(b_r - m_i) (midpoint
-// anchor, diagonal block) and by 2^(b_r - a_i) (first-row anchor a_i,
-// off-diagonal blocks) -- and the column operands k_s 2^(m_i - b_s)
-// (diagonal) and k_s 2^(a_i - b_s) (blocks j < i), so every exponent is a
-// midpoint or paired non-positive offset ("FLA KDA Skill", section "Safe gate
-// numerical note"). Non-safe gates take the diagonal block per pair (section
-// "Safe vs non-safe intra path"). Only causal blocks are formed ("[examples]
-// Read only the causal columns in chunk_fwd_A_diag_anchored", description).
-// With HS = 2 each half stores its scaled, masked partial sums of one matrix,
-// and after a barrier adds its own partial sums of the other and writes it.
+// the row operands of block i once -- q, k scaled by 2^(b_r - a_i), a_i the
+// block's first row -- and the column operands k_s 2^(a_i - b_s) of blocks
+// j <= i, so the row side never exceeds 1 and off-diagonal column exponents are
+// paired non-positive offsets ("FLA KDA Skill", section "Safe gate numerical
+// note"). The pages anchor the diagonal block at its midpoint to keep head room
+// below the FP32 exponent limit; the safe gate bounds one token's decay by
+// |lower_bound| <= 5, so the 15 steps from the first row reach at most
+// 2^(15 * 5 / ln 2) = 2^108 < 2^127 and the first-row anchor serves the diagonal
+// block too, with one exponential pair per element. Non-safe gates, unbounded,
+// take the diagonal block per pair (section "Safe vs non-safe intra path").
+// Only causal blocks are formed ("[examples] Read only the causal columns in
+// chunk_fwd_A_diag_anchored", description). With HS = 2 each half stores its
+// scaled, masked partial sums of one matrix, and after a barrier adds its own
+// partial sums of the other and writes it; the half that completes A_kk then
+// inverts the diagonal block T_ii from its own rows, with no further barrier.
 // ---------------------------------------------------------------------------------------------
 // Row block I of the grams over channels [c0, c0 + 32 NS), plus the chunk's
 // other operand tiles for the same (token, channel) elements:
 //   q~  = scale q 2^b      written over q (this wave alone reads these q)
 //   k~  = k 2^(b_L - b)    written to sKt
 //   X_w = beta k 2^b       returned in xw (written after the grams' barrier)
-// For the safe gate these reuse the midpoint exponentials: 2^b = 2^(b - m_I) T1
-// and 2^(b_L - b) = 2^(m_I - b) T2 with the per-channel tables T1 = 2^m_I,
-// T2 = 2^(b_L - m_I); other gates take them directly.
+// For the safe gate these reuse the anchored exponentials: scale 2^b =
+// 2^(b - a_I) T1 and 2^(b_L - b) = 2^(a_I - b) T2 with the per-channel tables
+// T1 = scale 2^a_I, T2 = 2^(b_L - a_I); other gates take them directly.
 template <int I, int NC, int NS, bool SAFE>
 __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                                  int c0, const float *sT1, const float *sT2, const float *sBL, int D,
@@ -335,14 +338,14 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
   const int rr = 16 * I + n16;
+  const float beta_over_scale = SAFE ? beta_r * __builtin_amdgcn_rcpf(scale) : 0.f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int kb = c0 + 32 * s + 4 * grp;  // slots e < 4: channel kb + e; e >= 4: kb + 16 + (e - 4)
-    f32x4_t br[2], bm[2], ba[2], t1[2], t2[2];
+    f32x4_t br[2], ba[2], t1[2], t2[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       br[hh] = *reinterpret_cast<const f32x4_t *>(sB + rr * ldb + kb + 16 * hh);
-      bm[hh] = *reinterpret_cast<const f32x4_t *>(sB + (16 * I + 8) * ldb + kb + 16 * hh);
       ba[hh] = *reinterpret_cast<const f32x4_t *>(sB + (16 * I) * ldb + kb + 16 * hh);
       if (SAFE) {
         t1[hh] = *reinterpret_cast<const f32x4_t *>(sT1 + I * D + kb + 16 * hh);
@@ -355,34 +358,47 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
     const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t *>(sQ + rr * ldt + kb + 16);
     const bf16x4_t k0 = *reinterpret_cast<const bf16x4_t *>(sK + rr * ldt + kb);
     const bf16x4_t k1 = *reinterpret_cast<const bf16x4_t *>(sK + rr * ldt + kb + 16);
-    bf16x8_t fqd, fkd, fqo, fko, fcd;
-    bf16x4_t qt[2], kt[2];
+    float vqo[8], vko[8], vkc[8], vqt[8], vxw[8], vkt[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int hh = e >> 2, ee = e & 3;
       const float qf = static_cast<float>(hh ? q1[ee] : q0[ee]);
       const float kf = static_cast<float>(hh ? k1[ee] : k0[ee]);
-      float E, El;  // 2^b and 2^(b_L - b) of this element
       if (SAFE) {
-        const float ed = fast_exp2(br[hh][ee] - bm[hh][ee]);
-        const float ec = fast_exp2(bm[hh][ee] - br[hh][ee]);
-        fqd[e] = static_cast<bf16_t>(qf * ed);
-        fkd[e] = static_cast<bf16_t>(kf * ed);
-        fcd[e] = static_cast<bf16_t>(kf * ec);  // the diagonal block's column operand (same token)
-        E = ed * t1[hh][ee];
-        El = ec * t2[hh][ee];
+        // one pair of exponentials per element: 2^(b - a_I) for the row
+        // operands, its inverse for the diagonal block's column operand
+        const float d = br[hh][ee] - ba[hh][ee];
+        const float eo = fast_exp2(d), ec = fast_exp2(-d);
+        vqo[e] = qf * eo;
+        vko[e] = kf * eo;
+        vkc[e] = kf * ec;
+        vqt[e] = vqo[e] * t1[hh][ee];                        // scale q 2^b
+        vxw[e] = vko[e] * (t1[hh][ee] * beta_over_scale);   // beta k 2^b
+        vkt[e] = vkc[e] * t2[hh][ee];                        // k 2^(b_L - b)
       } else {
-        E = fast_exp2(br[hh][ee]);
-        El = fast_exp2(t2[hh][ee] - br[hh][ee]);
+        const float E = fast_exp2(br[hh][ee]), El = fast_exp2(t2[hh][ee] - br[hh][ee]);
+        vqt[e] = scale * qf * E;
+        vxw[e] = beta_r * kf * E;
+        vkt[e] = kf * El;
+        if (I > 0) {
+          const float eo = fast_exp2(br[hh][ee] - ba[hh][ee]);
+          vqo[e] = qf * eo;
+          vko[e] = kf * eo;
+        } else {
+          vqo[e] = vko[e] = 0.f;
+        }
+        vkc[e] = 0.f;
       }
-      qt[hh][ee] = static_cast<bf16_t>(scale * qf * E);
-      xw[s][hh][ee] = static_cast<bf16_t>(beta_r * kf * E);
-      kt[hh][ee] = static_cast<bf16_t>(kf * El);
-      if (I > 0) {
-        const float eo = fast_exp2(br[hh][ee] - ba[hh][ee]);
-        fqo[e] = static_cast<bf16_t>(qf * eo);
-        fko[e] = static_cast<bf16_t>(kf * eo);
-      }
+    }
+    const bf16x8_t fqo = pack_bf16x8(vqo), fko = pack_bf16x8(vko);
+    bf16x8_t fcd;
+    if (SAFE) fcd = pack_bf16x8(vkc);
+    bf16x4_t qt[2], kt[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      qt[hh] = pack_bf16x4(vqt[4 * hh], vqt[4 * hh + 1], vqt[4 * hh + 2], vqt[4 * hh + 3]);
+      kt[hh] = pack_bf16x4(vkt[4 * hh], vkt[4 * hh + 1], vkt[4 * hh + 2], vkt[4 * hh + 3]);
+      xw[s][hh] = pack_bf16x4(vxw[4 * hh], vxw[4 * hh + 1], vxw[4 * hh + 2], vxw[4 * hh + 3]);
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -390,24 +406,25 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
       *reinterpret_cast<bf16x4_t *>(sKt + rr * ldt + kb + 16 * hh) = kt[hh];
     }
     if (SAFE) {
-      accQ[I] = M::mma(fcd, fqd, accQ[I]);
-      accK[I] = M::mma(fcd, fkd, accK[I]);
+      accQ[I] = M::mma(fcd, fqo, accQ[I]);
+      accK[I] = M::mma(fcd, fko, accK[I]);
     }
 #pragma unroll
     for (int j = 0; j < I; ++j) {
       const int cs = 16 * j + n16;
       const bf16x4_t c0v = *reinterpret_cast<const bf16x4_t *>(sK + cs * ldt + kb);
       const bf16x4_t c1v = *reinterpret_cast<const bf16x4_t *>(sK + cs * ldt + kb + 16);
-      bf16x8_t fc;
+      float vc[8];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const f32x4_t bc = *reinterpret_cast<const f32x4_t *>(sB + cs * ldb + kb + 16 * hh);
 #pragma unroll
         for (int ee = 0; ee < 4; ++ee) {
           const float kf = static_cast<float>(hh ? c1v[ee] : c0v[ee]);
-          fc[4 * hh + ee] = static_cast<bf16_t>(kf * fast_exp2(ba[hh][ee] - bc[ee]));
+          vc[4 * hh + ee] = kf * fast_exp2(ba[hh][ee] - bc[ee]);
         }
       }
+      const bf16x8_t fc = pack_bf16x8(vc);
       // column operand first: the accumulator holds the block transposed, so
       // lane (row n16, group g) gets A[16I + n16][16j + 4g .. 16j + 4g + 3]
       accQ[j] = M::mma(fc, fqo, accQ[j]);
@@ -420,7 +437,7 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
 // lane holds A[r = 16I + n16][16j + 4g .. 16j + 4g + 3]. doQ / doK select
 // A_qk / A_kk. With add, the other channel half's partial sums (A_qk in sAqk,
 // A_kk in sAkk) are added first. Final A_qk goes to sAqh as bf16, partial
-// A_qk to sAqk; A_kk always to sAkk.
+// A_qk to sAqk; -A_kk (partial or final) always to sAkk.
 template <int I, int NC>
 __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)[NC], bool doQ, bool doK, bool add,
                                             bool final, int r, int L, float scale, float beta_r, float *sAkk,
@@ -437,7 +454,7 @@ __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)
   const bool row_ok = r < L;
 #pragma unroll
   for (int j = 0; j <= I; ++j) {
-    f32x4_t aq = accQ[j] * scale, ak = accK[j] * beta_r;
+    f32x4_t aq = accQ[j] * scale, ak = accK[j] * (-beta_r);
     if (j == I) {  // diagonal block: causal masks inside the block
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -446,7 +463,7 @@ __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)
         ak[e] = (sj < r) ? ak[e] : 0.f;
       }
     }
-    if (!row_ok) {
+    if (L < 16 * NC && !row_ok) {
       aq = zero4();
       ak = zero4();
     }
@@ -469,15 +486,17 @@ __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)
   }
 }
 
-// A_kk comes out fp32 in sAkk; A_qk comes out bf16 in sAqh (row stride ldh),
-// with sAqk (fp32) holding the second channel half's partial sums meanwhile.
+// -A_kk comes out fp32 in sAkk (negated: the substitution subtracts it);
+// A_qk comes out bf16 in sAqh (row stride ldh), with sAqk (fp32) holding the
+// second channel half's partial sums meanwhile.
 // Besides the grams, writes q~ over q, k~ into sKt and X_w = beta k 2^b into
 // sXw (which may overlap sB: it is written after a barrier).
 template <int NT, int C, int D, bool SAFE>
 __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                             const float *sBeta, float scale, float *sAkk, float *sAqk, int lda,
                                             bf16_t *sAqh, int ldh, int L, const float *sT1, const float *sT2,
-                                            const float *sBL, bf16_t *sKt, bf16_t *sXw) {
+                                            const float *sBL, bf16_t *sKt, bf16_t *sXw, bf16_t *sTd,
+                                            int ldtd) {
   constexpr int NW = NT / 64, NC = C / 16;
   constexpr int HS = (NW / NC >= 2) ? 2 : 1, CW = D / HS, NS = CW / 32;
   static_assert(NW >= NC && CW % 32 == 0, "wave split of the grams");
@@ -571,11 +590,20 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
     __syncthreads();
     store_xw();
     if (active) {
-      if (hsel == 0) finish(true, false, true, true);
-      else finish(false, true, true, true);
+      if (hsel == 0) {
+        finish(true, false, true, true);
+      } else {
+        finish(false, true, true, true);
+        lds_wave_order();  // this wave's A_kk rows are read back across lanes
+        diag_inverse_block(sAkk, lda, sTd, ldtd, i);
+      }
     }
   } else {
-    if (active) finish(true, true, false, true);
+    if (active) {
+      finish(true, true, false, true);
+      lds_wave_order();
+      diag_inverse_block(sAkk, lda, sTd, ldtd, i);
+    }
     __syncthreads();
     store_xw();
   }

@@ -66,11 +66,9 @@ template <typename Tin, int NT_>
 __device__ __forceinline__ typename Mma<Tin>::frag_t acc_frag(const f32x4_t (&tiles)[NT_], int s) {
   typename Mma<Tin>::frag_t f;
   if constexpr (std::is_same<Tin, bf16_t>::value) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[e] = static_cast<bf16_t>(tiles[2 * s][e]);
-      f[e + 4] = static_cast<bf16_t>(tiles[2 * s + 1][e]);
-    }
+    const f32x4_t &a = tiles[2 * s], &b = tiles[2 * s + 1];
+    f = __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                             pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])});
   } else {
     f = tiles[s >> 2][s & 3];
   }
@@ -610,13 +608,8 @@ __device__ __forceinline__ void store_rows_from_f32(T *g, int64_t ldg, const flo
       if constexpr (EPV == 8) {
         const f32x4_t a = *reinterpret_cast<const f32x4_t *>(s + r * lds + c);
         const f32x4_t b = *reinterpret_cast<const f32x4_t *>(s + r * lds + c + 4);
-        bf16x8_t o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[e] = static_cast<bf16_t>(a[e]);
-          o[e + 4] = static_cast<bf16_t>(b[e]);
-        }
-        *reinterpret_cast<bf16x8_t *>(g + (int64_t)r * ldg + c) = o;
+        *reinterpret_cast<u32x4_t *>(g + (int64_t)r * ldg + c) =
+            u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
       } else {
         *reinterpret_cast<f32x4_t *>(g + (int64_t)r * ldg + c) = *reinterpret_cast<const f32x4_t *>(s + r * lds + c);
       }

@@ -32,6 +32,22 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return static_cast<bf16_t>(x); }
 
+// Two floats rounded to nearest-even bf16 in one dword (lo in bits 0..15):
+// one v_cvt_pk_bf16_f32. Vectors that feed a matrix instruction are built
+// from these dwords; assembled element by element, the compiler converts each
+// element on its own and merges the halves with extra permutes.
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ bf16x8_t pack_bf16x8(const float (&x)[8]) {
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                              pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])});
+}
+
 // threadIdx.x behind an empty volatile asm: values derived from it cannot be
 // hoisted out of loops, so per-thread LDS/global addresses are recomputed
 // where they are used instead of being held in registers across a whole loop
@@ -88,6 +104,15 @@ __device__ __forceinline__ float gate_log2(int kind, float x, float dt, float ex
 // iteration are consumed, so the wait never depends on the compiler's
 // tracking of loop-carried loads.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Lets one wave read back, from other lanes, what it has just written to LDS:
+// the LDS unit completes one wave's instructions in issue order, so it only
+// keeps the compiler from moving LDS accesses across this point.
+__device__ __forceinline__ void lds_wave_order() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------------------------
 // Slot / chunk location for packed (cu_seqlens) and dense batches.
