@@ -56,8 +56,8 @@ struct FusedSmem {
   static constexpr int LDAH = C + 8;    // A_qk [C][LDAH] bf16
   static constexpr size_t aqh = aqk + 4 * C * LDA;
   static constexpr size_t td = aqh + 2 * C * LDAH;
-  static constexpr size_t t1 = td + 2 * C * LDTD;     // 2^m_i per row block and channel, fp32 [C/16][D]
-  static constexpr size_t t2 = t1 + 4 * (C / 16) * D;  // 2^(b_L - m_i)
+  static constexpr size_t t1 = td + 2 * C * LDTD;     // scale 2^a_i per row block and channel, fp32 [C/16][D]
+  static constexpr size_t t2 = t1 + 4 * (C / 16) * D;  // 2^(b_L - a_i)
   static constexpr size_t beta = t2 + 4 * (C / 16) * D;
   static constexpr size_t bl = beta + 4 * C;
   static constexpr size_t decay = bl + 4 * D;
@@ -174,25 +174,33 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   static_assert(DT == NW, "one w column tile and at most one value tile per wave");
 
   extern __shared__ __align__(16) char smem[];
+  // buffers below 64 KB at constant offsets; the others from three opaque bases
+  char *baseB = lds_base(smem, S::b), *baseA = lds_base(smem, S::akk), *baseT = lds_base(smem, S::t1);
+  static_assert(S::b % 16 == 0 && S::wt_off % 16 == 0 && S::akk % 16 == 0 && S::kt % 16 == 0 && S::aqk % 16 == 0 &&
+                    S::aqh % 16 == 0 && S::td % 16 == 0 && S::t1 % 16 == 0 && S::t2 % 16 == 0 && S::beta % 16 == 0 &&
+                    S::bl % 16 == 0 && S::decay % 16 == 0 && S::dt % 16 == 0 && S::seg % 16 == 0,
+                "16-byte aligned buffers");
+  static_assert( S::td + 2 * C * S::LDTD - S::akk <= 65536 &&
+                    S::total - S::t1 <= 65536 && S::v + S::tile <= 65536,
+                "DS immediate offsets below 64 KB");
   Tin *sQ = reinterpret_cast<Tin *>(smem + S::q);    // q, then q~
   Tin *sK = reinterpret_cast<Tin *>(smem + S::k);    // k, then beta k 2^b
   Tin *sV = reinterpret_cast<Tin *>(smem + S::v);
-  float *sB = reinterpret_cast<float *>(smem + S::b);            // gate, then b
+  float *sB = reinterpret_cast<float *>(smem + S::b);             // gate, then b
   Tin *sXw = reinterpret_cast<Tin *>(smem + S::b + S::xw_off);  // beta k 2^b once b is consumed
-  Tin *sWT = reinterpret_cast<Tin *>(smem + S::b + S::wt_off);  // w^T
-  float *sT1 = reinterpret_cast<float *>(smem + S::t1);
-  float *sT2 = reinterpret_cast<float *>(smem + S::t2);
-  float *sAkk = reinterpret_cast<float *>(smem + S::akk);
-  Tin *sKt = reinterpret_cast<Tin *>(smem + S::kt);
-  float *sAqk = reinterpret_cast<float *>(smem + S::aqk);  // partial sums of A_qk
-  Tin *sAqh = reinterpret_cast<Tin *>(smem + S::aqh);      // A_qk
-
-  Tin *sTd = reinterpret_cast<Tin *>(smem + S::td);
-  float *sBeta = reinterpret_cast<float *>(smem + S::beta);
-  float *sBL = reinterpret_cast<float *>(smem + S::bl);
-  float *sDecay = reinterpret_cast<float *>(smem + S::decay);
-  float *sDt = reinterpret_cast<float *>(smem + S::dt);
-  float *sSeg = reinterpret_cast<float *>(smem + S::seg);
+  Tin *sWT = reinterpret_cast<Tin *>(baseB + S::wt_off);        // w^T
+  float *sAkk = reinterpret_cast<float *>(baseA);
+  Tin *sKt = reinterpret_cast<Tin *>(baseA + (S::kt - S::akk));
+  float *sAqk = reinterpret_cast<float *>(baseA + (S::aqk - S::akk));  // partial sums of A_qk
+  Tin *sAqh = reinterpret_cast<Tin *>(baseA + (S::aqh - S::akk));      // A_qk
+  Tin *sTd = reinterpret_cast<Tin *>(baseA + (S::td - S::akk));
+  float *sT1 = reinterpret_cast<float *>(baseT);
+  float *sT2 = reinterpret_cast<float *>(baseT + (S::t2 - S::t1));
+  float *sBeta = reinterpret_cast<float *>(baseT + (S::beta - S::t1));
+  float *sBL = reinterpret_cast<float *>(baseT + (S::bl - S::t1));
+  float *sDecay = reinterpret_cast<float *>(baseT + (S::decay - S::t1));
+  float *sDt = reinterpret_cast<float *>(baseT + (S::dt - S::t1));
+  float *sSeg = reinterpret_cast<float *>(baseT + (S::seg - S::t1));
 
   // workgroup = (sequence, head, block vb of D / vsplit value columns); waves
   // below tpb own one 16-column tile of the state, all waves share the key side

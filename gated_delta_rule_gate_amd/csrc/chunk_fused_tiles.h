@@ -95,14 +95,18 @@ __device__ __forceinline__ bf16x8_t load_frag32(const bf16_t *M, int ld, int k0,
 __device__ __forceinline__ void diag_inverse_block(const float *sAkk, int lda, bf16_t *sTd, int ldt, int i) {
   const int c = tid_opaque() & 63;
   if (c >= 16) return;
-  const float *A = sAkk + 16 * i * lda + 16 * i;
+  // rows read as 16-byte vectors (lda % 4 == 0); lane >> 4 is 0 here, and as an
+  // opaque per-lane term it keeps the addresses in one VGPR with immediate
+  // offsets instead of a scalar add and a move per row
+  const f32x4_t *A4 = reinterpret_cast<const f32x4_t *>(sAkk + 16 * i * lda + 16 * i) + ((tid_opaque() & 63) >> 4);
+  const int ld4 = lda / 4;
   float x[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
 #pragma unroll
-    for (int r = s + 1; r < 16; ++r) x[r] += A[r * lda + s] * x[s];
+    for (int r = s + 1; r < 16; ++r) x[r] += A4[r * ld4 + s / 4][s % 4] * x[s];
   }
   bf16_t *T = sTd + i * 16 * ldt;
 #pragma unroll

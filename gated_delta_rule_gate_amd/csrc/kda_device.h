@@ -105,6 +105,15 @@ __device__ __forceinline__ float gate_log2(int kind, float x, float dt, float ex
 // tracking of loop-carried loads.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// An LDS address the compiler cannot see as a constant. The DS offset field
+// holds 16 bits: with a buffer at a known offset beyond 64 KB, every access
+// would pay its own address add; from an opaque base (one SGPR) the lane part
+// is added once and the tile offsets stay immediates.
+__device__ __forceinline__ char *lds_base(char *smem, unsigned off) {
+  asm volatile("" : "+s"(off));
+  return static_cast<char *>(__builtin_assume_aligned(smem + off, 16));  // every buffer offset is a multiple of 16
+}
+
 // Lets one wave read back, from other lanes, what it has just written to LDS:
 // the LDS unit completes one wave's instructions in issue order, so it only
 // keeps the compiler from moving LDS accesses across this point.
