@@ -247,18 +247,11 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     if (more) regs.load_gate(p, t0 + C, Ln, h);
 
     // (1)
-    if constexpr (GK == kGateLog2Cumsum) gate_pad<NT, C, D>(sB, LDB, sBL, L);
-    else gate_cumsum<NT, C, D>(sB, LDB, sBL, sSeg);
-    for (int i = tid_opaque(); i < D; i += NT) sDecay[i] = fast_exp2(sBL[i]);
-    if constexpr (SAFE) {
-      // per row block and channel: scale 2^a_i and 2^(b_L - a_i), a_i the block's first row
-      for (int idx = tid_opaque(); idx < NC * D; idx += NT) {
-        const int i = idx / D, ch = idx % D;
-        const float a = sB[(16 * i) * LDB + ch];
-        sT1[idx] = p.scale * fast_exp2(a);
-        sT2[idx] = fast_exp2(sBL[ch] - a);
-      }
-      __syncthreads();
+    if constexpr (GK == kGateLog2Cumsum) {
+      gate_pad<NT, C, D>(sB, LDB, sBL, L);
+      for (int i = tid_opaque(); i < D; i += NT) sDecay[i] = fast_exp2(sBL[i]);  // read after later barriers
+    } else {
+      gate_cumsum_tables<NT, C, D, SAFE>(sB, LDB, sBL, sSeg, sDecay, sT1, sT2, p.scale);
     }
     // (2) the grams, and q~, k~, beta k 2^b; (3) the diagonal inverses
     grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT1, sT2,

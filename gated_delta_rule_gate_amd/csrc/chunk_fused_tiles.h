@@ -89,6 +89,60 @@ __device__ __forceinline__ bf16x8_t load_frag32(const bf16_t *M, int ld, int k0,
   return f;
 }
 
+// (1) The chunk-local cumsum b of the gate rows in sB (fp32, base 2, in place),
+// with b_L in sBL, the chunk decay 2^b_L in sDecay and, for the safe gate, the
+// anchor tables sT1 = scale 2^a_i and sT2 = 2^(b_L - a_i) of each 16-row block
+// (a_i = b at the block's first row): each thread scans RPS consecutive rows of
+// one channel, so segment starts that are block starts hold a_i after the
+// segment offsets are added. Ends with a barrier.
+template <int NT, int C, int D, bool SAFE>
+__device__ __forceinline__ void gate_cumsum_tables(float *sB, int ldb, float *sBL, float *sSeg, float *sDecay,
+                                                   float *sT1, float *sT2, float scale) {
+  static_assert(NT % D == 0, "thread mapping: whole channels per thread group");
+  constexpr int TPC = NT / D;  // threads per channel, each owning RPS consecutive rows
+  constexpr int RPS = C / TPC;
+  static_assert(RPS % 16 == 0 || 16 % RPS == 0, "segments and 16-row blocks nest");
+  const int tid = tid_opaque(), col = tid % D, seg = tid / D;
+  float vals[RPS];
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) vals[i] = sB[(seg * RPS + i) * ldb + col];
+#pragma unroll
+  for (int i = 1; i < RPS; ++i) vals[i] += vals[i - 1];
+  float bl = vals[RPS - 1];
+  if constexpr (TPC > 1) {
+    sSeg[seg * D + col] = vals[RPS - 1];
+    __syncthreads();
+    float off = 0.f, off_last = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < TPC - 1; ++s2) {
+      const float t = sSeg[s2 * D + col];
+      if (s2 < seg) off += t;
+      off_last += t;
+    }
+    bl = sSeg[(TPC - 1) * D + col] + off_last;  // the last row's value, summed in the same order
+#pragma unroll
+    for (int i = 0; i < RPS; ++i) vals[i] += off;
+  }
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) sB[(seg * RPS + i) * ldb + col] = vals[i];
+  if (seg == 0) {
+    sBL[col] = bl;
+    sDecay[col] = fast_exp2(bl);
+  }
+  if constexpr (SAFE) {
+#pragma unroll
+    for (int m = 0; m < RPS; m += 16) {
+      const int row = seg * RPS + m;
+      if (row % 16 == 0) {
+        const float a = vals[m];
+        sT1[(row / 16) * D + col] = scale * fast_exp2(a);
+        sT2[(row / 16) * D + col] = fast_exp2(bl - a);
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // (3) T_ii = (I + A_ii)^-1 of one 16 x 16 diagonal block by forward
 // substitution, one column per lane (lanes 0..15; the rest idle), written as
 // bf16 rows of sTd. -A_ii is read from sAkk (fp32, strictly lower, beta folded).
