@@ -67,11 +67,20 @@ struct FusedSmem {
 };
 
 // One chunk's raw inputs held in registers between the HBM load and the LDS store.
-template <typename Tin, int C, int D, int NT>
+// q, k and v are loaded and stored by NL threads (loader index in [0, NL)):
+// all of them, or one wave of each pair 2m, 2m + 1 (the pair's first half of
+// the grams), which issues those loads while the other inverts a diagonal
+// block. The gate input and beta use every thread.
+template <typename Tin, int C, int D, int NT, int NL>
 struct ChunkRegs {
   static constexpr int EPV = 16 / (int)sizeof(Tin);
-  static constexpr int VPR = D / EPV, NVT = C * VPR, IT = (NVT + NT - 1) / NT;  // q, k, v tiles
+  static constexpr int VPR = D / EPV, NVT = C * VPR, IT = (NVT + NL - 1) / NL;  // q, k, v tiles
   static constexpr int XPR = D / 4, NVX = C * XPR, IX = (NVX + NT - 1) / NT;    // gate tile (fp32)
+  // the q/k/v loader index of this thread (valid on loader waves)
+  static __device__ __forceinline__ unsigned loader_index() {
+    const unsigned t = (unsigned)tid_opaque();
+    return (NL == NT) ? t : (((t >> 7) << 6) | (t & 63));
+  }
   u32x4_t q[IT], k[IT], v[IT];
   f32x4_t x[IX];
   float beta;
@@ -79,11 +88,6 @@ struct ChunkRegs {
   // The chunk's first element is a uniform base pointer; each vector is a
   // 32-bit unsigned element offset from it, so the loads take the
   // scalar-base + vector-offset form.
-  __device__ __forceinline__ void load(const ChunkParams &p, int64_t t0, int L, int h) {
-    load_gate(p, t0, L, h);
-    load_qkv(p, t0, L, h);
-  }
-
   // q, k, v of the chunk at t0
   __device__ __forceinline__ void load_qkv(const ChunkParams &p, int64_t t0, int L, int h) {
     const unsigned ld = (unsigned)p.H * D;
@@ -93,9 +97,9 @@ struct ChunkRegs {
     const Tin *gv = reinterpret_cast<const Tin *>(p.v) + base;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const unsigned idx = it * NT + (unsigned)tid_opaque();
+      const unsigned idx = it * NL + loader_index();
       const int r = idx / VPR, c = (idx % VPR) * EPV;
-      const bool ok = (NVT % NT == 0 || idx < NVT) && r < L;
+      const bool ok = (NVT % NL == 0 || idx < NVT) && r < L;
       const unsigned off = (unsigned)r * ld + (unsigned)c;
       const u32x4_t z = {0u, 0u, 0u, 0u};
       q[it] = ok ? *reinterpret_cast<const u32x4_t *>(gq + off) : z;
@@ -125,15 +129,16 @@ struct ChunkRegs {
   // For the safe gate sDt holds dt_bias * c1 with c1 = -exp(A_log) log2(e),
   // so the sigmoid's exponent is one fma.
   template <int GK>
-  __device__ __forceinline__ void store(Tin *sQ, Tin *sK, Tin *sV, float *sB, float *sBeta, const float *sDt, int L,
-                                        float expA, float lower_bound) const {
+  __device__ __forceinline__ void store(bool loader, Tin *sQ, Tin *sK, Tin *sV, float *sB, float *sBeta,
+                                        const float *sDt, int L, float expA, float lower_bound) const {
     using TL = Tile<Tin, C, D>;
     wait_vmem();
+    if (loader)
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const unsigned idx = it * NT + (unsigned)tid_opaque();
+      const unsigned idx = it * NL + loader_index();
       const unsigned r = idx / VPR, c = (idx % VPR) * EPV;
-      if (NVT % NT == 0 || idx < NVT) {
+      if (NVT % NL == 0 || idx < NVT) {
         *reinterpret_cast<u32x4_t *>(sQ + r * TL::LDT + c) = q[it];
         *reinterpret_cast<u32x4_t *>(sK + r * TL::LDT + c) = k[it];
         *reinterpret_cast<u32x4_t *>(sV + r * TL::LDT + c) = v[it];
@@ -231,15 +236,23 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
       for (int v = 0; v < NVW; ++v) hs[t][v] = zero4();
   }
 
-  ChunkRegs<Tin, C, D, NT> regs;
-  if (nch > 0) regs.load(p, sr.t0, min(C, sr.len), h);
+  // with two waves per row block of the grams, the even waves load the next
+  // chunk's q, k, v while the odd ones invert the diagonal blocks
+  constexpr bool HALF_LOAD = (NW / NC >= 2);
+  constexpr int NL = HALF_LOAD ? NT / 2 : NT;
+  const bool loader = !HALF_LOAD || gram_half<NW, NC>(wid) == 0;
+  ChunkRegs<Tin, C, D, NT, NL> regs;
+  if (nch > 0) {
+    regs.load_gate(p, sr.t0, min(C, sr.len), h);
+    if (loader) regs.load_qkv(p, sr.t0, min(C, sr.len), h);
+  }
   __syncthreads();  // sDt visible
 
   for (int c = 0; c < nch; ++c) {
     const int64_t t0 = sr.t0 + (int64_t)c * C;
     const int L = min(C, sr.len - c * C);
     const int64_t off = t0 * ld + h * D;
-    regs.template store<GK>(sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound);
+    regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound);
     __syncthreads();
     // the next chunk's inputs are loaded in two parts while this chunk computes
     const bool more = c + 1 < nch;
@@ -254,10 +267,18 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
       gate_cumsum_tables<NT, C, D, SAFE>(sB, LDB, sBL, sSeg, sDecay, sT1, sT2, p.scale);
     }
     // (2) the grams, and q~, k~, beta k 2^b; (3) the diagonal inverses
-    grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT1, sT2,
-                                sBL, sKt, sXw, sTd, S::LDTD);
+    auto load_next = [&]() {
+      if (more) regs.load_qkv(p, t0 + C, Ln, h);
+    };
+    auto none = []() {};
+    if constexpr (HALF_LOAD)
+      grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT1, sT2,
+                                  sBL, sKt, sXw, sTd, S::LDTD, load_next);
+    else
+      grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT1, sT2,
+                                  sBL, sKt, sXw, sTd, S::LDTD, none);
     __syncthreads();
-    if (more) regs.load_qkv(p, t0 + C, Ln, h);
+    if (!HALF_LOAD && more) regs.load_qkv(p, t0 + C, Ln, h);
     // (4) this wave's column tiles of w (channels) and u (values)
     f32x4_t uv[NC][NVW];
     {

@@ -548,13 +548,23 @@ __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)
 // A_qk comes out bf16 in sAqh (row stride ldh), with sAqk (fp32) holding the
 // second channel half's partial sums meanwhile.
 // Besides the grams, writes q~ over q, k~ into sKt and X_w = beta k 2^b into
-// sXw (which may overlap sB: it is written after a barrier).
-template <int NT, int C, int D, bool SAFE>
+// sXw (which may overlap sB: it is written after a barrier). With two waves per
+// row block, the first of each pair calls idle() once its share is done.
+// The channel half of its row block that wave w takes in the grams. With 8
+// waves and 4 row blocks, the halves alternate so that each SIMD (waves w and
+// w + 4) holds one wave of either half.
+template <int NW, int NC>
+__device__ __forceinline__ int gram_half(int w) {
+  if constexpr (NW == 8 && NC == 4) return (w & 1) ^ (w >> 2);
+  else return w % ((NW / NC >= 2) ? 2 : 1);
+}
+
+template <int NT, int C, int D, bool SAFE, typename Idle>
 __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                             const float *sBeta, float scale, float *sAkk, float *sAqk, int lda,
                                             bf16_t *sAqh, int ldh, int L, const float *sT1, const float *sT2,
                                             const float *sBL, bf16_t *sKt, bf16_t *sXw, bf16_t *sTd,
-                                            int ldtd) {
+                                            int ldtd, Idle &&idle) {
   constexpr int NW = NT / 64, NC = C / 16;
   constexpr int HS = (NW / NC >= 2) ? 2 : 1, CW = D / HS, NS = CW / 32;
   static_assert(NW >= NC && CW % 32 == 0, "wave split of the grams");
@@ -562,14 +572,8 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
   const int n16 = lane & 15, grp = lane >> 4;
   // row block per wave; with 8 waves and 4 row blocks, blocks 0 and 3 (and 1
   // and 2) share a SIMD (waves w and w + 4), which evens out the per-SIMD work
-  int i, hsel;
-  if constexpr (NW == 8 && NC == 4) {
-    i = (w < 4) ? (w >> 1) : (3 - ((w - 4) >> 1));
-    hsel = w & 1;
-  } else {
-    i = w / HS;
-    hsel = w % HS;
-  }
+  const int i = (NW == 8 && NC == 4) ? ((w < 4) ? (w >> 1) : (3 - ((w - 4) >> 1))) : w / HS;
+  const int hsel = gram_half<NW, NC>(w);
   const bool active = i < NC;
   const int c0 = hsel * CW;
   const int r = 16 * i + n16;
@@ -647,14 +651,13 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
     }
     __syncthreads();
     store_xw();
-    if (active) {
-      if (hsel == 0) {
-        finish(true, false, true, true);
-      } else {
-        finish(false, true, true, true);
-        lds_wave_order();  // this wave's A_kk rows are read back across lanes
-        diag_inverse_block(sAkk, lda, sTd, ldtd, i);
-      }
+    if (hsel == 0) {
+      if (active) finish(true, false, true, true);
+      idle();  // while the other half inverts the diagonal blocks
+    } else if (active) {
+      finish(false, true, true, true);
+      lds_wave_order();  // this wave's A_kk rows are read back across lanes
+      diag_inverse_block(sAkk, lda, sTd, ldtd, i);
     }
   } else {
     if (active) {
