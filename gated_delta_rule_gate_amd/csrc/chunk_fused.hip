@@ -283,10 +283,11 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     f32x4_t uv[NC][NVW];
     {
       f32x4_t W[NC], U[NC];
-      if (owner)
+      if (owner) {
         wy_subst2<C, true>(sXw, wid, sV, ctu, LDT, sBeta, sAkk, LDA, sTd, S::LDTD, W, U);
-      else
+      } else {
         wy_subst2<C, false>(sXw, wid, sV, 0, LDT, sBeta, sAkk, LDA, sTd, S::LDTD, W, U);
+      }
       store_wT<C>(sWT, S::LDW, wid, W);
 #pragma unroll
       for (int i = 0; i < NC; ++i) uv[i][0] = U[i];
@@ -302,7 +303,8 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
           p1[i][v] = zero4();
           o[i][v] = zero4();
         }
-      wq_times_state<C, D, NVW>(p1, o, sWT, S::LDW, sQ, LDT, hs);
+      q_times_state<C, D, NVW>(o, sQ, LDT, hs);
+      w_times_state<C, D, NVW>(p1, sWT, S::LDW, hs);
 #pragma unroll
       for (int i = 0; i < NC; ++i)
 #pragma unroll

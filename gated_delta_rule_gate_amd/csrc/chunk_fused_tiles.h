@@ -225,15 +225,11 @@ __device__ __forceinline__ void store_wT(bf16_t *sWT, int ldw, int ct, const f32
 // chunk rows 16i + (lane % 16).
 // ---------------------------------------------------------------------------------------------
 template <int C, int D, int NVW>
-__device__ __forceinline__ void wq_times_state(f32x4_t (&p1)[C / 16][NVW], f32x4_t (&o)[C / 16][NVW],
-                                               const bf16_t *sWT, int ldw, const bf16_t *sQ, int ldt,
-                                               const f32x4_t (&h)[D / 16][NVW]) {
+__device__ __forceinline__ void w_times_state(f32x4_t (&p1)[C / 16][NVW], const bf16_t *sWT, int ldw,
+                                              const f32x4_t (&h)[D / 16][NVW]) {
   using M = Mma<bf16_t>;
   constexpr int NC = C / 16, DT = D / 16, SD = D / 32;
-  const int lane = tid_opaque() & 63;
-  const int n16 = lane & 15, grp = lane >> 4;
   const int lw = cfrag_lane_off(ldw);
-  const bf16_t *qRow = sQ + n16 * ldt + 4 * grp;
 #pragma unroll
   for (int s = 0; s < SD; ++s) {
     bf16x8_t fh[NVW];
@@ -247,25 +243,41 @@ __device__ __forceinline__ void wq_times_state(f32x4_t (&p1)[C / 16][NVW], f32x4
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const bf16x8_t fw = load_frag32_at(sWT + 32 * s * ldw + 16 * i, ldw, lw);
-      bf16x8_t fq;
-      const bf16x4_t q0 = *reinterpret_cast<const bf16x4_t *>(qRow + 16 * i * ldt + 32 * s);
-      const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t *>(qRow + 16 * i * ldt + 32 * s + 16);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        fq[e] = q0[e];
-        fq[e + 4] = q1[e];
-      }
-#pragma unroll
-      for (int v = 0; v < NVW; ++v) {
-        p1[i][v] = M::mma(fw, fh[v], p1[i][v]);
-        // o transposed: h^T (the same fragment) times q~^T, so a lane ends up
-        // with four adjacent value columns of one chunk row
-        o[i][v] = M::mma(fh[v], fq, o[i][v]);
-      }
+      for (int v = 0; v < NVW; ++v) p1[i][v] = M::mma(fw, fh[v], p1[i][v]);
     }
   }
 }
 
+// o += (q~ h) transposed: h^T (the h fragment as the A operand) times q~^T,
+// so a lane ends up with four adjacent value columns of one chunk row. Needs
+// only q~ and the incoming state, so it runs beside the WY substitution.
+template <int C, int D, int NVW>
+__device__ __forceinline__ void q_times_state(f32x4_t (&o)[C / 16][NVW], const bf16_t *sQ, int ldt,
+                                              const f32x4_t (&h)[D / 16][NVW]) {
+  using M = Mma<bf16_t>;
+  constexpr int NC = C / 16, DT = D / 16, SD = D / 32;
+  const int lane = tid_opaque() & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+  const bf16_t *qRow = sQ + n16 * ldt + 8 * grp;  // q~ in operand order: 8 per lane and 32-channel block
+#pragma unroll
+  for (int s = 0; s < SD; ++s) {
+    bf16x8_t fh[NVW];
+#pragma unroll
+    for (int v = 0; v < NVW; ++v) {
+      f32x4_t col[DT];
+#pragma unroll
+      for (int t = 0; t < DT; ++t) col[t] = h[t][v];
+      fh[v] = acc_frag<bf16_t, DT>(col, s);
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const bf16x8_t fq = *reinterpret_cast<const bf16x8_t *>(qRow + 16 * i * ldt + 32 * s);
+#pragma unroll
+      for (int v = 0; v < NVW; ++v) o[i][v] = M::mma(fh[v], fq, o[i][v]);
+    }
+  }
+}
 // o^T += v_new^T A_qk^T with A_qk bf16 row-major [C][ldh] (causal blocks only);
 // o in the transposed layout of wq_times_state.
 template <int C, int NVW>
@@ -381,7 +393,8 @@ namespace kda {
 // ---------------------------------------------------------------------------------------------
 // Row block I of the grams over channels [c0, c0 + 32 NS), plus the chunk's
 // other operand tiles for the same (token, channel) elements:
-//   q~  = scale q 2^b      written over q (this wave alone reads these q)
+//   q~  = scale q 2^b      written over q (this wave alone reads these q), with
+//                          the channels of each 32-block in operand order
 //   k~  = k 2^(b_L - b)    written to sKt
 //   X_w = beta k 2^b       returned in xw (written after the grams' barrier)
 // For the safe gate these reuse the anchored exponentials: scale 2^b =
@@ -458,11 +471,14 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
       kt[hh] = pack_bf16x4(vkt[4 * hh], vkt[4 * hh + 1], vkt[4 * hh + 2], vkt[4 * hh + 3]);
       xw[s][hh] = pack_bf16x4(vxw[4 * hh], vxw[4 * hh + 1], vxw[4 * hh + 2], vxw[4 * hh + 3]);
     }
+    // q~ goes back in the operand order of the 16x16x32 product (the lane's
+    // channels kb..kb+3, kb+16..kb+19 side by side at c0 + 32 s + 8 grp), so
+    // the product with h reads it as one 16-byte vector; the raw q of this
+    // 32-channel block was read above by the same lanes
+    *reinterpret_cast<bf16x8_t *>(sQ + rr * ldt + c0 + 32 * s + 8 * grp) =
+        __builtin_shufflevector(qt[0], qt[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      *reinterpret_cast<bf16x4_t *>(sQ + rr * ldt + kb + 16 * hh) = qt[hh];
-      *reinterpret_cast<bf16x4_t *>(sKt + rr * ldt + kb + 16 * hh) = kt[hh];
-    }
+    for (int hh = 0; hh < 2; ++hh) *reinterpret_cast<bf16x4_t *>(sKt + rr * ldt + kb + 16 * hh) = kt[hh];
     if (SAFE) {
       accQ[I] = M::mma(fcd, fqo, accQ[I]);
       accK[I] = M::mma(fcd, fko, accK[I]);
