@@ -61,7 +61,7 @@ struct FusedSmem {
   static constexpr size_t beta = t2 + 4 * (C / 16) * D;
   static constexpr size_t bl = beta + 4 * C;
   static constexpr size_t decay = bl + 4 * D;
-  static constexpr size_t dt = decay + 4 * D;
+  static constexpr size_t dt = decay + 2 * 4 * D;  // decay: two chunks (the state update trails by one)
   static constexpr size_t seg = dt + 4 * D;
   static constexpr size_t total = seg + 4 * NT;
 };
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   float *sT2 = reinterpret_cast<float *>(baseT + (S::t2 - S::t1));
   float *sBeta = reinterpret_cast<float *>(baseT + (S::beta - S::t1));
   float *sBL = reinterpret_cast<float *>(baseT + (S::bl - S::t1));
-  float *sDecay = reinterpret_cast<float *>(baseT + (S::decay - S::t1));
+  float *sDecay2 = reinterpret_cast<float *>(baseT + (S::decay - S::t1));  // [2][D], by chunk parity
   float *sDt = reinterpret_cast<float *>(baseT + (S::dt - S::t1));
   float *sSeg = reinterpret_cast<float *>(baseT + (S::seg - S::t1));
 
@@ -246,13 +246,26 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     regs.load_gate(p, sr.t0, min(C, sr.len), h);
     if (loader) regs.load_qkv(p, sr.t0, min(C, sr.len), h);
   }
-  __syncthreads();  // sDt visible
+  // v_new of the previous chunk: its state update h <- Diag(2^b_L) h + k~^T v_new
+  // runs right after the next chunk's inputs are stored, beside their gate
+  // activation; before the first chunk it is the identity (v_new = 0, k~ = 0,
+  // decay 1)
+  bf16x8_t vprev[NC / 2][NVW];
+#pragma unroll
+  for (int s2 = 0; s2 < NC / 2; ++s2)
+#pragma unroll
+    for (int v = 0; v < NVW; ++v) vprev[s2][v] = bf16x8_t{};
+  for (int i = tid_opaque(); i < D; i += NT) sDecay2[D + i] = 1.f;
+  for (int i = tid_opaque(); i < C * LDT / 8; i += NT) reinterpret_cast<u32x4_t *>(sKt)[i] = u32x4_t{0u, 0u, 0u, 0u};
+  __syncthreads();  // sDt, the identity update's operands visible
 
   for (int c = 0; c < nch; ++c) {
     const int64_t t0 = sr.t0 + (int64_t)c * C;
     const int L = min(C, sr.len - c * C);
     const int64_t off = t0 * ld + h * D;
+    float *sDecay = sDecay2 + (c & 1) * D;
     regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound);
+    state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((c + 1) & 1) * D);  // chunk c - 1's
     __syncthreads();
     // the next chunk's inputs are loaded in two parts while this chunk computes
     const bool more = c + 1 < nch;
@@ -310,12 +323,13 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int v = 0; v < NVW; ++v) uv[i][v] = uv[i][v] - p1[i][v];
       causal_times_h<C, NVW>(o, sAqh, S::LDAH, uv);
-      state_update_kt<C, D, NVW>(hs, sKt, LDT, uv, sDecay);
+      vnew_frags<C, NVW>(vprev, uv);
       // o from registers: four adjacent value columns per lane and row
       store_oT<C, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, L, o);
     }
     __syncthreads();
   }
+  if (nch > 0) state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((nch - 1) & 1) * D);
   if (owner && p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, D, col0, D, hs);
 }
 

@@ -334,11 +334,26 @@ __device__ __forceinline__ void store_oT(bf16_t *g, int64_t ldg, int col0, int L
 }
 
 // h <- Diag(2^b_L) h + k~^T v_new with k~ row-major [C][ldt].
+// v_new as the bf16 operand fragments of the state update, one per 32 chunk rows.
+template <int C, int NVW>
+__device__ __forceinline__ void vnew_frags(bf16x8_t (&fv)[C / 32][NVW], const f32x4_t (&vn)[C / 16][NVW]) {
+  constexpr int NC = C / 16;
+#pragma unroll
+  for (int s = 0; s < C / 32; ++s)
+#pragma unroll
+    for (int v = 0; v < NVW; ++v) {
+      f32x4_t col[NC];
+#pragma unroll
+      for (int t = 0; t < NC; ++t) col[t] = vn[t][v];
+      fv[s][v] = acc_frag<bf16_t, NC>(col, s);
+    }
+}
+
 template <int C, int D, int NVW>
 __device__ __forceinline__ void state_update_kt(f32x4_t (&h)[D / 16][NVW], const bf16_t *sKt, int ldt,
-                                                const f32x4_t (&vn)[C / 16][NVW], const float *sDecay) {
+                                                const bf16x8_t (&fv)[C / 32][NVW], const float *sDecay) {
   using M = Mma<bf16_t>;
-  constexpr int NC = C / 16, DT = D / 16, SC = C / 32;
+  constexpr int DT = D / 16, SC = C / 32;
   const int lane = tid_opaque() & 63;
   const int grp = lane >> 4;
   const int lk = cfrag_lane_off(ldt);
@@ -351,19 +366,11 @@ __device__ __forceinline__ void state_update_kt(f32x4_t (&h)[D / 16][NVW], const
   }
 #pragma unroll
   for (int s = 0; s < SC; ++s) {
-    bf16x8_t fv[NVW];
-#pragma unroll
-    for (int v = 0; v < NVW; ++v) {
-      f32x4_t col[NC];
-#pragma unroll
-      for (int t = 0; t < NC; ++t) col[t] = vn[t][v];
-      fv[v] = acc_frag<bf16_t, NC>(col, s);
-    }
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       const bf16x8_t fk = load_frag32_at(sKt + 32 * s * ldt + 16 * t, ldt, lk);
 #pragma unroll
-      for (int v = 0; v < NVW; ++v) h[t][v] = M::mma(fk, fv[v], h[t][v]);
+      for (int v = 0; v < NVW; ++v) h[t][v] = M::mma(fk, fv[s][v], h[t][v]);
     }
   }
 }
