@@ -143,28 +143,53 @@ __device__ __forceinline__ void gate_cumsum_tables(float *sB, int ldb, float *sB
   __syncthreads();
 }
 
-// (3) T_ii = (I + A_ii)^-1 of one 16 x 16 diagonal block by forward
-// substitution, one column per lane (lanes 0..15; the rest idle), written as
-// bf16 rows of sTd. -A_ii is read from sAkk (fp32, strictly lower, beta folded).
+// (3) T_ii = (I + A_ii)^-1 of one 16 x 16 diagonal block by blocked forward
+// substitution on one wave: lane 16g + c holds rows 4g..4g+3 of column c. In
+// stage k the lanes of group k finish their four rows (a 4-step chain), pass
+// them to every lane of the same column, and the later groups subtract their
+// part, so the chain crosses lanes four times instead of sixteen. -A_ii is
+// read from sAkk (fp32, strictly lower, beta folded), T_ii written as bf16 rows
+// of sTd.
 __device__ __forceinline__ void diag_inverse_block(const float *sAkk, int lda, bf16_t *sTd, int ldt, int i) {
-  const int c = tid_opaque() & 63;
-  if (c >= 16) return;
-  // rows read as 16-byte vectors (lda % 4 == 0); lane >> 4 is 0 here, and as an
-  // opaque per-lane term it keeps the addresses in one VGPR with immediate
-  // offsets instead of a scalar add and a move per row
-  const f32x4_t *A4 = reinterpret_cast<const f32x4_t *>(sAkk + 16 * i * lda + 16 * i) + ((tid_opaque() & 63) >> 4);
-  const int ld4 = lda / 4;
-  float x[16];
+  const int lane = tid_opaque() & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const float *A = sAkk + (16 * i + 4 * g) * lda + 16 * i;
+  f32x4_t a[4][4];  // rows 4g + e, column quads q
 #pragma unroll
-  for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+  for (int e = 0; e < 4; ++e)
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
+    for (int q = 0; q < 4; ++q) a[e][q] = *reinterpret_cast<const f32x4_t *>(A + e * lda + 4 * q);
+  float x[4];
 #pragma unroll
-    for (int r = s + 1; r < 16; ++r) x[r] += A4[r * ld4 + s / 4][s % 4] * x[s];
+  for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == c) ? 1.f : 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float z[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      z[e] = x[e];
+#pragma unroll
+      for (int e2 = 0; e2 < e; ++e2) z[e] += a[e][k][e2] * z[e2];
+    }
+    const bool mine = (g == k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = mine ? z[e] : x[e];
+    if (k == 3) break;
+    float y[4];  // group k's finished rows of this column
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = __int_as_float(__builtin_amdgcn_ds_bpermute((16 * k + c) * 4, __float_as_int(x[e])));
+    const bool later = (g > k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float acc = x[e];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) acc += a[e][k][e2] * y[e2];
+      x[e] = later ? acc : x[e];
+    }
   }
-  bf16_t *T = sTd + i * 16 * ldt;
+  bf16_t *T = sTd + (16 * i + 4 * g) * ldt + c;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) T[r * ldt + c] = static_cast<bf16_t>(x[r]);
+  for (int e = 0; e < 4; ++e) T[e * ldt] = static_cast<bf16_t>(x[e]);
 }
 
 
