@@ -56,9 +56,10 @@ struct FusedSmem {
   static constexpr int LDAH = C + 8;    // A_qk [C][LDAH] bf16
   static constexpr size_t aqh = aqk + 4 * C * LDA;
   static constexpr size_t td = aqh + 2 * C * LDAH;
-  static constexpr size_t t1 = td + 2 * C * LDTD;     // scale 2^a_i per row block and channel, fp32 [C/16][D]
-  static constexpr size_t t2 = t1 + 4 * (C / 16) * D;  // 2^(b_L - a_i)
-  static constexpr size_t beta = t2 + 4 * (C / 16) * D;
+  static constexpr size_t t1 = td + 2 * C * LDTD;     // scale 2^m_i per row block and channel, fp32 [C/16][D]
+  static constexpr size_t t2 = t1 + 4 * (C / 16) * D;  // 2^(b_L - m_i)
+  static constexpr size_t t0 = t2 + 4 * (C / 16) * D;  // 2^(m_i - a_i)
+  static constexpr size_t beta = t0 + 4 * (C / 16) * D;
   static constexpr size_t bl = beta + 4 * C;
   static constexpr size_t decay = bl + 4 * D;
   static constexpr size_t dt = decay + 2 * 4 * D;  // decay: two chunks (the state update trails by one)
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   // buffers below 64 KB at constant offsets; the others from three opaque bases
   char *baseB = lds_base(smem, S::b), *baseA = lds_base(smem, S::akk), *baseT = lds_base(smem, S::t1);
   static_assert(S::b % 16 == 0 && S::wt_off % 16 == 0 && S::akk % 16 == 0 && S::kt % 16 == 0 && S::aqk % 16 == 0 &&
-                    S::aqh % 16 == 0 && S::td % 16 == 0 && S::t1 % 16 == 0 && S::t2 % 16 == 0 && S::beta % 16 == 0 &&
+                    S::aqh % 16 == 0 && S::td % 16 == 0 && S::t1 % 16 == 0 && S::t2 % 16 == 0 && S::t0 % 16 == 0 && S::beta % 16 == 0 &&
                     S::bl % 16 == 0 && S::decay % 16 == 0 && S::dt % 16 == 0 && S::seg % 16 == 0,
                 "16-byte aligned buffers");
   static_assert( S::td + 2 * C * S::LDTD - S::akk <= 65536 &&
@@ -201,6 +202,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   Tin *sTd = reinterpret_cast<Tin *>(baseA + (S::td - S::akk));
   float *sT1 = reinterpret_cast<float *>(baseT);
   float *sT2 = reinterpret_cast<float *>(baseT + (S::t2 - S::t1));
+  float *sT0 = reinterpret_cast<float *>(baseT + (S::t0 - S::t1));
   float *sBeta = reinterpret_cast<float *>(baseT + (S::beta - S::t1));
   float *sBL = reinterpret_cast<float *>(baseT + (S::bl - S::t1));
   float *sDecay2 = reinterpret_cast<float *>(baseT + (S::decay - S::t1));  // [2][D], by chunk parity
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
       gate_pad<NT, C, D>(sB, LDB, sBL, L);
       for (int i = tid_opaque(); i < D; i += NT) sDecay[i] = fast_exp2(sBL[i]);  // read after later barriers
     } else {
-      gate_cumsum_tables<NT, C, D, SAFE>(sB, LDB, sBL, sSeg, sDecay, sT1, sT2, p.scale);
+      gate_cumsum_tables<NT, C, D, SAFE>(sB, LDB, sBL, sSeg, sDecay, sT0, sT1, sT2, p.scale);
     }
     // (2) the grams, and q~, k~, beta k 2^b; (3) the diagonal inverses
     auto load_next = [&]() {
@@ -285,11 +287,11 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     };
     auto none = []() {};
     if constexpr (HALF_LOAD)
-      grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT1, sT2,
-                                  sBL, sKt, sXw, sTd, S::LDTD, load_next);
+      grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT0, sT1,
+                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, load_next);
     else
-      grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT1, sT2,
-                                  sBL, sKt, sXw, sTd, S::LDTD, none);
+      grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT0, sT1,
+                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, none);
     __syncthreads();
     if (!HALF_LOAD && more) regs.load_qkv(p, t0 + C, Ln, h);
     // (4) this wave's column tiles of w (channels) and u (values)

@@ -91,21 +91,25 @@ __device__ __forceinline__ bf16x8_t load_frag32(const bf16_t *M, int ld, int k0,
 
 // (1) The chunk-local cumsum b of the gate rows in sB (fp32, base 2, in place),
 // with b_L in sBL, the chunk decay 2^b_L in sDecay and, for the safe gate, the
-// anchor tables sT1 = scale 2^a_i and sT2 = 2^(b_L - a_i) of each 16-row block
-// (a_i = b at the block's first row): each thread scans RPS consecutive rows of
-// one channel, so segment starts that are block starts hold a_i after the
-// segment offsets are added. Ends with a barrier.
+// anchor tables of each 16-row block i with midpoint m_i = b at row 16i + 8 and
+// first row a_i: sT1 = scale 2^m_i, sT2 = 2^(b_L - m_i), sT0 = 2^(m_i - a_i).
+// Each thread scans RPS consecutive rows of one channel; with RPS = 8 the thread
+// of a block's first half also reads the raw gate of row 16i + 8 to reach m_i.
+// Ends with a barrier.
 template <int NT, int C, int D, bool SAFE>
 __device__ __forceinline__ void gate_cumsum_tables(float *sB, int ldb, float *sBL, float *sSeg, float *sDecay,
-                                                   float *sT1, float *sT2, float scale) {
+                                                   float *sT0, float *sT1, float *sT2, float scale) {
   static_assert(NT % D == 0, "thread mapping: whole channels per thread group");
   constexpr int TPC = NT / D;  // threads per channel, each owning RPS consecutive rows
   constexpr int RPS = C / TPC;
-  static_assert(RPS % 16 == 0 || 16 % RPS == 0, "segments and 16-row blocks nest");
+  static_assert(RPS % 16 == 0 || RPS == 8, "segments and 16-row blocks nest");
   const int tid = tid_opaque(), col = tid % D, seg = tid / D;
   float vals[RPS];
 #pragma unroll
   for (int i = 0; i < RPS; ++i) vals[i] = sB[(seg * RPS + i) * ldb + col];
+  float g_mid = 0.f;  // RPS = 8: the raw gate of the next segment's first row
+  if constexpr (SAFE && RPS == 8)
+    if ((seg & 1) == 0) g_mid = sB[(seg * RPS + 8) * ldb + col];
 #pragma unroll
   for (int i = 1; i < RPS; ++i) vals[i] += vals[i - 1];
   float bl = vals[RPS - 1];
@@ -130,14 +134,16 @@ __device__ __forceinline__ void gate_cumsum_tables(float *sB, int ldb, float *sB
     sDecay[col] = fast_exp2(bl);
   }
   if constexpr (SAFE) {
+    auto tables = [&](int blk, float a, float m) {
+      sT1[blk * D + col] = scale * fast_exp2(m);
+      sT2[blk * D + col] = fast_exp2(bl - m);
+      sT0[blk * D + col] = fast_exp2(m - a);
+    };
+    if constexpr (RPS == 8) {
+      if ((seg & 1) == 0) tables(seg / 2, vals[0], vals[7] + g_mid);
+    } else {
 #pragma unroll
-    for (int m = 0; m < RPS; m += 16) {
-      const int row = seg * RPS + m;
-      if (row % 16 == 0) {
-        const float a = vals[m];
-        sT1[(row / 16) * D + col] = scale * fast_exp2(a);
-        sT2[(row / 16) * D + col] = fast_exp2(bl - a);
-      }
+      for (int j = 0; j < RPS; j += 16) tables((seg * RPS + j) / 16, vals[j], vals[j + 8]);
     }
   }
   __syncthreads();
@@ -407,16 +413,15 @@ namespace kda {
 // ---------------------------------------------------------------------------------------------
 // (2) grams for the fused kernel. Each wave owns one row block i of both grams
 // and a 1/HS share of the channels (HS = 1 or 2 waves per row block): it builds
-// the row operands of block i once -- q, k scaled by 2^(b_r - a_i), a_i the
-// block's first row -- and the column operands k_s 2^(a_i - b_s) of blocks
-// j <= i, so the row side never exceeds 1 and off-diagonal column exponents are
-// paired non-positive offsets ("FLA KDA Skill", section "Safe gate numerical
-// note"). The pages anchor the diagonal block at its midpoint to keep head room
-// below the FP32 exponent limit; the safe gate bounds one token's decay by
-// |lower_bound| <= 5, so the 15 steps from the first row reach at most
-// 2^(15 * 5 / ln 2) = 2^108 < 2^127 and the first-row anchor serves the diagonal
-// block too, with one exponential pair per element. Non-safe gates, unbounded,
-// take the diagonal block per pair (section "Safe vs non-safe intra path").
+// the row operands of block i once -- q, k scaled by 2^(b_r - m_i) (midpoint
+// anchor, diagonal block) and by 2^(b_r - a_i) (first-row anchor a_i,
+// off-diagonal blocks) -- and the column operands k_s 2^(m_i - b_s)
+// (diagonal) and k_s 2^(a_i - b_s) (blocks j < i), so every exponent is a
+// midpoint or paired non-positive offset ("FLA KDA Skill", section "Safe gate
+// numerical note"). One exponential pair per element serves the diagonal; the
+// off-diagonal row operands are those times the table 2^(m_i - a_i). Non-safe
+// gates, unbounded, take the diagonal block per pair (section "Safe vs
+// non-safe intra path").
 // Only causal blocks are formed ("[examples] Read only the causal columns in
 // chunk_fwd_A_diag_anchored", description). With HS = 2 each half stores its
 // scaled, masked partial sums of one matrix, and after a barrier adds its own
@@ -429,12 +434,13 @@ namespace kda {
 //                          the channels of each 32-block in operand order
 //   k~  = k 2^(b_L - b)    written to sKt
 //   X_w = beta k 2^b       returned in xw (written after the grams' barrier)
-// For the safe gate these reuse the anchored exponentials: scale 2^b =
-// 2^(b - a_I) T1 and 2^(b_L - b) = 2^(a_I - b) T2 with the per-channel tables
-// T1 = scale 2^a_I, T2 = 2^(b_L - a_I); other gates take them directly.
+// For the safe gate these reuse the midpoint exponentials: scale 2^b =
+// 2^(b - m_I) T1 and 2^(b_L - b) = 2^(m_I - b) T2 with the per-channel tables
+// T1 = scale 2^m_I, T2 = 2^(b_L - m_I); other gates take them directly.
 template <int I, int NC, int NS, bool SAFE>
 __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
-                                                 int c0, const float *sT1, const float *sT2, const float *sBL, int D,
+                                                 int c0, const float *sT0, const float *sT1, const float *sT2,
+                                                 const float *sBL, int D,
                                                  float scale, float beta_r, bf16_t *sKt, f32x4_t (&accQ)[NC],
                                                  f32x4_t (&accK)[NC], bf16x4_t (&xw)[NS][2]) {
   using M = Mma<bf16_t>;
@@ -445,12 +451,14 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int kb = c0 + 32 * s + 4 * grp;  // slots e < 4: channel kb + e; e >= 4: kb + 16 + (e - 4)
-    f32x4_t br[2], ba[2], t1[2], t2[2];
+    f32x4_t br[2], ba[2], bm[2], t0[2], t1[2], t2[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       br[hh] = *reinterpret_cast<const f32x4_t *>(sB + rr * ldb + kb + 16 * hh);
       ba[hh] = *reinterpret_cast<const f32x4_t *>(sB + (16 * I) * ldb + kb + 16 * hh);
       if (SAFE) {
+        bm[hh] = *reinterpret_cast<const f32x4_t *>(sB + (16 * I + 8) * ldb + kb + 16 * hh);
+        if (I > 0) t0[hh] = *reinterpret_cast<const f32x4_t *>(sT0 + I * D + kb + 16 * hh);
         t1[hh] = *reinterpret_cast<const f32x4_t *>(sT1 + I * D + kb + 16 * hh);
         t2[hh] = *reinterpret_cast<const f32x4_t *>(sT2 + I * D + kb + 16 * hh);
       } else {
@@ -461,22 +469,30 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
     const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t *>(sQ + rr * ldt + kb + 16);
     const bf16x4_t k0 = *reinterpret_cast<const bf16x4_t *>(sK + rr * ldt + kb);
     const bf16x4_t k1 = *reinterpret_cast<const bf16x4_t *>(sK + rr * ldt + kb + 16);
-    float vqo[8], vko[8], vkc[8], vqt[8], vxw[8], vkt[8];
+    float vqd[8], vkd[8], vqo[8], vko[8], vkc[8], vqt[8], vxw[8], vkt[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int hh = e >> 2, ee = e & 3;
       const float qf = static_cast<float>(hh ? q1[ee] : q0[ee]);
       const float kf = static_cast<float>(hh ? k1[ee] : k0[ee]);
       if (SAFE) {
-        // one pair of exponentials per element: 2^(b - a_I) for the row
-        // operands, its inverse for the diagonal block's column operand
-        const float d = br[hh][ee] - ba[hh][ee];
-        const float eo = fast_exp2(d), ec = fast_exp2(-d);
-        vqo[e] = qf * eo;
-        vko[e] = kf * eo;
+        // one pair of exponentials per element: 2^(b - m_I) for the diagonal
+        // block's row operands, its inverse for the column operand; the
+        // off-diagonal row operands 2^(b - a_I) and the other tiles are
+        // products with per-channel tables
+        const float d = br[hh][ee] - bm[hh][ee];
+        const float ed = fast_exp2(d), ec = fast_exp2(-d);
+        vqd[e] = qf * ed;
+        vkd[e] = kf * ed;
         vkc[e] = kf * ec;
-        vqt[e] = vqo[e] * t1[hh][ee];                        // scale q 2^b
-        vxw[e] = vko[e] * (t1[hh][ee] * beta_over_scale);   // beta k 2^b
+        if (I > 0) {
+          vqo[e] = vqd[e] * t0[hh][ee];
+          vko[e] = vkd[e] * t0[hh][ee];
+        } else {
+          vqo[e] = vko[e] = 0.f;
+        }
+        vqt[e] = vqd[e] * t1[hh][ee];                        // scale q 2^b
+        vxw[e] = vkd[e] * (t1[hh][ee] * beta_over_scale);   // beta k 2^b
         vkt[e] = vkc[e] * t2[hh][ee];                        // k 2^(b_L - b)
       } else {
         const float E = fast_exp2(br[hh][ee]), El = fast_exp2(t2[hh][ee] - br[hh][ee]);
@@ -493,9 +509,16 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
         vkc[e] = 0.f;
       }
     }
-    const bf16x8_t fqo = pack_bf16x8(vqo), fko = pack_bf16x8(vko);
-    bf16x8_t fcd;
-    if (SAFE) fcd = pack_bf16x8(vkc);
+    bf16x8_t fqo, fko, fqd, fkd, fcd;
+    if (I > 0) {
+      fqo = pack_bf16x8(vqo);
+      fko = pack_bf16x8(vko);
+    }
+    if (SAFE) {
+      fqd = pack_bf16x8(vqd);
+      fkd = pack_bf16x8(vkd);
+      fcd = pack_bf16x8(vkc);
+    }
     bf16x4_t qt[2], kt[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -512,8 +535,8 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) *reinterpret_cast<bf16x4_t *>(sKt + rr * ldt + kb + 16 * hh) = kt[hh];
     if (SAFE) {
-      accQ[I] = M::mma(fcd, fqo, accQ[I]);
-      accK[I] = M::mma(fcd, fko, accK[I]);
+      accQ[I] = M::mma(fcd, fqd, accQ[I]);
+      accK[I] = M::mma(fcd, fkd, accK[I]);
     }
 #pragma unroll
     for (int j = 0; j < I; ++j) {
@@ -610,9 +633,9 @@ __device__ __forceinline__ int gram_half(int w) {
 template <int NT, int C, int D, bool SAFE, typename Idle>
 __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                             const float *sBeta, float scale, float *sAkk, float *sAqk, int lda,
-                                            bf16_t *sAqh, int ldh, int L, const float *sT1, const float *sT2,
-                                            const float *sBL, bf16_t *sKt, bf16_t *sXw, bf16_t *sTd,
-                                            int ldtd, Idle &&idle) {
+                                            bf16_t *sAqh, int ldh, int L, const float *sT0, const float *sT1,
+                                            const float *sT2, const float *sBL, bf16_t *sKt, bf16_t *sXw,
+                                            bf16_t *sTd, int ldtd, Idle &&idle) {
   constexpr int NW = NT / 64, NC = C / 16;
   constexpr int HS = (NW / NC >= 2) ? 2 : 1, CW = D / HS, NS = CW / 32;
   static_assert(NW >= NC && CW % 32 == 0, "wave split of the grams");
@@ -654,7 +677,7 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
       }
     }
 #define KDA_GRAM_ROW(II)                                                                                     \
-  gram_row_partial<II, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, sT1, sT2, sBL, D, scale, beta_r, sKt, accQ, accK, \
+  gram_row_partial<II, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, sT0, sT1, sT2, sBL, D, scale, beta_r, sKt, accQ, accK, \
                                      xw)
     switch (i) {
       case 0: KDA_GRAM_ROW(0); break;
