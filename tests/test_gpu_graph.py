@@ -1,0 +1,141 @@
+"""HIP-graph replay of the entry points.
+
+Neither call reads a device value on the host, allocates inside the library or
+issues a memset, so each can be captured once and replayed ("attention-gym"
+page, "Agent note": graph-capturable, cu_seqlens on the device). Every replay
+here runs on inputs and cu_seqlens rewritten in place since the capture, with
+eager calls and synchronisations between the replays, and must equal an eager
+call on the same inputs bit for bit (both run the same kernels, which hold no
+state between calls).
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_synth
+from kda_testlib import need_gpu
+
+pytestmark = pytest.mark.gpu
+
+CAP, H, D, SLOTS = 1536, 4, 128, 5
+
+
+def _chunk_case(seed):
+    d = kda_synth.chunk_inputs(1, CAP, H, D, D, dtype=torch.bfloat16, seed=seed, n_slots=SLOTS)
+    cu = kda_synth.varlen_offsets(seed, n_slots=SLOTS, n_empty=1, total=CAP - 64 - seed % 37, max_len=CAP)
+    d["cu"] = torch.from_numpy(cu)
+    return d
+
+
+def _refill(dst, src):
+    for key, t in src.items():
+        if t is not None:
+            dst[key].copy_(t)
+
+
+@pytest.mark.parametrize("schedule", ["auto", "staged"])
+def test_chunk_graph_replay_with_new_offsets(schedule):
+    from gated_delta_rule_gate_amd import chunk_kda
+
+    need_gpu()
+    first = _chunk_case(11)
+    dev = {k: v.cuda() for k, v in first.items() if v is not None}
+    o_g = torch.zeros((1, CAP, H, D), dtype=torch.bfloat16, device="cuda")
+    ht_g = torch.empty((SLOTS, H, D, D), dtype=torch.float32, device="cuda")
+
+    def call(o, ht):
+        chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], dev["h0"], cu_seqlens=dev["cu"],
+                  chunk_size=64, gate_kind="safe", A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0,
+                  schedule=schedule, out=o, final_state=ht)
+
+    call(o_g, ht_g)  # warm-up outside the capture (loads the library, compiles nothing)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(o_g, ht_g)
+    torch.cuda.synchronize()
+
+    o_e = torch.zeros_like(o_g)
+    ht_e = torch.empty_like(ht_g)
+    for rep, seed in enumerate([12, 13, 14, 15]):
+        case = _chunk_case(seed)
+        _refill(dev, {k: v for k, v in case.items() if v is not None})
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        call(o_e, ht_e)  # eager, same inputs
+        torch.cuda.synchronize()
+        n_valid = int(case["cu"][-1])
+        assert torch.equal(o_g[:, :n_valid], o_e[:, :n_valid]), "replay %d: o differs from the eager call" % rep
+        assert torch.equal(ht_g, ht_e), "replay %d: ht differs from the eager call" % rep
+        # the replay really used the new offsets: an empty slot passes h0 through
+        cu = case["cu"].numpy()
+        for n in range(SLOTS):
+            if cu[n] == cu[n + 1]:
+                assert torch.equal(ht_g[n], dev["h0"][n])
+
+
+def test_recurrent_graph_replay_in_place_state():
+    from gated_delta_rule_gate_amd import recurrent_kda
+
+    need_gpu()
+    N, T = 8, 4
+
+    def case(seed):
+        d = kda_synth.chunk_inputs(N, T, H, D, D, dtype=torch.bfloat16, seed=seed)
+        d["g"] = kda_synth.log2_gate(d["x"].numpy(), d["A_log"].numpy(), d["dt_bias"].numpy())
+        return d
+
+    first = case(21)
+    dev = {k: v.cuda() for k, v in first.items() if v is not None}
+    state_g = dev["h0"].clone()
+    o_g = torch.empty((N, T, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def call(state, o):
+        recurrent_kda(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], state, final_state=state, out=o)
+
+    warm = state_g.clone()
+    call(warm, o_g)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(state_g, o_g)
+    torch.cuda.synchronize()
+    state_g.copy_(dev["h0"])  # the capture itself ran nothing
+
+    o_e = torch.empty_like(o_g)
+    for rep, seed in enumerate([22, 23, 24]):
+        _refill(dev, {k: v for k, v in case(seed).items() if v is not None and k != "h0"})
+        state_e = state_g.clone()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        call(state_e, o_e)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), "replay %d: o differs from the eager call" % rep
+        assert torch.equal(state_g, state_e), "replay %d: state differs from the eager call" % rep
+        assert not torch.equal(state_g, dev["h0"]), "the replay did not advance the state"
+
+
+def test_gate_cumsum_graph_replay():
+    from gated_delta_rule_gate_amd import gate_cumsum
+
+    need_gpu()
+    d = kda_synth.chunk_inputs(2, 200, H, D, D, dtype=torch.bfloat16, seed=31)
+    x = d["x"].cuda()
+    A_log, dt_bias = d["A_log"].cuda(), d["dt_bias"].cuda()
+    out_g = torch.empty_like(x)
+    gate_cumsum(x, chunk_size=64, A_log=A_log, dt_bias=dt_bias, out=out_g)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gate_cumsum(x, chunk_size=64, A_log=A_log, dt_bias=dt_bias, out=out_g)
+    rng = np.random.default_rng(32)
+    for rep in range(3):
+        x.copy_(torch.from_numpy(rng.standard_normal(x.shape).astype(np.float32)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        out_e = gate_cumsum(x, chunk_size=64, A_log=A_log, dt_bias=dt_bias)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), "replay %d differs from the eager call" % rep
