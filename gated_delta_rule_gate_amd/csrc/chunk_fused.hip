@@ -64,7 +64,8 @@ struct FusedSmem {
   static constexpr size_t decay = bl + 4 * D;
   static constexpr size_t dt = decay + 2 * 4 * D;  // decay: two chunks (the state update trails by one)
   static constexpr size_t seg = dt + 4 * D;
-  static constexpr size_t total = seg + 4 * NT;
+  static constexpr size_t qn = seg + 4 * NT;  // per chunk row: 1/sqrt(|q|^2 + eps) (q_l2norm)
+  static constexpr size_t total = qn + 4 * C;
 };
 
 // One chunk's raw inputs held in registers between the HBM load and the LDS store.
@@ -131,9 +132,27 @@ struct ChunkRegs {
   // so the sigmoid's exponent is one fma.
   template <int GK>
   __device__ __forceinline__ void store(bool loader, Tin *sQ, Tin *sK, Tin *sV, float *sB, float *sBeta,
-                                        const float *sDt, int L, float expA, float lower_bound) const {
+                                        const float *sDt, int L, float expA, float lower_bound, bool qnorm,
+                                        float *sQn) const {
     using TL = Tile<Tin, C, D>;
     wait_vmem();
+    if (loader && qnorm) {
+      // 1/sqrt(|q_r|^2 + eps) per row: a row's VPR vectors sit on VPR adjacent lanes
+      static_assert((VPR & (VPR - 1)) == 0 && VPR <= 64 && (NL % VPR) == 0, "rows within a wave");
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const unsigned idx = it * NL + loader_index();
+        float ss = 0.f;
+        if (NVT % NL == 0 || idx < NVT) {
+          const bf16x8_t x = __builtin_bit_cast(bf16x8_t, q[it]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf(static_cast<float>(x[e]), static_cast<float>(x[e]), ss);
+        }
+#pragma unroll
+        for (int m = 1; m < VPR; m <<= 1) ss += __shfl_xor(ss, m);
+        if ((NVT % NL == 0 || idx < NVT) && idx % VPR == 0) sQn[idx / VPR] = rsqrtf(ss + kQNormEps);
+      }
+    }
     if (loader)
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -184,7 +203,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   char *baseB = lds_base(smem, S::b), *baseA = lds_base(smem, S::akk), *baseT = lds_base(smem, S::t1);
   static_assert(S::b % 16 == 0 && S::wt_off % 16 == 0 && S::akk % 16 == 0 && S::kt % 16 == 0 && S::aqk % 16 == 0 &&
                     S::aqh % 16 == 0 && S::td % 16 == 0 && S::t1 % 16 == 0 && S::t2 % 16 == 0 && S::t0 % 16 == 0 && S::beta % 16 == 0 &&
-                    S::bl % 16 == 0 && S::decay % 16 == 0 && S::dt % 16 == 0 && S::seg % 16 == 0,
+                    S::bl % 16 == 0 && S::decay % 16 == 0 && S::dt % 16 == 0 && S::seg % 16 == 0 && S::qn % 16 == 0,
                 "16-byte aligned buffers");
   static_assert( S::td + 2 * C * S::LDTD - S::akk <= 65536 &&
                     S::total - S::t1 <= 65536 && S::v + S::tile <= 65536,
@@ -208,6 +227,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   float *sDecay2 = reinterpret_cast<float *>(baseT + (S::decay - S::t1));  // [2][D], by chunk parity
   float *sDt = reinterpret_cast<float *>(baseT + (S::dt - S::t1));
   float *sSeg = reinterpret_cast<float *>(baseT + (S::seg - S::t1));
+  float *sQn = reinterpret_cast<float *>(baseT + (S::qn - S::t1));
 
   // workgroup = (sequence, head, block vb of D / vsplit value columns); waves
   // below tpb own one 16-column tile of the state, all waves share the key side
@@ -266,7 +286,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     const int L = min(C, sr.len - c * C);
     const int64_t off = t0 * ld + h * D;
     float *sDecay = sDecay2 + (c & 1) * D;
-    regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound);
+    regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound, p.q_l2norm != 0, sQn);
     state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((c + 1) & 1) * D);  // chunk c - 1's
     __syncthreads();
     // the next chunk's inputs are loaded in two parts while this chunk computes
@@ -326,6 +346,13 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
         for (int v = 0; v < NVW; ++v) uv[i][v] = uv[i][v] - p1[i][v];
       causal_times_h<C, NVW>(o, sAqh, S::LDAH, uv);
       vnew_frags<C, NVW>(vprev, uv);
+      if (p.q_l2norm) {  // raw q: o is linear in each q row
+        const int n16 = tid_opaque() & 15;
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+#pragma unroll
+          for (int v = 0; v < NVW; ++v) o[i][v] = o[i][v] * sQn[16 * i + n16];
+      }
       // o from registers: four adjacent value columns per lane and row
       store_oT<C, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, L, o);
     }

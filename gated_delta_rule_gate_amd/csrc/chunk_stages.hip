@@ -269,6 +269,7 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
   float *sB = reinterpret_cast<float *>(sQ + C * LDT);
   float *sBL = sB + C * LDB;
   float *sAqk = sBL + D;
+  float *sQn = sAqk + C * TL::LDA;  // per row: 1/sqrt(|q|^2 + eps) with q_l2norm
   const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C;
   const int64_t off = lc.t0 * ld + h * D;
   load_rows<Tin, kNT, C, D>(sQ, LDT, reinterpret_cast<const Tin *>(p.q) + off, ld, lc.L);
@@ -276,6 +277,14 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
   load_rows<float, kNT, C, C>(sAqk, TL::LDA, p.Aqk + lc.t0 * ldc + h * C, ldc, lc.L);
   __syncthreads();
   pad_cumsum<kNT, C, D>(sB, LDB, sBL, lc.L);
+  if (p.q_l2norm && threadIdx.x < C) {  // raw q: o is linear in each q row
+    float ss = 0.f;
+    for (int c = 0; c < D; ++c) {
+      const float x = to_f32(sQ[threadIdx.x * LDT + c]);
+      ss = fmaf(x, x, ss);
+    }
+    sQn[threadIdx.x] = rsqrtf(ss + kQNormEps);
+  }
   __syncthreads();
   make_qtilde<Tin, kNT, C, D>(sQ, sB, p.scale);
   f32x4_t hs[DT][NVW], vn[NC][NVW], o[NC][NVW];
@@ -286,6 +295,11 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
   __syncthreads();
   rows_times_state<Tin, C, D, NVW, false>(o, o, sQ, sQ, hs);
   causal_times<Tin, C, NVW>(o, sAqk, vn);
+  if (p.q_l2norm) {
+    const int grp = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) o[i][0] = o[i][0] * *reinterpret_cast<const f32x4_t *>(sQn + 16 * i + 4 * grp);
+  }
   store_strip<Tin, NC, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, lc.L, o);
 }
 
@@ -382,7 +396,7 @@ hipError_t launch_stage_scan(const ChunkParams &p, hipStream_t st) {
 hipError_t launch_stage_output(const ChunkParams &p, hipStream_t st) {
   return dispatch(p, [&]<typename Tin, int C, int D>() {
     using TL = Tile<Tin, C, D>;
-    const size_t smem = sizeof(Tin) * C * TL::LDT + sizeof(float) * (C * TL::LDB + D + C * TL::LDA);
+    const size_t smem = sizeof(Tin) * C * TL::LDT + sizeof(float) * (C * TL::LDB + D + C * TL::LDA + C);
     return launch_dyn(stage_output_kernel<Tin, C, D>, dim3(p.max_chunks, p.H, D / 64), smem, st, p);
   });
 }

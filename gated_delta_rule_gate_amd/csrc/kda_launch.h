@@ -7,6 +7,8 @@
 
 namespace kda {
 
+constexpr float kQNormEps = 1e-6f;  // eps floor of the deferred q l2-normalisation
+
 struct RecurrentParams {
   const void *q, *k, *v;
   const float *g, *beta, *h0;
@@ -18,6 +20,7 @@ struct RecurrentParams {
   int gate_kind;
   int B, T, H, K, V, N;
   bool is_bf16;
+  int q_l2norm;  // scale each output row by 1/sqrt(|q|^2 + 1e-6)
 };
 
 hipError_t launch_recurrent(const RecurrentParams &p, hipStream_t st);
@@ -51,6 +54,7 @@ struct ChunkParams {
   int gate_kind;
   int B, T, H, D, N, C;
   bool is_bf16;
+  int q_l2norm;        // scale each output row by 1/sqrt(|q|^2 + 1e-6)
   int32_t *chunk_off;  // [N + 1] chunk prefix per slot (packed batches only)
   int max_chunks;      // upper bound of the number of chunks (grid size)
   int vsplit;          // fused schedule: value-column blocks per (sequence, head), set by its launcher

@@ -10,7 +10,9 @@
 //   S     = S' + k delta^T
 //
 // so both column reductions (S'^T k and S'^T q) happen in one pass over the
-// state, and o needs no second pass after the rank-1 update.
+// state, and o needs no second pass after the rank-1 update. With q_l2norm, o
+// is also scaled by 1/sqrt(|q|^2 + eps), which normalises q after the fact
+// (o is linear in q).
 //
 // Thread layout: thread = (column group cg of 4 adjacent columns, row group rg);
 // it holds RPT rows x 4 columns. A wave's 16-byte loads of the state cover whole
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
   __shared__ float s_red[2][RG][BV];
   __shared__ float s_d[BV];
   constexpr int NWAVE = Cfg::kThreads / 64;
-  __shared__ float s_kq[2][NWAVE];
+  __shared__ float s_kq[2][NWAVE], s_qq[2][NWAVE];
   __shared__ float s_beta[2];
 
   const float expA = (p.gate_kind == kGateSafe || p.gate_kind == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
@@ -121,12 +123,13 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
   for (int i = 0; i < sr.len; ++i) {
     const int buf = i & 1;
     // ---- phase A: stage this token's inputs in LDS, prefetch the next ----
-    float kq = 0.f;
+    float kq = 0.f, qq = 0.f;
     if (tid < K) {
       s_k[buf][tid] = nk;
       s_q[buf][tid] = nq;
       s_a[buf][tid] = fast_exp2(gate_log2(p.gate_kind, ng, dt, expA, p.lower_bound));
       kq = nk * nq;
+      qq = nq * nq;
     }
     if (tid < BV) s_v[buf][tid] = nv;
     if (tid == 0) s_beta[buf] = nb;
@@ -134,6 +137,11 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
     if ((tid & 63) == 0) s_kq[buf][tid >> 6] = kq;
+    if (p.q_l2norm) {  // |q|^2 for the deferred normalisation of q
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) qq += __shfl_xor(qq, off);
+      if ((tid & 63) == 0) s_qq[buf][tid >> 6] = qq;
+    }
     if (i + 1 < sr.len) fetch(i + 1);
     __syncthreads();
 
@@ -166,7 +174,14 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
       const float d = s_beta[buf] * (s_v[buf][tid] - sk);
       s_d[tid] = d;
       const int64_t th = (sr.t0 + i) * p.H + h;
-      op[th * p.V + vb * BV + tid] = from_f32<Tin>(p.scale * (sq + kqs * d));
+      float os = p.scale;
+      if (p.q_l2norm) {
+        float qqs = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) qqs += s_qq[buf][w];
+        os *= rsqrtf(qqs + kQNormEps);
+      }
+      op[th * p.V + vb * BV + tid] = from_f32<Tin>(os * (sq + kqs * d));
     }
     __syncthreads();
 

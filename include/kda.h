@@ -93,7 +93,21 @@ typedef struct {
   const float *dt_bias;    /* [H, K] device pointer or NULL (SAFE, SOFTPLUS)                    */
   float lower_bound;       /* SAFE only                                                         */
   kda_schedule schedule;   /* kda_chunk_fwd only                                                */
+  int q_l2norm;            /* 0: q arrives l2-normalised (the contract). 1: q arrives raw and each
+                              output row is scaled by 1 / sqrt(sum over K of q^2 + 1e-6), which
+                              equals running on l2-normalised q (see below). Other values:
+                              KDA_ERR_SHAPE                                                   */
 } kda_args;
+
+/*
+ * q_l2norm ("Add fused recurrent_kda ...", the stacked description of the
+ * fused q-l2norm option): every q-dependent term of the forward is linear in
+ * q's row and lands in the same output row, so the normalisation of q can be
+ * deferred to one 1/||q|| scale of that row of o. The eps floor is 1e-6, the
+ * default of the l2norm it replaces. The grams then run in the raw-q basis,
+ * about sqrt(K) larger, which the bounded safe gate tolerates. Forward only;
+ * kda_chunk_fwd (both schedules) and kda_recurrent_fwd honour it.
+ */
 
 /* Human-readable name of a status code. */
 const char *kda_status_string(kda_status s);

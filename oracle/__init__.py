@@ -80,6 +80,20 @@ def gate(kind, x, A_log=None, dt_bias=None, lower_bound=0.0):
     return out
 
 
+L2NORM_EPS = 1e-6
+
+
+def l2norm_rows(x, eps=L2NORM_EPS):
+    """Each row (last axis) divided by sqrt(sum of its squares + eps), in FP64.
+
+    The explicit normalisation that the kernels' q_l2norm option defers to the
+    output ("Add fused recurrent_kda ...", stacked description of the fused
+    q-l2norm option: the eps floor is l2norm's default, read as 1e-6).
+    """
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
 def _offsets(B, T, cu_seqlens):
     if cu_seqlens is None:
         return np.arange(B + 1, dtype=np.int32) * T

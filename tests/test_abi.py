@@ -69,6 +69,7 @@ FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fail
     (dict(K=48), 8),
     (dict(B=2, N=1), 2),               # dense needs N == B
     (dict(H=0), 2),
+    (dict(q_l2norm=2), 2),             # the q_l2norm flag is 0 or 1
 ])
 def test_recurrent_rejects(kda_lib, kw, code):
     a = _args(**kw)

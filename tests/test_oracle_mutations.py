@@ -141,3 +141,29 @@ def test_cumsum_mutation_is_caught(oracle_mod, tmp_path, name):
         assert _fails_some_pin([("test_chunk_cumsum_pins", {})]), "mutation %s survived every pin" % name
     finally:
         pins.chunk_cumsum_log2 = saved
+
+
+L2NORM_MUTATIONS = {
+    "no_eps": ("keepdims=True) + eps)", "keepdims=True))"),
+    "wrong_axis": ("axis=-1", "axis=0"),
+    "no_sqrt": ("np.sqrt(np.sum", "(np.sum"),
+    "no_square": ("np.sum(x * x,", "np.sum(np.abs(x),"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(L2NORM_MUTATIONS))
+def test_l2norm_mutation_is_caught(name):
+    import inspect
+    import types
+
+    import numpy as np
+
+    src = inspect.getsource(oracle.l2norm_rows)
+    old, new = L2NORM_MUTATIONS[name]
+    assert src.count(old) == 1, "mutation anchor missing or ambiguous: " + old
+    ns = {"np": np, "L2NORM_EPS": oracle.L2NORM_EPS, "_f64": oracle._f64}
+    exec(src.replace(old, new, 1), ns)
+    fake = types.SimpleNamespace(l2norm_rows=ns["l2norm_rows"])
+    with pytest.raises(AssertionError):
+        pins.test_l2norm_rows_pins(fake)
+

@@ -368,3 +368,26 @@ def test_chunk_cumsum_pins(oracle_mod):
     _, _, it = chunked_forward(q, k, v, gp, beta, cu_seqlens=cu, chunk_size=32, emit=True)
     valid = slice(0, int(cu[-1]))
     np.testing.assert_allclose(bp[:, valid], it["b"][:, valid], rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------------------
+# The explicit q normalisation behind the q_l2norm option
+# ----------------------------------------------------------------------------------------
+
+def test_l2norm_rows_pins(oracle_mod):
+    """Rows whose squared norm plus eps is exactly 1 come back unchanged; zero rows stay
+    zero; large rows reach unit norm (eps negligible); tiny rows are divided by
+    sqrt(eps); each row is normalised on its own."""
+    f = oracle_mod.l2norm_rows
+    eps = 1e-6
+    b = math.sqrt(0.64 - eps)
+    x = np.array([[0.6, b, 0.0], [0.0, 0.0, math.sqrt(1.0 - eps)], [0.0, 0.0, 0.0]])
+    np.testing.assert_allclose(f(x), x, rtol=0, atol=1e-15)
+    big = np.array([[3e6, 4e6, 0.0]])
+    np.testing.assert_allclose(f(big), [[0.6, 0.8, 0.0]], rtol=1e-12, atol=0)
+    tiny = np.array([[3e-9, -4e-9, 0.0]])
+    np.testing.assert_allclose(f(tiny), tiny / math.sqrt(eps), rtol=1e-9, atol=0)
+    rows = np.concatenate([big, tiny, x], axis=0)[None, :, None, :]  # [1, T, 1, K] like q
+    together = f(rows)
+    for t in range(rows.shape[1]):
+        np.testing.assert_allclose(together[0, t, 0], f(rows[:, t:t + 1])[0, 0, 0], rtol=1e-15, atol=0)
