@@ -29,7 +29,7 @@ class KdaArgs(ctypes.Structure):
                 ("V", ctypes.c_int), ("N", ctypes.c_int), ("chunk_size", ctypes.c_int), ("dtype", ctypes.c_int),
                 ("scale", ctypes.c_float), ("gate_kind", ctypes.c_int), ("A_log", ctypes.c_void_p),
                 ("dt_bias", ctypes.c_void_p), ("lower_bound", ctypes.c_float), ("schedule", ctypes.c_int),
-                ("q_l2norm", ctypes.c_int)]
+                ("Hk", ctypes.c_int), ("q_l2norm", ctypes.c_int)]
 
 
 def lib():
@@ -97,10 +97,11 @@ def _check_tensors(named, device):
 
 def make_args(q, v, H, N, gate_kind, chunk_size=64, scale=None, A_log=None, dt_bias=None, lower_bound=-5.0,
               schedule="auto", q_l2norm=False):
-    B, T, _, K = q.shape
+    B, T, Hk, K = q.shape
     V = v.shape[-1]
     a = KdaArgs()
     a.B, a.T, a.H, a.K, a.V, a.N = B, T, H, K, V, N
+    a.Hk = Hk if Hk != H else 0
     a.chunk_size = int(chunk_size)
     a.dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
     a.scale = float(scale) if scale is not None else 0.0
@@ -114,14 +115,15 @@ def make_args(q, v, H, N, gate_kind, chunk_size=64, scale=None, A_log=None, dt_b
 
 
 def _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias):
-    _require(q.dim() == 4 and k.shape == q.shape, "q, k must be [B, T, H, K] of one shape")
-    _require(v.dim() == 4 and v.shape[:3] == q.shape[:3], "v must be [B, T, H, V]")
+    _require(q.dim() == 4 and k.shape == q.shape, "q, k must be [B, T, Hk, K] of one shape")
+    _require(v.dim() == 4 and v.shape[:2] == q.shape[:2] and v.shape[2] % q.shape[2] == 0,
+             "v must be [B, T, H, V] with H a multiple of q's heads Hk")
     _require(q.dtype in (torch.bfloat16, torch.float32) and k.dtype == q.dtype and v.dtype == q.dtype,
              "q, k, v must share dtype bf16 or fp32")
-    _require(g.shape == q.shape and g.dtype == torch.float32, "g must be fp32 [B, T, H, K]")
-    _require(beta.shape == q.shape[:3] and beta.dtype == torch.float32, "beta must be fp32 [B, T, H]")
-    B, T, H, K = q.shape
-    V = v.shape[-1]
+    B, T, Hk, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    _require(g.shape == (B, T, H, K) and g.dtype == torch.float32, "g must be fp32 [B, T, H, K]")
+    _require(beta.shape == (B, T, H) and beta.dtype == torch.float32, "beta must be fp32 [B, T, H]")
     if cu_seqlens is not None:
         _require(B == 1, "packed inputs (cu_seqlens) need batch 1")
         _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1, "cu_seqlens must be int32 [N+1]")

@@ -92,20 +92,21 @@ struct ChunkRegs {
   // scalar-base + vector-offset form.
   // q, k, v of the chunk at t0
   __device__ __forceinline__ void load_qkv(const ChunkParams &p, int64_t t0, int L, int h) {
-    const unsigned ld = (unsigned)p.H * D;
+    const unsigned ld = (unsigned)p.H * D, ldk = (unsigned)p.Hk * D;
     const int64_t base = t0 * (int64_t)ld + (int64_t)h * D;
-    const Tin *gq = reinterpret_cast<const Tin *>(p.q) + base;
-    const Tin *gk = reinterpret_cast<const Tin *>(p.k) + base;
+    const int64_t basek = t0 * (int64_t)ldk + (int64_t)(h / (p.H / p.Hk)) * D;  // q/k head of value head h
+    const Tin *gq = reinterpret_cast<const Tin *>(p.q) + basek;
+    const Tin *gk = reinterpret_cast<const Tin *>(p.k) + basek;
     const Tin *gv = reinterpret_cast<const Tin *>(p.v) + base;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const unsigned idx = it * NL + loader_index();
       const int r = idx / VPR, c = (idx % VPR) * EPV;
       const bool ok = (NVT % NL == 0 || idx < NVT) && r < L;
-      const unsigned off = (unsigned)r * ld + (unsigned)c;
+      const unsigned off = (unsigned)r * ld + (unsigned)c, offk = (unsigned)r * ldk + (unsigned)c;
       const u32x4_t z = {0u, 0u, 0u, 0u};
-      q[it] = ok ? *reinterpret_cast<const u32x4_t *>(gq + off) : z;
-      k[it] = ok ? *reinterpret_cast<const u32x4_t *>(gk + off) : z;
+      q[it] = ok ? *reinterpret_cast<const u32x4_t *>(gq + offk) : z;
+      k[it] = ok ? *reinterpret_cast<const u32x4_t *>(gk + offk) : z;
       v[it] = ok ? *reinterpret_cast<const u32x4_t *>(gv + off) : z;
     }
   }

@@ -126,10 +126,10 @@ __global__ __launch_bounds__(256) void stage_grams_kernel(ChunkParams p) {
   float *sB = reinterpret_cast<float *>(sK + C * TL::LDT);
   float *sBL = sB + C * TL::LDB;
   float *sBeta = sBL + D;
-  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C;
-  const int64_t off = lc.t0 * ld + h * D;
-  load_rows<Tin, kNT, C, D>(sQ, TL::LDT, reinterpret_cast<const Tin *>(p.q) + off, ld, lc.L);
-  load_rows<Tin, kNT, C, D>(sK, TL::LDT, reinterpret_cast<const Tin *>(p.k) + off, ld, lc.L);
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * D;
+  const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * D;
+  load_rows<Tin, kNT, C, D>(sQ, TL::LDT, reinterpret_cast<const Tin *>(p.q) + offk, ldk, lc.L);
+  load_rows<Tin, kNT, C, D>(sK, TL::LDT, reinterpret_cast<const Tin *>(p.k) + offk, ldk, lc.L);
   load_rows<float, kNT, C, D>(sB, TL::LDB, p.b + off, ld, lc.L);
   load_beta<C>(sBeta, p, lc.t0, h, lc.L);
   __syncthreads();
@@ -171,10 +171,10 @@ __global__ __launch_bounds__(256) void stage_wy_kernel(ChunkParams p) {
   float *sBeta = sBL + D;
   Tin *sK = reinterpret_cast<Tin *>(sBeta + C);
   Tin *sV = sK + C * LDT;
-  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C;
-  const int64_t off = lc.t0 * ld + h * D;
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * D;
+  const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * D;
   load_rows<float, kNT, C, C>(sT, TL::LDA, p.Tm + lc.t0 * ldc + h * C, ldc, lc.L);
-  load_rows<Tin, kNT, C, D>(sK, LDT, reinterpret_cast<const Tin *>(p.k) + off, ld, lc.L);
+  load_rows<Tin, kNT, C, D>(sK, LDT, reinterpret_cast<const Tin *>(p.k) + offk, ldk, lc.L);
   load_rows<Tin, kNT, C, D>(sV, LDT, reinterpret_cast<const Tin *>(p.v) + off, ld, lc.L);
   load_rows<float, kNT, C, D>(sB, LDB, p.b + off, ld, lc.L);
   load_beta<C>(sBeta, p, lc.t0, h, lc.L);
@@ -210,7 +210,8 @@ __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
   const int nch = (sr.len + C - 1) / C;
   const int cbase = p.cu ? p.chunk_off[n] : n * ((p.T + C - 1) / C);
   const int64_t sbase = (int64_t)nh * D * D;
-  const int64_t ld = (int64_t)p.H * D;
+  const int64_t ld = (int64_t)p.H * D, ldk = (int64_t)p.Hk * D;
+  const int hk = h / (p.H / p.Hk);  // q/k head of value head h
 
   extern __shared__ __align__(16) char smem[];
   Tin *sW = reinterpret_cast<Tin *>(smem);
@@ -237,7 +238,8 @@ __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
       sDecay[i] = fast_exp2(bl);
     }
     __syncthreads();
-    make_ktilde_t_global<Tin, kNT, C, D>(sKT, reinterpret_cast<const Tin *>(p.k) + off, p.b + off, ld, sBL, L);
+    make_ktilde_t_global<Tin, kNT, C, D>(sKT, reinterpret_cast<const Tin *>(p.k) + t0 * ldk + hk * D, ldk,
+                                         p.b + off, ld, sBL, L);
     f32x4_t uv[NC][NVW];
     load_strip<NC, NVW>(uv, p.u + off, ld, col0, L);
     __syncthreads();
@@ -270,9 +272,9 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
   float *sBL = sB + C * LDB;
   float *sAqk = sBL + D;
   float *sQn = sAqk + C * TL::LDA;  // per row: 1/sqrt(|q|^2 + eps) with q_l2norm
-  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C;
-  const int64_t off = lc.t0 * ld + h * D;
-  load_rows<Tin, kNT, C, D>(sQ, LDT, reinterpret_cast<const Tin *>(p.q) + off, ld, lc.L);
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * D;
+  const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * D;
+  load_rows<Tin, kNT, C, D>(sQ, LDT, reinterpret_cast<const Tin *>(p.q) + offk, ldk, lc.L);
   load_rows<float, kNT, C, D>(sB, LDB, p.b + off, ld, lc.L);
   load_rows<float, kNT, C, C>(sAqk, TL::LDA, p.Aqk + lc.t0 * ldc + h * C, ldc, lc.L);
   __syncthreads();

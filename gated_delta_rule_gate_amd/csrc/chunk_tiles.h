@@ -427,13 +427,13 @@ __device__ __forceinline__ void pad_cumsum(float *sB, int ldb, float *sBL, int L
 // Same from global rows: k [L][D] (row stride ld) and the fp32 cumsum b [L][D];
 // rows >= L of k~^T are zero.
 template <typename Tin, int NT, int C, int D>
-__device__ __forceinline__ void make_ktilde_t_global(Tin *sKT, const Tin *gK, const float *gB, int64_t ld,
-                                                     const float *sBL, int L) {
+__device__ __forceinline__ void make_ktilde_t_global(Tin *sKT, const Tin *gK, int64_t ldk, const float *gB,
+                                                     int64_t ld, const float *sBL, int L) {
   using TL = Tile<Tin, C, D>;
   for (int idx = tid_opaque(); idx < C * D; idx += NT) {
     const int i = idx % D, c = idx / D;  // consecutive threads walk the channels (coalesced reads)
     float v = 0.f;
-    if (c < L) v = to_f32(gK[(int64_t)c * ld + i]) * fast_exp2(sBL[i] - gB[(int64_t)c * ld + i]);
+    if (c < L) v = to_f32(gK[(int64_t)c * ldk + i]) * fast_exp2(sBL[i] - gB[(int64_t)c * ld + i]);
     sKT[i * TL::LDKT + c] = from_f32<Tin>(v);
   }
 }

@@ -21,6 +21,7 @@ struct RecurrentParams {
   int B, T, H, K, V, N;
   bool is_bf16;
   int q_l2norm;  // scale each output row by 1/sqrt(|q|^2 + 1e-6)
+  int Hk;        // q/k heads; value head h reads q/k head h / (H / Hk)
 };
 
 hipError_t launch_recurrent(const RecurrentParams &p, hipStream_t st);
@@ -55,6 +56,7 @@ struct ChunkParams {
   int B, T, H, D, N, C;
   bool is_bf16;
   int q_l2norm;        // scale each output row by 1/sqrt(|q|^2 + 1e-6)
+  int Hk;              // q/k heads; value head h reads q/k head h / (H / Hk)
   int32_t *chunk_off;  // [N + 1] chunk prefix per slot (packed batches only)
   int max_chunks;      // upper bound of the number of chunks (grid size)
   int vsplit;          // fused schedule: value-column blocks per (sequence, head), set by its launcher

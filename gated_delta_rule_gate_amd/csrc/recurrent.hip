@@ -109,10 +109,10 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
   float nk = 0.f, nq = 0.f, ng = 0.f, nv = 0.f, nb = 0.f;
   auto fetch = [&](int i) {
     const int64_t t = sr.t0 + i;
-    const int64_t th = t * p.H + h;
+    const int64_t th = t * p.H + h, thk = t * p.Hk + h / (p.H / p.Hk);
     if (tid < K) {
-      nk = to_f32(kp[th * K + tid]);
-      nq = to_f32(qp[th * K + tid]);
+      nk = to_f32(kp[thk * K + tid]);
+      nq = to_f32(qp[thk * K + tid]);
       ng = p.g[th * K + tid];
     }
     if (tid < BV) nv = to_f32(vp[th * p.V + vb * BV + tid]);

@@ -83,7 +83,8 @@ typedef enum {
 } kda_schedule;
 
 typedef struct {
-  int B, T, H, K, V;       /* dense: tensors [B, T, H, *]; packed: B == 1, T = capacity         */
+  int B, T, H, K, V;       /* dense: tensors [B, T, H, *] (q, k: [B, T, Hk, K]); packed: B == 1,
+                              T = capacity                                                    */
   int N;                   /* sequences (slots); cu_seqlens has N + 1 entries (dense: N == B)   */
   int chunk_size;          /* chunk path: 32 or 64 (sub-chunk fixed at 16 rows)                 */
   kda_dtype dtype;         /* dtype of q, k, v and o                                            */
@@ -93,6 +94,9 @@ typedef struct {
   const float *dt_bias;    /* [H, K] device pointer or NULL (SAFE, SOFTPLUS)                    */
   float lower_bound;       /* SAFE only                                                         */
   kda_schedule schedule;   /* kda_chunk_fwd only                                                */
+  int Hk;                  /* heads of q and k; 0 means H. H must be a multiple of Hk: value head h
+                              (of v, g, beta, o and the states) reads q/k head h / (H / Hk)
+                              (grouped value heads, GVA)                                      */
   int q_l2norm;            /* 0: q arrives l2-normalised (the contract). 1: q arrives raw and each
                               output row is scaled by 1 / sqrt(sum over K of q^2 + 1e-6), which
                               equals running on l2-normalised q (see below). Other values:
