@@ -53,6 +53,10 @@ def lib():
             L.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
             L.kda_chunk_fwd.argtypes = [ap] + [vp] * 10 + [ctypes.c_size_t, vp]
             L.kda_chunk_fwd.restype = ctypes.c_int
+            L.kda_chunk_states_count.argtypes = [ap, ctypes.c_int]
+            L.kda_chunk_states_count.restype = ctypes.c_size_t
+            L.kda_chunk_fwd_states.argtypes = [ap] + [vp] * 11 + [ctypes.c_size_t, vp]
+            L.kda_chunk_fwd_states.restype = ctypes.c_int
         if hasattr(L, "kda_chunk_stage"):
             L.kda_chunk_stage.argtypes = [ap, ctypes.c_int] + [vp] * 10 + [ctypes.c_size_t, vp]
             L.kda_chunk_stage.restype = ctypes.c_int
@@ -192,7 +196,8 @@ def gate_cumsum(g, *, chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None,
 
 def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_final_state=False,
               chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None,
-              schedule="auto", final_state=None, out=None, q_l2norm=False):
+              schedule="auto", final_state=None, out=None, q_l2norm=False, return_intermediate_states=False,
+              intermediate_states=None):
     """Chunked KDA prefill forward. Returns (o, ht); ht is None unless requested.
 
     g is the raw gate input for ``gate_kind`` "safe" / "softplus" (activation in
@@ -200,6 +205,12 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
     ``gate_cumsum`` with the same chunk size for "log2_cumsum". ``out`` may
     preallocate o. ``q_l2norm=True`` takes raw q and normalises it inside: each
     output row is scaled by 1/sqrt(|q|^2 + 1e-6) (o is linear in each q row).
+
+    ``return_intermediate_states=True`` returns (o, ht, h_states): the fp32 state
+    entering every chunk, [B, ceil(T / C), H, K, V] for a dense batch and
+    [1, ceil(T / C) + N, H, K, V] for a packed one, whose chunks are numbered slot
+    by slot (slot n starts at the sum of ceil(len_m / C) over m < n; entries past
+    the last chunk are left as they are). ``intermediate_states`` may preallocate it.
     """
     B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
     o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
@@ -211,9 +222,23 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
     L = lib()
     ws_bytes = L.kda_chunk_workspace_bytes(ctypes.byref(a))
     ws = torch.empty((max(int(ws_bytes), 256),), dtype=torch.uint8, device=q.device)
-    check(L.kda_chunk_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                          _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))
-    return o, ht
+    if not (return_intermediate_states or intermediate_states is not None):
+        check(L.kda_chunk_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                              _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(ws),
+                              ctypes.c_size_t(ws.numel()), _stream()))
+        return o, ht
+    count = int(L.kda_chunk_states_count(ctypes.byref(a), 1 if cu_seqlens is not None else 0))
+    _require(count > 0 or T == 0, "unsupported shape for intermediate states")
+    shape = (B, count // B, H, K, V)
+    hs = intermediate_states
+    if hs is None:
+        hs = torch.empty(shape, dtype=torch.float32, device=q.device)
+    _require(hs.shape == shape and hs.dtype == torch.float32, "intermediate_states must be fp32 %s" % (shape,))
+    _check_tensors(dict(intermediate_states=hs), q.device)
+    check(L.kda_chunk_fwd_states(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(hs), _ptr(ws),
+                                 ctypes.c_size_t(ws.numel()), _stream()))
+    return o, ht, hs
 
 
 def workspace_bytes(q, v, H, N, chunk_size=64, schedule="auto"):

@@ -1,7 +1,8 @@
 // The fused schedule of the chunked KDA forward: one persistent workgroup per
 // (sequence, head) walks the sequence's chunks in order and runs steps (1)-(6)
 // for each chunk entirely on chip. Inputs are read from HBM exactly once and
-// only o and the final state are written; the [D, D] FP32 state lives in MFMA
+// only o and the final state are written (plus, when asked for, the state at
+// the start of every chunk); the [D, D] FP32 state lives in MFMA
 // accumulator registers for the whole sequence (each of the NT/64 waves owns
 // a 16*NVW-column strip of it). bf16 inputs only (fp32 inputs run the staged
 // schedule).
@@ -243,6 +244,8 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   const int nch = (sr.len + C - 1) / C;
   const int64_t sbase = (int64_t)nh * D * D;
   const int64_t ld = (int64_t)p.H * D;
+  // chunk-start states, if asked for: chunks numbered slot by slot
+  float *hcs = p.hc ? p.hc + ((int64_t)(p.cu ? p.chunk_off[n] : n * ((p.T + C - 1) / C)) * p.H + h) * D * D : nullptr;
   const float expA = (GK == kGateSafe || GK == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
   for (int i = tid_opaque(); i < D; i += NT) {
     const float dt = p.dt_bias ? p.dt_bias[h * D + i] : 0.f;
@@ -289,6 +292,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     float *sDecay = sDecay2 + (c & 1) * D;
     regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound, p.q_l2norm != 0, sQn);
     state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((c + 1) & 1) * D);  // chunk c - 1's
+    if (hcs && owner) store_strip<float, DT, NVW>(hcs + (int64_t)c * p.H * D * D, D, col0, D, hs);
     __syncthreads();
     // the next chunk's inputs are loaded in two parts while this chunk computes
     const bool more = c + 1 < nch;

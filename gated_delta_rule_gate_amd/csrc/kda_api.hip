@@ -314,17 +314,48 @@ extern "C" size_t kda_staged_workspace_offset(const kda_args *a, kda_ws_field fi
   return staged_layout(a).off[(int)field];
 }
 
+namespace {
+
+kda_status run_chunk(const kda_args *a, const kda::ChunkParams &p, hipStream_t st) {
+  kda_status s;
+  if (use_fused(a, p)) {
+    // the fused kernel reads the chunk prefix only to number the chunk-start states
+    if (p.hc && p.cu && (s = run_stage(p, KDA_STAGE_INDEX, st)) != KDA_OK) return s;
+    return hip_status(kda::launch_fused(p, st));
+  }
+  for (int stage = KDA_STAGE_INDEX; stage <= KDA_STAGE_OUTPUT; ++stage)
+    if ((s = run_stage(p, stage, st)) != KDA_OK) return s;
+  return KDA_OK;
+}
+
+}  // namespace
+
 extern "C" kda_status kda_chunk_fwd(const kda_args *a, const void *q, const void *k, const void *v, const float *g,
                                     const float *beta, const float *h0, const int32_t *cu_seqlens, void *o,
                                     float *ht, void *workspace, size_t ws_bytes, void *stream) {
   kda::ChunkParams p;
   kda_status s = prepare_chunk(a, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace, ws_bytes, p);
   if (s != KDA_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
-  if (use_fused(a, p)) return hip_status(kda::launch_fused(p, st));
-  for (int stage = KDA_STAGE_INDEX; stage <= KDA_STAGE_OUTPUT; ++stage)
-    if ((s = run_stage(p, stage, st)) != KDA_OK) return s;
-  return KDA_OK;
+  return run_chunk(a, p, (hipStream_t)stream);
+}
+
+extern "C" size_t kda_chunk_states_count(const kda_args *a, int packed) {
+  if (!chunk_shape_ok(a)) return 0;
+  if (packed ? a->B != 1 : a->N != a->B) return 0;
+  return (size_t)max_chunks(a, packed != 0);
+}
+
+extern "C" kda_status kda_chunk_fwd_states(const kda_args *a, const void *q, const void *k, const void *v,
+                                           const float *g, const float *beta, const float *h0,
+                                           const int32_t *cu_seqlens, void *o, float *ht, float *h_states,
+                                           void *workspace, size_t ws_bytes, void *stream) {
+  kda::ChunkParams p;
+  kda_status s = prepare_chunk(a, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace, ws_bytes, p);
+  if (s != KDA_OK) return s;
+  if (!h_states && kda_chunk_states_count(a, cu_seqlens != nullptr) > 0) return KDA_ERR_NULL;
+  if (!aligned16(h_states)) return KDA_ERR_ALIGN;
+  if (h_states) p.hc = h_states;  // the staged scan writes the chunk-start states here, not in the workspace
+  return run_chunk(a, p, (hipStream_t)stream);
 }
 
 extern "C" kda_status kda_chunk_stage(const kda_args *a, kda_stage stage, const void *q, const void *k,

@@ -182,6 +182,37 @@ kda_status kda_chunk_fwd(const kda_args *args, const void *q, const void *k, con
                          void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Entries of [H, K, V] floats that h_states of kda_chunk_fwd_states must hold
+ * (0 when the arguments are invalid or packed does not match B and N):
+ *   dense  (packed == 0, N == B)  B * ceil(T / C), exactly the chunks;
+ *   packed (packed != 0, B == 1)  ceil(T / C) + N, an upper bound of the sum
+ *                                 over slots of ceil(len_n / C), since the
+ *                                 offsets stay on the device.
+ */
+size_t kda_chunk_states_count(const kda_args *args, int packed);
+
+/*
+ * kda_chunk_fwd that also writes the state entering every chunk (the
+ * return_intermediate_states option that "FLA KDA Skill", section
+ * "Correctness checklist", lists as an axis of the forward):
+ *   h_states[j] = the fp32 [H, K, V] state before the first token of chunk j,
+ * chunks numbered slot by slot and in order within a slot: dense j = n *
+ * ceil(T / C) + c; packed j = (sum over m < n of ceil(len_m / C)) + c. A
+ * slot's first chunk holds h0 (zeros when h0 is NULL). Empty slots own no
+ * chunk. Entries past the last chunk of a packed batch are not written.
+ * Arguments: those of kda_chunk_fwd, plus
+ *   h_states   fp32 device pointer, kda_chunk_states_count(args, cu_seqlens
+ *              != NULL) * H * K * V floats, 16-byte aligned (KDA_ERR_ALIGN),
+ *              not NULL unless that count is 0 (KDA_ERR_NULL); must not overlap
+ *              any other buffer.
+ * Both schedules honour it; the workspace is the one kda_chunk_fwd takes.
+ * The extra traffic is K * V * 4 bytes per chunk and head, written once.
+ */
+kda_status kda_chunk_fwd_states(const kda_args *args, const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *h0, const int32_t *cu_seqlens, void *o, float *ht,
+                                float *h_states, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Fused token-sequential recurrence (recurrent_kda forward), for decode and
  * inference prefill ("Add fused recurrent_kda ...", section "Agent note"):
  * one kernel; each workgroup owns a (sequence, head, value-block) and scans its

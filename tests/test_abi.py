@@ -134,3 +134,24 @@ def test_recurrent_rejects_precumsummed_gate(kda_lib):
     a = _args(gate_kind=3)
     st = kda_lib.kda_recurrent_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None)
     assert st == 5
+
+
+def test_chunk_states_count(kda_lib):
+    """Entries of the chunk-start states: B * ceil(T / C) dense, ceil(T / C) + N packed."""
+    a = _args(gate_kind=0, B=3, N=3, T=203)
+    assert kda_lib.kda_chunk_states_count(ctypes.byref(a), 0) == 3 * 4
+    assert kda_lib.kda_chunk_states_count(ctypes.byref(a), 1) == 0  # packed needs B == 1
+    a = _args(gate_kind=0, B=1, N=5, T=420, chunk_size=32)
+    assert kda_lib.kda_chunk_states_count(ctypes.byref(a), 1) == 14 + 5
+    assert kda_lib.kda_chunk_states_count(ctypes.byref(a), 0) == 0  # dense needs N == B
+    assert kda_lib.kda_chunk_states_count(ctypes.byref(_args(gate_kind=0, V=64)), 0) == 0  # K != V
+
+
+def test_chunk_states_rejects(kda_lib):
+    a = _args(gate_kind=0)
+    call = lambda hs: kda_lib.kda_chunk_fwd_states(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                                                   None, hs, FAKE2, ctypes.c_size_t(1 << 30), None)
+    assert call(None) == 1                          # states wanted but no buffer
+    assert call(ctypes.c_void_p(0x100004)) == 6     # misaligned
+    a.chunk_size = 16
+    assert call(FAKE) == 4                          # the checks of kda_chunk_fwd come first
