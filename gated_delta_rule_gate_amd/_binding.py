@@ -271,8 +271,9 @@ class StagedRun:
         C = int(chunk_size)
         rows = B * T
         nch = max((T + C - 1) // C + N, B * ((T + C - 1) // C))
-        shapes = dict(b=(rows, H, K), Akk=(rows, H, C), Aqk=(rows, H, C), T=(rows, H, C), w=(rows, H, K),
-                      u=(rows, H, V), vnew=(rows, H, V), hc=(nch, H, K, V))
+        D = 64 if max(K, V) <= 64 else (128 if max(K, V) <= 128 else 256)  # the kernels' tile width
+        shapes = dict(b=(rows, H, D), Akk=(rows, H, C), Aqk=(rows, H, C), T=(rows, H, C), w=(rows, H, D),
+                      u=(rows, H, D), vnew=(rows, H, D), hc=(nch, H, K, V))
         self.views = {}
         for name, shp in shapes.items():
             off = int(L.kda_staged_workspace_offset(ctypes.byref(self.args), WS_FIELDS[name]))

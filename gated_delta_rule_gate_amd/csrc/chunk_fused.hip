@@ -93,9 +93,9 @@ struct ChunkRegs {
   // scalar-base + vector-offset form.
   // q, k, v of the chunk at t0
   __device__ __forceinline__ void load_qkv(const ChunkParams &p, int64_t t0, int L, int h) {
-    const unsigned ld = (unsigned)p.H * D, ldk = (unsigned)p.Hk * D;
-    const int64_t base = t0 * (int64_t)ld + (int64_t)h * D;
-    const int64_t basek = t0 * (int64_t)ldk + (int64_t)(h / (p.H / p.Hk)) * D;  // q/k head of value head h
+    const unsigned ld = (unsigned)p.H * p.Vr, ldk = (unsigned)p.Hk * p.Kr;
+    const int64_t base = t0 * (int64_t)ld + (int64_t)h * p.Vr;
+    const int64_t basek = t0 * (int64_t)ldk + (int64_t)(h / (p.H / p.Hk)) * p.Kr;  // q/k head of value head h
     const Tin *gq = reinterpret_cast<const Tin *>(p.q) + basek;
     const Tin *gk = reinterpret_cast<const Tin *>(p.k) + basek;
     const Tin *gv = reinterpret_cast<const Tin *>(p.v) + base;
@@ -106,22 +106,23 @@ struct ChunkRegs {
       const bool ok = (NVT % NL == 0 || idx < NVT) && r < L;
       const unsigned off = (unsigned)r * ld + (unsigned)c, offk = (unsigned)r * ldk + (unsigned)c;
       const u32x4_t z = {0u, 0u, 0u, 0u};
-      q[it] = ok ? *reinterpret_cast<const u32x4_t *>(gq + offk) : z;
-      k[it] = ok ? *reinterpret_cast<const u32x4_t *>(gk + offk) : z;
-      v[it] = ok ? *reinterpret_cast<const u32x4_t *>(gv + off) : z;
+      // channels >= Kr and value columns >= Vr are zeros (whole vectors: widths are multiples of 8)
+      q[it] = ok && c < p.Kr ? *reinterpret_cast<const u32x4_t *>(gq + offk) : z;
+      k[it] = ok && c < p.Kr ? *reinterpret_cast<const u32x4_t *>(gk + offk) : z;
+      v[it] = ok && c < p.Vr ? *reinterpret_cast<const u32x4_t *>(gv + off) : z;
     }
   }
 
   // gate input and beta of the chunk at t0
   __device__ __forceinline__ void load_gate(const ChunkParams &p, int64_t t0, int L, int h) {
-    const unsigned ld = (unsigned)p.H * D;
-    const int64_t base = t0 * (int64_t)ld + (int64_t)h * D;
+    const unsigned ld = (unsigned)p.H * p.Kr;
+    const int64_t base = t0 * (int64_t)ld + (int64_t)h * p.Kr;
     const float *gx = p.g + base;
 #pragma unroll
     for (int it = 0; it < IX; ++it) {
       const unsigned idx = it * NT + (unsigned)tid_opaque();
       const int r = idx / XPR, c = (idx % XPR) * 4;
-      const bool ok = (NVX % NT == 0 || idx < NVX) && r < L;
+      const bool ok = (NVX % NT == 0 || idx < NVX) && r < L && c < p.Kr;
       const unsigned off = (unsigned)r * ld + (unsigned)c;
       x[it] = ok ? *reinterpret_cast<const f32x4_t *>(gx + off) : zero4();
     }
@@ -237,24 +238,25 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   const int nh = blockIdx.x / vs, vb = blockIdx.x % vs;
   const int n = nh / p.H, h = nh % p.H;
   const int wid = wave_id();
-  const bool owner = wid < tpb;
   const int ctu = vb * tpb + wid;  // this wave's value tile (owners)
+  const bool owner = wid < tpb && ctu * 16 < p.Vr;  // tiles wholly past Vr are zero
   const int col0 = ctu * 16;
+  const int Kr = p.Kr, Vr = p.Vr;
   const SlotRange sr = slot_range(p.cu, n, p.T);
   const int nch = (sr.len + C - 1) / C;
-  const int64_t sbase = (int64_t)nh * D * D;
-  const int64_t ld = (int64_t)p.H * D;
+  const int64_t sbase = (int64_t)nh * Kr * Vr;  // states [Kr, Vr]
+  const int64_t ld = (int64_t)p.H * Vr;
   // chunk-start states, if asked for: chunks numbered slot by slot
-  float *hcs = p.hc ? p.hc + ((int64_t)(p.cu ? p.chunk_off[n] : n * ((p.T + C - 1) / C)) * p.H + h) * D * D : nullptr;
+  float *hcs = p.hc ? p.hc + ((int64_t)(p.cu ? p.chunk_off[n] : n * ((p.T + C - 1) / C)) * p.H + h) * Kr * Vr : nullptr;
   const float expA = (GK == kGateSafe || GK == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
   for (int i = tid_opaque(); i < D; i += NT) {
-    const float dt = p.dt_bias ? p.dt_bias[h * D + i] : 0.f;
+    const float dt = (p.dt_bias && i < Kr) ? p.dt_bias[h * Kr + i] : 0.f;
     sDt[i] = (GK == kGateSafe) ? dt * (-expA * kLog2e) : dt;
   }
 
   f32x4_t hs[DT][NVW];
   if (p.h0 && owner) {
-    load_strip<DT, NVW>(hs, p.h0 + sbase, D, col0, D);
+    load_strip<DT, NVW>(hs, p.h0 + sbase, Vr, col0, Kr, Vr);
   } else {
 #pragma unroll
     for (int t = 0; t < DT; ++t)
@@ -288,11 +290,11 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   for (int c = 0; c < nch; ++c) {
     const int64_t t0 = sr.t0 + (int64_t)c * C;
     const int L = min(C, sr.len - c * C);
-    const int64_t off = t0 * ld + h * D;
+    const int64_t off = t0 * ld + h * Vr;
     float *sDecay = sDecay2 + (c & 1) * D;
     regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound, p.q_l2norm != 0, sQn);
     state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((c + 1) & 1) * D);  // chunk c - 1's
-    if (hcs && owner) store_strip<float, DT, NVW>(hcs + (int64_t)c * p.H * D * D, D, col0, D, hs);
+    if (hcs && owner) store_strip<float, DT, NVW>(hcs + (int64_t)c * p.H * Kr * Vr, Vr, col0, Kr, hs, Vr);
     __syncthreads();
     // the next chunk's inputs are loaded in two parts while this chunk computes
     const bool more = c + 1 < nch;
@@ -359,12 +361,12 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
           for (int v = 0; v < NVW; ++v) o[i][v] = o[i][v] * sQn[16 * i + n16];
       }
       // o from registers: four adjacent value columns per lane and row
-      store_oT<C, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, L, o);
+      store_oT<C, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, L, o, Vr);
     }
     __syncthreads();
   }
   if (nch > 0) state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((nch - 1) & 1) * D);
-  if (owner && p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, D, col0, D, hs);
+  if (owner && p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, Vr, col0, Kr, hs, Vr);
 }
 
 bool fused_supported(const ChunkParams &p) { return p.is_bf16 && (p.D == 64 || p.D == 128); }

@@ -350,7 +350,8 @@ __device__ __forceinline__ void causal_times_h(f32x4_t (&o)[C / 16][NVW], const 
 // type bf16: lane writes o[16i + l%16][col0 + 16v + 4g .. + 3] as 8 bytes; rows
 // >= L are not written.
 template <int C, int NVW>
-__device__ __forceinline__ void store_oT(bf16_t *g, int64_t ldg, int col0, int L, const f32x4_t (&o)[C / 16][NVW]) {
+__device__ __forceinline__ void store_oT(bf16_t *g, int64_t ldg, int col0, int L, const f32x4_t (&o)[C / 16][NVW],
+                                         int ncol) {
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
@@ -358,8 +359,10 @@ __device__ __forceinline__ void store_oT(bf16_t *g, int64_t ldg, int col0, int L
     const int r = 16 * i + n16;
     if (r < L) {
 #pragma unroll
-      for (int v = 0; v < NVW; ++v)
-        *reinterpret_cast<bf16x4_t *>(g + (int64_t)r * ldg + col0 + 16 * v + 4 * grp) = to_bf16x4(o[i][v]);
+      for (int v = 0; v < NVW; ++v) {
+        const int c = col0 + 16 * v + 4 * grp;  // four columns, all below ncol or none (ncol % 4 == 0)
+        if (c < ncol) *reinterpret_cast<bf16x4_t *>(g + (int64_t)r * ldg + c) = to_bf16x4(o[i][v]);
+      }
     }
   }
 }

@@ -103,9 +103,9 @@ __global__ __launch_bounds__(256) void stage_gate_kernel(ChunkParams p) {
   float *sBL = sB + C * TL::LDB;
   float *sSeg = sBL + D;
   float *sDt = sSeg + kNT;
-  const int64_t ld = (int64_t)p.H * D;
-  for (int i = threadIdx.x; i < D; i += kNT) sDt[i] = p.dt_bias ? p.dt_bias[h * D + i] : 0.f;
-  load_rows<float, kNT, C, D>(sB, TL::LDB, p.g + lc.t0 * ld + h * D, ld, lc.L);
+  const int64_t ld = (int64_t)p.H * D, ldg = (int64_t)p.H * p.Kr;
+  for (int i = threadIdx.x; i < D; i += kNT) sDt[i] = (p.dt_bias && i < p.Kr) ? p.dt_bias[h * p.Kr + i] : 0.f;
+  load_rows<float, kNT, C, D>(sB, TL::LDB, p.g + lc.t0 * ldg + h * p.Kr, ldg, lc.L, p.Kr);
   __syncthreads();
   gate_activate<kNT, C, D, GK>(sB, TL::LDB, lc.L, sDt, head_expA(p, h), p.lower_bound);
   __syncthreads();
@@ -126,10 +126,10 @@ __global__ __launch_bounds__(256) void stage_grams_kernel(ChunkParams p) {
   float *sB = reinterpret_cast<float *>(sK + C * TL::LDT);
   float *sBL = sB + C * TL::LDB;
   float *sBeta = sBL + D;
-  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * D;
-  const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * D;
-  load_rows<Tin, kNT, C, D>(sQ, TL::LDT, reinterpret_cast<const Tin *>(p.q) + offk, ldk, lc.L);
-  load_rows<Tin, kNT, C, D>(sK, TL::LDT, reinterpret_cast<const Tin *>(p.k) + offk, ldk, lc.L);
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * p.Kr;
+  const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * p.Kr;
+  load_rows<Tin, kNT, C, D>(sQ, TL::LDT, reinterpret_cast<const Tin *>(p.q) + offk, ldk, lc.L, p.Kr);
+  load_rows<Tin, kNT, C, D>(sK, TL::LDT, reinterpret_cast<const Tin *>(p.k) + offk, ldk, lc.L, p.Kr);
   load_rows<float, kNT, C, D>(sB, TL::LDB, p.b + off, ld, lc.L);
   load_beta<C>(sBeta, p, lc.t0, h, lc.L);
   __syncthreads();
@@ -171,11 +171,11 @@ __global__ __launch_bounds__(256) void stage_wy_kernel(ChunkParams p) {
   float *sBeta = sBL + D;
   Tin *sK = reinterpret_cast<Tin *>(sBeta + C);
   Tin *sV = sK + C * LDT;
-  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * D;
-  const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * D;
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * p.Kr, ldv = (int64_t)p.H * p.Vr;
+  const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * p.Kr;
   load_rows<float, kNT, C, C>(sT, TL::LDA, p.Tm + lc.t0 * ldc + h * C, ldc, lc.L);
-  load_rows<Tin, kNT, C, D>(sK, LDT, reinterpret_cast<const Tin *>(p.k) + offk, ldk, lc.L);
-  load_rows<Tin, kNT, C, D>(sV, LDT, reinterpret_cast<const Tin *>(p.v) + off, ld, lc.L);
+  load_rows<Tin, kNT, C, D>(sK, LDT, reinterpret_cast<const Tin *>(p.k) + offk, ldk, lc.L, p.Kr);
+  load_rows<Tin, kNT, C, D>(sV, LDT, reinterpret_cast<const Tin *>(p.v) + lc.t0 * ldv + h * p.Vr, ldv, lc.L, p.Vr);
   load_rows<float, kNT, C, D>(sB, LDB, p.b + off, ld, lc.L);
   load_beta<C>(sBeta, p, lc.t0, h, lc.L);
   __syncthreads();
@@ -201,7 +201,7 @@ template <typename Tin, int C, int D>
 __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
   using TL = Tile<Tin, C, D>;
   constexpr int BV = 64, NVW = 1, NC = TL::NC, DT = TL::DT, LDT = TL::LDT;
-  const int nvb = D / BV;
+  const int nvb = (p.Vr + BV - 1) / BV;  // value blocks wholly past Vr would compute zeros
   const int vb = blockIdx.x % nvb, nh = blockIdx.x / nvb;
   const int n = nh / p.H, h = nh % p.H;
   const int wid = threadIdx.x >> 6;
@@ -209,8 +209,9 @@ __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
   const SlotRange sr = slot_range(p.cu, n, p.T);
   const int nch = (sr.len + C - 1) / C;
   const int cbase = p.cu ? p.chunk_off[n] : n * ((p.T + C - 1) / C);
-  const int64_t sbase = (int64_t)nh * D * D;
-  const int64_t ld = (int64_t)p.H * D, ldk = (int64_t)p.Hk * D;
+  const int Kr = p.Kr, Vr = p.Vr;
+  const int64_t sbase = (int64_t)nh * Kr * Vr;  // states [Kr, Vr]
+  const int64_t ld = (int64_t)p.H * D, ldk = (int64_t)p.Hk * Kr;
   const int hk = h / (p.H / p.Hk);  // q/k head of value head h
 
   extern __shared__ __align__(16) char smem[];
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
 
   f32x4_t hs[DT][NVW];
   if (p.h0) {
-    load_strip<DT, NVW>(hs, p.h0 + sbase, D, col0, D);
+    load_strip<DT, NVW>(hs, p.h0 + sbase, Vr, col0, Kr, Vr);
   } else {
 #pragma unroll
     for (int t = 0; t < DT; ++t) hs[t][0] = zero4();
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
     const int64_t t0 = sr.t0 + (int64_t)c * C;
     const int L = min(C, sr.len - c * C);
     const int64_t off = t0 * ld + h * D;
-    store_strip<float, DT, NVW>(p.hc + ((int64_t)(cbase + c) * p.H + h) * D * D, D, col0, D, hs);
+    store_strip<float, DT, NVW>(p.hc + ((int64_t)(cbase + c) * p.H + h) * Kr * Vr, Vr, col0, Kr, hs, Vr);
     load_rows_cvt<Tin, kNT, C, D>(sW, LDT, p.w + off, ld, L);
     for (int i = threadIdx.x; i < D; i += kNT) {
       const float bl = p.b[off + (int64_t)(L - 1) * ld + i];  // cumsum at the chunk's last row
@@ -238,8 +239,8 @@ __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
       sDecay[i] = fast_exp2(bl);
     }
     __syncthreads();
-    make_ktilde_t_global<Tin, kNT, C, D>(sKT, reinterpret_cast<const Tin *>(p.k) + t0 * ldk + hk * D, ldk,
-                                         p.b + off, ld, sBL, L);
+    make_ktilde_t_global<Tin, kNT, C, D>(sKT, reinterpret_cast<const Tin *>(p.k) + t0 * ldk + hk * Kr, ldk,
+                                         p.b + off, ld, sBL, L, Kr);
     f32x4_t uv[NC][NVW];
     load_strip<NC, NVW>(uv, p.u + off, ld, col0, L);
     __syncthreads();
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
     state_update<Tin, C, D, NVW>(hs, sKT, TL::LDKT, uv, sDecay);
     __syncthreads();
   }
-  if (p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, D, col0, D, hs);
+  if (p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, Vr, col0, Kr, hs, Vr);
 }
 
 // ---- (6) output o = q~ h_c + A_qk v_new, per (chunk, head, 64-column value block) ----
@@ -272,9 +273,9 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
   float *sBL = sB + C * LDB;
   float *sAqk = sBL + D;
   float *sQn = sAqk + C * TL::LDA;  // per row: 1/sqrt(|q|^2 + eps) with q_l2norm
-  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * D;
-  const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * D;
-  load_rows<Tin, kNT, C, D>(sQ, LDT, reinterpret_cast<const Tin *>(p.q) + offk, ldk, lc.L);
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * p.Kr, ldv = (int64_t)p.H * p.Vr;
+  const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * p.Kr;
+  load_rows<Tin, kNT, C, D>(sQ, LDT, reinterpret_cast<const Tin *>(p.q) + offk, ldk, lc.L, p.Kr);
   load_rows<float, kNT, C, D>(sB, LDB, p.b + off, ld, lc.L);
   load_rows<float, kNT, C, C>(sAqk, TL::LDA, p.Aqk + lc.t0 * ldc + h * C, ldc, lc.L);
   __syncthreads();
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
   __syncthreads();
   make_qtilde<Tin, kNT, C, D>(sQ, sB, p.scale);
   f32x4_t hs[DT][NVW], vn[NC][NVW], o[NC][NVW];
-  load_strip<DT, NVW>(hs, p.hc + ((int64_t)lc.gci * p.H + h) * D * D, D, col0, D);
+  load_strip<DT, NVW>(hs, p.hc + ((int64_t)lc.gci * p.H + h) * p.Kr * p.Vr, p.Vr, col0, p.Kr, p.Vr);
   load_strip<NC, NVW>(vn, p.vnew + off, ld, col0, lc.L);
 #pragma unroll
   for (int i = 0; i < NC; ++i) o[i][0] = zero4();
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
 #pragma unroll
     for (int i = 0; i < NC; ++i) o[i][0] = o[i][0] * *reinterpret_cast<const f32x4_t *>(sQn + 16 * i + 4 * grp);
   }
-  store_strip<Tin, NC, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, lc.L, o);
+  store_strip<Tin, NC, NVW>(reinterpret_cast<Tin *>(p.o) + lc.t0 * ldv + h * p.Vr, ldv, col0, lc.L, o, p.Vr);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -391,7 +392,7 @@ hipError_t launch_stage_scan(const ChunkParams &p, hipStream_t st) {
   return dispatch(p, [&]<typename Tin, int C, int D>() {
     using TL = Tile<Tin, C, D>;
     const size_t smem = sizeof(Tin) * (C * TL::LDT + D * TL::LDKT) + sizeof(float) * 2 * D;
-    return launch_dyn(stage_scan_kernel<Tin, C, D>, dim3(p.N * p.H * (D / 64)), smem, st, p);
+    return launch_dyn(stage_scan_kernel<Tin, C, D>, dim3(p.N * p.H * ((p.Vr + 63) / 64)), smem, st, p);
   });
 }
 
@@ -399,7 +400,7 @@ hipError_t launch_stage_output(const ChunkParams &p, hipStream_t st) {
   return dispatch(p, [&]<typename Tin, int C, int D>() {
     using TL = Tile<Tin, C, D>;
     const size_t smem = sizeof(Tin) * C * TL::LDT + sizeof(float) * (C * TL::LDB + D + C * TL::LDA + C);
-    return launch_dyn(stage_output_kernel<Tin, C, D>, dim3(p.max_chunks, p.H, D / 64), smem, st, p);
+    return launch_dyn(stage_output_kernel<Tin, C, D>, dim3(p.max_chunks, p.H, (p.Vr + 63) / 64), smem, st, p);
   });
 }
 

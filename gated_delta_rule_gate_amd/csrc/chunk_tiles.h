@@ -95,7 +95,7 @@ struct Tile {
 // tile of row stride lds; rows L..ROWS-1 are zero-filled. 16-byte accesses,
 // all loads of a thread issued before its first LDS write.
 template <typename T, int NT, int ROWS, int COLS>
-__device__ __forceinline__ void load_rows(T *s, int lds, const T *g, int64_t ldg, int L) {
+__device__ __forceinline__ void load_rows(T *s, int lds, const T *g, int64_t ldg, int L, int ncol = COLS) {
   constexpr int EPV = 16 / (int)sizeof(T);
   constexpr int VPR = COLS / EPV, NV = ROWS * VPR, IT = (NV + NT - 1) / NT;
   u32x4_t buf[IT];
@@ -104,7 +104,9 @@ __device__ __forceinline__ void load_rows(T *s, int lds, const T *g, int64_t ldg
     const int idx = it * NT + tid_opaque();
     const int r = idx / VPR, c = (idx % VPR) * EPV;
     buf[it] = u32x4_t{0u, 0u, 0u, 0u};
-    if ((NV % NT == 0 || idx < NV) && r < L) buf[it] = *reinterpret_cast<const u32x4_t *>(g + (int64_t)r * ldg + c);
+    // columns >= ncol read as zeros (ncol is a multiple of the vector width)
+    if ((NV % NT == 0 || idx < NV) && r < L && c < ncol)
+      buf[it] = *reinterpret_cast<const u32x4_t *>(g + (int64_t)r * ldg + c);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -428,12 +430,12 @@ __device__ __forceinline__ void pad_cumsum(float *sB, int ldb, float *sBL, int L
 // rows >= L of k~^T are zero.
 template <typename Tin, int NT, int C, int D>
 __device__ __forceinline__ void make_ktilde_t_global(Tin *sKT, const Tin *gK, int64_t ldk, const float *gB,
-                                                     int64_t ld, const float *sBL, int L) {
+                                                     int64_t ld, const float *sBL, int L, int kr) {
   using TL = Tile<Tin, C, D>;
   for (int idx = tid_opaque(); idx < C * D; idx += NT) {
     const int i = idx % D, c = idx / D;  // consecutive threads walk the channels (coalesced reads)
     float v = 0.f;
-    if (c < L) v = to_f32(gK[(int64_t)c * ldk + i]) * fast_exp2(sBL[i] - gB[(int64_t)c * ld + i]);
+    if (c < L && i < kr) v = to_f32(gK[(int64_t)c * ldk + i]) * fast_exp2(sBL[i] - gB[(int64_t)c * ld + i]);
     sKT[i * TL::LDKT + c] = from_f32<Tin>(v);
   }
 }
@@ -550,7 +552,8 @@ __device__ __forceinline__ void state_update(f32x4_t (&h)[D / 16][NVW], const Ti
 // tile (t, v) covers rows 16t.., columns col0 + 16v... Rows >= L read as 0 /
 // are not stored.
 template <int RT, int NVW>
-__device__ __forceinline__ void load_strip(f32x4_t (&x)[RT][NVW], const float *g, int64_t ld, int col0, int L) {
+__device__ __forceinline__ void load_strip(f32x4_t (&x)[RT][NVW], const float *g, int64_t ld, int col0, int L,
+                                           int ncol = 1 << 30) {
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
@@ -559,13 +562,14 @@ __device__ __forceinline__ void load_strip(f32x4_t (&x)[RT][NVW], const float *g
     for (int v = 0; v < NVW; ++v)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * t + 4 * grp + e;
-        x[t][v][e] = (r < L) ? g[(int64_t)r * ld + col0 + 16 * v + n16] : 0.f;
+        const int r = 16 * t + 4 * grp + e, c = col0 + 16 * v + n16;
+        x[t][v][e] = (r < L && c < ncol) ? g[(int64_t)r * ld + c] : 0.f;
       }
 }
 
 template <typename T, int RT, int NVW>
-__device__ __forceinline__ void store_strip(T *g, int64_t ld, int col0, int L, const f32x4_t (&x)[RT][NVW]) {
+__device__ __forceinline__ void store_strip(T *g, int64_t ld, int col0, int L, const f32x4_t (&x)[RT][NVW],
+                                            int ncol = 1 << 30) {
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
@@ -574,8 +578,8 @@ __device__ __forceinline__ void store_strip(T *g, int64_t ld, int col0, int L, c
     for (int v = 0; v < NVW; ++v)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * t + 4 * grp + e;
-        if (r < L) g[(int64_t)r * ld + col0 + 16 * v + n16] = from_f32<T>(x[t][v][e]);
+        const int r = 16 * t + 4 * grp + e, c = col0 + 16 * v + n16;
+        if (r < L && c < ncol) g[(int64_t)r * ld + c] = from_f32<T>(x[t][v][e]);
       }
 }
 

@@ -33,10 +33,13 @@ __device__ __forceinline__ int slot_of(const int32_t *cu, int N, int64_t r) {
   return lo;
 }
 
-template <int K>
-__global__ __launch_bounds__(K) void gate_cumsum_kernel(GateCumsumParams p) {
+// One thread per channel: KP >= K threads, the ones past K idle.
+template <int KP>
+__global__ __launch_bounds__(KP) void gate_cumsum_kernel(GateCumsumParams p) {
   const int h = blockIdx.y;
   const int i = threadIdx.x;
+  const int K = p.K;
+  if (i >= K) return;  // no barriers below
   // rows outside [cu_seqlens[0], cu_seqlens[N]) are neither read nor written
   const int64_t beg = p.cu ? (int64_t)p.cu[0] : 0;
   const int64_t end = p.cu ? (int64_t)p.cu[p.N] : (int64_t)p.B * p.T;
@@ -105,12 +108,10 @@ hipError_t launch_gate_cumsum(const GateCumsumParams &p, hipStream_t st) {
   if (nblk == 0 || p.H == 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nblk, p.H);
-  switch (p.K) {
-    case 64: hipLaunchKernelGGL(gate_cumsum_kernel<64>, grid, dim3(64), 0, st, p); break;
-    case 128: hipLaunchKernelGGL(gate_cumsum_kernel<128>, grid, dim3(128), 0, st, p); break;
-    case 256: hipLaunchKernelGGL(gate_cumsum_kernel<256>, grid, dim3(256), 0, st, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (p.K < 1 || p.K > 256) return hipErrorInvalidValue;
+  if (p.K <= 64) hipLaunchKernelGGL(gate_cumsum_kernel<64>, grid, dim3(64), 0, st, p);
+  else if (p.K <= 128) hipLaunchKernelGGL(gate_cumsum_kernel<128>, grid, dim3(128), 0, st, p);
+  else hipLaunchKernelGGL(gate_cumsum_kernel<256>, grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -23,7 +23,11 @@ kda_status hip_status(hipError_t e) {
 
 bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool width_ok(int d) { return d == 64 || d == 128 || d == 256; }
+// Widths of q/k (K) and v (V): multiples of 8 up to 256, so every row of a
+// 16-byte aligned tensor starts 16-byte aligned. The kernels run at the tile
+// width pad_width(max(K, V)) and mask the rest.
+bool width_ok(int d) { return d >= 8 && d <= 256 && d % 8 == 0; }
+int pad_width(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
 
 // Checks shared by both entry points.
 kda_status check_common(const kda_args *a, const void *q, const void *k, const void *v, const float *g,
@@ -185,7 +189,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool chunk_shape_ok(const kda_args *a) {
   if (!a) return false;
   if (a->B < 1 || a->T < 0 || a->H < 1 || a->N < 0) return false;
-  if (a->K != a->V || !width_ok(a->K)) return false;
+  if (!width_ok(a->K) || !width_ok(a->V)) return false;
   if (a->chunk_size != 32 && a->chunk_size != 64) return false;
   return true;
 }
@@ -207,10 +211,10 @@ struct WsLayout {
 WsLayout staged_layout(const kda_args *a) {
   WsLayout L{};
   const size_t rows = (size_t)a->B * a->T * a->H;
-  const size_t D = a->K, C = a->chunk_size;
+  const size_t D = pad_width(std::max(a->K, a->V)), C = a->chunk_size;
   const size_t nch = (size_t)std::max<int64_t>(max_chunks(a, true), max_chunks(a, false));
   const size_t sz[9] = {sizeof(int32_t) * (a->N + 1), 4 * rows * D, 4 * rows * C, 4 * rows * C, 4 * rows * C,
-                        4 * rows * D, 4 * rows * D, 4 * rows * D, 4 * nch * a->H * D * D};
+                        4 * rows * D, 4 * rows * D, 4 * rows * D, 4 * nch * a->H * (size_t)a->K * a->V};
   size_t cur = 0;
   for (int i = 0; i < 9; ++i) {
     L.off[i] = cur;
@@ -232,7 +236,6 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
   if (s != KDA_OK) return s;
   if ((s = check_slots(a, cu)) != KDA_OK) return s;
   if (a->chunk_size != 32 && a->chunk_size != 64) return KDA_ERR_CHUNK;
-  if (a->K != a->V) return KDA_ERR_UNSUPPORTED;
   if (a->schedule != KDA_SCHED_AUTO && a->schedule != KDA_SCHED_STAGED && a->schedule != KDA_SCHED_FUSED)
     return KDA_ERR_SHAPE;
   p = kda::ChunkParams{};
@@ -253,7 +256,9 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
   p.B = a->B;
   p.T = a->T;
   p.H = a->H;
-  p.D = a->K;
+  p.D = pad_width(std::max(a->K, a->V));
+  p.Kr = a->K;
+  p.Vr = a->V;
   p.N = n_slots(a, cu);
   p.C = a->chunk_size;
   p.is_bf16 = a->dtype == KDA_BF16;
@@ -302,7 +307,7 @@ kda_status run_stage(const kda::ChunkParams &p, int stage, hipStream_t st) {
 extern "C" size_t kda_chunk_workspace_bytes(const kda_args *a) {
   if (!chunk_shape_ok(a)) return 0;
   kda::ChunkParams p{};
-  p.D = a->K;
+  p.D = pad_width(std::max(a->K, a->V));
   p.is_bf16 = a->dtype == KDA_BF16;
   if (a->schedule != KDA_SCHED_STAGED && kda::fused_supported(p)) return align_up(sizeof(int32_t) * (a->N + 1));
   if (a->schedule == KDA_SCHED_FUSED) return 0;

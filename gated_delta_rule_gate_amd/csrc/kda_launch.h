@@ -40,10 +40,14 @@ struct GateCumsumParams {
 
 hipError_t launch_gate_cumsum(const GateCumsumParams &p, hipStream_t st);
 
-// Chunked prefill. D = K = V. Intermediates of the staged schedule are fp32,
+// Chunked prefill. The kernels run at a tile width D in {64, 128, 256} that
+// covers both real widths Kr (q, k, g channels) and Vr (v, o columns); channels
+// >= Kr and columns >= Vr are loaded as zeros, which leaves every product
+// exact, and are never stored. Intermediates of the staged schedule are fp32,
 // token-major like the inputs: b, w, u, vnew [B*T, H, D]; Akk, Aqk, Tm
-// [B*T, H, C] (column = row within the chunk); hc [n_chunks, H, D, D], the
-// state at the start of every chunk, chunks numbered slot by slot.
+// [B*T, H, C] (column = row within the chunk); hc [n_chunks, H, Kr, Vr], the
+// state at the start of every chunk, chunks numbered slot by slot (the layout
+// of h0 and ht).
 struct ChunkParams {
   const void *q, *k, *v;
   const float *g, *beta, *h0;
@@ -54,6 +58,7 @@ struct ChunkParams {
   float lower_bound, scale;
   int gate_kind;
   int B, T, H, D, N, C;
+  int Kr, Vr;          // real widths of q/k/g and of v/o (<= D, multiples of 8)
   bool is_bf16;
   int q_l2norm;        // scale each output row by 1/sqrt(|q|^2 + 1e-6)
   int Hk;              // q/k heads; value head h reads q/k head h / (H / Hk)

@@ -17,6 +17,11 @@
 // Thread layout: thread = (column group cg of 4 adjacent columns, row group rg);
 // it holds RPT rows x 4 columns. A wave's 16-byte loads of the state cover whole
 // 512-byte rows, so the state streams through HBM fully coalesced.
+//
+// Widths K and V that are not 64, 128 or 256 run in the next larger tile
+// (KP rows, value blocks of BV columns): channels past K enter as zeros and the
+// state rows and value columns past the real widths are neither loaded nor
+// stored, which leaves every reduction exact.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -62,11 +67,12 @@ struct RecCfg {
   static_assert(kThreads % kCG == 0 && K % kRG == 0, "tile");
 };
 
-template <typename Tin, int K, int BV>
+template <typename Tin, int KP, int BV>
 __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentParams p) {
-  using Cfg = RecCfg<K, BV>;
+  using Cfg = RecCfg<KP, BV>;
   constexpr int RPT = Cfg::kRPT, CG = Cfg::kCG, RG = Cfg::kRG;
-  const int nvb = p.V / BV;
+  const int K = p.K;
+  const int nvb = (p.V + BV - 1) / BV;
   const int vb = blockIdx.x % nvb;
   const int nh = blockIdx.x / nvb;
   const int n = nh / p.H, h = nh % p.H;
@@ -74,6 +80,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
   const int cg = tid % CG, rg = tid / CG;
   const int row0 = rg * RPT;
   const int col0 = vb * BV + cg * 4;
+  const bool col_ok = col0 < p.V;  // four columns, all inside V or none (V % 4 == 0)
 
   const SlotRange sr = slot_range(p.cu, n, p.T);
   const int64_t sbase = ((int64_t)(n * p.H + h) * K) * p.V;
@@ -83,13 +90,14 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
   if (p.h0) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-      S[r] = load_state4(p.h0 + sbase + (int64_t)(row0 + r) * p.V + col0);
+      S[r] = (col_ok && row0 + r < K) ? load_state4(p.h0 + sbase + (int64_t)(row0 + r) * p.V + col0)
+                                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
   } else {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  __shared__ float s_k[2][K], s_q[2][K], s_a[2][K];
+  __shared__ float s_k[2][KP], s_q[2][KP], s_a[2][KP];
   __shared__ float s_v[2][BV];
   __shared__ float s_red[2][RG][BV];
   __shared__ float s_d[BV];
@@ -115,7 +123,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
       nq = to_f32(qp[thk * K + tid]);
       ng = p.g[th * K + tid];
     }
-    if (tid < BV) nv = to_f32(vp[th * p.V + vb * BV + tid]);
+    if (tid < BV && vb * BV + tid < p.V) nv = to_f32(vp[th * p.V + vb * BV + tid]);
     if (tid == 0) nb = p.beta[th];
   };
   if (sr.len > 0) fetch(0);
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
     const int buf = i & 1;
     // ---- phase A: stage this token's inputs in LDS, prefetch the next ----
     float kq = 0.f, qq = 0.f;
-    if (tid < K) {
+    if (tid < KP) {  // channels >= K hold zeros (never fetched)
       s_k[buf][tid] = nk;
       s_q[buf][tid] = nq;
       s_a[buf][tid] = fast_exp2(gate_log2(p.gate_kind, ng, dt, expA, p.lower_bound));
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
     __syncthreads();
 
     // ---- phase C: delta and the output ----
-    if (tid < BV) {
+    if (tid < BV) {  // columns >= V compute zeros and are not stored
       float sk = 0.f, sq = 0.f;
 #pragma unroll
       for (int g2 = 0; g2 < RG; ++g2) {
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
         for (int w = 0; w < NWAVE; ++w) qqs += s_qq[buf][w];
         os *= rsqrtf(qqs + kQNormEps);
       }
-      op[th * p.V + vb * BV + tid] = from_f32<Tin>(os * (sq + kqs * d));
+      if (vb * BV + tid < p.V) op[th * p.V + vb * BV + tid] = from_f32<Tin>(os * (sq + kqs * d));
     }
     __syncthreads();
 
@@ -195,33 +203,31 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
   if (p.ht && !(sr.len == 0 && p.ht == p.h0)) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-      store_state4(p.ht + sbase + (int64_t)(row0 + r) * p.V + col0, S[r]);
+      if (col_ok && row0 + r < K) store_state4(p.ht + sbase + (int64_t)(row0 + r) * p.V + col0, S[r]);
   }
 }
 
-template <typename Tin, int K, int BV>
+template <typename Tin, int KP, int BV>
 static hipError_t launch_rec(const RecurrentParams &p, hipStream_t st) {
-  const int grid = p.N * p.H * (p.V / BV);
+  const int grid = p.N * p.H * ((p.V + BV - 1) / BV);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((recurrent_kernel<Tin, K, BV>), dim3(grid), dim3(RecCfg<K, BV>::kThreads), 0, st, p);
+  hipLaunchKernelGGL((recurrent_kernel<Tin, KP, BV>), dim3(grid), dim3(RecCfg<KP, BV>::kThreads), 0, st, p);
   return hipGetLastError();
 }
 
-template <typename Tin, int K>
+template <typename Tin, int KP>
 static hipError_t launch_rec_k(const RecurrentParams &p, hipStream_t st) {
   // value block: 128 columns when V allows (one 64 KB contiguous state block at K = 128)
-  if (KDA_REC_MAX_BV >= 128 && p.V % 128 == 0) return launch_rec<Tin, K, 128>(p, st);
-  return launch_rec<Tin, K, 64>(p, st);
+  if (KDA_REC_MAX_BV >= 128 && p.V % 128 == 0) return launch_rec<Tin, KP, 128>(p, st);
+  return launch_rec<Tin, KP, 64>(p, st);
 }
 
 template <typename Tin>
 static hipError_t launch_rec_t(const RecurrentParams &p, hipStream_t st) {
-  switch (p.K) {
-    case 64: return launch_rec_k<Tin, 64>(p, st);
-    case 128: return launch_rec_k<Tin, 128>(p, st);
-    case 256: return launch_rec_k<Tin, 256>(p, st);
-  }
-  return hipErrorInvalidValue;
+  if (p.K < 1 || p.K > 256 || p.V < 1 || p.V > 256) return hipErrorInvalidValue;
+  if (p.K <= 64) return launch_rec_k<Tin, 64>(p, st);
+  if (p.K <= 128) return launch_rec_k<Tin, 128>(p, st);
+  return launch_rec_k<Tin, 256>(p, st);
 }
 
 hipError_t launch_recurrent(const RecurrentParams &p, hipStream_t st) {

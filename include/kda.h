@@ -55,7 +55,7 @@ typedef enum {
   KDA_ERR_GATE = 5,        /* gate kind unknown, A_log missing, lower bound range  */
   KDA_ERR_ALIGN = 6,       /* a tensor pointer is not 16-byte aligned              */
   KDA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the query says        */
-  KDA_ERR_UNSUPPORTED = 8, /* valid but not implemented (e.g. K not in {64,128,256}) */
+  KDA_ERR_UNSUPPORTED = 8, /* valid but not implemented (e.g. K or V not a multiple of 8 in [8, 256]) */
   KDA_ERR_HIP = 9          /* a HIP launch failed                                  */
 } kda_status;
 
@@ -147,7 +147,7 @@ size_t kda_chunk_workspace_bytes(const kda_args *args);
  *   cu_seqlens  int32 [N + 1] or NULL (dense: sequences of T rows)
  *   g_out       fp32 [B, T, H, K] device pointer; must not overlap g_in
  *               (KDA_ERR_SHAPE). Rows at or beyond cu_seqlens[N] are not written.
- * Supported: K in {64, 128, 256}; chunk_size in {1, 32, 64} (else KDA_ERR_CHUNK).
+ * Supported: K a multiple of 8 in [8, 256]; chunk_size in {1, 32, 64} (else KDA_ERR_CHUNK).
  */
 kda_status kda_gate_cumsum(const kda_args *args, const float *g_in, const int32_t *cu_seqlens, int chunk_size,
                            float *g_out, void *stream);
@@ -175,7 +175,12 @@ kda_status kda_gate_cumsum(const kda_args *args, const float *g_in, const int32_
  *   ht           fp32 [N, H, K, V] or NULL; may alias h0
  *   workspace    device buffer of ws_bytes >= kda_chunk_workspace_bytes(args),
  *                256-byte aligned; contents on entry are ignored
- * Supported: K == V in {64, 128, 256}; chunk_size in {32, 64}; dtype bf16 or fp32.
+ * Supported: K and V multiples of 8 in [8, 256], equal or not ("FLA KDA Skill",
+ * section "Correctness checklist": D != Dv); chunk_size in {32, 64}; dtype bf16
+ * or fp32. The kernels run at the tile width 64, 128 or 256 that covers
+ * max(K, V), with channels past K and value columns past V masked to zero, so
+ * other widths cost what the next tile width costs. The fused schedule runs
+ * bf16 with max(K, V) <= 128; other cases run the staged one.
  */
 kda_status kda_chunk_fwd(const kda_args *args, const void *q, const void *k, const void *v, const float *g,
                          const float *beta, const float *h0, const int32_t *cu_seqlens, void *o, float *ht,
@@ -221,7 +226,9 @@ kda_status kda_chunk_fwd_states(const kda_args *args, const void *q, const void 
  * Same arguments and layouts as kda_chunk_fwd, with no workspace; g is the
  * per-token decay of gate_kind LOG2 (log2 units, as the recurrent contract
  * has it), LOGE, SAFE or SOFTPLUS. args->chunk_size and args->schedule are ignored.
- * Supported: K in {64, 128, 256}, V in {64, 128, 256}.
+ * Supported: K and V multiples of 8 in [8, 256] (non-power-of-two widths run
+ * in the next power-of-two tile with the rest masked, "Add fused recurrent_kda
+ * ...", section "Test Plan").
  */
 kda_status kda_recurrent_fwd(const kda_args *args, const void *q, const void *k, const void *v, const float *g,
                              const float *beta, const float *h0, const int32_t *cu_seqlens, void *o, float *ht,

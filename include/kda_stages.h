@@ -8,6 +8,8 @@
  * kda_staged_workspace_offset reports, all fp32, token-major like the inputs:
  *
  *   CHUNK_OFF int32 [N + 1]   chunks before each slot (packed batches only)
+ *   (D = the tile width: 64, 128 or 256, the smallest >= max(K, V); columns
+ *   past K or V hold zeros)
  *   B         [B*T, H, D]     chunk-local gate cumsum, log2 units (step 1)
  *   AKK, AQK  [B*T, H, C]     intra-chunk grams; column = row within the chunk;
  *                             beta folded into A_kk rows, the query scale into
@@ -15,7 +17,7 @@
  *   T         [B*T, H, C]     (I + A_kk)^-1 (step 3)
  *   W, U      [B*T, H, D]     WY factors (step 4)
  *   VNEW      [B*T, H, D]     u - w h (step 5)
- *   HC        [n_chunks, H, D, D]  state at the start of each chunk, chunks
+ *   HC        [n_chunks, H, K, V]  state at the start of each chunk, chunks
  *                             numbered slot by slot (step 5)
  *
  * The steps follow the same passages as kda_chunk_fwd in kda.h. Arguments,

@@ -66,7 +66,9 @@ FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fail
     (dict(dtype=7), 3),
     (dict(gate_kind=9), 5),
     (dict(gate_kind=1), 5),            # SAFE without A_log
-    (dict(K=48), 8),
+    (dict(K=44), 8),                   # widths are multiples of 8
+    (dict(K=264), 8),                  # ... up to 256
+    (dict(V=0), 2),
     (dict(B=2, N=1), 2),               # dense needs N == B
     (dict(H=0), 2),
     (dict(q_l2norm=2), 2),             # the q_l2norm flag is 0 or 1
@@ -101,7 +103,7 @@ FAKE2 = ctypes.c_void_p(0x40000000)  # a second aligned address far from FAKE (n
     (dict(gate_kind=0), 16, 4),                 # chunk size not in {1, 32, 64}
     (dict(gate_kind=3), 64, 5),                 # a pre-cumsummed gate is no input here
     (dict(gate_kind=2), 64, 5),                 # SOFTPLUS without A_log
-    (dict(gate_kind=0, K=48), 64, 8),
+    (dict(gate_kind=0, K=44), 64, 8),
     (dict(gate_kind=0, B=2, N=1), 64, 2),
 ])
 def test_gate_cumsum_rejects(kda_lib, kw, chunk, code):
@@ -120,8 +122,8 @@ def test_gate_cumsum_rejects_overlap_and_null(kda_lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(gate_kind=4), 5),                    # per-token log2 gate is the recurrent contract
     (dict(gate_kind=0, chunk_size=16), 4),
-    (dict(gate_kind=0, V=64), 8),              # K != V
-    (dict(gate_kind=0, K=48, V=48), 8),
+    (dict(gate_kind=0, V=12), 8),              # widths are multiples of 8
+    (dict(gate_kind=0, K=52, V=48), 8),
 ])
 def test_chunk_rejects(kda_lib, kw, code):
     a = _args(**kw)
@@ -144,7 +146,7 @@ def test_chunk_states_count(kda_lib):
     a = _args(gate_kind=0, B=1, N=5, T=420, chunk_size=32)
     assert kda_lib.kda_chunk_states_count(ctypes.byref(a), 1) == 14 + 5
     assert kda_lib.kda_chunk_states_count(ctypes.byref(a), 0) == 0  # dense needs N == B
-    assert kda_lib.kda_chunk_states_count(ctypes.byref(_args(gate_kind=0, V=64)), 0) == 0  # K != V
+    assert kda_lib.kda_chunk_states_count(ctypes.byref(_args(gate_kind=0, V=68)), 0) == 0  # V % 8 != 0
 
 
 def test_chunk_states_rejects(kda_lib):

@@ -64,7 +64,7 @@ def test_gate_cumsum_dense_ragged(gate, C):
     _check_b(got, want)
 
 
-@pytest.mark.parametrize("K", [64, 256])
+@pytest.mark.parametrize("K", [64, 256, 40, 96, 200])  # and non-powers of two (multiples of 8)
 def test_gate_cumsum_widths(K):
     need_gpu()
     d = _inputs(1, 150, 2, K, 2100 + K, "safe")

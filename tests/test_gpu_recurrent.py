@@ -172,6 +172,6 @@ def test_rejects_grad_and_bad_args():
     with pytest.raises(KdaError, match="GATE"):
         recurrent_kda(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], gate_kind="safe", A_log=dd["A_log"],
                       lower_bound=-6.0)
-    q48 = torch.zeros((1, 4, 1, 48), device="cuda")
+    q44 = torch.zeros((1, 4, 1, 44), device="cuda")  # widths are multiples of 8
     with pytest.raises(KdaError, match="UNSUPPORTED"):
-        recurrent_kda(q48, q48, dd["v"], q48, dd["beta"])
+        recurrent_kda(q44, q44, dd["v"], q44, dd["beta"])
