@@ -29,7 +29,7 @@ class KdaArgs(ctypes.Structure):
                 ("V", ctypes.c_int), ("N", ctypes.c_int), ("chunk_size", ctypes.c_int), ("dtype", ctypes.c_int),
                 ("scale", ctypes.c_float), ("gate_kind", ctypes.c_int), ("A_log", ctypes.c_void_p),
                 ("dt_bias", ctypes.c_void_p), ("lower_bound", ctypes.c_float), ("schedule", ctypes.c_int),
-                ("Hk", ctypes.c_int), ("q_l2norm", ctypes.c_int)]
+                ("Hk", ctypes.c_int), ("q_l2norm", ctypes.c_int), ("beta_logits", ctypes.c_int)]
 
 
 def lib():
@@ -100,7 +100,7 @@ def _check_tensors(named, device):
 
 
 def make_args(q, v, H, N, gate_kind, chunk_size=64, scale=None, A_log=None, dt_bias=None, lower_bound=-5.0,
-              schedule="auto", q_l2norm=False):
+              schedule="auto", q_l2norm=False, beta_logits=False):
     B, T, Hk, K = q.shape
     V = v.shape[-1]
     a = KdaArgs()
@@ -115,6 +115,7 @@ def make_args(q, v, H, N, gate_kind, chunk_size=64, scale=None, A_log=None, dt_b
     a.lower_bound = float(lower_bound) if lower_bound is not None else 0.0
     a.schedule = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
     a.q_l2norm = 1 if q_l2norm else 0
+    a.beta_logits = 1 if beta_logits else 0
     return a
 
 
@@ -144,7 +145,7 @@ def _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias):
 
 def recurrent_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_final_state=False,
                   gate_kind="log2", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None, final_state=None,
-                  out=None, q_l2norm=False):
+                  out=None, q_l2norm=False, beta_logits=False):
     """Fused token-sequential KDA forward. Returns (o, ht); ht is None unless requested.
 
     g is the per-token decay (log2 units by default; ``gate_kind`` "loge", "safe"
@@ -153,6 +154,7 @@ def recurrent_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, outp
     an in-place state update. ``out`` may preallocate o; rows outside the
     packed contract are left as they are. ``q_l2norm=True`` takes raw q and
     normalises it inside (each output row scaled by 1/sqrt(|q|^2 + 1e-6)).
+    ``beta_logits=True`` takes beta as logits (the sigmoid runs in the kernel).
     """
     B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
     o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
@@ -163,7 +165,7 @@ def recurrent_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, outp
         _require(ht.shape == (N, H, K, V) and ht.dtype == torch.float32 and ht.is_contiguous(),
                  "final_state must be fp32 [N, H, K, V]")
     a = make_args(q, v, H, N, gate_kind, scale=scale, A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
-                  q_l2norm=q_l2norm)
+                  q_l2norm=q_l2norm, beta_logits=beta_logits)
     check(lib().kda_recurrent_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(ht), _stream()))
     return o, ht
@@ -197,7 +199,7 @@ def gate_cumsum(g, *, chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None,
 def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_final_state=False,
               chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None,
               schedule="auto", final_state=None, out=None, q_l2norm=False, return_intermediate_states=False,
-              intermediate_states=None):
+              intermediate_states=None, beta_logits=False):
     """Chunked KDA prefill forward. Returns (o, ht); ht is None unless requested.
 
     g is the raw gate input for ``gate_kind`` "safe" / "softplus" (activation in
@@ -205,6 +207,7 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
     ``gate_cumsum`` with the same chunk size for "log2_cumsum". ``out`` may
     preallocate o. ``q_l2norm=True`` takes raw q and normalises it inside: each
     output row is scaled by 1/sqrt(|q|^2 + 1e-6) (o is linear in each q row).
+    ``beta_logits=True`` takes beta as logits (the sigmoid runs in the kernels).
 
     ``return_intermediate_states=True`` returns (o, ht, h_states): the fp32 state
     entering every chunk, [B, ceil(T / C), H, K, V] for a dense batch and
@@ -218,7 +221,7 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
     if ht is None and output_final_state:
         ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
     a = make_args(q, v, H, N, gate_kind, chunk_size=chunk_size, scale=scale, A_log=A_log, dt_bias=dt_bias,
-                  lower_bound=lower_bound, schedule=schedule, q_l2norm=q_l2norm)
+                  lower_bound=lower_bound, schedule=schedule, q_l2norm=q_l2norm, beta_logits=beta_logits)
     L = lib()
     ws_bytes = L.kda_chunk_workspace_bytes(ctypes.byref(a))
     ws = torch.empty((max(int(ws_bytes), 256),), dtype=torch.uint8, device=q.device)

@@ -136,7 +136,7 @@ struct ChunkRegs {
   template <int GK>
   __device__ __forceinline__ void store(bool loader, Tin *sQ, Tin *sK, Tin *sV, float *sB, float *sBeta,
                                         const float *sDt, int L, float expA, float lower_bound, bool qnorm,
-                                        float *sQn) const {
+                                        float *sQn, bool blogit) const {
     using TL = Tile<Tin, C, D>;
     wait_vmem();
     if (loader && qnorm) {
@@ -187,7 +187,7 @@ struct ChunkRegs {
         *reinterpret_cast<f32x4_t *>(sB + r * TL::LDB + c) = la;
       }
     }
-    if (tid_opaque() < C) sBeta[tid_opaque()] = beta;
+    if (tid_opaque() < C) sBeta[tid_opaque()] = (blogit && tid_opaque() < L) ? sigmoid_f32(beta) : beta;
   }
 };
 
@@ -292,7 +292,8 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     const int L = min(C, sr.len - c * C);
     const int64_t off = t0 * ld + h * Vr;
     float *sDecay = sDecay2 + (c & 1) * D;
-    regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound, p.q_l2norm != 0, sQn);
+    regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound, p.q_l2norm != 0, sQn,
+                            p.beta_logits != 0);
     state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((c + 1) & 1) * D);  // chunk c - 1's
     if (hcs && owner) store_strip<float, DT, NVW>(hcs + (int64_t)c * p.H * Kr * Vr, Vr, col0, Kr, hs, Vr);
     __syncthreads();

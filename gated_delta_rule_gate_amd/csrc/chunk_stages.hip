@@ -51,7 +51,11 @@ __device__ __forceinline__ float head_expA(const ChunkParams &p, int h) {
 
 template <int C>
 __device__ __forceinline__ void load_beta(float *sBeta, const ChunkParams &p, int64_t t0, int h, int L) {
-  for (int r = threadIdx.x; r < C; r += kNT) sBeta[r] = (r < L) ? p.beta[(t0 + r) * p.H + h] : 0.f;
+  for (int r = threadIdx.x; r < C; r += kNT) {
+    float b = (r < L) ? p.beta[(t0 + r) * p.H + h] : 0.f;
+    if (p.beta_logits && r < L) b = sigmoid_f32(b);
+    sBeta[r] = b;
+  }
 }
 
 template <int ROWS, int COLS, int LDS>

@@ -35,6 +35,7 @@ kda_status check_common(const kda_args *a, const void *q, const void *k, const v
   if (!a) return KDA_ERR_NULL;
   if (a->B < 1 || a->T < 0 || a->H < 1 || a->N < 0) return KDA_ERR_SHAPE;
   if (a->q_l2norm != 0 && a->q_l2norm != 1) return KDA_ERR_SHAPE;
+  if (a->beta_logits != 0 && a->beta_logits != 1) return KDA_ERR_SHAPE;
   if (a->Hk < 0 || (a->Hk > 0 && a->H % a->Hk != 0)) return KDA_ERR_SHAPE;
   if (a->K < 1 || a->V < 1) return KDA_ERR_SHAPE;
   if (a->dtype != KDA_BF16 && a->dtype != KDA_F32) return KDA_ERR_DTYPE;
@@ -175,6 +176,7 @@ extern "C" kda_status kda_recurrent_fwd(const kda_args *a, const void *q, const 
   p.is_bf16 = a->dtype == KDA_BF16;
   p.q_l2norm = a->q_l2norm;
   p.Hk = a->Hk > 0 ? a->Hk : a->H;
+  p.beta_logits = a->beta_logits;
   return hip_status(kda::launch_recurrent(p, (hipStream_t)stream));
 }
 
@@ -264,6 +266,7 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
   p.is_bf16 = a->dtype == KDA_BF16;
   p.q_l2norm = a->q_l2norm;
   p.Hk = a->Hk > 0 ? a->Hk : a->H;
+  p.beta_logits = a->beta_logits;
   p.max_chunks = (int)max_chunks(a, cu != nullptr);
   if (a->schedule == KDA_SCHED_FUSED && !kda::fused_supported(p)) return KDA_ERR_UNSUPPORTED;
   const size_t need = kda_chunk_workspace_bytes(a);

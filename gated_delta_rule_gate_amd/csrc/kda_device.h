@@ -99,6 +99,9 @@ __device__ __forceinline__ float gate_log2(int kind, float x, float dt, float ex
   return c3 * sp;
 }
 
+// beta from its logit: 1 / (1 + e^-x), hardware exp2 and reciprocal.
+__device__ __forceinline__ float sigmoid_f32(float x) { return fast_rcp(1.0f + fast_exp2(-x * kLog2e)); }
+
 // s_waitcnt vmcnt(0): every vector memory load this wave issued has returned.
 // Used where registers filled by a prefetch issued in an earlier loop
 // iteration are consumed, so the wait never depends on the compiler's

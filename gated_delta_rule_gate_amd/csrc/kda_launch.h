@@ -22,6 +22,7 @@ struct RecurrentParams {
   bool is_bf16;
   int q_l2norm;  // scale each output row by 1/sqrt(|q|^2 + 1e-6)
   int Hk;        // q/k heads; value head h reads q/k head h / (H / Hk)
+  int beta_logits;  // beta holds logits: the kernel applies the sigmoid
 };
 
 hipError_t launch_recurrent(const RecurrentParams &p, hipStream_t st);
@@ -62,6 +63,7 @@ struct ChunkParams {
   bool is_bf16;
   int q_l2norm;        // scale each output row by 1/sqrt(|q|^2 + 1e-6)
   int Hk;              // q/k heads; value head h reads q/k head h / (H / Hk)
+  int beta_logits;     // beta holds logits: the kernels apply the sigmoid
   int32_t *chunk_off;  // [N + 1] chunk prefix per slot (packed batches only)
   int max_chunks;      // upper bound of the number of chunks (grid size)
   int vsplit;          // fused schedule: value-column blocks per (sequence, head), set by its launcher

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
       ng = p.g[th * K + tid];
     }
     if (tid < BV && vb * BV + tid < p.V) nv = to_f32(vp[th * p.V + vb * BV + tid]);
-    if (tid == 0) nb = p.beta[th];
+    if (tid == 0) nb = p.beta_logits ? sigmoid_f32(p.beta[th]) : p.beta[th];
   };
   if (sr.len > 0) fetch(0);
 

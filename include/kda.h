@@ -101,6 +101,10 @@ typedef struct {
                               output row is scaled by 1 / sqrt(sum over K of q^2 + 1e-6), which
                               equals running on l2-normalised q (see below). Other values:
                               KDA_ERR_SHAPE                                                   */
+  int beta_logits;         /* 0: beta arrives post-sigmoid (the contract). 1: beta holds raw
+                              logits and every kernel uses 1 / (1 + exp(-beta)) ("FLA KDA
+                              Skill", section "Correctness checklist": raw beta logits and
+                              post-sigmoid beta). Other values: KDA_ERR_SHAPE                 */
 } kda_args;
 
 /*
@@ -169,7 +173,7 @@ kda_status kda_gate_cumsum(const kda_args *args, const float *g_in, const int32_
  *   q, k, v, o   see the layout conventions; dtype args->dtype
  *   g            fp32 [B, T, H, K]; gate_kind LOGE, SAFE, SOFTPLUS or
  *                LOG2_CUMSUM (step (1) already done by kda_gate_cumsum)
- *   beta         fp32 [B, T, H]
+ *   beta         fp32 [B, T, H] (logits when args->beta_logits)
  *   h0           fp32 [N, H, K, V] or NULL (zero initial state)
  *   cu_seqlens   int32 [N + 1] or NULL (dense)
  *   ht           fp32 [N, H, K, V] or NULL; may alias h0

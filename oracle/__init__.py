@@ -94,6 +94,16 @@ def l2norm_rows(x, eps=L2NORM_EPS):
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
 
 
+def beta_from_logits(x):
+    """The logistic sigmoid 1 / (1 + e^-x) in FP64: beta from raw logits ("FLA KDA
+    Skill", section "Correctness checklist": raw beta logits and post-sigmoid beta).
+    Written as e^x / (1 + e^x) for x < 0 so that neither branch overflows.
+    """
+    x = _f64(x)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
 def _offsets(B, T, cu_seqlens):
     if cu_seqlens is None:
         return np.arange(B + 1, dtype=np.int32) * T

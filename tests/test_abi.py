@@ -72,6 +72,7 @@ FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fail
     (dict(B=2, N=1), 2),               # dense needs N == B
     (dict(H=0), 2),
     (dict(q_l2norm=2), 2),             # the q_l2norm flag is 0 or 1
+    (dict(beta_logits=-1), 2),         # so is beta_logits
     (dict(H=3, Hk=2), 2),              # value heads must be a multiple of the q/k heads
 ])
 def test_recurrent_rejects(kda_lib, kw, code):

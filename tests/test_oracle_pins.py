@@ -391,3 +391,15 @@ def test_l2norm_rows_pins(oracle_mod):
     together = f(rows)
     for t in range(rows.shape[1]):
         np.testing.assert_allclose(together[0, t, 0], f(rows[:, t:t + 1])[0, 0, 0], rtol=1e-15, atol=0)
+
+
+def test_beta_from_logits_pins(oracle_mod):
+    """sigma(0) = 1/2, sigma(ln 3) = 3/4 and sigma(-ln 3) = 1/4 exactly; sigma(x) +
+    sigma(-x) = 1; the far tails are 1 and e^x without overflow."""
+    f = oracle_mod.beta_from_logits
+    np.testing.assert_allclose(f(np.array([0.0, math.log(3.0), -math.log(3.0)])), [0.5, 0.75, 0.25],
+                               rtol=0, atol=1e-15)
+    x = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(f(x) + f(-x), 1.0, rtol=0, atol=1e-15)
+    assert f(np.array([800.0]))[0] == 1.0
+    np.testing.assert_allclose(f(np.array([-700.0]))[0], math.exp(-700.0), rtol=1e-12)
