@@ -48,6 +48,10 @@ def _lib():
                                              ip, dp, dp, dp, dp, ctypes.c_int, dp, ctypes.c_double,
                                              dp, dp, dp, ctypes.c_int]
         lib.kda_oracle_recurrent.restype = None
+        lib.kda_oracle_recurrent_bwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                 ip, dp, dp, dp, dp, dp, ctypes.c_double, dp, dp, dp,
+                                                 dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.kda_oracle_recurrent_bwd.restype = None
         _LIB = lib
     return _LIB
 
@@ -133,3 +137,69 @@ def recurrent(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, g_is_log2=
                                 _ptr(q), _ptr(k), _ptr(v), _ptr(g), int(bool(g_is_log2)), _ptr(beta),
                                 float(scale), _ptr(h0a), _ptr(o), _ptr(ht), int(nthreads))
     return o, ht
+
+
+def recurrent_bwd(q, k, v, g, beta, do, dht=None, h0=None, cu_seqlens=None, scale=None, nthreads=0):
+    """Gradients of L = sum(do * o) + sum(dht * ht) through O1 (natural-log gate g).
+
+    Reverse mode through the token recurrence, FP64 (``kda_oracle.c``). Shapes as
+    in ``recurrent``; do [B, T, H, V]; dht [N, H, K, V] or None. Returns (dq, dk,
+    dv, dg, dbeta, dh0), each shaped like its input (dh0 [N, H, K, V]); rows
+    outside the packed contract are NaN. dg is the gradient of the per-token
+    natural-log decay; ``gate_bwd`` carries it to a raw gate input.
+    """
+    q, k, v, g, beta, do = (_f64(a) for a in (q, k, v, g, beta, do))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    cu = _offsets(B, T, cu_seqlens)
+    N = len(cu) - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    h0a = _f64(h0).reshape(N, H, K, V) if h0 is not None else None
+    dhta = _f64(dht).reshape(N, H, K, V) if dht is not None else None
+    dq = np.full((B, T, H, K), np.nan)
+    dk = np.full((B, T, H, K), np.nan)
+    dv = np.full((B, T, H, V), np.nan)
+    dg = np.full((B, T, H, K), np.nan)
+    dbeta = np.full((B, T, H), np.nan)
+    dh0 = np.empty((N, H, K, V))
+    _lib().kda_oracle_recurrent_bwd(N, H, K, V, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                    _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(h0a),
+                                    _ptr(do), _ptr(dhta), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
+                                    _ptr(dh0), int(nthreads))
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+def gate_bwd(kind, x, dg, A_log=None, dt_bias=None, lower_bound=0.0):
+    """Carries dg (gradient of the natural-log decay that ``gate`` returns) back to
+    the raw input x [..., H, K], A_log [H] and dt_bias [H, K] ("FLA KDA Skill",
+    section "Gate modes", differentiated):
+
+      safe      g = lb s(z), z = e^A (x + dt):  dg/dx = dg/d dt = lb s(z)(1 - s(z)) e^A,
+                dg/dA = dg/dx (x + dt)
+      softplus  g = -e^A sp(z), z = x + dt:     dg/dx = dg/d dt = -e^A s(z),  dg/dA = g
+      pre-gated g = x:                           dg/dx = 1, no parameters
+
+    Returns (dx, dA_log [H] or None, ddt_bias [H, K] or None); the parameter
+    gradients sum over every token. Rows of dg that are NaN (outside the packed
+    contract) must be masked by the caller.
+    """
+    x, dg = _f64(x), _f64(dg)
+    H, K = x.shape[-2], x.shape[-1]
+    if kind == GATE_LOGE:
+        return dg.copy(), None, None
+    A = _f64(A_log).reshape(H)
+    dt = _f64(dt_bias).reshape(H, K) if dt_bias is not None else np.zeros((H, K))
+    eA = np.exp(A)[:, None]
+    z0 = x + dt
+    if kind == GATE_SAFE:
+        s = beta_from_logits(eA * z0)
+        gx = lower_bound * s * (1.0 - s) * eA
+        ga = gx * z0
+    else:
+        s = beta_from_logits(z0)
+        gx = -eA * s
+        ga = gate(GATE_SOFTPLUS, x, A_log, dt_bias, lower_bound)
+    dx = dg * gx
+    lead = tuple(range(x.ndim - 2))
+    return dx, np.sum(dg * ga, axis=lead).sum(axis=-1), np.sum(dx, axis=lead)

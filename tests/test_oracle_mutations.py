@@ -32,6 +32,18 @@ C_MUTATIONS = {
                               "acc += S[(int64_t)(j % K) * V + (i % V)] * kt[i];"),
 }
 
+# slips in the reverse-mode pass; each must fail the finite-difference pin
+BWD_MUTATIONS = {
+    "bwd_dq_no_scale": ("dqt[i] = scale * acc;", "dqt[i] = acc;"),
+    "bwd_dk_sign": ("dkt[i] = a1 - bt * a2;", "dkt[i] = a1 + bt * a2;"),
+    "bwd_dg_no_alpha": ("dgt[i] = al * acc;", "dgt[i] = acc;"),
+    "bwd_no_decay_carry": ("dS[(int64_t)i * V + j] = al * dp;", "dS[(int64_t)i * V + j] = dp;"),
+    "bwd_dbeta_drops_state": ("db += acc * (vt[j] - u[j]);", "db += acc * vt[j];"),
+    "bwd_dp_without_beta": ("double dp = dS[(int64_t)i * V + j] - bt * kt[i] * ddl[j];",
+                            "double dp = dS[(int64_t)i * V + j] - kt[i] * ddl[j];"),
+    "bwd_dg_against_new_state": ("acc += dp * Sp[(int64_t)i * V + j];", "acc += dp * St[(int64_t)i * V + j];"),
+}
+
 PY_MUTATIONS = {
     "diag_in_Akk": ("Akk = np.tril(Akk, -1) * bc[:, None]", "Akk = np.tril(Akk) * bc[:, None]"),
     "no_state_decay": ("h_next = np.exp2(bL)[:, None] * h +", "h_next = h +"),
@@ -103,6 +115,29 @@ def test_c_mutation_is_caught(oracle_mod, tmp_path, name):
     oracle._LIB = lib
     try:
         assert _fails_some_pin(RECURRENCE_PINS), "mutation %s survived every pin" % name
+    finally:
+        oracle._LIB = saved
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_bwd_mutation_is_caught(oracle_mod, tmp_path, name):
+    src = open(os.path.join(ORACLE_DIR, "kda_oracle.c")).read()
+    old, new = BWD_MUTATIONS[name]
+    assert src.count(old) == 1, "mutation anchor missing or ambiguous: " + old
+    mutated = tmp_path / "m.c"
+    mutated.write_text(src.replace(old, new, 1))
+    so = tmp_path / "libm.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", str(mutated), "-o", str(so), "-lm"],
+                   check=True)
+    good = oracle._lib()
+    lib = ctypes.CDLL(str(so))
+    for fn in ("kda_oracle_gate", "kda_oracle_recurrent", "kda_oracle_recurrent_bwd"):
+        getattr(lib, fn).argtypes = getattr(good, fn).argtypes
+    saved = oracle._LIB
+    oracle._LIB = lib
+    try:
+        assert _fails_some_pin([("test_recurrent_bwd_finite_differences", {})]), \
+            "mutation %s survived every pin" % name
     finally:
         oracle._LIB = saved
 

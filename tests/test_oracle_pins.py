@@ -403,3 +403,71 @@ def test_beta_from_logits_pins(oracle_mod):
     np.testing.assert_allclose(f(x) + f(-x), 1.0, rtol=0, atol=1e-15)
     assert f(np.array([800.0]))[0] == 1.0
     np.testing.assert_allclose(f(np.array([-700.0]))[0], math.exp(-700.0), rtol=1e-12)
+
+
+def _fd_grad(f, x, eps=1e-6):
+    """Central finite differences of the scalar f at every element of x (in place, restored)."""
+    gr = np.zeros_like(x)
+    flat, gflat = x.reshape(-1), gr.reshape(-1)
+    for i in range(flat.size):
+        keep = flat[i]
+        flat[i] = keep + eps
+        fp = f()
+        flat[i] = keep - eps
+        fm = f()
+        flat[i] = keep
+        gflat[i] = (fp - fm) / (2 * eps)
+    return gr
+
+
+def test_recurrent_bwd_finite_differences(oracle_mod):
+    """The reverse-mode gradients of the token recurrence equal central finite
+    differences of L = sum(do * o) + sum(dht * ht) through the forward oracle, for
+    every input element, on a packed batch with an empty slot (whose dh0 is dht)."""
+    rng = np.random.default_rng(41)
+    lens = [3, 0, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H, K, V, N = int(cu[-1]) + 2, 2, 3, 2, len(lens)
+    q = rng.standard_normal((1, T, H, K))
+    k = rng.standard_normal((1, T, H, K)) / math.sqrt(K)
+    v = rng.standard_normal((1, T, H, V))
+    g = -rng.uniform(0.05, 0.6, (1, T, H, K))
+    beta = rng.uniform(0.1, 0.9, (1, T, H))
+    h0 = rng.standard_normal((N, H, K, V))
+    do = rng.standard_normal((1, T, H, V))
+    dht = rng.standard_normal((N, H, K, V))
+    n = int(cu[-1])
+
+    def loss():
+        o, ht = oracle_mod.recurrent(q, k, v, g, beta, h0=h0, cu_seqlens=cu)
+        return float(np.sum(do[:, :n] * o[:, :n]) + np.sum(dht * ht))
+
+    dq, dk, dv, dg, db, dh0 = oracle_mod.recurrent_bwd(q, k, v, g, beta, do, dht=dht, h0=h0, cu_seqlens=cu)
+    for name, x, got in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("g", g, dg), ("beta", beta, db),
+                         ("h0", h0, dh0)):
+        want = _fd_grad(loss, x)
+        if got.shape[:2] == (1, T):
+            got, want = got[:, :n], want[:, :n]
+        np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-8, err_msg=name)
+    np.testing.assert_array_equal(dh0[1], dht[1])  # empty slot
+    assert np.isnan(dq[:, n:]).all()
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_gate_bwd_finite_differences(oracle_mod, kind):
+    """gate_bwd equals central finite differences of sum(w * gate(x)) in x, A_log and dt_bias."""
+    rng = np.random.default_rng(42 + kind)
+    T, H, K = 5, 2, 3
+    x = 2.0 * rng.standard_normal((1, T, H, K))
+    A_log = rng.uniform(-1.0, 2.0, H)
+    dt = rng.standard_normal((H, K))
+    w = rng.standard_normal((1, T, H, K))
+    lb = -3.0
+    f = lambda: float(np.sum(w * oracle_mod.gate(kind, x, A_log, dt, lb)))
+    dx, dA, ddt = oracle_mod.gate_bwd(kind, x, w, A_log, dt, lb)
+    np.testing.assert_allclose(dx, _fd_grad(f, x), rtol=1e-6, atol=1e-9)
+    if kind == oracle_mod.GATE_LOGE:
+        assert dA is None and ddt is None
+        return
+    np.testing.assert_allclose(dA, _fd_grad(f, A_log), rtol=1e-6, atol=1e-9)
+    np.testing.assert_allclose(ddt, _fd_grad(f, dt), rtol=1e-6, atol=1e-9)
