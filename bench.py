@@ -153,6 +153,30 @@ def bench_decode(steps, warmup):
                 GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS, Mtokens_per_s=N / (t["median"] * 1e-3) / 1e6)
 
 
+def bench_bwd(B, T, H, D, steps, warmup, C=64):
+    """Flushed-cache HIP-event timing of kda_chunk_bwd (forward recompute included)
+    on the headline shape: safe gate, bf16, h0 and dht given."""
+    import kda_synth
+    from gated_delta_rule_gate_amd import chunk_kda_bwd
+
+    d = kda_synth.chunk_inputs(B, T, H, D, D, dtype=torch.bfloat16, seed=1002)
+    dev = {k: v.cuda() for k, v in d.items() if v is not None}
+    del d
+    gen = torch.Generator(device="cuda").manual_seed(1003)
+    do = torch.randn((B, T, H, D), device="cuda", generator=gen).to(torch.bfloat16)
+    dht = 0.1 * torch.randn((B, H, D, D), device="cuda", generator=gen)
+    flush_buf = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+
+    def step():
+        chunk_kda_bwd(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], do, dev["h0"], dht=dht, chunk_size=C,
+                      gate_kind="safe", A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0)
+
+    t = event_time_ms(step, steps, warmup, flush=lambda: flush_buf.zero_())
+    return {"config": "chunk_kda bwd B%d T%d H%d K=V=%d bf16, C=%d, safe gate, h0 + dht; forward recompute "
+                      "included" % (B, T, H, D, C),
+            "ms": round(t["mean"], 4), "Mtokens_per_s": round(B * T / (t["mean"] * 1e-3) / 1e6, 3)}
+
+
 SWEEP_SHAPES = [(1, 8192, 96, 128), (2, 16384, 16, 128), (4, 2048, 16, 128), (4, 4096, 64, 128),
                    (8, 2048, 32, 256), (8, 1024, 8, 64)]
 
@@ -195,6 +219,7 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--sweep", action="store_true", help="also time a sweep of six shapes")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward figure")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -268,6 +293,8 @@ def main():
     }
     if not args.no_decode:
         line["recurrent_decode"] = bench_decode(max(10, args.steps), 3)
+    if not args.no_bwd and args.schedule != "fused":
+        line["backward"] = bench_bwd(B, T, H, D, steps=max(3, args.steps // 4), warmup=1, C=C)
     if args.sweep:
         del dev, o, ht, flush_buf
         torch.cuda.empty_cache()

@@ -1,8 +1,9 @@
-"""MI355X (gfx950) Kimi Delta Attention forward: chunked prefill and fused recurrence.
+"""MI355X (gfx950) Kimi Delta Attention: chunked prefill, its backward, and the fused recurrence.
 
 The computation lives in the HIP library ``_build/libkda.so`` (C ABI in
 ``include/kda.h``); this package only marshals arguments to it.
 """
-from ._binding import (KdaError, chunk_kda, gate_cumsum, lib, recurrent_kda, workspace_bytes)  # noqa: F401
+from ._binding import (KdaError, chunk_kda, chunk_kda_bwd, gate_cumsum, lib, recurrent_kda,  # noqa: F401
+                       workspace_bytes)
 
-__all__ = ["chunk_kda", "recurrent_kda", "gate_cumsum", "KdaError", "lib", "workspace_bytes"]
+__all__ = ["chunk_kda", "chunk_kda_bwd", "recurrent_kda", "gate_cumsum", "KdaError", "lib", "workspace_bytes"]

@@ -57,6 +57,11 @@ def lib():
             L.kda_chunk_states_count.restype = ctypes.c_size_t
             L.kda_chunk_fwd_states.argtypes = [ap] + [vp] * 11 + [ctypes.c_size_t, vp]
             L.kda_chunk_fwd_states.restype = ctypes.c_int
+        if hasattr(L, "kda_chunk_bwd"):
+            L.kda_chunk_bwd_workspace_bytes.argtypes = [ap]
+            L.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+            L.kda_chunk_bwd.argtypes = [ap] + [vp] * 18 + [ctypes.c_size_t, vp]
+            L.kda_chunk_bwd.restype = ctypes.c_int
         if hasattr(L, "kda_chunk_stage"):
             L.kda_chunk_stage.argtypes = [ap, ctypes.c_int] + [vp] * 10 + [ctypes.c_size_t, vp]
             L.kda_chunk_stage.restype = ctypes.c_int
@@ -242,6 +247,40 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
                                  _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(hs), _ptr(ws),
                                  ctypes.c_size_t(ws.numel()), _stream()))
     return o, ht, hs
+
+
+def chunk_kda_bwd(q, k, v, g, beta, do, initial_state=None, *, dht=None, cu_seqlens=None, chunk_size=64,
+                  gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None, beta_logits=False):
+    """Backward of ``chunk_kda``: gradients of sum(do * o) + sum(dht * ht).
+
+    Returns a dict with dq, dk (dtype of q), dv (dtype of v), dg (fp32, of g as
+    passed: the raw gate input for "safe" / "softplus"), dbeta (fp32), dh0 (fp32,
+    [N, H, K, V]) and, for "safe" / "softplus", dA_log [H] and ddt_bias [H, K].
+    The forward is recomputed inside the library.
+    """
+    B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
+    _require(do.shape == (B, T, H, V) and do.dtype == q.dtype, "do must be [B, T, H, V] in q's dtype")
+    if dht is not None:
+        _require(dht.shape == (N, H, K, V) and dht.dtype == torch.float32, "dht must be fp32 [N, H, K, V]")
+    _check_tensors(dict(do=do, dht=dht), q.device)
+    a = make_args(q, v, H, N, gate_kind, chunk_size=chunk_size, scale=scale, A_log=A_log, dt_bias=dt_bias,
+                  lower_bound=lower_bound, schedule="staged", beta_logits=beta_logits)
+    L = lib()
+    ws_bytes = int(L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a)))
+    ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=q.device)
+    dev = q.device
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dg=torch.empty(g.shape, dtype=torch.float32, device=dev),
+               dbeta=torch.empty(beta.shape, dtype=torch.float32, device=dev),
+               dh0=torch.empty((N, H, K, V), dtype=torch.float32, device=dev))
+    gated = gate_kind in ("safe", "softplus")
+    out["dA_log"] = torch.empty((H,), dtype=torch.float32, device=dev) if gated else None
+    out["ddt_bias"] = torch.empty((H, K), dtype=torch.float32, device=dev) if gated and dt_bias is not None else None
+    check(L.kda_chunk_bwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                          _ptr(cu_seqlens), _ptr(do), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                          _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(out["dA_log"]),
+                          _ptr(out["ddt_bias"]), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))
+    return out
 
 
 def workspace_bytes(q, v, H, N, chunk_size=64, schedule="auto"):

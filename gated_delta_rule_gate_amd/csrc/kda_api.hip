@@ -377,3 +377,90 @@ extern "C" kda_status kda_chunk_stage(const kda_args *a, kda_stage stage, const 
   if (s != KDA_OK) return s;
   return run_stage(p, (int)stage, (hipStream_t)stream);
 }
+
+namespace {
+
+// Workspace of kda_chunk_bwd: the staged forward's layout, then the backward's
+// own fp32 intermediates (BwdParams in kda_launch.h), each 256-byte aligned.
+struct BwdLayout {
+  size_t fwd, off[13], total;
+};
+
+BwdLayout bwd_layout(const kda_args *a) {
+  kda_args s = *a;
+  s.schedule = KDA_SCHED_STAGED;
+  BwdLayout L{};
+  L.fwd = staged_layout(&s).total;
+  const size_t rows = (size_t)a->B * a->T * a->H;
+  const size_t D = pad_width(std::max(a->K, a->V)), C = a->chunk_size;
+  const size_t nch = (size_t)std::max<int64_t>(max_chunks(a, true), max_chunks(a, false));
+  // dvn, dqt, dkt, dw, dXw, dAqk, dT, dAkk, dbp, dhn, dlam, ddt_part, dA_part
+  const size_t sz[13] = {4 * rows * D, 4 * rows * D, 4 * rows * D, 4 * rows * D, 4 * rows * D,
+                         4 * rows * C, 4 * rows * C, 4 * rows * C, 4 * rows,
+                         4 * nch * a->H * (size_t)a->K * a->V, 4 * nch * a->H * D, 4 * nch * a->H * D,
+                         4 * nch * a->H};
+  size_t cur = L.fwd;
+  for (int i = 0; i < 13; ++i) {
+    L.off[i] = cur;
+    cur += align_up(sz[i]);
+  }
+  L.total = cur;
+  return L;
+}
+
+bool bwd_shape_ok(const kda_args *a) {
+  if (!chunk_shape_ok(a)) return false;
+  return pad_width(std::max(a->K, a->V)) <= 128;
+}
+
+}  // namespace
+
+extern "C" size_t kda_chunk_bwd_workspace_bytes(const kda_args *a) {
+  if (!bwd_shape_ok(a)) return 0;
+  return bwd_layout(a).total;
+}
+
+extern "C" kda_status kda_chunk_bwd(const kda_args *a, const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, const float *h0, const int32_t *cu_seqlens,
+                                    const void *d_o, const float *dht, void *dq, void *dk, void *dv, float *dg,
+                                    float *dbeta, float *dh0, float *dA_log, float *ddt_bias, void *workspace,
+                                    size_t ws_bytes, void *stream) {
+  if (!a) return KDA_ERR_NULL;
+  if (!d_o || !dq || !dk || !dv || !dg || !dbeta) return KDA_ERR_NULL;
+  if (!aligned16(d_o) || !aligned16(dht) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) ||
+      !aligned16(dh0))
+    return KDA_ERR_ALIGN;
+  kda_args s = *a;
+  s.schedule = KDA_SCHED_STAGED;
+  kda::ChunkParams p;
+  // o is never written here: the forward is recomputed up to the state scan only
+  kda_status st = prepare_chunk(&s, q, k, v, g, beta, h0, cu_seqlens, const_cast<void *>(d_o), nullptr, workspace,
+                                ws_bytes, p);
+  if (st != KDA_OK) return st;
+  if (a->gate_kind == KDA_GATE_LOG2_CUMSUM) return KDA_ERR_UNSUPPORTED;
+  if (a->q_l2norm) return KDA_ERR_UNSUPPORTED;
+  if (a->Hk != 0 && a->Hk != a->H) return KDA_ERR_UNSUPPORTED;
+  if (!bwd_shape_ok(a)) return KDA_ERR_UNSUPPORTED;
+  const BwdLayout L = bwd_layout(a);
+  if (ws_bytes < L.total) return KDA_ERR_WORKSPACE;
+  char *base = static_cast<char *>(workspace);
+  kda::BwdParams b{};
+  b.dout = d_o;
+  b.dht = dht;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dg = dg;
+  b.dbeta = dbeta;
+  b.dh0 = dh0;
+  b.dA_log = dA_log;
+  b.ddt = (a->gate_kind == KDA_GATE_LOGE) ? nullptr : ddt_bias;
+  if (a->gate_kind == KDA_GATE_LOGE) b.dA_log = nullptr;
+  float **slots[13] = {&b.dvn, &b.dqt, &b.dkt, &b.dw, &b.dXw, &b.dAqk, &b.dT, &b.dAkk, &b.dbp, &b.dhn, &b.dlam,
+                       &b.ddt_part, &b.dA_part};
+  for (int i = 0; i < 13; ++i) *slots[i] = reinterpret_cast<float *>(base + L.off[i]);
+  hipStream_t hs = (hipStream_t)stream;
+  for (int stage = KDA_STAGE_INDEX; stage <= KDA_STAGE_SCAN; ++stage)
+    if ((st = run_stage(p, stage, hs)) != KDA_OK) return st;
+  return hip_status(kda::launch_bwd(p, b, hs));
+}

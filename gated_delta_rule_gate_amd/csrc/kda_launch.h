@@ -70,6 +70,24 @@ struct ChunkParams {
   float *b, *Akk, *Aqk, *Tm, *w, *u, *vnew, *hc;
 };
 
+// Backward of the chunked forward (staged). The forward intermediates come from
+// the staged steps (1)-(5) in the same workspace (ChunkParams b, Akk, Aqk, Tm,
+// w, vnew, hc); the backward's own fp32 intermediates follow them:
+//   dvn, dqt, dkt, dw, dXw [B*T, H, D]   gradients of v_new, q~, k~, w, beta k 2^b
+//   dAqk, dT, dAkk         [B*T, H, C]   gradients of A_qk, T (first its u part), A_kk
+//   dbp                    [B*T, H]      the beta gradient through u
+//   dhn                    [n_chunks, H, Kr, Vr]  gradient of the state after each chunk
+//   dlam, ddt_part         [n_chunks, H, D]; dA_part [n_chunks, H]
+struct BwdParams {
+  const void *dout;  // [B*T, H, Vr] dtype of q
+  const float *dht;  // [N, H, Kr, Vr] or null
+  void *dq, *dk, *dv;
+  float *dg, *dbeta, *dh0, *dA_log, *ddt;
+  float *dvn, *dqt, *dkt, *dw, *dXw, *dAqk, *dT, *dAkk, *dbp, *dhn, *dlam, *ddt_part, *dA_part;
+};
+
+hipError_t launch_bwd(const ChunkParams &p, const BwdParams &b, hipStream_t st);
+
 hipError_t launch_chunk_index(const ChunkParams &p, hipStream_t st);
 hipError_t launch_stage_gate(const ChunkParams &p, hipStream_t st);
 hipError_t launch_stage_grams(const ChunkParams &p, hipStream_t st);

@@ -222,6 +222,42 @@ kda_status kda_chunk_fwd_states(const kda_args *args, const void *q, const void 
                                 float *h_states, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Bytes of device workspace that kda_chunk_bwd needs (0 when the arguments are
+ * invalid or not supported by the backward).
+ */
+size_t kda_chunk_bwd_workspace_bytes(const kda_args *args);
+
+/*
+ * Backward of kda_chunk_fwd (the chunk_kda_bwd family that "FLA KDA Skill",
+ * section "Public code map", names without printing it). Returns the gradients
+ * of L = sum(d_o * o) + sum(dht * ht) for the forward of the same arguments.
+ * The forward's steps (1)-(5) are recomputed inside (staged), then the chunks
+ * are walked in reverse for the state gradient and each chunk's gradients are
+ * formed on its own; every product is fp32.
+ * Arguments (all device pointers; the caller owns every buffer):
+ *   q, k, v, g, beta, h0, cu_seqlens   as kda_chunk_fwd
+ *   d_o      [B, T, H, V], dtype args->dtype: gradient of o
+ *   dht      fp32 [N, H, K, V] or NULL (zero): gradient of ht
+ *   dq, dk   [B, T, H, K], dtype args->dtype     dv  [B, T, H, V], dtype args->dtype
+ *   dg       fp32 [B, T, H, K]: gradient of g as passed (the raw gate input
+ *            for SAFE and SOFTPLUS, the natural-log decay for LOGE)
+ *   dbeta    fp32 [B, T, H] (of the logits when args->beta_logits)
+ *   dh0      fp32 [N, H, K, V] or NULL; an empty slot gets dht (zeros without dht)
+ *   dA_log   fp32 [H] or NULL, ddt_bias fp32 [H, K] or NULL: parameter
+ *            gradients of the SAFE and SOFTPLUS gates (not written for LOGE)
+ *   workspace  ws_bytes >= kda_chunk_bwd_workspace_bytes(args), 256-byte aligned
+ * Rows at or beyond cu_seqlens[N] are not written. dq..dbeta are required
+ * (KDA_ERR_NULL); they must not overlap the inputs.
+ * Supported: K and V multiples of 8 with max(K, V) <= 128, chunk_size 32 or 64,
+ * bf16 or fp32, gate kinds LOGE, SAFE and SOFTPLUS, Hk == H and q_l2norm == 0;
+ * other valid arguments return KDA_ERR_UNSUPPORTED.
+ */
+kda_status kda_chunk_bwd(const kda_args *args, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *h0, const int32_t *cu_seqlens, const void *d_o,
+                         const float *dht, void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dh0,
+                         float *dA_log, float *ddt_bias, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Fused token-sequential recurrence (recurrent_kda forward), for decode and
  * inference prefill ("Add fused recurrent_kda ...", section "Agent note"):
  * one kernel; each workgroup owns a (sequence, head, value-block) and scans its
