@@ -50,6 +50,50 @@ __device__ __forceinline__ f32x4_t mm16(f32x4_t acc, const float *A, int am, int
   return acc;
 }
 
+// A [ROWS][COLS] fp32 LDS tile (row stride lds, a multiple of 4) from global rows
+// of T (row stride ldg elements) with 16-byte loads: 4 fp32 or 8 bf16 columns
+// per load. Rows >= L and columns >= ncol read as 0 (ncol, ldg and the base
+// are multiples of the vector width). fn(r, c, v) may then rewrite the EPV
+// values of row r, columns c.. before they are stored.
+template <typename T, int ROWS, int COLS, typename Fn>
+__device__ __forceinline__ void tile_f32(float *s, int lds, const T *g, int64_t ldg, int L, int ncol, Fn &&fn) {
+  constexpr int EPV = 16 / (int)sizeof(T);
+  constexpr int VPR = COLS / EPV, NV = ROWS * VPR;
+  static_assert(COLS % EPV == 0, "whole vectors per row");
+#pragma unroll 4
+  for (int idx = threadIdx.x; idx < NV; idx += kBT) {
+    const int r = idx / VPR, c = (idx % VPR) * EPV;
+    float v[EPV];
+    if (r < L && c < ncol) {
+      const u32x4_t raw = *reinterpret_cast<const u32x4_t *>(g + (int64_t)r * ldg + c);
+      if constexpr (sizeof(T) == 4) {
+        const f32x4_t f = __builtin_bit_cast(f32x4_t, raw);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) v[e] = f[e];
+      } else {
+        const bf16x8_t f = __builtin_bit_cast(bf16x8_t, raw);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) v[e] = static_cast<float>(f[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) v[e] = 0.f;
+    }
+    fn(r, c, v);
+#pragma unroll
+    for (int e = 0; e < EPV; e += 4)
+      *reinterpret_cast<f32x4_t *>(s + r * lds + c + e) = f32x4_t{v[e], v[e + 1], v[e + 2], v[e + 3]};
+  }
+}
+
+template <typename T, int ROWS, int COLS>
+__device__ __forceinline__ void tile_f32(float *s, int lds, const T *g, int64_t ldg, int L, int ncol) {
+  tile_f32<T, ROWS, COLS>(s, lds, g, ldg, L, ncol, [](int, int, float *) {});
+}
+
+// 4 fp32 values at p (16-byte aligned)
+__device__ __forceinline__ f32x4_t ld4(const float *p) { return *reinterpret_cast<const f32x4_t *>(p); }
+
 __device__ __forceinline__ int tile_row(int e) { return 4 * ((threadIdx.x & 63) >> 4) + e; }
 __device__ __forceinline__ int tile_col() { return threadIdx.x & 15; }
 
@@ -99,22 +143,23 @@ __global__ __launch_bounds__(kBT) void bwd_scan_kernel(ChunkParams p, BwdParams 
       const int i = idx / BV, j = idx % BV;
       if (i < Kr && col0 + j < Vr) dhn[(int64_t)i * Vr + col0 + j] = sDh[i * LH + j];
     }
-    for (int i = threadIdx.x; i < D; i += kBT) sBL[i] = gb[(int64_t)(L - 1) * ld + i];
-    for (int idx = threadIdx.x; idx < C * C; idx += kBT) {
-      const int r = idx / C, s = idx % C;
-      sA[r * LA + s] = (r < L && s <= r) ? p.Aqk[(t0 + r) * ldc + h * C + s] : 0.f;
-    }
-    for (int idx = threadIdx.x; idx < C * BV; idx += kBT) {
-      const int r = idx / BV, j = idx % BV;
-      sDo[r * LH + j] = (r < L && col0 + j < Vr) ? to_f32(gdo[(t0 + r) * ldv + h * Vr + col0 + j]) : 0.f;
-    }
-    for (int idx = threadIdx.x; idx < C * D; idx += kBT) {
-      const int r = idx / D, i = idx % D;
-      float x = 0.f;
-      if (r < L && i < Kr)
-        x = to_f32(gk[(t0 + r) * ldk + h * Kr + i]) * fast_exp2(gb[(int64_t)(L - 1) * ld + i] - gb[(int64_t)r * ld + i]);
-      sX[r * LX + i] = x;
-    }
+    const float *gbl = gb + (int64_t)(L - 1) * ld;  // b_L
+    tile_f32<float, C, C>(sA, LA, p.Aqk + t0 * ldc + h * C, ldc, L, C, [](int r, int c, float *v) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (c + e <= r) ? v[e] : 0.f;
+    });
+    tile_f32<Tin, C, BV>(sDo, LH, gdo + t0 * ldv + h * Vr + col0, ldv, L, Vr - col0);
+    tile_f32<Tin, C, D>(sX, LX, gk + t0 * ldk + h * Kr, ldk, L, Kr, [&](int r, int c, float *v) {
+      constexpr int E = 16 / (int)sizeof(Tin);
+      if (r >= L) return;
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const f32x4_t bl = ld4(gbl + c + e), br = ld4(gb + (int64_t)r * ld + c + e);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[e + u] *= fast_exp2(bl[u] - br[u]);
+      }
+    });
+    for (int i = threadIdx.x; i < D; i += kBT) sBL[i] = gbl[i];
     __syncthreads();
     // dv_new = A_qk^T do + k~ dh (this wave: value columns 16 wid..)
     for (int rt = 0; rt < NC; ++rt) {
@@ -129,16 +174,17 @@ __global__ __launch_bounds__(kBT) void bwd_scan_kernel(ChunkParams p, BwdParams 
       }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < C * D; idx += kBT) {
-      const int r = idx / D, i = idx % D;
-      float x = 0.f, wv = 0.f;
-      if (r < L) {
-        if (i < Kr) x = p.scale * to_f32(gq[(t0 + r) * ldk + h * Kr + i]) * fast_exp2(gb[(int64_t)r * ld + i]);
-        wv = p.w[(t0 + r) * ld + h * D + i];
+    tile_f32<Tin, C, D>(sX, LX, gq + t0 * ldk + h * Kr, ldk, L, Kr, [&](int r, int c, float *v) {
+      constexpr int E = 16 / (int)sizeof(Tin);
+      if (r >= L) return;
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const f32x4_t br = ld4(gb + (int64_t)r * ld + c + e);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[e + u] *= p.scale * fast_exp2(br[u]);
       }
-      sX[r * LX + i] = x;
-      sW[r * LX + i] = wv;
-    }
+    });
+    tile_f32<float, C, D>(sW, LX, p.w + t0 * ld + h * D, ld, L, D);
     __syncthreads();
     // dh <- 2^b_L dh + q~^T do - w^T dv_new (this wave's columns only)
     for (int it = 0; it < DT; ++it) {
@@ -182,8 +228,11 @@ __global__ __launch_bounds__(kBT) void bwd_contract_kernel(ChunkParams p, BwdPar
   float *sBv = sDvn + C * LS;
   float *sH = sBv + C * LS;  // [D][LS]
   float *sDhn = sH + D * LS;
+  float *sBeta = sDhn + D * LS;  // [C]
   const Tin *gdo = reinterpret_cast<const Tin *>(bw.dout), *gv = reinterpret_cast<const Tin *>(p.v);
 
+  for (int r = threadIdx.x; r < C; r += kBT) sBeta[r] = r < L ? beta_at(p, t0 + r, h) : 0.f;
+  float dlam = 0.f;  // this thread's channel (threads < D): sum over j of h dh'
   f32x4_t aq[NTW], ak[NTW], aw[NTW], aa[NCW], at[NCW];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) aq[t] = ak[t] = aw[t] = zero4();
@@ -192,22 +241,25 @@ __global__ __launch_bounds__(kBT) void bwd_contract_kernel(ChunkParams p, BwdPar
 
   for (int j0 = 0; j0 < Vr; j0 += SJ) {
     __syncthreads();  // the previous slab is consumed
-    for (int idx = threadIdx.x; idx < C * SJ; idx += kBT) {
-      const int r = idx / SJ, j = idx % SJ, jj = j0 + j;
-      const bool ok = r < L && jj < Vr;
-      const int64_t row = t0 + r;
-      sDo[r * LS + j] = ok ? to_f32(gdo[row * ldv + h * Vr + jj]) : 0.f;
-      sVn[r * LS + j] = ok ? p.vnew[row * ld + h * D + jj] : 0.f;
-      sDvn[r * LS + j] = ok ? bw.dvn[row * ld + h * D + jj] : 0.f;
-      sBv[r * LS + j] = ok ? beta_at(p, row, h) * to_f32(gv[row * ldv + h * Vr + jj]) : 0.f;
-    }
-    for (int idx = threadIdx.x; idx < D * SJ; idx += kBT) {
-      const int i = idx / SJ, j = idx % SJ, jj = j0 + j;
-      const bool ok = i < Kr && jj < Vr;
-      sH[i * LS + j] = ok ? p.hc[hbase + (int64_t)i * Vr + jj] : 0.f;
-      sDhn[i * LS + j] = ok ? bw.dhn[hbase + (int64_t)i * Vr + jj] : 0.f;
-    }
+    const int nj = Vr - j0;
+    tile_f32<Tin, C, SJ>(sDo, LS, gdo + t0 * ldv + h * Vr + j0, ldv, L, nj);
+    tile_f32<float, C, SJ>(sVn, LS, p.vnew + t0 * ld + h * D + j0, ld, L, nj);
+    tile_f32<float, C, SJ>(sDvn, LS, bw.dvn + t0 * ld + h * D + j0, ld, L, nj);
+    tile_f32<Tin, C, SJ>(sBv, LS, gv + t0 * ldv + h * Vr + j0, ldv, L, nj, [&](int r, int, float *v) {
+      if (r >= L) return;
+      const float be = sBeta[r];
+#pragma unroll
+      for (int e = 0; e < 16 / (int)sizeof(Tin); ++e) v[e] *= be;
+    });
+    tile_f32<float, D, SJ>(sH, LS, p.hc + hbase + j0, Vr, Kr, nj);
+    tile_f32<float, D, SJ>(sDhn, LS, bw.dhn + hbase + j0, Vr, Kr, nj);
     __syncthreads();
+    for (int i = threadIdx.x; i < D; i += kBT) {
+      float acc = 0.f;
+#pragma unroll 8
+      for (int j = 0; j < SJ; ++j) acc += sH[i * LS + j] * sDhn[i * LS + j];
+      dlam += acc;
+    }
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       const int tile = wid * NTW + t, rt = tile / DT, ct = tile % DT;
@@ -249,12 +301,7 @@ __global__ __launch_bounds__(kBT) void bwd_contract_kernel(ChunkParams p, BwdPar
       }
     }
   }
-  for (int i = threadIdx.x; i < D; i += kBT) {
-    float acc = 0.f;
-    if (i < Kr)
-      for (int j = 0; j < Vr; ++j) acc += p.hc[hbase + (int64_t)i * Vr + j] * bw.dhn[hbase + (int64_t)i * Vr + j];
-    bw.dlam[((int64_t)lc.gci * p.H + h) * D + i] = acc;
-  }
+  for (int i = threadIdx.x; i < D; i += kBT) bw.dlam[((int64_t)lc.gci * p.H + h) * D + i] = dlam;
 }
 
 // ---- the WY factors and the triangular inverse ----
@@ -279,20 +326,26 @@ __global__ __launch_bounds__(kBT) void bwd_wy_kernel(ChunkParams p, BwdParams bw
   float *sBeta = sDvn + C * LX;                 // [C]
   const Tin *gk = reinterpret_cast<const Tin *>(p.k), *gv = reinterpret_cast<const Tin *>(p.v);
 
-  for (int idx = threadIdx.x; idx < C * C; idx += kBT) {
-    const int r = idx / C, s = idx % C;
-    const bool ok = r < L && s < L;
-    const int64_t o = (t0 + r) * ldc + h * C + s;
-    sT[r * LA + s] = (ok && s <= r) ? p.Tm[o] : 0.f;
-    sDT[r * LA + s] = ok ? bw.dT[o] : 0.f;
-  }
-  for (int idx = threadIdx.x; idx < C * D; idx += kBT) {
-    const int r = idx / D, i = idx % D;
-    const int64_t o = (t0 + r) * ld + h * D + i;
-    sDw[r * LX + i] = r < L ? bw.dw[o] : 0.f;
-    sDvn[r * LX + i] = r < L ? bw.dvn[o] : 0.f;
-    sKG[r * LX + i] = (r < L && i < Kr) ? to_f32(gk[(t0 + r) * ldk + h * Kr + i]) * fast_exp2(p.b[o]) : 0.f;
-  }
+  tile_f32<float, C, C>(sT, LA, p.Tm + t0 * ldc + h * C, ldc, L, C, [&](int r, int c, float *v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (c + e <= r && c + e < L) ? v[e] : 0.f;
+  });
+  tile_f32<float, C, C>(sDT, LA, bw.dT + t0 * ldc + h * C, ldc, L, C, [&](int, int c, float *v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (c + e < L) ? v[e] : 0.f;
+  });
+  tile_f32<float, C, D>(sDw, LX, bw.dw + t0 * ld + h * D, ld, L, D);
+  tile_f32<float, C, D>(sDvn, LX, bw.dvn + t0 * ld + h * D, ld, L, D);
+  const float *gb = p.b + t0 * ld + h * D;
+  tile_f32<Tin, C, D>(sKG, LX, gk + t0 * ldk + h * Kr, ldk, L, Kr, [&](int r, int c, float *v) {
+    if (r >= L) return;
+#pragma unroll
+    for (int e = 0; e < 16 / (int)sizeof(Tin); e += 4) {
+      const f32x4_t br = ld4(gb + (int64_t)r * ld + c + e);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[e + u] *= fast_exp2(br[u]);
+    }
+  });
   for (int r = threadIdx.x; r < C; r += kBT) sBeta[r] = r < L ? beta_at(p, t0 + r, h) : 0.f;
   __syncthreads();
   // dT = dT_u + beta_s (dw (k 2^b)^T)_rs
@@ -366,121 +419,259 @@ __global__ __launch_bounds__(kBT) void bwd_wy_kernel(ChunkParams p, BwdParams bw
 }
 
 // ---- pairwise decays: dq, dk, the cumsum gradient, dg and the gate activation ----
+// For row r, channel i (E_rs = 2^(b_r - b_s)):
+//   Q[r] = sum_{s<r} dA_kk[r,s] k_s E_rs      R[r] = sum_{s<=r} dA_qk[r,s] k_s E_rs
+//   U[s] = sum_{r>=s} (dA_kk[r,s] beta_r k_r + dA_qk[r,s] scale q_r) E_rs
+// Off-diagonal 16x16 blocks (row block I > column block J) factor the decay
+// through the first row a_I of block I, E_rs = 2^(b_r - a_I) 2^(a_I - b_s),
+// both exponents non-positive for any decaying gate ("FLA KDA Skill", "Safe
+// gate numerical note"), and run as fp32 MFMA products; diagonal blocks take
+// E_rs per pair. Each wave owns 16 channels of a 64-channel slab.
 template <typename Tin, int C, int D, int GK>
 __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams bw) {
   ChunkLoc lc;
   if (!locate_chunk(p, blockIdx.x, lc)) return;
   const int h = blockIdx.y;
-  constexpr int SI = 32, LS = SI + 1, LA = C + 1, TPR = kBT / C, CPT = SI / TPR;
+  constexpr int SI = 64, LS = SI + 4, LA = C + 4, NC = C / 16, NW = kBT / 64;
+  static_assert(SI == 16 * NW, "one 16-channel tile per wave");
   const int Kr = p.Kr, L = lc.L;
   const int64_t t0 = lc.t0;
   const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.H * Kr;
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63, n16 = lane & 15, grp = lane >> 4;
   extern __shared__ __align__(16) char smem[];
-  float *sDAkk = reinterpret_cast<float *>(smem);  // [C][LA]
-  float *sDAqk = sDAkk + C * LA;                   // [C][LA]
-  float *sK = sDAqk + C * LA;                      // [C][LS] slabs of SI channels
+  float *sDAkk = reinterpret_cast<float *>(smem);  // [C][LA] strictly lower
+  float *sDAqk = sDAkk + C * LA;                   // [C][LA] lower
+  float *sK = sDAqk + C * LA;                      // [C][LS] slab of SI channels
   float *sQ = sK + C * LS;
-  float *sB = sQ + C * LS;
-  float *sDB = sB + C * LS;
-  float *sCT = sDB + C * LS;
-  float *sBeta = sCT + C * LS;  // [C]
-  float *sDbeta = sBeta + C;    // [C]
-  float *sBL = sDbeta + C;      // [SI]
+  float *sB = sQ + C * LS;   // b; rows >= L repeat row L - 1, so every exponent below stays <= 0
+  float *sCT = sB + C * LS;  // [SI] per channel: sum over rows of k 2^(b_L - b) dk~ (b_L's share)
+  float *sBeta = sCT + SI;   // [C]
+  float *sDbw = sBeta + C;      // [NW][C] per-wave partial beta gradients
+  float *sBL = sDbw + NW * C;   // [SI]
   float *sDA = sBL + SI;        // [SI]
   const Tin *gq = reinterpret_cast<const Tin *>(p.q), *gk = reinterpret_cast<const Tin *>(p.k);
   Tin *gdq = reinterpret_cast<Tin *>(bw.dq), *gdk = reinterpret_cast<Tin *>(bw.dk);
   const float scale = p.scale;
   const float expA = (GK == kGateSafe || GK == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
 
-  for (int idx = threadIdx.x; idx < C * C; idx += kBT) {
-    const int r = idx / C, s = idx % C;
-    const int64_t o = (t0 + r) * ldc + h * C + s;
-    sDAkk[r * LA + s] = (r < L && s < r) ? bw.dAkk[o] : 0.f;
-    sDAqk[r * LA + s] = (r < L && s <= r) ? bw.dAqk[o] : 0.f;
-  }
-  for (int r = threadIdx.x; r < C; r += kBT) {
-    sBeta[r] = r < L ? beta_at(p, t0 + r, h) : 0.f;
-    sDbeta[r] = 0.f;
-  }
+  tile_f32<float, C, C>(sDAkk, LA, bw.dAkk + t0 * ldc + h * C, ldc, L, C, [](int r, int c, float *v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (c + e < r) ? v[e] : 0.f;
+  });
+  tile_f32<float, C, C>(sDAqk, LA, bw.dAqk + t0 * ldc + h * C, ldc, L, C, [](int r, int c, float *v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (c + e <= r) ? v[e] : 0.f;
+  });
+  for (int r = threadIdx.x; r < C; r += kBT) sBeta[r] = r < L ? beta_at(p, t0 + r, h) : 0.f;
+  for (int idx = threadIdx.x; idx < NW * C; idx += kBT) sDbw[idx] = 0.f;
   float dA_total = 0.f;
-  const int r = threadIdx.x / TPR, q4 = threadIdx.x % TPR;
+  const float *gb = p.b + t0 * ld + h * D;
   for (int i0 = 0; i0 < Kr; i0 += SI) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < C * SI; idx += kBT) {
-      const int rr = idx / SI, ii = idx % SI, i = i0 + ii;
-      const bool ok = rr < L && i < Kr;
-      sK[rr * LS + ii] = ok ? to_f32(gk[(t0 + rr) * ldk + h * Kr + i]) : 0.f;
-      sQ[rr * LS + ii] = ok ? to_f32(gq[(t0 + rr) * ldk + h * Kr + i]) : 0.f;
-      sB[rr * LS + ii] = rr < L ? p.b[(t0 + rr) * ld + h * D + i] : 0.f;
-    }
-    for (int ii = threadIdx.x; ii < SI; ii += kBT) sBL[ii] = p.b[(t0 + L - 1) * ld + h * D + i0 + ii];
-    __syncthreads();
-    float dbr = 0.f;
-    for (int cc = 0; cc < CPT; ++cc) {
-      const int ii = cc * TPR + q4, i = i0 + ii;
-      if (r >= L || i >= Kr) {
-        sDB[r * LS + ii] = 0.f;
-        sCT[r * LS + ii] = 0.f;
-        continue;
-      }
-      const float br = sB[r * LS + ii], kr = sK[r * LS + ii], qr = sQ[r * LS + ii], be = sBeta[r];
-      const float gam = fast_exp2(br), ktf = fast_exp2(sBL[ii] - br);
-      const int64_t eo = (t0 + r) * ld + h * D + i;
-      const float dqt = bw.dqt[eo], dkt = bw.dkt[eo], dxw = bw.dXw[eo];
-      float Q = 0.f, R = 0.f, U = 0.f;
-      for (int s = 0; s <= r; ++s) {
-        const float ks = sK[s * LS + ii] * fast_exp2(br - sB[s * LS + ii]);
-        Q += sDAkk[r * LA + s] * ks;
-        R += sDAqk[r * LA + s] * ks;
-      }
-      for (int t = r; t < L; ++t) {
-        const float e = fast_exp2(sB[t * LS + ii] - br);
-        U += (sDAkk[t * LA + r] * sBeta[t] * sK[t * LS + ii] + sDAqk[t * LA + r] * scale * sQ[t * LS + ii]) * e;
-      }
-      const float dq = scale * (gam * dqt + R);
-      const float dk = be * (gam * dxw + Q) + ktf * dkt + U;
-      const float dB = scale * qr * (gam * dqt + R) + be * kr * (gam * dxw + Q) - kr * (ktf * dkt + U);
-      dbr += kr * (gam * dxw + Q);
-      sDB[r * LS + ii] = dB;
-      sCT[r * LS + ii] = kr * ktf * dkt;
-      gdq[(t0 + r) * ldk + h * Kr + i] = from_f32<Tin>(dq);
-      gdk[(t0 + r) * ldk + h * Kr + i] = from_f32<Tin>(dk);
-    }
+    tile_f32<Tin, C, SI>(sK, LS, gk + t0 * ldk + h * Kr + i0, ldk, L, Kr - i0);
+    tile_f32<Tin, C, SI>(sQ, LS, gq + t0 * ldk + h * Kr + i0, ldk, L, Kr - i0);
+    tile_f32<float, C, SI>(sB, LS, gb + i0, ld, L, SI, [&](int r, int c, float *v) {
+      if (r < L) return;
+      const f32x4_t bl = ld4(gb + (int64_t)(L - 1) * ld + i0 + c);
 #pragma unroll
-    for (int m = 1; m < TPR; m <<= 1) dbr += __shfl_xor(dbr, m);
-    if (q4 == 0 && r < L) sDbeta[r] += dbr;
+      for (int e = 0; e < 4; ++e) v[e] = bl[e];
+    });
+    for (int ii = threadIdx.x; ii < SI; ii += kBT) sBL[ii] = gb[(int64_t)(L - 1) * ld + i0 + ii];
     __syncthreads();
-    // per channel: b_L's terms, the reverse cumsum and the gate activation
+
+    const int cl = 16 * wid + n16;  // this lane's channel within the slab
+    float ctl = 0.f;                // sum over this lane's rows of k 2^(b_L - b) dk~
+#pragma unroll 1
+    for (int I = 0; I < NC; ++I) {
+      const float aI = sB[16 * I * LS + cl];
+      // this lane's elements of dq~, dX_w, dk~, loaded while the products run
+      float pq[4], px[4], pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * I + 4 * grp + e, i = i0 + cl;
+        const bool ok = r < L && i < Kr;
+        const int64_t eo = (t0 + (ok ? r : 0)) * ld + h * D + (ok ? i : 0);
+        pq[e] = ok ? bw.dqt[eo] : 0.f;
+        px[e] = ok ? bw.dXw[eo] : 0.f;
+        pk[e] = ok ? bw.dkt[eo] : 0.f;
+      }
+      // Q and R of rows 16I + 4grp + e: blocks J < I, then the diagonal block
+      f32x4_t aq = zero4(), ar = zero4();
+#pragma unroll 1
+      for (int J = 0; J < I; ++J) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int s = 16 * J + 4 * st + grp;
+          const float kh = sK[s * LS + cl] * fast_exp2(aI - sB[s * LS + cl]);
+          aq = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAkk[(16 * I + n16) * LA + s], kh, aq, 0, 0, 0);
+          ar = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAqk[(16 * I + n16) * LA + s], kh, ar, 0, 0, 0);
+        }
+      }
+      // U of rows (as columns) 16I + 4grp + e: row blocks I2 > I
+      f32x4_t u = zero4();
+#pragma unroll 1
+      for (int I2 = I + 1; I2 < NC; ++I2) {
+        const float a2 = sB[16 * I2 * LS + cl];
+        f32x4_t au = zero4();
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int rr = 16 * I2 + 4 * st + grp;
+          const float f = fast_exp2(sB[rr * LS + cl] - a2);
+          const float xh = sBeta[rr] * sK[rr * LS + cl] * f, qh = scale * sQ[rr * LS + cl] * f;
+          au = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAkk[rr * LA + 16 * I + n16], xh, au, 0, 0, 0);
+          au = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAqk[rr * LA + 16 * I + n16], qh, au, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] += au[e] * fast_exp2(a2 - sB[(16 * I + 4 * grp + e) * LS + cl]);
+      }
+      // the diagonal block
+      float qd[4], rd[4], ud[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fo = fast_exp2(sB[(16 * I + 4 * grp + e) * LS + cl] - aI);
+        qd[e] = aq[e] * fo;
+        rd[e] = ar[e] * fo;
+        ud[e] = u[e];
+      }
+      if constexpr (GK == kGateSafe) {
+        // bounded decay: the block's midpoint m (row 16I + 8) anchors both sides,
+        // E_rs = 2^(b_r - m) 2^(m - b_s), with |exponents| at most 8 rows of decay
+        const float mI = sB[(16 * I + 8) * LS + cl];
+        f32x4_t dq4 = zero4(), dr4 = zero4(), du4 = zero4();
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int s = 16 * I + 4 * st + grp;  // contraction index
+          const float bs = sB[s * LS + cl];
+          const float km = sK[s * LS + cl] * fast_exp2(mI - bs);
+          dq4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAkk[(16 * I + n16) * LA + s], km, dq4, 0, 0, 0);
+          dr4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAqk[(16 * I + n16) * LA + s], km, dr4, 0, 0, 0);
+          const float fm = fast_exp2(bs - mI);
+          du4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAkk[s * LA + 16 * I + n16], sBeta[s] * sK[s * LS + cl] * fm, du4,
+                                                     0, 0, 0);
+          du4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAqk[s * LA + 16 * I + n16], scale * sQ[s * LS + cl] * fm, du4,
+                                                     0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float br = sB[(16 * I + 4 * grp + e) * LS + cl];
+          const float fr = fast_exp2(br - mI), fc = fast_exp2(mI - br);
+          qd[e] += dq4[e] * fr;
+          rd[e] += dr4[e] * fr;
+          ud[e] += du4[e] * fc;
+        }
+      } else {
+        // unbounded decay: one exponential per pair, every exponent <= 0
+        float br[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) br[e] = sB[(16 * I + 4 * grp + e) * LS + cl];
+#pragma unroll 4
+        for (int sl = 0; sl < 16; ++sl) {
+          const int s = 16 * I + sl;
+          const float ks = sK[s * LS + cl], bs = sB[s * LS + cl];
+          const float xs = sBeta[s] * ks, qs = scale * sQ[s * LS + cl];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * I + 4 * grp + e;
+            if (s <= r) {
+              const float f = fast_exp2(br[e] - bs) * ks;
+              qd[e] += sDAkk[r * LA + s] * f;
+              rd[e] += sDAqk[r * LA + s] * f;
+            }
+            if (s >= r) ud[e] += (sDAkk[s * LA + r] * xs + sDAqk[s * LA + r] * qs) * fast_exp2(bs - br[e]);
+          }
+        }
+      }
+      float dBv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * I + 4 * grp + e, i = i0 + cl;
+        const float br = sB[r * LS + cl];
+        // dq, dk, the cumsum gradient and the beta gradient of (r, i)
+        float dbp = 0.f, dB = 0.f, ct = 0.f;
+        if (r < L && i < Kr) {
+          const float kr = sK[r * LS + cl], qr = sQ[r * LS + cl], be = sBeta[r];
+          const float gam = fast_exp2(br), ktf = fast_exp2(sBL[cl] - br);
+          const float t1 = gam * pq[e] + rd[e];
+          const float t2 = gam * px[e] + qd[e];
+          const float kd = ktf * pk[e];
+          const float t3 = kd + ud[e];
+          gdq[(t0 + r) * ldk + h * Kr + i] = from_f32<Tin>(scale * t1);
+          gdk[(t0 + r) * ldk + h * Kr + i] = from_f32<Tin>(be * t2 + t3);
+          dB = scale * qr * t1 + be * kr * t2 - kr * t3;
+          ct = kr * kd;
+          dbp = kr * t2;
+        }
+        dBv[e] = dB;
+        ctl += ct;
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) dbp += __shfl_xor(dbp, m);
+        if (n16 == 0) sDbw[wid * C + r] += dbp;
+      }
+      // this wave alone reads these rows of its channels again: dB goes over q
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sQ[(16 * I + 4 * grp + e) * LS + cl] = dBv[e];
+    }
+    // b_L's share summed over the rows: the lanes of one channel hold 4 rows each
+    ctl += __shfl_xor(ctl, 16);
+    ctl += __shfl_xor(ctl, 32);
+    if (grp == 0) sCT[cl] = ctl;
+    __syncthreads();
+    // per channel: b_L's terms and the reverse cumsum, in place in sQ (which holds dB)
     if (threadIdx.x < SI) {
       const int ii = threadIdx.x, i = i0 + ii;
-      float dsum = 0.f, dAcc = 0.f;
       if (i < Kr) {
-        float ct = 0.f;
-        for (int rr = 0; rr < L; ++rr) ct += sCT[rr * LS + ii];
-        const float extra = ct + fast_exp2(sBL[ii]) * bw.dlam[((int64_t)lc.gci * p.H + h) * D + i];
-        const float dt = p.dt_bias ? p.dt_bias[h * Kr + i] : 0.f;
-        float acc = extra;
+        float acc = sCT[ii] + fast_exp2(sBL[ii]) * bw.dlam[((int64_t)lc.gci * p.H + h) * D + i];
         for (int rr = L - 1; rr >= 0; --rr) {
-          acc += sDB[rr * LS + ii];
-          float out = acc;  // gradient of the natural-log decay of token rr
-          if constexpr (GK == kGateSafe || GK == kGateSoftplus) {
-            const float x = p.g[(t0 + rr) * ldk + h * Kr + i];
-            if constexpr (GK == kGateSafe) {
-              const float s = sigmoid_f32(expA * (x + dt));
-              out = acc * (p.lower_bound * s * (1.f - s) * expA);
-              dAcc += out * (x + dt);
-            } else {
-              const float z = x + dt;
-              const float sp = fmaxf(z, 0.f) + log1p_pos(fast_exp2(-fabsf(z) * kLog2e));
-              out = acc * (-expA * sigmoid_f32(z));
-              dAcc += acc * (-expA * sp);
-            }
-            dsum += out;
-          }
-          bw.dg[(t0 + rr) * ldk + h * Kr + i] = out;
+          acc += sQ[rr * LS + ii];
+          sQ[rr * LS + ii] = acc;  // gradient of the natural-log decay of token rr
         }
-        if (bw.ddt_part) bw.ddt_part[((int64_t)lc.gci * p.H + h) * D + i] = dsum;
       }
+    }
+    __syncthreads();
+    // per element: the gate activation's derivative; thread = (row group, 4 channels)
+    {
+      constexpr int CG = SI / 4, RG = kBT / CG;  // channel groups, row groups
+      const int c4 = 4 * (threadIdx.x % CG), rg = threadIdx.x / CG, i = i0 + c4;
+      float ddt4[4] = {0.f, 0.f, 0.f, 0.f}, dA4 = 0.f;
+      f32x4_t dt4 = zero4();
+      if (p.dt_bias && i < Kr) dt4 = ld4(p.dt_bias + h * Kr + i);
+      for (int rr = rg; rr < L; rr += RG) {
+        if (i >= Kr) break;
+        const f32x4_t g4 = ld4(sQ + rr * LS + c4);
+        f32x4_t out = g4;
+        if constexpr (GK == kGateSafe || GK == kGateSoftplus) {
+          const f32x4_t x4 = ld4(p.g + (t0 + rr) * ldk + h * Kr + i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float z = x4[e] + dt4[e];
+            if constexpr (GK == kGateSafe) {
+              const float sg = sigmoid_f32(expA * z);
+              out[e] = g4[e] * (p.lower_bound * sg * (1.f - sg) * expA);
+              dA4 += out[e] * z;
+            } else {
+              const float sp = fmaxf(z, 0.f) + log1p_pos(fast_exp2(-fabsf(z) * kLog2e));
+              out[e] = g4[e] * (-expA * sigmoid_f32(z));
+              dA4 += g4[e] * (-expA * sp);
+            }
+            ddt4[e] += out[e];
+          }
+        }
+        *reinterpret_cast<f32x4_t *>(bw.dg + (t0 + rr) * ldk + h * Kr + i) = out;
+      }
+      // per-channel sums over the row groups (sK and sB are free now)
+      *reinterpret_cast<f32x4_t *>(sB + rg * LS + c4) = f32x4_t{ddt4[0], ddt4[1], ddt4[2], ddt4[3]};
+      sK[rg * LS + c4] = dA4;
+    }
+    __syncthreads();
+    if (threadIdx.x < SI) {
+      constexpr int RG = kBT / (SI / 4);
+      const int ii = threadIdx.x, i = i0 + ii;
+      float dsum = 0.f, dAcc = 0.f;
+      for (int g2 = 0; g2 < RG; ++g2) {
+        dsum += sB[g2 * LS + ii];
+        if ((ii & 3) == 0) dAcc += sK[g2 * LS + ii];
+      }
+      if (bw.ddt_part && i < Kr) bw.ddt_part[((int64_t)lc.gci * p.H + h) * D + i] = dsum;
       sDA[ii] = dAcc;
     }
     __syncthreads();
@@ -488,7 +679,9 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
       for (int ii = 0; ii < SI; ++ii) dA_total += sDA[ii];
   }
   for (int rr = threadIdx.x; rr < L; rr += kBT) {
-    float d = sDbeta[rr] + bw.dbp[(t0 + rr) * p.H + h];
+    float d = bw.dbp[(t0 + rr) * p.H + h];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) d += sDbw[w * C + rr];
     if (p.beta_logits) {
       const float b = sBeta[rr];
       d *= b * (1.f - b);
@@ -545,7 +738,7 @@ hipError_t launch_bwd_t(const ChunkParams &p, const BwdParams &b, hipStream_t st
   const dim3 grid(p.max_chunks, p.H);
   {
     constexpr int LS = 32 + 4;
-    const size_t smem = sizeof(float) * ((size_t)4 * C * LS + 2 * D * LS);
+    const size_t smem = sizeof(float) * ((size_t)4 * C * LS + 2 * D * LS + C);
     if ((e = launch_k(bwd_contract_kernel<Tin, C, D>, grid, smem, st, p, b)) != hipSuccess) return e;
   }
   {
@@ -553,8 +746,8 @@ hipError_t launch_bwd_t(const ChunkParams &p, const BwdParams &b, hipStream_t st
     if ((e = launch_k(bwd_wy_kernel<Tin, C, D>, grid, smem, st, p, b)) != hipSuccess) return e;
   }
   {
-    constexpr int LS = 32 + 1, LA1 = C + 1;
-    const size_t smem = sizeof(float) * ((size_t)2 * C * LA1 + 5 * C * LS + 2 * C + 2 * 32);
+    constexpr int LS = 64 + 4, NW = kBT / 64;
+    const size_t smem = sizeof(float) * ((size_t)2 * C * LA + 3 * C * LS + 64 + C + NW * C + 2 * 64);
     switch (p.gate_kind) {
       case kGateSafe: e = launch_k(bwd_grams_kernel<Tin, C, D, kGateSafe>, grid, smem, st, p, b); break;
       case kGateSoftplus: e = launch_k(bwd_grams_kernel<Tin, C, D, kGateSoftplus>, grid, smem, st, p, b); break;
