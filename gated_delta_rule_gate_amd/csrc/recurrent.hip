@@ -67,12 +67,14 @@ struct RecCfg {
   static_assert(kThreads % kCG == 0 && K % kRG == 0, "tile");
 };
 
-template <typename Tin, int KP, int BV>
+// FULL: K == KP and V a multiple of BV, so no row or column needs a mask and
+// the widths are compile-time constants.
+template <typename Tin, int KP, int BV, bool FULL>
 __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentParams p) {
   using Cfg = RecCfg<KP, BV>;
   constexpr int RPT = Cfg::kRPT, CG = Cfg::kCG, RG = Cfg::kRG;
-  const int K = p.K;
-  const int nvb = (p.V + BV - 1) / BV;
+  const int K = FULL ? KP : p.K;
+  const int nvb = FULL ? p.V / BV : (p.V + BV - 1) / BV;
   const int vb = blockIdx.x % nvb;
   const int nh = blockIdx.x / nvb;
   const int n = nh / p.H, h = nh % p.H;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
   const int cg = tid % CG, rg = tid / CG;
   const int row0 = rg * RPT;
   const int col0 = vb * BV + cg * 4;
-  const bool col_ok = col0 < p.V;  // four columns, all inside V or none (V % 4 == 0)
+  const bool col_ok = FULL || col0 < p.V;  // four columns, all inside V or none (V % 4 == 0)
 
   const SlotRange sr = slot_range(p.cu, n, p.T);
   const int64_t sbase = ((int64_t)(n * p.H + h) * K) * p.V;
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
   if (p.h0) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-      S[r] = (col_ok && row0 + r < K) ? load_state4(p.h0 + sbase + (int64_t)(row0 + r) * p.V + col0)
-                                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      S[r] = (FULL || (col_ok && row0 + r < K)) ? load_state4(p.h0 + sbase + (int64_t)(row0 + r) * p.V + col0)
+                                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
   } else {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
       nq = to_f32(qp[thk * K + tid]);
       ng = p.g[th * K + tid];
     }
-    if (tid < BV && vb * BV + tid < p.V) nv = to_f32(vp[th * p.V + vb * BV + tid]);
+    if (tid < BV && (FULL || vb * BV + tid < p.V)) nv = to_f32(vp[th * p.V + vb * BV + tid]);
     if (tid == 0) nb = p.beta_logits ? sigmoid_f32(p.beta[th]) : p.beta[th];
   };
   if (sr.len > 0) fetch(0);
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
         for (int w = 0; w < NWAVE; ++w) qqs += s_qq[buf][w];
         os *= rsqrtf(qqs + kQNormEps);
       }
-      if (vb * BV + tid < p.V) op[th * p.V + vb * BV + tid] = from_f32<Tin>(os * (sq + kqs * d));
+      if (FULL || vb * BV + tid < p.V) op[th * p.V + vb * BV + tid] = from_f32<Tin>(os * (sq + kqs * d));
     }
     __syncthreads();
 
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(KDA_REC_THREADS) void recurrent_kernel(RecurrentPar
   if (p.ht && !(sr.len == 0 && p.ht == p.h0)) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-      if (col_ok && row0 + r < K) store_state4(p.ht + sbase + (int64_t)(row0 + r) * p.V + col0, S[r]);
+      if (FULL || (col_ok && row0 + r < K)) store_state4(p.ht + sbase + (int64_t)(row0 + r) * p.V + col0, S[r]);
   }
 }
 
@@ -211,7 +213,10 @@ template <typename Tin, int KP, int BV>
 static hipError_t launch_rec(const RecurrentParams &p, hipStream_t st) {
   const int grid = p.N * p.H * ((p.V + BV - 1) / BV);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((recurrent_kernel<Tin, KP, BV>), dim3(grid), dim3(RecCfg<KP, BV>::kThreads), 0, st, p);
+  if (p.K == KP && p.V % BV == 0)
+    hipLaunchKernelGGL((recurrent_kernel<Tin, KP, BV, true>), dim3(grid), dim3(RecCfg<KP, BV>::kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<Tin, KP, BV, false>), dim3(grid), dim3(RecCfg<KP, BV>::kThreads), 0, st, p);
   return hipGetLastError();
 }
 
