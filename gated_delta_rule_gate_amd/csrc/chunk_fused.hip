@@ -292,9 +292,11 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     const int L = min(C, sr.len - c * C);
     const int64_t off = t0 * ld + h * Vr;
     float *sDecay = sDecay2 + (c & 1) * D;
+    // chunk c - 1's state update first: it needs no new input, so the loads of
+    // this chunk's inputs land meanwhile
+    state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((c + 1) & 1) * D);
     regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound, p.q_l2norm != 0, sQn,
                             p.beta_logits != 0);
-    state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((c + 1) & 1) * D);  // chunk c - 1's
     if (hcs && owner) store_strip<float, DT, NVW>(hcs + (int64_t)c * p.H * Kr * Vr, Vr, col0, Kr, hs, Vr);
     __syncthreads();
     // the next chunk's inputs are loaded in two parts while this chunk computes
