@@ -660,6 +660,12 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
     accQ[j] = zero4();
     accK[j] = zero4();
   }
+  // the row blocks with more causal blocks have the longer dependency chains:
+  // they take the issue slots first, the short ones fill the gaps
+  if (NW == 8 && NC == 4) {
+    if (i == 3) __builtin_amdgcn_s_setprio(3);
+    else if (i == 2) __builtin_amdgcn_s_setprio(2);
+  }
   if (active) {
     if constexpr (!SAFE) {
       // token-parallel diagonal block over this wave's channels (before q is
@@ -716,6 +722,7 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
         break;
     }
   };
+  if (NW == 8 && NC == 4) __builtin_amdgcn_s_setprio(0);
   if constexpr (HS == 2) {
     // the two halves split the merge: half 1 finishes A_qk's partner and half 0
     // A_kk's, so each wave stores one partial and completes the other matrix
