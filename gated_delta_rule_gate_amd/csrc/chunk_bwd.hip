@@ -42,7 +42,7 @@ constexpr int kBT = 256;  // threads per workgroup (4 waves)
 template <int KN>
 __device__ __forceinline__ f32x4_t mm16(f32x4_t acc, const float *A, int am, int ak, const float *B, int bk, int bn,
                                        int m0, int n0) {
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const int lane = tid_opaque() & 63, r = lane & 15, g = lane >> 4;  // recomputed per use, never hoisted
   const float *pa = A + (m0 + r) * am + g * ak;
   const float *pb = B + g * bk + (n0 + r) * bn;
 #pragma unroll 8
@@ -94,8 +94,8 @@ __device__ __forceinline__ void tile_f32(float *s, int lds, const T *g, int64_t 
 // 4 fp32 values at p (16-byte aligned)
 __device__ __forceinline__ f32x4_t ld4(const float *p) { return *reinterpret_cast<const f32x4_t *>(p); }
 
-__device__ __forceinline__ int tile_row(int e) { return 4 * ((threadIdx.x & 63) >> 4) + e; }
-__device__ __forceinline__ int tile_col() { return threadIdx.x & 15; }
+__device__ __forceinline__ int tile_row(int e) { return 4 * ((tid_opaque() & 63) >> 4) + e; }
+__device__ __forceinline__ int tile_col() { return tid_opaque() & 15; }
 
 __device__ __forceinline__ float beta_at(const ChunkParams &p, int64_t row, int h) {
   const float b = p.beta[row * p.H + h];
@@ -103,14 +103,21 @@ __device__ __forceinline__ float beta_at(const ChunkParams &p, int64_t row, int 
 }
 
 // ---- scan: dv_new and the state gradients, reverse over the chunks ----
+// Per (sequence, head, 64 value columns); wave w keeps the state gradient of
+// its 16 columns in accumulator registers (C layout: tile t holds channels
+// 16t + 4(l/16) + e of column l % 16), which serve unchanged as the B operand
+// of the product with k~ under the contraction map of Mma<float>. The chunk's
+// k~, q~ and w pass through one LDS buffer in turn, so two workgroups fit on
+// a compute unit.
 template <typename Tin, int C, int D>
-__global__ __launch_bounds__(kBT) void bwd_scan_kernel(ChunkParams p, BwdParams bw) {
+__global__ __launch_bounds__(kBT, 2) void bwd_scan_kernel(ChunkParams p, BwdParams bw) {
+  using M = Mma<float>;
   constexpr int BV = 64, LH = BV + 4, LA = C + 4, LX = D + 4, NC = C / 16, DT = D / 16;
   const int nvb = (p.Vr + BV - 1) / BV;
   const int vb = blockIdx.x % nvb, nh = blockIdx.x / nvb;
   const int n = nh / p.H, h = nh % p.H;
-  const int wid = threadIdx.x >> 6;
-  const int col0 = vb * BV;
+  const int wid = wave_id();
+  const int col0 = vb * BV, jc = col0 + 16 * wid + (threadIdx.x & 15);  // this lane's value column
   const int Kr = p.Kr, Vr = p.Vr;
   const SlotRange sr = slot_range(p.cu, n, p.T);
   const int nch = (sr.len + C - 1) / C;
@@ -118,92 +125,111 @@ __global__ __launch_bounds__(kBT) void bwd_scan_kernel(ChunkParams p, BwdParams 
   const int64_t sbase = (int64_t)nh * Kr * Vr;
   const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.H * Kr, ldv = (int64_t)p.H * Vr;
   extern __shared__ __align__(16) char smem[];
-  float *sDh = reinterpret_cast<float *>(smem);  // [D][LH] gradient of the state (this value block)
-  float *sA = sDh + D * LH;                      // [C][LA] A_qk
-  float *sDo = sA + C * LA;                      // [C][LH] do
-  float *sX = sDo + C * LH;                      // [C][LX] k~, then q~
-  float *sW = sX + C * LX;                       // [C][LX] w
-  float *sDv = sW + C * LX;                      // [C][LH] dv_new
-  float *sBL = sDv + C * LH;                     // [D] b_L
+  float *sA = reinterpret_cast<float *>(smem);  // [C][LA] A_qk
+  float *sDo = sA + C * LA;                     // [C][LH] do
+  float *sX = sDo + C * LH;                     // [C][LX] k~, then q~, then w
+  float *sBL = sX + C * LX;                     // [D] b_L
   const Tin *gq = reinterpret_cast<const Tin *>(p.q), *gk = reinterpret_cast<const Tin *>(p.k);
   const Tin *gdo = reinterpret_cast<const Tin *>(bw.dout);
 
-  for (int idx = threadIdx.x; idx < D * BV; idx += kBT) {
-    const int i = idx / BV, j = idx % BV;
-    sDh[i * LH + j] = (bw.dht && i < Kr && col0 + j < Vr) ? bw.dht[sbase + (int64_t)i * Vr + col0 + j] : 0.f;
-  }
-  __syncthreads();
+  f32x4_t dh[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * t + tile_row(e);
+      dh[t][e] = (bw.dht && i < Kr && jc < Vr) ? bw.dht[sbase + (int64_t)i * Vr + jc] : 0.f;
+    }
   for (int c = nch - 1; c >= 0; --c) {
     const int64_t t0 = sr.t0 + (int64_t)c * C;
     const int L = min(C, sr.len - c * C);
     const int64_t gc = cbase + c;
     const float *gb = p.b + t0 * ld + h * D;  // this chunk's rows of b (log2)
-    float *dhn = bw.dhn + (gc * p.H + h) * Kr * Vr;
-    for (int idx = threadIdx.x; idx < D * BV; idx += kBT) {
-      const int i = idx / BV, j = idx % BV;
-      if (i < Kr && col0 + j < Vr) dhn[(int64_t)i * Vr + col0 + j] = sDh[i * LH + j];
-    }
-    const float *gbl = gb + (int64_t)(L - 1) * ld;  // b_L
-    tile_f32<float, C, C>(sA, LA, p.Aqk + t0 * ldc + h * C, ldc, L, C, [](int r, int c, float *v) {
+    const float *gbl = gb + (int64_t)(L - 1) * ld;
+    // gradient of the state after this chunk
+    if (jc < Vr) {
+      float *dhn = bw.dhn + (gc * p.H + h) * Kr * Vr;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (c + e <= r) ? v[e] : 0.f;
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * t + tile_row(e);
+          if (i < Kr) dhn[(int64_t)i * Vr + jc] = dh[t][e];
+        }
+    }
+    tile_f32<float, C, C>(sA, LA, p.Aqk + t0 * ldc + h * C, ldc, L, C, [](int r, int cc, float *v) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (cc + e <= r) ? v[e] : 0.f;
     });
     tile_f32<Tin, C, BV>(sDo, LH, gdo + t0 * ldv + h * Vr + col0, ldv, L, Vr - col0);
-    tile_f32<Tin, C, D>(sX, LX, gk + t0 * ldk + h * Kr, ldk, L, Kr, [&](int r, int c, float *v) {
-      constexpr int E = 16 / (int)sizeof(Tin);
+    tile_f32<Tin, C, D>(sX, LX, gk + t0 * ldk + h * Kr, ldk, L, Kr, [&](int r, int cc, float *v) {
       if (r >= L) return;
 #pragma unroll
-      for (int e = 0; e < E; e += 4) {
-        const f32x4_t bl = ld4(gbl + c + e), br = ld4(gb + (int64_t)r * ld + c + e);
+      for (int e = 0; e < 16 / (int)sizeof(Tin); e += 4) {
+        const f32x4_t bl = ld4(gbl + cc + e), br = ld4(gb + (int64_t)r * ld + cc + e);
 #pragma unroll
         for (int u = 0; u < 4; ++u) v[e + u] *= fast_exp2(bl[u] - br[u]);
       }
     });
     for (int i = threadIdx.x; i < D; i += kBT) sBL[i] = gbl[i];
     __syncthreads();
-    // dv_new = A_qk^T do + k~ dh (this wave: value columns 16 wid..)
+    // dv_new = A_qk^T do + k~ dh
+    f32x4_t dv[NC];
+#pragma unroll
     for (int rt = 0; rt < NC; ++rt) {
-      f32x4_t acc = zero4();
-      acc = mm16<C>(acc, sA, 1, LA, sDo, LH, 1, 16 * rt, 16 * wid);
-      acc = mm16<D>(acc, sX, LX, 1, sDh, LH, 1, 16 * rt, 16 * wid);
+      const int n16 = tid_opaque() & 15, grp = (tid_opaque() & 63) >> 4;
+      f32x4_t acc = mm16<C>(zero4(), sA, 1, LA, sDo, LH, 1, 16 * rt, 16 * wid);
+#pragma unroll
+      for (int st = 0; st < D / 4; ++st)
+        acc = M::mma(sX[(16 * rt + n16) * LX + M::kidx(st, grp, 0)], dh[st >> 2][st & 3], acc);  // dh: registers
+      dv[rt] = acc;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + tile_row(e), j = 16 * wid + tile_col();
-        sDv[r * LH + j] = acc[e];
-        if (r < L) bw.dvn[(t0 + r) * ld + h * D + col0 + j] = acc[e];
+        const int r = 16 * rt + tile_row(e);
+        if (r < L) bw.dvn[(t0 + r) * ld + h * D + jc] = acc[e];
       }
     }
     __syncthreads();
-    tile_f32<Tin, C, D>(sX, LX, gq + t0 * ldk + h * Kr, ldk, L, Kr, [&](int r, int c, float *v) {
-      constexpr int E = 16 / (int)sizeof(Tin);
+    tile_f32<Tin, C, D>(sX, LX, gq + t0 * ldk + h * Kr, ldk, L, Kr, [&](int r, int cc, float *v) {
       if (r >= L) return;
 #pragma unroll
-      for (int e = 0; e < E; e += 4) {
-        const f32x4_t br = ld4(gb + (int64_t)r * ld + c + e);
+      for (int e = 0; e < 16 / (int)sizeof(Tin); e += 4) {
+        const f32x4_t br = ld4(gb + (int64_t)r * ld + cc + e);
 #pragma unroll
         for (int u = 0; u < 4; ++u) v[e + u] *= p.scale * fast_exp2(br[u]);
       }
     });
-    tile_f32<float, C, D>(sW, LX, p.w + t0 * ld + h * D, ld, L, D);
     __syncthreads();
-    // dh <- 2^b_L dh + q~^T do - w^T dv_new (this wave's columns only)
-    for (int it = 0; it < DT; ++it) {
-      f32x4_t a1 = zero4(), a2 = zero4();
-      a1 = mm16<C>(a1, sX, 1, LX, sDo, LH, 1, 16 * it, 16 * wid);
-      a2 = mm16<C>(a2, sW, 1, LX, sDv, LH, 1, 16 * it, 16 * wid);
+    // dh <- 2^b_L dh + q~^T do
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const f32x4_t acc = mm16<C>(zero4(), sX, 1, LX, sDo, LH, 1, 16 * t, 16 * wid);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh[t][e] = fast_exp2(sBL[16 * t + tile_row(e)]) * dh[t][e] + acc[e];
+    }
+    __syncthreads();
+    tile_f32<float, C, D>(sX, LX, p.w + t0 * ld + h * D, ld, L, D);
+    __syncthreads();
+    // dh -= w^T dv_new (dv_new from registers, under the same contraction map)
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const int n16 = tid_opaque() & 15, grp = (tid_opaque() & 63) >> 4;
+      f32x4_t acc = zero4();
+#pragma unroll
+      for (int st = 0; st < C / 4; ++st)
+        acc = M::mma(sX[M::kidx(st, grp, 0) * LX + 16 * t + n16], dv[st >> 2][st & 3], acc);
+      dh[t] = dh[t] - acc;
+    }
+    __syncthreads();  // sA, sDo and sX are rewritten by the next chunk
+  }
+  if (bw.dh0 && jc < Vr) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * it + tile_row(e), j = 16 * wid + tile_col();
-        sDh[i * LH + j] = fast_exp2(sBL[i]) * sDh[i * LH + j] + a1[e] - a2[e];
+        const int i = 16 * t + tile_row(e);
+        if (i < Kr) bw.dh0[sbase + (int64_t)i * Vr + jc] = dh[t][e];
       }
-    }
-    __syncthreads();
-  }
-  if (bw.dh0) {
-    for (int idx = threadIdx.x; idx < D * BV; idx += kBT) {
-      const int i = idx / BV, j = idx % BV;
-      if (i < Kr && col0 + j < Vr) bw.dh0[sbase + (int64_t)i * Vr + col0 + j] = sDh[i * LH + j];
-    }
   }
 }
 
@@ -731,7 +757,7 @@ hipError_t launch_bwd_t(const ChunkParams &p, const BwdParams &b, hipStream_t st
   hipError_t e;
   {
     constexpr int LH = 64 + 4;
-    const size_t smem = sizeof(float) * ((size_t)D * LH + C * LA + 2 * C * LH + 2 * C * LX + D);
+    const size_t smem = sizeof(float) * ((size_t)C * LA + C * LH + C * LX + D);
     const int nvb = (p.Vr + 63) / 64;
     if ((e = launch_k(bwd_scan_kernel<Tin, C, D>, dim3(p.N * p.H * nvb), smem, st, p, b)) != hipSuccess) return e;
   }

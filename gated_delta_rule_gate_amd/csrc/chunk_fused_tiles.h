@@ -736,9 +736,12 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
       if (active) finish(true, false, true, true);
       idle();  // while the other half inverts the diagonal blocks
     } else if (active) {
+      // the inverse is a chain of cross-lane steps: it takes the issue slots first
+      __builtin_amdgcn_s_setprio(2);
       finish(false, true, true, true);
       lds_wave_order();  // this wave's A_kk rows are read back across lanes
       diag_inverse_block(sAkk, lda, sTd, ldtd, i);
+      __builtin_amdgcn_s_setprio(0);
     }
   } else {
     if (active) {
