@@ -158,3 +158,28 @@ def test_chunk_states_rejects(kda_lib):
     assert call(ctypes.c_void_p(0x100004)) == 6     # misaligned
     a.chunk_size = 16
     assert call(FAKE) == 4                          # the checks of kda_chunk_fwd come first
+
+
+def _bwd(kda_lib, a, **ptr):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, do=FAKE, dht=None, dq=FAKE2, dk=FAKE2,
+                dv=FAKE2, dg=FAKE2, dbeta=FAKE2, dh0=None, dA=None, ddt=None, ws=FAKE2)
+    args.update(ptr)
+    return kda_lib.kda_chunk_bwd(ctypes.byref(a), args["q"], args["k"], args["v"], args["g"], args["beta"],
+                                 args["h0"], args["cu"], args["do"], args["dht"], args["dq"], args["dk"], args["dv"],
+                                 args["dg"], args["dbeta"], args["dh0"], args["dA"], args["ddt"], args["ws"],
+                                 ctypes.c_size_t(1 << 40), None)
+
+
+def test_chunk_bwd_rejects(kda_lib):
+    """The backward's own limits, checked before any launch."""
+    ok = dict(gate_kind=0)
+    assert _bwd(kda_lib, _args(**ok), do=None) == 1             # d_o required
+    assert _bwd(kda_lib, _args(**ok), dg=None) == 1             # gradients required
+    assert _bwd(kda_lib, _args(**ok), dq=ctypes.c_void_p(0x40000004)) == 6
+    assert _bwd(kda_lib, _args(gate_kind=3)) == 8                # pre-cumsummed gate
+    assert _bwd(kda_lib, _args(gate_kind=0, q_l2norm=1)) == 8    # forward-only option
+    assert _bwd(kda_lib, _args(gate_kind=0, H=4, Hk=2)) == 8     # grouped value heads
+    assert _bwd(kda_lib, _args(gate_kind=0, K=256, V=256)) == 8  # tile wider than 128
+    assert _bwd(kda_lib, _args(gate_kind=0, chunk_size=16)) == 4
+    assert kda_lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_args(gate_kind=0, K=256, V=256))) == 0
+    assert kda_lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_args(gate_kind=0))) > 0

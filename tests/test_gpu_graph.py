@@ -139,3 +139,58 @@ def test_gate_cumsum_graph_replay():
         out_e = gate_cumsum(x, chunk_size=64, A_log=A_log, dt_bias=dt_bias)
         torch.cuda.synchronize()
         assert torch.equal(out_g, out_e), "replay %d differs from the eager call" % rep
+
+
+def test_chunk_bwd_graph_replay():
+    """The backward allocates nothing inside the library and never syncs: captured
+    once with its workspace and outputs fixed, each replay on rewritten inputs
+    equals an eager call bit for bit."""
+    from gated_delta_rule_gate_amd import _binding as kb
+
+    need_gpu()
+    import ctypes
+
+    first = _chunk_case(41)
+    dev = {k: v.cuda() for k, v in first.items() if v is not None}
+    rng = np.random.default_rng(42)
+    do = torch.from_numpy(rng.standard_normal((1, CAP, H, D)).astype(np.float32)).to(torch.bfloat16).cuda()
+    a = kb.make_args(dev["q"], dev["v"], H, SLOTS, "safe", chunk_size=64, A_log=dev["A_log"], dt_bias=dev["dt_bias"],
+                     lower_bound=-5.0, schedule="staged")
+    L = kb.lib()
+    ws = torch.empty((int(L.kda_chunk_bwd_workspace_bytes(ctypes.byref(a))),), dtype=torch.uint8, device="cuda")
+
+    def outputs():
+        return dict(dq=torch.zeros_like(dev["q"]), dk=torch.zeros_like(dev["k"]), dv=torch.zeros_like(dev["v"]),
+                    dg=torch.zeros_like(dev["x"]), dbeta=torch.zeros_like(dev["beta"]),
+                    dh0=torch.zeros_like(dev["h0"]), dA=torch.zeros((H,), device="cuda"),
+                    ddt=torch.zeros((H, D), device="cuda"))
+
+    def call(o):
+        P = kb._ptr
+        kb.check(L.kda_chunk_bwd(ctypes.byref(a), P(dev["q"]), P(dev["k"]), P(dev["v"]), P(dev["x"]), P(dev["beta"]),
+                                 P(dev["h0"]), P(dev["cu"]), P(do), None, P(o["dq"]), P(o["dk"]), P(o["dv"]),
+                                 P(o["dg"]), P(o["dbeta"]), P(o["dh0"]), P(o["dA"]), P(o["ddt"]), P(ws),
+                                 ctypes.c_size_t(ws.numel()), kb._stream()))
+
+    og = outputs()
+    call(og)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(og)
+    torch.cuda.synchronize()
+    for rep, seed in enumerate([43, 44, 45]):
+        case = _chunk_case(seed)
+        _refill(dev, {k: v for k, v in case.items() if v is not None})
+        do.copy_(torch.from_numpy(rng.standard_normal(do.shape).astype(np.float32)).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        oe = outputs()
+        call(oe)
+        torch.cuda.synchronize()
+        n = int(case["cu"][-1])
+        for key in ("dq", "dk", "dv", "dg", "dbeta"):
+            assert torch.equal(og[key][:, :n], oe[key][:, :n]), "replay %d: %s differs" % (rep, key)
+        for key in ("dh0", "dA", "ddt"):
+            assert torch.equal(og[key], oe[key]), "replay %d: %s differs" % (rep, key)
