@@ -299,10 +299,11 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
                             p.beta_logits != 0);
     if (hcs && owner) store_strip<float, DT, NVW>(hcs + (int64_t)c * p.H * Kr * Vr, Vr, col0, Kr, hs, Vr);
     __syncthreads();
-    // the next chunk's inputs are loaded in two parts while this chunk computes
+    // the next chunk's inputs are loaded in two parts while this chunk computes:
+    // the gate by every wave as it finishes the grams' first phase (the waves get
+    // there at different times, so their loads do not queue at once), then q, k, v
     const bool more = c + 1 < nch;
     const int Ln = more ? min(C, sr.len - (c + 1) * C) : 0;
-    if (more) regs.load_gate(p, t0 + C, Ln, h);
 
     // (1)
     if constexpr (GK == kGateLog2Cumsum) {
@@ -316,12 +317,15 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
       if (more) regs.load_qkv(p, t0 + C, Ln, h);
     };
     auto none = []() {};
+    auto gate_next = [&]() {
+      if (more) regs.load_gate(p, t0 + C, Ln, h);
+    };
     if constexpr (HALF_LOAD)
       grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT0, sT1,
-                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, load_next);
+                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, load_next, gate_next);
     else
       grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT0, sT1,
-                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, none);
+                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, none, gate_next);
     __syncthreads();
     if (!HALF_LOAD && more) regs.load_qkv(p, t0 + C, Ln, h);
     // (4) this wave's column tiles of w (channels) and u (values)

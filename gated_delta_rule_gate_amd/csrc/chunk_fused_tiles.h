@@ -623,7 +623,8 @@ __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)
 // second channel half's partial sums meanwhile.
 // Besides the grams, writes q~ over q, k~ into sKt and X_w = beta k 2^b into
 // sXw (which may overlap sB: it is written after a barrier). With two waves per
-// row block, the first of each pair calls idle() once its share is done.
+// row block, the first of each pair calls idle() once its share is done; every
+// wave calls pre() when its first-phase share is done, before the grams' barrier.
 // The channel half of its row block that wave w takes in the grams. With 8
 // waves and 4 row blocks, the halves alternate so that each SIMD (waves w and
 // w + 4) holds one wave of either half.
@@ -633,12 +634,12 @@ __device__ __forceinline__ int gram_half(int w) {
   else return w % ((NW / NC >= 2) ? 2 : 1);
 }
 
-template <int NT, int C, int D, bool SAFE, typename Idle>
+template <int NT, int C, int D, bool SAFE, typename Idle, typename Pre>
 __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                             const float *sBeta, float scale, float *sAkk, float *sAqk, int lda,
                                             bf16_t *sAqh, int ldh, int L, const float *sT0, const float *sT1,
                                             const float *sT2, const float *sBL, bf16_t *sKt, bf16_t *sXw,
-                                            bf16_t *sTd, int ldtd, Idle &&idle) {
+                                            bf16_t *sTd, int ldtd, Idle &&idle, Pre &&pre) {
   constexpr int NW = NT / 64, NC = C / 16;
   constexpr int HS = (NW / NC >= 2) ? 2 : 1, CW = D / HS, NS = CW / 32;
   static_assert(NW >= NC && CW % 32 == 0, "wave split of the grams");
@@ -730,6 +731,7 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
       if (hsel == 1) finish(true, false, false, false);
       else finish(false, true, false, false);
     }
+    pre();  // each wave as it finishes its share: the waves reach this point at different times
     __syncthreads();
     store_xw();
     if (hsel == 0) {
@@ -749,6 +751,7 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
       lds_wave_order();
       diag_inverse_block(sAkk, lda, sTd, ldtd, i);
     }
+    pre();
     __syncthreads();
     store_xw();
   }
