@@ -177,6 +177,72 @@ def bench_bwd(B, T, H, D, steps, warmup, C=64):
             "ms": round(t["mean"], 4), "Mtokens_per_s": round(B * T / (t["mean"] * 1e-3) / 1e6, 3)}
 
 
+def bench_prefill(steps, warmup):
+    """recurrent_kda over 256 sequences x 64 tokens (the recurrent prefill), H64 K=V=128 bf16, log2 gate."""
+    import kda_synth
+    from gated_delta_rule_gate_amd import recurrent_kda
+
+    N, T, H, D = 256, 64, 64, 128
+    d = kda_synth.chunk_inputs(N, T, H, D, D, dtype=torch.bfloat16, seed=1004)
+    g2 = kda_synth.log2_gate(d["x"].numpy(), d["A_log"].numpy(), d["dt_bias"].numpy()).cuda()
+    dev = {k: v.cuda() for k, v in d.items() if v is not None}
+    o = torch.empty((N, T, H, D), dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty_like(dev["h0"])
+    flush_buf = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+
+    def step():
+        recurrent_kda(dev["q"], dev["k"], dev["v"], g2, dev["beta"], dev["h0"], final_state=ht, out=o)
+
+    t = event_time_ms(step, steps, warmup, flush=lambda: flush_buf.zero_())
+    return dict(config="256 seq x 64 tokens, H64 K=V=128, bf16, log2 gate, h0 + ht", ms=round(t["mean"], 4),
+                Mtokens_per_s=round(N * T / (t["mean"] * 1e-3) / 1e6, 3))
+
+
+def bench_varlen(steps, warmup):
+    """chunk_kda on the packed workload: capacity 16384, ten slots (two empty) holding 15872
+    tokens, H16 K=V=128 bf16, softplus gate, h0 per slot."""
+    import kda_synth
+    from gated_delta_rule_gate_amd import chunk_kda
+
+    CAP, H, D, SLOTS = 16384, 16, 128, 10
+    cu = torch.from_numpy(kda_synth.varlen_offsets(1003, n_slots=SLOTS, n_empty=2, total=15872, max_len=4096))
+    d = kda_synth.chunk_inputs(1, CAP, H, D, D, dtype=torch.bfloat16, seed=1003, n_slots=SLOTS)
+    dev = {k: v.cuda() for k, v in d.items() if v is not None}
+    cu_d = cu.cuda()
+    o = torch.empty((1, CAP, H, D), dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty_like(dev["h0"])
+    flush_buf = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+
+    def step():
+        chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], dev["h0"], cu_seqlens=cu_d, chunk_size=64,
+                  gate_kind="softplus", A_log=dev["A_log"], dt_bias=dev["dt_bias"], out=o, final_state=ht)
+
+    t = event_time_ms(step, steps, warmup, flush=lambda: flush_buf.zero_())
+    n = int(cu[-1])
+    nbytes = n * H * (2 * 3 * D + 4 * D + 4 + 2 * D) + 2 * 4 * SLOTS * H * D * D
+    return dict(config="packed, capacity 16384, 10 slots (2 empty), 15872 tokens, H16 K=V=128 bf16, softplus, h0+ht",
+                ms=round(t["mean"], 4), Mtokens_per_s=round(n / (t["mean"] * 1e-3) / 1e6, 3),
+                roofline_frac=round(nbytes / (t["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
+
+def copy_bandwidth():
+    """Device copy of 1 GiB (read + write), for context beside the roofline."""
+    src = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t = event_time_ms(lambda: dst.copy_(src), 10, 2)
+    return round(2 * src.numel() * 4 / (t["median"] * 1e-3) / 1e9, 1)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 SWEEP_SHAPES = [(1, 8192, 96, 128), (2, 16384, 16, 128), (4, 2048, 16, 128), (4, 4096, 64, 128),
                    (8, 2048, 32, 256), (8, 1024, 8, 64)]
 
@@ -220,6 +286,8 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--sweep", action="store_true", help="also time a sweep of six shapes")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward figure")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed-batch and copy figures")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 64-token recurrent prefill figure")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -293,6 +361,11 @@ def main():
     }
     if not args.no_decode:
         line["recurrent_decode"] = bench_decode(max(10, args.steps), 3)
+    if not args.no_decode and not args.no_prefill:
+        line["recurrent_prefill"] = bench_prefill(max(5, args.steps // 2), 2)
+    if not args.no_varlen:
+        line["varlen"] = bench_varlen(max(5, args.steps // 2), 2)
+        line["copy_GBps"] = copy_bandwidth()
     if not args.no_bwd and args.schedule != "fused":
         line["backward"] = bench_bwd(B, T, H, D, steps=max(3, args.steps // 4), warmup=1, C=C)
     if args.sweep:
@@ -302,6 +375,8 @@ def main():
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
         line["cpu_baseline"] = cpu_baseline(d, H, T, threads)
+        line["cpu_baseline"]["cpu_model"] = cpu_model()
+        line["cpu_baseline"]["nproc"] = os.cpu_count()
     print(json.dumps(line), flush=True)
 
 
