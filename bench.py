@@ -198,7 +198,7 @@ def bench_prefill(steps, warmup):
                 Mtokens_per_s=round(N * T / (t["mean"] * 1e-3) / 1e6, 3))
 
 
-def bench_varlen(steps, warmup):
+def bench_varlen(steps, warmup, schedule="auto"):
     """chunk_kda on the packed workload: capacity 16384, ten slots (two empty) holding 15872
     tokens, H16 K=V=128 bf16, softplus gate, h0 per slot."""
     import kda_synth
@@ -215,7 +215,8 @@ def bench_varlen(steps, warmup):
 
     def step():
         chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], dev["h0"], cu_seqlens=cu_d, chunk_size=64,
-                  gate_kind="softplus", A_log=dev["A_log"], dt_bias=dev["dt_bias"], out=o, final_state=ht)
+                  gate_kind="softplus", A_log=dev["A_log"], dt_bias=dev["dt_bias"], out=o, final_state=ht,
+                  schedule=schedule)
 
     t = event_time_ms(step, steps, warmup, flush=lambda: flush_buf.zero_())
     n = int(cu[-1])
@@ -250,7 +251,7 @@ SWEEP_SHAPES = [(1, 8192, 96, 128), (2, 16384, 16, 128), (4, 2048, 16, 128), (4,
 def bench_shape(B, T, H, D, steps, warmup, schedule="auto", C=64):
     """Flushed-cache HIP-event timing of kda_chunk_fwd on one synthetic shape (safe gate)."""
     import kda_synth
-    from gated_delta_rule_gate_amd import chunk_kda
+    from gated_delta_rule_gate_amd import chunk_kda, resolved_schedule
 
     d = kda_synth.chunk_inputs(B, T, H, D, D, dtype=torch.bfloat16, seed=1002)
     dev = {k: v.cuda() for k, v in d.items() if v is not None}
@@ -270,7 +271,7 @@ def bench_shape(B, T, H, D, steps, warmup, schedule="auto", C=64):
     return {"shape": "B%d T%d H%d D%d" % (B, T, H, D), "ms": round(ms, 4),
             "Mtokens_per_s": round(B * T / (ms * 1e-3) / 1e6, 3),
             "roofline_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "schedule": "fused" if (schedule != "staged" and D <= 128) else "staged"}
+            "schedule": resolved_schedule(dev["q"], dev["v"], H, B, chunk_size=C, schedule=schedule)}
 
 
 def main():
@@ -278,7 +279,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--schedule", default="auto", choices=["auto", "fused", "staged"])
+    ap.add_argument("--schedule", default="auto", choices=["auto", "fused", "split", "staged"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the recurrent decode figure")
     ap.add_argument("--shape", default="4,4096,64,128", help="B,T,H,D")

@@ -4,6 +4,7 @@ The computation lives in the HIP library ``_build/libkda.so`` (C ABI in
 ``include/kda.h``); this package only marshals arguments to it.
 """
 from ._binding import (KdaError, chunk_kda, chunk_kda_bwd, gate_cumsum, lib, recurrent_kda,  # noqa: F401
-                       workspace_bytes)
+                       resolved_schedule, workspace_bytes)
 
-__all__ = ["chunk_kda", "chunk_kda_bwd", "recurrent_kda", "gate_cumsum", "KdaError", "lib", "workspace_bytes"]
+__all__ = ["chunk_kda", "chunk_kda_bwd", "recurrent_kda", "gate_cumsum", "KdaError", "lib", "resolved_schedule",
+           "workspace_bytes"]

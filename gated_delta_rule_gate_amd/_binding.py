@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "_build", "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
 GATE_KINDS = {"loge": 0, "safe": 1, "softplus": 2, "log2_cumsum": 3, "log2": 4}
-SCHEDULES = {"auto": 0, "staged": 1, "fused": 2}
+SCHEDULES = {"auto": 0, "staged": 1, "fused": 2, "split": 3}
 
 _LIB = None
 
@@ -51,6 +51,8 @@ def lib():
         if hasattr(L, "kda_chunk_fwd"):
             L.kda_chunk_workspace_bytes.argtypes = [ap]
             L.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
+            L.kda_chunk_schedule.argtypes = [ap]
+            L.kda_chunk_schedule.restype = ctypes.c_int
             L.kda_chunk_fwd.argtypes = [ap] + [vp] * 10 + [ctypes.c_size_t, vp]
             L.kda_chunk_fwd.restype = ctypes.c_int
             L.kda_chunk_states_count.argtypes = [ap, ctypes.c_int]
@@ -286,6 +288,13 @@ def chunk_kda_bwd(q, k, v, g, beta, do, initial_state=None, *, dht=None, cu_seql
 def workspace_bytes(q, v, H, N, chunk_size=64, schedule="auto"):
     a = make_args(q, v, H, N, "safe", chunk_size=chunk_size, schedule=schedule)
     return int(lib().kda_chunk_workspace_bytes(ctypes.byref(a)))
+
+
+def resolved_schedule(q, v, H, N, chunk_size=64, schedule="auto"):
+    """The schedule kda_chunk_fwd runs for these sizes ("staged", "fused" or "split"), or None."""
+    a = make_args(q, v, H, N, "safe", chunk_size=chunk_size, schedule=schedule)
+    r = int(lib().kda_chunk_schedule(ctypes.byref(a)))
+    return {v_: k for k, v_ in SCHEDULES.items()}.get(r)
 
 
 STAGES = {"index": 0, "gate": 1, "grams": 2, "solve": 3, "wy": 4, "scan": 5, "output": 6}

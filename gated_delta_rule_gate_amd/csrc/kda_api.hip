@@ -226,9 +226,31 @@ WsLayout staged_layout(const kda_args *a) {
   return L;
 }
 
+// AUTO on a shape the fused kernel takes: split when its cost model says so.
+// Depends on the arguments' sizes (and the device's compute units) only, so
+// kda_chunk_workspace_bytes makes the same choice.
+bool auto_split(const kda_args *a) {
+  const int64_t chain = ((int64_t)a->T + a->chunk_size - 1) / a->chunk_size;
+  const int64_t items = std::max<int64_t>(max_chunks(a, true), max_chunks(a, false)) * a->H;
+  return kda::split_preferred(chain, (int64_t)a->N * a->H, items, pad_width(std::max(a->K, a->V)));
+}
+
+bool use_split(const kda_args *a, const kda::ChunkParams &p) {
+  if (!kda::fused_supported(p)) return false;
+  return a->schedule == KDA_SCHED_SPLIT || (a->schedule == KDA_SCHED_AUTO && auto_split(a));
+}
+
 bool use_fused(const kda_args *a, const kda::ChunkParams &p) {
-  if (a->schedule == KDA_SCHED_STAGED) return false;
-  return kda::fused_supported(p);
+  if (a->schedule == KDA_SCHED_STAGED || a->schedule == KDA_SCHED_SPLIT) return false;
+  return kda::fused_supported(p) && !use_split(a, p);
+}
+
+// Split schedule: the chunk prefix, then the key side's records for every
+// (chunk, head) of the packed or dense bound.
+size_t split_ws_bytes(const kda_args *a) {
+  const int64_t nch = std::max<int64_t>(max_chunks(a, true), max_chunks(a, false));
+  return align_up(sizeof(int32_t) * (a->N + 1)) +
+         align_up(kda::split_workspace_bytes(a->chunk_size, pad_width(std::max(a->K, a->V)), nch * a->H));
 }
 
 kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const void *v, const float *g,
@@ -238,7 +260,8 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
   if (s != KDA_OK) return s;
   if ((s = check_slots(a, cu)) != KDA_OK) return s;
   if (a->chunk_size != 32 && a->chunk_size != 64) return KDA_ERR_CHUNK;
-  if (a->schedule != KDA_SCHED_AUTO && a->schedule != KDA_SCHED_STAGED && a->schedule != KDA_SCHED_FUSED)
+  if (a->schedule != KDA_SCHED_AUTO && a->schedule != KDA_SCHED_STAGED && a->schedule != KDA_SCHED_FUSED &&
+      a->schedule != KDA_SCHED_SPLIT)
     return KDA_ERR_SHAPE;
   p = kda::ChunkParams{};
   p.q = q;
@@ -268,13 +291,20 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
   p.Hk = a->Hk > 0 ? a->Hk : a->H;
   p.beta_logits = a->beta_logits;
   p.max_chunks = (int)max_chunks(a, cu != nullptr);
-  if (a->schedule == KDA_SCHED_FUSED && !kda::fused_supported(p)) return KDA_ERR_UNSUPPORTED;
+  if ((a->schedule == KDA_SCHED_FUSED || a->schedule == KDA_SCHED_SPLIT) && !kda::fused_supported(p))
+    return KDA_ERR_UNSUPPORTED;
   const size_t need = kda_chunk_workspace_bytes(a);
   if (need > 0 && (!ws || ws_bytes < need)) return KDA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return KDA_ERR_ALIGN;
   char *base = static_cast<char *>(ws);
   if (use_fused(a, p)) {
     p.chunk_off = reinterpret_cast<int32_t *>(base);
+  } else if (use_split(a, p)) {
+    const int64_t nch = std::max<int64_t>(max_chunks(a, true), max_chunks(a, false));
+    const size_t bf = (size_t)nch * a->H * 2 * (3 * (size_t)p.C * p.D + (size_t)p.C * p.C);
+    p.chunk_off = reinterpret_cast<int32_t *>(base);
+    p.sws = base + align_up(sizeof(int32_t) * (a->N + 1));
+    p.swf = reinterpret_cast<float *>(static_cast<char *>(p.sws) + bf);
   } else {
     const WsLayout L = staged_layout(a);
     p.chunk_off = reinterpret_cast<int32_t *>(base + L.off[0]);
@@ -312,9 +342,25 @@ extern "C" size_t kda_chunk_workspace_bytes(const kda_args *a) {
   kda::ChunkParams p{};
   p.D = pad_width(std::max(a->K, a->V));
   p.is_bf16 = a->dtype == KDA_BF16;
+  if (a->schedule == KDA_SCHED_SPLIT) return kda::fused_supported(p) ? split_ws_bytes(a) : 0;
+  if (a->schedule == KDA_SCHED_AUTO && kda::fused_supported(p) && auto_split(a)) return split_ws_bytes(a);
   if (a->schedule != KDA_SCHED_STAGED && kda::fused_supported(p)) return align_up(sizeof(int32_t) * (a->N + 1));
   if (a->schedule == KDA_SCHED_FUSED) return 0;
   return staged_layout(a).total;
+}
+
+extern "C" int kda_chunk_schedule(const kda_args *a) {
+  if (!chunk_shape_ok(a)) return -1;
+  if (a->schedule != KDA_SCHED_AUTO && a->schedule != KDA_SCHED_STAGED && a->schedule != KDA_SCHED_FUSED &&
+      a->schedule != KDA_SCHED_SPLIT)
+    return -1;
+  kda::ChunkParams p{};
+  p.D = pad_width(std::max(a->K, a->V));
+  p.is_bf16 = a->dtype == KDA_BF16;
+  if ((a->schedule == KDA_SCHED_FUSED || a->schedule == KDA_SCHED_SPLIT) && !kda::fused_supported(p)) return -1;
+  if (use_split(a, p)) return KDA_SCHED_SPLIT;
+  if (use_fused(a, p)) return KDA_SCHED_FUSED;
+  return KDA_SCHED_STAGED;
 }
 
 extern "C" size_t kda_staged_workspace_offset(const kda_args *a, kda_ws_field field) {
@@ -330,6 +376,10 @@ kda_status run_chunk(const kda_args *a, const kda::ChunkParams &p, hipStream_t s
     // the fused kernel reads the chunk prefix only to number the chunk-start states
     if (p.hc && p.cu && (s = run_stage(p, KDA_STAGE_INDEX, st)) != KDA_OK) return s;
     return hip_status(kda::launch_fused(p, st));
+  }
+  if (use_split(a, p)) {
+    if (p.cu && (s = run_stage(p, KDA_STAGE_INDEX, st)) != KDA_OK) return s;
+    return hip_status(kda::launch_split(p, st));
   }
   for (int stage = KDA_STAGE_INDEX; stage <= KDA_STAGE_OUTPUT; ++stage)
     if ((s = run_stage(p, stage, st)) != KDA_OK) return s;

@@ -68,6 +68,10 @@ struct ChunkParams {
   int max_chunks;      // upper bound of the number of chunks (grid size)
   int vsplit;          // fused schedule: value-column blocks per (sequence, head), set by its launcher
   float *b, *Akk, *Aqk, *Tm, *w, *u, *vnew, *hc;
+  // split schedule: the key side's operands per (chunk, head), bf16 and fp32
+  // records (sizes from split_workspace_bytes)
+  void *sws;
+  float *swf;
 };
 
 // Backward of the chunked forward (staged). The forward intermediates come from
@@ -97,5 +101,16 @@ hipError_t launch_stage_scan(const ChunkParams &p, hipStream_t st);
 hipError_t launch_stage_output(const ChunkParams &p, hipStream_t st);
 hipError_t launch_fused(const ChunkParams &p, hipStream_t st);
 bool fused_supported(const ChunkParams &p);
+// split schedule: the key side of every chunk in parallel, then the state side
+hipError_t launch_split(const ChunkParams &p, hipStream_t st);
+// workspace of the split schedule for chunk_heads (chunk, head) pairs: the bf16
+// records, then the fp32 ones
+size_t split_workspace_bytes(int C, int D, int64_t chunk_heads);
+// whether the split schedule is expected to beat the fused one for a longest
+// chain of `chain` chunks, `pairs` (sequence, head) pairs and `items` (chunk,
+// head) pairs at tile width D
+bool split_preferred(int64_t chain, int64_t pairs, int64_t items, int D);
+// compute units of the current device (cached per device)
+int device_cus();
 
 }  // namespace kda

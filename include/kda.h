@@ -79,7 +79,10 @@ typedef enum {
 typedef enum {
   KDA_SCHED_AUTO = 0,   /* pick per shape                                                   */
   KDA_SCHED_STAGED = 1, /* six kernels, one per step, intermediates in the workspace        */
-  KDA_SCHED_FUSED = 2   /* one persistent kernel per (sequence, head); state kept on chip   */
+  KDA_SCHED_FUSED = 2,  /* one persistent kernel per (sequence, head); state kept on chip   */
+  KDA_SCHED_SPLIT = 3   /* steps (1)-(4) for every chunk at once, their operands through the
+                           workspace, then one kernel per (sequence, head) for steps (5)-(6)
+                           and the state; for few (sequence, head) pairs with long sequences */
 } kda_schedule;
 
 typedef struct {
@@ -125,10 +128,20 @@ const char *kda_last_error(void);
 
 /*
  * Bytes of device workspace that kda_chunk_fwd needs for these arguments
- * (0 when the arguments are invalid). Depends on B, T, H, K, V, N, chunk_size
- * and schedule only.
+ * (0 when the arguments are invalid). Depends on B, T, H, K, V, N, chunk_size,
+ * dtype and schedule only -- and, under KDA_SCHED_AUTO, on the compute units of
+ * the current device, which the choice between the fused and split schedules
+ * weighs (call it with the device current that kda_chunk_fwd will run on).
  */
 size_t kda_chunk_workspace_bytes(const kda_args *args);
+
+/*
+ * The schedule kda_chunk_fwd runs for these arguments: KDA_SCHED_STAGED,
+ * KDA_SCHED_FUSED or KDA_SCHED_SPLIT (what KDA_SCHED_AUTO resolves to on the
+ * current device), or -1 when the arguments' sizes are invalid or the named
+ * schedule does not take them (fused and split: bf16 with K, V <= 128).
+ */
+int kda_chunk_schedule(const kda_args *args);
 
 /*
  * Step (1) of the chunked forward on its own: the gate activation and the

@@ -183,3 +183,45 @@ def test_chunk_bwd_rejects(kda_lib):
     assert _bwd(kda_lib, _args(gate_kind=0, chunk_size=16)) == 4
     assert kda_lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_args(gate_kind=0, K=256, V=256))) == 0
     assert kda_lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_args(gate_kind=0))) > 0
+
+
+def test_split_schedule_limits_and_workspace(kda_lib):
+    """The split schedule: bf16 and tiles up to 128 only, a schedule value past
+    the enumeration rejected, and a workspace that holds the chunk prefix and, per
+    (chunk, head) of the larger of the dense and packed chunk bounds, the bf16
+    operands q~, k~, w^T (C*D each) and A_qk (C*C) and the fp32 u (C*D), 2^b_L
+    (D) and row scales (C)."""
+    call = lambda a: kda_lib.kda_chunk_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None,
+                                           FAKE2, ctypes.c_size_t(1 << 40), None)
+    assert call(_args(gate_kind=0, schedule=3, dtype=1)) == 8            # fp32
+    assert call(_args(gate_kind=0, schedule=3, K=256, V=256)) == 8       # tile 256
+    assert call(_args(gate_kind=0, schedule=4)) == 2                     # no such schedule
+    align = lambda x: (x + 255) // 256 * 256
+    for B, N, T, H, K, V, C in ((3, 3, 203, 2, 128, 128, 64), (1, 5, 420, 4, 96, 64, 32)):
+        a = _args(gate_kind=0, schedule=3, B=B, N=N, T=T, H=H, K=K, V=V, chunk_size=C)
+        D = 64 if max(K, V) <= 64 else 128
+        nt = (T + C - 1) // C
+        nch = max(B * nt, nt + N)
+        per = 2 * (3 * C * D + C * C) + 4 * (C * D + D + C)
+        assert kda_lib.kda_chunk_workspace_bytes(ctypes.byref(a)) == align(4 * (N + 1)) + align(nch * H * per)
+    assert kda_lib.kda_chunk_workspace_bytes(ctypes.byref(_args(gate_kind=0, schedule=3, dtype=1))) == 0
+
+
+def test_resolved_schedule(kda_lib):
+    """What AUTO runs: fused for one (sequence, head) pair per compute unit, split
+    for few pairs with long sequences, staged for fp32 or tiles past 128; a named
+    schedule that cannot take the arguments resolves to -1. (Without a device the
+    library assumes 256 compute units.)"""
+    sched = lambda **kw: kda_lib.kda_chunk_schedule(ctypes.byref(_args(gate_kind=0, **kw)))
+    assert sched(B=4, N=4, T=4096, H=64) == 2
+    assert sched(B=2, N=2, T=16384, H=16) == 3
+    assert sched(B=2, N=2, T=16384, H=16, dtype=1) == 1
+    assert sched(B=2, N=2, T=16384, H=16, K=256, V=256) == 1
+    assert sched(B=4, N=4, T=4096, H=64, schedule=3) == 3
+    assert sched(B=2, N=2, T=16384, H=16, schedule=2) == 2
+    assert sched(dtype=1, schedule=2) == -1
+    assert sched(K=256, V=256, schedule=3) == -1
+    assert sched(chunk_size=16) == -1
+    a = _args(gate_kind=0, B=2, N=2, T=16384, H=16)
+    b = _args(gate_kind=0, B=2, N=2, T=16384, H=16, schedule=3)
+    assert kda_lib.kda_chunk_workspace_bytes(ctypes.byref(a)) == kda_lib.kda_chunk_workspace_bytes(ctypes.byref(b))

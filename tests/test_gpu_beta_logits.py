@@ -26,7 +26,7 @@ def _logits(shape, seed):
     return torch.from_numpy(x)
 
 
-@pytest.mark.parametrize("schedule", ["fused", "staged"])
+@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
 @pytest.mark.parametrize("C", [64, 32])
 def test_chunk_beta_logits(schedule, C):
     from gated_delta_rule_gate_amd import chunk_kda

@@ -1,6 +1,7 @@
 """GPU parity of kda_chunk_fwd (chunked prefill) against the FP64 oracle.
 
-Both schedules (six staged kernels, and the fused persistent kernel) are
+All schedules (six staged kernels, the fused persistent kernel, and the
+split pair of a per-chunk key-side kernel and a per-sequence state kernel) are
 compared element by element with the token recurrence on the same seeded
 inputs; the full-size shapes compare sampled (sequence, head) pairs, each an
 exact sub-problem the oracle computes on its own.
@@ -62,14 +63,14 @@ def oracle_pairs(d, gate, pairs):
     return np.stack(os_), np.stack(hts)
 
 
-SCHEDULES = ["fused", "staged"]
+SCHEDULES = ["fused", "split", "staged"]
 
 
-def expect_fused_unsupported(d, cu=None):
+def expect_fused_unsupported(d, cu=None, schedule="fused"):
     from gated_delta_rule_gate_amd import KdaError
 
     with pytest.raises(KdaError, match="UNSUPPORTED"):
-        gpu_run(d, "safe", "fused", cu=cu)
+        gpu_run(d, "safe", schedule, cu=cu)
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES)
@@ -79,8 +80,8 @@ def test_fp32_small_config(schedule, C):
     kernel takes bf16 only: fp32 runs the staged schedule, also under "auto")."""
     need_gpu()
     d = make(1, 256, 2, 64, torch.float32, 1000, with_h0=False)
-    if schedule == "fused":
-        expect_fused_unsupported(d)
+    if schedule in ("fused", "split"):
+        expect_fused_unsupported(d, schedule=schedule)
         schedule = "auto"
     o, ht = gpu_run(d, "safe", schedule, C=C)
     o_ref, ht_ref = oracle_run(d, "safe")
@@ -106,7 +107,7 @@ def test_bf16_ragged(schedule, gate, C):
 def test_bf16_widths(schedule, D):
     need_gpu()
     d = make(2, 150, 2, D, torch.bfloat16, 300 + D)
-    if schedule == "fused" and D == 256:
+    if schedule in ("fused", "split") and D == 256:
         from gated_delta_rule_gate_amd import KdaError
 
         with pytest.raises(KdaError, match="UNSUPPORTED"):  # the fused tile needs D <= 128
@@ -129,8 +130,8 @@ def test_packed_empty_slots_tail(schedule, dtype):
     cap = int(cu[-1]) + 37
     D = 64 if dtype == torch.float32 else 128
     d = make(1, cap, 2, D, dtype, 400, gate="safe", n_slots=len(lens))
-    if schedule == "fused" and dtype == torch.float32:
-        expect_fused_unsupported(d, cu)
+    if schedule in ("fused", "split") and dtype == torch.float32:
+        expect_fused_unsupported(d, cu, schedule)
         schedule = "auto"
     end = int(cu[-1])
     for key in ("q", "k", "v", "g"):

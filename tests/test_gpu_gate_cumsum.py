@@ -112,7 +112,7 @@ def test_gate_cumsum_rejects_overlap():
         gate_cumsum(g, chunk_size=16, gate_kind="loge")
 
 
-@pytest.mark.parametrize("schedule", ["fused", "staged"])
+@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
 @pytest.mark.parametrize("C", [64, 32])
 def test_chunk_with_precumsummed_gate(schedule, C):
     """kda_gate_cumsum then kda_chunk_fwd(LOG2_CUMSUM) equals the recurrence on the raw gate,

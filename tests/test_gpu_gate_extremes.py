@@ -62,7 +62,7 @@ def _chunk(d, gate, lb, schedule, cu=None):
     return o.float().cpu().numpy(), ht.cpu().numpy()
 
 
-@pytest.mark.parametrize("schedule", ["fused", "staged"])
+@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
 @pytest.mark.parametrize("gate,lb", [("safe", -5.0), ("safe", -1e-3), ("softplus", -5.0)])
 def test_chunk_gate_extremes(schedule, gate, lb):
     need_gpu()
@@ -73,7 +73,7 @@ def test_chunk_gate_extremes(schedule, gate, lb):
     parity(ht, ht_ref, "bf16", "ht")
 
 
-@pytest.mark.parametrize("schedule", ["fused", "staged"])
+@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
 def test_chunk_long_decay_packed(schedule):
     """A long slot (2048 tokens) beside short ragged ones, bound close to 0, so
     the cumulative decay stays near 1 over the whole sequence."""

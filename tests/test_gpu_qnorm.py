@@ -50,7 +50,7 @@ def _gpu_chunk(d, schedule, cu=None, C=64, q_l2norm=True):
     return o.float().cpu().numpy(), ht.cpu().numpy()
 
 
-@pytest.mark.parametrize("schedule", ["fused", "staged"])
+@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
 @pytest.mark.parametrize("D,C", [(128, 64), (128, 32), (64, 64)])
 def test_chunk_q_l2norm(schedule, D, C):
     need_gpu()

@@ -39,12 +39,18 @@ def _chunk(d, schedule, C=64, cu=None):
     return o.float().cpu().numpy(), ht.cpu().numpy()
 
 
-@pytest.mark.parametrize("schedule", ["auto", "staged"])
+@pytest.mark.parametrize("schedule", ["auto", "split", "staged"])
 @pytest.mark.parametrize("K,V", PAIRS)
 def test_chunk_widths(schedule, K, V):
     need_gpu()
     B, T, H = 2, 203, 2
     d = kda_synth.chunk_inputs(B, T, H, K, V, dtype=torch.bfloat16, seed=1200 + K + V)
+    if schedule == "split" and max(K, V) > 128:
+        from gated_delta_rule_gate_amd import KdaError
+
+        with pytest.raises(KdaError, match="UNSUPPORTED"):  # its tiles stop at 128
+            _chunk(d, schedule)
+        return
     o, ht = _chunk(d, schedule)
     assert o.shape == (B, T, H, V) and ht.shape == (B, H, K, V)
     o_ref, ht_ref = oracle.recurrent(f64(d["q"]), f64(d["k"]), f64(d["v"]), _gate(d), f64(d["beta"]),
@@ -64,7 +70,7 @@ def test_chunk_widths_fp32(K, V):
     parity(ht, ht_ref, "fp32", "ht")
 
 
-@pytest.mark.parametrize("schedule", ["auto", "staged"])
+@pytest.mark.parametrize("schedule", ["auto", "split", "staged"])
 def test_chunk_widths_packed_states(schedule):
     """K != V, packed with an empty slot and few (sequence, head) pairs, with the
     chunk-start states in the [K, V] layout of h0."""
