@@ -407,12 +407,6 @@ size_t split_workspace_bytes(int C, int D, int64_t chunk_heads) {
   return (size_t)chunk_heads * (size_t)(2 * bf + 4 * f);
 }
 
-// Item i of the key side: (chunk gc, head h) with the items of a head
-// consecutive; false past the last chunk.
-__device__ __forceinline__ bool split_item(const ChunkParams &p, int64_t i, int total, ChunkLoc &lc, int &h) {
-  h = (int)(i / total);
-  return locate_chunk(p, (int)(i % total), lc);
-}
 
 // Steps (1)-(4) for a contiguous range of (chunk, head) items per workgroup (one
 // workgroup per compute unit), the next item's inputs loaded while the current
@@ -461,18 +455,20 @@ __global__ __launch_bounds__(NT) void split_key_kernel(ChunkParams p) {
   constexpr int NL = HALF_LOAD ? NT / 2 : NT;
   const bool loader = !HALF_LOAD || gram_half<NW, NC>(wid) == 0;
   ChunkRegs<Tin, C, D, NT, NL> regs;
+  // item i is (chunk i % total, head i / total): the items of a head are consecutive
+  int h = (int)(i0 / total), gc = (int)(i0 % total);
   ChunkLoc lc;
-  int h;
-  split_item(p, i0, total, lc, h);
+  locate_chunk(p, gc, lc);
   regs.load_gate(p, lc.t0, lc.L, h);
   if (loader) regs.load_qkv(p, lc.t0, lc.L, h);
-  int hdt = -1;  // head whose dt_bias sDt holds
+  int hdt = -1;  // head whose dt_bias sDt and exp(A_log) expA hold
+  float expA = 0.f;
 
   for (int64_t it = i0; it < i1; ++it) {
     const int L = lc.L;
     const int64_t t0 = lc.t0, gh = (int64_t)lc.gci * p.H + h;
-    const float expA = (GK == kGateSafe || GK == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
     if (h != hdt) {  // uniform: a new head (the first item, or a range that crosses heads)
+      expA = (GK == kGateSafe || GK == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
       for (int i = tid_opaque(); i < D; i += NT) {
         const float dt = (p.dt_bias && i < p.Kr) ? p.dt_bias[h * p.Kr + i] : 0.f;
         sDt[i] = (GK == kGateSafe) ? dt * (-expA * kLog2e) : dt;
@@ -485,9 +481,10 @@ __global__ __launch_bounds__(NT) void split_key_kernel(ChunkParams p) {
     __syncthreads();
     // the next item, loaded while this one computes
     ChunkLoc ln = lc;
-    int hn = h;
     const bool more = it + 1 < i1;
-    if (more) split_item(p, it + 1, total, ln, hn);
+    const bool wrap = gc + 1 == total;
+    const int hn = wrap ? h + 1 : h, gn = wrap ? 0 : gc + 1;
+    if (more) locate_chunk(p, gn, ln);
     // (1)
     if constexpr (GK == kGateLog2Cumsum) {
       gate_pad<NT, C, D>(sB, LDB, sBL, L);
@@ -544,6 +541,7 @@ __global__ __launch_bounds__(NT) void split_key_kernel(ChunkParams p) {
     __syncthreads();  // the tiles are read out before the next item's store
     lc = ln;
     h = hn;
+    gc = gn;
   }
 }
 
