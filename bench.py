@@ -51,7 +51,7 @@ def alg_flops_chunk(B, T, H, D, C=64):
     return B * T * H * per
 
 
-FUSED_SOURCES = ("chunk_fused.hip", "chunk_fused_tiles.h", "chunk_tiles.h", "kda_device.h", "kda_launch.h")
+FUSED_SOURCES = ("chunk_fused.hip", "chunk_fused_layout.h", "chunk_fused_tiles.h", "chunk_tiles.h", "kda_device.h", "kda_launch.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_chunk_b4t4096h64d128_traffic.txt")
 
 
@@ -285,7 +285,7 @@ def main():
     ap.add_argument("--shape", default="4,4096,64,128", help="B,T,H,D")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
-    ap.add_argument("--sweep", action="store_true", help="also time a sweep of six shapes")
+    ap.add_argument("--sweep", action="store_true", help="also time a sweep of six shapes (and, where AUTO chose fused or split, the other one)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward figure")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed-batch and copy figures")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 64-token recurrent prefill figure")
@@ -300,13 +300,14 @@ def main():
         sys.exit(2)
 
     import kda_synth
-    from gated_delta_rule_gate_amd import chunk_kda, lib
+    from gated_delta_rule_gate_amd import chunk_kda, lib, resolved_schedule
 
     lib()
     B, T, H, D = (int(x) for x in args.shape.split(","))
     C = 64
     d = kda_synth.chunk_inputs(B, T, H, D, D, dtype=torch.bfloat16, seed=1002)
     dev = {k: v.cuda() for k, v in d.items() if v is not None}
+    sched = resolved_schedule(dev["q"], dev["v"], H, B, chunk_size=C, schedule=args.schedule)
     o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
     ht = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
     flush_buf = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
@@ -348,12 +349,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "chunk_kda fwd B%d T%d H%d K=V=%d bf16, C=%d, safe gate lb=-5, h0+ht" % (B, T, H, D, C),
-                   "B": B, "T": T, "H": H, "D": D, "chunk": C, "schedule": args.schedule, "cache": "flushed"},
+                   "B": B, "T": T, "H": H, "D": D, "chunk": C, "schedule": args.schedule, "runs": sched,
+                   "cache": "flushed"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if args.schedule != "staged" and (B, T, H, D) == (4, 4096, 64, 128)
+                     "traffic": measured_traffic() if sched == "fused" and (B, T, H, D) == (4, 4096, 64, 128)
                      else None,
-                     "kernel": "fused_chunk_kernel" if args.schedule != "staged" else "staged chain",
+                     "kernel": {"fused": "fused_chunk_kernel", "split": "split_key_kernel + split_state_kernel"}.get(
+                         sched, "staged chain"),
                      "alg_bytes_per_launch": nbytes,
                      "alg_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
                      "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
@@ -372,7 +375,15 @@ def main():
     if args.sweep:
         del dev, o, ht, flush_buf
         torch.cuda.empty_cache()
-        line["shape_sweep"] = [bench_shape(*shp, steps=max(5, args.steps // 2), warmup=2) for shp in SWEEP_SHAPES]
+        line["shape_sweep"] = []
+        for shp in SWEEP_SHAPES:
+            r = bench_shape(*shp, steps=max(5, args.steps // 2), warmup=2)
+            if r["schedule"] in ("fused", "split"):  # the schedule AUTO passed over, for comparison
+                other = "split" if r["schedule"] == "fused" else "fused"
+                r["other"] = {"schedule": other,
+                              "ms": bench_shape(*shp, steps=max(5, args.steps // 2), warmup=2, schedule=other)["ms"]}
+            line["shape_sweep"].append(r)
+            torch.cuda.empty_cache()
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
         line["cpu_baseline"] = cpu_baseline(d, H, T, threads)
