@@ -94,6 +94,22 @@ def test_stage_solve(dtype, D, gate):
     got = get(run, "T")[valid]
     want = it["T"].reshape(B * T, 2, -1)[valid]
     assert np.abs(got - want).max() <= 2e-5 * max(1.0, np.abs(want).max()), np.abs(got - want).max()
+    # residual of the GPU's inverse itself: (I + A_kk) T = I on every chunk (rows of a
+    # partial chunk past its end do not exist)
+    C = got.shape[-1]
+    A = it["Akk"].reshape(B, T, 2, C)
+    Tg = got.reshape(B, T, 2, C)
+    worst = 0.0
+    for b in range(B):
+        for c0 in range(0, T, C):
+            L = min(C, T - c0)
+            for h in range(2):
+                M = np.eye(L) + np.tril(A[b, c0:c0 + L, h, :L], -1)
+                Ti = Tg[b, c0:c0 + L, h, :L].astype(np.float64)
+                R = M @ Ti - np.eye(L)
+                bound = 1e-5 * max(1.0, np.abs(M).sum(1).max() * np.abs(Ti).sum(1).max())
+                assert np.abs(R).max() <= bound, (b, c0, h, np.abs(R).max(), bound)
+                worst = max(worst, np.abs(R).max())
 
 
 @pytest.mark.parametrize("dtype,D,gate", CASES)
