@@ -225,6 +225,30 @@ def test_contract_shapes_sampled(shape):
     parity(got_h, ht_ref, "bf16", "ht")
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES + ["recurrent"])
+def test_long_sequence(schedule):
+    """One 65536-token sequence (1024 chunks in one chain; token offsets past
+    2^24 elements), two heads, safe gate with the bound close to 0 so the state
+    keeps its history: every output against the oracle."""
+    need_gpu()
+    from gated_delta_rule_gate_amd import recurrent_kda
+
+    B, T, H, D = 1, 65536, 2, 128
+    d = make(B, T, H, D, torch.bfloat16, 1700)
+    lb = -0.05
+    if schedule == "recurrent":
+        dd = {k: (v.cuda() if v is not None else None) for k, v in d.items()}
+        o, ht = recurrent_kda(dd["q"], dd["k"], dd["v"], dd["x"], dd["beta"], dd["h0"], output_final_state=True,
+                              gate_kind="safe", A_log=dd["A_log"], dt_bias=dd["dt_bias"], lower_bound=lb)
+        torch.cuda.synchronize()
+        o, ht = o.float().cpu().numpy(), ht.cpu().numpy()
+    else:
+        o, ht = gpu_run(d, "safe", schedule, lb=lb)
+    o_ref, ht_ref = oracle_run(d, "safe", lb=lb)
+    parity(o, o_ref, "bf16", "o")
+    parity(ht, ht_ref, "bf16", "ht")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("pairs", [144, 96, 48, 6])
 def test_value_column_split(D, pairs):
