@@ -39,7 +39,8 @@ kda_status check_common(const kda_args *a, const void *q, const void *k, const v
   if (a->Hk < 0 || (a->Hk > 0 && a->H % a->Hk != 0)) return KDA_ERR_SHAPE;
   if (a->K < 1 || a->V < 1) return KDA_ERR_SHAPE;
   if (a->dtype != KDA_BF16 && a->dtype != KDA_F32) return KDA_ERR_DTYPE;
-  if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL;
+  // with no tokens (T == 0) the token tensors are never touched and may be NULL
+  if (a->T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) || !aligned16(h0) ||
       !aligned16(ht))
     return KDA_ERR_ALIGN;
@@ -106,7 +107,7 @@ extern "C" kda_status kda_gate_cumsum(const kda_args *a, const float *g_in, cons
                                       int chunk_size, float *g_out, void *stream) {
   if (!a) return KDA_ERR_NULL;
   if (a->B < 1 || a->T < 0 || a->H < 1 || a->N < 0 || a->K < 1) return KDA_ERR_SHAPE;
-  if (!g_in || !g_out) return KDA_ERR_NULL;
+  if (a->T > 0 && (!g_in || !g_out)) return KDA_ERR_NULL;
   if (!aligned16(g_in) || !aligned16(g_out)) return KDA_ERR_ALIGN;
   if (chunk_size != 1 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_CHUNK;
   switch (a->gate_kind) {
@@ -476,7 +477,7 @@ extern "C" kda_status kda_chunk_bwd(const kda_args *a, const void *q, const void
                                     float *dbeta, float *dh0, float *dA_log, float *ddt_bias, void *workspace,
                                     size_t ws_bytes, void *stream) {
   if (!a) return KDA_ERR_NULL;
-  if (!d_o || !dq || !dk || !dv || !dg || !dbeta) return KDA_ERR_NULL;
+  if (a->T > 0 && (!d_o || !dq || !dk || !dv || !dg || !dbeta)) return KDA_ERR_NULL;
   if (!aligned16(d_o) || !aligned16(dht) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) ||
       !aligned16(dh0))
     return KDA_ERR_ALIGN;

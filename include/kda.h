@@ -31,6 +31,9 @@
  *     them ("Add fused recurrent_kda ...", PR #345 text: k keeps an explicit
  *     l2norm; inference callers normalise q before the op).
  *   - ht may alias h0 (in-place state update). ht == NULL skips the final state.
+ *   - With T == 0 there are no tokens: the per-token tensors (q, k, v, g, beta,
+ *     o; in the backward d_o and the per-token gradients) are never touched and
+ *     may be NULL, and every final state is its h0 (the backward: dh0 = dht).
  *   - Errors: arguments that the host can check return a status code and
  *     launch nothing. Device-side contract violations (offsets that decrease,
  *     cu_seqlens[N] > T) are undefined behaviour. A failed launch returns

@@ -284,3 +284,36 @@ def test_config_varlen_softplus():
     end = int(cu[-1])
     parity(o[:, :end][:, :, heads], o_ref[:, :end], "bf16", "o")
     parity(ht[:, heads], ht_ref, "bf16", "ht")
+
+
+def test_empty_batch():
+    """T = 0: no tokens, NULL token pointers; every final state is its h0 bit for bit
+    (every schedule and the recurrent kernel), the chunk cumsum writes nothing, and
+    the backward returns dh0 = dht and zero parameter gradients."""
+    need_gpu()
+    from gated_delta_rule_gate_amd import chunk_kda, chunk_kda_bwd, gate_cumsum, recurrent_kda
+
+    B, H, D = 2, 3, 128
+    d = make(B, 0, H, D, torch.bfloat16, 1800)
+    dd = {k: (v.cuda() if v is not None else None) for k, v in d.items()}
+    h0 = d["h0"].numpy()
+    kw = dict(gate_kind="safe", A_log=dd["A_log"], dt_bias=dd["dt_bias"], lower_bound=-5.0)
+    for schedule in SCHEDULES:
+        o, ht = chunk_kda(dd["q"], dd["k"], dd["v"], dd["x"], dd["beta"], dd["h0"], output_final_state=True,
+                          schedule=schedule, **kw)
+        torch.cuda.synchronize()
+        assert o.shape == (B, 0, H, D)
+        assert np.array_equal(ht.cpu().numpy().view(np.uint32), h0.view(np.uint32)), schedule
+    o, ht = recurrent_kda(dd["q"], dd["k"], dd["v"], dd["x"], dd["beta"], dd["h0"], output_final_state=True, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(ht.cpu().numpy().view(np.uint32), h0.view(np.uint32))
+    b = gate_cumsum(dd["x"], chunk_size=64, **kw)
+    torch.cuda.synchronize()
+    assert b.shape == (B, 0, H, D)
+    dht = torch.randn((B, H, D, D), dtype=torch.float32, device="cuda")
+    do = torch.empty((B, 0, H, D), dtype=torch.bfloat16, device="cuda")
+    g = chunk_kda_bwd(dd["q"], dd["k"], dd["v"], dd["x"], dd["beta"], do, dd["h0"], dht=dht, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dht)
+    assert g["dq"].shape == (B, 0, H, D) and g["dg"].shape == (B, 0, H, D)
+    assert not g["dA_log"].any() and not g["ddt_bias"].any()
