@@ -53,6 +53,8 @@ def lib():
             L.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
             L.kda_chunk_schedule.argtypes = [ap]
             L.kda_chunk_schedule.restype = ctypes.c_int
+            L.kda_check_offsets.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp]
+            L.kda_check_offsets.restype = ctypes.c_int
             L.kda_chunk_fwd.argtypes = [ap] + [vp] * 10 + [ctypes.c_size_t, vp]
             L.kda_chunk_fwd.restype = ctypes.c_int
             L.kda_chunk_states_count.argtypes = [ap, ctypes.c_int]
@@ -288,6 +290,19 @@ def chunk_kda_bwd(q, k, v, g, beta, do, initial_state=None, *, dht=None, cu_seql
 def workspace_bytes(q, v, H, N, chunk_size=64, schedule="auto"):
     a = make_args(q, v, H, N, "safe", chunk_size=chunk_size, schedule=schedule)
     return int(lib().kda_chunk_workspace_bytes(ctypes.byref(a)))
+
+
+OFFSET_FLAGS = {1: "offsets decrease", 2: "first offset negative", 4: "last offset past the capacity"}
+
+
+def check_offsets(cu_seqlens, T):
+    """Flag bits of the packed-offset contract for capacity T (0: valid), checked on the
+    device by kda_check_offsets; this wrapper synchronises to read the flag."""
+    _require(cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1,
+             "cu_seqlens must be a 1-D int32 device tensor")
+    flags = torch.empty((1,), dtype=torch.int32, device=cu_seqlens.device)
+    check(lib().kda_check_offsets(_ptr(cu_seqlens), cu_seqlens.numel() - 1, int(T), _ptr(flags), _stream()))
+    return int(flags.item())
 
 
 def resolved_schedule(q, v, H, N, chunk_size=64, schedule="auto"):

@@ -4,6 +4,7 @@
 // (sequence, head, 64-column value block) and walks the chunks in order.
 // Grids are sized from capacity; workgroups past the last chunk exit at once,
 // so no launch depends on a host read of cu_seqlens.
+#include "../../include/kda.h"
 #include "chunk_loc.h"
 #include "chunk_tiles.h"
 #include "kda_launch.h"
@@ -316,6 +317,28 @@ hipError_t dispatch(const ChunkParams &p, F &&f) {
 }
 
 }  // namespace
+
+// ---- offsets check: the device-side contract of cu_seqlens, as flag bits ----
+__global__ __launch_bounds__(256) void check_offsets_kernel(const int32_t *cu, int N, int T, int32_t *flags) {
+  __shared__ int s_bad;
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int n = threadIdx.x; n < N; n += 256)
+    if (cu[n + 1] < cu[n]) bad |= KDA_OFFSETS_DECREASE;
+  if (threadIdx.x == 0) {
+    if (cu[0] < 0) bad |= KDA_OFFSETS_NEGATIVE;
+    if (cu[N] > T) bad |= KDA_OFFSETS_PAST_END;
+  }
+  if (bad) atomicOr(&s_bad, bad);
+  __syncthreads();
+  if (threadIdx.x == 0) flags[0] = s_bad;
+}
+
+hipError_t launch_check_offsets(const int32_t *cu, int N, int T, int32_t *flags, hipStream_t st) {
+  hipLaunchKernelGGL(check_offsets_kernel, dim3(1), dim3(256), 0, st, cu, N, T, flags);
+  return hipGetLastError();
+}
 
 hipError_t launch_chunk_index(const ChunkParams &p, hipStream_t st) {
   if (!p.cu) return hipSuccess;

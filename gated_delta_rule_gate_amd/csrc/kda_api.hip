@@ -100,6 +100,12 @@ extern "C" const char *kda_status_string(kda_status s) {
 
 extern "C" const char *kda_last_error(void) { return g_last_error; }
 
+extern "C" kda_status kda_check_offsets(const int32_t *cu_seqlens, int N, int T, int32_t *flags, void *stream) {
+  if (!cu_seqlens || !flags) return KDA_ERR_NULL;
+  if (N < 0 || T < 0) return KDA_ERR_SHAPE;
+  return hip_status(kda::launch_check_offsets(cu_seqlens, N, T, flags, (hipStream_t)stream));
+}
+
 // ---------------------------------------------------------------------------------------------
 // step (1) on its own
 // ---------------------------------------------------------------------------------------------

@@ -93,6 +93,8 @@ struct BwdParams {
 hipError_t launch_bwd(const ChunkParams &p, const BwdParams &b, hipStream_t st);
 
 hipError_t launch_chunk_index(const ChunkParams &p, hipStream_t st);
+// flag bits (kda.h) of the contract of cu_seqlens [N + 1] for capacity T, into flags[0]
+hipError_t launch_check_offsets(const int32_t *cu, int N, int T, int32_t *flags, hipStream_t st);
 hipError_t launch_stage_gate(const ChunkParams &p, hipStream_t st);
 hipError_t launch_stage_grams(const ChunkParams &p, hipStream_t st);
 hipError_t launch_stage_solve(const ChunkParams &p, hipStream_t st);

@@ -130,6 +130,25 @@ const char *kda_status_string(kda_status s);
 const char *kda_last_error(void);
 
 /*
+ * Checks the device-side contract of packed offsets, which the other calls
+ * cannot check without a host read ("Attention-gym KDA ...", the varlen
+ * contract: offsets that never decrease and end within the capacity). One
+ * asynchronous launch on `stream` reads cu_seqlens [N + 1] (device) and writes
+ * into flags[0] (device int32, caller-owned) the OR of
+ *   KDA_OFFSETS_DECREASE   some cu_seqlens[n + 1] < cu_seqlens[n]
+ *   KDA_OFFSETS_NEGATIVE   cu_seqlens[0] < 0
+ *   KDA_OFFSETS_PAST_END   cu_seqlens[N] > T
+ * or 0 when the offsets are valid for a call with capacity T. A debugging aid:
+ * run it before kda_chunk_fwd or kda_recurrent_fwd and read the flag at the
+ * next synchronisation. Errors: KDA_ERR_NULL (cu_seqlens or flags NULL),
+ * KDA_ERR_SHAPE (N < 0 or T < 0), KDA_ERR_HIP (launch failure).
+ */
+#define KDA_OFFSETS_DECREASE 1
+#define KDA_OFFSETS_NEGATIVE 2
+#define KDA_OFFSETS_PAST_END 4
+kda_status kda_check_offsets(const int32_t *cu_seqlens, int N, int T, int32_t *flags, void *stream);
+
+/*
  * Bytes of device workspace that kda_chunk_fwd needs for these arguments
  * (0 when the arguments are invalid). Depends on B, T, H, K, V, N, chunk_size,
  * dtype and schedule only -- and, under KDA_SCHED_AUTO, on the compute units of

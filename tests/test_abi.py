@@ -225,3 +225,11 @@ def test_resolved_schedule(kda_lib):
     a = _args(gate_kind=0, B=2, N=2, T=16384, H=16)
     b = _args(gate_kind=0, B=2, N=2, T=16384, H=16, schedule=3)
     assert kda_lib.kda_chunk_workspace_bytes(ctypes.byref(a)) == kda_lib.kda_chunk_workspace_bytes(ctypes.byref(b))
+
+
+def test_check_offsets_rejects(kda_lib):
+    """kda_check_offsets: NULL offsets or flags, negative N or T, checked before any launch."""
+    assert kda_lib.kda_check_offsets(None, 3, 100, FAKE2, None) == 1
+    assert kda_lib.kda_check_offsets(FAKE, 3, 100, None, None) == 1
+    assert kda_lib.kda_check_offsets(FAKE, -1, 100, FAKE2, None) == 2
+    assert kda_lib.kda_check_offsets(FAKE, 3, -5, FAKE2, None) == 2

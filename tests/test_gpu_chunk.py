@@ -317,3 +317,22 @@ def test_empty_batch():
     assert torch.equal(g["dh0"], dht)
     assert g["dq"].shape == (B, 0, H, D) and g["dg"].shape == (B, 0, H, D)
     assert not g["dA_log"].any() and not g["ddt_bias"].any()
+
+
+@pytest.mark.parametrize("offsets,T,want", [
+    ([0, 70, 134, 135, 135, 264], 300, 0),     # valid, an empty slot, tail below capacity
+    ([0, 0, 0], 0, 0),                         # all empty, zero capacity
+    ([0, 70, 60, 200], 300, 1),                # a decreasing offset
+    ([-4, 10, 20], 300, 2),                    # negative first offset
+    ([0, 70, 301], 300, 4),                    # past the capacity
+    ([5, 3, 400], 300, 1 | 4),                 # several at once
+    (list(range(0, 3000, 3)), 2997, 0),        # many slots (several rounds of the check's loop)
+    (list(range(0, 3000, 3))[:700] + [5] + list(range(2100, 2997, 3)), 2997, 1),
+])
+def test_check_offsets(offsets, T, want):
+    """The device-side check of the packed-offset contract, one flag bit per violation."""
+    need_gpu()
+    from gated_delta_rule_gate_amd import check_offsets
+
+    cu = torch.tensor(offsets, dtype=torch.int32, device="cuda")
+    assert check_offsets(cu, T) == want
