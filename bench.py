@@ -226,6 +226,75 @@ def bench_varlen(steps, warmup, schedule="auto"):
                 roofline_frac=round(nbytes / (t["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
 
 
+def alg_bytes_general(B, T, H, Hk, K, V, n_chunks=0, dtype_bytes=2):
+    """Bytes moved once: q, k (Hk heads), v and o (H heads) in dtype; gate input fp32; beta fp32;
+    h0 and ht fp32; plus n_chunks chunk-start states fp32 when those are returned."""
+    tokens = B * T
+    return (tokens * (2 * Hk * K * dtype_bytes + 2 * H * V * dtype_bytes + H * K * 4 + H * 4)
+            + 2 * B * H * K * V * 4 + n_chunks * H * K * V * 4)
+
+
+def bench_variants(steps, warmup):
+    """The headline call (B4 T4096 H64, C=64, safe gate, h0 + ht, flushed caches) and its
+    variants: q_l2norm on raw q, beta as logits, the chunk-start states returned, grouped
+    value heads (16 q/k heads), K != V and a non-power-of-two width, chunk size 32, and the
+    plain call replayed from a HIP graph. Each variant's fraction is of its own algorithmic bytes."""
+    import kda_synth
+    from gated_delta_rule_gate_amd import chunk_kda, resolved_schedule
+
+    B, T, H, C = 4, 4096, 64, 64
+    flush_buf = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+    flush = lambda: flush_buf.zero_()
+    out = []
+
+    def run(name, K, V, Hk=H, chunk=C, **kw):
+        d = kda_synth.chunk_inputs(B, T, H, K, V, dtype=torch.bfloat16, seed=1002)
+        dev = {k: v.cuda() for k, v in d.items() if v is not None}
+        del d
+        if Hk != H:
+            dev["q"] = dev["q"][:, :, :Hk].contiguous()
+            dev["k"] = dev["k"][:, :, :Hk].contiguous()
+        o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device="cuda")
+        ht = torch.empty((B, H, K, V), dtype=torch.float32, device="cuda")
+        n_chunks = B * ((T + chunk - 1) // chunk) if kw.get("return_intermediate_states") else 0
+        hs = torch.empty((B, n_chunks // B, H, K, V), dtype=torch.float32, device="cuda") if n_chunks else None
+        extra = dict(intermediate_states=hs) if hs is not None else {}
+        kw2 = {k: v for k, v in kw.items() if k not in ("return_intermediate_states", "graph")}
+
+        def step():
+            chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], dev["h0"], chunk_size=chunk, gate_kind="safe",
+                      A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0, out=o, final_state=ht, **extra,
+                      **kw2)
+
+        fn = step
+        if kw.get("graph"):
+            step()  # the first call builds what the capture then reuses
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            fn = g.replay
+        t = event_time_ms(fn, steps, warmup, flush=flush)
+        nbytes = alg_bytes_general(B, T, H, Hk, K, V, n_chunks)
+        out.append({"variant": name, "ms": round(t["mean"], 4),
+                    "Mtokens_per_s": round(B * T / (t["mean"] * 1e-3) / 1e6, 3),
+                    "alg_bytes": nbytes, "roofline_frac": round(nbytes / (t["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "schedule": resolved_schedule(dev["q"], dev["v"], H, B, chunk_size=chunk)})
+        del dev, o, ht, hs
+        torch.cuda.empty_cache()
+
+    run("plain", 128, 128)
+    run("q_l2norm (raw q)", 128, 128, q_l2norm=True)
+    run("beta as logits", 128, 128, beta_logits=True)
+    run("chunk-start states returned", 128, 128, return_intermediate_states=True)
+    run("GVA: 16 q/k heads for 64 value heads", 128, 128, Hk=16)
+    run("K=128, V=64", 128, 64)
+    run("K=V=96 (tile 128)", 96, 96)
+    run("chunk size 32", 128, 128, chunk=32)
+    run("HIP graph replay", 128, 128, graph=True)
+    return out
+
+
 def copy_bandwidth():
     """Device copy of 1 GiB (read + write), for context beside the roofline."""
     src = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")
@@ -287,6 +356,8 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--sweep", action="store_true", help="also time a sweep of six shapes (and, where AUTO chose fused or split, the other one)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward figure")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the headline call's variants (q_l2norm, beta logits, states, GVA, widths, C=32, graph)")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed-batch and copy figures")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 64-token recurrent prefill figure")
     args = ap.parse_args()
@@ -372,9 +443,12 @@ def main():
         line["copy_GBps"] = copy_bandwidth()
     if not args.no_bwd and args.schedule != "fused":
         line["backward"] = bench_bwd(B, T, H, D, steps=max(3, args.steps // 4), warmup=1, C=C)
-    if args.sweep:
+    if args.variants or args.sweep:
         del dev, o, ht, flush_buf
         torch.cuda.empty_cache()
+    if args.variants:
+        line["variants"] = bench_variants(max(5, args.steps // 2), 2)
+    if args.sweep:
         line["shape_sweep"] = []
         for shp in SWEEP_SHAPES:
             r = bench_shape(*shp, steps=max(5, args.steps // 2), warmup=2)
