@@ -120,7 +120,7 @@ typedef struct {
  * deferred to one 1/||q|| scale of that row of o. The eps floor is 1e-6, the
  * default of the l2norm it replaces. The grams then run in the raw-q basis,
  * about sqrt(K) larger, which the bounded safe gate tolerates. Forward only;
- * kda_chunk_fwd (both schedules) and kda_recurrent_fwd honour it.
+ * kda_chunk_fwd (every schedule) and kda_recurrent_fwd honour it.
  */
 
 /* Human-readable name of a status code. */
@@ -218,8 +218,10 @@ kda_status kda_gate_cumsum(const kda_args *args, const float *g_in, const int32_
  * section "Correctness checklist": D != Dv); chunk_size in {32, 64}; dtype bf16
  * or fp32. The kernels run at the tile width 64, 128 or 256 that covers
  * max(K, V), with channels past K and value columns past V masked to zero, so
- * other widths cost what the next tile width costs. The fused schedule runs
- * bf16 with max(K, V) <= 128; other cases run the staged one.
+ * other widths cost what the next tile width costs. The fused and split
+ * schedules run bf16 with max(K, V) <= 128 (KDA_ERR_UNSUPPORTED when named for
+ * other cases); other cases run the staged one. KDA_SCHED_AUTO picks
+ * (kda_chunk_schedule reports which).
  */
 kda_status kda_chunk_fwd(const kda_args *args, const void *q, const void *k, const void *v, const float *g,
                          const float *beta, const float *h0, const int32_t *cu_seqlens, void *o, float *ht,
@@ -249,7 +251,7 @@ size_t kda_chunk_states_count(const kda_args *args, int packed);
  *              != NULL) * H * K * V floats, 16-byte aligned (KDA_ERR_ALIGN),
  *              not NULL unless that count is 0 (KDA_ERR_NULL); must not overlap
  *              any other buffer.
- * Both schedules honour it; the workspace is the one kda_chunk_fwd takes.
+ * Every schedule honours it; the workspace is the one kda_chunk_fwd takes.
  * The extra traffic is K * V * 4 bytes per chunk and head, written once.
  */
 kda_status kda_chunk_fwd_states(const kda_args *args, const void *q, const void *k, const void *v, const float *g,
