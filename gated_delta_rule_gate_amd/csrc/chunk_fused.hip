@@ -118,27 +118,16 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     regs.load_gate(p, sr.t0, min(C, sr.len), h);
     if (loader) regs.load_qkv(p, sr.t0, min(C, sr.len), h);
   }
-  // v_new of the previous chunk: its state update h <- Diag(2^b_L) h + k~^T v_new
-  // runs right after the next chunk's inputs are stored, beside their gate
-  // activation; before the first chunk it is the identity (v_new = 0, k~ = 0,
-  // decay 1)
+  // v_new of the chunk as bf16 operand fragments of its state update
+  // h <- Diag(2^b_L) h + k~^T v_new
   bf16x8_t vprev[NC / 2][NVW];
-#pragma unroll
-  for (int s2 = 0; s2 < NC / 2; ++s2)
-#pragma unroll
-    for (int v = 0; v < NVW; ++v) vprev[s2][v] = bf16x8_t{};
-  for (int i = tid_opaque(); i < D; i += NT) sDecay2[D + i] = 1.f;
-  for (int i = tid_opaque(); i < C * LDT / 8; i += NT) reinterpret_cast<u32x4_t *>(sKt)[i] = u32x4_t{0u, 0u, 0u, 0u};
-  __syncthreads();  // sDt, the identity update's operands visible
+  __syncthreads();  // sDt visible
 
   for (int c = 0; c < nch; ++c) {
     const int64_t t0 = sr.t0 + (int64_t)c * C;
     const int L = min(C, sr.len - c * C);
     const int64_t off = t0 * ld + h * Vr;
     float *sDecay = sDecay2 + (c & 1) * D;
-    // chunk c - 1's state update first: it needs no new input, so the loads of
-    // this chunk's inputs land meanwhile
-    state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((c + 1) & 1) * D);
     regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound, p.q_l2norm != 0, sQn,
                             p.beta_logits != 0);
     if (hcs && owner) store_strip<float, DT, NVW>(hcs + (int64_t)c * p.H * Kr * Vr, Vr, col0, Kr, hs, Vr);
@@ -213,10 +202,13 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
       }
       // o from registers: four adjacent value columns per lane and row
       store_oT<C, NVW>(reinterpret_cast<Tin *>(p.o) + off, ld, col0, L, o, Vr);
+      // this chunk's state update, before the barrier: it reads only k~ and 2^b_L,
+      // which the next chunk's store leaves alone, so each wave runs it while the
+      // slower waves finish their products
+      state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay);
     }
     __syncthreads();
   }
-  if (nch > 0) state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((nch - 1) & 1) * D);
   if (owner && p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, Vr, col0, Kr, hs, Vr);
 }
 
