@@ -336,8 +336,10 @@ __global__ __launch_bounds__(kBT) void bwd_wy_kernel(ChunkParams p, BwdParams bw
   ChunkLoc lc;
   if (!locate_chunk(p, blockIdx.x, lc)) return;
   const int h = blockIdx.y;
-  constexpr int LA = C + 4, LX = D + 4, NC = C / 16, DT = D / 16;
-  constexpr int NTW = NC * DT / 4, NCW = NC * NC / 4, TPR = kBT / C;
+  // the [C][D] operands pass through two slabs of SW columns, so two workgroups fit a compute unit
+  constexpr int SW = 32, LA = C + 4, LS = SW + 4, NC = C / 16, ST = SW / 16;
+  constexpr int NCW = NC * NC / 4, NSW = NC * ST / 4, TPR = kBT / C;
+  static_assert(NCW >= 1 && NSW >= 1 && D % SW == 0, "tiles per wave");
   const int wid = threadIdx.x >> 6;
   const int Kr = p.Kr, Vr = p.Vr, L = lc.L;
   const int64_t t0 = lc.t0;
@@ -346,11 +348,11 @@ __global__ __launch_bounds__(kBT) void bwd_wy_kernel(ChunkParams p, BwdParams bw
   float *sT = reinterpret_cast<float *>(smem);  // [C][LA] T
   float *sDT = sT + C * LA;                     // [C][LA] dT
   float *sX = sDT + C * LA;                     // [C][LA] dT T^T
-  float *sDw = sX + C * LA;                     // [C][LX] dw, later dX_u
-  float *sKG = sDw + C * LX;                    // [C][LX] k 2^b
-  float *sDvn = sKG + C * LX;                   // [C][LX] dv_new
-  float *sBeta = sDvn + C * LX;                 // [C]
+  float *sA = sX + C * LA;                      // [C][LS] slab of dw, later of dX_u
+  float *sB = sA + C * LS;                      // [C][LS] slab of k 2^b, later of dv_new
+  float *sBeta = sB + C * LS;                   // [C]
   const Tin *gk = reinterpret_cast<const Tin *>(p.k), *gv = reinterpret_cast<const Tin *>(p.v);
+  const float *gb = p.b + t0 * ld + h * D;
 
   tile_f32<float, C, C>(sT, LA, p.Tm + t0 * ldc + h * C, ldc, L, C, [&](int r, int c, float *v) {
 #pragma unroll
@@ -360,29 +362,38 @@ __global__ __launch_bounds__(kBT) void bwd_wy_kernel(ChunkParams p, BwdParams bw
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (c + e < L) ? v[e] : 0.f;
   });
-  tile_f32<float, C, D>(sDw, LX, bw.dw + t0 * ld + h * D, ld, L, D);
-  tile_f32<float, C, D>(sDvn, LX, bw.dvn + t0 * ld + h * D, ld, L, D);
-  const float *gb = p.b + t0 * ld + h * D;
-  tile_f32<Tin, C, D>(sKG, LX, gk + t0 * ldk + h * Kr, ldk, L, Kr, [&](int r, int c, float *v) {
-    if (r >= L) return;
-#pragma unroll
-    for (int e = 0; e < 16 / (int)sizeof(Tin); e += 4) {
-      const f32x4_t br = ld4(gb + (int64_t)r * ld + c + e);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[e + u] *= fast_exp2(br[u]);
-    }
-  });
   for (int r = threadIdx.x; r < C; r += kBT) sBeta[r] = r < L ? beta_at(p, t0 + r, h) : 0.f;
-  __syncthreads();
-  // dT = dT_u + beta_s (dw (k 2^b)^T)_rs
+  // dT = dT_u + beta_s (dw (k 2^b)^T)_rs, the contraction over channels slab by slab
+  f32x4_t acc[NCW];
+#pragma unroll
+  for (int t = 0; t < NCW; ++t) acc[t] = zero4();
+#pragma unroll 1
+  for (int j0 = 0; j0 < D; j0 += SW) {
+    __syncthreads();  // the previous slab is consumed
+    tile_f32<float, C, SW>(sA, LS, bw.dw + t0 * ld + h * D + j0, ld, L, SW);
+    tile_f32<Tin, C, SW>(sB, LS, gk + t0 * ldk + h * Kr + j0, ldk, L, Kr - j0, [&](int r, int c, float *v) {
+      if (r >= L) return;
+#pragma unroll
+      for (int e = 0; e < 16 / (int)sizeof(Tin); e += 4) {
+        const f32x4_t br = ld4(gb + (int64_t)r * ld + j0 + c + e);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[e + u] *= fast_exp2(br[u]);
+      }
+    });
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NCW; ++t) {
+      const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
+      acc[t] = mm16<SW>(acc[t], sA, LS, 1, sB, 1, LS, 16 * rt, 16 * st);
+    }
+  }
 #pragma unroll
   for (int t = 0; t < NCW; ++t) {
     const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
-    const f32x4_t acc = mm16<D>(zero4(), sDw, LX, 1, sKG, 1, LX, 16 * rt, 16 * st);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * rt + tile_row(e), s = 16 * st + tile_col();
-      sDT[r * LA + s] += sBeta[s] * acc[e];
+      sDT[r * LA + s] += sBeta[s] * acc[t][e];
     }
   }
   __syncthreads();
@@ -390,58 +401,64 @@ __global__ __launch_bounds__(kBT) void bwd_wy_kernel(ChunkParams p, BwdParams bw
 #pragma unroll
   for (int t = 0; t < NCW; ++t) {
     const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
-    const f32x4_t acc = mm16<C>(zero4(), sDT, LA, 1, sT, 1, LA, 16 * rt, 16 * st);
+    const f32x4_t a = mm16<C>(zero4(), sDT, LA, 1, sT, 1, LA, 16 * rt, 16 * st);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sX[(16 * rt + tile_row(e)) * LA + 16 * st + tile_col()] = acc[e];
+    for (int e = 0; e < 4; ++e) sX[(16 * rt + tile_row(e)) * LA + 16 * st + tile_col()] = a[e];
   }
   __syncthreads();
-  // dA_kk = -strict_lower(T^T X); dX_w = T^T dw
+  // dA_kk = -strict_lower(T^T X)
 #pragma unroll
   for (int t = 0; t < NCW; ++t) {
     const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
-    const f32x4_t acc = mm16<C>(zero4(), sT, 1, LA, sX, LA, 1, 16 * rt, 16 * st);
+    const f32x4_t a = mm16<C>(zero4(), sT, 1, LA, sX, LA, 1, 16 * rt, 16 * st);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * rt + tile_row(e), s = 16 * st + tile_col();
-      if (r < L) bw.dAkk[(t0 + r) * ldc + h * C + s] = (s < r) ? -acc[e] : 0.f;
+      if (r < L) bw.dAkk[(t0 + r) * ldc + h * C + s] = (s < r) ? -a[e] : 0.f;
     }
   }
+  // dX_w = T^T dw and dX_u = T^T dv_new slab by slab; dv = beta dX_u; the beta
+  // gradient through u, sum over j of dX_u v, accumulates across the slabs
+  const int rr = threadIdx.x / TPR, qq = threadIdx.x % TPR;
+  float dbp = 0.f;
+#pragma unroll 1
+  for (int j0 = 0; j0 < D; j0 += SW) {
+    __syncthreads();  // the previous slab (or the last dT slab) is consumed
+    tile_f32<float, C, SW>(sA, LS, bw.dw + t0 * ld + h * D + j0, ld, L, SW);
+    tile_f32<float, C, SW>(sB, LS, bw.dvn + t0 * ld + h * D + j0, ld, L, SW);
+    __syncthreads();
+    f32x4_t xu[NSW];
 #pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    const int tile = wid * NTW + t, rt = tile / DT, ct = tile % DT;
-    const f32x4_t acc = mm16<C>(zero4(), sT, 1, LA, sDw, LX, 1, 16 * rt, 16 * ct);
+    for (int t = 0; t < NSW; ++t) {
+      const int tile = wid * NSW + t, rt = tile / ST, ct = tile % ST;
+      const f32x4_t a = mm16<C>(zero4(), sT, 1, LA, sA, LS, 1, 16 * rt, 16 * ct);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + tile_row(e), i = 16 * ct + tile_col();
-      if (r < L) bw.dXw[(t0 + r) * ld + h * D + i] = acc[e];
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + tile_row(e), i = j0 + 16 * ct + tile_col();
+        if (r < L) bw.dXw[(t0 + r) * ld + h * D + i] = a[e];
+      }
+      xu[t] = mm16<C>(zero4(), sT, 1, LA, sB, LS, 1, 16 * rt, 16 * ct);
     }
-  }
-  __syncthreads();
-  // dX_u = T^T dv_new, into sDw
+    __syncthreads();  // every wave is done reading this slab of dw
 #pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    const int tile = wid * NTW + t, rt = tile / DT, ct = tile % DT;
-    const f32x4_t acc = mm16<C>(zero4(), sT, 1, LA, sDvn, LX, 1, 16 * rt, 16 * ct);
+    for (int t = 0; t < NSW; ++t) {
+      const int tile = wid * NSW + t, rt = tile / ST, ct = tile % ST;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sDw[(16 * rt + tile_row(e)) * LX + 16 * ct + tile_col()] = acc[e];
-  }
-  __syncthreads();
-  // dv = beta dX_u; the beta gradient through u: sum over j of dX_u v
-  {
-    const int r = threadIdx.x / TPR, q = threadIdx.x % TPR;
-    float acc = 0.f;
-    if (r < L) {
-      Tin *gdv = reinterpret_cast<Tin *>(bw.dv) + (t0 + r) * ldv + h * Vr;
-      for (int j = q; j < Vr; j += TPR) {
-        const float x = sDw[r * LX + j];
-        acc += x * to_f32(gv[(t0 + r) * ldv + h * Vr + j]);
-        gdv[j] = from_f32<Tin>(sBeta[r] * x);
+      for (int e = 0; e < 4; ++e) sA[(16 * rt + tile_row(e)) * LS + 16 * ct + tile_col()] = xu[t][e];
+    }
+    __syncthreads();
+    if (rr < L) {
+      Tin *gdv = reinterpret_cast<Tin *>(bw.dv) + (t0 + rr) * ldv + h * Vr;
+      for (int j = qq; j < SW && j0 + j < Vr; j += TPR) {
+        const float x = sA[rr * LS + j];
+        dbp += x * to_f32(gv[(t0 + rr) * ldv + h * Vr + j0 + j]);
+        gdv[j0 + j] = from_f32<Tin>(sBeta[rr] * x);
       }
     }
-#pragma unroll
-    for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m);
-    if (q == 0 && r < L) bw.dbp[(t0 + r) * p.H + h] = acc;
   }
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) dbp += __shfl_xor(dbp, m);
+  if (qq == 0 && rr < L) bw.dbp[(t0 + rr) * p.H + h] = dbp;
 }
 
 // ---- pairwise decays: dq, dk, the cumsum gradient, dg and the gate activation ----
@@ -768,7 +785,7 @@ hipError_t launch_bwd_t(const ChunkParams &p, const BwdParams &b, hipStream_t st
     if ((e = launch_k(bwd_contract_kernel<Tin, C, D>, grid, smem, st, p, b)) != hipSuccess) return e;
   }
   {
-    const size_t smem = sizeof(float) * ((size_t)3 * C * LA + 3 * C * LX + C);
+    const size_t smem = sizeof(float) * ((size_t)3 * C * LA + 2 * C * (32 + 4) + C);
     if ((e = launch_k(bwd_wy_kernel<Tin, C, D>, grid, smem, st, p, b)) != hipSuccess) return e;
   }
   {
