@@ -482,9 +482,11 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
   const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.H * Kr;
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63, n16 = lane & 15, grp = lane >> 4;
   extern __shared__ __align__(16) char smem[];
-  float *sDAkk = reinterpret_cast<float *>(smem);  // [C][LA] strictly lower
-  float *sDAqk = sDAkk + C * LA;                   // [C][LA] lower
-  float *sK = sDAqk + C * LA;                      // [C][LS] slab of SI channels
+  // [C][LA], both gradients of the grams in one tile: dA_kk (strictly lower) in
+  // place, dA_qk (lower) transposed, so dA_kk[r][s] = sDAg[r][s] for s < r and
+  // dA_qk[r][s] = sDAg[s][r] for s <= r
+  float *sDAg = reinterpret_cast<float *>(smem);
+  float *sK = sDAg + C * LA;                        // [C][LS] slab of SI channels
   float *sQ = sK + C * LS;
   float *sB = sQ + C * LS;   // b; rows >= L repeat row L - 1, so every exponent below stays <= 0
   float *sCT = sB + C * LS;  // [SI] per channel: sum over rows of k 2^(b_L - b) dk~ (b_L's share)
@@ -497,14 +499,15 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
   const float scale = p.scale;
   const float expA = (GK == kGateSafe || GK == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
 
-  tile_f32<float, C, C>(sDAkk, LA, bw.dAkk + t0 * ldc + h * C, ldc, L, C, [](int r, int c, float *v) {
+  tile_f32<float, C, C>(sDAg, LA, bw.dAkk + t0 * ldc + h * C, ldc, L, C, [](int r, int c, float *v) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (c + e < r) ? v[e] : 0.f;
   });
-  tile_f32<float, C, C>(sDAqk, LA, bw.dAqk + t0 * ldc + h * C, ldc, L, C, [](int r, int c, float *v) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (c + e <= r) ? v[e] : 0.f;
-  });
+  __syncthreads();  // the upper triangle and the diagonal are zero before dA_qk goes in
+  for (int idx = threadIdx.x; idx < C * C; idx += kBT) {
+    const int r = idx / C, c = idx % C;  // coalesced rows of dA_qk, written transposed
+    if (c <= r && r < L) sDAg[c * LA + r] = bw.dAqk[(t0 + r) * ldc + h * C + c];
+  }
   for (int r = threadIdx.x; r < C; r += kBT) sBeta[r] = r < L ? beta_at(p, t0 + r, h) : 0.f;
   for (int idx = threadIdx.x; idx < NW * C; idx += kBT) sDbw[idx] = 0.f;
   float dA_total = 0.f;
@@ -546,8 +549,8 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
         for (int st = 0; st < 4; ++st) {
           const int s = 16 * J + 4 * st + grp;
           const float kh = sK[s * LS + cl] * fast_exp2(aI - sB[s * LS + cl]);
-          aq = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAkk[(16 * I + n16) * LA + s], kh, aq, 0, 0, 0);
-          ar = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAqk[(16 * I + n16) * LA + s], kh, ar, 0, 0, 0);
+          aq = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAg[(16 * I + n16) * LA + s], kh, aq, 0, 0, 0);
+          ar = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAg[s * LA + 16 * I + n16], kh, ar, 0, 0, 0);
         }
       }
       // U of rows (as columns) 16I + 4grp + e: row blocks I2 > I
@@ -561,8 +564,8 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
           const int rr = 16 * I2 + 4 * st + grp;
           const float f = fast_exp2(sB[rr * LS + cl] - a2);
           const float xh = sBeta[rr] * sK[rr * LS + cl] * f, qh = scale * sQ[rr * LS + cl] * f;
-          au = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAkk[rr * LA + 16 * I + n16], xh, au, 0, 0, 0);
-          au = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAqk[rr * LA + 16 * I + n16], qh, au, 0, 0, 0);
+          au = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAg[rr * LA + 16 * I + n16], xh, au, 0, 0, 0);
+          au = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAg[(16 * I + n16) * LA + rr], qh, au, 0, 0, 0);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) u[e] += au[e] * fast_exp2(a2 - sB[(16 * I + 4 * grp + e) * LS + cl]);
@@ -586,13 +589,14 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
           const int s = 16 * I + 4 * st + grp;  // contraction index
           const float bs = sB[s * LS + cl];
           const float km = sK[s * LS + cl] * fast_exp2(mI - bs);
-          dq4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAkk[(16 * I + n16) * LA + s], km, dq4, 0, 0, 0);
-          dr4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAqk[(16 * I + n16) * LA + s], km, dr4, 0, 0, 0);
+          const int rl = 16 * I + n16;  // this lane's row (the operand's m index)
+          const float akk_rs = s < rl ? sDAg[rl * LA + s] : 0.f, aqk_rs = s <= rl ? sDAg[s * LA + rl] : 0.f;
+          const float akk_sr = rl < s ? sDAg[s * LA + rl] : 0.f, aqk_sr = rl <= s ? sDAg[rl * LA + s] : 0.f;
+          dq4 = __builtin_amdgcn_mfma_f32_16x16x4f32(akk_rs, km, dq4, 0, 0, 0);
+          dr4 = __builtin_amdgcn_mfma_f32_16x16x4f32(aqk_rs, km, dr4, 0, 0, 0);
           const float fm = fast_exp2(bs - mI);
-          du4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAkk[s * LA + 16 * I + n16], sBeta[s] * sK[s * LS + cl] * fm, du4,
-                                                     0, 0, 0);
-          du4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sDAqk[s * LA + 16 * I + n16], scale * sQ[s * LS + cl] * fm, du4,
-                                                     0, 0, 0);
+          du4 = __builtin_amdgcn_mfma_f32_16x16x4f32(akk_sr, sBeta[s] * sK[s * LS + cl] * fm, du4, 0, 0, 0);
+          du4 = __builtin_amdgcn_mfma_f32_16x16x4f32(aqk_sr, scale * sQ[s * LS + cl] * fm, du4, 0, 0, 0);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -617,10 +621,11 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
             const int r = 16 * I + 4 * grp + e;
             if (s <= r) {
               const float f = fast_exp2(br[e] - bs) * ks;
-              qd[e] += sDAkk[r * LA + s] * f;
-              rd[e] += sDAqk[r * LA + s] * f;
+              qd[e] += (s < r ? sDAg[r * LA + s] : 0.f) * f;
+              rd[e] += sDAg[s * LA + r] * f;
             }
-            if (s >= r) ud[e] += (sDAkk[s * LA + r] * xs + sDAqk[s * LA + r] * qs) * fast_exp2(bs - br[e]);
+            if (s >= r)
+              ud[e] += ((r < s ? sDAg[s * LA + r] : 0.f) * xs + sDAg[r * LA + s] * qs) * fast_exp2(bs - br[e]);
           }
         }
       }
@@ -790,7 +795,7 @@ hipError_t launch_bwd_t(const ChunkParams &p, const BwdParams &b, hipStream_t st
   }
   {
     constexpr int LS = 64 + 4, NW = kBT / 64;
-    const size_t smem = sizeof(float) * ((size_t)2 * C * LA + 3 * C * LS + 64 + C + NW * C + 2 * 64);
+    const size_t smem = sizeof(float) * ((size_t)C * LA + 3 * C * LS + 64 + C + NW * C + 2 * 64);
     switch (p.gate_kind) {
       case kGateSafe: e = launch_k(bwd_grams_kernel<Tin, C, D, kGateSafe>, grid, smem, st, p, b); break;
       case kGateSoftplus: e = launch_k(bwd_grams_kernel<Tin, C, D, kGateSoftplus>, grid, smem, st, p, b); break;
