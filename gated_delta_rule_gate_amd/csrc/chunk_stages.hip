@@ -171,6 +171,49 @@ __global__ __launch_bounds__(256) void stage_wy_kernel(ChunkParams p) {
 }
 
 // ---- (5) inter-chunk state scan, per (sequence, head, 64-column value block) ----
+// k~^T = (k 2^(b_L - b))^T of one chunk into LDS [D][LDKT] (Tin), straight from
+// the global rows of k and b (b_L read from the chunk's last row): four channels
+// per item, and every load of a half of the items issued before its first LDS
+// write, so the loads' latencies overlap.
+template <typename Tin, int NT, int C, int D>
+__device__ __forceinline__ void ktilde_t_from_global(Tin *sKT, const Tin *gK, int64_t ldk, const float *gB, int64_t ld,
+                                                     int L, int kr) {
+  using TL = Tile<Tin, C, D>;
+  constexpr int VPR = D / 4, NI = C * VPR, IT = (NI + NT - 1) / NT, HALF = (IT + 1) / 2;
+  const float *gBL = gB + (int64_t)(L - 1) * ld;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f32x4_t kv[HALF], ev[HALF];
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+      const int idx = (hf * HALF + j) * NT + tid_opaque();
+      const int r = idx / VPR, i = (idx % VPR) * 4;
+      const bool ok = hf * HALF + j < IT && idx < NI && r < L && i < kr;  // kr % 8 == 0: all four or none
+      if (ok) {
+        const f32x4_t b = *reinterpret_cast<const f32x4_t *>(gB + (int64_t)r * ld + i);
+        const f32x4_t bl = *reinterpret_cast<const f32x4_t *>(gBL + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv[j][e] = to_f32(gK[(int64_t)r * ldk + i + e]);
+          ev[j][e] = bl[e] - b[e];
+        }
+      } else {
+        kv[j] = zero4();
+        ev[j] = zero4();
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+      const int idx = (hf * HALF + j) * NT + tid_opaque();
+      if (hf * HALF + j < IT && idx < NI) {
+        const int r = idx / VPR, i = (idx % VPR) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sKT[(i + e) * TL::LDKT + r] = from_f32<Tin>(kv[j][e] * fast_exp2(ev[j][e]));
+      }
+    }
+  }
+}
+
 template <typename Tin, int C, int D>
 __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
   using TL = Tile<Tin, C, D>;
@@ -207,14 +250,9 @@ __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
     const int64_t off = t0 * ld + h * D;
     store_strip<float, DT, NVW>(p.hc + ((int64_t)(cbase + c) * p.H + h) * Kr * Vr, Vr, col0, Kr, hs, Vr);
     load_rows_cvt<Tin, kNT, C, D>(sW, LDT, p.w + off, ld, L);
-    for (int i = threadIdx.x; i < D; i += kNT) {
-      const float bl = p.b[off + (int64_t)(L - 1) * ld + i];  // cumsum at the chunk's last row
-      sBL[i] = bl;
-      sDecay[i] = fast_exp2(bl);
-    }
-    __syncthreads();
-    make_ktilde_t_global<Tin, kNT, C, D>(sKT, reinterpret_cast<const Tin *>(p.k) + t0 * ldk + hk * Kr, ldk,
-                                         p.b + off, ld, sBL, L, Kr);
+    for (int i = threadIdx.x; i < D; i += kNT) sDecay[i] = fast_exp2(p.b[off + (int64_t)(L - 1) * ld + i]);
+    ktilde_t_from_global<Tin, kNT, C, D>(sKT, reinterpret_cast<const Tin *>(p.k) + t0 * ldk + hk * Kr, ldk, p.b + off,
+                                         ld, L, Kr);
     f32x4_t uv[NC][NVW];
     load_strip<NC, NVW>(uv, p.u + off, ld, col0, L);
     __syncthreads();
