@@ -140,28 +140,58 @@ __global__ __launch_bounds__(256) void stage_wy_kernel(ChunkParams p) {
   constexpr int NC = TL::NC, DT = TL::DT, LDT = TL::LDT, LDB = TL::LDB, NW = kNT / 64;
   extern __shared__ __align__(16) char smem[];
   float *sT = reinterpret_cast<float *>(smem);
-  float *sB = sT + C * TL::LDA;
-  float *sBL = sB + C * LDB;
-  float *sBeta = sBL + D;
-  Tin *sK = reinterpret_cast<Tin *>(sBeta + C);
+  float *sBeta = sT + C * TL::LDA;
+  Tin *sK = reinterpret_cast<Tin *>(sBeta + C);  // k, then beta k 2^b (rounded to Tin once, as an operand)
   Tin *sV = sK + C * LDT;
   const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * p.Kr, ldv = (int64_t)p.H * p.Vr;
   const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * p.Kr;
-  load_rows<float, kNT, C, C>(sT, TL::LDA, p.Tm + lc.t0 * ldc + h * C, ldc, lc.L);
-  load_rows<Tin, kNT, C, D>(sK, LDT, reinterpret_cast<const Tin *>(p.k) + offk, ldk, lc.L, p.Kr);
-  load_rows<Tin, kNT, C, D>(sV, LDT, reinterpret_cast<const Tin *>(p.v) + lc.t0 * ldv + h * p.Vr, ldv, lc.L, p.Vr);
-  load_rows<float, kNT, C, D>(sB, LDB, p.b + off, ld, lc.L);
-  load_beta<C>(sBeta, p, lc.t0, h, lc.L);
+  const int L = lc.L;
+  // b of the chunk's rows, four channels per item, loaded beside the tiles (rows past L are never read)
+  // (all of them before the tiles' barrier up to 8 vectors a thread; wider tiles take them in groups of 8 after it)
+  constexpr int VPR = D / 4, NI = C * VPR, IB = (NI + kNT - 1) / kNT, GB = IB <= 8 ? IB : 8;
+  auto load_b = [&](f32x4_t (&bv)[GB], int j0) {
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      const int idx = (j0 + j) * kNT + threadIdx.x, r = idx / VPR, i = (idx % VPR) * 4;
+      bv[j] = (idx < NI && r < L) ? *reinterpret_cast<const f32x4_t *>(p.b + off + (int64_t)r * ld + i) : zero4();
+    }
+  };
+  auto scale_k = [&](const f32x4_t (&bv)[GB], int j0) {
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      const int idx = (j0 + j) * kNT + threadIdx.x, r = idx / VPR, i = (idx % VPR) * 4;
+      if (idx < NI && r < L) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Tin &x = sK[r * LDT + i + e];
+          x = from_f32<Tin>(sBeta[r] * to_f32(x) * fast_exp2(bv[j][e]));
+        }
+      }
+    }
+  };
+  f32x4_t bv[GB];
+  if constexpr (IB <= 8) load_b(bv, 0);
+  load_rows<float, kNT, C, C>(sT, TL::LDA, p.Tm + lc.t0 * ldc + h * C, ldc, L);
+  load_rows<Tin, kNT, C, D>(sK, LDT, reinterpret_cast<const Tin *>(p.k) + offk, ldk, L, p.Kr);
+  load_rows<Tin, kNT, C, D>(sV, LDT, reinterpret_cast<const Tin *>(p.v) + lc.t0 * ldv + h * p.Vr, ldv, L, p.Vr);
+  load_beta<C>(sBeta, p, lc.t0, h, L);
   __syncthreads();
-  pad_cumsum<kNT, C, D>(sB, LDB, sBL, lc.L);
+  // beta k 2^b in place of k; rows past L stay zero
+  if constexpr (IB <= 8) {
+    scale_k(bv, 0);
+  } else {
+#pragma unroll 1
+    for (int j0 = 0; j0 < IB; j0 += GB) {
+      load_b(bv, j0);
+      scale_k(bv, j0);
+    }
+  }
   __syncthreads();
   const int wid = threadIdx.x >> 6;
   for (int ct = wid; ct < 2 * DT; ct += NW) {
     f32x4_t acc[NC][1];
     if (ct < DT) {
-      tri_mm<Tin, C, 1>(sT, ct, acc, 0, [&](int c, int col) {
-        return sBeta[c] * to_f32(sK[c * LDT + col]) * fast_exp2(sB[c * LDB + col]);
-      });
+      tri_mm<Tin, C, 1>(sT, ct, acc, 0, [&](int c, int col) { return to_f32(sK[c * LDT + col]); });
       store_strip<float, NC, 1>(p.w + off, ld, 16 * ct, lc.L, acc);
     } else {
       tri_mm<Tin, C, 1>(sT, ct - DT, acc, 0, [&](int c, int col) { return sBeta[c] * to_f32(sV[c * LDT + col]); });
@@ -417,7 +447,7 @@ hipError_t launch_stage_solve(const ChunkParams &p, hipStream_t st) {
 hipError_t launch_stage_wy(const ChunkParams &p, hipStream_t st) {
   return dispatch(p, [&]<typename Tin, int C, int D>() {
     using TL = Tile<Tin, C, D>;
-    const size_t smem = sizeof(float) * (C * TL::LDA + C * TL::LDB + D + C) + sizeof(Tin) * 2 * C * TL::LDT;
+    const size_t smem = sizeof(float) * (C * TL::LDA + C) + sizeof(Tin) * 2 * C * TL::LDT;
     return launch_dyn(stage_wy_kernel<Tin, C, D>, dim3(p.max_chunks, p.H), smem, st, p);
   });
 }
