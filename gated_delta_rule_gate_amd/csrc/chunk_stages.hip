@@ -310,18 +310,40 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
   const int wid = threadIdx.x >> 6;
   const int col0 = vb * BV + wid * 16;
   extern __shared__ __align__(16) char smem[];
-  Tin *sQ = reinterpret_cast<Tin *>(smem);
-  float *sB = reinterpret_cast<float *>(sQ + C * LDT);
-  float *sBL = sB + C * LDB;
-  float *sAqk = sBL + D;
+  Tin *sQ = reinterpret_cast<Tin *>(smem);   // q, then q~ = scale q 2^b
+  float *sAqk = reinterpret_cast<float *>(sQ + C * LDT);
   float *sQn = sAqk + C * TL::LDA;  // per row: 1/sqrt(|q|^2 + eps) with q_l2norm
   const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * p.Kr, ldv = (int64_t)p.H * p.Vr;
   const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * p.Kr;
-  load_rows<Tin, kNT, C, D>(sQ, LDT, reinterpret_cast<const Tin *>(p.q) + offk, ldk, lc.L, p.Kr);
-  load_rows<float, kNT, C, D>(sB, LDB, p.b + off, ld, lc.L);
-  load_rows<float, kNT, C, C>(sAqk, TL::LDA, p.Aqk + lc.t0 * ldc + h * C, ldc, lc.L);
+  const int L = lc.L;
+  // b of the chunk's rows, four channels per item (before the tiles' barrier up to 8
+  // vectors a thread; wider tiles take them in groups of 8 after it); rows past L stay zero
+  constexpr int VPR = D / 4, NI = C * VPR, IB = (NI + kNT - 1) / kNT, GB = IB <= 8 ? IB : 8;
+  auto load_b = [&](f32x4_t (&bv)[GB], int j0) {
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      const int idx = (j0 + j) * kNT + threadIdx.x, r = idx / VPR, i = (idx % VPR) * 4;
+      bv[j] = (idx < NI && r < L) ? *reinterpret_cast<const f32x4_t *>(p.b + off + (int64_t)r * ld + i) : zero4();
+    }
+  };
+  auto scale_q = [&](const f32x4_t (&bv)[GB], int j0) {
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      const int idx = (j0 + j) * kNT + threadIdx.x, r = idx / VPR, i = (idx % VPR) * 4;
+      if (idx < NI && r < L) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Tin &x = sQ[r * LDT + i + e];
+          x = from_f32<Tin>(p.scale * to_f32(x) * fast_exp2(bv[j][e]));
+        }
+      }
+    }
+  };
+  f32x4_t bv[GB];
+  if constexpr (IB <= 8) load_b(bv, 0);
+  load_rows<Tin, kNT, C, D>(sQ, LDT, reinterpret_cast<const Tin *>(p.q) + offk, ldk, L, p.Kr);
+  load_rows<float, kNT, C, C>(sAqk, TL::LDA, p.Aqk + lc.t0 * ldc + h * C, ldc, L);
   __syncthreads();
-  pad_cumsum<kNT, C, D>(sB, LDB, sBL, lc.L);
   if (p.q_l2norm && threadIdx.x < C) {  // raw q: o is linear in each q row
     float ss = 0.f;
     for (int c = 0; c < D; ++c) {
@@ -330,8 +352,16 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
     }
     sQn[threadIdx.x] = rsqrtf(ss + kQNormEps);
   }
-  __syncthreads();
-  make_qtilde<Tin, kNT, C, D>(sQ, sB, p.scale);
+  __syncthreads();  // the row norms read raw q
+  if constexpr (IB <= 8) {
+    scale_q(bv, 0);
+  } else {
+#pragma unroll 1
+    for (int j0 = 0; j0 < IB; j0 += GB) {
+      load_b(bv, j0);
+      scale_q(bv, j0);
+    }
+  }
   f32x4_t hs[DT][NVW], vn[NC][NVW], o[NC][NVW];
   load_strip<DT, NVW>(hs, p.hc + ((int64_t)lc.gci * p.H + h) * p.Kr * p.Vr, p.Vr, col0, p.Kr, p.Vr);
   load_strip<NC, NVW>(vn, p.vnew + off, ld, col0, lc.L);
@@ -463,7 +493,7 @@ hipError_t launch_stage_scan(const ChunkParams &p, hipStream_t st) {
 hipError_t launch_stage_output(const ChunkParams &p, hipStream_t st) {
   return dispatch(p, [&]<typename Tin, int C, int D>() {
     using TL = Tile<Tin, C, D>;
-    const size_t smem = sizeof(Tin) * C * TL::LDT + sizeof(float) * (C * TL::LDB + D + C * TL::LDA + C);
+    const size_t smem = sizeof(Tin) * C * TL::LDT + sizeof(float) * (C * TL::LDA + C);
     return launch_dyn(stage_output_kernel<Tin, C, D>, dim3(p.max_chunks, p.H, (p.Vr + 63) / 64), smem, st, p);
   });
 }
