@@ -304,13 +304,46 @@ def copy_bandwidth():
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family / model / stepping numbers."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                key, val = (x.strip() for x in line.split(":", 1))
+                if key in ("model name", "cpu family", "model", "stepping") and key not in info:
+                    info[key] = val
+            if not line.strip() and info:
+                break
     except OSError:
         pass
-    return "unknown"
+    if not info:
+        return "unknown"
+    return "%s (family %s, model %s, stepping %s)" % (info.get("model name", "?"), info.get("cpu family", "?"),
+                                                      info.get("model", "?"), info.get("stepping", "?"))
+
+
+def affinity_ranges(cpus):
+    """A CPU id set as a compact range list, e.g. '0-15,32-47'."""
+    cpus = sorted(cpus)
+    out, i = [], 0
+    while i < len(cpus):
+        j = i
+        while j + 1 < len(cpus) and cpus[j + 1] == cpus[j] + 1:
+            j += 1
+        out.append(str(cpus[i]) if i == j else "%d-%d" % (cpus[i], cpus[j]))
+        i = j + 1
+    return ",".join(out)
+
+
+def cpu_threads():
+    """Threads for the oracle: every CPU this process may run on (its affinity mask),
+    capped by OMP_NUM_THREADS where the host sets it (the CPU share allotted per GPU)."""
+    allowed = os.sched_getaffinity(0)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    n = len(allowed)
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n), allowed
 
 
 SWEEP_SHAPES = [(1, 8192, 96, 128), (2, 16384, 16, 128), (4, 2048, 16, 128), (4, 4096, 64, 128),
@@ -459,10 +492,12 @@ def main():
             line["shape_sweep"].append(r)
             torch.cuda.empty_cache()
     if not args.no_cpu:
-        threads = min(16, os.cpu_count() or 1)
+        threads, allowed = cpu_threads()
         line["cpu_baseline"] = cpu_baseline(d, H, T, threads)
         line["cpu_baseline"]["cpu_model"] = cpu_model()
         line["cpu_baseline"]["nproc"] = os.cpu_count()
+        line["cpu_baseline"]["affinity"] = affinity_ranges(allowed)
+        line["cpu_baseline"]["omp_num_threads"] = os.environ.get("OMP_NUM_THREADS")
     print(json.dumps(line), flush=True)
 
 

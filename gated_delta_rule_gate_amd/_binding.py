@@ -152,6 +152,19 @@ def _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias):
     return B, T, H, K, V, N
 
 
+def _check_outputs(out, final_state, B, T, H, K, V, N, dtype, device):
+    """Caller-supplied outputs: the kernels write B*T*H*V elements of o and N*H*K*V
+    fp32 of the final state through raw pointers, so shape, dtype, layout and
+    device are checked here (the C ABI cannot see them)."""
+    if out is not None:
+        _require(tuple(out.shape) == (B, T, H, V) and out.dtype == dtype,
+                 "out must be %s [B, T, H, V] = %s" % (dtype, (B, T, H, V)))
+    if final_state is not None:
+        _require(tuple(final_state.shape) == (N, H, K, V) and final_state.dtype == torch.float32,
+                 "final_state must be fp32 [N, H, K, V] = %s" % ((N, H, K, V),))
+    _check_tensors(dict(out=out, final_state=final_state), device)
+
+
 def recurrent_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_final_state=False,
                   gate_kind="log2", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None, final_state=None,
                   out=None, q_l2norm=False, beta_logits=False):
@@ -166,13 +179,11 @@ def recurrent_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, outp
     ``beta_logits=True`` takes beta as logits (the sigmoid runs in the kernel).
     """
     B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
+    _check_outputs(out, final_state, B, T, H, K, V, N, q.dtype, q.device)
     o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
     ht = final_state
     if ht is None and output_final_state:
         ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
-    if ht is not None:
-        _require(ht.shape == (N, H, K, V) and ht.dtype == torch.float32 and ht.is_contiguous(),
-                 "final_state must be fp32 [N, H, K, V]")
     a = make_args(q, v, H, N, gate_kind, scale=scale, A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
                   q_l2norm=q_l2norm, beta_logits=beta_logits)
     check(lib().kda_recurrent_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
@@ -225,6 +236,7 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
     the last chunk are left as they are). ``intermediate_states`` may preallocate it.
     """
     B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
+    _check_outputs(out, final_state, B, T, H, K, V, N, q.dtype, q.device)
     o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
     ht = final_state
     if ht is None and output_final_state:
@@ -324,6 +336,7 @@ class StagedRun:
                  gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None, out=None,
                  final_state=None):
         B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
+        _check_outputs(out, final_state, B, T, H, K, V, N, q.dtype, q.device)
         self.t = dict(q=q, k=k, v=v, g=g, beta=beta, h0=initial_state, cu=cu_seqlens)
         self.o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
         self.ht = final_state if final_state is not None else \

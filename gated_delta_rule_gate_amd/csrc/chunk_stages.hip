@@ -81,9 +81,13 @@ __global__ __launch_bounds__(256) void stage_gate_kernel(ChunkParams p) {
   for (int i = threadIdx.x; i < D; i += kNT) sDt[i] = (p.dt_bias && i < p.Kr) ? p.dt_bias[h * p.Kr + i] : 0.f;
   load_rows<float, kNT, C, D>(sB, TL::LDB, p.g + lc.t0 * ldg + h * p.Kr, ldg, lc.L, p.Kr);
   __syncthreads();
-  gate_activate<kNT, C, D, GK>(sB, TL::LDB, lc.L, sDt, head_expA(p, h), p.lower_bound);
-  __syncthreads();
-  gate_cumsum<kNT, C, D>(sB, TL::LDB, sBL, sSeg);
+  // a pre-cumsummed log2 gate already is b: it is only restrided from the
+  // caller's K channels per row to the tile width D (channels >= K zero)
+  if constexpr (GK != kGateLog2Cumsum) {
+    gate_activate<kNT, C, D, GK>(sB, TL::LDB, lc.L, sDt, head_expA(p, h), p.lower_bound);
+    __syncthreads();
+    gate_cumsum<kNT, C, D>(sB, TL::LDB, sBL, sSeg);
+  }
   store_rows_f32<C, D, TL::LDB>(p.b + lc.t0 * ld + h * D, ld, sB, lc.L);
 }
 
@@ -445,7 +449,6 @@ hipError_t launch_chunk_index(const ChunkParams &p, hipStream_t st) {
 }
 
 hipError_t launch_stage_gate(const ChunkParams &p, hipStream_t st) {
-  if (p.gate_kind == kGateLog2Cumsum) return hipSuccess;  // g already is b (p.b points at it)
   return dispatch(p, [&]<typename Tin, int C, int D>() {
     const size_t smem = sizeof(float) * ((size_t)C * (D + 4) + 2 * D + kNT);
     const dim3 grid(p.max_chunks, p.H);
@@ -453,6 +456,7 @@ hipError_t launch_stage_gate(const ChunkParams &p, hipStream_t st) {
       case kGateSafe: return launch_dyn(stage_gate_kernel<C, D, kGateSafe>, grid, smem, st, p);
       case kGateSoftplus: return launch_dyn(stage_gate_kernel<C, D, kGateSoftplus>, grid, smem, st, p);
       case kGateLogE: return launch_dyn(stage_gate_kernel<C, D, kGateLogE>, grid, smem, st, p);
+      case kGateLog2Cumsum: return launch_dyn(stage_gate_kernel<C, D, kGateLog2Cumsum>, grid, smem, st, p);
     }
     return hipErrorInvalidValue;
   });

@@ -323,8 +323,6 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
     p.u = reinterpret_cast<float *>(base + L.off[6]);
     p.vnew = reinterpret_cast<float *>(base + L.off[7]);
     p.hc = reinterpret_cast<float *>(base + L.off[8]);
-    // a pre-cumsummed gate is b itself: the gate step is skipped and the later steps read g
-    if (a->gate_kind == KDA_GATE_LOG2_CUMSUM) p.b = const_cast<float *>(g);
   }
   return KDA_OK;
 }

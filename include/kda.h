@@ -131,8 +131,9 @@ const char *kda_last_error(void);
 
 /*
  * Checks the device-side contract of packed offsets, which the other calls
- * cannot check without a host read ("Attention-gym KDA ...", the varlen
- * contract: offsets that never decrease and end within the capacity). One
+ * cannot check without a host read ("Add fused recurrent_kda for decode and
+ * inference prefill", section "Agent note": the varlen contract, offsets that
+ * never decrease and end within the capacity). One
  * asynchronous launch on `stream` reads cu_seqlens [N + 1] (device) and writes
  * into flags[0] (device int32, caller-owned) the OR of
  *   KDA_OFFSETS_DECREASE   some cu_seqlens[n + 1] < cu_seqlens[n]

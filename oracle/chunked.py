@@ -55,7 +55,13 @@ def _chunk(qc, kc, vc, gc, bc, h, scale, anchored, mid):
                 gqk = (qc[R] * row) @ (kc[S] * col).T
                 gkk = (kc[R] * row) @ (kc[S] * col).T
             else:
-                E = np.exp2(b[R][:, None, :] - b[S][None, :, :])
+                # only causal pairs s <= r enter the grams: the exponent of every other
+                # pair is masked before exponentiating (it would be positive)
+                diff = b[R][:, None, :] - b[S][None, :, :]
+                if i == j:
+                    causal = np.arange(R.start, R.stop)[:, None] >= np.arange(S.start, S.stop)[None, :]
+                    diff = np.where(causal[:, :, None], diff, -np.inf)
+                E = np.exp2(diff)
                 gqk = np.einsum("ri,si,rsi->rs", qc[R], kc[S], E)
                 gkk = np.einsum("ri,si,rsi->rs", kc[R], kc[S], E)
             Aqk[R, S] = gqk

@@ -233,3 +233,30 @@ def test_check_offsets_rejects(kda_lib):
     assert kda_lib.kda_check_offsets(FAKE, 3, 100, None, None) == 1
     assert kda_lib.kda_check_offsets(FAKE, -1, 100, FAKE2, None) == 2
     assert kda_lib.kda_check_offsets(FAKE, 3, -5, FAKE2, None) == 2
+
+
+def test_binding_rejects_bad_outputs():
+    """Caller-supplied o and final-state buffers are checked before any pointer
+    reaches the library: wrong shape, dtype, layout or device raise."""
+    import torch
+
+    from gated_delta_rule_gate_amd._binding import _check_outputs
+
+    B, T, H, K, V, N = 2, 5, 3, 8, 16, 2
+    cpu = torch.device("cpu")
+    bad_out = [torch.empty((B, T, H, V + 1), dtype=torch.bfloat16),
+               torch.empty((B, T, H, V), dtype=torch.float32),
+               torch.empty((B, T, V, H), dtype=torch.bfloat16).transpose(2, 3)]
+    for o in bad_out:
+        with pytest.raises(ValueError):
+            _check_outputs(o, None, B, T, H, K, V, N, torch.bfloat16, cpu)
+    bad_ht = [torch.empty((N, H, K, V + 8), dtype=torch.float32),
+              torch.empty((N, H, K, V), dtype=torch.bfloat16),
+              torch.empty((N, H, V, K), dtype=torch.float32).transpose(2, 3)]
+    for ht in bad_ht:
+        with pytest.raises(ValueError):
+            _check_outputs(None, ht, B, T, H, K, V, N, torch.bfloat16, cpu)
+    # right shapes on the wrong device (host memory) are refused too
+    with pytest.raises(ValueError):
+        _check_outputs(torch.empty((B, T, H, V), dtype=torch.bfloat16), None, B, T, H, K, V, N, torch.bfloat16,
+                       torch.device("cuda", 0))

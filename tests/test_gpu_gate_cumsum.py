@@ -136,3 +136,31 @@ def test_chunk_with_precumsummed_gate(schedule, C):
     end = int(cu[-1])
     parity(o.float().cpu().numpy()[:, :end], o_ref[:, :end], "bf16", "o")
     parity(ht.cpu().numpy(), ht_ref, "bf16", "ht")
+
+
+@pytest.mark.parametrize("schedule", ["auto", "staged"])
+@pytest.mark.parametrize("K,V", [(64, 128), (96, 96), (48, 200)])
+def test_precumsummed_gate_narrow_keys(schedule, K, V):
+    """The pre-cumsummed gate has K channels per row while the kernels run at the
+    tile width max(K, V) rounded up: every schedule must read it at its own
+    stride. Packed with an empty slot, against the recurrence on the raw gate."""
+    need_gpu()
+    from gated_delta_rule_gate_amd import chunk_kda, gate_cumsum
+
+    lens = [70, 0, 129, 33]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    d = kda_synth.chunk_inputs(1, int(cu[-1]) + 7, 2, K, V, dtype=torch.bfloat16, seed=2450 + K + V,
+                               n_slots=len(lens))
+    dev = {k: (v.cuda() if v is not None else None) for k, v in d.items()}
+    cu_d = torch.from_numpy(cu).cuda()
+    b = gate_cumsum(dev["x"], chunk_size=64, gate_kind="softplus", A_log=dev["A_log"], dt_bias=dev["dt_bias"],
+                    cu_seqlens=cu_d, out=torch.zeros_like(dev["x"]))
+    o, ht = chunk_kda(dev["q"], dev["k"], dev["v"], b, dev["beta"], dev["h0"], cu_seqlens=cu_d,
+                      output_final_state=True, chunk_size=64, gate_kind="log2_cumsum", schedule=schedule)
+    torch.cuda.synchronize()
+    g = oracle.gate(oracle.GATE_SOFTPLUS, f64(d["x"]), f64(d["A_log"]), f64(d["dt_bias"]), -5.0)
+    o_ref, ht_ref = oracle.recurrent(f64(d["q"]), f64(d["k"]), f64(d["v"]), g, f64(d["beta"]), h0=f64(d["h0"]),
+                                     cu_seqlens=cu)
+    end = int(cu[-1])
+    parity(o.float().cpu().numpy()[:, :end], o_ref[:, :end], "bf16", "o")
+    parity(ht.cpu().numpy(), ht_ref, "bf16", "ht")

@@ -105,6 +105,74 @@ def test_exact_bruteforce_dyadic(oracle_mod, K, V, T, seed):
     np.testing.assert_allclose(ht2[0, 0], f(S_ex), rtol=0, atol=1e-12)
 
 
+def _product_form_applied(q, k, v, g2, beta, S0, scale):
+    """The explicit product form of ``_product_form``, with each P(t, u) applied to its
+    operand one factor at a time (M_{u+1} first), so that K = 64 stays cheap in
+    exact rationals: S_t = P(t, 0) S0 + sum_{u <= t} P(t, u) beta_u k_u v_u^T."""
+    T, K, V = len(q), len(q[0]), len(v[0])
+
+    def apply_M(t, X):  # M_t X = (I - beta_t k_t k_t^T) Diag(2^g_t) X for a K x n matrix X
+        DX = [[(Fr(2) ** g2[t][i]) * X[i][j] for j in range(len(X[0]))] for i in range(K)]
+        kDX = [sum(k[t][i] * DX[i][j] for i in range(K)) for j in range(len(X[0]))]
+        return [[DX[i][j] - beta[t] * k[t][i] * kDX[j] for j in range(len(X[0]))] for i in range(K)]
+
+    outs, S_t = [], None
+    for t in range(T):
+        S_t = [[Fr(0)] * V for _ in range(K)]
+        for u in range(-1, t + 1):  # u = -1 stands for the initial state
+            X = S0 if u < 0 else [[beta[u] * k[u][i] * v[u][j] for j in range(V)] for i in range(K)]
+            for w in range(u + 1, t + 1):
+                X = apply_M(w, X)
+            S_t = [[S_t[i][j] + X[i][j] for j in range(V)] for i in range(K)]
+        outs.append([sum(S_t[i][j] * q[t][i] for i in range(K)) * scale for j in range(V)])
+    return outs, S_t
+
+
+def test_exact_bruteforce_dyadic_k64(oracle_mod):
+    """K = V = 64, the chunk kernels' smallest tile width: keys and queries of entries
+    +-1/8 (unit rows, scale 1/8 exact), log2 gates in {0, -1, -2}, beta in quarters,
+    small-integer values and an initial state in eighths; the oracle's recurrence
+    against the exact product form, in the log2 and the natural-log gate."""
+    K = V = 64
+    T = 3
+    rng = np.random.default_rng(64)
+    e = Fr(1, 8)
+    q = [[e * int(a) for a in row] for row in rng.choice([-1, 1], size=(T, K))]
+    k = [[e * int(a) for a in row] for row in rng.choice([-1, 1], size=(T, K))]
+    v = [[Fr(int(a)) for a in row] for row in rng.integers(-3, 4, size=(T, V))]
+    g2 = rng.integers(-2, 1, size=(T, K))
+    beta = [Fr(int(b), 4) for b in rng.choice([1, 2, 3, 4], size=T)]
+    S0 = [[Fr(int(a), 8) for a in row] for row in rng.integers(-4, 5, size=(K, V))]
+    o_ex, S_ex = _product_form_applied(q, k, v, g2.tolist(), beta, S0, e)
+
+    f = lambda rows: np.array([[float(a) for a in r] for r in rows])
+    b = np.array([float(x) for x in beta])[None, :, None]
+    o, ht = oracle.recurrent(f(q)[None, :, None], f(k)[None, :, None], f(v)[None, :, None],
+                             g2.astype(float)[None, :, None], b, h0=f(S0)[None, None], scale=float(e),
+                             g_is_log2=True)
+    np.testing.assert_allclose(o[0, :, 0], f(o_ex), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ht[0, 0], f(S_ex), rtol=0, atol=1e-12)
+    o2, ht2 = oracle.recurrent(f(q)[None, :, None], f(k)[None, :, None], f(v)[None, :, None],
+                               (g2 * math.log(2.0))[None, :, None], b, h0=f(S0)[None, None], scale=float(e))
+    np.testing.assert_allclose(o2[0, :, 0], f(o_ex), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(ht2[0, 0], f(S_ex), rtol=0, atol=1e-11)
+
+
+def test_product_forms_agree():
+    """The two exact product forms (whole P(t, u) matrices, and factors applied one at
+    a time) are the same rationals on a small case."""
+    rng = np.random.default_rng(11)
+    K, V, T = 4, 3, 5
+    e = Fr(1, 2)
+    q = [[e * int(a) for a in row] for row in rng.choice([-1, 1], size=(T, K))]
+    k = [[e * int(a) for a in row] for row in rng.choice([-1, 1], size=(T, K))]
+    v = [[Fr(int(a)) for a in row] for row in rng.integers(-3, 4, size=(T, V))]
+    g2 = rng.integers(-2, 1, size=(T, K)).tolist()
+    beta = [Fr(int(b), 4) for b in rng.choice([1, 2, 3, 4], size=T)]
+    S0 = [[Fr(int(a), 8) for a in row] for row in rng.integers(-4, 5, size=(K, V))]
+    assert _product_form(q, k, v, g2, beta, S0, e) == _product_form_applied(q, k, v, g2, beta, S0, e)
+
+
 # ----------------------------------------------------------------------------------------
 # Closed forms and limits
 # ----------------------------------------------------------------------------------------
