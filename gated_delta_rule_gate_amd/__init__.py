@@ -3,8 +3,8 @@
 The computation lives in the HIP library ``_build/libkda.so`` (C ABI in
 ``include/kda.h``); this package only marshals arguments to it.
 """
-from ._binding import (KdaError, chunk_kda, chunk_kda_bwd, gate_cumsum, lib, recurrent_kda,  # noqa: F401
+from ._binding import (KdaError, chunk_kda, chunk_kda_bwd, chunk_kda_noalloc, gate_cumsum, lib, recurrent_kda,  # noqa: F401
                        resolved_schedule, workspace_bytes, check_offsets)
 
-__all__ = ["chunk_kda", "chunk_kda_bwd", "recurrent_kda", "gate_cumsum", "KdaError", "lib", "resolved_schedule", "check_offsets",
+__all__ = ["chunk_kda", "chunk_kda_bwd", "chunk_kda_noalloc", "recurrent_kda", "gate_cumsum", "KdaError", "lib", "resolved_schedule", "check_offsets",
            "workspace_bytes"]

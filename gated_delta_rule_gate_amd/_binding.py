@@ -61,6 +61,11 @@ def lib():
             L.kda_chunk_states_count.restype = ctypes.c_size_t
             L.kda_chunk_fwd_states.argtypes = [ap] + [vp] * 11 + [ctypes.c_size_t, vp]
             L.kda_chunk_fwd_states.restype = ctypes.c_int
+        if hasattr(L, "kda_chunk_fwd_noalloc"):
+            L.kda_chunk_fwd_noalloc.argtypes = [ap] + [vp] * 10
+            L.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+            L.kda_chunk_noalloc_max_bytes.argtypes = []
+            L.kda_chunk_noalloc_max_bytes.restype = ctypes.c_size_t
         if hasattr(L, "kda_chunk_bwd"):
             L.kda_chunk_bwd_workspace_bytes.argtypes = [ap]
             L.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -263,6 +268,24 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
                                  _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(hs), _ptr(ws),
                                  ctypes.c_size_t(ws.numel()), _stream()))
     return o, ht, hs
+
+
+def chunk_kda_noalloc(q, k, v, g, beta, initial_state=None, *, out, final_state=None, cu_seqlens=None,
+                      chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None,
+                      schedule="auto", q_l2norm=False, beta_logits=False):
+    """``chunk_kda`` through kda_chunk_fwd_noalloc, which allocates nothing: the
+    intermediates live in the library's static device array. The caller passes the
+    output ``out`` (and ``final_state`` to receive the final state); this wrapper
+    allocates nothing either. Returns (out, final_state)."""
+    B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
+    _require(out is not None, "out must be preallocated")
+    _check_outputs(out, final_state, B, T, H, K, V, N, q.dtype, q.device)
+    a = make_args(q, v, H, N, gate_kind, chunk_size=chunk_size, scale=scale, A_log=A_log, dt_bias=dt_bias,
+                  lower_bound=lower_bound, schedule=schedule, q_l2norm=q_l2norm, beta_logits=beta_logits)
+    check(lib().kda_chunk_fwd_noalloc(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(initial_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
+                                      _stream()))
+    return out, final_state
 
 
 def chunk_kda_bwd(q, k, v, g, beta, do, initial_state=None, *, dht=None, cu_seqlens=None, chunk_size=64,

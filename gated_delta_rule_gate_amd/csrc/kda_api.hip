@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "../../include/kda_stages.h"
@@ -400,6 +401,75 @@ extern "C" kda_status kda_chunk_fwd(const kda_args *a, const void *q, const void
   kda_status s = prepare_chunk(a, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace, ws_bytes, p);
   if (s != KDA_OK) return s;
   return run_chunk(a, p, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// kda_chunk_fwd without a caller workspace: the intermediates live in a static
+// device array. In host code the array's name is a host-side stand-in; the
+// device address comes from hipGetSymbolAddress, looked up once per device.
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocBytes = (size_t)64 << 20;
+__device__ __align__(256) char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`.
+kda_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) {
+    snprintf(g_last_error, sizeof(g_last_error), "device %d beyond the %d devices the static array covers", dev,
+             kMaxDevices);
+    return KDA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) {
+      snprintf(g_last_error, sizeof(g_last_error), "hipGetSymbolAddress returned NULL for the static array");
+      return KDA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t kda_chunk_noalloc_max_bytes(void) { return kNoAllocBytes; }
+
+extern "C" kda_status kda_chunk_fwd_noalloc(const kda_args *a, const void *q, const void *k, const void *v,
+                                            const float *g, const float *beta, const float *h0,
+                                            const int32_t *cu_seqlens, void *o, float *ht, void *stream) {
+  if (!a) return KDA_ERR_NULL;
+  kda_args s = *a;
+  size_t need = kda_chunk_workspace_bytes(&s);
+  if (need > kNoAllocBytes && s.schedule == KDA_SCHED_AUTO) {
+    kda_args f = s;
+    f.schedule = KDA_SCHED_FUSED;
+    if (kda_chunk_schedule(&f) == KDA_SCHED_FUSED) {
+      s = f;
+      need = kda_chunk_workspace_bytes(&s);
+    }
+  }
+  if (need > kNoAllocBytes) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "the schedule for these arguments needs %zu bytes of workspace; the static array holds %zu", need,
+             kNoAllocBytes);
+    return KDA_ERR_WORKSPACE;
+  }
+  void *ws = nullptr;
+  kda_status st = scratch_address(&ws);
+  if (st != KDA_OK) return st;
+  return kda_chunk_fwd(&s, q, k, v, g, beta, h0, cu_seqlens, o, ht, ws, kNoAllocBytes, stream);
 }
 
 extern "C" size_t kda_chunk_states_count(const kda_args *a, int packed) {

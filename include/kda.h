@@ -229,6 +229,32 @@ kda_status kda_chunk_fwd(const kda_args *args, const void *q, const void *k, con
                          void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * kda_chunk_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments and results as kda_chunk_fwd without the workspace: the
+ * intermediates live in a library-owned static device array of
+ * kda_chunk_noalloc_max_bytes() bytes (64 MiB), one copy per GPU the library
+ * runs on, held until the process ends. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); the caller still passes
+ * every input and output.
+ *   - Schedules: the one kda_chunk_fwd would run, when its workspace fits the
+ *     array; under KDA_SCHED_AUTO a split schedule whose records would not fit
+ *     runs the fused schedule instead (the same function). Otherwise
+ *     KDA_ERR_WORKSPACE, with the sizes in kda_last_error(), and nothing runs.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *     contents (no kernel here needs it cleared). Calls that overlap on one GPU
+ *     (concurrent streams or host threads) race on it: serialise them.
+ *   - The first call on each device looks up that device's address of the
+ *     array (KDA_ERR_HIP if the lookup fails).
+ */
+kda_status kda_chunk_fwd_noalloc(const kda_args *args, const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *h0, const int32_t *cu_seqlens, void *o,
+                                 float *ht, void *stream);
+
+/* Bytes of the static device array behind kda_chunk_fwd_noalloc. */
+size_t kda_chunk_noalloc_max_bytes(void);
+
+/*
  * Entries of [H, K, V] floats that h_states of kda_chunk_fwd_states must hold
  * (0 when the arguments are invalid or packed does not match B and N):
  *   dense  (packed == 0, N == B)  B * ceil(T / C), exactly the chunks;
