@@ -51,30 +51,40 @@ def alg_flops_chunk(B, T, H, D, C=64):
     return B * T * H * per
 
 
-FUSED_SOURCES = ("chunk_fused.hip", "chunk_fused_layout.h", "chunk_fused_tiles.h", "chunk_tiles.h", "kda_device.h", "kda_launch.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_chunk_b4t4096h64d128_traffic.txt")
+# per single-kernel schedule: the sources its kernel is built from and the
+# committed counter summary of its HBM traffic at the headline shape
+_HEADERS = ("chunk_fused_layout.h", "chunk_fused_tiles.h", "chunk_tiles.h", "kda_device.h", "kda_launch.h")
+TRAFFIC = {
+    "fused": (("chunk_fused.hip",) + _HEADERS, "fused_chunk_b4t4096h64d128_traffic.txt", "fused_chunk_kernel"),
+    "pipe": (("chunk_pipe.hip",) + _HEADERS, "pipe_chunk_b4t4096h64d128_traffic.txt", "pipe_chunk_kernel"),
+}
+# kept for the traffic summaries' own commands
+FUSED_SOURCES = TRAFFIC["fused"][0]
 
 
-def kernel_source_sha():
-    """sha256 over the sources the fused chunk kernel is built from."""
+def kernel_source_sha(sched="fused"):
+    """sha256 over the sources the schedule's chunk kernel is built from."""
     h = hashlib.sha256()
-    for name in FUSED_SOURCES:
+    for name in TRAFFIC[sched][0]:
         with open(os.path.join(ROOT, "gated_delta_rule_gate_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(sched):
     """HBM bytes per launch from the committed counter summary, or None when the
     kernel sources changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if sched not in TRAFFIC:
+        return None
+    path = os.path.join(ROOT, "profiles", TRAFFIC[sched][1])
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             vals[key.strip()] = val.strip()
-    if vals.get("source_sha256") != kernel_source_sha():
+    if vals.get("source_sha256") != kernel_source_sha(sched):
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
@@ -457,10 +467,9 @@ def main():
                    "cache": "flushed"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if sched == "fused" and (B, T, H, D) == (4, 4096, 64, 128)
-                     else None,
-                     "kernel": {"fused": "fused_chunk_kernel", "split": "split_key_kernel + split_state_kernel"}.get(
-                         sched, "staged chain"),
+                     "traffic": measured_traffic(sched) if (B, T, H, D) == (4, 4096, 64, 128) else None,
+                     "kernel": {"fused": "fused_chunk_kernel", "pipe": "pipe_chunk_kernel",
+                                "split": "split_key_kernel + split_state_kernel"}.get(sched, "staged chain"),
                      "alg_bytes_per_launch": nbytes,
                      "alg_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
                      "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},

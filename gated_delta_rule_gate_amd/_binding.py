@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "_build", "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
 GATE_KINDS = {"loge": 0, "safe": 1, "softplus": 2, "log2_cumsum": 3, "log2": 4}
-SCHEDULES = {"auto": 0, "staged": 1, "fused": 2, "split": 3}
+SCHEDULES = {"auto": 0, "staged": 1, "fused": 2, "split": 3, "pipe": 4}
 
 _LIB = None
 

@@ -154,12 +154,12 @@ __device__ __forceinline__ void gate_cumsum_tables(float *sB, int ldb, float *sB
 // stage k the lanes of group k finish their four rows (a 4-step chain), pass
 // them to every lane of the same column, and the later groups subtract their
 // part, so the chain crosses lanes four times instead of sixteen. -A_ii is
-// read from sAkk (fp32, strictly lower, beta folded), T_ii written as bf16 rows
-// of sTd.
-__device__ __forceinline__ void diag_inverse_block(const float *sAkk, int lda, bf16_t *sTd, int ldt, int i) {
+// read at its origin Ablk (fp32, row stride lda, strictly lower, beta folded),
+// T_ii written as bf16 rows at Tblk (row stride ldt).
+__device__ __forceinline__ void diag_inverse16(const float *Ablk, int lda, bf16_t *Tblk, int ldt) {
   const int lane = tid_opaque() & 63;
   const int g = lane >> 4, c = lane & 15;
-  const float *A = sAkk + (16 * i + 4 * g) * lda + 16 * i;
+  const float *A = Ablk + 4 * g * lda;
   f32x4_t a[4][4];  // rows 4g + e, column quads q
 #pragma unroll
   for (int e = 0; e < 4; ++e)
@@ -193,9 +193,14 @@ __device__ __forceinline__ void diag_inverse_block(const float *sAkk, int lda, b
       x[e] = later ? acc : x[e];
     }
   }
-  bf16_t *T = sTd + (16 * i + 4 * g) * ldt + c;
+  bf16_t *T = Tblk + 4 * g * ldt + c;
 #pragma unroll
   for (int e = 0; e < 4; ++e) T[e * ldt] = static_cast<bf16_t>(x[e]);
+}
+
+// The same for diagonal block i of -A_kk in sAkk, into rows 16i.. of sTd.
+__device__ __forceinline__ void diag_inverse_block(const float *sAkk, int lda, bf16_t *sTd, int ldt, int i) {
+  diag_inverse16(sAkk + 16 * i * lda + 16 * i, lda, sTd + 16 * i * ldt, ldt);
 }
 
 

@@ -248,9 +248,34 @@ bool use_split(const kda_args *a, const kda::ChunkParams &p) {
   return a->schedule == KDA_SCHED_SPLIT || (a->schedule == KDA_SCHED_AUTO && auto_split(a));
 }
 
+// The pipelined fused kernel: when named, or under AUTO / FUSED where it takes the
+// arguments and there are more (sequence, head) pairs than half the compute units
+// (fewer leave the serial fused kernel room to split value columns).
+bool use_pipe(const kda_args *a, const kda::ChunkParams &p) {
+  if (!kda::pipe_supported(p)) return false;
+  if (a->schedule == KDA_SCHED_PIPE) return true;
+  if (a->schedule != KDA_SCHED_AUTO && a->schedule != KDA_SCHED_FUSED) return false;
+  return !use_split(a, p) && 2 * (int64_t)a->N * a->H > kda::device_cus();
+}
+
 bool use_fused(const kda_args *a, const kda::ChunkParams &p) {
-  if (a->schedule == KDA_SCHED_STAGED || a->schedule == KDA_SCHED_SPLIT) return false;
-  return kda::fused_supported(p) && !use_split(a, p);
+  if (a->schedule != KDA_SCHED_AUTO && a->schedule != KDA_SCHED_FUSED) return false;
+  return kda::fused_supported(p) && !use_split(a, p) && !use_pipe(a, p);
+}
+
+bool schedule_known(const kda_args *a) {
+  return a->schedule == KDA_SCHED_AUTO || a->schedule == KDA_SCHED_STAGED || a->schedule == KDA_SCHED_FUSED ||
+         a->schedule == KDA_SCHED_SPLIT || a->schedule == KDA_SCHED_PIPE;
+}
+
+// The fields of ChunkParams that the schedule choice reads.
+kda::ChunkParams shape_params(const kda_args *a) {
+  kda::ChunkParams p{};
+  p.D = pad_width(std::max(a->K, a->V));
+  p.C = a->chunk_size;
+  p.is_bf16 = a->dtype == KDA_BF16;
+  p.gate_kind = (int)a->gate_kind;
+  return p;
 }
 
 // Split schedule: the chunk prefix, then the key side's records for every
@@ -268,9 +293,7 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
   if (s != KDA_OK) return s;
   if ((s = check_slots(a, cu)) != KDA_OK) return s;
   if (a->chunk_size != 32 && a->chunk_size != 64) return KDA_ERR_CHUNK;
-  if (a->schedule != KDA_SCHED_AUTO && a->schedule != KDA_SCHED_STAGED && a->schedule != KDA_SCHED_FUSED &&
-      a->schedule != KDA_SCHED_SPLIT)
-    return KDA_ERR_SHAPE;
+  if (!schedule_known(a)) return KDA_ERR_SHAPE;
   p = kda::ChunkParams{};
   p.q = q;
   p.k = k;
@@ -301,11 +324,12 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
   p.max_chunks = (int)max_chunks(a, cu != nullptr);
   if ((a->schedule == KDA_SCHED_FUSED || a->schedule == KDA_SCHED_SPLIT) && !kda::fused_supported(p))
     return KDA_ERR_UNSUPPORTED;
+  if (a->schedule == KDA_SCHED_PIPE && !kda::pipe_supported(p)) return KDA_ERR_UNSUPPORTED;
   const size_t need = kda_chunk_workspace_bytes(a);
   if (need > 0 && (!ws || ws_bytes < need)) return KDA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return KDA_ERR_ALIGN;
   char *base = static_cast<char *>(ws);
-  if (use_fused(a, p)) {
+  if (use_fused(a, p) || use_pipe(a, p)) {
     p.chunk_off = reinterpret_cast<int32_t *>(base);
   } else if (use_split(a, p)) {
     const int64_t nch = std::max<int64_t>(max_chunks(a, true), max_chunks(a, false));
@@ -345,9 +369,8 @@ kda_status run_stage(const kda::ChunkParams &p, int stage, hipStream_t st) {
 
 extern "C" size_t kda_chunk_workspace_bytes(const kda_args *a) {
   if (!chunk_shape_ok(a)) return 0;
-  kda::ChunkParams p{};
-  p.D = pad_width(std::max(a->K, a->V));
-  p.is_bf16 = a->dtype == KDA_BF16;
+  const kda::ChunkParams p = shape_params(a);
+  if (a->schedule == KDA_SCHED_PIPE) return kda::pipe_supported(p) ? align_up(sizeof(int32_t) * (a->N + 1)) : 0;
   if (a->schedule == KDA_SCHED_SPLIT) return kda::fused_supported(p) ? split_ws_bytes(a) : 0;
   if (a->schedule == KDA_SCHED_AUTO && kda::fused_supported(p) && auto_split(a)) return split_ws_bytes(a);
   if (a->schedule != KDA_SCHED_STAGED && kda::fused_supported(p)) return align_up(sizeof(int32_t) * (a->N + 1));
@@ -356,14 +379,11 @@ extern "C" size_t kda_chunk_workspace_bytes(const kda_args *a) {
 }
 
 extern "C" int kda_chunk_schedule(const kda_args *a) {
-  if (!chunk_shape_ok(a)) return -1;
-  if (a->schedule != KDA_SCHED_AUTO && a->schedule != KDA_SCHED_STAGED && a->schedule != KDA_SCHED_FUSED &&
-      a->schedule != KDA_SCHED_SPLIT)
-    return -1;
-  kda::ChunkParams p{};
-  p.D = pad_width(std::max(a->K, a->V));
-  p.is_bf16 = a->dtype == KDA_BF16;
+  if (!chunk_shape_ok(a) || !schedule_known(a)) return -1;
+  const kda::ChunkParams p = shape_params(a);
   if ((a->schedule == KDA_SCHED_FUSED || a->schedule == KDA_SCHED_SPLIT) && !kda::fused_supported(p)) return -1;
+  if (a->schedule == KDA_SCHED_PIPE && !kda::pipe_supported(p)) return -1;
+  if (use_pipe(a, p)) return KDA_SCHED_PIPE;
   if (use_split(a, p)) return KDA_SCHED_SPLIT;
   if (use_fused(a, p)) return KDA_SCHED_FUSED;
   return KDA_SCHED_STAGED;
@@ -378,6 +398,11 @@ namespace {
 
 kda_status run_chunk(const kda_args *a, const kda::ChunkParams &p, hipStream_t st) {
   kda_status s;
+  if (use_pipe(a, p)) {
+    // the chunk prefix only numbers the chunk-start states
+    if (p.hc && p.cu && (s = run_stage(p, KDA_STAGE_INDEX, st)) != KDA_OK) return s;
+    return hip_status(kda::launch_pipe(p, st));
+  }
   if (use_fused(a, p)) {
     // the fused kernel reads the chunk prefix only to number the chunk-start states
     if (p.hc && p.cu && (s = run_stage(p, KDA_STAGE_INDEX, st)) != KDA_OK) return s;
@@ -455,7 +480,8 @@ extern "C" kda_status kda_chunk_fwd_noalloc(const kda_args *a, const void *q, co
   if (need > kNoAllocBytes && s.schedule == KDA_SCHED_AUTO) {
     kda_args f = s;
     f.schedule = KDA_SCHED_FUSED;
-    if (kda_chunk_schedule(&f) == KDA_SCHED_FUSED) {
+    const int r = kda_chunk_schedule(&f);
+    if (r == KDA_SCHED_FUSED || r == KDA_SCHED_PIPE) {
       s = f;
       need = kda_chunk_workspace_bytes(&s);
     }

@@ -103,6 +103,10 @@ hipError_t launch_stage_scan(const ChunkParams &p, hipStream_t st);
 hipError_t launch_stage_output(const ChunkParams &p, hipStream_t st);
 hipError_t launch_fused(const ChunkParams &p, hipStream_t st);
 bool fused_supported(const ChunkParams &p);
+// the pipelined fused kernel (bf16, C = 64, D = 128, safe gate; one workgroup per
+// (sequence, head))
+bool pipe_supported(const ChunkParams &p);
+hipError_t launch_pipe(const ChunkParams &p, hipStream_t st);
 // split schedule: the key side of every chunk in parallel, then the state side
 hipError_t launch_split(const ChunkParams &p, hipStream_t st);
 // workspace of the split schedule for chunk_heads (chunk, head) pairs: the bf16

@@ -83,9 +83,14 @@ typedef enum {
   KDA_SCHED_AUTO = 0,   /* pick per shape                                                   */
   KDA_SCHED_STAGED = 1, /* six kernels, one per step, intermediates in the workspace        */
   KDA_SCHED_FUSED = 2,  /* one persistent kernel per (sequence, head); state kept on chip   */
-  KDA_SCHED_SPLIT = 3   /* steps (1)-(4) for every chunk at once, their operands through the
+  KDA_SCHED_SPLIT = 3,  /* steps (1)-(4) for every chunk at once, their operands through the
                            workspace, then one kernel per (sequence, head) for steps (5)-(6)
                            and the state; for few (sequence, head) pairs with long sequences */
+  KDA_SCHED_PIPE = 4    /* the fused schedule's pipelined kernel (bf16, chunk 64, max(K, V) in
+                           (64, 128], safe gate): per (sequence, head), four waves run steps
+                           (1)-(4) of one chunk while four run steps (5)-(6) of the previous
+                           one. AUTO and FUSED run it where it applies and the (sequence, head)
+                           pairs fill the device                                              */
 } kda_schedule;
 
 typedef struct {

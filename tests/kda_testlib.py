@@ -69,3 +69,24 @@ def dtype_name(t):
 
 def log2e():
     return 1.0 / math.log(2.0)
+
+
+def tile_width(K, V=None):
+    """The chunk kernels' tile width: 64, 128 or 256, the smallest covering max(K, V)."""
+    m = max(K, V if V is not None else K)
+    return 64 if m <= 64 else (128 if m <= 128 else 256)
+
+
+def pipe_refuses(schedule, gate="safe", C=64, K=128, V=None, dtype=torch.bfloat16):
+    """Whether the named schedule is the pipelined kernel and these arguments are outside
+    what it takes (bf16, chunk 64, tile width 128, safe gate)."""
+    return schedule == "pipe" and not (gate == "safe" and C == 64 and tile_width(K, V) == 128 and
+                                       dtype == torch.bfloat16)
+
+
+def expect_unsupported(fn):
+    """Asserts that fn() raises the library's KDA_ERR_UNSUPPORTED."""
+    from gated_delta_rule_gate_amd import KdaError
+
+    with pytest.raises(KdaError, match="UNSUPPORTED"):
+        fn()

@@ -195,7 +195,8 @@ def test_split_schedule_limits_and_workspace(kda_lib):
                                            FAKE2, ctypes.c_size_t(1 << 40), None)
     assert call(_args(gate_kind=0, schedule=3, dtype=1)) == 8            # fp32
     assert call(_args(gate_kind=0, schedule=3, K=256, V=256)) == 8       # tile 256
-    assert call(_args(gate_kind=0, schedule=4)) == 2                     # no such schedule
+    assert call(_args(gate_kind=0, schedule=5)) == 2                     # no such schedule
+    assert call(_args(gate_kind=0, schedule=4)) == 8                     # the pipelined kernel: safe gate only
     align = lambda x: (x + 255) // 256 * 256
     for B, N, T, H, K, V, C in ((3, 3, 203, 2, 128, 128, 64), (1, 5, 420, 4, 96, 64, 32)):
         a = _args(gate_kind=0, schedule=3, B=B, N=N, T=T, H=H, K=K, V=V, chunk_size=C)
@@ -222,6 +223,21 @@ def test_resolved_schedule(kda_lib):
     assert sched(dtype=1, schedule=2) == -1
     assert sched(K=256, V=256, schedule=3) == -1
     assert sched(chunk_size=16) == -1
+    # the pipelined kernel (safe gate, bf16, chunk 64, tile 128): what AUTO and FUSED run
+    # for more (sequence, head) pairs than half the compute units; named, on any count
+    safe = lambda **kw: kda_lib.kda_chunk_schedule(ctypes.byref(_args(gate_kind=1, **kw)))
+    assert safe(B=4, N=4, T=4096, H=64) == 4
+    assert safe(B=4, N=4, T=4096, H=64, schedule=2) == 4
+    assert safe(B=4, N=4, T=4096, H=64, K=96, V=72) == 4
+    assert safe(B=1, N=1, T=300, H=2, schedule=4) == 4
+    assert safe(B=1, N=1, T=300, H=2, schedule=2) == 2
+    assert safe(B=4, N=4, T=4096, H=64, chunk_size=32) == 2
+    assert safe(B=4, N=4, T=4096, H=64, K=64, V=64) == 2
+    assert safe(B=2, N=2, T=16384, H=16) == 3
+    assert safe(schedule=4, chunk_size=32) == -1
+    assert safe(schedule=4, K=64, V=64) == -1
+    assert safe(schedule=4, dtype=1) == -1
+    assert safe(schedule=5) == -1
     a = _args(gate_kind=0, B=2, N=2, T=16384, H=16)
     b = _args(gate_kind=0, B=2, N=2, T=16384, H=16, schedule=3)
     assert kda_lib.kda_chunk_workspace_bytes(ctypes.byref(a)) == kda_lib.kda_chunk_workspace_bytes(ctypes.byref(b))

@@ -26,8 +26,8 @@ def _logits(shape, seed):
     return torch.from_numpy(x)
 
 
-@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
-@pytest.mark.parametrize("C", [64, 32])
+@pytest.mark.parametrize("schedule,C", [(s_, c_) for s_ in ("fused", "split", "staged") for c_ in (64, 32)]
+                         + [("pipe", 64)])
 def test_chunk_beta_logits(schedule, C):
     from gated_delta_rule_gate_amd import chunk_kda
 

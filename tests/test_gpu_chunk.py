@@ -12,7 +12,7 @@ import torch
 
 import kda_synth
 import oracle
-from kda_testlib import f64, need_gpu, parity
+from kda_testlib import expect_unsupported, f64, need_gpu, parity, pipe_refuses
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,7 @@ def oracle_pairs(d, gate, pairs):
     return np.stack(os_), np.stack(hts)
 
 
-SCHEDULES = ["fused", "split", "staged"]
+SCHEDULES = ["fused", "split", "staged", "pipe"]
 
 
 def expect_fused_unsupported(d, cu=None, schedule="fused"):
@@ -80,7 +80,7 @@ def test_fp32_small_config(schedule, C):
     kernel takes bf16 only: fp32 runs the staged schedule, also under "auto")."""
     need_gpu()
     d = make(1, 256, 2, 64, torch.float32, 1000, with_h0=False)
-    if schedule in ("fused", "split"):
+    if schedule in ("fused", "split", "pipe"):
         expect_fused_unsupported(d, schedule=schedule)
         schedule = "auto"
     o, ht = gpu_run(d, "safe", schedule, C=C)
@@ -96,6 +96,8 @@ def test_bf16_ragged(schedule, gate, C):
     """bf16, T not a multiple of the chunk (several chunks and a ragged tail)."""
     need_gpu()
     d = make(2, 203, 3, 128, torch.bfloat16, 200 + C, gate=gate)
+    if pipe_refuses(schedule, gate, C):
+        return expect_unsupported(lambda: gpu_run(d, gate, schedule, C=C))
     o, ht = gpu_run(d, gate, schedule, C=C)
     o_ref, ht_ref = oracle_run(d, gate)
     parity(o, o_ref, "bf16", "o")
@@ -107,6 +109,8 @@ def test_bf16_ragged(schedule, gate, C):
 def test_bf16_widths(schedule, D):
     need_gpu()
     d = make(2, 150, 2, D, torch.bfloat16, 300 + D)
+    if pipe_refuses(schedule, K=D):
+        return expect_unsupported(lambda: gpu_run(d, "safe", schedule))
     if schedule in ("fused", "split") and D == 256:
         from gated_delta_rule_gate_amd import KdaError
 
@@ -130,7 +134,7 @@ def test_packed_empty_slots_tail(schedule, dtype):
     cap = int(cu[-1]) + 37
     D = 64 if dtype == torch.float32 else 128
     d = make(1, cap, 2, D, dtype, 400, gate="safe", n_slots=len(lens))
-    if schedule in ("fused", "split") and dtype == torch.float32:
+    if schedule in ("fused", "split", "pipe") and dtype == torch.float32:
         expect_fused_unsupported(d, cu, schedule)
         schedule = "auto"
     end = int(cu[-1])

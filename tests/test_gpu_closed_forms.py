@@ -97,7 +97,7 @@ def test_zero_beta_only_decays_the_initial_state(path):
     parity(ht, ht_ref, "bf16", "ht")
 
 
-@pytest.mark.parametrize("path", CHUNK_SCHEDULES + ["recurrent"])
+@pytest.mark.parametrize("path", CHUNK_SCHEDULES + ["pipe", "recurrent"])
 def test_unit_beta_with_query_equal_key_returns_v(path):
     need_gpu()
     d = _base(2102)
@@ -113,8 +113,8 @@ def test_unit_beta_with_query_equal_key_returns_v(path):
     parity(o, f64(d["v"]) * SCALE, "bf16", "o")
 
 
-@pytest.mark.parametrize("path", CHUNK_SCHEDULES + ["recurrent"])
-@pytest.mark.parametrize("gate", ["safe", "softplus"])
+@pytest.mark.parametrize("path,gate", [(p_, g_) for p_ in CHUNK_SCHEDULES + ["recurrent"]
+                                        for g_ in ("safe", "softplus")] + [("pipe", "safe")])
 def test_axis_aligned_keys_decouple_rows(path, gate):
     need_gpu()
     d = _base(2103 + (gate == "softplus"))

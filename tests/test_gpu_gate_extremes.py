@@ -62,8 +62,9 @@ def _chunk(d, gate, lb, schedule, cu=None):
     return o.float().cpu().numpy(), ht.cpu().numpy()
 
 
-@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
-@pytest.mark.parametrize("gate,lb", [("safe", -5.0), ("safe", -1e-3), ("softplus", -5.0)])
+@pytest.mark.parametrize("schedule,gate,lb", [(s_, g_, l_) for s_ in ("fused", "split", "staged")
+                                              for g_, l_ in (("safe", -5.0), ("safe", -1e-3), ("softplus", -5.0))]
+                         + [("pipe", "safe", -5.0), ("pipe", "safe", -1e-3)])
 def test_chunk_gate_extremes(schedule, gate, lb):
     need_gpu()
     d = _case(2, 333, 1600, a_log="chunk_softplus" if gate == "softplus" else "wide")
@@ -73,7 +74,7 @@ def test_chunk_gate_extremes(schedule, gate, lb):
     parity(ht, ht_ref, "bf16", "ht")
 
 
-@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
+@pytest.mark.parametrize("schedule", ["fused", "split", "staged", "pipe"])
 def test_chunk_long_decay_packed(schedule):
     """A long slot (2048 tokens) beside short ragged ones, bound close to 0, so
     the cumulative decay stays near 1 over the whole sequence."""

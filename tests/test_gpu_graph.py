@@ -33,7 +33,7 @@ def _refill(dst, src):
             dst[key].copy_(t)
 
 
-@pytest.mark.parametrize("schedule", ["auto", "split", "staged"])
+@pytest.mark.parametrize("schedule", ["auto", "split", "staged", "pipe"])
 def test_chunk_graph_replay_with_new_offsets(schedule):
     from gated_delta_rule_gate_amd import chunk_kda
 

@@ -36,7 +36,7 @@ def _oracle(d, H, gate="safe"):
     return oracle.recurrent(q, k, f64(d["v"]), g, f64(d["beta"]), h0=f64(d["h0"]))
 
 
-@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
+@pytest.mark.parametrize("schedule", ["fused", "split", "staged", "pipe"])
 @pytest.mark.parametrize("Hk", [1, 2])
 def test_chunk_gva(schedule, Hk):
     from gated_delta_rule_gate_amd import chunk_kda

@@ -50,8 +50,8 @@ def _gpu_chunk(d, schedule, cu=None, C=64, q_l2norm=True):
     return o.float().cpu().numpy(), ht.cpu().numpy()
 
 
-@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
-@pytest.mark.parametrize("D,C", [(128, 64), (128, 32), (64, 64)])
+@pytest.mark.parametrize("schedule,D,C", [(s_, d_, c_) for s_ in ("fused", "split", "staged")
+                                          for d_, c_ in ((128, 64), (128, 32), (64, 64))] + [("pipe", 128, 64)])
 def test_chunk_q_l2norm(schedule, D, C):
     need_gpu()
     d = _chunk_case(2, 203, 3, D, 700 + D + C)

@@ -44,8 +44,8 @@ def _run(d, schedule, C, cu=None, states=True, prefill=None):
     return [None if r is None else r.float().cpu() for r in res]
 
 
-@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
-@pytest.mark.parametrize("D,C", [(128, 64), (128, 32), (64, 64)])
+@pytest.mark.parametrize("schedule,D,C", [(s_, d_, c_) for s_ in ("fused", "split", "staged")
+                                          for d_, c_ in ((128, 64), (128, 32), (64, 64))] + [("pipe", 128, 64)])
 def test_dense_states(schedule, D, C):
     need_gpu()
     B, T, H = 2, 203, 3
@@ -64,7 +64,7 @@ def test_dense_states(schedule, D, C):
     assert torch.equal(o, o2) and torch.equal(ht, ht2)
 
 
-@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
+@pytest.mark.parametrize("schedule", ["fused", "split", "staged", "pipe"])
 def test_packed_states_with_empty_slots(schedule):
     """Five slots, one empty, two (sequence, head) pairs per slot: the fused
     kernel also splits the value columns. Entries past the last chunk keep the

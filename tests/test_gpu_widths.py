@@ -39,8 +39,8 @@ def _chunk(d, schedule, C=64, cu=None):
     return o.float().cpu().numpy(), ht.cpu().numpy()
 
 
-@pytest.mark.parametrize("schedule", ["auto", "split", "staged"])
-@pytest.mark.parametrize("K,V", PAIRS)
+@pytest.mark.parametrize("schedule,K,V", [(s_, k_, v_) for s_ in ("auto", "split", "staged") for k_, v_ in PAIRS]
+                         + [("pipe", k_, v_) for k_, v_ in PAIRS if 64 < max(k_, v_) <= 128] + [("pipe", 80, 128)])
 def test_chunk_widths(schedule, K, V):
     need_gpu()
     B, T, H = 2, 203, 2
@@ -70,7 +70,7 @@ def test_chunk_widths_fp32(K, V):
     parity(ht, ht_ref, "fp32", "ht")
 
 
-@pytest.mark.parametrize("schedule", ["auto", "split", "staged"])
+@pytest.mark.parametrize("schedule", ["auto", "split", "staged", "pipe"])
 def test_chunk_widths_packed_states(schedule):
     """K != V, packed with an empty slot and few (sequence, head) pairs, with the
     chunk-start states in the [K, V] layout of h0."""
