@@ -182,9 +182,44 @@ def bench_bwd(B, T, H, D, steps, warmup, C=64):
                       gate_kind="safe", A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0)
 
     t = event_time_ms(step, steps, warmup, flush=lambda: flush_buf.zero_())
+    nbytes = alg_bytes_bwd(B, T, H, D)
     return {"config": "chunk_kda bwd B%d T%d H%d K=V=%d bf16, C=%d, safe gate, h0 + dht; forward recompute "
                       "included" % (B, T, H, D, C),
-            "ms": round(t["mean"], 4), "Mtokens_per_s": round(B * T / (t["mean"] * 1e-3) / 1e6, 3)}
+            "ms": round(t["mean"], 4), "Mtokens_per_s": round(B * T / (t["mean"] * 1e-3) / 1e6, 3),
+            "alg_bytes": nbytes, "roofline_frac": round(nbytes / (t["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def alg_bytes_bwd(B, T, H, D, dtype_bytes=2):
+    """Bytes the backward must move once: it reads q, k, v, do (dtype) and the gate
+    input x (fp32), beta, h0 and dht; it writes dq, dk, dv (dtype), dx (fp32),
+    dbeta and dh0 (dA_log and ddt_bias are per head and negligible)."""
+    per_elem = 4 * dtype_bytes + 4 + 3 * dtype_bytes + 4
+    return B * T * H * (per_elem * D + 4 + 4) + 3 * B * H * D * D * 4
+
+
+def bench_fp32_small(steps, warmup):
+    """The fp32 configuration: B1 T256 H2 K=V=64, C=64, safe gate, h0 = 0 and the
+    final state returned (one chunk chain of four chunks per head)."""
+    import kda_synth
+    from gated_delta_rule_gate_amd import chunk_kda, resolved_schedule
+
+    B, T, H, D = 1, 256, 2, 64
+    d = kda_synth.chunk_inputs(B, T, H, D, D, dtype=torch.float32, seed=1001, with_h0=False)
+    dev = {k: v.cuda() for k, v in d.items() if v is not None}
+    o = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
+    ht = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+
+    def step():
+        chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], None, chunk_size=64, gate_kind="safe",
+                  A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0, out=o, final_state=ht)
+
+    t = event_time_ms(step, steps, warmup)
+    ms = t["median"]
+    nbytes = alg_bytes_chunk(B, T, H, D, dtype_bytes=4, with_h0=False)
+    return {"config": "chunk_kda fwd fp32 B1 T256 H2 K=V=64, C=64, safe gate lb=-5, h0=0, ht", "ms": round(ms, 5),
+            "Mtokens_per_s": round(B * T / (ms * 1e-3) / 1e6, 3),
+            "roofline_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 6),
+            "schedule": resolved_schedule(dev["q"], dev["v"], H, B, chunk_size=64)}
 
 
 def bench_prefill(steps, warmup):
@@ -391,7 +426,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--schedule", default="auto", choices=["auto", "fused", "split", "staged"])
+    ap.add_argument("--schedule", default="auto", choices=["auto", "pipe", "fused", "split", "staged"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the recurrent decode figure")
     ap.add_argument("--shape", default="4,4096,64,128", help="B,T,H,D")
@@ -481,6 +516,7 @@ def main():
     if not args.no_decode and not args.no_prefill:
         line["recurrent_prefill"] = bench_prefill(max(5, args.steps // 2), 2)
     if not args.no_varlen:
+        line["fp32_small"] = bench_fp32_small(max(10, args.steps), 3)
         line["varlen"] = bench_varlen(max(5, args.steps // 2), 2)
         line["copy_GBps"] = copy_bandwidth()
     if not args.no_bwd and args.schedule != "fused":

@@ -26,6 +26,9 @@ struct RecurrentParams {
 };
 
 hipError_t launch_recurrent(const RecurrentParams &p, hipStream_t st);
+// the blocked recurrence (bf16, K = V = 128, sequences longer than one token)
+bool recurrent_block_supported(const RecurrentParams &p);
+hipError_t launch_recurrent_block(const RecurrentParams &p, hipStream_t st);
 
 // Step (1) on its own: gate activation and chunk-local cumsum in log2 units
 // over [B*T, H, K] rows; C in {1, 32, 64}.

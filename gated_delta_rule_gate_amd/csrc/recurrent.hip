@@ -236,6 +236,7 @@ static hipError_t launch_rec_t(const RecurrentParams &p, hipStream_t st) {
 }
 
 hipError_t launch_recurrent(const RecurrentParams &p, hipStream_t st) {
+  if (recurrent_block_supported(p)) return launch_recurrent_block(p, st);
   return p.is_bf16 ? launch_rec_t<bf16_t>(p, st) : launch_rec_t<float>(p, st);
 }
 
