@@ -212,7 +212,10 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   if (owner && p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, Vr, col0, Kr, hs, Vr);
 }
 
-bool fused_supported(const ChunkParams &p) { return p.is_bf16 && (p.D == 64 || p.D == 128); }
+// D = 256 runs 32-row chunks: one wave per 16-column tile (16 waves), 133 KB of LDS
+bool fused_supported(const ChunkParams &p) {
+  return p.is_bf16 && (p.D == 64 || p.D == 128 || (p.D == 256 && p.C == 32));
+}
 
 // Compute units of the current device (cached per device).
 int device_cus() {
@@ -246,7 +249,8 @@ hipError_t launch_fused_g(const ChunkParams &p, hipStream_t st) {
 
 template <int C, int D>
 hipError_t launch_fused_t(const ChunkParams &p0, hipStream_t st) {
-  constexpr int NT = (KDA_FUSED_THREADS > 0) ? KDA_FUSED_THREADS : ((D / 16 >= 8) ? 512 : 256);
+  // one wave per 16-column tile of w (and of the state)
+  constexpr int NT = (KDA_FUSED_THREADS > 0 && D <= 128) ? KDA_FUSED_THREADS : 4 * D;
   if (p0.N * p0.H == 0) return hipSuccess;
   // with fewer (sequence, head) pairs than compute units, split the value
   // columns so that the workgroups still cover the chip
@@ -271,6 +275,7 @@ hipError_t launch_fused(const ChunkParams &p, hipStream_t st) {
   if (p.C == 64 && p.D == 64) return launch_fused_t<64, 64>(p, st);
   if (p.C == 32 && p.D == 128) return launch_fused_t<32, 128>(p, st);
   if (p.C == 32 && p.D == 64) return launch_fused_t<32, 64>(p, st);
+  if (p.C == 32 && p.D == 256) return launch_fused_t<32, 256>(p, st);
   return hipErrorInvalidValue;
 }
 

@@ -357,6 +357,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_state_kernel(ChunkParams 
 // compute unit, and its state side ~3.3 us a chunk with one workgroup per
 // D / 64 value tiles a unit. The chain is the longest sequence in chunks (for
 // packed calls, bounded by the capacity T); items are the (chunk, head) pairs.
+bool split_supported(const ChunkParams &p) { return p.is_bf16 && (p.D == 64 || p.D == 128); }
+
 bool split_preferred(int64_t chain, int64_t pairs, int64_t items, int D) {
   const int64_t cus = device_cus();
   const double fused = 8.7 * chain * ((pairs + cus - 1) / cus);

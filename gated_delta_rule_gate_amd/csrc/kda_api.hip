@@ -243,8 +243,16 @@ bool auto_split(const kda_args *a) {
   return kda::split_preferred(chain, (int64_t)a->N * a->H, items, pad_width(std::max(a->K, a->V)));
 }
 
+// AUTO at tile width 256 with 64-row chunks: the fused kernel takes 32-row chunks
+// at this width (its LDS holds a 32-row chunk of 256 channels), which give the
+// same o and ht up to rounding; the chunk-start states keep the requested chunk.
+bool auto_fused_c32(const kda_args *a) {
+  return a->schedule == KDA_SCHED_AUTO && a->dtype == KDA_BF16 && a->chunk_size == 64 &&
+         pad_width(std::max(a->K, a->V)) == 256;
+}
+
 bool use_split(const kda_args *a, const kda::ChunkParams &p) {
-  if (!kda::fused_supported(p)) return false;
+  if (!kda::split_supported(p)) return false;
   return a->schedule == KDA_SCHED_SPLIT || (a->schedule == KDA_SCHED_AUTO && auto_split(a));
 }
 
@@ -254,7 +262,7 @@ bool use_split(const kda_args *a, const kda::ChunkParams &p) {
 bool use_pipe(const kda_args *a, const kda::ChunkParams &p) {
   if (!kda::pipe_supported(p)) return false;
   if (a->schedule == KDA_SCHED_PIPE) return true;
-  if (a->schedule != KDA_SCHED_AUTO && a->schedule != KDA_SCHED_FUSED) return false;
+  if (a->schedule != KDA_SCHED_AUTO) return false;  // an explicit schedule runs its own kernel
   return !use_split(a, p) && 2 * (int64_t)a->N * a->H > kda::device_cus();
 }
 
@@ -322,7 +330,8 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
   p.Hk = a->Hk > 0 ? a->Hk : a->H;
   p.beta_logits = a->beta_logits;
   p.max_chunks = (int)max_chunks(a, cu != nullptr);
-  if ((a->schedule == KDA_SCHED_FUSED || a->schedule == KDA_SCHED_SPLIT) && !kda::fused_supported(p))
+  if ((a->schedule == KDA_SCHED_FUSED && !kda::fused_supported(p)) ||
+      (a->schedule == KDA_SCHED_SPLIT && !kda::split_supported(p)))
     return KDA_ERR_UNSUPPORTED;
   if (a->schedule == KDA_SCHED_PIPE && !kda::pipe_supported(p)) return KDA_ERR_UNSUPPORTED;
   const size_t need = kda_chunk_workspace_bytes(a);
@@ -371,8 +380,8 @@ extern "C" size_t kda_chunk_workspace_bytes(const kda_args *a) {
   if (!chunk_shape_ok(a)) return 0;
   const kda::ChunkParams p = shape_params(a);
   if (a->schedule == KDA_SCHED_PIPE) return kda::pipe_supported(p) ? align_up(sizeof(int32_t) * (a->N + 1)) : 0;
-  if (a->schedule == KDA_SCHED_SPLIT) return kda::fused_supported(p) ? split_ws_bytes(a) : 0;
-  if (a->schedule == KDA_SCHED_AUTO && kda::fused_supported(p) && auto_split(a)) return split_ws_bytes(a);
+  if (a->schedule == KDA_SCHED_SPLIT) return kda::split_supported(p) ? split_ws_bytes(a) : 0;
+  if (a->schedule == KDA_SCHED_AUTO && kda::split_supported(p) && auto_split(a)) return split_ws_bytes(a);
   if (a->schedule != KDA_SCHED_STAGED && kda::fused_supported(p)) return align_up(sizeof(int32_t) * (a->N + 1));
   if (a->schedule == KDA_SCHED_FUSED) return 0;
   return staged_layout(a).total;
@@ -381,8 +390,11 @@ extern "C" size_t kda_chunk_workspace_bytes(const kda_args *a) {
 extern "C" int kda_chunk_schedule(const kda_args *a) {
   if (!chunk_shape_ok(a) || !schedule_known(a)) return -1;
   const kda::ChunkParams p = shape_params(a);
-  if ((a->schedule == KDA_SCHED_FUSED || a->schedule == KDA_SCHED_SPLIT) && !kda::fused_supported(p)) return -1;
+  if ((a->schedule == KDA_SCHED_FUSED && !kda::fused_supported(p)) ||
+      (a->schedule == KDA_SCHED_SPLIT && !kda::split_supported(p)))
+    return -1;
   if (a->schedule == KDA_SCHED_PIPE && !kda::pipe_supported(p)) return -1;
+  if (auto_fused_c32(a)) return KDA_SCHED_FUSED;
   if (use_pipe(a, p)) return KDA_SCHED_PIPE;
   if (use_split(a, p)) return KDA_SCHED_SPLIT;
   if (use_fused(a, p)) return KDA_SCHED_FUSED;
@@ -396,8 +408,16 @@ extern "C" size_t kda_staged_workspace_offset(const kda_args *a, kda_ws_field fi
 
 namespace {
 
-kda_status run_chunk(const kda_args *a, const kda::ChunkParams &p, hipStream_t st) {
+// states: the caller asked for the chunk-start states (they follow its chunk size)
+kda_status run_chunk(const kda_args *a, const kda::ChunkParams &p, hipStream_t st, bool states) {
   kda_status s;
+  if (auto_fused_c32(a) && !states) {
+    // the same o and ht as 64-row chunks, up to rounding, on chip
+    kda::ChunkParams q = p;
+    q.C = 32;
+    q.hc = nullptr;  // p.hc points into the staged layout of the workspace: no states here
+    return hip_status(kda::launch_fused(q, st));
+  }
   if (use_pipe(a, p)) {
     // the chunk prefix only numbers the chunk-start states
     if (p.hc && p.cu && (s = run_stage(p, KDA_STAGE_INDEX, st)) != KDA_OK) return s;
@@ -425,7 +445,7 @@ extern "C" kda_status kda_chunk_fwd(const kda_args *a, const void *q, const void
   kda::ChunkParams p;
   kda_status s = prepare_chunk(a, q, k, v, g, beta, h0, cu_seqlens, o, ht, workspace, ws_bytes, p);
   if (s != KDA_OK) return s;
-  return run_chunk(a, p, (hipStream_t)stream);
+  return run_chunk(a, p, (hipStream_t)stream, false);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -514,7 +534,7 @@ extern "C" kda_status kda_chunk_fwd_states(const kda_args *a, const void *q, con
   if (!h_states && kda_chunk_states_count(a, cu_seqlens != nullptr) > 0) return KDA_ERR_NULL;
   if (!aligned16(h_states)) return KDA_ERR_ALIGN;
   if (h_states) p.hc = h_states;  // the staged scan writes the chunk-start states here, not in the workspace
-  return run_chunk(a, p, (hipStream_t)stream);
+  return run_chunk(a, p, (hipStream_t)stream, h_states != nullptr);
 }
 
 extern "C" kda_status kda_chunk_stage(const kda_args *a, kda_stage stage, const void *q, const void *k,

@@ -111,6 +111,8 @@ bool fused_supported(const ChunkParams &p);
 bool pipe_supported(const ChunkParams &p);
 hipError_t launch_pipe(const ChunkParams &p, hipStream_t st);
 // split schedule: the key side of every chunk in parallel, then the state side
+// (bf16, D in {64, 128})
+bool split_supported(const ChunkParams &p);
 hipError_t launch_split(const ChunkParams &p, hipStream_t st);
 // workspace of the split schedule for chunk_heads (chunk, head) pairs: the bf16
 // records, then the fp32 ones

@@ -82,15 +82,19 @@ typedef enum {
 typedef enum {
   KDA_SCHED_AUTO = 0,   /* pick per shape                                                   */
   KDA_SCHED_STAGED = 1, /* six kernels, one per step, intermediates in the workspace        */
-  KDA_SCHED_FUSED = 2,  /* one persistent kernel per (sequence, head); state kept on chip   */
+  KDA_SCHED_FUSED = 2,  /* one persistent kernel per (sequence, head); state kept on chip.
+                           bf16, max(K, V) <= 128, or up to 256 with 32-row chunks; AUTO
+                           runs it at width 256 with 32-row chunks also when 64 are asked
+                           for (same o and ht up to rounding) unless the call returns the
+                           chunk-start states                                              */
   KDA_SCHED_SPLIT = 3,  /* steps (1)-(4) for every chunk at once, their operands through the
                            workspace, then one kernel per (sequence, head) for steps (5)-(6)
                            and the state; for few (sequence, head) pairs with long sequences */
   KDA_SCHED_PIPE = 4    /* the fused schedule's pipelined kernel (bf16, chunk 64, max(K, V) in
                            (64, 128], safe gate): per (sequence, head), four waves run steps
                            (1)-(4) of one chunk while four run steps (5)-(6) of the previous
-                           one. AUTO and FUSED run it where it applies and the (sequence, head)
-                           pairs fill the device                                              */
+                           one. AUTO runs it where it applies and the (sequence, head) pairs
+                           fill the device; KDA_SCHED_FUSED always runs the fused kernel      */
 } kda_schedule;
 
 typedef struct {
@@ -165,9 +169,10 @@ size_t kda_chunk_workspace_bytes(const kda_args *args);
 
 /*
  * The schedule kda_chunk_fwd runs for these arguments: KDA_SCHED_STAGED,
- * KDA_SCHED_FUSED or KDA_SCHED_SPLIT (what KDA_SCHED_AUTO resolves to on the
- * current device), or -1 when the arguments' sizes are invalid or the named
- * schedule does not take them (fused and split: bf16 with K, V <= 128).
+ * KDA_SCHED_FUSED, KDA_SCHED_SPLIT or KDA_SCHED_PIPE (what KDA_SCHED_AUTO
+ * resolves to on the current device), or -1 when the arguments' sizes are
+ * invalid or the named schedule does not take them (fused and split: bf16 with
+ * K, V <= 128; pipe: as listed at KDA_SCHED_PIPE).
  */
 int kda_chunk_schedule(const kda_args *args);
 

@@ -217,17 +217,21 @@ def test_resolved_schedule(kda_lib):
     assert sched(B=4, N=4, T=4096, H=64) == 2
     assert sched(B=2, N=2, T=16384, H=16) == 3
     assert sched(B=2, N=2, T=16384, H=16, dtype=1) == 1
-    assert sched(B=2, N=2, T=16384, H=16, K=256, V=256) == 1
+    assert sched(B=2, N=2, T=16384, H=16, K=256, V=256) == 2                   # fused at 32-row chunks
+    assert sched(B=2, N=2, T=16384, H=16, K=256, V=256, dtype=1) == 1          # fp32: staged
+    assert sched(B=2, N=2, T=16384, H=16, K=256, V=256, chunk_size=32, schedule=2) == 2
+    assert sched(B=2, N=2, T=16384, H=16, K=256, V=256, schedule=2) == -1      # named fused: 32-row chunks only
     assert sched(B=4, N=4, T=4096, H=64, schedule=3) == 3
     assert sched(B=2, N=2, T=16384, H=16, schedule=2) == 2
     assert sched(dtype=1, schedule=2) == -1
     assert sched(K=256, V=256, schedule=3) == -1
     assert sched(chunk_size=16) == -1
-    # the pipelined kernel (safe gate, bf16, chunk 64, tile 128): what AUTO and FUSED run
-    # for more (sequence, head) pairs than half the compute units; named, on any count
+    # the pipelined kernel (safe gate, bf16, chunk 64, tile 128): what AUTO runs for more
+    # (sequence, head) pairs than half the compute units; named, on any count; a named
+    # fused schedule runs the fused kernel
     safe = lambda **kw: kda_lib.kda_chunk_schedule(ctypes.byref(_args(gate_kind=1, **kw)))
     assert safe(B=4, N=4, T=4096, H=64) == 4
-    assert safe(B=4, N=4, T=4096, H=64, schedule=2) == 4
+    assert safe(B=4, N=4, T=4096, H=64, schedule=2) == 2
     assert safe(B=4, N=4, T=4096, H=64, K=96, V=72) == 4
     assert safe(B=1, N=1, T=300, H=2, schedule=4) == 4
     assert safe(B=1, N=1, T=300, H=2, schedule=2) == 2
