@@ -92,9 +92,25 @@ def measured_traffic(sched):
         return None
 
 
+def gpu_ramp(buf, seconds=0.3):
+    """Keeps the GPU busy with a plain fill kernel for about `seconds` before any
+    timing: from idle, the part needs on the order of 100 ms of load to reach its
+    working clock, and calls timed earlier run up to 15% slower. The fill is not
+    the measured step, touches none of its data, and the flush before every timed
+    call evicts what it leaves in the caches. (A bf16 matmul ramp measured slower.)"""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(64):
+            buf.zero_()
+        torch.cuda.synchronize()
+
+
 def event_time_ms(fn, steps, warmup, flush=None):
-    """Mean / median / p10 / p90 of per-call HIP event times (ms) on the current stream."""
+    """Mean / median / p10 / p90 of per-call HIP event times (ms) on the current stream.
+    Warm-up calls run with the same flush as the timed ones."""
     for _ in range(warmup):
+        if flush is not None:
+            flush()
         fn()
     torch.cuda.synchronize()
     times = []
@@ -438,6 +454,8 @@ def main():
                     help="also time the headline call's variants (q_l2norm, beta logits, states, GVA, widths, C=32, graph)")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed-batch and copy figures")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 64-token recurrent prefill figure")
+    ap.add_argument("--ramp-s", type=float, default=0.3,
+                    help="seconds of a plain fill kernel before the warm-up, to bring the GPU to its working clock")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -476,6 +494,7 @@ def main():
         torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
 
+    gpu_ramp(flush_buf, args.ramp_s)
     cold = event_time_ms(step, args.steps, args.warmup, flush=flush)
     warm = event_time_ms(step, max(5, args.steps // 2), 1)
     ms = cold["mean"]
