@@ -59,7 +59,8 @@ struct BlkSmem {
   static constexpr size_t lam = ak + 4 * kBT * kLA;  // 2^b_L [128]
   static constexpr size_t beta = lam + 4 * kBD;      // beta per block row [16]
   static constexpr size_t qn = beta + 4 * kBT;       // 1/sqrt(|q|^2 + eps) per block row [16]
-  static constexpr size_t total = qn + 4 * kBT;
+  static constexpr size_t flag = qn + 4 * kBT;       // out-of-range flag per block parity [2] (int)
+  static constexpr size_t total = flag + 16;
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -92,7 +93,7 @@ __device__ __forceinline__ f32x4_t mma16(s16x4_t a, s16x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-template <bool QN>
+template <bool QN, int GK>
 __global__ __launch_bounds__(kBThreads, 2) void recurrent_block_kernel(RecurrentParams p) {
   using M = Mma<bf16_t>;
   using S = BlkSmem;
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(kBThreads, 2) void recurrent_block_kernel(Recurrent
       }
     }
 
-  const bool gated = p.gate_kind == kGateSafe || p.gate_kind == kGateSoftplus;
+  constexpr bool gated = GK == kGateSafe || GK == kGateSoftplus;
   const float expA = gated ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
   const float dtc = p.dt_bias ? p.dt_bias[h * kBD + 64 * (w & 1) + (tid_opaque() & 63)] : 0.f;
 
@@ -187,6 +188,7 @@ __global__ __launch_bounds__(kBThreads, 2) void recurrent_block_kernel(Recurrent
       m = g0;
       bL = g0;
     }
+    const float tm = fast_exp2(m), tl = fast_exp2(bL - m);
     const bf16_t *rq = reinterpret_cast<const bf16_t *>(smem + S::rq);
     const bf16_t *rk = reinterpret_cast<const bf16_t *>(smem + S::rk);
     const bf16_t *rv = reinterpret_cast<const bf16_t *>(smem + S::rv);
@@ -207,10 +209,12 @@ __global__ __launch_bounds__(kBThreads, 2) void recurrent_block_kernel(Recurrent
       const float be = valid ? sb[row] : 0.f;
       // a block of one token has b = m = b_L: its only exponential is 2^b
       // (0 for a gate of -inf), the others are exactly 1
+      // with the range check passed, 2^b = 2^(b - m) 2^m and 2^(b_L - b) = 2^(m - b) 2^(b_L - m)
+      // with both factors finite
       const float br = b[j];
-      const float eb = fast_exp2(br);
       const float e1 = fast ? fast_exp2(br - m) : 1.f, e2 = fast ? fast_exp2(m - br) : 1.f;
-      const float el = fast ? fast_exp2(bL - br) : 1.f;
+      const float eb = fast ? e1 * tm : fast_exp2(br);
+      const float el = fast ? e2 * tl : 1.f;
       qd[rr * kLR + c] = static_cast<bf16_t>(valid ? q * e1 : 0.f);
       kd[rr * kLR + c] = static_cast<bf16_t>(valid ? k * e1 : 0.f);
       cd[rr * kLR + c] = static_cast<bf16_t>(valid ? k * e2 : 0.f);
@@ -331,11 +335,39 @@ __global__ __launch_bounds__(kBThreads, 2) void recurrent_block_kernel(Recurrent
   };
 
   const int nb = (sr.len + kBT - 1) / kBT;
-  if (nb > 0) fetch(0);
+  int *flags = reinterpret_cast<int *>(smem + S::flag);
+  // the next block's activated gate of channel c (log2 units), and whether any
+  // exponent of its anchored operands could leave range; the flag of block j
+  // is ORed into flags[j & 1] before a barrier that precedes its use
+  float gl[kBT];
+  auto gate_and_check = [&](int blk) {
+    const int L = min(kBT, sr.len - kBT * blk);
+#pragma unroll
+    for (int r = 0; r < kBT; ++r) gl[r] = (r < L) ? gate_log2(GK, pg[r], dtc, expA, p.lower_bound) : 0.f;
+    float acc = 0.f, b8 = 0.f, bmin = 0.f, bmax = 0.f;
+#pragma unroll
+    for (int r = 0; r < kBT; ++r) {
+      acc += gl[r];
+      if (r == 8) b8 = acc;
+      bmin = (r == 0) ? acc : fminf(bmin, acc);
+      bmax = (r == 0) ? acc : fmaxf(bmax, acc);
+    }
+    const float m = (L > 8) ? b8 : acc;
+    const bool bad = !(bmax - m <= kExpLimit && m - bmin <= kExpLimit && bmax <= kExpLimit &&
+                       acc - bmin <= kExpLimit && acc - m <= kExpLimit);
+    if (bad) atomicOr(flags + (blk & 1), 1);
+  };
+  if (tid_opaque() < 2) flags[tid_opaque()] = 0;
+  __syncthreads();
+  if (nb > 0) {
+    fetch(0);
+    wait_vmem();
+    gate_and_check(0);
+  }
   for (int blk = 0; blk < nb; ++blk) {
     const int64_t t0 = sr.t0 + (int64_t)kBT * blk;
     const int L = min(kBT, sr.len - kBT * blk);
-    // stage the raw block, activate the gate of channel c, start the next block's loads
+    // stage the raw block, start the next block's loads
     {
       const int t = tid_opaque();
       const int off = 2 * ((t >> 4) * kBD + (t & 15) * 8);
@@ -344,33 +376,29 @@ __global__ __launch_bounds__(kBThreads, 2) void recurrent_block_kernel(Recurrent
       *reinterpret_cast<u32x4_t *>(smem + S::rv + off) = pv;
       if (t < kBT) reinterpret_cast<float *>(smem + S::beta)[t] = (p.beta_logits && t < L) ? sigmoid_f32(pb) : pb;
     }
-    float gl[kBT];
+    float glc[kBT];
 #pragma unroll
-    for (int r = 0; r < kBT; ++r) gl[r] = (r < L) ? gate_log2(p.gate_kind, pg[r], dtc, expA, p.lower_bound) : 0.f;
+    for (int r = 0; r < kBT; ++r) glc[r] = gl[r];
     if (blk + 1 < nb) fetch(blk + 1);
-    // exponent range of the anchored operands over the whole block
-    bool bad = false;
-    {
-      float acc = 0.f, b8 = 0.f, bmin = 0.f, bmax = 0.f;
-#pragma unroll
-      for (int r = 0; r < kBT; ++r) {
-        acc += gl[r];
-        if (r == 8) b8 = acc;
-        bmin = (r == 0) ? acc : fminf(bmin, acc);
-        bmax = (r == 0) ? acc : fmaxf(bmax, acc);
-      }
-      const float m = (L > 8) ? b8 : acc;
-      bad = !(bmax - m <= kExpLimit && m - bmin <= kExpLimit && bmax <= kExpLimit && acc - bmin <= kExpLimit);
-    }
+    __syncthreads();  // the raw block and this block's flag are visible
     // the whole block at once, or (any exponent out of range) one token at a time
-    const bool fast = !__syncthreads_or(bad);
+    const bool fast = flags[blk & 1] == 0;
     const int Ls = fast ? L : 1;
     for (int r0 = 0; r0 < L; r0 += Ls) {
       if (w < 2)
-        operands(std::integral_constant<int, 0>{}, gl, fast, r0, Ls);
+        operands(std::integral_constant<int, 0>{}, glc, fast, r0, Ls);
       else
-        operands(std::integral_constant<int, 1>{}, gl, fast, r0, Ls);
+        operands(std::integral_constant<int, 1>{}, glc, fast, r0, Ls);
       __syncthreads();
+      if (r0 + Ls >= L) {
+        // last pass of the block: clear this block's flag for block + 2 and check
+        // the next block, both before the products' final barrier
+        if (tid_opaque() == 0) flags[blk & 1] = 0;
+        if (blk + 1 < nb) {
+          wait_vmem();
+          gate_and_check(blk + 1);
+        }
+      }
       products(t0 + r0, r0, Ls);
     }
   }
@@ -400,7 +428,18 @@ hipError_t launch_recurrent_block(const RecurrentParams &p, hipStream_t st) {
   const int grid = p.N * p.H;
   if (grid == 0) return hipSuccess;
   constexpr size_t smem = BlkSmem::total;
-  auto kern = p.q_l2norm ? recurrent_block_kernel<true> : recurrent_block_kernel<false>;
+  auto pick = [&](auto gk) {
+    constexpr int GK = decltype(gk)::value;
+    return p.q_l2norm ? recurrent_block_kernel<true, GK> : recurrent_block_kernel<false, GK>;
+  };
+  decltype(pick(std::integral_constant<int, kGateLog2>{})) kern;
+  switch (p.gate_kind) {
+    case kGateLog2: kern = pick(std::integral_constant<int, kGateLog2>{}); break;
+    case kGateLogE: kern = pick(std::integral_constant<int, kGateLogE>{}); break;
+    case kGateSafe: kern = pick(std::integral_constant<int, kGateSafe>{}); break;
+    case kGateSoftplus: kern = pick(std::integral_constant<int, kGateSoftplus>{}); break;
+    default: return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBThreads), smem, st, p);
   return hipGetLastError();
 }
