@@ -677,17 +677,25 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
       // token-parallel diagonal block over this wave's channels (before q is
       // overwritten), in the transposed layout: lane owns row r = 16i + n16 and
       // columns 16i + 4*grp + e
-      for (int kk = c0; kk < c0 + CW; ++kk) {
-        const float qr = static_cast<float>(sQ[r * ldt + kk]);
-        const float kr = static_cast<float>(sK[r * ldt + kk]);
-        const float br = sB[r * ldb + kk];
+      // columns, four channels per step (vector LDS reads; the sums keep the
+      // channel order)
+      for (int kk = c0; kk < c0 + CW; kk += 4) {
+        const bf16x4_t q4 = *reinterpret_cast<const bf16x4_t *>(sQ + r * ldt + kk);
+        const bf16x4_t k4 = *reinterpret_cast<const bf16x4_t *>(sK + r * ldt + kk);
+        const f32x4_t b4 = *reinterpret_cast<const f32x4_t *>(sB + r * ldb + kk);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int sc = 16 * i + 4 * grp + e;
-          const float f = (r >= sc) ? fast_exp2(br - sB[sc * ldb + kk]) : 0.f;
-          const float kf = static_cast<float>(sK[sc * ldt + kk]) * f;
-          accQ[i][e] += qr * kf;
-          accK[i][e] += kr * kf;
+          const f32x4_t bc = *reinterpret_cast<const f32x4_t *>(sB + sc * ldb + kk);
+          const bf16x4_t kc = *reinterpret_cast<const bf16x4_t *>(sK + sc * ldt + kk);
+          const bool on = r >= sc;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float f = on ? fast_exp2(b4[u] - bc[u]) : 0.f;
+            const float kf = static_cast<float>(kc[u]) * f;
+            accQ[i][e] += static_cast<float>(q4[u]) * kf;
+            accK[i][e] += static_cast<float>(k4[u]) * kf;
+          }
         }
       }
     }
