@@ -113,8 +113,12 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   constexpr bool HALF_LOAD = (NW / NC >= 2);
   constexpr int NL = HALF_LOAD ? NT / 2 : NT;
   const bool loader = !HALF_LOAD || gram_half<NW, NC>(wid) == 0;
+  // the next chunk's raw inputs wait in registers while a chunk computes; at
+  // D = 256 (16 waves, 128 VGPRs each, half of them the state strip) those
+  // registers would spill, so each chunk loads its own inputs at its start
+  constexpr bool PREFETCH = D <= 128;
   ChunkRegs<Tin, C, D, NT, NL> regs;
-  if (nch > 0) {
+  if (PREFETCH && nch > 0) {
     regs.load_gate(p, sr.t0, min(C, sr.len), h);
     if (loader) regs.load_qkv(p, sr.t0, min(C, sr.len), h);
   }
@@ -128,6 +132,10 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     const int L = min(C, sr.len - c * C);
     const int64_t off = t0 * ld + h * Vr;
     float *sDecay = sDecay2 + (c & 1) * D;
+    if constexpr (!PREFETCH) {
+      regs.load_gate(p, t0, L, h);
+      if (loader) regs.load_qkv(p, t0, L, h);
+    }
     regs.template store<GK>(loader, sQ, sK, sV, sB, sBeta, sDt, L, expA, p.lower_bound, p.q_l2norm != 0, sQn,
                             p.beta_logits != 0);
     if (hcs && owner) store_strip<float, DT, NVW>(hcs + (int64_t)c * p.H * Kr * Vr, Vr, col0, Kr, hs, Vr);
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     // the next chunk's inputs are loaded in two parts while this chunk computes:
     // the gate by every wave as it finishes the grams' first phase (the waves get
     // there at different times, so their loads do not queue at once), then q, k, v
-    const bool more = c + 1 < nch;
+    const bool more = PREFETCH && c + 1 < nch;
     const int Ln = more ? min(C, sr.len - (c + 1) * C) : 0;
 
     // (1)
