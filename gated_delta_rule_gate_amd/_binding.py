@@ -29,7 +29,8 @@ class KdaArgs(ctypes.Structure):
                 ("V", ctypes.c_int), ("N", ctypes.c_int), ("chunk_size", ctypes.c_int), ("dtype", ctypes.c_int),
                 ("scale", ctypes.c_float), ("gate_kind", ctypes.c_int), ("A_log", ctypes.c_void_p),
                 ("dt_bias", ctypes.c_void_p), ("lower_bound", ctypes.c_float), ("schedule", ctypes.c_int),
-                ("Hk", ctypes.c_int), ("q_l2norm", ctypes.c_int), ("beta_logits", ctypes.c_int)]
+                ("Hk", ctypes.c_int), ("q_l2norm", ctypes.c_int), ("beta_logits", ctypes.c_int),
+                ("segment", ctypes.c_int)]
 
 
 def lib():
@@ -53,6 +54,8 @@ def lib():
             L.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
             L.kda_chunk_schedule.argtypes = [ap]
             L.kda_chunk_schedule.restype = ctypes.c_int
+            L.kda_chunk_segment.argtypes = [ap]
+            L.kda_chunk_segment.restype = ctypes.c_int
             L.kda_check_offsets.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp]
             L.kda_check_offsets.restype = ctypes.c_int
             L.kda_chunk_fwd.argtypes = [ap] + [vp] * 10 + [ctypes.c_size_t, vp]
@@ -114,7 +117,7 @@ def _check_tensors(named, device):
 
 
 def make_args(q, v, H, N, gate_kind, chunk_size=64, scale=None, A_log=None, dt_bias=None, lower_bound=-5.0,
-              schedule="auto", q_l2norm=False, beta_logits=False):
+              schedule="auto", q_l2norm=False, beta_logits=False, segment=0):
     B, T, Hk, K = q.shape
     V = v.shape[-1]
     a = KdaArgs()
@@ -130,6 +133,7 @@ def make_args(q, v, H, N, gate_kind, chunk_size=64, scale=None, A_log=None, dt_b
     a.schedule = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
     a.q_l2norm = 1 if q_l2norm else 0
     a.beta_logits = 1 if beta_logits else 0
+    a.segment = int(segment)
     return a
 
 
@@ -224,7 +228,7 @@ def gate_cumsum(g, *, chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None,
 def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_final_state=False,
               chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None,
               schedule="auto", final_state=None, out=None, q_l2norm=False, return_intermediate_states=False,
-              intermediate_states=None, beta_logits=False):
+              intermediate_states=None, beta_logits=False, segment=0):
     """Chunked KDA prefill forward. Returns (o, ht); ht is None unless requested.
 
     g is the raw gate input for ``gate_kind`` "safe" / "softplus" (activation in
@@ -239,6 +243,10 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
     [1, ceil(T / C) + N, H, K, V] for a packed one, whose chunks are numbered slot
     by slot (slot n starts at the sum of ceil(len_m / C) over m < n; entries past
     the last chunk are left as they are). ``intermediate_states`` may preallocate it.
+
+    ``segment`` (split schedule): chunks per segment of the chain-parallel state
+    scan; 0 lets the library choose from the sizes, -1 keeps one serial chain per
+    (sequence, head). The states path always runs the serial chain.
     """
     B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
     _check_outputs(out, final_state, B, T, H, K, V, N, q.dtype, q.device)
@@ -247,7 +255,8 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
     if ht is None and output_final_state:
         ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
     a = make_args(q, v, H, N, gate_kind, chunk_size=chunk_size, scale=scale, A_log=A_log, dt_bias=dt_bias,
-                  lower_bound=lower_bound, schedule=schedule, q_l2norm=q_l2norm, beta_logits=beta_logits)
+                  lower_bound=lower_bound, schedule=schedule, q_l2norm=q_l2norm, beta_logits=beta_logits,
+                  segment=segment)
     L = lib()
     ws_bytes = L.kda_chunk_workspace_bytes(ctypes.byref(a))
     ws = torch.empty((max(int(ws_bytes), 256),), dtype=torch.uint8, device=q.device)
@@ -272,7 +281,7 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
 
 def chunk_kda_noalloc(q, k, v, g, beta, initial_state=None, *, out, final_state=None, cu_seqlens=None,
                       chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None,
-                      schedule="auto", q_l2norm=False, beta_logits=False):
+                      schedule="auto", q_l2norm=False, beta_logits=False, segment=0):
     """``chunk_kda`` through kda_chunk_fwd_noalloc, which allocates nothing: the
     intermediates live in the library's static device array. The caller passes the
     output ``out`` (and ``final_state`` to receive the final state); this wrapper
@@ -281,7 +290,8 @@ def chunk_kda_noalloc(q, k, v, g, beta, initial_state=None, *, out, final_state=
     _require(out is not None, "out must be preallocated")
     _check_outputs(out, final_state, B, T, H, K, V, N, q.dtype, q.device)
     a = make_args(q, v, H, N, gate_kind, chunk_size=chunk_size, scale=scale, A_log=A_log, dt_bias=dt_bias,
-                  lower_bound=lower_bound, schedule=schedule, q_l2norm=q_l2norm, beta_logits=beta_logits)
+                  lower_bound=lower_bound, schedule=schedule, q_l2norm=q_l2norm, beta_logits=beta_logits,
+                  segment=segment)
     check(lib().kda_chunk_fwd_noalloc(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                       _ptr(initial_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
                                       _stream()))
@@ -322,8 +332,8 @@ def chunk_kda_bwd(q, k, v, g, beta, do, initial_state=None, *, dht=None, cu_seql
     return out
 
 
-def workspace_bytes(q, v, H, N, chunk_size=64, schedule="auto"):
-    a = make_args(q, v, H, N, "safe", chunk_size=chunk_size, schedule=schedule)
+def workspace_bytes(q, v, H, N, chunk_size=64, schedule="auto", segment=0):
+    a = make_args(q, v, H, N, "safe", chunk_size=chunk_size, schedule=schedule, segment=segment)
     return int(lib().kda_chunk_workspace_bytes(ctypes.byref(a)))
 
 
@@ -345,6 +355,13 @@ def resolved_schedule(q, v, H, N, chunk_size=64, schedule="auto"):
     a = make_args(q, v, H, N, "safe", chunk_size=chunk_size, schedule=schedule)
     r = int(lib().kda_chunk_schedule(ctypes.byref(a)))
     return {v_: k for k, v_ in SCHEDULES.items()}.get(r)
+
+
+def resolved_segment(q, v, H, N, chunk_size=64, schedule="auto", segment=0):
+    """Chunks per segment of the split schedule's state scan for these sizes (0: one
+    serial chain per (sequence, head), or not the split schedule)."""
+    a = make_args(q, v, H, N, "safe", chunk_size=chunk_size, schedule=schedule, segment=segment)
+    return int(lib().kda_chunk_segment(ctypes.byref(a)))
 
 
 STAGES = {"index": 0, "gate": 1, "grams": 2, "solve": 3, "wy": 4, "scan": 5, "output": 6}

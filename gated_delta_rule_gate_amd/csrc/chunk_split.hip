@@ -350,6 +350,357 @@ __global__ __launch_bounds__(kSplitThreads) void split_state_kernel(ChunkParams 
   if (owner && p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, Vr, col0, Kr, hs, Vr);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Chain-parallel state side. One chunk's state map is affine in the incoming
+// state, h' = (Diag(2^b_L) - k~^T w) h + k~^T u, so a run of chunks maps
+// h_out = M h_in + B; the run's outputs are affine in h_in as well,
+// o = o_local + E h_in, where E is what the output step makes of the columns of
+// M (q~ M - A_qk w M per chunk, with the row scales). A sequence's chunks are
+// cut into segments of seg_len chunks. Its first segment runs from h0 and
+// writes o itself; every later one runs the state side over 2D columns: D from
+// the identity with u = 0 (M, and E per chunk) and the value columns from zero
+// (B, and o_local per chunk). The segments run side by side; a combine pass
+// then chains their maps, h_in(s + 1) = M_s h_in(s) + B_s, in fp32, and a
+// correction pass adds E h_in to o_local for every chunk after the first
+// segment, all chunks at once. Channels >= Kr stay exact: their columns of M
+// only decay (k~, q~ and w vanish there) and the states' rows there are zero.
+// ---------------------------------------------------------------------------------------------
+
+struct SegLoc {
+  int n, s, nseg;  // slot, segment within the slot, segments of the slot
+  int c0, c1;      // chunks [c0, c1) of the slot
+  int gs0;         // global index of the slot's first segment
+};
+
+__device__ __forceinline__ int dense_segments(const ChunkParams &p) {
+  const int nt = (p.T + p.C - 1) / p.C;
+  return max(1, (nt + p.seg_len - 1) / p.seg_len);
+}
+
+// Maps a global segment index to its slot and chunk range (false past the last).
+__device__ __forceinline__ bool locate_segment(const ChunkParams &p, int gs, SegLoc &sl) {
+  int nch;
+  if (!p.cu) {
+    const int ns = dense_segments(p);
+    if (gs >= p.B * ns) return false;
+    sl.n = gs / ns;
+    sl.nseg = ns;
+    sl.gs0 = sl.n * ns;
+    nch = (p.T + p.C - 1) / p.C;
+  } else {
+    if (gs >= p.seg_off[p.N]) return false;
+    int lo = 0, hi = p.N;  // largest n with seg_off[n] <= gs (every slot has a segment)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.seg_off[mid] <= gs) lo = mid;
+      else hi = mid;
+    }
+    sl.n = lo;
+    sl.gs0 = p.seg_off[lo];
+    sl.nseg = p.seg_off[lo + 1] - sl.gs0;
+    nch = p.chunk_off[lo + 1] - p.chunk_off[lo];
+  }
+  sl.s = gs - sl.gs0;
+  sl.c0 = sl.s * p.seg_len;
+  sl.c1 = min(sl.c0 + p.seg_len, nch);
+  return true;
+}
+
+// One (segment, head, block of four 16-column tiles) of the 2D columns [M | B]:
+// the walk of split_state_kernel over the segment's chunks, from the identity
+// (M tiles, u = 0), from zero (B tiles) or from h0 (the first segment, which
+// has B tiles only and writes o). Two workgroups fit a compute unit.
+template <int C, int D>
+__global__ __launch_bounds__(kSplitThreads, 2) void split_seg_kernel(ChunkParams p) {
+  using Tin = bf16_t;
+  using TL = Tile<Tin, C, D>;
+  using S = SplitSmem<C, D>;
+  constexpr int NT = kSplitThreads, NC = TL::NC, DT = TL::DT, LDT = TL::LDT;
+  constexpr int NVW = 1, NB = 2 * (D / 64);
+  static_assert(S::total <= 65536, "DS immediate offsets");
+  extern __shared__ __align__(16) char smem[];
+  Tin *sQ = reinterpret_cast<Tin *>(smem + S::q);
+  Tin *sKt = reinterpret_cast<Tin *>(smem + S::kt);
+  Tin *sWT = reinterpret_cast<Tin *>(smem + S::wt);
+  Tin *sAqh = reinterpret_cast<Tin *>(smem + S::aqh);
+  float *sDecay2 = reinterpret_cast<float *>(smem + S::decay);
+  float *sQn = reinterpret_cast<float *>(smem + S::qn);
+
+  // the NB workgroups of one (segment, head) share an XCD and its L2
+  const int G = p.seg_max * p.H * NB;
+  const int bid = blockIdx.x;
+  const int li = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int cb = li % NB, gh = li / NB;
+  const int h = gh % p.H, gs = gh / p.H;
+  SegLoc sg;
+  if (!locate_segment(p, gs, sg)) return;
+  const bool isM = cb < D / 64;
+  if (isM && sg.s == 0) return;
+  const int wid = wave_id();
+  const int ctu = (isM ? cb : cb - D / 64) * 4 + wid;
+  const int col0 = ctu * 16;
+  const bool owner = isM || col0 < p.Vr;
+  const int Kr = p.Kr, Vr = p.Vr, n = sg.n;
+  const SlotRange sr = slot_range(p.cu, n, p.T);
+  const int cbase = p.cu ? p.chunk_off[n] : n * ((p.T + C - 1) / C);
+  const int64_t ld = (int64_t)p.H * Vr;
+  const int64_t sbase = ((int64_t)n * p.H + h) * Kr * Vr;
+  const int lane = tid_opaque() & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+
+  SplitRegs<C, D, NT> R;
+  if (sg.c0 < sg.c1) R.load(p, (int64_t)(cbase + sg.c0) * p.H + h, ctu, owner && !isM);
+  f32x4_t hs[DT][NVW];
+  if (isM) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hs[t][0][e] = (16 * t + 4 * grp + e == col0 + n16) ? 1.f : 0.f;
+  } else if (sg.s == 0 && p.h0 && owner) {
+    load_strip<DT, NVW>(hs, p.h0 + sbase, Vr, col0, Kr, Vr);
+  } else {
+#pragma unroll
+    for (int t = 0; t < DT; ++t) hs[t][0] = zero4();
+  }
+  bf16x8_t vprev[NC / 2][NVW];
+#pragma unroll
+  for (int s2 = 0; s2 < NC / 2; ++s2) vprev[s2][0] = bf16x8_t{};
+  // the first chunk's "previous" update is the identity: decay 1, k~ = 0
+  for (int i = tid_opaque(); i < D; i += NT) sDecay2[((sg.c0 + 1) & 1) * D + i] = 1.f;
+  for (int i = tid_opaque(); i < C * LDT / 8; i += NT) reinterpret_cast<u32x4_t *>(sKt)[i] = u32x4_t{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  for (int c = sg.c0; c < sg.c1; ++c) {
+    const int64_t t0 = sr.t0 + (int64_t)c * C;
+    const int L = min(C, sr.len - c * C);
+    const int64_t gch = (int64_t)(cbase + c) * p.H + h;
+    // chunk c - 1's state update
+    if (owner) state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((c + 1) & 1) * D);
+    __syncthreads();  // every wave is done with chunk c - 1's operands
+    R.store(sQ, sKt, sWT, sAqh, LDT, S::LDW, S::LDAH, sDecay2 + (c & 1) * D, sQn, p.q_l2norm != 0);
+    f32x4_t uv[NC][NVW];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) uv[i][0] = isM ? zero4() : R.u[i];
+    __syncthreads();
+    if (c + 1 < sg.c1) R.load(p, gch + p.H, ctu, owner && !isM);
+    if (owner) {
+      f32x4_t p1[NC][NVW], o[NC][NVW];
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        p1[i][0] = zero4();
+        o[i][0] = zero4();
+      }
+      q_times_state<C, D, NVW>(o, sQ, LDT, hs);
+      w_times_state<C, D, NVW>(p1, sWT, S::LDW, hs);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) uv[i][0] = uv[i][0] - p1[i][0];
+      causal_times_h<C, NVW>(o, sAqh, S::LDAH, uv);
+      vnew_frags<C, NVW>(vprev, uv);
+      if (p.q_l2norm) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) o[i][0] = o[i][0] * sQn[16 * i + n16];
+      }
+      if (sg.s == 0) {
+        store_oT<C, NVW>(reinterpret_cast<Tin *>(p.o) + t0 * ld + h * Vr, ld, col0, L, o, Vr);
+      } else if (isM) {
+        // E rows with the channels of each 32-block in the operand order of q~
+        // (the lane's channels 4g.., 16 + 4g.. of the block side by side at 8g)
+        Tin *E = static_cast<Tin *>(p.seg_e) + gch * C * D + 32 * (ctu >> 1) + 8 * grp + 4 * (ctu & 1);
+#pragma unroll
+        for (int i = 0; i < NC; ++i) *reinterpret_cast<bf16x4_t *>(E + (16 * i + n16) * D) = to_bf16x4(o[i][0]);
+      } else {
+        float *OL = p.seg_ol + gch * C * D + col0 + 4 * grp;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) *reinterpret_cast<f32x4_t *>(OL + (16 * i + n16) * D) = o[i][0];
+      }
+    }
+  }
+  if (sg.c1 > sg.c0 && owner) state_update_kt<C, D, NVW>(hs, sKt, LDT, vprev, sDecay2 + ((sg.c1 - 1) & 1) * D);
+  if (sg.nseg == 1) {
+    if (owner && p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, Vr, col0, Kr, hs, Vr);
+  } else if (owner) {
+    float *mb = p.seg_mb + ((int64_t)gs * p.H + h) * (int64_t)D * (2 * D);
+    store_strip<float, DT, NVW>(mb, 2 * D, (isM ? 0 : D) + col0, D, hs);
+  }
+}
+
+// The segments' incoming states, h_in(s + 1) = M_s h_in(s) + B_s with h_in(1) =
+// B_0, in fp32, and the final state. One workgroup per (slot, head, 16-column
+// tile): wave w forms row tiles w*DT/4.. of the next state with 16x16x4 fp32
+// products (a C-layout state tile is the B operand as it stands, contraction
+// index of step (t, e) at rows 16t + 4g + e), and the whole strip goes through
+// LDS to every wave for the next step. Each h_in(s) also goes out as the bf16
+// operand fragments of the correction's product.
+template <int D>
+__global__ __launch_bounds__(256) void seg_combine_kernel(ChunkParams p) {
+  constexpr int DT = D / 16, SD = D / 32, IW = DT / 4, LDS_ = 20;
+  constexpr int64_t MBS = (int64_t)D * 2 * D;
+  __shared__ __align__(16) float sS[2][D * LDS_];
+  const int bid = blockIdx.x;
+  const int ctu = bid % DT, nh = bid / DT;
+  const int n = nh / p.H, h = nh % p.H;
+  int gs0, nseg;
+  if (p.cu) {
+    gs0 = p.seg_off[n];
+    nseg = p.seg_off[n + 1] - gs0;
+  } else {
+    nseg = dense_segments(p);
+    gs0 = n * nseg;
+  }
+  const int col0 = 16 * ctu;
+  if (nseg <= 1 || col0 >= p.Vr) return;  // uniform over the workgroup
+  const int w = wave_id(), lane = tid_opaque() & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+  const float *mb0 = p.seg_mb + ((int64_t)gs0 * p.H + h) * MBS;
+  f32x4_t acc[IW];
+  // B_0 rows of this wave's tiles
+#pragma unroll
+  for (int i = 0; i < IW; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[i][e] = mb0[(int64_t)(16 * (w * IW + i) + 4 * grp + e) * (2 * D) + D + col0 + n16];
+  int cur = 0;
+#pragma unroll
+  for (int i = 0; i < IW; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sS[0][(16 * (w * IW + i) + 4 * grp + e) * LDS_ + n16] = acc[i][e];
+  __syncthreads();
+  for (int s = 1; s < nseg; ++s) {
+    const int64_t gsh = (int64_t)(gs0 + s) * p.H + h;
+    const float *S = sS[cur];
+    // h_in(s) as bf16 fragments: k-step j holds rows 32j + 4g + e and 32j + 16 + 4g + e
+    for (int j = w; j < SD; j += 4) {
+      u32x4_t f;
+      f[0] = pack_bf16x2(S[(32 * j + 4 * grp) * LDS_ + n16], S[(32 * j + 4 * grp + 1) * LDS_ + n16]);
+      f[1] = pack_bf16x2(S[(32 * j + 4 * grp + 2) * LDS_ + n16], S[(32 * j + 4 * grp + 3) * LDS_ + n16]);
+      f[2] = pack_bf16x2(S[(32 * j + 16 + 4 * grp) * LDS_ + n16], S[(32 * j + 16 + 4 * grp + 1) * LDS_ + n16]);
+      f[3] = pack_bf16x2(S[(32 * j + 16 + 4 * grp + 2) * LDS_ + n16], S[(32 * j + 16 + 4 * grp + 3) * LDS_ + n16]);
+      static_cast<u32x4_t *>(p.seg_sin)[((gsh * DT + ctu) * SD + j) * 64 + lane] = f;
+    }
+    const float *mb = p.seg_mb + gsh * MBS;
+    // two accumulators per row tile (even and odd contraction tiles) keep the
+    // dependent products apart
+    f32x4_t a2[IW][2];
+#pragma unroll
+    for (int i = 0; i < IW; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a2[i][0][e] = mb[(int64_t)(16 * (w * IW + i) + 4 * grp + e) * (2 * D) + D + col0 + n16];
+      a2[i][1] = zero4();
+    }
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      f32x4_t a[IW];
+#pragma unroll
+      for (int i = 0; i < IW; ++i)
+        a[i] = *reinterpret_cast<const f32x4_t *>(mb + (int64_t)(16 * (w * IW + i) + n16) * (2 * D) + 16 * t + 4 * grp);
+      f32x4_t b;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = S[(16 * t + 4 * grp + e) * LDS_ + n16];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < IW; ++i) a2[i][t & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][e], b[e], a2[i][t & 1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < IW; ++i) acc[i] = a2[i][0] + a2[i][1];
+#pragma unroll
+    for (int i = 0; i < IW; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sS[cur ^ 1][(16 * (w * IW + i) + 4 * grp + e) * LDS_ + n16] = acc[i][e];
+    __syncthreads();
+    cur ^= 1;
+  }
+  if (p.ht) {
+    float *ht = p.ht + (int64_t)nh * p.Kr * p.Vr;
+#pragma unroll
+    for (int i = 0; i < IW; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * (w * IW + i) + 4 * grp + e, c = col0 + n16;
+        if (r < p.Kr && c < p.Vr) ht[(int64_t)r * p.Vr + c] = acc[i][e];
+      }
+  }
+}
+
+// Chunks per workgroup of the correction: they share one load of h_in.
+constexpr int kCorrChunks = 8;
+
+// o = o_local + E h_in for every chunk after its sequence's first segment: one
+// workgroup of D/16 waves (one 16-column tile each) per (segment, head,
+// kCorrChunks chunks). h_in's fragments are loaded once; each chunk's E is
+// staged in LDS for all waves, and the next chunk's E and o_local are in flight
+// while a chunk computes.
+template <int C, int D>
+__global__ __launch_bounds__(4 * D) void seg_correct_kernel(ChunkParams p) {
+  using M = Mma<bf16_t>;
+  constexpr int NT = 4 * D, NC = C / 16, DT = D / 16, SD = D / 32, LDE = D + 8;
+  constexpr int EV = C * D / 8, EI = EV / NT;  // 16-byte vectors of E per chunk, per thread
+  static_assert(EV % NT == 0, "whole vectors per thread");
+  __shared__ __align__(16) bf16_t sE[C * LDE];
+  const int NGR = (p.seg_len + kCorrChunks - 1) / kCorrChunks;
+  const int64_t G = (int64_t)p.seg_max * p.H * NGR;
+  const int64_t bid = blockIdx.x;
+  const int64_t li = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int gr = (int)(li % NGR);
+  const int64_t gh = li / NGR;
+  const int h = (int)(gh % p.H), gs = (int)(gh / p.H);
+  SegLoc sg;
+  if (!locate_segment(p, gs, sg) || sg.s == 0) return;
+  const int ca = sg.c0 + gr * kCorrChunks, cz = min(ca + kCorrChunks, sg.c1);
+  if (ca >= cz) return;  // uniform over the workgroup
+  const int ctu = wave_id(), col0 = 16 * ctu, t = tid_opaque();
+  const bool owner = col0 < p.Vr;
+  const int lane = t & 63;
+  const int n16 = lane & 15, grp = lane >> 4;
+  const int64_t gsh = (int64_t)gs * p.H + h;
+  bf16x8_t fh[SD];
+#pragma unroll
+  for (int j = 0; j < SD; ++j)
+    fh[j] = owner ? __builtin_bit_cast(bf16x8_t, static_cast<const u32x4_t *>(p.seg_sin)[((gsh * DT + ctu) * SD + j) * 64 + lane])
+                  : bf16x8_t{};
+  const SlotRange sr = slot_range(p.cu, sg.n, p.T);
+  const int cbase = p.cu ? p.chunk_off[sg.n] : sg.n * ((p.T + C - 1) / C);
+  const int64_t ld = (int64_t)p.H * p.Vr;
+  u32x4_t ev[EI];
+  f32x4_t ol[NC];
+  auto fetch = [&](int c) {
+    const int64_t gch = (int64_t)(cbase + c) * p.H + h;
+    const u32x4_t *E = reinterpret_cast<const u32x4_t *>(static_cast<const bf16_t *>(p.seg_e) + gch * C * D);
+#pragma unroll
+    for (int i = 0; i < EI; ++i) ev[i] = E[i * NT + t];
+    if (owner) {
+      const float *OL = p.seg_ol + gch * C * D + col0 + 4 * grp;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) ol[i] = *reinterpret_cast<const f32x4_t *>(OL + (16 * i + n16) * D);
+    }
+  };
+  fetch(ca);
+  for (int c = ca; c < cz; ++c) {
+    __syncthreads();  // the previous chunk's reads of sE are done
+#pragma unroll
+    for (int i = 0; i < EI; ++i) {
+      const int v = i * NT + t;
+      *reinterpret_cast<u32x4_t *>(sE + (v / (D / 8)) * LDE + (v % (D / 8)) * 8) = ev[i];
+    }
+    f32x4_t o[NC][1];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) o[i][0] = ol[i];
+    __syncthreads();
+    if (c + 1 < cz) fetch(c + 1);
+    if (owner) {
+      const bf16_t *eRow = sE + n16 * LDE + 8 * grp;
+#pragma unroll
+      for (int j = 0; j < SD; ++j)
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const bf16x8_t fq = *reinterpret_cast<const bf16x8_t *>(eRow + 16 * i * LDE + 32 * j);
+          o[i][0] = M::mma(fh[j], fq, o[i][0]);
+        }
+      const int64_t t0 = sr.t0 + (int64_t)c * C;
+      store_oT<C, 1>(reinterpret_cast<bf16_t *>(p.o) + t0 * ld + h * p.Vr, ld, col0, min(C, sr.len - c * C), o, p.Vr);
+    }
+  }
+}
+
 // Whether the split schedule is expected to beat the fused one, from a cost
 // model of the two measured on MI355X (C = 64, D = 128, safe gate): the fused
 // kernel walks each (sequence, head)'s chunks at ~8.7 us a chunk, one pair per
@@ -365,6 +716,45 @@ bool split_preferred(int64_t chain, int64_t pairs, int64_t items, int D) {
   const int64_t wgs = pairs * (D / 64);
   const double split = 11.0 * ((items + cus - 1) / cus) + 3.3 * chain * ((wgs + cus - 1) / cus);
   return split < 0.9 * fused;
+}
+
+// The segment length from a cost model of the state side measured on MI355X
+// (C = 64, D = 128): the serial chain takes ~3.4 us a chunk with one workgroup
+// per compute unit; the segment walk ~5.9 us a chunk per round of two
+// workgroups per compute unit; the combine ~8 us plus ~4 us a step; the
+// correction ~18 ns per (chunk, head) after the first segment. Segments double
+// the state side's work past the first, so they pay only where the serial chain
+// leaves most compute units idle (few pairs, long sequences).
+int split_segment_len(int64_t chain, int64_t pairs, int D, int C) {
+  (void)C;
+  if (chain < 8 || pairs <= 0) return 0;
+  const int64_t cus = device_cus(), nb = D / 64;
+  const double serial = 3.4 * chain * ((pairs * nb + cus - 1) / cus);
+  double best = 0.9 * serial;
+  int best_len = 0;
+  for (int64_t P = 2; P <= 64; P *= 2) {
+    const int64_t len = (chain + P - 1) / P;
+    if (len < 4) break;
+    const int64_t ns = (chain + len - 1) / len;
+    const int64_t wgs = pairs * nb * (2 * ns - 1);
+    const double t = 5.9 * len * ((wgs + 2 * cus - 1) / (2 * cus)) + 8.0 + 4.0 * (ns - 1) + 5.0 +
+                     0.018 * pairs * (chain - len);
+    if (t < best) {
+      best = t;
+      best_len = (int)len;
+    }
+  }
+  return best_len;
+}
+
+int64_t split_segment_bound(int B, int N, int64_t nt, bool packed, int seg_len) {
+  if (seg_len <= 0) return 0;
+  if (packed) return (int64_t)N + (nt + N + seg_len - 1) / seg_len;
+  return (int64_t)B * std::max<int64_t>(1, (nt + seg_len - 1) / seg_len);
+}
+
+size_t split_segment_bytes(int C, int D, int64_t chunk_heads, int64_t seg_heads) {
+  return (size_t)chunk_heads * C * D * (2 + 4) + (size_t)seg_heads * D * D * (2 * 4 + 2);
 }
 
 namespace {
@@ -388,6 +778,21 @@ hipError_t launch_split_g(const ChunkParams &p, hipStream_t st) {
   }
   if (p.N * p.H == 0) return hipSuccess;
   constexpr size_t smem2 = SplitSmem<C, D>::total;
+  if (p.seg_len > 0) {
+    // segments side by side, then the combine chain, then the correction
+    const int64_t G = (int64_t)p.seg_max * p.H * (2 * D / 64);
+    if (G > 0) {
+      hipLaunchKernelGGL((split_seg_kernel<C, D>), dim3(G), dim3(kSplitThreads), smem2, st, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((seg_combine_kernel<D>), dim3(p.N * p.H * (D / 16)), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || G == 0) return e;
+    const int64_t G2 = (int64_t)p.seg_max * p.H * ((p.seg_len + kCorrChunks - 1) / kCorrChunks);
+    hipLaunchKernelGGL((seg_correct_kernel<C, D>), dim3(G2), dim3(4 * D), 0, st, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((split_state_kernel<C, D>), dim3(p.N * p.H * (D / 64)), dim3(kSplitThreads), smem2, st, p);
   return hipGetLastError();
 }

@@ -38,29 +38,42 @@ __device__ __forceinline__ void store_rows_f32(float *g, int64_t ldg, const floa
 
 }  // namespace
 
-// ---- chunk index: chunk_off[n] = sum_{m<n} ceil(len_m / C) ----
-__global__ __launch_bounds__(256) void chunk_index_kernel(const int32_t *cu, int N, int C, int32_t *off) {
-  __shared__ int s[256];
+// ---- chunk index: chunk_off[n] = sum_{m<n} ceil(len_m / C); with seg_len > 0
+// also seg_off[n] = sum_{m<n} max(1, ceil(ceil(len_m / C) / seg_len)) ----
+__global__ __launch_bounds__(256) void chunk_index_kernel(const int32_t *cu, int N, int C, int32_t *off, int seg_len,
+                                                          int32_t *soff) {
+  __shared__ int s[256], g[256];
   const int tid = threadIdx.x;
-  int carry = 0;
-  if (tid == 0) off[0] = 0;
+  int carry = 0, gcarry = 0;
+  if (tid == 0) {
+    off[0] = 0;
+    if (seg_len > 0) soff[0] = 0;
+  }
   for (int base = 0; base < N; base += 256) {
     const int n = base + tid;
-    int cnt = 0;
+    int cnt = 0, sc = 0;
     if (n < N) {
       const int len = cu[n + 1] - cu[n];
       cnt = len > 0 ? (len + C - 1) / C : 0;
+      sc = seg_len > 0 ? max(1, (cnt + seg_len - 1) / seg_len) : 0;
     }
     s[tid] = cnt;
+    g[tid] = sc;
     __syncthreads();
     for (int o = 1; o < 256; o <<= 1) {
       const int v = tid >= o ? s[tid - o] : 0;
+      const int w = tid >= o ? g[tid - o] : 0;
       __syncthreads();
       s[tid] += v;
+      g[tid] += w;
       __syncthreads();
     }
-    if (n < N) off[n + 1] = carry + s[tid];
+    if (n < N) {
+      off[n + 1] = carry + s[tid];
+      if (seg_len > 0) soff[n + 1] = gcarry + g[tid];
+    }
     carry += s[255];
+    gcarry += g[255];
     __syncthreads();
   }
 }
@@ -444,7 +457,8 @@ hipError_t launch_check_offsets(const int32_t *cu, int N, int T, int32_t *flags,
 
 hipError_t launch_chunk_index(const ChunkParams &p, hipStream_t st) {
   if (!p.cu) return hipSuccess;
-  hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, st, p.cu, p.N, p.C, p.chunk_off);
+  hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, st, p.cu, p.N, p.C, p.chunk_off, p.seg_len,
+                     p.seg_off);
   return hipGetLastError();
 }
 

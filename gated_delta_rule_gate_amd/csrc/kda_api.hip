@@ -246,9 +246,11 @@ bool auto_split(const kda_args *a) {
 // AUTO at tile width 256 with 64-row chunks: the fused kernel takes 32-row chunks
 // at this width (its LDS holds a 32-row chunk of 256 channels), which give the
 // same o and ht up to rounding; the chunk-start states keep the requested chunk.
+// A gate cumsummed by the caller is chunk-local to the requested chunk size, so
+// it keeps that size (and the staged schedule).
 bool auto_fused_c32(const kda_args *a) {
   return a->schedule == KDA_SCHED_AUTO && a->dtype == KDA_BF16 && a->chunk_size == 64 &&
-         pad_width(std::max(a->K, a->V)) == 256;
+         a->gate_kind != KDA_GATE_LOG2_CUMSUM && pad_width(std::max(a->K, a->V)) == 256;
 }
 
 bool use_split(const kda_args *a, const kda::ChunkParams &p) {
@@ -286,12 +288,39 @@ kda::ChunkParams shape_params(const kda_args *a) {
   return p;
 }
 
+// Chunks per segment of the split schedule's state side (0: the serial chain):
+// args->segment when set, else the cost model's choice for a dense batch's chain
+// of ceil(T / C) chunks. A packed batch (N != B) keeps the serial chain unless
+// asked: its lengths are on the device, and the capacity bounds its longest
+// slot only loosely.
+int seg_len_for(const kda_args *a) {
+  if (a->segment < 0) return 0;
+  if (a->segment > 0) return a->segment;
+  if (a->N != a->B) return 0;
+  const int64_t nt = ((int64_t)a->T + a->chunk_size - 1) / a->chunk_size;
+  return kda::split_segment_len(nt, (int64_t)a->N * a->H, pad_width(std::max(a->K, a->V)), a->chunk_size);
+}
+
+// Upper bound of the segments of a split call (packed or dense sizes).
+int64_t seg_bound(const kda_args *a, int len) {
+  const int64_t nt = ((int64_t)a->T + a->chunk_size - 1) / a->chunk_size;
+  return std::max<int64_t>(kda::split_segment_bound(a->B, a->N, nt, true, len),
+                           kda::split_segment_bound(a->B, a->N, nt, false, len));
+}
+
 // Split schedule: the chunk prefix, then the key side's records for every
-// (chunk, head) of the packed or dense bound.
+// (chunk, head) of the packed or dense bound; with segments, the segment
+// prefix, E and o_local per (chunk, head), [M | B] and the incoming state per
+// (segment, head).
 size_t split_ws_bytes(const kda_args *a) {
   const int64_t nch = std::max<int64_t>(max_chunks(a, true), max_chunks(a, false));
-  return align_up(sizeof(int32_t) * (a->N + 1)) +
-         align_up(kda::split_workspace_bytes(a->chunk_size, pad_width(std::max(a->K, a->V)), nch * a->H));
+  const int D = pad_width(std::max(a->K, a->V));
+  size_t b = align_up(sizeof(int32_t) * (a->N + 1)) + align_up(kda::split_workspace_bytes(a->chunk_size, D, nch * a->H));
+  const int len = seg_len_for(a);
+  if (len > 0)
+    b += align_up(sizeof(int32_t) * (a->N + 1)) +
+         align_up(kda::split_segment_bytes(a->chunk_size, D, nch * a->H, seg_bound(a, len) * a->H));
+  return b;
 }
 
 kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const void *v, const float *g,
@@ -346,6 +375,18 @@ kda_status prepare_chunk(const kda_args *a, const void *q, const void *k, const 
     p.chunk_off = reinterpret_cast<int32_t *>(base);
     p.sws = base + align_up(sizeof(int32_t) * (a->N + 1));
     p.swf = reinterpret_cast<float *>(static_cast<char *>(p.sws) + bf);
+    p.seg_len = seg_len_for(a);
+    if (p.seg_len > 0) {
+      p.seg_max = (int)seg_bound(a, p.seg_len);
+      char *sb = static_cast<char *>(p.sws) + align_up(kda::split_workspace_bytes(p.C, p.D, nch * a->H));
+      p.seg_off = reinterpret_cast<int32_t *>(sb);
+      sb += align_up(sizeof(int32_t) * (a->N + 1));
+      const size_t ch = (size_t)nch * a->H * p.C * p.D;
+      p.seg_e = sb;
+      p.seg_ol = reinterpret_cast<float *>(sb + 2 * ch);
+      p.seg_mb = reinterpret_cast<float *>(sb + 6 * ch);
+      p.seg_sin = p.seg_mb + (size_t)p.seg_max * a->H * p.D * 2 * p.D;  // bf16 fragments
+    }
   } else {
     const WsLayout L = staged_layout(a);
     p.chunk_off = reinterpret_cast<int32_t *>(base + L.off[0]);
@@ -401,6 +442,11 @@ extern "C" int kda_chunk_schedule(const kda_args *a) {
   return KDA_SCHED_STAGED;
 }
 
+extern "C" int kda_chunk_segment(const kda_args *a) {
+  if (kda_chunk_schedule(a) != KDA_SCHED_SPLIT) return 0;
+  return seg_len_for(a);
+}
+
 extern "C" size_t kda_staged_workspace_offset(const kda_args *a, kda_ws_field field) {
   if (!chunk_shape_ok(a) || (int)field < 0 || (int)field > 8) return (size_t)-1;
   return staged_layout(a).off[(int)field];
@@ -429,8 +475,10 @@ kda_status run_chunk(const kda_args *a, const kda::ChunkParams &p, hipStream_t s
     return hip_status(kda::launch_fused(p, st));
   }
   if (use_split(a, p)) {
-    if (p.cu && (s = run_stage(p, KDA_STAGE_INDEX, st)) != KDA_OK) return s;
-    return hip_status(kda::launch_split(p, st));
+    kda::ChunkParams q = p;
+    if (states) q.seg_len = 0;  // the chunk-start states come from the serial chain
+    if (q.cu && (s = run_stage(q, KDA_STAGE_INDEX, st)) != KDA_OK) return s;
+    return hip_status(kda::launch_split(q, st));
   }
   for (int stage = KDA_STAGE_INDEX; stage <= KDA_STAGE_OUTPUT; ++stage)
     if ((s = run_stage(p, stage, st)) != KDA_OK) return s;

@@ -75,6 +75,21 @@ struct ChunkParams {
   // records (sizes from split_workspace_bytes)
   void *sws;
   float *swf;
+  // split schedule, chain-parallel state side: each sequence's chunks are cut
+  // into segments of seg_len chunks (0: one segment, the serial chain). A
+  // segment after the first runs from the identity (the columns of M) and from
+  // zero (those of B), giving its affine map h_out = M h_in + B, per-chunk
+  // output parts E (o = o_local + E h_in) and o_local; a combine pass chains
+  // the maps for every segment's incoming state and a correction pass adds
+  // E h_in to o_local.
+  int seg_len;
+  int seg_max;          // upper bound of the number of segments (grid size)
+  int32_t *seg_off;     // [N + 1] segment prefix per slot (packed batches only)
+  float *seg_mb;        // [seg_max, H, D, 2D] fp32: [M | B] of each segment
+  void *seg_sin;        // [seg_max, H, D/16, D/32, 64] 16-byte bf16 operand fragments of each
+                        // segment's incoming state (column tile, contraction step, lane)
+  void *seg_e;          // [n_chunks, H, C, D] bf16: E, channels in operand order
+  float *seg_ol;        // [n_chunks, H, C, D] fp32: o_local
 };
 
 // Backward of the chunked forward (staged). The forward intermediates come from
@@ -121,6 +136,17 @@ size_t split_workspace_bytes(int C, int D, int64_t chunk_heads);
 // chain of `chain` chunks, `pairs` (sequence, head) pairs and `items` (chunk,
 // head) pairs at tile width D
 bool split_preferred(int64_t chain, int64_t pairs, int64_t items, int D);
+// chunks per segment of the split schedule's chain-parallel state side for a
+// chain of `chain` chunks over `pairs` (sequence, head) pairs at tile width D,
+// or 0 where the serial chain is expected to be faster
+int split_segment_len(int64_t chain, int64_t pairs, int D, int C);
+// upper bound of the number of segments of seg_len chunks: dense B * ceil(nt /
+// seg_len) with nt = ceil(T / C); packed N + ceil((nt + N) / seg_len)
+int64_t split_segment_bound(int B, int N, int64_t nt, bool packed, int seg_len);
+// workspace of the chain-parallel state side beyond the records: E and o_local
+// for chunk_heads (chunk, head) pairs, [M | B] and the incoming state for
+// seg_heads (segment, head) pairs
+size_t split_segment_bytes(int C, int D, int64_t chunk_heads, int64_t seg_heads);
 // compute units of the current device (cached per device)
 int device_cus();
 

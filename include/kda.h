@@ -88,8 +88,10 @@ typedef enum {
                            for (same o and ht up to rounding) unless the call returns the
                            chunk-start states                                              */
   KDA_SCHED_SPLIT = 3,  /* steps (1)-(4) for every chunk at once, their operands through the
-                           workspace, then one kernel per (sequence, head) for steps (5)-(6)
-                           and the state; for few (sequence, head) pairs with long sequences */
+                           workspace, then steps (5)-(6) and the state per (sequence, head),
+                           the chain cut into segments that run side by side where that pays
+                           (see kda_args.segment); for few (sequence, head) pairs with long
+                           sequences                                                         */
   KDA_SCHED_PIPE = 4    /* the fused schedule's pipelined kernel (bf16, chunk 64, max(K, V) in
                            (64, 128], safe gate): per (sequence, head), four waves run steps
                            (1)-(4) of one chunk while four run steps (5)-(6) of the previous
@@ -120,7 +122,27 @@ typedef struct {
                               logits and every kernel uses 1 / (1 + exp(-beta)) ("FLA KDA
                               Skill", section "Correctness checklist": raw beta logits and
                               post-sigmoid beta). Other values: KDA_ERR_SHAPE                 */
+  int segment;             /* KDA_SCHED_SPLIT's state scan: chunks per segment. 0 chooses from
+                              the sizes (kda_chunk_segment reports it), < 0 keeps one chain per
+                              (sequence, head). Segments after a sequence's first run side by
+                              side from the identity and from zero, and their affine maps are
+                              chained afterwards (see below); o and ht agree with the serial
+                              chain up to rounding. kda_chunk_fwd_states always runs the serial
+                              chain. The workspace size depends on it                          */
 } kda_args;
+
+/*
+ * Segments of the state scan (the context-parallel path that "FLA KDA Skill",
+ * section "Correctness checklist", lists beside initial and final states and
+ * long-sequence cumulative decay): one chunk maps the incoming state affinely,
+ * h' = (Diag(2^b_L) - k~^T w) h + k~^T u, so a segment of chunks maps
+ * h_out = M h_in + B and its outputs are o = o_local + E h_in. Each later
+ * segment computes M, B, E and o_local from the identity and from zero, in
+ * parallel with the others; an fp32 pass chains h_in(s + 1) = M_s h_in(s) + B_s
+ * and a last pass adds E h_in to o_local. It trades about twice the state-side
+ * work after the first segment for a chain of seg_len chunks instead of the
+ * whole sequence.
+ */
 
 /*
  * q_l2norm ("Add fused recurrent_kda ...", the stacked description of the
@@ -175,6 +197,15 @@ size_t kda_chunk_workspace_bytes(const kda_args *args);
  * K, V <= 128; pipe: as listed at KDA_SCHED_PIPE).
  */
 int kda_chunk_schedule(const kda_args *args);
+
+/*
+ * Chunks per segment of the split schedule's state scan for these arguments
+ * (args->segment if positive, else the choice of a cost model of the state side
+ * from the sizes and the device's compute units; a packed batch keeps one chain
+ * per slot unless args->segment asks otherwise), or 0 when kda_chunk_fwd runs
+ * one serial chain per (sequence, head) or another schedule. Host-only.
+ */
+int kda_chunk_segment(const kda_args *args);
 
 /*
  * Step (1) of the chunked forward on its own: the gate activation and the

@@ -199,13 +199,25 @@ def test_split_schedule_limits_and_workspace(kda_lib):
     assert call(_args(gate_kind=0, schedule=4)) == 8                     # the pipelined kernel: safe gate only
     align = lambda x: (x + 255) // 256 * 256
     for B, N, T, H, K, V, C in ((3, 3, 203, 2, 128, 128, 64), (1, 5, 420, 4, 96, 64, 32)):
-        a = _args(gate_kind=0, schedule=3, B=B, N=N, T=T, H=H, K=K, V=V, chunk_size=C)
         D = 64 if max(K, V) <= 64 else 128
         nt = (T + C - 1) // C
         nch = max(B * nt, nt + N)
         per = 2 * (3 * C * D + C * C) + 4 * (C * D + D + C)
-        assert kda_lib.kda_chunk_workspace_bytes(ctypes.byref(a)) == align(4 * (N + 1)) + align(nch * H * per)
+        serial = align(4 * (N + 1)) + align(nch * H * per)
+        a = _args(gate_kind=0, schedule=3, B=B, N=N, T=T, H=H, K=K, V=V, chunk_size=C, segment=-1)
+        assert kda_lib.kda_chunk_workspace_bytes(ctypes.byref(a)) == serial
+        assert kda_lib.kda_chunk_segment(ctypes.byref(a)) == 0
+        # segments of 3 chunks add the segment prefix, E (bf16) and o_local (fp32) per
+        # (chunk, head), and [M | B] (fp32, D x 2D) plus the incoming state (bf16, D x D)
+        # per (segment, head) of the larger of the dense and packed segment bounds
+        a = _args(gate_kind=0, schedule=3, B=B, N=N, T=T, H=H, K=K, V=V, chunk_size=C, segment=3)
+        nseg = max(B * max(1, (nt + 2) // 3), N + (nt + N + 2) // 3)
+        seg = align(4 * (N + 1)) + align(nch * H * C * D * 6 + nseg * H * D * D * 10)
+        assert kda_lib.kda_chunk_workspace_bytes(ctypes.byref(a)) == serial + seg
+        assert kda_lib.kda_chunk_segment(ctypes.byref(a)) == 3
     assert kda_lib.kda_chunk_workspace_bytes(ctypes.byref(_args(gate_kind=0, schedule=3, dtype=1))) == 0
+    # the segment length applies to the split schedule only
+    assert kda_lib.kda_chunk_segment(ctypes.byref(_args(gate_kind=0, schedule=2, segment=3))) == 0
 
 
 def test_resolved_schedule(kda_lib):
@@ -218,6 +230,8 @@ def test_resolved_schedule(kda_lib):
     assert sched(B=2, N=2, T=16384, H=16) == 3
     assert sched(B=2, N=2, T=16384, H=16, dtype=1) == 1
     assert sched(B=2, N=2, T=16384, H=16, K=256, V=256) == 2                   # fused at 32-row chunks
+    # a gate the caller cumsummed over 64-row chunks cannot switch to 32-row chunks
+    assert kda_lib.kda_chunk_schedule(ctypes.byref(_args(gate_kind=3, B=2, N=2, T=16384, H=16, K=256, V=256))) == 1
     assert sched(B=2, N=2, T=16384, H=16, K=256, V=256, dtype=1) == 1          # fp32: staged
     assert sched(B=2, N=2, T=16384, H=16, K=256, V=256, chunk_size=32, schedule=2) == 2
     assert sched(B=2, N=2, T=16384, H=16, K=256, V=256, schedule=2) == -1      # named fused: 32-row chunks only
