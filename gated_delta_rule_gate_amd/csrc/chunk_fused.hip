@@ -42,15 +42,19 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   using S = FusedSmem<C, D, NT>;
   constexpr bool SAFE = (GK == kGateSafe);
   constexpr int NW = NT / 64, NC = TL::NC, DT = TL::DT, LDT = TL::LDT, LDB = TL::LDB, LDA = TL::LDA;
-  constexpr int NVW = 1;  // value tiles (and w column tiles) per wave
-  static_assert(DT == NW, "one w column tile and at most one value tile per wave");
+  // one value tile per wave; at D = 256 the eight waves also solve two w tiles
+  // each (with the whole state in eight waves, half of every wave's 256 VGPRs
+  // would hold state and the rest spill: 1.39 against 1.12 ms at B8 T2048 H32)
+  constexpr int NVW = 1;
+  constexpr int WT = DT / NW;
+  static_assert(WT * NW == DT && (WT == 1 || WT == 2), "w column tiles per wave");
 
   extern __shared__ __align__(16) char smem[];
   // buffers below 64 KB at constant offsets; the others from three opaque bases
   char *baseB = lds_base(smem, S::b), *baseA = lds_base(smem, S::akk), *baseT = lds_base(smem, S::t1);
   static_assert(S::b % 16 == 0 && S::wt_off % 16 == 0 && S::akk % 16 == 0 && S::kt % 16 == 0 && S::aqk % 16 == 0 &&
                     S::aqh % 16 == 0 && S::td % 16 == 0 && S::t1 % 16 == 0 && S::t2 % 16 == 0 && S::t0 % 16 == 0 && S::beta % 16 == 0 &&
-                    S::bl % 16 == 0 && S::decay % 16 == 0 && S::dt % 16 == 0 && S::seg % 16 == 0 && S::qn % 16 == 0,
+                    S::bl % 16 == 0 && S::decay % 16 == 0 && S::dt % 16 == 0 && S::seg % 16 == 0 && S::qn % 16 == 0 && S::part % 16 == 0,
                 "16-byte aligned buffers");
   static_assert( S::td + 2 * C * S::LDTD - S::akk <= 65536 &&
                     S::total - S::t1 <= 65536 && S::v + S::tile <= 65536,
@@ -75,6 +79,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   float *sDt = reinterpret_cast<float *>(baseT + (S::dt - S::t1));
   float *sSeg = reinterpret_cast<float *>(baseT + (S::seg - S::t1));
   float *sQn = reinterpret_cast<float *>(baseT + (S::qn - S::t1));
+  float *sPart = reinterpret_cast<float *>(baseT + (S::part - S::t1));
 
   // workgroup = (sequence, head, block vb of D / vsplit value columns); waves
   // below tpb own one 16-column tile of the state, all waves share the key side
@@ -112,12 +117,10 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   // chunk's q, k, v while the odd ones invert the diagonal blocks
   constexpr bool HALF_LOAD = (NW / NC >= 2);
   constexpr int NL = HALF_LOAD ? NT / 2 : NT;
-  const bool loader = !HALF_LOAD || gram_half<NW, NC>(wid) == 0;
-  // the next chunk's raw inputs wait in registers while a chunk computes; at
-  // D = 256 (16 waves, 128 VGPRs each, half of them the state strip) those
-  // registers would spill, so each chunk loads its own inputs at its start
-  constexpr bool PREFETCH = D <= 128;
-  ChunkRegs<Tin, C, D, NT, NL> regs;
+  const bool loader = !HALF_LOAD || gram_loader<NW, NC>(wid);
+  // the next chunk's raw inputs wait in registers while a chunk computes
+  constexpr bool PREFETCH = true;
+  ChunkRegs<Tin, C, D, NT, NL, gram_shares<NW, NC>() == 4> regs;
   if (PREFETCH && nch > 0) {
     regs.load_gate(p, sr.t0, min(C, sr.len), h);
     if (loader) regs.load_qkv(p, sr.t0, min(C, sr.len), h);
@@ -163,10 +166,10 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     };
     if constexpr (HALF_LOAD)
       grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT0, sT1,
-                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, load_next, gate_next);
+                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, sPart, load_next, gate_next);
     else
       grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT0, sT1,
-                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, none, gate_next);
+                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, sPart, none, gate_next);
     __syncthreads();
     if (!HALF_LOAD && more) regs.load_qkv(p, t0 + C, Ln, h);
     // (4) this wave's column tiles of w (channels) and u (values)
@@ -181,6 +184,10 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
       store_wT<C>(sWT, S::LDW, wid, W);
 #pragma unroll
       for (int i = 0; i < NC; ++i) uv[i][0] = U[i];
+      if constexpr (WT == 2) {  // the wave's second w tile
+        wy_subst2<C, false>(sXw, wid + NW, sXw, 0, LDT, sBeta, sAkk, LDA, sTd, S::LDTD, W, W);
+        store_wT<C>(sWT, S::LDW, wid + NW, W);
+      }
     }
     __syncthreads();
     // (5) + (6) on the waves that own a value tile
@@ -220,7 +227,8 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   if (owner && p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, Vr, col0, Kr, hs, Vr);
 }
 
-// D = 256 runs 32-row chunks: one wave per 16-column tile (16 waves), 133 KB of LDS
+// D = 256 runs 32-row chunks with eight waves (two w tiles each) and the value
+// columns split over two workgroups, each holding half the state; 131 KB of LDS
 bool fused_supported(const ChunkParams &p) {
   return p.is_bf16 && (p.D == 64 || p.D == 128 || (p.D == 256 && p.C == 32));
 }
@@ -257,14 +265,16 @@ hipError_t launch_fused_g(const ChunkParams &p, hipStream_t st) {
 
 template <int C, int D>
 hipError_t launch_fused_t(const ChunkParams &p0, hipStream_t st) {
-  // one wave per 16-column tile of w (and of the state)
-  constexpr int NT = (KDA_FUSED_THREADS > 0 && D <= 128) ? KDA_FUSED_THREADS : 4 * D;
+  // one wave per 16-column tile of w (and of the state); at D = 256 eight waves
+  // with two w tiles each, and at least two value blocks
+  constexpr int NT = (KDA_FUSED_THREADS > 0 && D <= 128) ? KDA_FUSED_THREADS : (D == 256 ? 512 : 4 * D);
+  constexpr int VS0 = (D / 16) / (NT / 64);
   if (p0.N * p0.H == 0) return hipSuccess;
   // with fewer (sequence, head) pairs than compute units, split the value
   // columns so that the workgroups still cover the chip
   ChunkParams p = p0;
   const int cus = device_cus();
-  p.vsplit = 1;
+  p.vsplit = VS0;
   while (2 * p.vsplit <= D / 16 && (int64_t)p.N * p.H * 2 * p.vsplit <= cus) p.vsplit *= 2;
   switch (p.gate_kind) {
     case kGateSafe: return launch_fused_g<C, D, NT, kGateSafe>(p, st);

@@ -38,15 +38,17 @@ struct FusedSmem {
   static constexpr size_t dt = decay + 2 * 4 * D;  // decay: two chunks (the state update trails by one)
   static constexpr size_t seg = dt + 4 * D;
   static constexpr size_t qn = seg + 4 * NT;  // per chunk row: 1/sqrt(|q|^2 + eps) (q_l2norm)
-  static constexpr size_t total = qn + 4 * C;
+  // with four channel shares in the grams, their extra partial sums: fp32 [4][C][LDA]
+  static constexpr size_t part = qn + 4 * C;
+  static constexpr size_t total = part + ((gram_shares<NT / 64, C / 16>() == 4) ? 4 * 4 * C * LDA : 0);
 };
 
 // One chunk's raw inputs held in registers between the HBM load and the LDS store.
 // q, k and v are loaded and stored by NL threads (loader index in [0, NL)):
-// all of them, or one wave of each pair 2m, 2m + 1 (the pair's first half of
-// the grams), which issues those loads while the other inverts a diagonal
-// block. The gate input and beta use every thread.
-template <typename Tin, int C, int D, int NT, int NL>
+// all of them, one wave of each pair 2m, 2m + 1 (the pair's first half of the
+// grams), which issues those loads while the other inverts a diagonal block,
+// or (LOW) the first NT / 2 threads. The gate input and beta use every thread.
+template <typename Tin, int C, int D, int NT, int NL, bool LOW = false>
 struct ChunkRegs {
   static constexpr int EPV = 16 / (int)sizeof(Tin);
   static constexpr int VPR = D / EPV, NVT = C * VPR, IT = (NVT + NL - 1) / NL;  // q, k, v tiles
@@ -54,7 +56,7 @@ struct ChunkRegs {
   // the q/k/v loader index of this thread (valid on loader waves)
   static __device__ __forceinline__ unsigned loader_index() {
     const unsigned t = (unsigned)tid_opaque();
-    return (NL == NT) ? t : (((t >> 7) << 6) | (t & 63));
+    return (NL == NT || LOW) ? t : (((t >> 7) << 6) | (t & 63));
   }
   u32x4_t q[IT], k[IT], v[IT];
   f32x4_t x[IX];

@@ -575,17 +575,28 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
 // A_qk / A_kk. With add, the other channel half's partial sums (A_qk in sAqk,
 // A_kk in sAkk) are added first. Final A_qk goes to sAqh as bf16, partial
 // A_qk to sAqk; -A_kk (partial or final) always to sAkk.
+// With four channel quarters, xq0/xq1 and xk0/xk1 hold two more partial sums of
+// A_qk and -A_kk (same layout), added with the one in sAqk / sAkk.
 template <int I, int NC>
 __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)[NC], bool doQ, bool doK, bool add,
                                             bool final, int r, int L, float scale, float beta_r, float *sAkk,
-                                            float *sAqk, int lda, bf16_t *sAqh, int ldh) {
+                                            float *sAqk, int lda, bf16_t *sAqh, int ldh,
+                                            const float *xq0 = nullptr, const float *xq1 = nullptr,
+                                            const float *xk0 = nullptr, const float *xk1 = nullptr) {
   const int grp = (tid_opaque() & 63) >> 4;
   f32x4_t prevQ[I + 1], prevK[I + 1];
   if (add) {
 #pragma unroll
     for (int j = 0; j <= I; ++j) {
-      if (doQ) prevQ[j] = *reinterpret_cast<const f32x4_t *>(sAqk + r * lda + 16 * j + 4 * grp);
-      if (doK) prevK[j] = *reinterpret_cast<const f32x4_t *>(sAkk + r * lda + 16 * j + 4 * grp);
+      const int o = r * lda + 16 * j + 4 * grp;
+      if (doQ) {
+        prevQ[j] = *reinterpret_cast<const f32x4_t *>(sAqk + o);
+        if (xq0) prevQ[j] = prevQ[j] + *reinterpret_cast<const f32x4_t *>(xq0 + o) + *reinterpret_cast<const f32x4_t *>(xq1 + o);
+      }
+      if (doK) {
+        prevK[j] = *reinterpret_cast<const f32x4_t *>(sAkk + o);
+        if (xk0) prevK[j] = prevK[j] + *reinterpret_cast<const f32x4_t *>(xk0 + o) + *reinterpret_cast<const f32x4_t *>(xk1 + o);
+      }
     }
   }
   const bool row_ok = r < L;
@@ -633,20 +644,40 @@ __device__ __forceinline__ void gram_finish(f32x4_t (&accQ)[NC], f32x4_t (&accK)
 // The channel half of its row block that wave w takes in the grams. With 8
 // waves and 4 row blocks, the halves alternate so that each SIMD (waves w and
 // w + 4) holds one wave of either half.
+// Channel shares per row block: 4 when there are at least four waves per row
+// block (eight waves on 32-row chunks), else 2 or 1.
+template <int NW, int NC>
+constexpr int gram_shares() {
+  return (NW / NC >= 4) ? 4 : ((NW / NC >= 2) ? 2 : 1);
+}
+
 template <int NW, int NC>
 __device__ __forceinline__ int gram_half(int w) {
   if constexpr (NW == 8 && NC == 4) return (w & 1) ^ (w >> 2);
-  else return w % ((NW / NC >= 2) ? 2 : 1);
+  else return w % gram_shares<NW, NC>();
 }
 
+// The waves that load the next chunk's q, k, v during the grams: with two
+// shares one of each pair 2m, 2m + 1 (share 0, after the barrier); with four
+// the waves of row block 0 (the first half), whose channel pass is the shorter,
+// before the barrier.
+template <int NW, int NC>
+__device__ __forceinline__ bool gram_loader(int w) {
+  if constexpr (gram_shares<NW, NC>() == 4) return w < NW / 2;
+  else return gram_half<NW, NC>(w) == 0;
+}
+
+// With four shares, sPart holds four more [C][lda] fp32 partial-sum tiles
+// (A_qk of shares 2 and 3, then -A_kk of shares 2 and 3); share 0 completes
+// A_qk, share 1 -A_kk and its diagonal inverse.
 template <int NT, int C, int D, bool SAFE, typename Idle, typename Pre>
 __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                             const float *sBeta, float scale, float *sAkk, float *sAqk, int lda,
                                             bf16_t *sAqh, int ldh, int L, const float *sT0, const float *sT1,
                                             const float *sT2, const float *sBL, bf16_t *sKt, bf16_t *sXw,
-                                            bf16_t *sTd, int ldtd, Idle &&idle, Pre &&pre) {
+                                            bf16_t *sTd, int ldtd, float *sPart, Idle &&idle, Pre &&pre) {
   constexpr int NW = NT / 64, NC = C / 16;
-  constexpr int HS = (NW / NC >= 2) ? 2 : 1, CW = D / HS, NS = CW / 32;
+  constexpr int HS = gram_shares<NW, NC>(), CW = D / HS, NS = CW / 32;
   static_assert(NW >= NC && CW % 32 == 0, "wave split of the grams");
   const int lane = tid_opaque() & 63, w = wave_id();
   const int n16 = lane & 15, grp = lane >> 4;
@@ -724,20 +755,51 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
           *reinterpret_cast<bf16x4_t *>(sXw + r * ldt + c0 + 32 * s + 4 * grp + 16 * hh) = xw[s][hh];
     }
   };
-  auto finish = [&](bool doQ, bool doK, bool add, bool final) {
+  auto finish_at = [&](bool doQ, bool doK, bool add, bool final, float *dK, float *dQ, const float *xq0,
+                       const float *xq1, const float *xk0, const float *xk1) {
     switch (i) {
-      case 0: gram_finish<0, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh); break;
-      case 1: gram_finish<1, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh); break;
+      case 0: gram_finish<0, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, dK, dQ, lda, sAqh, ldh, xq0, xq1, xk0, xk1); break;
+      case 1: gram_finish<1, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, dK, dQ, lda, sAqh, ldh, xq0, xq1, xk0, xk1); break;
       case 2:
-        if constexpr (NC > 2) gram_finish<2, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh);
+        if constexpr (NC > 2) gram_finish<2, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, dK, dQ, lda, sAqh, ldh, xq0, xq1, xk0, xk1);
         break;
       case 3:
-        if constexpr (NC > 3) gram_finish<3, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, sAkk, sAqk, lda, sAqh, ldh);
+        if constexpr (NC > 3) gram_finish<3, NC>(accQ, accK, doQ, doK, add, final, r, L, scale, beta_r, dK, dQ, lda, sAqh, ldh, xq0, xq1, xk0, xk1);
         break;
     }
   };
+  auto finish = [&](bool doQ, bool doK, bool add, bool final) {
+    finish_at(doQ, doK, add, final, sAkk, sAqk, nullptr, nullptr, nullptr, nullptr);
+  };
   if (NW == 8 && NC == 4) __builtin_amdgcn_s_setprio(0);
-  if constexpr (HS == 2) {
+  if constexpr (HS == 4) {
+    // each share stores the partial sums of the matrices it does not complete:
+    // share 0 -A_kk (to sAkk), share 1 A_qk (to sAqk), shares 2 and 3 both (to sPart)
+    const int tile = C * lda;
+    if (active) {
+      if (hsel == 0) finish(false, true, false, false);
+      else if (hsel == 1) finish(true, false, false, false);
+      else finish_at(true, true, false, false, sPart + (hsel == 2 ? 2 : 3) * tile, sPart + (hsel == 2 ? 0 : 1) * tile,
+                     nullptr, nullptr, nullptr, nullptr);
+    }
+    // row block 0's pass is the shorter (no off-diagonal block): its waves issue
+    // the next chunk's loads while the others finish theirs
+    if (w < NW / 2) idle();
+    pre();
+    __syncthreads();
+    store_xw();
+    if (hsel == 0) {
+      if (active) finish_at(true, false, true, true, sAkk, sAqk, sPart, sPart + tile, nullptr, nullptr);
+    } else if (hsel == 1) {
+      if (active) {
+        __builtin_amdgcn_s_setprio(2);
+        finish_at(false, true, true, true, sAkk, sAqk, nullptr, nullptr, sPart + 2 * tile, sPart + 3 * tile);
+        lds_wave_order();
+        diag_inverse_block(sAkk, lda, sTd, ldtd, i);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+  } else if constexpr (HS == 2) {
     // the two halves split the merge: half 1 finishes A_qk's partner and half 0
     // A_kk's, so each wave stores one partial and completes the other matrix
     if (active) {
