@@ -54,7 +54,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   char *baseB = lds_base(smem, S::b), *baseA = lds_base(smem, S::akk), *baseT = lds_base(smem, S::t1);
   static_assert(S::b % 16 == 0 && S::wt_off % 16 == 0 && S::akk % 16 == 0 && S::kt % 16 == 0 && S::aqk % 16 == 0 &&
                     S::aqh % 16 == 0 && S::td % 16 == 0 && S::t1 % 16 == 0 && S::t2 % 16 == 0 && S::t0 % 16 == 0 && S::beta % 16 == 0 &&
-                    S::bl % 16 == 0 && S::decay % 16 == 0 && S::dt % 16 == 0 && S::seg % 16 == 0 && S::qn % 16 == 0 && S::part % 16 == 0,
+                    S::bl % 16 == 0 && S::decay % 16 == 0 && S::dt % 16 == 0 && S::seg % 16 == 0 && S::qn % 16 == 0 && S::part % 16 == 0 && S::xc % 16 == 0,
                 "16-byte aligned buffers");
   static_assert( S::td + 2 * C * S::LDTD - S::akk <= 65536 &&
                     S::total - S::t1 <= 65536 && S::v + S::tile <= 65536,
@@ -80,6 +80,7 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
   float *sSeg = reinterpret_cast<float *>(baseT + (S::seg - S::t1));
   float *sQn = reinterpret_cast<float *>(baseT + (S::qn - S::t1));
   float *sPart = reinterpret_cast<float *>(baseT + (S::part - S::t1));
+  bf16x8_t *sXc = reinterpret_cast<bf16x8_t *>(baseT + (S::xc - S::t1));
 
   // workgroup = (sequence, head, block vb of D / vsplit value columns); waves
   // below tpb own one 16-column tile of the state, all waves share the key side
@@ -115,9 +116,10 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
 
   // with two waves per row block of the grams, the even waves load the next
   // chunk's q, k, v while the odd ones invert the diagonal blocks
-  constexpr bool HALF_LOAD = (NW / NC >= 2);
-  constexpr int NL = HALF_LOAD ? NT / 2 : NT;
-  const bool loader = !HALF_LOAD || gram_loader<NW, NC>(wid);
+  // the grams issue the next chunk's q, k, v loads, from half the waves
+  constexpr bool GRAM_LOADS = (NW / NC >= 2);
+  constexpr int NL = GRAM_LOADS ? NT / 2 : NT;
+  const bool loader = !GRAM_LOADS || gram_loader<NW, NC>(wid);
   // the next chunk's raw inputs wait in registers while a chunk computes
   constexpr bool PREFETCH = true;
   ChunkRegs<Tin, C, D, NT, NL, gram_shares<NW, NC>() == 4> regs;
@@ -164,14 +166,14 @@ __global__ __launch_bounds__(NT) void fused_chunk_kernel(ChunkParams p) {
     auto gate_next = [&]() {
       if (more) regs.load_gate(p, t0 + C, Ln, h);
     };
-    if constexpr (HALF_LOAD)
+    if constexpr (GRAM_LOADS)
       grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT0, sT1,
-                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, sPart, load_next, gate_next);
+                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, sPart, sXc, load_next, gate_next);
     else
       grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT0, sT1,
-                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, sPart, none, gate_next);
+                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, sPart, sXc, none, gate_next);
     __syncthreads();
-    if (!HALF_LOAD && more) regs.load_qkv(p, t0 + C, Ln, h);
+    if (!GRAM_LOADS && more) regs.load_qkv(p, t0 + C, Ln, h);
     // (4) this wave's column tiles of w (channels) and u (values)
     f32x4_t uv[NC][NVW];
     {

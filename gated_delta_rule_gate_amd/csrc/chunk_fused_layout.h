@@ -38,9 +38,14 @@ struct FusedSmem {
   static constexpr size_t dt = decay + 2 * 4 * D;  // decay: two chunks (the state update trails by one)
   static constexpr size_t seg = dt + 4 * D;
   static constexpr size_t qn = seg + 4 * NT;  // per chunk row: 1/sqrt(|q|^2 + eps) (q_l2norm)
-  // with four channel shares in the grams, their extra partial sums: fp32 [4][C][LDA]
+  // with four channel shares in the grams, their extra partial sums: fp32 [4][C][LDA];
+  // and on 32-row chunks block pair (1, 0)'s column operand, 16-byte fragments
+  // [4 shares][D / 128 steps][64 lanes]
+  static constexpr bool SHARES4 = gram_shares<NT / 64, C / 16>() == 4;
   static constexpr size_t part = qn + 4 * C;
-  static constexpr size_t total = part + ((gram_shares<NT / 64, C / 16>() == 4) ? 4 * 4 * C * LDA : 0);
+  static constexpr size_t xc = part + (SHARES4 ? 4 * 4 * C * LDA : 0);
+  static constexpr size_t total = xc + ((SHARES4 && C == 32) ? 4 * (D / 128) * 64 * 16 : 0);
+  static_assert(total <= 160 * 1024, "LDS");
 };
 
 // One chunk's raw inputs held in registers between the HBM load and the LDS store.

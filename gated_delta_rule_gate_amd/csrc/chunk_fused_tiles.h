@@ -445,12 +445,20 @@ namespace kda {
 // For the safe gate these reuse the midpoint exponentials: scale 2^b =
 // 2^(b - m_I) T1 and 2^(b_L - b) = 2^(m_I - b) T2 with the per-channel tables
 // T1 = scale 2^m_I, T2 = 2^(b_L - m_I); other gates take them directly.
-template <int I, int NC, int NS, bool SAFE>
+//
+// XP = 1 (row block 0 of a 32-row chunk): the wave also forms the column operand
+// of block pair (1, 0), k_s 2^(a_1 - b_s) for its own rows s, and stores it in
+// operand order to sXc at step slot xs + s. XP = 2 (row block 1): the
+// off-diagonal products are left out; the row operands come back in fo for
+// the caller to multiply with sXc once the other wave has written it.
+template <int I, int NC, int NS, bool SAFE, int XP = 0>
 __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                                  int c0, const float *sT0, const float *sT1, const float *sT2,
                                                  const float *sBL, int D,
                                                  float scale, float beta_r, bf16_t *sKt, f32x4_t (&accQ)[NC],
-                                                 f32x4_t (&accK)[NC], bf16x4_t (&xw)[NS][2]) {
+                                                 f32x4_t (&accK)[NC], bf16x4_t (&xw)[NS][2],
+                                                 bf16x8_t *sXc = nullptr, int xs = 0,
+                                                 bf16x8_t (*fo)[2] = nullptr) {
   using M = Mma<bf16_t>;
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
@@ -521,6 +529,24 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
     if (I > 0) {
       fqo = pack_bf16x8(vqo);
       fko = pack_bf16x8(vko);
+      if constexpr (XP == 2) {
+        fo[s][0] = fqo;
+        fo[s][1] = fko;
+      }
+    }
+    if constexpr (XP == 1) {
+      // k_s 2^(a_1 - b_s) for this lane's row s = n16 of block 0 (a_1 = b at row 16)
+      float vx[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4_t a1 = *reinterpret_cast<const f32x4_t *>(sB + 16 * ldb + kb + 16 * hh);
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) {
+          const float kf = static_cast<float>(hh ? k1[ee] : k0[ee]);
+          vx[4 * hh + ee] = kf * fast_exp2(a1[ee] - br[hh][ee]);
+        }
+      }
+      sXc[(xs + s) * 64 + lane] = pack_bf16x8(vx);
     }
     if (SAFE) {
       fqd = pack_bf16x8(vqd);
@@ -547,7 +573,7 @@ __device__ __forceinline__ void gram_row_partial(bf16_t *sQ, const bf16_t *sK, i
       accK[I] = M::mma(fcd, fkd, accK[I]);
     }
 #pragma unroll
-    for (int j = 0; j < I; ++j) {
+    for (int j = 0; j < (XP == 2 ? 0 : I); ++j) {
       const int cs = 16 * j + n16;
       const bf16x4_t c0v = *reinterpret_cast<const bf16x4_t *>(sK + cs * ldt + kb);
       const bf16x4_t c1v = *reinterpret_cast<const bf16x4_t *>(sK + cs * ldt + kb + 16);
@@ -659,23 +685,27 @@ __device__ __forceinline__ int gram_half(int w) {
 
 // The waves that load the next chunk's q, k, v during the grams: with two
 // shares one of each pair 2m, 2m + 1 (share 0, after the barrier); with four
-// the waves of row block 0 (the first half), whose channel pass is the shorter,
-// before the barrier.
+// the waves of row block 0 (the first half), whose pass is the shorter, before
+// the barrier.
 template <int NW, int NC>
 __device__ __forceinline__ bool gram_loader(int w) {
   if constexpr (gram_shares<NW, NC>() == 4) return w < NW / 2;
   else return gram_half<NW, NC>(w) == 0;
 }
 
-// With four shares, sPart holds four more [C][lda] fp32 partial-sum tiles
-// (A_qk of shares 2 and 3, then -A_kk of shares 2 and 3); share 0 completes
-// A_qk, share 1 -A_kk and its diagonal inverse.
+// With four shares (32-row chunks, eight waves), sPart holds four more [C][lda]
+// fp32 partial-sum tiles (A_qk of shares 2 and 3, then -A_kk of shares 2 and 3);
+// share 0 completes A_qk, share 1 -A_kk and its diagonal inverse. Row block 0's
+// waves also form block pair (1, 0)'s column operand into sXc before a barrier;
+// row block 1's waves, whose pass is the longer, multiply it after the barrier.
+// Row block 0's waves also issue the next chunk's loads (idle) before it.
 template <int NT, int C, int D, bool SAFE, typename Idle, typename Pre>
 __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ldt, const float *sB, int ldb,
                                             const float *sBeta, float scale, float *sAkk, float *sAqk, int lda,
                                             bf16_t *sAqh, int ldh, int L, const float *sT0, const float *sT1,
                                             const float *sT2, const float *sBL, bf16_t *sKt, bf16_t *sXw,
-                                            bf16_t *sTd, int ldtd, float *sPart, Idle &&idle, Pre &&pre) {
+                                            bf16_t *sTd, int ldtd, float *sPart, bf16x8_t *sXc, Idle &&idle,
+                                            Pre &&pre) {
   constexpr int NW = NT / 64, NC = C / 16;
   constexpr int HS = gram_shares<NW, NC>(), CW = D / HS, NS = CW / 32;
   static_assert(NW >= NC && CW % 32 == 0, "wave split of the grams");
@@ -690,6 +720,7 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
   const int r = 16 * i + n16;
   const float beta_r = active ? sBeta[r] : 0.f;
   bf16x4_t xw[NS][2];
+  bf16x8_t fo[NS][2];  // row block 1's off-diagonal row operands (four shares, 32-row chunks)
 
   f32x4_t accQ[NC], accK[NC];
 #pragma unroll
@@ -733,6 +764,18 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
 #define KDA_GRAM_ROW(II)                                                                                     \
   gram_row_partial<II, NC, NS, SAFE>(sQ, sK, ldt, sB, ldb, c0, sT0, sT1, sT2, sBL, D, scale, beta_r, sKt, accQ, accK, \
                                      xw)
+    if constexpr (HS == 4) {
+      // row block 0 forms block pair (1, 0)'s column operand for block 1's
+      // waves, whose own pass is the longer; they multiply it after the barrier below
+      if (i == 0) {
+        gram_row_partial<0, NC, NS, SAFE, 1>(sQ, sK, ldt, sB, ldb, c0, sT0, sT1, sT2, sBL, D, scale, beta_r, sKt, accQ,
+                                             accK, xw, sXc, hsel * NS);
+        // this block's pass is the shorter: its waves issue the next chunk's loads
+        idle();
+      } else
+        gram_row_partial<1, NC, NS, SAFE, 2>(sQ, sK, ldt, sB, ldb, c0, sT0, sT1, sT2, sBL, D, scale, beta_r, sKt, accQ,
+                                             accK, xw, nullptr, 0, fo);
+    } else
     switch (i) {
       case 0: KDA_GRAM_ROW(0); break;
       case 1: KDA_GRAM_ROW(1); break;
@@ -744,6 +787,19 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
         break;
     }
 #undef KDA_GRAM_ROW
+  }
+  static_assert(HS != 4 || NC == 2, "four shares on 32-row chunks only");
+  if constexpr (HS == 4) {
+    __syncthreads();  // block pair (1, 0)'s column operand is in sXc
+    if (i == 1) {
+      using M = Mma<bf16_t>;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8_t fc = sXc[(hsel * NS + s) * 64 + lane];
+        accQ[0] = M::mma(fc, fo[s][0], accQ[0]);
+        accK[0] = M::mma(fc, fo[s][1], accK[0]);
+      }
+    }
   }
   // X_w over b once every wave is past its reads of b
   auto store_xw = [&]() {
@@ -782,9 +838,6 @@ __device__ __forceinline__ void grams_fused(bf16_t *sQ, const bf16_t *sK, int ld
       else finish_at(true, true, false, false, sPart + (hsel == 2 ? 2 : 3) * tile, sPart + (hsel == 2 ? 0 : 1) * tile,
                      nullptr, nullptr, nullptr, nullptr);
     }
-    // row block 0's pass is the shorter (no off-diagonal block): its waves issue
-    // the next chunk's loads while the others finish theirs
-    if (w < NW / 2) idle();
     pre();
     __syncthreads();
     store_xw();

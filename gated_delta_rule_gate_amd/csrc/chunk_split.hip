@@ -82,12 +82,14 @@ __global__ __launch_bounds__(NT) void split_key_kernel(ChunkParams p) {
   float *sSeg = reinterpret_cast<float *>(baseT + (S::seg - S::t1));
   float *sQn = reinterpret_cast<float *>(baseT + (S::qn - S::t1));
   float *sPart = reinterpret_cast<float *>(baseT + (S::part - S::t1));
+  bf16x8_t *sXc = reinterpret_cast<bf16x8_t *>(baseT + (S::xc - S::t1));
 
   const int wid = wave_id();
   const bool owner = wid * 16 < p.Vr;
-  constexpr bool HALF_LOAD = (NW / NC >= 2);
-  constexpr int NL = HALF_LOAD ? NT / 2 : NT;
-  const bool loader = !HALF_LOAD || gram_loader<NW, NC>(wid);
+  // the grams issue the next chunk's q, k, v loads, from half the waves
+  constexpr bool GRAM_LOADS = (NW / NC >= 2);
+  constexpr int NL = GRAM_LOADS ? NT / 2 : NT;
+  const bool loader = !GRAM_LOADS || gram_loader<NW, NC>(wid);
   ChunkRegs<Tin, C, D, NT, NL, gram_shares<NW, NC>() == 4> regs;
   // item i is (chunk i % total, head i / total): the items of a head are consecutive
   int h = (int)(i0 / total), gc = (int)(i0 % total);
@@ -134,14 +136,14 @@ __global__ __launch_bounds__(NT) void split_key_kernel(ChunkParams p) {
     auto gate_next = [&]() {
       if (more) regs.load_gate(p, ln.t0, ln.L, hn);
     };
-    if constexpr (HALF_LOAD)
+    if constexpr (GRAM_LOADS)
       grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT0, sT1,
-                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, sPart, load_next, gate_next);
+                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, sPart, sXc, load_next, gate_next);
     else
       grams_fused<NT, C, D, SAFE>(sQ, sK, LDT, sB, LDB, sBeta, p.scale, sAkk, sAqk, LDA, sAqh, S::LDAH, L, sT0, sT1,
-                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, sPart, none, gate_next);
+                                  sT2, sBL, sKt, sXw, sTd, S::LDTD, sPart, sXc, none, gate_next);
     __syncthreads();
-    if (!HALF_LOAD && more) regs.load_qkv(p, ln.t0, ln.L, hn);
+    if (!GRAM_LOADS && more) regs.load_qkv(p, ln.t0, ln.L, hn);
     // (4): w^T to LDS, u of this wave's value tile straight to the workspace
     {
       f32x4_t W[NC], U[NC];
