@@ -642,8 +642,10 @@ __device__ __forceinline__ void state_side(const ChunkParams &p, char *smem, int
     if (c > 0) tail(t0p, Lp);
     __syncthreads();
     // ---- P2: column operands of block sidx (k~ into this chunk's parity buffer);
-    // the two heaviest state waves (blocks 0 and 1: the most exports) issue first
-    wait_vmem();
+    // the two heaviest state waves (blocks 0 and 1: the most exports) issue first.
+    // This chunk's k and v loads came before the previous chunk's eight o stores
+    // (P1), and vector memory operations retire in order: wait for all but those.
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
     if (sidx <= 1) __builtin_amdgcn_s_setprio(2);
     switch (sidx) {
       case 0: state_col_operands<0>(kr, smem, c & 1); break;
