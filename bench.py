@@ -105,6 +105,14 @@ def gpu_ramp(buf, seconds=0.3):
         torch.cuda.synchronize()
 
 
+def workspace_for(q, v, H, N, C, schedule, gate_kind):
+    """The call's workspace, allocated once so that no timed call allocates."""
+    from gated_delta_rule_gate_amd import workspace_bytes
+
+    n = workspace_bytes(q, v, H, N, chunk_size=C, schedule=schedule, gate_kind=gate_kind)
+    return torch.empty((max(n, 256),), dtype=torch.uint8, device=q.device)
+
+
 def event_time_ms(fn, steps, warmup, flush=None):
     """Mean / median / p10 / p90 of per-call HIP event times (ms) on the current stream.
     Warm-up calls run with the same flush as the timed ones."""
@@ -224,10 +232,11 @@ def bench_fp32_small(steps, warmup):
     dev = {k: v.cuda() for k, v in d.items() if v is not None}
     o = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
     ht = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ws = workspace_for(dev["q"], dev["v"], H, B, 64, "auto", "safe")
 
     def step():
         chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], None, chunk_size=64, gate_kind="safe",
-                  A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0, out=o, final_state=ht)
+                  A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0, out=o, final_state=ht, workspace=ws)
 
     t = event_time_ms(step, steps, warmup)
     ms = t["median"]
@@ -273,11 +282,12 @@ def bench_varlen(steps, warmup, schedule="auto"):
     o = torch.empty((1, CAP, H, D), dtype=torch.bfloat16, device="cuda")
     ht = torch.empty_like(dev["h0"])
     flush_buf = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+    ws = workspace_for(dev["q"], dev["v"], H, SLOTS, 64, schedule, "softplus")
 
     def step():
         chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], dev["h0"], cu_seqlens=cu_d, chunk_size=64,
                   gate_kind="softplus", A_log=dev["A_log"], dt_bias=dev["dt_bias"], out=o, final_state=ht,
-                  schedule=schedule)
+                  schedule=schedule, workspace=ws)
 
     t = event_time_ms(step, steps, warmup, flush=lambda: flush_buf.zero_())
     n = int(cu[-1])
@@ -422,11 +432,12 @@ def bench_shape(B, T, H, D, steps, warmup, schedule="auto", C=64):
     o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
     ht = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
     flush_buf = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+    ws = workspace_for(dev["q"], dev["v"], H, B, C, schedule, "safe")
 
     def step():
         chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], dev["h0"], chunk_size=C, gate_kind="safe",
                   A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0, schedule=schedule, out=o,
-                  final_state=ht)
+                  final_state=ht, workspace=ws)
 
     t = event_time_ms(step, steps, warmup, flush=lambda: flush_buf.zero_())
     ms = t["mean"]
@@ -478,11 +489,12 @@ def main():
     o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
     ht = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
     flush_buf = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+    ws = workspace_for(dev["q"], dev["v"], H, B, C, args.schedule, "safe")
 
     def step():
         chunk_kda(dev["q"], dev["k"], dev["v"], dev["x"], dev["beta"], dev["h0"], chunk_size=C, gate_kind="safe",
                   A_log=dev["A_log"], dt_bias=dev["dt_bias"], lower_bound=-5.0, schedule=args.schedule, out=o,
-                  final_state=ht)
+                  final_state=ht, workspace=ws)
 
     def flush():
         flush_buf.zero_()

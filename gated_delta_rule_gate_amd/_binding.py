@@ -228,7 +228,7 @@ def gate_cumsum(g, *, chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None,
 def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_final_state=False,
               chunk_size=64, gate_kind="safe", A_log=None, dt_bias=None, lower_bound=-5.0, scale=None,
               schedule="auto", final_state=None, out=None, q_l2norm=False, return_intermediate_states=False,
-              intermediate_states=None, beta_logits=False, segment=0):
+              intermediate_states=None, beta_logits=False, segment=0, workspace=None):
     """Chunked KDA prefill forward. Returns (o, ht); ht is None unless requested.
 
     g is the raw gate input for ``gate_kind`` "safe" / "softplus" (activation in
@@ -247,6 +247,9 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
     ``segment`` (split schedule): chunks per segment of the chain-parallel state
     scan; 0 lets the library choose from the sizes, -1 keeps one serial chain per
     (sequence, head). The states path always runs the serial chain.
+
+    ``workspace`` may pass a uint8 device tensor of at least ``workspace_bytes``
+    for these arguments, reused across calls; otherwise each call allocates one.
     """
     B, T, H, K, V, N = _common(q, k, v, g, beta, initial_state, cu_seqlens, A_log, dt_bias)
     _check_outputs(out, final_state, B, T, H, K, V, N, q.dtype, q.device)
@@ -259,7 +262,13 @@ def chunk_kda(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, output_f
                   segment=segment)
     L = lib()
     ws_bytes = L.kda_chunk_workspace_bytes(ctypes.byref(a))
-    ws = torch.empty((max(int(ws_bytes), 256),), dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _require(workspace.dtype == torch.uint8 and workspace.dim() == 1 and workspace.numel() >= ws_bytes,
+                 "workspace must be a 1-D uint8 tensor of at least %d bytes" % ws_bytes)
+        _check_tensors(dict(workspace=workspace), q.device)
+        ws = workspace
+    else:
+        ws = torch.empty((max(int(ws_bytes), 256),), dtype=torch.uint8, device=q.device)
     if not (return_intermediate_states or intermediate_states is not None):
         check(L.kda_chunk_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                               _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(ht), _ptr(ws),
@@ -332,8 +341,8 @@ def chunk_kda_bwd(q, k, v, g, beta, do, initial_state=None, *, dht=None, cu_seql
     return out
 
 
-def workspace_bytes(q, v, H, N, chunk_size=64, schedule="auto", segment=0):
-    a = make_args(q, v, H, N, "safe", chunk_size=chunk_size, schedule=schedule, segment=segment)
+def workspace_bytes(q, v, H, N, chunk_size=64, schedule="auto", segment=0, gate_kind="safe"):
+    a = make_args(q, v, H, N, gate_kind, chunk_size=chunk_size, schedule=schedule, segment=segment)
     return int(lib().kda_chunk_workspace_bytes(ctypes.byref(a)))
 
 

@@ -254,10 +254,26 @@ struct SplitRegs {
   }
 };
 
+// Workgroup index -> (unit, block) for `units` units of nb workgroups each:
+// workgroups are dealt to the eight XCDs in turn, so with a multiple of eight
+// units, unit u goes to XCD u % 8 and all nb workgroups of a unit to the same
+// XCD (they read the same records, through its L2). Units of unequal length
+// (packed slots) then spread over all XCDs instead of one XCD holding a run of
+// long ones while another idles.
+__device__ __forceinline__ void xcd_unit(int bid, int units, int nb, int &unit, int &blk) {
+  if (units % 8 == 0) {
+    const int x = bid % 8, k = bid / 8;
+    blk = k % nb;
+    unit = 8 * (k / nb) + x;
+  } else {
+    unit = bid / nb;
+    blk = bid % nb;
+  }
+}
+
 // (5), (6) and the state update of one (sequence, head, block of value tiles),
 // walking the sequence's chunks with the key side's operands from the
-// workspace. Workgroups of one (sequence, head) sit on one XCD (workgroups are
-// dealt to the XCDs round-robin), so they share its L2.
+// workspace.
 template <int C, int D>
 __global__ __launch_bounds__(kSplitThreads) void split_state_kernel(ChunkParams p) {
   using Tin = bf16_t;
@@ -276,10 +292,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_state_kernel(ChunkParams 
   float *sQn = reinterpret_cast<float *>(smem + S::qn);
 
   const int vs = D / 64;  // value-tile blocks per (sequence, head)
-  const int G = p.N * p.H * vs;
-  const int bid = blockIdx.x;
-  const int li = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  const int nh = li / vs, vb = li % vs;
+  int nh, vb;
+  xcd_unit(blockIdx.x, p.N * p.H, vs, nh, vb);
   const int n = nh / p.H, h = nh % p.H;
   const int wid = wave_id();
   const int ctu = vb * 4 + wid;
@@ -429,7 +443,9 @@ __global__ __launch_bounds__(kSplitThreads, 2) void split_seg_kernel(ChunkParams
   float *sDecay2 = reinterpret_cast<float *>(smem + S::decay);
   float *sQn = reinterpret_cast<float *>(smem + S::qn);
 
-  // the NB workgroups of one (segment, head) share an XCD and its L2
+  // the NB workgroups of one (segment, head) share an XCD and its L2; each XCD
+  // takes a contiguous range of (segment, head) units (segments of dense
+  // batches are of equal length, and the heads of one segment read adjacent records)
   const int G = p.seg_max * p.H * NB;
   const int bid = blockIdx.x;
   const int li = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
