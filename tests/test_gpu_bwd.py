@@ -21,6 +21,8 @@ in two parts instead:
   (b) as the sum of the GPU's own terms, to 1e-5 of their L1 norm (FP32
       accumulation).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -46,6 +48,11 @@ def grad_parity(got, want, kind, what):
     rel = float(np.sqrt(np.sum(diff * diff)) / den) if den > 0 else float(np.sqrt(np.sum(diff * diff)))
     mx = float(np.abs(diff).max()) if diff.size else 0.0
     ref = max(1.0, float(np.abs(want).max()) if want.size else 0.0)
+    log = os.environ.get("KDA_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write("%s | %s | %s | max-abs/ref %.3e | rel-RMS %.3e\n" % (
+                os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0], what, kind, mx / ref, rel))
     assert rel <= rel_b, "%s: rel-RMS %.3e > %.1e (max-abs %.3e)" % (what, rel, rel_b, mx)
     assert mx <= abs_b * ref, "%s: max-abs %.3e > %.1e * %.3g" % (what, mx, abs_b, ref)
 
