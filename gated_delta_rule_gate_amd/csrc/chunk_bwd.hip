@@ -102,35 +102,177 @@ __device__ __forceinline__ float beta_at(const ChunkParams &p, int64_t row, int 
   return p.beta_logits ? sigmoid_f32(b) : b;
 }
 
+// Raw buffer stores: offsets at or past `bytes` are dropped, so the masked rows
+// and channels of a tile need no branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t store_rsrc(void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void bstore_f32(rsrc_t r, uint32_t voff, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)voff, 0, 0);
+}
+
 // ---- scan: dv_new and the state gradients, reverse over the chunks ----
-// Per (sequence, head, 64 value columns); wave w keeps the state gradient of
-// its 16 columns in accumulator registers (C layout: tile t holds channels
-// 16t + 4(l/16) + e of column l % 16), which serve unchanged as the B operand
-// of the product with k~ under the contraction map of Mma<float>. The chunk's
-// k~, q~ and w pass through one LDS buffer in turn, so two workgroups fit on
-// a compute unit.
+// One workgroup per (sequence, head), D / 16 waves; wave w keeps the state
+// gradient of value columns 16w .. 16w + 15 in accumulator registers (C layout:
+// tile t holds channels 16t + 4(l/16) + e of column l % 16), which serve
+// unchanged as the B operand of the product with k~ under the contraction map
+// of Mma<float>. A chunk's operands (A_qk, do, k~, q~, w, b_L) each have an
+// LDS buffer, written from registers when the chunk starts; the loads of the
+// chunk before it (the next in the reverse walk) are issued right after, so
+// they are in flight while this chunk's products run.
+template <int C, int D>
+struct ScanSmem {
+  static constexpr int LA = C + 4, LX = D + 4;
+  static constexpr size_t a = 0;                // fp32 [C][LA] A_qk, causal
+  static constexpr size_t dO = a + 4 * C * LA;  // fp32 [C][LX] do (value columns)
+  static constexpr size_t k = dO + 4 * C * LX;  // fp32 [C][LX] k~ = k 2^(b_L - b)
+  static constexpr size_t q = k + 4 * C * LX;   // q~ = scale q 2^b
+  static constexpr size_t w = q + 4 * C * LX;   // w
+  static constexpr size_t bl = w + 4 * C * LX;  // fp32 [D] b_L
+  static constexpr size_t total = bl + 4 * D;
+  static_assert(total <= 160 * 1024, "LDS");
+};
+
+// One chunk's scan operands in registers, between their global loads and the
+// LDS stores. Thread t covers the same channel vector (t % VPR) in every row it
+// loads, so one b_L vector pair serves all of its k rows.
+template <typename Tin, int C, int D, int NT>
+struct ScanRegs {
+  static constexpr int EPV = 16 / (int)sizeof(Tin), NB = EPV / 4;  // inputs per vector; b vectors per input vector
+  static constexpr int NA = C * C / 4, IA = (NA + NT - 1) / NT;     // A_qk vectors
+  static constexpr int VPR = D / EPV, NI = C * VPR, II = (NI + NT - 1) / NT;  // do, k, q vectors
+  static constexpr int NF = C * D / 4, IF = (NF + NT - 1) / NT;     // w vectors
+  static_assert(NT % VPR == 0, "one channel vector per thread");
+  u32x4_t a[IA], dO[II], k[II], q[II], w[IF];
+  f32x4_t b[II][NB], bl[NB];
+
+  __device__ __forceinline__ void load(const ChunkParams &p, const BwdParams &bw, int64_t t0, int L, int h) {
+    const int t = threadIdx.x;
+    const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.H * p.Kr, ldv = (int64_t)p.H * p.Vr;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int it = 0; it < IA; ++it) {
+      const int idx = it * NT + t, r = idx / (C / 4), c = (idx % (C / 4)) * 4;
+      a[it] = ((NA % NT == 0 || idx < NA) && r < L)
+                  ? *reinterpret_cast<const u32x4_t *>(p.Aqk + (t0 + r) * ldc + h * C + c) : z;
+    }
+    const Tin *gdo = reinterpret_cast<const Tin *>(bw.dout) + t0 * ldv + h * p.Vr;
+    const Tin *gk = reinterpret_cast<const Tin *>(p.k) + t0 * ldk + h * p.Kr;
+    const Tin *gq = reinterpret_cast<const Tin *>(p.q) + t0 * ldk + h * p.Kr;
+    const float *gb = p.b + t0 * ld + h * D;
+#pragma unroll
+    for (int it = 0; it < II; ++it) {
+      const int idx = it * NT + t, r = idx / VPR, c = (idx % VPR) * EPV;
+      const bool ok = (NI % NT == 0 || idx < NI) && r < L;
+      dO[it] = ok && c < p.Vr ? *reinterpret_cast<const u32x4_t *>(gdo + r * ldv + c) : z;
+      k[it] = ok && c < p.Kr ? *reinterpret_cast<const u32x4_t *>(gk + r * ldk + c) : z;
+      q[it] = ok && c < p.Kr ? *reinterpret_cast<const u32x4_t *>(gq + r * ldk + c) : z;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) b[it][j] = ok ? ld4(gb + r * ld + c + 4 * j) : zero4();
+    }
+    const int c0 = (t % VPR) * EPV;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bl[j] = L > 0 ? ld4(gb + (int64_t)(L - 1) * ld + c0 + 4 * j) : zero4();
+  }
+
+  // w, loaded apart from the rest (later in the chunk before, where fewer registers are live)
+  __device__ __forceinline__ void load_w(const ChunkParams &p, int64_t t0, int L, int h) {
+    const int t = threadIdx.x;
+    const int64_t ld = (int64_t)p.H * D;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int it = 0; it < IF; ++it) {
+      const int idx = it * NT + t, r = idx / (D / 4), c = (idx % (D / 4)) * 4;
+      w[it] = ((NF % NT == 0 || idx < NF) && r < L)
+                  ? *reinterpret_cast<const u32x4_t *>(p.w + (t0 + r) * ld + h * D + c) : z;
+    }
+  }
+
+  // the EPV inputs of a vector as floats
+  static __device__ __forceinline__ void unpack(u32x4_t raw, float (&v)[EPV]) {
+    if constexpr (sizeof(Tin) == 4) {
+      const f32x4_t f = __builtin_bit_cast(f32x4_t, raw);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) v[e] = f[e];
+    } else {
+      const bf16x8_t f = __builtin_bit_cast(bf16x8_t, raw);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) v[e] = static_cast<float>(f[e]);
+    }
+  }
+
+  __device__ __forceinline__ void store(char *smem, float scale) const {
+    using S = ScanSmem<C, D>;
+    const int t = threadIdx.x;
+    float *sA = reinterpret_cast<float *>(smem + S::a), *sDo = reinterpret_cast<float *>(smem + S::dO);
+    float *sK = reinterpret_cast<float *>(smem + S::k), *sQ = reinterpret_cast<float *>(smem + S::q);
+    float *sW = reinterpret_cast<float *>(smem + S::w), *sBL = reinterpret_cast<float *>(smem + S::bl);
+#pragma unroll
+    for (int it = 0; it < IA; ++it) {
+      const int idx = it * NT + t, r = idx / (C / 4), c = (idx % (C / 4)) * 4;
+      if (NA % NT == 0 || idx < NA) {
+        f32x4_t v = __builtin_bit_cast(f32x4_t, a[it]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (c + e <= r) ? v[e] : 0.f;
+        *reinterpret_cast<f32x4_t *>(sA + r * S::LA + c) = v;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < II; ++it) {
+      const int idx = it * NT + t, r = idx / VPR, c = (idx % VPR) * EPV;
+      if (NI % NT == 0 || idx < NI) {
+        float fo[EPV], fk[EPV], fq[EPV];
+        unpack(dO[it], fo);
+        unpack(k[it], fk);
+        unpack(q[it], fq);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          f32x4_t ko, qo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ko[e] = fk[4 * j + e] * fast_exp2(bl[j][e] - b[it][j][e]);
+            qo[e] = fq[4 * j + e] * (scale * fast_exp2(b[it][j][e]));
+          }
+          *reinterpret_cast<f32x4_t *>(sDo + r * S::LX + c + 4 * j) =
+              f32x4_t{fo[4 * j], fo[4 * j + 1], fo[4 * j + 2], fo[4 * j + 3]};
+          *reinterpret_cast<f32x4_t *>(sK + r * S::LX + c + 4 * j) = ko;
+          *reinterpret_cast<f32x4_t *>(sQ + r * S::LX + c + 4 * j) = qo;
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < IF; ++it) {
+      const int idx = it * NT + t, r = idx / (D / 4), c = (idx % (D / 4)) * 4;
+      if (NF % NT == 0 || idx < NF) *reinterpret_cast<u32x4_t *>(sW + r * S::LX + c) = w[it];
+    }
+    if (t < VPR) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) *reinterpret_cast<f32x4_t *>(sBL + t * EPV + 4 * j) = bl[j];
+    }
+  }
+};
+
 template <typename Tin, int C, int D>
-__global__ __launch_bounds__(kBT, 2) void bwd_scan_kernel(ChunkParams p, BwdParams bw) {
+__global__ __launch_bounds__(4 * D) void bwd_scan_kernel(ChunkParams p, BwdParams bw) {
   using M = Mma<float>;
-  constexpr int BV = 64, LH = BV + 4, LA = C + 4, LX = D + 4, NC = C / 16, DT = D / 16;
-  const int nvb = (p.Vr + BV - 1) / BV;
-  const int vb = blockIdx.x % nvb, nh = blockIdx.x / nvb;
+  using S = ScanSmem<C, D>;
+  constexpr int NT = 4 * D, NC = C / 16, DT = D / 16, LA = S::LA, LX = S::LX;
+  const int nh = blockIdx.x;
   const int n = nh / p.H, h = nh % p.H;
   const int wid = wave_id();
-  const int col0 = vb * BV, jc = col0 + 16 * wid + (threadIdx.x & 15);  // this lane's value column
+  const int n16 = tid_opaque() & 15, grp = (tid_opaque() & 63) >> 4;
+  const int jc = 16 * wid + n16;  // this lane's value column
   const int Kr = p.Kr, Vr = p.Vr;
   const SlotRange sr = slot_range(p.cu, n, p.T);
   const int nch = (sr.len + C - 1) / C;
   const int cbase = p.cu ? p.chunk_off[n] : n * ((p.T + C - 1) / C);
   const int64_t sbase = (int64_t)nh * Kr * Vr;
-  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.H * Kr, ldv = (int64_t)p.H * Vr;
+  const int64_t ld = (int64_t)p.H * D;
   extern __shared__ __align__(16) char smem[];
-  float *sA = reinterpret_cast<float *>(smem);  // [C][LA] A_qk
-  float *sDo = sA + C * LA;                     // [C][LH] do
-  float *sX = sDo + C * LH;                     // [C][LX] k~, then q~, then w
-  float *sBL = sX + C * LX;                     // [D] b_L
-  const Tin *gq = reinterpret_cast<const Tin *>(p.q), *gk = reinterpret_cast<const Tin *>(p.k);
-  const Tin *gdo = reinterpret_cast<const Tin *>(bw.dout);
+  const float *sA = reinterpret_cast<const float *>(smem + S::a), *sDo = reinterpret_cast<const float *>(smem + S::dO);
+  const float *sK = reinterpret_cast<const float *>(smem + S::k), *sQ = reinterpret_cast<const float *>(smem + S::q);
+  const float *sW = reinterpret_cast<const float *>(smem + S::w), *sBL = reinterpret_cast<const float *>(smem + S::bl);
 
   f32x4_t dh[DT];
 #pragma unroll
@@ -140,87 +282,53 @@ __global__ __launch_bounds__(kBT, 2) void bwd_scan_kernel(ChunkParams p, BwdPara
       const int i = 16 * t + tile_row(e);
       dh[t][e] = (bw.dht && i < Kr && jc < Vr) ? bw.dht[sbase + (int64_t)i * Vr + jc] : 0.f;
     }
+  ScanRegs<Tin, C, D, NT> R;
+  if (nch > 0) {
+    const int c = nch - 1;
+    R.load(p, bw, sr.t0 + (int64_t)c * C, min(C, sr.len - c * C), h);
+    R.load_w(p, sr.t0 + (int64_t)c * C, min(C, sr.len - c * C), h);
+  }
   for (int c = nch - 1; c >= 0; --c) {
     const int64_t t0 = sr.t0 + (int64_t)c * C;
     const int L = min(C, sr.len - c * C);
     const int64_t gc = cbase + c;
-    const float *gb = p.b + t0 * ld + h * D;  // this chunk's rows of b (log2)
-    const float *gbl = gb + (int64_t)(L - 1) * ld;
-    // gradient of the state after this chunk
+    R.store(smem, p.scale);
+    // gradient of the state after this chunk (channels past Kr fall outside the range)
     if (jc < Vr) {
-      float *dhn = bw.dhn + (gc * p.H + h) * Kr * Vr;
+      const rsrc_t rdh = store_rsrc(bw.dhn + (gc * p.H + h) * Kr * Vr, (uint32_t)(Kr * Vr) * 4u);
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * t + tile_row(e);
-          if (i < Kr) dhn[(int64_t)i * Vr + jc] = dh[t][e];
-        }
+        for (int e = 0; e < 4; ++e) bstore_f32(rdh, (uint32_t)((16 * t + tile_row(e)) * Vr + jc) * 4u, dh[t][e]);
     }
-    tile_f32<float, C, C>(sA, LA, p.Aqk + t0 * ldc + h * C, ldc, L, C, [](int r, int cc, float *v) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (cc + e <= r) ? v[e] : 0.f;
-    });
-    tile_f32<Tin, C, BV>(sDo, LH, gdo + t0 * ldv + h * Vr + col0, ldv, L, Vr - col0);
-    tile_f32<Tin, C, D>(sX, LX, gk + t0 * ldk + h * Kr, ldk, L, Kr, [&](int r, int cc, float *v) {
-      if (r >= L) return;
-#pragma unroll
-      for (int e = 0; e < 16 / (int)sizeof(Tin); e += 4) {
-        const f32x4_t bl = ld4(gbl + cc + e), br = ld4(gb + (int64_t)r * ld + cc + e);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[e + u] *= fast_exp2(bl[u] - br[u]);
-      }
-    });
-    for (int i = threadIdx.x; i < D; i += kBT) sBL[i] = gbl[i];
     __syncthreads();
-    // dv_new = A_qk^T do + k~ dh
+    if (c > 0) R.load(p, bw, t0 - C, C, h);  // every chunk but a slot's last has C rows
+    // dv_new = A_qk^T do + k~ dh (rows past L fall outside the range)
+    const rsrc_t rdv = store_rsrc(bw.dvn + t0 * ld + h * D, (uint32_t)((L - 1) * ld + D) * 4u);
     f32x4_t dv[NC];
 #pragma unroll
     for (int rt = 0; rt < NC; ++rt) {
-      const int n16 = tid_opaque() & 15, grp = (tid_opaque() & 63) >> 4;
-      f32x4_t acc = mm16<C>(zero4(), sA, 1, LA, sDo, LH, 1, 16 * rt, 16 * wid);
+      f32x4_t acc = mm16<C>(zero4(), sA, 1, LA, sDo, LX, 1, 16 * rt, 16 * wid);
 #pragma unroll
       for (int st = 0; st < D / 4; ++st)
-        acc = M::mma(sX[(16 * rt + n16) * LX + M::kidx(st, grp, 0)], dh[st >> 2][st & 3], acc);  // dh: registers
+        acc = M::mma(sK[(16 * rt + n16) * LX + M::kidx(st, grp, 0)], dh[st >> 2][st & 3], acc);  // dh: registers
       dv[rt] = acc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + tile_row(e);
-        if (r < L) bw.dvn[(t0 + r) * ld + h * D + jc] = acc[e];
-      }
+      for (int e = 0; e < 4; ++e) bstore_f32(rdv, (uint32_t)((16 * rt + tile_row(e)) * ld + jc) * 4u, acc[e]);
     }
-    __syncthreads();
-    tile_f32<Tin, C, D>(sX, LX, gq + t0 * ldk + h * Kr, ldk, L, Kr, [&](int r, int cc, float *v) {
-      if (r >= L) return;
-#pragma unroll
-      for (int e = 0; e < 16 / (int)sizeof(Tin); e += 4) {
-        const f32x4_t br = ld4(gb + (int64_t)r * ld + cc + e);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[e + u] *= p.scale * fast_exp2(br[u]);
-      }
-    });
-    __syncthreads();
-    // dh <- 2^b_L dh + q~^T do
+    if (c > 0) R.load_w(p, t0 - C, C, h);
+    // dh <- 2^b_L dh + q~^T do - w^T dv_new (dv_new from registers, under the same contraction map)
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      const f32x4_t acc = mm16<C>(zero4(), sX, 1, LX, sDo, LH, 1, 16 * t, 16 * wid);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dh[t][e] = fast_exp2(sBL[16 * t + tile_row(e)]) * dh[t][e] + acc[e];
-    }
-    __syncthreads();
-    tile_f32<float, C, D>(sX, LX, p.w + t0 * ld + h * D, ld, L, D);
-    __syncthreads();
-    // dh -= w^T dv_new (dv_new from registers, under the same contraction map)
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const int n16 = tid_opaque() & 15, grp = (tid_opaque() & 63) >> 4;
-      f32x4_t acc = zero4();
+      f32x4_t acc = mm16<C>(zero4(), sQ, 1, LX, sDo, LX, 1, 16 * t, 16 * wid);
+      f32x4_t wv = zero4();
 #pragma unroll
       for (int st = 0; st < C / 4; ++st)
-        acc = M::mma(sX[M::kidx(st, grp, 0) * LX + 16 * t + n16], dv[st >> 2][st & 3], acc);
-      dh[t] = dh[t] - acc;
+        wv = M::mma(sW[M::kidx(st, grp, 0) * LX + 16 * t + n16], dv[st >> 2][st & 3], wv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh[t][e] = fast_exp2(sBL[16 * t + tile_row(e)]) * dh[t][e] + acc[e] - wv[e];
     }
-    __syncthreads();  // sA, sDo and sX are rewritten by the next chunk
+    __syncthreads();  // every buffer is rewritten by the next chunk
   }
   if (bw.dh0 && jc < Vr) {
 #pragma unroll
@@ -759,7 +867,8 @@ __global__ __launch_bounds__(kBT) void bwd_params_kernel(ChunkParams p, BwdParam
 }
 
 template <typename Kern>
-hipError_t launch_k(Kern kernel, dim3 grid, size_t smem, hipStream_t st, const ChunkParams &p, const BwdParams &b) {
+hipError_t launch_k(Kern kernel, dim3 grid, size_t smem, hipStream_t st, const ChunkParams &p, const BwdParams &b,
+                    int threads = kBT) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
@@ -769,7 +878,7 @@ hipError_t launch_k(Kern kernel, dim3 grid, size_t smem, hipStream_t st, const C
       return e;
     }
   }
-  hipLaunchKernelGGL(kernel, grid, dim3(kBT), smem, st, p, b);
+  hipLaunchKernelGGL(kernel, grid, dim3(threads), smem, st, p, b);
   return hipGetLastError();
 }
 
@@ -777,12 +886,9 @@ template <typename Tin, int C, int D>
 hipError_t launch_bwd_t(const ChunkParams &p, const BwdParams &b, hipStream_t st) {
   constexpr int LA = C + 4, LX = D + 4;
   hipError_t e;
-  {
-    constexpr int LH = 64 + 4;
-    const size_t smem = sizeof(float) * ((size_t)C * LA + C * LH + C * LX + D);
-    const int nvb = (p.Vr + 63) / 64;
-    if ((e = launch_k(bwd_scan_kernel<Tin, C, D>, dim3(p.N * p.H * nvb), smem, st, p, b)) != hipSuccess) return e;
-  }
+  if ((e = launch_k(bwd_scan_kernel<Tin, C, D>, dim3(p.N * p.H), ScanSmem<C, D>::total, st, p, b, 4 * D)) !=
+      hipSuccess)
+    return e;
   const dim3 grid(p.max_chunks, p.H);
   {
     constexpr int LS = 32 + 4;
