@@ -342,19 +342,128 @@ __global__ __launch_bounds__(4 * D) void bwd_scan_kernel(ChunkParams p, BwdParam
 }
 
 // ---- contractions over the value columns ----
+// Persistent workgroups of eight waves walk (chunk, head) items, each in slabs
+// of SJ value columns; the next slab's tiles (of the same item or the next
+// one) are loaded into registers while the current slab's products run. Wave
+// w accumulates its share of the output tiles over the item's slabs.
+template <typename Tin, int C, int D, int NT>
+struct ContractRegs {
+  static constexpr int SJ = 32, EPV = 16 / (int)sizeof(Tin);
+  static constexpr int VI = C * SJ / EPV, II = (VI + NT - 1) / NT;  // do, v vectors of a slab
+  static constexpr int VF = C * SJ / 4, IF = (VF + NT - 1) / NT;    // v_new, dv_new
+  static constexpr int VH = D * SJ / 4, IH = (VH + NT - 1) / NT;    // h, dh'
+  u32x4_t dO[II], v[II], vn[IF], dvn[IF], hh[IH], dh[IH];
+  float beta;
+
+  // slab j0 of the chunk at t0 (L rows, global index gci) and head h
+  __device__ __forceinline__ void load(const ChunkParams &p, const BwdParams &bw, int64_t t0, int L, int gci, int h,
+                                       int j0) {
+    const int t = threadIdx.x;
+    const int Kr = p.Kr, Vr = p.Vr, nj = Vr - j0;
+    const int64_t ld = (int64_t)p.H * D, ldv = (int64_t)p.H * Vr;
+    const int64_t hbase = ((int64_t)gci * p.H + h) * Kr * Vr + j0;
+    const Tin *gdo = reinterpret_cast<const Tin *>(bw.dout) + t0 * ldv + h * Vr + j0;
+    const Tin *gv = reinterpret_cast<const Tin *>(p.v) + t0 * ldv + h * Vr + j0;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int it = 0; it < II; ++it) {
+      const int idx = it * NT + t, r = idx / (SJ / EPV), c = (idx % (SJ / EPV)) * EPV;
+      const bool ok = (VI % NT == 0 || idx < VI) && r < L && c < nj;
+      dO[it] = ok ? *reinterpret_cast<const u32x4_t *>(gdo + r * ldv + c) : z;
+      v[it] = ok ? *reinterpret_cast<const u32x4_t *>(gv + r * ldv + c) : z;
+    }
+#pragma unroll
+    for (int it = 0; it < IF; ++it) {
+      const int idx = it * NT + t, r = idx / (SJ / 4), c = (idx % (SJ / 4)) * 4;
+      const bool ok = (VF % NT == 0 || idx < VF) && r < L && c < nj;
+      const int64_t o = (t0 + r) * ld + h * D + j0 + c;
+      vn[it] = ok ? *reinterpret_cast<const u32x4_t *>(p.vnew + o) : z;
+      dvn[it] = ok ? *reinterpret_cast<const u32x4_t *>(bw.dvn + o) : z;
+    }
+#pragma unroll
+    for (int it = 0; it < IH; ++it) {
+      const int idx = it * NT + t, i = idx / (SJ / 4), c = (idx % (SJ / 4)) * 4;
+      const bool ok = (VH % NT == 0 || idx < VH) && i < Kr && c < nj;
+      const int64_t o = hbase + (int64_t)i * Vr + c;
+      hh[it] = ok ? *reinterpret_cast<const u32x4_t *>(p.hc + o) : z;
+      dh[it] = ok ? *reinterpret_cast<const u32x4_t *>(bw.dhn + o) : z;
+    }
+    if (t < C) beta = t < L ? beta_at(p, t0 + t, h) : 0.f;
+  }
+
+  static __device__ __forceinline__ void put(float *s, int lds, int r, int c, u32x4_t raw) {
+    if constexpr (sizeof(Tin) == 4) {
+      *reinterpret_cast<u32x4_t *>(s + r * lds + c) = raw;
+    } else {
+      const bf16x8_t f = __builtin_bit_cast(bf16x8_t, raw);
+      *reinterpret_cast<f32x4_t *>(s + r * lds + c) = f32x4_t{(float)f[0], (float)f[1], (float)f[2], (float)f[3]};
+      *reinterpret_cast<f32x4_t *>(s + r * lds + c + 4) = f32x4_t{(float)f[4], (float)f[5], (float)f[6], (float)f[7]};
+    }
+  }
+
+  // the slab's tiles to LDS; beta of a new item first (v's rows are scaled by it)
+  __device__ __forceinline__ void store(float *sDo, float *sVn, float *sDvn, float *sBv, float *sH, float *sDhn,
+                                        float *sBeta, int lds, bool item_start) const {
+    const int t = threadIdx.x;
+    if (item_start) {
+      if (t < C) sBeta[t] = beta;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int it = 0; it < II; ++it) {
+      const int idx = it * NT + t, r = idx / (SJ / EPV), c = (idx % (SJ / EPV)) * EPV;
+      if (VI % NT == 0 || idx < VI) {
+        put(sDo, lds, r, c, dO[it]);
+        float f[EPV];
+        if constexpr (sizeof(Tin) == 4) {
+          const f32x4_t x = __builtin_bit_cast(f32x4_t, v[it]);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) f[e] = x[e];
+        } else {
+          const bf16x8_t x = __builtin_bit_cast(bf16x8_t, v[it]);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) f[e] = (float)x[e];
+        }
+        const float be = sBeta[r];
+#pragma unroll
+        for (int e = 0; e < EPV; e += 4)
+          *reinterpret_cast<f32x4_t *>(sBv + r * lds + c + e) =
+              f32x4_t{f[e] * be, f[e + 1] * be, f[e + 2] * be, f[e + 3] * be};
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < IF; ++it) {
+      const int idx = it * NT + t, r = idx / (SJ / 4), c = (idx % (SJ / 4)) * 4;
+      if (VF % NT == 0 || idx < VF) {
+        *reinterpret_cast<u32x4_t *>(sVn + r * lds + c) = vn[it];
+        *reinterpret_cast<u32x4_t *>(sDvn + r * lds + c) = dvn[it];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < IH; ++it) {
+      const int idx = it * NT + t, i = idx / (SJ / 4), c = (idx % (SJ / 4)) * 4;
+      if (VH % NT == 0 || idx < VH) {
+        *reinterpret_cast<u32x4_t *>(sH + i * lds + c) = hh[it];
+        *reinterpret_cast<u32x4_t *>(sDhn + i * lds + c) = dh[it];
+      }
+    }
+  }
+};
+
+constexpr int kContractThreads = 512;
+
 template <typename Tin, int C, int D>
-__global__ __launch_bounds__(kBT) void bwd_contract_kernel(ChunkParams p, BwdParams bw) {
-  ChunkLoc lc;
-  if (!locate_chunk(p, blockIdx.x, lc)) return;
-  const int h = blockIdx.y;
-  constexpr int SJ = 32, LS = SJ + 4, NC = C / 16, DT = D / 16;
-  constexpr int NTW = NC * DT / 4, NCW = NC * NC / 4;  // tiles per wave of a [C][D] and a [C][C] product
-  static_assert(NTW >= 1 && NCW >= 1, "tiles per wave");
+__global__ __launch_bounds__(kContractThreads) void bwd_contract_kernel(ChunkParams p, BwdParams bw) {
+  constexpr int NT = kContractThreads, NW = NT / 64;
+  using R = ContractRegs<Tin, C, D, NT>;
+  constexpr int SJ = R::SJ, LS = SJ + 4, NC = C / 16, DT = D / 16;
+  constexpr int NTW = (NC * DT + NW - 1) / NW, NCW = (NC * NC + NW - 1) / NW;  // tiles per wave
   const int wid = threadIdx.x >> 6;
-  const int Kr = p.Kr, Vr = p.Vr, L = lc.L;
-  const int64_t t0 = lc.t0;
-  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldv = (int64_t)p.H * Vr;
-  const int64_t hbase = ((int64_t)lc.gci * p.H + h) * Kr * Vr;
+  const int total = p.cu ? p.chunk_off[p.N] : p.B * ((p.T + C - 1) / C);
+  const int64_t items = (int64_t)total * p.H;
+  const int nsl = (p.Vr + SJ - 1) / SJ;
+  const int64_t steps = items > blockIdx.x ? ((items - 1 - blockIdx.x) / gridDim.x + 1) * nsl : 0;
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C;
   extern __shared__ __align__(16) char smem[];
   float *sDo = reinterpret_cast<float *>(smem);  // [C][LS] slabs of SJ value columns
   float *sVn = sDo + C * LS;
@@ -363,79 +472,102 @@ __global__ __launch_bounds__(kBT) void bwd_contract_kernel(ChunkParams p, BwdPar
   float *sH = sBv + C * LS;  // [D][LS]
   float *sDhn = sH + D * LS;
   float *sBeta = sDhn + D * LS;  // [C]
-  const Tin *gdo = reinterpret_cast<const Tin *>(bw.dout), *gv = reinterpret_cast<const Tin *>(p.v);
 
-  for (int r = threadIdx.x; r < C; r += kBT) sBeta[r] = r < L ? beta_at(p, t0 + r, h) : 0.f;
+  // step s -> item (chunk, head) and slab
+  auto at = [&](int64_t st, ChunkLoc &lc, int &h, int &j0) {
+    const int64_t it = blockIdx.x + (st / nsl) * gridDim.x;
+    h = (int)(it % p.H);
+    locate_chunk(p, (int)(it / p.H), lc);
+    j0 = (int)(st % nsl) * SJ;
+  };
+  R regs;
+  if (steps > 0) {
+    ChunkLoc lc;
+    int h, j0;
+    at(0, lc, h, j0);
+    regs.load(p, bw, lc.t0, lc.L, lc.gci, h, j0);
+  }
   float dlam = 0.f;  // this thread's channel (threads < D): sum over j of h dh'
-  f32x4_t aq[NTW], ak[NTW], aw[NTW], aa[NCW], at[NCW];
+  f32x4_t aq[NTW], ak[NTW], aw[NTW], aa[NCW], at2[NCW];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) aq[t] = ak[t] = aw[t] = zero4();
 #pragma unroll
-  for (int t = 0; t < NCW; ++t) aa[t] = at[t] = zero4();
+  for (int t = 0; t < NCW; ++t) aa[t] = at2[t] = zero4();
 
-  for (int j0 = 0; j0 < Vr; j0 += SJ) {
-    __syncthreads();  // the previous slab is consumed
-    const int nj = Vr - j0;
-    tile_f32<Tin, C, SJ>(sDo, LS, gdo + t0 * ldv + h * Vr + j0, ldv, L, nj);
-    tile_f32<float, C, SJ>(sVn, LS, p.vnew + t0 * ld + h * D + j0, ld, L, nj);
-    tile_f32<float, C, SJ>(sDvn, LS, bw.dvn + t0 * ld + h * D + j0, ld, L, nj);
-    tile_f32<Tin, C, SJ>(sBv, LS, gv + t0 * ldv + h * Vr + j0, ldv, L, nj, [&](int r, int, float *v) {
-      if (r >= L) return;
-      const float be = sBeta[r];
-#pragma unroll
-      for (int e = 0; e < 16 / (int)sizeof(Tin); ++e) v[e] *= be;
-    });
-    tile_f32<float, D, SJ>(sH, LS, p.hc + hbase + j0, Vr, Kr, nj);
-    tile_f32<float, D, SJ>(sDhn, LS, bw.dhn + hbase + j0, Vr, Kr, nj);
+  for (int64_t st = 0; st < steps; ++st) {
+    ChunkLoc lc;
+    int h, j0;
+    at(st, lc, h, j0);
+    regs.store(sDo, sVn, sDvn, sBv, sH, sDhn, sBeta, LS, j0 == 0);
     __syncthreads();
-    for (int i = threadIdx.x; i < D; i += kBT) {
+    if (st + 1 < steps) {
+      ChunkLoc ln;
+      int hn, jn;
+      at(st + 1, ln, hn, jn);
+      regs.load(p, bw, ln.t0, ln.L, ln.gci, hn, jn);
+    }
+    if (threadIdx.x < D) {
       float acc = 0.f;
 #pragma unroll 8
-      for (int j = 0; j < SJ; ++j) acc += sH[i * LS + j] * sDhn[i * LS + j];
+      for (int j = 0; j < SJ; ++j) acc += sH[threadIdx.x * LS + j] * sDhn[threadIdx.x * LS + j];
       dlam += acc;
     }
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       const int tile = wid * NTW + t, rt = tile / DT, ct = tile % DT;
-      aq[t] = mm16<SJ>(aq[t], sDo, LS, 1, sH, 1, LS, 16 * rt, 16 * ct);    // do h^T
-      ak[t] = mm16<SJ>(ak[t], sVn, LS, 1, sDhn, 1, LS, 16 * rt, 16 * ct);  // v_new dh'^T
-      aw[t] = mm16<SJ>(aw[t], sDvn, LS, 1, sH, 1, LS, 16 * rt, 16 * ct);   // dv_new h^T
+      if (NC * DT % NW == 0 || tile < NC * DT) {
+        aq[t] = mm16<SJ>(aq[t], sDo, LS, 1, sH, 1, LS, 16 * rt, 16 * ct);    // do h^T
+        ak[t] = mm16<SJ>(ak[t], sVn, LS, 1, sDhn, 1, LS, 16 * rt, 16 * ct);  // v_new dh'^T
+        aw[t] = mm16<SJ>(aw[t], sDvn, LS, 1, sH, 1, LS, 16 * rt, 16 * ct);   // dv_new h^T
+      }
     }
 #pragma unroll
     for (int t = 0; t < NCW; ++t) {
-      const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
-      aa[t] = mm16<SJ>(aa[t], sDo, LS, 1, sVn, 1, LS, 16 * rt, 16 * st);   // do v_new^T
-      at[t] = mm16<SJ>(at[t], sDvn, LS, 1, sBv, 1, LS, 16 * rt, 16 * st);  // dv_new (beta v)^T
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    const int tile = wid * NTW + t, rt = tile / DT, ct = tile % DT;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + tile_row(e), i = 16 * ct + tile_col();
-      if (r < L) {
-        const int64_t o = (t0 + r) * ld + h * D + i;
-        bw.dqt[o] = aq[t][e];
-        bw.dkt[o] = ak[t][e];
-        bw.dw[o] = -aw[t][e];
+      const int tile = wid * NCW + t, rt = tile / NC, sc = tile % NC;
+      if (NC * NC % NW == 0 || tile < NC * NC) {
+        aa[t] = mm16<SJ>(aa[t], sDo, LS, 1, sVn, 1, LS, 16 * rt, 16 * sc);    // do v_new^T
+        at2[t] = mm16<SJ>(at2[t], sDvn, LS, 1, sBv, 1, LS, 16 * rt, 16 * sc);  // dv_new (beta v)^T
       }
     }
-  }
+    if (j0 + SJ >= p.Vr) {  // the item's last slab: its outputs (rows past L fall outside the ranges)
+      const int64_t t0 = lc.t0;
+      const uint32_t bytes = (uint32_t)((lc.L - 1) * ld + D) * 4u, bytc = (uint32_t)((lc.L - 1) * ldc + C) * 4u;
+      const rsrc_t rq = store_rsrc(bw.dqt + t0 * ld + h * D, bytes), rk = store_rsrc(bw.dkt + t0 * ld + h * D, bytes);
+      const rsrc_t rw = store_rsrc(bw.dw + t0 * ld + h * D, bytes);
+      const rsrc_t ra = store_rsrc(bw.dAqk + t0 * ldc + h * C, bytc), rt_ = store_rsrc(bw.dT + t0 * ldc + h * C, bytc);
 #pragma unroll
-  for (int t = 0; t < NCW; ++t) {
-    const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
+      for (int t = 0; t < NTW; ++t) {
+        const int tile = wid * NTW + t, rt = tile / DT, ct = tile % DT;
+        if (NC * DT % NW == 0 || tile < NC * DT) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + tile_row(e), s = 16 * st + tile_col();
-      if (r < L) {
-        const int64_t o = (t0 + r) * ldc + h * C + s;
-        bw.dAqk[o] = (s <= r) ? aa[t][e] : 0.f;
-        bw.dT[o] = at[t][e];
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t o = (uint32_t)((16 * rt + tile_row(e)) * ld + 16 * ct + tile_col()) * 4u;
+            bstore_f32(rq, o, aq[t][e]);
+            bstore_f32(rk, o, ak[t][e]);
+            bstore_f32(rw, o, -aw[t][e]);
+          }
+        }
+        aq[t] = ak[t] = aw[t] = zero4();
       }
+#pragma unroll
+      for (int t = 0; t < NCW; ++t) {
+        const int tile = wid * NCW + t, rt = tile / NC, sc = tile % NC;
+        if (NC * NC % NW == 0 || tile < NC * NC) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rt + tile_row(e), s2 = 16 * sc + tile_col();
+            const uint32_t o = (uint32_t)(r * ldc + s2) * 4u;
+            bstore_f32(ra, o, (s2 <= r) ? aa[t][e] : 0.f);
+            bstore_f32(rt_, o, at2[t][e]);
+          }
+        }
+        aa[t] = at2[t] = zero4();
+      }
+      if (threadIdx.x < D) bw.dlam[((int64_t)lc.gci * p.H + h) * D + threadIdx.x] = dlam;
+      dlam = 0.f;
     }
+    __syncthreads();  // the slab is consumed before the next one is stored
   }
-  for (int i = threadIdx.x; i < D; i += kBT) bw.dlam[((int64_t)lc.gci * p.H + h) * D + i] = dlam;
 }
 
 // ---- the WY factors and the triangular inverse ----
@@ -847,22 +979,48 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
   if (threadIdx.x == 0 && bw.dA_part) bw.dA_part[(int64_t)lc.gci * p.H + h] = dA_total;
 }
 
-// ---- dA_log and ddt_bias: sums of the per-chunk parts, in chunk order ----
+// ---- dA_log and ddt_bias: sums of the per-chunk parts ----
+// Per head: the chunks split into contiguous ranges, each summed in chunk order
+// by one thread, and the range sums added in range order (a fixed order: the
+// result does not vary from run to run).
 template <int D>
 __global__ __launch_bounds__(kBT) void bwd_params_kernel(ChunkParams p, BwdParams bw) {
-  const int h = blockIdx.x;
+  constexpr int G = kBT / 64;  // chunk ranges per channel
+  __shared__ float sPart[kBT];
+  const int h = blockIdx.x, t = threadIdx.x;
   const int total = p.cu ? p.chunk_off[p.N] : p.B * ((p.T + p.C - 1) / p.C);
   if (bw.ddt) {
-    for (int i = threadIdx.x; i < p.Kr; i += kBT) {
+    const int lane = t % 64, g = t / 64;
+    const int g0 = (int)((int64_t)total * g / G), g1 = (int)((int64_t)total * (g + 1) / G);
+    for (int i0 = 0; i0 < p.Kr; i0 += 64) {
+      const int i = i0 + lane;
       float acc = 0.f;
-      for (int gc = 0; gc < total; ++gc) acc += bw.ddt_part[((int64_t)gc * p.H + h) * D + i];
-      bw.ddt[h * p.Kr + i] = acc;
+      if (i < p.Kr) {
+#pragma unroll 8
+        for (int gc = g0; gc < g1; ++gc) acc += bw.ddt_part[((int64_t)gc * p.H + h) * D + i];
+      }
+      sPart[t] = acc;
+      __syncthreads();
+      if (g == 0 && i < p.Kr) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < G; ++q) sum += sPart[64 * q + lane];
+        bw.ddt[h * p.Kr + i] = sum;
+      }
+      __syncthreads();
     }
   }
-  if (bw.dA_log && threadIdx.x == 0) {
+  if (bw.dA_log) {
+    const int g0 = (int)((int64_t)total * t / kBT), g1 = (int)((int64_t)total * (t + 1) / kBT);
     float acc = 0.f;
-    for (int gc = 0; gc < total; ++gc) acc += bw.dA_part[(int64_t)gc * p.H + h];
-    bw.dA_log[h] = acc;
+    for (int gc = g0; gc < g1; ++gc) acc += bw.dA_part[(int64_t)gc * p.H + h];
+    sPart[t] = acc;
+    __syncthreads();
+    if (t == 0) {
+      float sum = 0.f;
+      for (int q = 0; q < kBT; ++q) sum += sPart[q];
+      bw.dA_log[h] = sum;
+    }
   }
 }
 
@@ -893,7 +1051,10 @@ hipError_t launch_bwd_t(const ChunkParams &p, const BwdParams &b, hipStream_t st
   {
     constexpr int LS = 32 + 4;
     const size_t smem = sizeof(float) * ((size_t)4 * C * LS + 2 * D * LS + C);
-    if ((e = launch_k(bwd_contract_kernel<Tin, C, D>, grid, smem, st, p, b)) != hipSuccess) return e;
+    const int64_t items = (int64_t)p.max_chunks * p.H;
+    const int wgs = (int)std::min<int64_t>(items, device_cus());
+    if ((e = launch_k(bwd_contract_kernel<Tin, C, D>, dim3(wgs), smem, st, p, b, kContractThreads)) != hipSuccess)
+      return e;
   }
   {
     const size_t smem = sizeof(float) * ((size_t)3 * C * LA + 2 * C * (32 + 4) + C);
