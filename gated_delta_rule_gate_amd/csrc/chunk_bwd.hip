@@ -571,134 +571,281 @@ __global__ __launch_bounds__(kContractThreads) void bwd_contract_kernel(ChunkPar
 }
 
 // ---- the WY factors and the triangular inverse ----
-template <typename Tin, int C, int D>
-__global__ __launch_bounds__(kBT) void bwd_wy_kernel(ChunkParams p, BwdParams bw) {
-  ChunkLoc lc;
-  if (!locate_chunk(p, blockIdx.x, lc)) return;
-  const int h = blockIdx.y;
-  // the [C][D] operands pass through two slabs of SW columns, so two workgroups fit a compute unit
-  constexpr int SW = 32, LA = C + 4, LS = SW + 4, NC = C / 16, ST = SW / 16;
-  constexpr int NCW = NC * NC / 4, NSW = NC * ST / 4, TPR = kBT / C;
-  static_assert(NCW >= 1 && NSW >= 1 && D % SW == 0, "tiles per wave");
-  const int wid = threadIdx.x >> 6;
-  const int Kr = p.Kr, Vr = p.Vr, L = lc.L;
-  const int64_t t0 = lc.t0;
-  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.H * Kr, ldv = (int64_t)p.H * Vr;
-  extern __shared__ __align__(16) char smem[];
-  float *sT = reinterpret_cast<float *>(smem);  // [C][LA] T
-  float *sDT = sT + C * LA;                     // [C][LA] dT
-  float *sX = sDT + C * LA;                     // [C][LA] dT T^T
-  float *sA = sX + C * LA;                      // [C][LS] slab of dw, later of dX_u
-  float *sB = sA + C * LS;                      // [C][LS] slab of k 2^b, later of dv_new
-  float *sBeta = sB + C * LS;                   // [C]
-  const Tin *gk = reinterpret_cast<const Tin *>(p.k), *gv = reinterpret_cast<const Tin *>(p.v);
-  const float *gb = p.b + t0 * ld + h * D;
+// Persistent workgroups of eight waves walk (chunk, head) items. An item's
+// operands (T, dT_u, dw, X_w = k 2^b, dv_new, v) go to LDS once, from registers
+// loaded while the item before computed; the next item's loads are issued once
+// X_w has been consumed.
+template <int C, int D>
+struct WySmem {
+  static constexpr int LA = C + 4, LX = D + 4;
+  static constexpr size_t t = 0;               // fp32 [C][LA] T
+  static constexpr size_t dt = t + 4 * C * LA;  // dT
+  static constexpr size_t x = dt + 4 * C * LA;  // dT T^T
+  static constexpr size_t dw = x + 4 * C * LA;  // fp32 [C][LX] dw, later dX_u
+  static constexpr size_t xw = dw + 4 * C * LX;  // X_w, later v
+  static constexpr size_t dvn = xw + 4 * C * LX;  // dv_new
+  static constexpr size_t beta = dvn + 4 * C * LX;  // [C]
+  static constexpr size_t total = beta + 4 * C;
+  static_assert(total <= 160 * 1024, "LDS");
+};
 
-  tile_f32<float, C, C>(sT, LA, p.Tm + t0 * ldc + h * C, ldc, L, C, [&](int r, int c, float *v) {
+template <typename Tin, int C, int D, int NT>
+struct WyRegs {
+  static constexpr int EPV = 16 / (int)sizeof(Tin), NB = EPV / 4;
+  static constexpr int NA = C * C / 4, IA = (NA + NT - 1) / NT;               // T, dT_u
+  static constexpr int NF = C * D / 4, IF = (NF + NT - 1) / NT;               // dw, dv_new
+  static constexpr int VPR = D / EPV, NI = C * VPR, II = (NI + NT - 1) / NT;  // k, v
+  u32x4_t tm[IA], dtu[IA], dw[IF], dvn[IF], k[II], v[II];
+  f32x4_t b[II][NB];
+  float beta;
+
+  __device__ __forceinline__ void load(const ChunkParams &p, const BwdParams &bw, int64_t t0, int L, int h) {
+    const int t = threadIdx.x;
+    const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.H * p.Kr, ldv = (int64_t)p.H * p.Vr;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (c + e <= r && c + e < L) ? v[e] : 0.f;
-  });
-  tile_f32<float, C, C>(sDT, LA, bw.dT + t0 * ldc + h * C, ldc, L, C, [&](int, int c, float *v) {
+    for (int it = 0; it < IA; ++it) {
+      const int idx = it * NT + t, r = idx / (C / 4), c = (idx % (C / 4)) * 4;
+      const bool ok = (NA % NT == 0 || idx < NA) && r < L;
+      const int64_t o = (t0 + r) * ldc + h * C + c;
+      tm[it] = ok ? *reinterpret_cast<const u32x4_t *>(p.Tm + o) : z;
+      dtu[it] = ok ? *reinterpret_cast<const u32x4_t *>(bw.dT + o) : z;
+    }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (c + e < L) ? v[e] : 0.f;
-  });
-  for (int r = threadIdx.x; r < C; r += kBT) sBeta[r] = r < L ? beta_at(p, t0 + r, h) : 0.f;
-  // dT = dT_u + beta_s (dw (k 2^b)^T)_rs, the contraction over channels slab by slab
-  f32x4_t acc[NCW];
+    for (int it = 0; it < IF; ++it) {
+      const int idx = it * NT + t, r = idx / (D / 4), c = (idx % (D / 4)) * 4;
+      const bool ok = (NF % NT == 0 || idx < NF) && r < L;
+      const int64_t o = (t0 + r) * ld + h * D + c;
+      dw[it] = ok ? *reinterpret_cast<const u32x4_t *>(bw.dw + o) : z;
+      dvn[it] = ok ? *reinterpret_cast<const u32x4_t *>(bw.dvn + o) : z;
+    }
+    const Tin *gk = reinterpret_cast<const Tin *>(p.k) + t0 * ldk + h * p.Kr;
+    const Tin *gv = reinterpret_cast<const Tin *>(p.v) + t0 * ldv + h * p.Vr;
+    const float *gb = p.b + t0 * ld + h * D;
 #pragma unroll
-  for (int t = 0; t < NCW; ++t) acc[t] = zero4();
-#pragma unroll 1
-  for (int j0 = 0; j0 < D; j0 += SW) {
-    __syncthreads();  // the previous slab is consumed
-    tile_f32<float, C, SW>(sA, LS, bw.dw + t0 * ld + h * D + j0, ld, L, SW);
-    tile_f32<Tin, C, SW>(sB, LS, gk + t0 * ldk + h * Kr + j0, ldk, L, Kr - j0, [&](int r, int c, float *v) {
-      if (r >= L) return;
+    for (int it = 0; it < II; ++it) {
+      const int idx = it * NT + t, r = idx / VPR, c = (idx % VPR) * EPV;
+      const bool ok = (NI % NT == 0 || idx < NI) && r < L;
+      k[it] = ok && c < p.Kr ? *reinterpret_cast<const u32x4_t *>(gk + r * ldk + c) : z;
+      v[it] = ok && c < p.Vr ? *reinterpret_cast<const u32x4_t *>(gv + r * ldv + c) : z;
 #pragma unroll
-      for (int e = 0; e < 16 / (int)sizeof(Tin); e += 4) {
-        const f32x4_t br = ld4(gb + (int64_t)r * ld + j0 + c + e);
+      for (int j = 0; j < NB; ++j) b[it][j] = ok ? ld4(gb + r * ld + c + 4 * j) : zero4();
+    }
+    if (t < C) beta = t < L ? beta_at(p, t0 + t, h) : 0.f;
+  }
+
+  static __device__ __forceinline__ void unpack(u32x4_t raw, float (&f)[EPV]) {
+    if constexpr (sizeof(Tin) == 4) {
+      const f32x4_t x = __builtin_bit_cast(f32x4_t, raw);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[e + u] *= fast_exp2(br[u]);
+      for (int e = 0; e < EPV; ++e) f[e] = x[e];
+    } else {
+      const bf16x8_t x = __builtin_bit_cast(bf16x8_t, raw);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) f[e] = static_cast<float>(x[e]);
+    }
+  }
+
+  // everything but v; L masks the columns of T and dT_u
+  __device__ __forceinline__ void store(char *smem, int L) const {
+    using S = WySmem<C, D>;
+    const int t = threadIdx.x;
+    float *sT = reinterpret_cast<float *>(smem + S::t), *sDT = reinterpret_cast<float *>(smem + S::dt);
+    float *sDw = reinterpret_cast<float *>(smem + S::dw), *sXw = reinterpret_cast<float *>(smem + S::xw);
+    float *sDvn = reinterpret_cast<float *>(smem + S::dvn);
+#pragma unroll
+    for (int it = 0; it < IA; ++it) {
+      const int idx = it * NT + t, r = idx / (C / 4), c = (idx % (C / 4)) * 4;
+      if (NA % NT == 0 || idx < NA) {
+        f32x4_t a = __builtin_bit_cast(f32x4_t, tm[it]), d = __builtin_bit_cast(f32x4_t, dtu[it]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = (c + e <= r && c + e < L) ? a[e] : 0.f;
+          d[e] = (c + e < L) ? d[e] : 0.f;
+        }
+        *reinterpret_cast<f32x4_t *>(sT + r * S::LA + c) = a;
+        *reinterpret_cast<f32x4_t *>(sDT + r * S::LA + c) = d;
       }
-    });
+    }
+#pragma unroll
+    for (int it = 0; it < IF; ++it) {
+      const int idx = it * NT + t, r = idx / (D / 4), c = (idx % (D / 4)) * 4;
+      if (NF % NT == 0 || idx < NF) {
+        *reinterpret_cast<u32x4_t *>(sDw + r * S::LX + c) = dw[it];
+        *reinterpret_cast<u32x4_t *>(sDvn + r * S::LX + c) = dvn[it];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < II; ++it) {
+      const int idx = it * NT + t, r = idx / VPR, c = (idx % VPR) * EPV;
+      if (NI % NT == 0 || idx < NI) {
+        float f[EPV];
+        unpack(k[it], f);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          f32x4_t x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = f[4 * j + e] * fast_exp2(b[it][j][e]);
+          *reinterpret_cast<f32x4_t *>(sXw + r * S::LX + c + 4 * j) = x;
+        }
+      }
+    }
+    if (t < C) reinterpret_cast<float *>(smem + S::beta)[t] = beta;
+  }
+
+  // v, over X_w once the latter is consumed
+  __device__ __forceinline__ void store_v(char *smem) const {
+    using S = WySmem<C, D>;
+    float *sV = reinterpret_cast<float *>(smem + S::xw);
+#pragma unroll
+    for (int it = 0; it < II; ++it) {
+      const int idx = it * NT + threadIdx.x, r = idx / VPR, c = (idx % VPR) * EPV;
+      if (NI % NT == 0 || idx < NI) {
+        float f[EPV];
+        unpack(v[it], f);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          *reinterpret_cast<f32x4_t *>(sV + r * S::LX + c + 4 * j) = f32x4_t{f[4 * j], f[4 * j + 1], f[4 * j + 2], f[4 * j + 3]};
+      }
+    }
+  }
+};
+
+constexpr int kWyThreads = 512;
+
+template <typename Tin, int C, int D>
+__global__ __launch_bounds__(kWyThreads) void bwd_wy_kernel(ChunkParams p, BwdParams bw) {
+  constexpr int NT = kWyThreads, NW = NT / 64, NC = C / 16, DT = D / 16;
+  using S = WySmem<C, D>;
+  constexpr int LA = S::LA, LX = S::LX;
+  constexpr int NCW = (NC * NC + NW - 1) / NW, NDW = (NC * DT + NW - 1) / NW;  // tiles per wave
+  constexpr int TPR = NT / C, CPT = D / TPR;  // threads per row and columns per thread of the dv pass
+  static_assert(TPR <= 64 && 64 % TPR == 0 && D % TPR == 0, "row groups inside a wave");
+  const int wid = threadIdx.x >> 6;
+  const int total = p.cu ? p.chunk_off[p.N] : p.B * ((p.T + C - 1) / C);
+  const int64_t items = (int64_t)total * p.H;
+  const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldv = (int64_t)p.H * p.Vr;
+  extern __shared__ __align__(16) char smem[];
+  float *sT = reinterpret_cast<float *>(smem + S::t), *sDT = reinterpret_cast<float *>(smem + S::dt);
+  float *sX = reinterpret_cast<float *>(smem + S::x), *sDw = reinterpret_cast<float *>(smem + S::dw);
+  const float *sXw = reinterpret_cast<const float *>(smem + S::xw), *sDvn = reinterpret_cast<const float *>(smem + S::dvn);
+  const float *sV = sXw, *sBeta = reinterpret_cast<const float *>(smem + S::beta);
+
+  WyRegs<Tin, C, D, NT> R;
+  auto locate = [&](int64_t it, ChunkLoc &lc, int &h) {
+    h = (int)(it % p.H);
+    locate_chunk(p, (int)(it / p.H), lc);
+  };
+  int64_t it = blockIdx.x;
+  if (it < items) {
+    ChunkLoc lc;
+    int h;
+    locate(it, lc, h);
+    R.load(p, bw, lc.t0, lc.L, h);
+  }
+  for (; it < items; it += gridDim.x) {
+    ChunkLoc lc;
+    int h;
+    locate(it, lc, h);
+    const int L = lc.L;
+    const int64_t t0 = lc.t0;
+    R.store(smem, L);
     __syncthreads();
+    // dT = dT_u + beta_s (dw X_w^T)_rs
+    f32x4_t acc[NCW];
 #pragma unroll
     for (int t = 0; t < NCW; ++t) {
       const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
-      acc[t] = mm16<SW>(acc[t], sA, LS, 1, sB, 1, LS, 16 * rt, 16 * st);
+      acc[t] = (NC * NC % NW == 0 || tile < NC * NC) ? mm16<D>(zero4(), sDw, LX, 1, sXw, 1, LX, 16 * rt, 16 * st)
+                                                     : zero4();
     }
-  }
 #pragma unroll
-  for (int t = 0; t < NCW; ++t) {
-    const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
+    for (int t = 0; t < NCW; ++t) {
+      const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
+      if (NC * NC % NW == 0 || tile < NC * NC) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + tile_row(e), s = 16 * st + tile_col();
-      sDT[r * LA + s] += sBeta[s] * acc[t][e];
-    }
-  }
-  __syncthreads();
-  // X = dT T^T
-#pragma unroll
-  for (int t = 0; t < NCW; ++t) {
-    const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
-    const f32x4_t a = mm16<C>(zero4(), sDT, LA, 1, sT, 1, LA, 16 * rt, 16 * st);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sX[(16 * rt + tile_row(e)) * LA + 16 * st + tile_col()] = a[e];
-  }
-  __syncthreads();
-  // dA_kk = -strict_lower(T^T X)
-#pragma unroll
-  for (int t = 0; t < NCW; ++t) {
-    const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
-    const f32x4_t a = mm16<C>(zero4(), sT, 1, LA, sX, LA, 1, 16 * rt, 16 * st);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + tile_row(e), s = 16 * st + tile_col();
-      if (r < L) bw.dAkk[(t0 + r) * ldc + h * C + s] = (s < r) ? -a[e] : 0.f;
-    }
-  }
-  // dX_w = T^T dw and dX_u = T^T dv_new slab by slab; dv = beta dX_u; the beta
-  // gradient through u, sum over j of dX_u v, accumulates across the slabs
-  const int rr = threadIdx.x / TPR, qq = threadIdx.x % TPR;
-  float dbp = 0.f;
-#pragma unroll 1
-  for (int j0 = 0; j0 < D; j0 += SW) {
-    __syncthreads();  // the previous slab (or the last dT slab) is consumed
-    tile_f32<float, C, SW>(sA, LS, bw.dw + t0 * ld + h * D + j0, ld, L, SW);
-    tile_f32<float, C, SW>(sB, LS, bw.dvn + t0 * ld + h * D + j0, ld, L, SW);
-    __syncthreads();
-    f32x4_t xu[NSW];
-#pragma unroll
-    for (int t = 0; t < NSW; ++t) {
-      const int tile = wid * NSW + t, rt = tile / ST, ct = tile % ST;
-      const f32x4_t a = mm16<C>(zero4(), sT, 1, LA, sA, LS, 1, 16 * rt, 16 * ct);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + tile_row(e), i = j0 + 16 * ct + tile_col();
-        if (r < L) bw.dXw[(t0 + r) * ld + h * D + i] = a[e];
-      }
-      xu[t] = mm16<C>(zero4(), sT, 1, LA, sB, LS, 1, 16 * rt, 16 * ct);
-    }
-    __syncthreads();  // every wave is done reading this slab of dw
-#pragma unroll
-    for (int t = 0; t < NSW; ++t) {
-      const int tile = wid * NSW + t, rt = tile / ST, ct = tile % ST;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sA[(16 * rt + tile_row(e)) * LS + 16 * ct + tile_col()] = xu[t][e];
-    }
-    __syncthreads();
-    if (rr < L) {
-      Tin *gdv = reinterpret_cast<Tin *>(bw.dv) + (t0 + rr) * ldv + h * Vr;
-      for (int j = qq; j < SW && j0 + j < Vr; j += TPR) {
-        const float x = sA[rr * LS + j];
-        dbp += x * to_f32(gv[(t0 + rr) * ldv + h * Vr + j0 + j]);
-        gdv[j0 + j] = from_f32<Tin>(sBeta[rr] * x);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + tile_row(e), sc = 16 * st + tile_col();
+          sDT[r * LA + sc] += sBeta[sc] * acc[t][e];
+        }
       }
     }
-  }
+    __syncthreads();
+    // X_w is consumed: v takes its place, and the next item's loads go out
+    R.store_v(smem);
+    if (it + gridDim.x < items) {
+      ChunkLoc ln;
+      int hn;
+      locate(it + gridDim.x, ln, hn);
+      R.load(p, bw, ln.t0, ln.L, hn);
+    }
+    // X = dT T^T
 #pragma unroll
-  for (int m = 1; m < TPR; m <<= 1) dbp += __shfl_xor(dbp, m);
-  if (qq == 0 && rr < L) bw.dbp[(t0 + rr) * p.H + h] = dbp;
+    for (int t = 0; t < NCW; ++t) {
+      const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
+      if (NC * NC % NW == 0 || tile < NC * NC) {
+        const f32x4_t a = mm16<C>(zero4(), sDT, LA, 1, sT, 1, LA, 16 * rt, 16 * st);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sX[(16 * rt + tile_row(e)) * LA + 16 * st + tile_col()] = a[e];
+      }
+    }
+    __syncthreads();
+    // dA_kk = -strict_lower(T^T X); dX_w = T^T dw; dX_u = T^T dv_new (rows past L fall outside the ranges)
+    const rsrc_t rak = store_rsrc(bw.dAkk + t0 * ldc + h * C, (uint32_t)((L - 1) * ldc + C) * 4u);
+    const rsrc_t rxw = store_rsrc(bw.dXw + t0 * ld + h * D, (uint32_t)((L - 1) * ld + D) * 4u);
+#pragma unroll
+    for (int t = 0; t < NCW; ++t) {
+      const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
+      if (NC * NC % NW == 0 || tile < NC * NC) {
+        const f32x4_t a = mm16<C>(zero4(), sT, 1, LA, sX, LA, 1, 16 * rt, 16 * st);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + tile_row(e), sc = 16 * st + tile_col();
+          bstore_f32(rak, (uint32_t)(r * ldc + sc) * 4u, (sc < r) ? -a[e] : 0.f);
+        }
+      }
+    }
+    f32x4_t xu[NDW];
+#pragma unroll
+    for (int t = 0; t < NDW; ++t) {
+      const int tile = wid * NDW + t, rt = tile / DT, ct = tile % DT;
+      if (NC * DT % NW == 0 || tile < NC * DT) {
+        const f32x4_t a = mm16<C>(zero4(), sT, 1, LA, sDw, LX, 1, 16 * rt, 16 * ct);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          bstore_f32(rxw, (uint32_t)((16 * rt + tile_row(e)) * ld + 16 * ct + tile_col()) * 4u, a[e]);
+        xu[t] = mm16<C>(zero4(), sT, 1, LA, sDvn, LX, 1, 16 * rt, 16 * ct);
+      }
+    }
+    __syncthreads();  // every wave is done reading dw
+#pragma unroll
+    for (int t = 0; t < NDW; ++t) {
+      const int tile = wid * NDW + t, rt = tile / DT, ct = tile % DT;
+      if (NC * DT % NW == 0 || tile < NC * DT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sDw[(16 * rt + tile_row(e)) * LX + 16 * ct + tile_col()] = xu[t][e];
+      }
+    }
+    __syncthreads();
+    // dv = beta dX_u; the beta gradient through u, sum over j of dX_u v
+    {
+      const int rr = threadIdx.x / TPR, q = threadIdx.x % TPR;
+      float dbp = 0.f;
+      Tin *gdv = reinterpret_cast<Tin *>(bw.dv) + (t0 + rr) * ldv + h * p.Vr;
+      const float be = sBeta[rr];
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) {
+        const int j = q * CPT + m;
+        const float x = sDw[rr * LX + j];
+        dbp += x * sV[rr * LX + j];
+        if (rr < L && j < p.Vr) gdv[j] = from_f32<Tin>(be * x);
+      }
+#pragma unroll
+      for (int m = 1; m < TPR; m <<= 1) dbp += __shfl_xor(dbp, m);
+      if (q == 0 && rr < L) bw.dbp[(t0 + rr) * p.H + h] = dbp;
+    }
+    __syncthreads();  // the buffers are rewritten by the next item
+  }
 }
 
 // ---- pairwise decays: dq, dk, the cumsum gradient, dg and the gate activation ----
@@ -1057,8 +1204,10 @@ hipError_t launch_bwd_t(const ChunkParams &p, const BwdParams &b, hipStream_t st
       return e;
   }
   {
-    const size_t smem = sizeof(float) * ((size_t)3 * C * LA + 2 * C * (32 + 4) + C);
-    if ((e = launch_k(bwd_wy_kernel<Tin, C, D>, grid, smem, st, p, b)) != hipSuccess) return e;
+    const int64_t items = (int64_t)p.max_chunks * p.H;
+    const int wgs = (int)std::min<int64_t>(items, device_cus());
+    if ((e = launch_k(bwd_wy_kernel<Tin, C, D>, dim3(wgs), WySmem<C, D>::total, st, p, b, kWyThreads)) != hipSuccess)
+      return e;
   }
   {
     constexpr int LS = 64 + 4, NW = kBT / 64;
