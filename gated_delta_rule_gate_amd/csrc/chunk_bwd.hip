@@ -343,15 +343,44 @@ __global__ __launch_bounds__(4 * D) void bwd_scan_kernel(ChunkParams p, BwdParam
 
 // ---- contractions over the value columns ----
 // Persistent workgroups of eight waves walk (chunk, head) items, each in slabs
-// of SJ value columns; the next slab's tiles (of the same item or the next
-// one) are loaded into registers while the current slab's products run. Wave
+// of SJ value columns; the next two slabs' tiles (of the same item or the next
+// ones) are in flight in registers while the current slab's products run. Wave
 // w accumulates its share of the output tiles over the item's slabs.
+//
+// The products contract over the slab's value columns on the bf16 matrix cores
+// with fp32 accuracy: each fp32 operand x is held as hi = bf16(x) and
+// lo = bf16(x - hi), and A B ~ A_hi B_hi + A_hi B_lo + A_lo B_hi (the dropped
+// A_lo B_lo and the rounding of lo are about 2^-16 of each term); operands that
+// arrive in bf16 (do, for bf16 inputs) are exact and take no lo part.
+
+// x = hi + lo + (about 2^-16 |x|), both rounded to nearest-even bf16; two dwords each
+__device__ __forceinline__ void split_bf16x4(const f32x4_t &x, u32x2_t &hi, u32x2_t &lo) {
+  hi = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  const float h0 = __uint_as_float(hi[0] << 16), h1 = __uint_as_float(hi[0] & 0xFFFF0000u);
+  const float h2 = __uint_as_float(hi[1] << 16), h3 = __uint_as_float(hi[1] & 0xFFFF0000u);
+  lo = u32x2_t{pack_bf16x2(x[0] - h0, x[1] - h1), pack_bf16x2(x[2] - h2, x[3] - h3)};
+}
+
+template <int C, int D>
+struct ContractSmem {
+  static constexpr int SJ = 32, LB = SJ + 8;  // bf16 row stride of every tile (80 bytes)
+  // hi and lo tiles: do, beta v, v_new, dv_new [C][LB]; h, dh' [D][LB]
+  static constexpr size_t tc = 2 * C * LB, td = 2 * D * LB;
+  static constexpr size_t doH = 0, doL = doH + tc, bvH = doL + tc, bvL = bvH + tc, vnH = bvL + tc, vnL = vnH + tc;
+  static constexpr size_t dvH = vnL + tc, dvL = dvH + tc, hH = dvL + tc, hL = hH + td, dhH = hL + td, dhL = dhH + td;
+  static constexpr size_t beta = dhL + td;  // fp32 [C]
+  static constexpr size_t total = beta + 4 * C;
+  static_assert(total <= 160 * 1024, "LDS");
+};
+
 template <typename Tin, int C, int D, int NT>
 struct ContractRegs {
-  static constexpr int SJ = 32, EPV = 16 / (int)sizeof(Tin);
+  using S = ContractSmem<C, D>;
+  static constexpr int SJ = S::SJ, EPV = 16 / (int)sizeof(Tin);
   static constexpr int VI = C * SJ / EPV, II = (VI + NT - 1) / NT;  // do, v vectors of a slab
   static constexpr int VF = C * SJ / 4, IF = (VF + NT - 1) / NT;    // v_new, dv_new
   static constexpr int VH = D * SJ / 4, IH = (VH + NT - 1) / NT;    // h, dh'
+  static_assert(NT % (SJ / 4) == 0, "whole rows of h per group of threads");
   u32x4_t dO[II], v[II], vn[IF], dvn[IF], hh[IH], dh[IH];
   float beta;
 
@@ -391,20 +420,19 @@ struct ContractRegs {
     if (t < C) beta = t < L ? beta_at(p, t0 + t, h) : 0.f;
   }
 
-  static __device__ __forceinline__ void put(float *s, int lds, int r, int c, u32x4_t raw) {
-    if constexpr (sizeof(Tin) == 4) {
-      *reinterpret_cast<u32x4_t *>(s + r * lds + c) = raw;
-    } else {
-      const bf16x8_t f = __builtin_bit_cast(bf16x8_t, raw);
-      *reinterpret_cast<f32x4_t *>(s + r * lds + c) = f32x4_t{(float)f[0], (float)f[1], (float)f[2], (float)f[3]};
-      *reinterpret_cast<f32x4_t *>(s + r * lds + c + 4) = f32x4_t{(float)f[4], (float)f[5], (float)f[6], (float)f[7]};
-    }
+  static __device__ __forceinline__ void put(char *smem, size_t hiOff, size_t loOff, int r, int c, const f32x4_t &x) {
+    u32x2_t hi, lo;
+    split_bf16x4(x, hi, lo);
+    *reinterpret_cast<u32x2_t *>(smem + hiOff + 2 * (r * S::LB + c)) = hi;
+    *reinterpret_cast<u32x2_t *>(smem + loOff + 2 * (r * S::LB + c)) = lo;
   }
 
-  // the slab's tiles to LDS; beta of a new item first (v's rows are scaled by it)
-  __device__ __forceinline__ void store(float *sDo, float *sVn, float *sDvn, float *sBv, float *sH, float *sDhn,
-                                        float *sBeta, int lds, bool item_start) const {
+  // the slab's tiles to LDS as hi / lo pairs (beta of a new item first: v's rows
+  // are scaled by it); adds this slab's h dh' row sums to dlam (threads that
+  // lead a row group of h)
+  __device__ __forceinline__ void store(char *smem, bool item_start, float (&dlam)[IH]) const {
     const int t = threadIdx.x;
+    float *sBeta = reinterpret_cast<float *>(smem + S::beta);
     if (item_start) {
       if (t < C) sBeta[t] = beta;
       __syncthreads();
@@ -413,42 +441,65 @@ struct ContractRegs {
     for (int it = 0; it < II; ++it) {
       const int idx = it * NT + t, r = idx / (SJ / EPV), c = (idx % (SJ / EPV)) * EPV;
       if (VI % NT == 0 || idx < VI) {
-        put(sDo, lds, r, c, dO[it]);
-        float f[EPV];
-        if constexpr (sizeof(Tin) == 4) {
-          const f32x4_t x = __builtin_bit_cast(f32x4_t, v[it]);
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) f[e] = x[e];
-        } else {
-          const bf16x8_t x = __builtin_bit_cast(bf16x8_t, v[it]);
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) f[e] = (float)x[e];
-        }
         const float be = sBeta[r];
-#pragma unroll
-        for (int e = 0; e < EPV; e += 4)
-          *reinterpret_cast<f32x4_t *>(sBv + r * lds + c + e) =
-              f32x4_t{f[e] * be, f[e + 1] * be, f[e + 2] * be, f[e + 3] * be};
+        if constexpr (sizeof(Tin) == 4) {
+          const f32x4_t x = __builtin_bit_cast(f32x4_t, dO[it]), y = __builtin_bit_cast(f32x4_t, v[it]);
+          put(smem, S::doH, S::doL, r, c, x);
+          put(smem, S::bvH, S::bvL, r, c, y * be);
+        } else {
+          // bf16 do is exact: its lo tile stays unused
+          *reinterpret_cast<u32x4_t *>(smem + S::doH + 2 * (r * S::LB + c)) = dO[it];
+          const bf16x8_t y = __builtin_bit_cast(bf16x8_t, v[it]);
+          put(smem, S::bvH, S::bvL, r, c, f32x4_t{(float)y[0], (float)y[1], (float)y[2], (float)y[3]} * be);
+          put(smem, S::bvH, S::bvL, r, c + 4, f32x4_t{(float)y[4], (float)y[5], (float)y[6], (float)y[7]} * be);
+        }
       }
     }
 #pragma unroll
     for (int it = 0; it < IF; ++it) {
       const int idx = it * NT + t, r = idx / (SJ / 4), c = (idx % (SJ / 4)) * 4;
       if (VF % NT == 0 || idx < VF) {
-        *reinterpret_cast<u32x4_t *>(sVn + r * lds + c) = vn[it];
-        *reinterpret_cast<u32x4_t *>(sDvn + r * lds + c) = dvn[it];
+        put(smem, S::vnH, S::vnL, r, c, __builtin_bit_cast(f32x4_t, vn[it]));
+        put(smem, S::dvH, S::dvL, r, c, __builtin_bit_cast(f32x4_t, dvn[it]));
       }
     }
 #pragma unroll
     for (int it = 0; it < IH; ++it) {
       const int idx = it * NT + t, i = idx / (SJ / 4), c = (idx % (SJ / 4)) * 4;
+      const f32x4_t x = __builtin_bit_cast(f32x4_t, hh[it]), y = __builtin_bit_cast(f32x4_t, dh[it]);
+      float part = 0.f;
       if (VH % NT == 0 || idx < VH) {
-        *reinterpret_cast<u32x4_t *>(sH + i * lds + c) = hh[it];
-        *reinterpret_cast<u32x4_t *>(sDhn + i * lds + c) = dh[it];
+        put(smem, S::hH, S::hL, i, c, x);
+        put(smem, S::dhH, S::dhL, i, c, y);
+        part = x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
       }
+#pragma unroll
+      for (int m = 1; m < SJ / 4; m <<= 1) part += __shfl_xor(part, m);
+      dlam[it] += part;
     }
   }
 };
+
+// One 16x16 output tile over the slab: acc += A B^T with A rows a0.. of (aH, aL)
+// and B rows b0.. of (bH, bL), both [rows][LB] bf16 with the slab's columns
+// contiguous; A_lo is skipped when A is exact.
+template <int LB, bool A_EXACT>
+__device__ __forceinline__ f32x4_t mma_split(f32x4_t acc, const char *smem, size_t aH, size_t aL, int a0, size_t bH,
+                                             size_t bL, int b0) {
+  using M = Mma<bf16_t>;
+  const int lane = tid_opaque() & 63, r = lane & 15, g = lane >> 4;
+  const int ao = 2 * ((a0 + r) * LB + 8 * g), bo = 2 * ((b0 + r) * LB + 8 * g);
+  const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(smem + aH + ao);
+  const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(smem + bH + bo);
+  const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(smem + bL + bo);
+  acc = M::mma(ah, bh, acc);
+  acc = M::mma(ah, bl, acc);
+  if constexpr (!A_EXACT) {
+    const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(smem + aL + ao);
+    acc = M::mma(al, bh, acc);
+  }
+  return acc;
+}
 
 constexpr int kContractThreads = 512;
 
@@ -456,8 +507,11 @@ template <typename Tin, int C, int D>
 __global__ __launch_bounds__(kContractThreads) void bwd_contract_kernel(ChunkParams p, BwdParams bw) {
   constexpr int NT = kContractThreads, NW = NT / 64;
   using R = ContractRegs<Tin, C, D, NT>;
-  constexpr int SJ = R::SJ, LS = SJ + 4, NC = C / 16, DT = D / 16;
+  using S = ContractSmem<C, D>;
+  constexpr int SJ = S::SJ, LB = S::LB, NC = C / 16, DT = D / 16;
   constexpr int NTW = (NC * DT + NW - 1) / NW, NCW = (NC * NC + NW - 1) / NW;  // tiles per wave
+  constexpr bool DO_EXACT = sizeof(Tin) == 2;
+  static_assert(SJ == Mma<bf16_t>::KS, "one contraction step per slab");
   const int wid = threadIdx.x >> 6;
   const int total = p.cu ? p.chunk_off[p.N] : p.B * ((p.T + C - 1) / C);
   const int64_t items = (int64_t)total * p.H;
@@ -465,13 +519,6 @@ __global__ __launch_bounds__(kContractThreads) void bwd_contract_kernel(ChunkPar
   const int64_t steps = items > blockIdx.x ? ((items - 1 - blockIdx.x) / gridDim.x + 1) * nsl : 0;
   const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C;
   extern __shared__ __align__(16) char smem[];
-  float *sDo = reinterpret_cast<float *>(smem);  // [C][LS] slabs of SJ value columns
-  float *sVn = sDo + C * LS;
-  float *sDvn = sVn + C * LS;
-  float *sBv = sDvn + C * LS;
-  float *sH = sBv + C * LS;  // [D][LS]
-  float *sDhn = sH + D * LS;
-  float *sBeta = sDhn + D * LS;  // [C]
 
   // step s -> item (chunk, head) and slab
   auto at = [&](int64_t st, ChunkLoc &lc, int &h, int &j0) {
@@ -480,53 +527,56 @@ __global__ __launch_bounds__(kContractThreads) void bwd_contract_kernel(ChunkPar
     locate_chunk(p, (int)(it / p.H), lc);
     j0 = (int)(st % nsl) * SJ;
   };
-  R regs;
+  // two slabs' loads in flight: a slab's registers are refilled with the slab two steps on
+  R regs0, regs1;
   if (steps > 0) {
     ChunkLoc lc;
     int h, j0;
     at(0, lc, h, j0);
-    regs.load(p, bw, lc.t0, lc.L, lc.gci, h, j0);
+    regs0.load(p, bw, lc.t0, lc.L, lc.gci, h, j0);
   }
-  float dlam = 0.f;  // this thread's channel (threads < D): sum over j of h dh'
+  if (steps > 1) {
+    ChunkLoc lc;
+    int h, j0;
+    at(1, lc, h, j0);
+    regs1.load(p, bw, lc.t0, lc.L, lc.gci, h, j0);
+  }
+  float dlam[R::IH];  // row sums of h dh' for the rows this thread leads
+#pragma unroll
+  for (int q = 0; q < R::IH; ++q) dlam[q] = 0.f;
   f32x4_t aq[NTW], ak[NTW], aw[NTW], aa[NCW], at2[NCW];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) aq[t] = ak[t] = aw[t] = zero4();
 #pragma unroll
   for (int t = 0; t < NCW; ++t) aa[t] = at2[t] = zero4();
 
-  for (int64_t st = 0; st < steps; ++st) {
+  auto step = [&](int64_t st, R &regs) {
     ChunkLoc lc;
     int h, j0;
     at(st, lc, h, j0);
-    regs.store(sDo, sVn, sDvn, sBv, sH, sDhn, sBeta, LS, j0 == 0);
+    regs.store(smem, j0 == 0, dlam);
     __syncthreads();
-    if (st + 1 < steps) {
+    if (st + 2 < steps) {
       ChunkLoc ln;
       int hn, jn;
-      at(st + 1, ln, hn, jn);
+      at(st + 2, ln, hn, jn);
       regs.load(p, bw, ln.t0, ln.L, ln.gci, hn, jn);
-    }
-    if (threadIdx.x < D) {
-      float acc = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < SJ; ++j) acc += sH[threadIdx.x * LS + j] * sDhn[threadIdx.x * LS + j];
-      dlam += acc;
     }
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       const int tile = wid * NTW + t, rt = tile / DT, ct = tile % DT;
       if (NC * DT % NW == 0 || tile < NC * DT) {
-        aq[t] = mm16<SJ>(aq[t], sDo, LS, 1, sH, 1, LS, 16 * rt, 16 * ct);    // do h^T
-        ak[t] = mm16<SJ>(ak[t], sVn, LS, 1, sDhn, 1, LS, 16 * rt, 16 * ct);  // v_new dh'^T
-        aw[t] = mm16<SJ>(aw[t], sDvn, LS, 1, sH, 1, LS, 16 * rt, 16 * ct);   // dv_new h^T
+        aq[t] = mma_split<LB, DO_EXACT>(aq[t], smem, S::doH, S::doL, 16 * rt, S::hH, S::hL, 16 * ct);    // do h^T
+        ak[t] = mma_split<LB, false>(ak[t], smem, S::vnH, S::vnL, 16 * rt, S::dhH, S::dhL, 16 * ct);     // v_new dh'^T
+        aw[t] = mma_split<LB, false>(aw[t], smem, S::dvH, S::dvL, 16 * rt, S::hH, S::hL, 16 * ct);       // dv_new h^T
       }
     }
 #pragma unroll
     for (int t = 0; t < NCW; ++t) {
       const int tile = wid * NCW + t, rt = tile / NC, sc = tile % NC;
       if (NC * NC % NW == 0 || tile < NC * NC) {
-        aa[t] = mm16<SJ>(aa[t], sDo, LS, 1, sVn, 1, LS, 16 * rt, 16 * sc);    // do v_new^T
-        at2[t] = mm16<SJ>(at2[t], sDvn, LS, 1, sBv, 1, LS, 16 * rt, 16 * sc);  // dv_new (beta v)^T
+        aa[t] = mma_split<LB, DO_EXACT>(aa[t], smem, S::doH, S::doL, 16 * rt, S::vnH, S::vnL, 16 * sc);  // do v_new^T
+        at2[t] = mma_split<LB, false>(at2[t], smem, S::dvH, S::dvL, 16 * rt, S::bvH, S::bvL, 16 * sc);   // dv_new (beta v)^T
       }
     }
     if (j0 + SJ >= p.Vr) {  // the item's last slab: its outputs (rows past L fall outside the ranges)
@@ -563,10 +613,20 @@ __global__ __launch_bounds__(kContractThreads) void bwd_contract_kernel(ChunkPar
         }
         aa[t] = at2[t] = zero4();
       }
-      if (threadIdx.x < D) bw.dlam[((int64_t)lc.gci * p.H + h) * D + threadIdx.x] = dlam;
-      dlam = 0.f;
+      if (threadIdx.x % (SJ / 4) == 0) {
+#pragma unroll
+        for (int q = 0; q < R::IH; ++q) {
+          const int i = (q * NT + threadIdx.x) / (SJ / 4);
+          if (i < D) bw.dlam[((int64_t)lc.gci * p.H + h) * D + i] = dlam[q];
+          dlam[q] = 0.f;
+        }
+      }
     }
     __syncthreads();  // the slab is consumed before the next one is stored
+  };
+  for (int64_t st = 0; st < steps; st += 2) {
+    step(st, regs0);
+    if (st + 1 < steps) step(st + 1, regs1);
   }
 }
 
@@ -1196,11 +1256,10 @@ hipError_t launch_bwd_t(const ChunkParams &p, const BwdParams &b, hipStream_t st
     return e;
   const dim3 grid(p.max_chunks, p.H);
   {
-    constexpr int LS = 32 + 4;
-    const size_t smem = sizeof(float) * ((size_t)4 * C * LS + 2 * D * LS + C);
     const int64_t items = (int64_t)p.max_chunks * p.H;
     const int wgs = (int)std::min<int64_t>(items, device_cus());
-    if ((e = launch_k(bwd_contract_kernel<Tin, C, D>, dim3(wgs), smem, st, p, b, kContractThreads)) != hipSuccess)
+    if ((e = launch_k(bwd_contract_kernel<Tin, C, D>, dim3(wgs), ContractSmem<C, D>::total, st, p, b,
+                      kContractThreads)) != hipSuccess)
       return e;
   }
   {
