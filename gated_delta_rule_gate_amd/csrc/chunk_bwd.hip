@@ -341,6 +341,244 @@ __global__ __launch_bounds__(4 * D) void bwd_scan_kernel(ChunkParams p, BwdParam
   }
 }
 
+// x = hi + lo + (about 2^-16 |x|), both rounded to nearest-even bf16; two dwords each
+__device__ __forceinline__ void split_bf16x4(const f32x4_t &x, u32x2_t &hi, u32x2_t &lo) {
+  hi = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  const float h0 = __uint_as_float(hi[0] << 16), h1 = __uint_as_float(hi[0] & 0xFFFF0000u);
+  const float h2 = __uint_as_float(hi[1] << 16), h3 = __uint_as_float(hi[1] & 0xFFFF0000u);
+  lo = u32x2_t{pack_bf16x2(x[0] - h0, x[1] - h1), pack_bf16x2(x[2] - h2, x[3] - h3)};
+}
+
+// ---- the scan for bf16 inputs: the same steps on the bf16 matrix cores ----
+// Every product contracts either over the chunk's tokens or over channels, with
+// fp32 operands split into bf16 high and low parts (see the contractions
+// below). LDS holds, as hi / lo pairs, A_qk^T, q~^T and w^T (channel or output
+// row by token), k~ (token by channel, in the operand order of the products
+// with the register-resident dh), and do^T (exact in bf16). The register
+// operands, dh (channels) and dv_new (tokens), feed the matrix cores in their
+// accumulator layout under the contraction map of Mma<bf16_t>; the LDS operand
+// they meet is stored in that map's order.
+template <int C, int D>
+struct ScanSplitSmem {
+  static constexpr int LC = C + 8, LD = D + 8;  // bf16 row strides
+  static constexpr size_t atH = 0, atL = atH + 2 * C * LC;  // [C][LC] A_qk^T (row m, token k)
+  static constexpr size_t doT = atL + 2 * C * LC;           // [D][LC] do^T (value column, token)
+  static constexpr size_t kH = doT + 2 * D * LC, kL = kH + 2 * C * LD;  // [C][LD] k~, channels in operand order
+  static constexpr size_t qH = kL + 2 * C * LD, qL = qH + 2 * D * LC;   // [D][LC] q~^T
+  static constexpr size_t wH = qL + 2 * D * LC, wL = wH + 2 * D * LC;   // [D][LC] w^T, tokens in operand order
+  static constexpr size_t bl = wL + 2 * D * LC;                         // fp32 [D] b_L
+  static constexpr size_t total = bl + 4 * D;
+  static_assert(total <= 160 * 1024, "LDS");
+};
+
+// Position of contraction index x (channel or token) in the operand order of
+// Mma<bf16_t>: within each block of 32, lane group g's eight slots hold
+// 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3.
+__device__ __forceinline__ int op_pos(int x) {
+  const int w = x & 31;
+  return (x & ~31) + 8 * ((w >> 2) & 3) + ((w >> 4) << 2) + (w & 3);
+}
+
+// hi / lo bf16 operand fragments of slots (a[0..3], b[0..3])
+__device__ __forceinline__ void split_frag(const f32x4_t &a, const f32x4_t &b, bf16x8_t &hi, bf16x8_t &lo) {
+  u32x2_t ha, la, hb, lb;
+  split_bf16x4(a, ha, la);
+  split_bf16x4(b, hb, lb);
+  hi = __builtin_bit_cast(bf16x8_t, u32x4_t{ha[0], ha[1], hb[0], hb[1]});
+  lo = __builtin_bit_cast(bf16x8_t, u32x4_t{la[0], la[1], lb[0], lb[1]});
+}
+
+template <int C, int D>
+__device__ __forceinline__ void scan_split_store(const ScanRegs<bf16_t, C, D, 4 * D> &R, char *smem, float scale) {
+  using S = ScanSplitSmem<C, D>;
+  using Rg = ScanRegs<bf16_t, C, D, 4 * D>;
+  constexpr int NT = 4 * D;
+  const int t = threadIdx.x;
+  bf16_t *atH = reinterpret_cast<bf16_t *>(smem + S::atH), *atL = reinterpret_cast<bf16_t *>(smem + S::atL);
+  bf16_t *doT = reinterpret_cast<bf16_t *>(smem + S::doT);
+  bf16_t *qH = reinterpret_cast<bf16_t *>(smem + S::qH), *qL = reinterpret_cast<bf16_t *>(smem + S::qL);
+  bf16_t *wH = reinterpret_cast<bf16_t *>(smem + S::wH), *wL = reinterpret_cast<bf16_t *>(smem + S::wL);
+  auto hl = [](float x, bf16_t &h, bf16_t &l) {
+    h = static_cast<bf16_t>(x);
+    l = static_cast<bf16_t>(x - static_cast<float>(h));
+  };
+  // A_qk row k, columns m .. m + 3 -> A_qk^T[m][k] (causal: m <= k)
+#pragma unroll
+  for (int it = 0; it < Rg::IA; ++it) {
+    const int idx = it * NT + t, k = idx / (C / 4), m0 = (idx % (C / 4)) * 4;
+    if (Rg::NA % NT == 0 || idx < Rg::NA) {
+      const f32x4_t a = __builtin_bit_cast(f32x4_t, R.a[it]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bf16_t h, l;
+        hl(m0 + e <= k ? a[e] : 0.f, h, l);
+        atH[(m0 + e) * S::LC + k] = h;
+        atL[(m0 + e) * S::LC + k] = l;
+      }
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < Rg::II; ++it) {
+    const int idx = it * NT + t, k = idx / Rg::VPR, c = (idx % Rg::VPR) * 8;
+    if (Rg::NI % NT == 0 || idx < Rg::NI) {
+      const bf16x8_t o8 = __builtin_bit_cast(bf16x8_t, R.dO[it]);
+      const bf16x8_t k8 = __builtin_bit_cast(bf16x8_t, R.k[it]), q8 = __builtin_bit_cast(bf16x8_t, R.q[it]);
+      float kt[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        doT[(c + e) * S::LC + k] = o8[e];
+        const float bb = R.b[it][e >> 2][e & 3];
+        kt[e] = static_cast<float>(k8[e]) * fast_exp2(R.bl[e >> 2][e & 3] - bb);
+        bf16_t h, l;
+        hl(static_cast<float>(q8[e]) * (scale * fast_exp2(bb)), h, l);
+        qH[(c + e) * S::LC + k] = h;
+        qL[(c + e) * S::LC + k] = l;
+      }
+      // k~ row k: channels c .. c + 7 land in two runs of four operand slots
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x2_t hi, lo;
+        split_bf16x4(f32x4_t{kt[4 * hh], kt[4 * hh + 1], kt[4 * hh + 2], kt[4 * hh + 3]}, hi, lo);
+        const int o = 2 * (k * S::LD + op_pos(c + 4 * hh));
+        *reinterpret_cast<u32x2_t *>(smem + S::kH + o) = hi;
+        *reinterpret_cast<u32x2_t *>(smem + S::kL + o) = lo;
+      }
+    }
+  }
+  // w row k, channels i .. i + 3 -> w^T[i][op_pos(k)]
+#pragma unroll
+  for (int it = 0; it < Rg::IF; ++it) {
+    const int idx = it * NT + t, k = idx / (D / 4), i0 = (idx % (D / 4)) * 4;
+    if (Rg::NF % NT == 0 || idx < Rg::NF) {
+      const f32x4_t w4 = __builtin_bit_cast(f32x4_t, R.w[it]);
+      const int pk = op_pos(k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bf16_t h, l;
+        hl(w4[e], h, l);
+        wH[(i0 + e) * S::LC + pk] = h;
+        wL[(i0 + e) * S::LC + pk] = l;
+      }
+    }
+  }
+  if (t < Rg::VPR) {
+#pragma unroll
+    for (int j = 0; j < Rg::NB; ++j)
+      *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(smem + S::bl) + t * 8 + 4 * j) = R.bl[j];
+  }
+}
+
+template <int C, int D>
+__global__ __launch_bounds__(4 * D) void bwd_scan_split_kernel(ChunkParams p, BwdParams bw) {
+  using M = Mma<bf16_t>;
+  using S = ScanSplitSmem<C, D>;
+  constexpr int NT = 4 * D, NC = C / 16, DT = D / 16, LC = S::LC, LD = S::LD;
+  const int nh = blockIdx.x;
+  const int n = nh / p.H, h = nh % p.H;
+  const int wid = wave_id();
+  const int n16 = tid_opaque() & 15, grp = (tid_opaque() & 63) >> 4;
+  const int jc = 16 * wid + n16;  // this lane's value column
+  const int Kr = p.Kr, Vr = p.Vr;
+  const SlotRange sr = slot_range(p.cu, n, p.T);
+  const int nch = (sr.len + C - 1) / C;
+  const int cbase = p.cu ? p.chunk_off[n] : n * ((p.T + C - 1) / C);
+  const int64_t sbase = (int64_t)nh * Kr * Vr;
+  const int64_t ld = (int64_t)p.H * D;
+  extern __shared__ __align__(16) char smem[];
+  const float *sBL = reinterpret_cast<const float *>(smem + S::bl);
+  // a 16-byte operand fragment: row r of a bf16 tile, slots 8 g .. 8 g + 7 of contraction block s
+  auto frag = [&](size_t base, int ldr, int r, int s) {
+    return *reinterpret_cast<const bf16x8_t *>(smem + base + 2 * (r * ldr + 32 * s + 8 * grp));
+  };
+
+  f32x4_t dh[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * t + tile_row(e);
+      dh[t][e] = (bw.dht && i < Kr && jc < Vr) ? bw.dht[sbase + (int64_t)i * Vr + jc] : 0.f;
+    }
+  ScanRegs<bf16_t, C, D, NT> R;
+  if (nch > 0) {
+    const int c = nch - 1;
+    R.load(p, bw, sr.t0 + (int64_t)c * C, min(C, sr.len - c * C), h);
+    R.load_w(p, sr.t0 + (int64_t)c * C, min(C, sr.len - c * C), h);
+  }
+  for (int c = nch - 1; c >= 0; --c) {
+    const int64_t t0 = sr.t0 + (int64_t)c * C;
+    const int L = min(C, sr.len - c * C);
+    const int64_t gc = cbase + c;
+    scan_split_store<C, D>(R, smem, p.scale);
+    // gradient of the state after this chunk (channels past Kr fall outside the range)
+    if (jc < Vr) {
+      const rsrc_t rdh = store_rsrc(bw.dhn + (gc * p.H + h) * Kr * Vr, (uint32_t)(Kr * Vr) * 4u);
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bstore_f32(rdh, (uint32_t)((16 * t + tile_row(e)) * Vr + jc) * 4u, dh[t][e]);
+    }
+    __syncthreads();
+    if (c > 0) R.load(p, bw, t0 - C, C, h);  // every chunk but a slot's last has C rows
+    // dv_new = A_qk^T do + k~ dh (rows past L fall outside the range)
+    const rsrc_t rdv = store_rsrc(bw.dvn + t0 * ld + h * D, (uint32_t)((L - 1) * ld + D) * 4u);
+    f32x4_t dv[NC];
+#pragma unroll
+    for (int rt = 0; rt < NC; ++rt) {
+      f32x4_t acc = zero4();
+#pragma unroll
+      for (int s = 0; s < C / 32; ++s) {
+        const bf16x8_t o = frag(S::doT, LC, 16 * wid + n16, s);
+        acc = M::mma(frag(S::atH, LC, 16 * rt + n16, s), o, acc);
+        acc = M::mma(frag(S::atL, LC, 16 * rt + n16, s), o, acc);
+      }
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        bf16x8_t bh, bl;
+        split_frag(dh[2 * s], dh[2 * s + 1], bh, bl);
+        const bf16x8_t ah = frag(S::kH, LD, 16 * rt + n16, s), al = frag(S::kL, LD, 16 * rt + n16, s);
+        acc = M::mma(ah, bh, acc);
+        acc = M::mma(ah, bl, acc);
+        acc = M::mma(al, bh, acc);
+      }
+      dv[rt] = acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bstore_f32(rdv, (uint32_t)((16 * rt + tile_row(e)) * ld + jc) * 4u, acc[e]);
+    }
+    if (c > 0) R.load_w(p, t0 - C, C, h);
+    // dh <- 2^b_L dh + q~^T do - w^T dv_new
+    bf16x8_t vh[C / 32], vl[C / 32];
+#pragma unroll
+    for (int s = 0; s < C / 32; ++s) split_frag(dv[2 * s], dv[2 * s + 1], vh[s], vl[s]);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      f32x4_t acc = zero4(), wv = zero4();
+#pragma unroll
+      for (int s = 0; s < C / 32; ++s) {
+        const bf16x8_t o = frag(S::doT, LC, 16 * wid + n16, s);
+        acc = M::mma(frag(S::qH, LC, 16 * t + n16, s), o, acc);
+        acc = M::mma(frag(S::qL, LC, 16 * t + n16, s), o, acc);
+        const bf16x8_t ah = frag(S::wH, LC, 16 * t + n16, s), al = frag(S::wL, LC, 16 * t + n16, s);
+        wv = M::mma(ah, vh[s], wv);
+        wv = M::mma(ah, vl[s], wv);
+        wv = M::mma(al, vh[s], wv);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh[t][e] = fast_exp2(sBL[16 * t + tile_row(e)]) * dh[t][e] + acc[e] - wv[e];
+    }
+    __syncthreads();  // every buffer is rewritten by the next chunk
+  }
+  if (bw.dh0 && jc < Vr) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * t + tile_row(e);
+        if (i < Kr) bw.dh0[sbase + (int64_t)i * Vr + jc] = dh[t][e];
+      }
+  }
+}
+
 // ---- contractions over the value columns ----
 // Persistent workgroups of eight waves walk (chunk, head) items, each in slabs
 // of SJ value columns; the next two slabs' tiles (of the same item or the next
@@ -352,14 +590,6 @@ __global__ __launch_bounds__(4 * D) void bwd_scan_kernel(ChunkParams p, BwdParam
 // lo = bf16(x - hi), and A B ~ A_hi B_hi + A_hi B_lo + A_lo B_hi (the dropped
 // A_lo B_lo and the rounding of lo are about 2^-16 of each term); operands that
 // arrive in bf16 (do, for bf16 inputs) are exact and take no lo part.
-
-// x = hi + lo + (about 2^-16 |x|), both rounded to nearest-even bf16; two dwords each
-__device__ __forceinline__ void split_bf16x4(const f32x4_t &x, u32x2_t &hi, u32x2_t &lo) {
-  hi = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-  const float h0 = __uint_as_float(hi[0] << 16), h1 = __uint_as_float(hi[0] & 0xFFFF0000u);
-  const float h2 = __uint_as_float(hi[1] << 16), h3 = __uint_as_float(hi[1] & 0xFFFF0000u);
-  lo = u32x2_t{pack_bf16x2(x[0] - h0, x[1] - h1), pack_bf16x2(x[2] - h2, x[3] - h3)};
-}
 
 template <int C, int D>
 struct ContractSmem {
@@ -1251,9 +1481,15 @@ template <typename Tin, int C, int D>
 hipError_t launch_bwd_t(const ChunkParams &p, const BwdParams &b, hipStream_t st) {
   constexpr int LA = C + 4, LX = D + 4;
   hipError_t e;
-  if ((e = launch_k(bwd_scan_kernel<Tin, C, D>, dim3(p.N * p.H), ScanSmem<C, D>::total, st, p, b, 4 * D)) !=
-      hipSuccess)
-    return e;
+  if constexpr (sizeof(Tin) == 2) {
+    if ((e = launch_k(bwd_scan_split_kernel<C, D>, dim3(p.N * p.H), ScanSplitSmem<C, D>::total, st, p, b, 4 * D)) !=
+        hipSuccess)
+      return e;
+  } else {
+    if ((e = launch_k(bwd_scan_kernel<Tin, C, D>, dim3(p.N * p.H), ScanSmem<C, D>::total, st, p, b, 4 * D)) !=
+        hipSuccess)
+      return e;
+  }
   const dim3 grid(p.max_chunks, p.H);
   {
     const int64_t items = (int64_t)p.max_chunks * p.H;
