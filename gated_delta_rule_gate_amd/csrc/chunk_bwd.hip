@@ -25,6 +25,7 @@
 // chunk_kda_bwd_wy_dqkg_fused); the steps above are the reverse mode of the
 // forward steps as the chunked forward computes them.
 #include "chunk_loc.h"
+#include "chunk_fused_tiles.h"
 #include "chunk_tiles.h"
 #include "kda_launch.h"
 
@@ -350,43 +351,26 @@ __device__ __forceinline__ void split_bf16x4(const f32x4_t &x, u32x2_t &hi, u32x
 }
 
 // ---- the scan for bf16 inputs: the same steps on the bf16 matrix cores ----
-// Every product contracts either over the chunk's tokens or over channels, with
-// fp32 operands split into bf16 high and low parts (see the contractions
-// below). LDS holds, as hi / lo pairs, A_qk^T, q~^T and w^T (channel or output
-// row by token), k~ (token by channel, in the operand order of the products
-// with the register-resident dh), and do^T (exact in bf16). The register
-// operands, dh (channels) and dv_new (tokens), feed the matrix cores in their
-// accumulator layout under the contraction map of Mma<bf16_t>; the LDS operand
-// they meet is stored in that map's order.
+// Every product runs as 16x16x16 bf16 matrix products with fp32 operands split
+// into bf16 high and low parts (x = hi + lo + about 2^-16 |x|; A B is taken as
+// A_hi B_hi + A_hi B_lo + A_lo B_hi). LDS holds the chunk's tiles row-major as
+// the loads deliver them (A_qk, do, k~, q~, w by token), written with wide
+// stores; the products that contract over tokens read their operands with the
+// transposing LDS load (load_cfrag), whose four K elements per lane are the
+// rows 4g .. 4g + 3 of a 16-row block -- the layout in which dh (channels) and
+// dv_new (tokens) already sit in their accumulators.
 template <int C, int D>
 struct ScanSplitSmem {
-  static constexpr int LC = C + 8, LD = D + 8;  // bf16 row strides
-  static constexpr size_t atH = 0, atL = atH + 2 * C * LC;  // [C][LC] A_qk^T (row m, token k)
-  static constexpr size_t doT = atL + 2 * C * LC;           // [D][LC] do^T (value column, token)
-  static constexpr size_t kH = doT + 2 * D * LC, kL = kH + 2 * C * LD;  // [C][LD] k~, channels in operand order
-  static constexpr size_t qH = kL + 2 * C * LD, qL = qH + 2 * D * LC;   // [D][LC] q~^T
-  static constexpr size_t wH = qL + 2 * D * LC, wL = wH + 2 * D * LC;   // [D][LC] w^T, tokens in operand order
-  static constexpr size_t bl = wL + 2 * D * LC;                         // fp32 [D] b_L
+  static constexpr int LA = C + 8, LT = D + 8;  // bf16 row strides
+  static constexpr size_t atH = 0, atL = atH + 2 * C * LA;  // [C][LA] A_qk (token k, column m), causal
+  static constexpr size_t dO = atL + 2 * C * LA;            // [C][LT] do
+  static constexpr size_t kH = dO + 2 * C * LT, kL = kH + 2 * C * LT;  // k~ = k 2^(b_L - b)
+  static constexpr size_t qH = kL + 2 * C * LT, qL = qH + 2 * C * LT;  // q~ = scale q 2^b
+  static constexpr size_t wH = qL + 2 * C * LT, wL = wH + 2 * C * LT;  // w
+  static constexpr size_t bl = wL + 2 * C * LT;                        // fp32 [D] b_L
   static constexpr size_t total = bl + 4 * D;
   static_assert(total <= 160 * 1024, "LDS");
 };
-
-// Position of contraction index x (channel or token) in the operand order of
-// Mma<bf16_t>: within each block of 32, lane group g's eight slots hold
-// 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3.
-__device__ __forceinline__ int op_pos(int x) {
-  const int w = x & 31;
-  return (x & ~31) + 8 * ((w >> 2) & 3) + ((w >> 4) << 2) + (w & 3);
-}
-
-// hi / lo bf16 operand fragments of slots (a[0..3], b[0..3])
-__device__ __forceinline__ void split_frag(const f32x4_t &a, const f32x4_t &b, bf16x8_t &hi, bf16x8_t &lo) {
-  u32x2_t ha, la, hb, lb;
-  split_bf16x4(a, ha, la);
-  split_bf16x4(b, hb, lb);
-  hi = __builtin_bit_cast(bf16x8_t, u32x4_t{ha[0], ha[1], hb[0], hb[1]});
-  lo = __builtin_bit_cast(bf16x8_t, u32x4_t{la[0], la[1], lb[0], lb[1]});
-}
 
 template <int C, int D>
 __device__ __forceinline__ void scan_split_store(const ScanRegs<bf16_t, C, D, 4 * D> &R, char *smem, float scale) {
@@ -394,71 +378,55 @@ __device__ __forceinline__ void scan_split_store(const ScanRegs<bf16_t, C, D, 4 
   using Rg = ScanRegs<bf16_t, C, D, 4 * D>;
   constexpr int NT = 4 * D;
   const int t = threadIdx.x;
-  bf16_t *atH = reinterpret_cast<bf16_t *>(smem + S::atH), *atL = reinterpret_cast<bf16_t *>(smem + S::atL);
-  bf16_t *doT = reinterpret_cast<bf16_t *>(smem + S::doT);
-  bf16_t *qH = reinterpret_cast<bf16_t *>(smem + S::qH), *qL = reinterpret_cast<bf16_t *>(smem + S::qL);
-  bf16_t *wH = reinterpret_cast<bf16_t *>(smem + S::wH), *wL = reinterpret_cast<bf16_t *>(smem + S::wL);
-  auto hl = [](float x, bf16_t &h, bf16_t &l) {
-    h = static_cast<bf16_t>(x);
-    l = static_cast<bf16_t>(x - static_cast<float>(h));
-  };
-  // A_qk row k, columns m .. m + 3 -> A_qk^T[m][k] (causal: m <= k)
 #pragma unroll
   for (int it = 0; it < Rg::IA; ++it) {
     const int idx = it * NT + t, k = idx / (C / 4), m0 = (idx % (C / 4)) * 4;
     if (Rg::NA % NT == 0 || idx < Rg::NA) {
-      const f32x4_t a = __builtin_bit_cast(f32x4_t, R.a[it]);
+      f32x4_t a = __builtin_bit_cast(f32x4_t, R.a[it]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bf16_t h, l;
-        hl(m0 + e <= k ? a[e] : 0.f, h, l);
-        atH[(m0 + e) * S::LC + k] = h;
-        atL[(m0 + e) * S::LC + k] = l;
-      }
+      for (int e = 0; e < 4; ++e) a[e] = (m0 + e <= k) ? a[e] : 0.f;
+      u32x2_t hi, lo;
+      split_bf16x4(a, hi, lo);
+      const int o = 2 * (k * S::LA + m0);
+      *reinterpret_cast<u32x2_t *>(smem + S::atH + o) = hi;
+      *reinterpret_cast<u32x2_t *>(smem + S::atL + o) = lo;
     }
   }
 #pragma unroll
   for (int it = 0; it < Rg::II; ++it) {
-    const int idx = it * NT + t, k = idx / Rg::VPR, c = (idx % Rg::VPR) * 8;
+    const int idx = it * NT + t, r = idx / Rg::VPR, c = (idx % Rg::VPR) * 8;
     if (Rg::NI % NT == 0 || idx < Rg::NI) {
-      const bf16x8_t o8 = __builtin_bit_cast(bf16x8_t, R.dO[it]);
+      const int o = 2 * (r * S::LT + c);
+      *reinterpret_cast<u32x4_t *>(smem + S::dO + o) = R.dO[it];
       const bf16x8_t k8 = __builtin_bit_cast(bf16x8_t, R.k[it]), q8 = __builtin_bit_cast(bf16x8_t, R.q[it]);
-      float kt[8];
+      u32x2_t kh[2], kl[2], qh[2], ql[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        doT[(c + e) * S::LC + k] = o8[e];
-        const float bb = R.b[it][e >> 2][e & 3];
-        kt[e] = static_cast<float>(k8[e]) * fast_exp2(R.bl[e >> 2][e & 3] - bb);
-        bf16_t h, l;
-        hl(static_cast<float>(q8[e]) * (scale * fast_exp2(bb)), h, l);
-        qH[(c + e) * S::LC + k] = h;
-        qL[(c + e) * S::LC + k] = l;
-      }
-      // k~ row k: channels c .. c + 7 land in two runs of four operand slots
+      for (int j = 0; j < 2; ++j) {
+        f32x4_t kt, qt;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        u32x2_t hi, lo;
-        split_bf16x4(f32x4_t{kt[4 * hh], kt[4 * hh + 1], kt[4 * hh + 2], kt[4 * hh + 3]}, hi, lo);
-        const int o = 2 * (k * S::LD + op_pos(c + 4 * hh));
-        *reinterpret_cast<u32x2_t *>(smem + S::kH + o) = hi;
-        *reinterpret_cast<u32x2_t *>(smem + S::kL + o) = lo;
+        for (int e = 0; e < 4; ++e) {
+          const float bb = R.b[it][j][e];
+          kt[e] = static_cast<float>(k8[4 * j + e]) * fast_exp2(R.bl[j][e] - bb);
+          qt[e] = static_cast<float>(q8[4 * j + e]) * (scale * fast_exp2(bb));
+        }
+        split_bf16x4(kt, kh[j], kl[j]);
+        split_bf16x4(qt, qh[j], ql[j]);
       }
+      *reinterpret_cast<u32x4_t *>(smem + S::kH + o) = u32x4_t{kh[0][0], kh[0][1], kh[1][0], kh[1][1]};
+      *reinterpret_cast<u32x4_t *>(smem + S::kL + o) = u32x4_t{kl[0][0], kl[0][1], kl[1][0], kl[1][1]};
+      *reinterpret_cast<u32x4_t *>(smem + S::qH + o) = u32x4_t{qh[0][0], qh[0][1], qh[1][0], qh[1][1]};
+      *reinterpret_cast<u32x4_t *>(smem + S::qL + o) = u32x4_t{ql[0][0], ql[0][1], ql[1][0], ql[1][1]};
     }
   }
-  // w row k, channels i .. i + 3 -> w^T[i][op_pos(k)]
 #pragma unroll
   for (int it = 0; it < Rg::IF; ++it) {
-    const int idx = it * NT + t, k = idx / (D / 4), i0 = (idx % (D / 4)) * 4;
+    const int idx = it * NT + t, r = idx / (D / 4), c = (idx % (D / 4)) * 4;
     if (Rg::NF % NT == 0 || idx < Rg::NF) {
-      const f32x4_t w4 = __builtin_bit_cast(f32x4_t, R.w[it]);
-      const int pk = op_pos(k);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bf16_t h, l;
-        hl(w4[e], h, l);
-        wH[(i0 + e) * S::LC + pk] = h;
-        wL[(i0 + e) * S::LC + pk] = l;
-      }
+      u32x2_t hi, lo;
+      split_bf16x4(__builtin_bit_cast(f32x4_t, R.w[it]), hi, lo);
+      const int o = 2 * (r * S::LT + c);
+      *reinterpret_cast<u32x2_t *>(smem + S::wH + o) = hi;
+      *reinterpret_cast<u32x2_t *>(smem + S::wL + o) = lo;
     }
   }
   if (t < Rg::VPR) {
@@ -468,11 +436,18 @@ __device__ __forceinline__ void scan_split_store(const ScanRegs<bf16_t, C, D, 4 
   }
 }
 
+// hi / lo bf16 halves of four floats, as 16x16x16 operand fragments
+__device__ __forceinline__ void split4(const f32x4_t &x, bf16x4_t &hi, bf16x4_t &lo) {
+  u32x2_t h, l;
+  split_bf16x4(x, h, l);
+  hi = __builtin_bit_cast(bf16x4_t, h);
+  lo = __builtin_bit_cast(bf16x4_t, l);
+}
+
 template <int C, int D>
 __global__ __launch_bounds__(4 * D) void bwd_scan_split_kernel(ChunkParams p, BwdParams bw) {
-  using M = Mma<bf16_t>;
   using S = ScanSplitSmem<C, D>;
-  constexpr int NT = 4 * D, NC = C / 16, DT = D / 16, LC = S::LC, LD = S::LD;
+  constexpr int NT = 4 * D, NC = C / 16, DT = D / 16, LA = S::LA, LT = S::LT;
   const int nh = blockIdx.x;
   const int n = nh / p.H, h = nh % p.H;
   const int wid = wave_id();
@@ -486,10 +461,11 @@ __global__ __launch_bounds__(4 * D) void bwd_scan_split_kernel(ChunkParams p, Bw
   const int64_t ld = (int64_t)p.H * D;
   extern __shared__ __align__(16) char smem[];
   const float *sBL = reinterpret_cast<const float *>(smem + S::bl);
-  // a 16-byte operand fragment: row r of a bf16 tile, slots 8 g .. 8 g + 7 of contraction block s
-  auto frag = [&](size_t base, int ldr, int r, int s) {
-    return *reinterpret_cast<const bf16x8_t *>(smem + base + 2 * (r * ldr + 32 * s + 8 * grp));
-  };
+  const bf16_t *atH = reinterpret_cast<const bf16_t *>(smem + S::atH), *atL = reinterpret_cast<const bf16_t *>(smem + S::atL);
+  const bf16_t *dO = reinterpret_cast<const bf16_t *>(smem + S::dO);
+  const bf16_t *kH = reinterpret_cast<const bf16_t *>(smem + S::kH), *kL = reinterpret_cast<const bf16_t *>(smem + S::kL);
+  const bf16_t *qH = reinterpret_cast<const bf16_t *>(smem + S::qH), *qL = reinterpret_cast<const bf16_t *>(smem + S::qL);
+  const bf16_t *wH = reinterpret_cast<const bf16_t *>(smem + S::wH), *wL = reinterpret_cast<const bf16_t *>(smem + S::wL);
 
   f32x4_t dh[DT];
 #pragma unroll
@@ -520,26 +496,30 @@ __global__ __launch_bounds__(4 * D) void bwd_scan_split_kernel(ChunkParams p, Bw
     }
     __syncthreads();
     if (c > 0) R.load(p, bw, t0 - C, C, h);  // every chunk but a slot's last has C rows
+    const int loA = cfrag_lane_off(LA), loT = cfrag_lane_off(LT);
     // dv_new = A_qk^T do + k~ dh (rows past L fall outside the range)
     const rsrc_t rdv = store_rsrc(bw.dvn + t0 * ld + h * D, (uint32_t)((L - 1) * ld + D) * 4u);
+    bf16x4_t dhH[DT], dhL[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) split4(dh[t], dhH[t], dhL[t]);
     f32x4_t dv[NC];
 #pragma unroll
     for (int rt = 0; rt < NC; ++rt) {
       f32x4_t acc = zero4();
 #pragma unroll
-      for (int s = 0; s < C / 32; ++s) {
-        const bf16x8_t o = frag(S::doT, LC, 16 * wid + n16, s);
-        acc = M::mma(frag(S::atH, LC, 16 * rt + n16, s), o, acc);
-        acc = M::mma(frag(S::atL, LC, 16 * rt + n16, s), o, acc);
+      for (int kb = 0; kb < NC; ++kb) {
+        const bf16x4_t o = load_cfrag_at(dO + 16 * kb * LT + 16 * wid, loT);
+        acc = mma16(load_cfrag_at(atH + 16 * kb * LA + 16 * rt, loA), o, acc);
+        acc = mma16(load_cfrag_at(atL + 16 * kb * LA + 16 * rt, loA), o, acc);
       }
+      const int ko = (16 * rt + n16) * LT + 4 * grp;  // k~ row of this lane, channels 16 ib + 4 g ..
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        bf16x8_t bh, bl;
-        split_frag(dh[2 * s], dh[2 * s + 1], bh, bl);
-        const bf16x8_t ah = frag(S::kH, LD, 16 * rt + n16, s), al = frag(S::kL, LD, 16 * rt + n16, s);
-        acc = M::mma(ah, bh, acc);
-        acc = M::mma(ah, bl, acc);
-        acc = M::mma(al, bh, acc);
+      for (int ib = 0; ib < DT; ++ib) {
+        const bf16x4_t ah = *reinterpret_cast<const bf16x4_t *>(kH + ko + 16 * ib);
+        const bf16x4_t al = *reinterpret_cast<const bf16x4_t *>(kL + ko + 16 * ib);
+        acc = mma16(ah, dhH[ib], acc);
+        acc = mma16(ah, dhL[ib], acc);
+        acc = mma16(al, dhH[ib], acc);
       }
       dv[rt] = acc;
 #pragma unroll
@@ -547,21 +527,21 @@ __global__ __launch_bounds__(4 * D) void bwd_scan_split_kernel(ChunkParams p, Bw
     }
     if (c > 0) R.load_w(p, t0 - C, C, h);
     // dh <- 2^b_L dh + q~^T do - w^T dv_new
-    bf16x8_t vh[C / 32], vl[C / 32];
+    bf16x4_t vh[NC], vl[NC];
 #pragma unroll
-    for (int s = 0; s < C / 32; ++s) split_frag(dv[2 * s], dv[2 * s + 1], vh[s], vl[s]);
+    for (int kb = 0; kb < NC; ++kb) split4(dv[kb], vh[kb], vl[kb]);
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       f32x4_t acc = zero4(), wv = zero4();
 #pragma unroll
-      for (int s = 0; s < C / 32; ++s) {
-        const bf16x8_t o = frag(S::doT, LC, 16 * wid + n16, s);
-        acc = M::mma(frag(S::qH, LC, 16 * t + n16, s), o, acc);
-        acc = M::mma(frag(S::qL, LC, 16 * t + n16, s), o, acc);
-        const bf16x8_t ah = frag(S::wH, LC, 16 * t + n16, s), al = frag(S::wL, LC, 16 * t + n16, s);
-        wv = M::mma(ah, vh[s], wv);
-        wv = M::mma(ah, vl[s], wv);
-        wv = M::mma(al, vh[s], wv);
+      for (int kb = 0; kb < NC; ++kb) {
+        const bf16x4_t o = load_cfrag_at(dO + 16 * kb * LT + 16 * wid, loT);
+        acc = mma16(load_cfrag_at(qH + 16 * kb * LT + 16 * t, loT), o, acc);
+        acc = mma16(load_cfrag_at(qL + 16 * kb * LT + 16 * t, loT), o, acc);
+        const bf16x4_t ah = load_cfrag_at(wH + 16 * kb * LT + 16 * t, loT);
+        wv = mma16(ah, vh[kb], wv);
+        wv = mma16(ah, vl[kb], wv);
+        wv = mma16(load_cfrag_at(wL + 16 * kb * LT + 16 * t, loT), vh[kb], wv);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) dh[t][e] = fast_exp2(sBL[16 * t + tile_row(e)]) * dh[t][e] + acc[e] - wv[e];
