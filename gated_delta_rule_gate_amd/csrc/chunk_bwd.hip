@@ -841,21 +841,25 @@ __global__ __launch_bounds__(kContractThreads) void bwd_contract_kernel(ChunkPar
 }
 
 // ---- the WY factors and the triangular inverse ----
-// Persistent workgroups of eight waves walk (chunk, head) items. An item's
-// operands (T, dT_u, dw, X_w = k 2^b, dv_new, v) go to LDS once, from registers
-// loaded while the item before computed; the next item's loads are issued once
-// X_w has been consumed.
+// Persistent workgroups of eight waves walk (chunk, head) items; the next
+// item's loads are in flight while the current one computes. The products run
+// on the bf16 matrix cores with fp32 operands split into high and low parts
+// (as in the contractions and the scan): dT = dT_u + beta_s (dw X_w^T) and
+// X = dT T^T contract along rows (16x16x32 products from row-major tiles);
+// dA_kk = -T^T X, dX_w = T^T dw and dX_u = T^T dv_new contract over tokens
+// (16x16x16 products, operands through the transposing LDS load).
 template <int C, int D>
 struct WySmem {
-  static constexpr int LA = C + 4, LX = D + 4;
-  static constexpr size_t t = 0;               // fp32 [C][LA] T
-  static constexpr size_t dt = t + 4 * C * LA;  // dT
-  static constexpr size_t x = dt + 4 * C * LA;  // dT T^T
-  static constexpr size_t dw = x + 4 * C * LA;  // fp32 [C][LX] dw, later dX_u
-  static constexpr size_t xw = dw + 4 * C * LX;  // X_w, later v
-  static constexpr size_t dvn = xw + 4 * C * LX;  // dv_new
-  static constexpr size_t beta = dvn + 4 * C * LX;  // [C]
-  static constexpr size_t total = beta + 4 * C;
+  static constexpr int LA = C + 8, LT = D + 8, LU = C + 4;  // bf16 strides; fp32 stride of dT_u
+  static constexpr size_t tH = 0, tL = tH + 2 * C * LA;     // T [C][LA]
+  static constexpr size_t dtH = tL + 2 * C * LA, dtL = dtH + 2 * C * LA;  // dT
+  static constexpr size_t dwH = dtL + 2 * C * LA, dwL = dwH + 2 * C * LT;  // dw [C][LT]
+  static constexpr size_t xwH = dwL + 2 * C * LT, xwL = xwH + 2 * C * LT;  // X_w = k 2^b, later X = dT T^T [C][LA]
+  static constexpr size_t dvH = xwL + 2 * C * LT, dvL = dvH + 2 * C * LT;  // dv_new
+  static constexpr size_t dtu = dvL + 2 * C * LT;  // fp32 [C][LU] dT_u
+  static constexpr size_t beta = dtu + 4 * C * LU;  // fp32 [C]
+  static constexpr size_t dbp = beta + 4 * C;      // fp32 [4][C] partial beta gradients
+  static constexpr size_t total = dbp + 16 * C;
   static_assert(total <= 160 * 1024, "LDS");
 };
 
@@ -864,14 +868,14 @@ struct WyRegs {
   static constexpr int EPV = 16 / (int)sizeof(Tin), NB = EPV / 4;
   static constexpr int NA = C * C / 4, IA = (NA + NT - 1) / NT;               // T, dT_u
   static constexpr int NF = C * D / 4, IF = (NF + NT - 1) / NT;               // dw, dv_new
-  static constexpr int VPR = D / EPV, NI = C * VPR, II = (NI + NT - 1) / NT;  // k, v
-  u32x4_t tm[IA], dtu[IA], dw[IF], dvn[IF], k[II], v[II];
+  static constexpr int VPR = D / EPV, NI = C * VPR, II = (NI + NT - 1) / NT;  // k
+  u32x4_t tm[IA], dtu[IA], dw[IF], dvn[IF], k[II];
   f32x4_t b[II][NB];
   float beta;
 
   __device__ __forceinline__ void load(const ChunkParams &p, const BwdParams &bw, int64_t t0, int L, int h) {
     const int t = threadIdx.x;
-    const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.H * p.Kr, ldv = (int64_t)p.H * p.Vr;
+    const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.H * p.Kr;
     const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int it = 0; it < IA; ++it) {
@@ -890,39 +894,29 @@ struct WyRegs {
       dvn[it] = ok ? *reinterpret_cast<const u32x4_t *>(bw.dvn + o) : z;
     }
     const Tin *gk = reinterpret_cast<const Tin *>(p.k) + t0 * ldk + h * p.Kr;
-    const Tin *gv = reinterpret_cast<const Tin *>(p.v) + t0 * ldv + h * p.Vr;
     const float *gb = p.b + t0 * ld + h * D;
 #pragma unroll
     for (int it = 0; it < II; ++it) {
       const int idx = it * NT + t, r = idx / VPR, c = (idx % VPR) * EPV;
       const bool ok = (NI % NT == 0 || idx < NI) && r < L;
       k[it] = ok && c < p.Kr ? *reinterpret_cast<const u32x4_t *>(gk + r * ldk + c) : z;
-      v[it] = ok && c < p.Vr ? *reinterpret_cast<const u32x4_t *>(gv + r * ldv + c) : z;
 #pragma unroll
       for (int j = 0; j < NB; ++j) b[it][j] = ok ? ld4(gb + r * ld + c + 4 * j) : zero4();
     }
     if (t < C) beta = t < L ? beta_at(p, t0 + t, h) : 0.f;
   }
 
-  static __device__ __forceinline__ void unpack(u32x4_t raw, float (&f)[EPV]) {
-    if constexpr (sizeof(Tin) == 4) {
-      const f32x4_t x = __builtin_bit_cast(f32x4_t, raw);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) f[e] = x[e];
-    } else {
-      const bf16x8_t x = __builtin_bit_cast(bf16x8_t, raw);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) f[e] = static_cast<float>(x[e]);
-    }
+  static __device__ __forceinline__ void put(char *smem, size_t hiOff, size_t loOff, int o, const f32x4_t &x) {
+    u32x2_t hi, lo;
+    split_bf16x4(x, hi, lo);
+    *reinterpret_cast<u32x2_t *>(smem + hiOff + o) = hi;
+    *reinterpret_cast<u32x2_t *>(smem + loOff + o) = lo;
   }
 
-  // everything but v; L masks the columns of T and dT_u
+  // L masks the columns of T and dT_u
   __device__ __forceinline__ void store(char *smem, int L) const {
     using S = WySmem<C, D>;
     const int t = threadIdx.x;
-    float *sT = reinterpret_cast<float *>(smem + S::t), *sDT = reinterpret_cast<float *>(smem + S::dt);
-    float *sDw = reinterpret_cast<float *>(smem + S::dw), *sXw = reinterpret_cast<float *>(smem + S::xw);
-    float *sDvn = reinterpret_cast<float *>(smem + S::dvn);
 #pragma unroll
     for (int it = 0; it < IA; ++it) {
       const int idx = it * NT + t, r = idx / (C / 4), c = (idx % (C / 4)) * 4;
@@ -933,16 +927,16 @@ struct WyRegs {
           a[e] = (c + e <= r && c + e < L) ? a[e] : 0.f;
           d[e] = (c + e < L) ? d[e] : 0.f;
         }
-        *reinterpret_cast<f32x4_t *>(sT + r * S::LA + c) = a;
-        *reinterpret_cast<f32x4_t *>(sDT + r * S::LA + c) = d;
+        put(smem, S::tH, S::tL, 2 * (r * S::LA + c), a);
+        *reinterpret_cast<f32x4_t *>(smem + S::dtu + 4 * (r * S::LU + c)) = d;
       }
     }
 #pragma unroll
     for (int it = 0; it < IF; ++it) {
       const int idx = it * NT + t, r = idx / (D / 4), c = (idx % (D / 4)) * 4;
       if (NF % NT == 0 || idx < NF) {
-        *reinterpret_cast<u32x4_t *>(sDw + r * S::LX + c) = dw[it];
-        *reinterpret_cast<u32x4_t *>(sDvn + r * S::LX + c) = dvn[it];
+        put(smem, S::dwH, S::dwL, 2 * (r * S::LT + c), __builtin_bit_cast(f32x4_t, dw[it]));
+        put(smem, S::dvH, S::dvL, 2 * (r * S::LT + c), __builtin_bit_cast(f32x4_t, dvn[it]));
       }
     }
 #pragma unroll
@@ -950,36 +944,61 @@ struct WyRegs {
       const int idx = it * NT + t, r = idx / VPR, c = (idx % VPR) * EPV;
       if (NI % NT == 0 || idx < NI) {
         float f[EPV];
-        unpack(k[it], f);
+        if constexpr (sizeof(Tin) == 4) {
+          const f32x4_t x = __builtin_bit_cast(f32x4_t, k[it]);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) f[e] = x[e];
+        } else {
+          const bf16x8_t x = __builtin_bit_cast(bf16x8_t, k[it]);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) f[e] = static_cast<float>(x[e]);
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           f32x4_t x;
 #pragma unroll
           for (int e = 0; e < 4; ++e) x[e] = f[4 * j + e] * fast_exp2(b[it][j][e]);
-          *reinterpret_cast<f32x4_t *>(sXw + r * S::LX + c + 4 * j) = x;
+          put(smem, S::xwH, S::xwL, 2 * (r * S::LT + c + 4 * j), x);
         }
       }
     }
     if (t < C) reinterpret_cast<float *>(smem + S::beta)[t] = beta;
   }
-
-  // v, over X_w once the latter is consumed
-  __device__ __forceinline__ void store_v(char *smem) const {
-    using S = WySmem<C, D>;
-    float *sV = reinterpret_cast<float *>(smem + S::xw);
-#pragma unroll
-    for (int it = 0; it < II; ++it) {
-      const int idx = it * NT + threadIdx.x, r = idx / VPR, c = (idx % VPR) * EPV;
-      if (NI % NT == 0 || idx < NI) {
-        float f[EPV];
-        unpack(v[it], f);
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          *reinterpret_cast<f32x4_t *>(sV + r * S::LX + c + 4 * j) = f32x4_t{f[4 * j], f[4 * j + 1], f[4 * j + 2], f[4 * j + 3]};
-      }
-    }
-  }
 };
+
+// acc += A B^T over K columns k0 .. k0 + 31 of two [rows][ld] bf16 hi / lo tile pairs
+template <int LDR>
+__device__ __forceinline__ f32x4_t mma_split_rows(f32x4_t acc, const char *smem, size_t aH, size_t aL, int a0,
+                                                  size_t bH, size_t bL, int b0, int k0) {
+  using M = Mma<bf16_t>;
+  const int lane = tid_opaque() & 63, r = lane & 15, g = lane >> 4;
+  const int ao = 2 * ((a0 + r) * LDR + k0 + 8 * g), bo = 2 * ((b0 + r) * LDR + k0 + 8 * g);
+  const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(smem + aH + ao);
+  const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(smem + aL + ao);
+  const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(smem + bH + bo);
+  const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(smem + bL + bo);
+  acc = M::mma(ah, bh, acc);
+  acc = M::mma(ah, bl, acc);
+  return M::mma(al, bh, acc);
+}
+
+// acc += A^T B over 16-token blocks: A [C][lda] and B [C][ldb] bf16 hi / lo pairs
+// (row = token), output rows a0 .., columns b0 ..
+template <int C, int LDA_, int LDB_>
+__device__ __forceinline__ f32x4_t mma_split_tokens(f32x4_t acc, const char *smem, size_t aH, size_t aL, int a0,
+                                                    size_t bH, size_t bL, int b0, int loA, int loB) {
+  const bf16_t *pAh = reinterpret_cast<const bf16_t *>(smem + aH), *pAl = reinterpret_cast<const bf16_t *>(smem + aL);
+  const bf16_t *pBh = reinterpret_cast<const bf16_t *>(smem + bH), *pBl = reinterpret_cast<const bf16_t *>(smem + bL);
+#pragma unroll
+  for (int kb = 0; kb < C / 16; ++kb) {
+    const bf16x4_t ah = load_cfrag_at(pAh + 16 * kb * LDA_ + a0, loA), al = load_cfrag_at(pAl + 16 * kb * LDA_ + a0, loA);
+    const bf16x4_t bh = load_cfrag_at(pBh + 16 * kb * LDB_ + b0, loB), bl = load_cfrag_at(pBl + 16 * kb * LDB_ + b0, loB);
+    acc = mma16(ah, bh, acc);
+    acc = mma16(ah, bl, acc);
+    acc = mma16(al, bh, acc);
+  }
+  return acc;
+}
 
 constexpr int kWyThreads = 512;
 
@@ -987,19 +1006,19 @@ template <typename Tin, int C, int D>
 __global__ __launch_bounds__(kWyThreads) void bwd_wy_kernel(ChunkParams p, BwdParams bw) {
   constexpr int NT = kWyThreads, NW = NT / 64, NC = C / 16, DT = D / 16;
   using S = WySmem<C, D>;
-  constexpr int LA = S::LA, LX = S::LX;
+  constexpr int LA = S::LA, LT = S::LT, LU = S::LU;
   constexpr int NCW = (NC * NC + NW - 1) / NW, NDW = (NC * DT + NW - 1) / NW;  // tiles per wave
-  constexpr int TPR = NT / C, CPT = D / TPR;  // threads per row and columns per thread of the dv pass
-  static_assert(TPR <= 64 && 64 % TPR == 0 && D % TPR == 0, "row groups inside a wave");
-  const int wid = threadIdx.x >> 6;
+  static_assert(NC * DT % NW == 0, "whole tiles per wave");
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63, n16 = lane & 15, grp = lane >> 4;
   const int total = p.cu ? p.chunk_off[p.N] : p.B * ((p.T + C - 1) / C);
   const int64_t items = (int64_t)total * p.H;
   const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldv = (int64_t)p.H * p.Vr;
   extern __shared__ __align__(16) char smem[];
-  float *sT = reinterpret_cast<float *>(smem + S::t), *sDT = reinterpret_cast<float *>(smem + S::dt);
-  float *sX = reinterpret_cast<float *>(smem + S::x), *sDw = reinterpret_cast<float *>(smem + S::dw);
-  const float *sXw = reinterpret_cast<const float *>(smem + S::xw), *sDvn = reinterpret_cast<const float *>(smem + S::dvn);
-  const float *sV = sXw, *sBeta = reinterpret_cast<const float *>(smem + S::beta);
+  const float *sBeta = reinterpret_cast<const float *>(smem + S::beta);
+  const float *sDtu = reinterpret_cast<const float *>(smem + S::dtu);
+  float *sDbp = reinterpret_cast<float *>(smem + S::dbp);
+  bf16_t *dtH = reinterpret_cast<bf16_t *>(smem + S::dtH), *dtL = reinterpret_cast<bf16_t *>(smem + S::dtL);
+  bf16_t *xH = reinterpret_cast<bf16_t *>(smem + S::xwH), *xL = reinterpret_cast<bf16_t *>(smem + S::xwL);
 
   WyRegs<Tin, C, D, NT> R;
   auto locate = [&](int64_t it, ChunkLoc &lc, int &h) {
@@ -1020,99 +1039,129 @@ __global__ __launch_bounds__(kWyThreads) void bwd_wy_kernel(ChunkParams p, BwdPa
     const int L = lc.L;
     const int64_t t0 = lc.t0;
     R.store(smem, L);
-    __syncthreads();
-    // dT = dT_u + beta_s (dw X_w^T)_rs
-    f32x4_t acc[NCW];
+    // v of this wave's dX_u elements (rows 16 rt + 4 g + e, column 16 ct + n16), for the beta gradient
+    float vv[NDW][4];
 #pragma unroll
-    for (int t = 0; t < NCW; ++t) {
-      const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
-      acc[t] = (NC * NC % NW == 0 || tile < NC * NC) ? mm16<D>(zero4(), sDw, LX, 1, sXw, 1, LX, 16 * rt, 16 * st)
-                                                     : zero4();
-    }
+    for (int t = 0; t < NDW; ++t) {
+      const int tile = wid * NDW + t, rt = tile / DT, ct = tile % DT;
+      const int j = 16 * ct + n16;
 #pragma unroll
-    for (int t = 0; t < NCW; ++t) {
-      const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
-      if (NC * NC % NW == 0 || tile < NC * NC) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rt + tile_row(e), sc = 16 * st + tile_col();
-          sDT[r * LA + sc] += sBeta[sc] * acc[t][e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + tile_row(e);
+        vv[t][e] = (r < L && j < p.Vr) ? to_f32(reinterpret_cast<const Tin *>(p.v)[(t0 + r) * ldv + h * p.Vr + j]) : 0.f;
       }
     }
     __syncthreads();
-    // X_w is consumed: v takes its place, and the next item's loads go out
-    R.store_v(smem);
     if (it + gridDim.x < items) {
       ChunkLoc ln;
       int hn;
       locate(it + gridDim.x, ln, hn);
       R.load(p, bw, ln.t0, ln.L, hn);
     }
-    // X = dT T^T
+    // dT = dT_u + beta_s (dw X_w^T)_rs, to LDS as hi / lo
 #pragma unroll
     for (int t = 0; t < NCW; ++t) {
       const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
       if (NC * NC % NW == 0 || tile < NC * NC) {
-        const f32x4_t a = mm16<C>(zero4(), sDT, LA, 1, sT, 1, LA, 16 * rt, 16 * st);
+        f32x4_t acc = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sX[(16 * rt + tile_row(e)) * LA + 16 * st + tile_col()] = a[e];
+        for (int k0 = 0; k0 < D; k0 += 32)
+          acc = mma_split_rows<LT>(acc, smem, S::dwH, S::dwL, 16 * rt, S::xwH, S::xwL, 16 * st, k0);
+        const int sc = 16 * st + n16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + tile_row(e);
+          const float x = sDtu[r * LU + sc] + sBeta[sc] * acc[e];
+          const bf16_t hh = static_cast<bf16_t>(x);
+          dtH[r * LA + sc] = hh;
+          dtL[r * LA + sc] = static_cast<bf16_t>(x - static_cast<float>(hh));
+        }
+      }
+    }
+    __syncthreads();  // dT complete; X_w consumed
+    // X = dT T^T, over X_w's place
+#pragma unroll
+    for (int t = 0; t < NCW; ++t) {
+      const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
+      if (NC * NC % NW == 0 || tile < NC * NC) {
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32)
+          acc = mma_split_rows<LA>(acc, smem, S::dtH, S::dtL, 16 * rt, S::tH, S::tL, 16 * st, k0);
+        const int sc = 16 * st + n16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + tile_row(e);
+          const bf16_t hh = static_cast<bf16_t>(acc[e]);
+          xH[r * LA + sc] = hh;
+          xL[r * LA + sc] = static_cast<bf16_t>(acc[e] - static_cast<float>(hh));
+        }
       }
     }
     __syncthreads();
-    // dA_kk = -strict_lower(T^T X); dX_w = T^T dw; dX_u = T^T dv_new (rows past L fall outside the ranges)
+    const int loA = cfrag_lane_off(LA), loT = cfrag_lane_off(LT);
+    // dA_kk = -strict_lower(T^T X) (rows past L fall outside the range)
     const rsrc_t rak = store_rsrc(bw.dAkk + t0 * ldc + h * C, (uint32_t)((L - 1) * ldc + C) * 4u);
-    const rsrc_t rxw = store_rsrc(bw.dXw + t0 * ld + h * D, (uint32_t)((L - 1) * ld + D) * 4u);
 #pragma unroll
     for (int t = 0; t < NCW; ++t) {
       const int tile = wid * NCW + t, rt = tile / NC, st = tile % NC;
       if (NC * NC % NW == 0 || tile < NC * NC) {
-        const f32x4_t a = mm16<C>(zero4(), sT, 1, LA, sX, LA, 1, 16 * rt, 16 * st);
+        const f32x4_t a = mma_split_tokens<C, LA, LA>(zero4(), smem, S::tH, S::tL, 16 * rt, S::xwH, S::xwL, 16 * st,
+                                                      loA, loA);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rt + tile_row(e), sc = 16 * st + tile_col();
+          const int r = 16 * rt + tile_row(e), sc = 16 * st + n16;
           bstore_f32(rak, (uint32_t)(r * ldc + sc) * 4u, (sc < r) ? -a[e] : 0.f);
         }
       }
     }
-    f32x4_t xu[NDW];
+    // dX_w = T^T dw; dX_u = T^T dv_new, dv = beta dX_u, and the beta gradient through u
+    const rsrc_t rxw = store_rsrc(bw.dXw + t0 * ld + h * D, (uint32_t)((L - 1) * ld + D) * 4u);
+    float dbp[NDW][4];
 #pragma unroll
     for (int t = 0; t < NDW; ++t) {
       const int tile = wid * NDW + t, rt = tile / DT, ct = tile % DT;
-      if (NC * DT % NW == 0 || tile < NC * DT) {
-        const f32x4_t a = mm16<C>(zero4(), sT, 1, LA, sDw, LX, 1, 16 * rt, 16 * ct);
+      const f32x4_t a = mma_split_tokens<C, LA, LT>(zero4(), smem, S::tH, S::tL, 16 * rt, S::dwH, S::dwL, 16 * ct,
+                                                    loA, loT);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          bstore_f32(rxw, (uint32_t)((16 * rt + tile_row(e)) * ld + 16 * ct + tile_col()) * 4u, a[e]);
-        xu[t] = mm16<C>(zero4(), sT, 1, LA, sDvn, LX, 1, 16 * rt, 16 * ct);
+      for (int e = 0; e < 4; ++e)
+        bstore_f32(rxw, (uint32_t)((16 * rt + tile_row(e)) * ld + 16 * ct + n16) * 4u, a[e]);
+      const f32x4_t u = mma_split_tokens<C, LA, LT>(zero4(), smem, S::tH, S::tL, 16 * rt, S::dvH, S::dvL, 16 * ct,
+                                                    loA, loT);
+      const int j = 16 * ct + n16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + tile_row(e);
+        if (r < L && j < p.Vr)
+          reinterpret_cast<Tin *>(bw.dv)[(t0 + r) * ldv + h * p.Vr + j] = from_f32<Tin>(sBeta[r] * u[e]);
+        dbp[t][e] = u[e] * vv[t][e];
       }
     }
-    __syncthreads();  // every wave is done reading dw
-#pragma unroll
-    for (int t = 0; t < NDW; ++t) {
-      const int tile = wid * NDW + t, rt = tile / DT, ct = tile % DT;
-      if (NC * DT % NW == 0 || tile < NC * DT) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sDw[(16 * rt + tile_row(e)) * LX + 16 * ct + tile_col()] = xu[t][e];
-      }
-    }
-    __syncthreads();
-    // dv = beta dX_u; the beta gradient through u, sum over j of dX_u v
+    // beta gradient: per row, over the lane's columns, then the 16 lanes of a row
+    // group, then the waves sharing the row block (in a fixed order)
     {
-      const int rr = threadIdx.x / TPR, q = threadIdx.x % TPR;
-      float dbp = 0.f;
-      Tin *gdv = reinterpret_cast<Tin *>(bw.dv) + (t0 + rr) * ldv + h * p.Vr;
-      const float be = sBeta[rr];
+      constexpr int WPR = DT / NDW;  // waves per 16-row block
+      static_assert(WPR >= 1 && WPR <= 4 && DT % NDW == 0, "waves per row block");
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < CPT; ++m) {
-        const int j = q * CPT + m;
-        const float x = sDw[rr * LX + j];
-        dbp += x * sV[rr * LX + j];
-        if (rr < L && j < p.Vr) gdv[j] = from_f32<Tin>(be * x);
+      for (int t = 0; t < NDW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rs[e] += dbp[t][e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) rs[e] += __shfl_xor(rs[e], m);
+      const int rt = (wid * NDW) / DT, part = ((wid * NDW) % DT) / NDW;
+      if (n16 == 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sDbp[part * C + 16 * rt + tile_row(e)] = rs[e];
+      __syncthreads();
+      if (threadIdx.x < C && threadIdx.x < L) {
+        float d = sDbp[threadIdx.x];
+#pragma unroll
+        for (int q = 1; q < WPR; ++q) d += sDbp[q * C + threadIdx.x];
+        bw.dbp[(t0 + threadIdx.x) * p.H + h] = d;
       }
-#pragma unroll
-      for (int m = 1; m < TPR; m <<= 1) dbp += __shfl_xor(dbp, m);
-      if (q == 0 && rr < L) bw.dbp[(t0 + rr) * p.H + h] = dbp;
     }
     __syncthreads();  // the buffers are rewritten by the next item
   }
