@@ -1218,8 +1218,34 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
   for (int idx = threadIdx.x; idx < NW * C; idx += kBT) sDbw[idx] = 0.f;
   float dA_total = 0.f;
   const float *gb = p.b + t0 * ld + h * D;
+  const int cl = 16 * wid + n16;  // this lane's channel within a slab
+  // this lane's elements of dq~, dX_w, dk~ of row block I (rows 16I + 4grp + e)
+  auto load_p = [&](int i0, int I, float (&pq)[4], float (&px)[4], float (&pk)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * I + 4 * grp + e, i = i0 + cl;
+      const bool ok = r < L && i < Kr;
+      const int64_t eo = (t0 + (ok ? r : 0)) * ld + h * D + (ok ? i : 0);
+      pq[e] = ok ? bw.dqt[eo] : 0.f;
+      px[e] = ok ? bw.dXw[eo] : 0.f;
+      pk[e] = ok ? bw.dkt[eo] : 0.f;
+    }
+  };
+  // the gate activation's pass: thread = (row group, 4 channels)
+  constexpr int CG = SI / 4, RG = kBT / CG, NXR = (C + RG - 1) / RG;
+  const int c4 = 4 * (threadIdx.x % CG), rg = threadIdx.x / CG;
   for (int i0 = 0; i0 < Kr; i0 += SI) {
     __syncthreads();
+    // issued first, consumed later: block 0's elements and the gate input of the activation pass
+    float pq[4], px[4], pk[4];
+    load_p(i0, 0, pq, px, pk);
+    f32x4_t xs[NXR];
+#pragma unroll
+    for (int m = 0; m < NXR; ++m) {
+      const int rr = rg + RG * m, i = i0 + c4;
+      xs[m] = ((GK == kGateSafe || GK == kGateSoftplus) && rr < L && i < Kr)
+                  ? ld4(p.g + (t0 + rr) * ldk + h * Kr + i) : zero4();
+    }
     tile_f32<Tin, C, SI>(sK, LS, gk + t0 * ldk + h * Kr + i0, ldk, L, Kr - i0);
     tile_f32<Tin, C, SI>(sQ, LS, gq + t0 * ldk + h * Kr + i0, ldk, L, Kr - i0);
     tile_f32<float, C, SI>(sB, LS, gb + i0, ld, L, SI, [&](int r, int c, float *v) {
@@ -1231,22 +1257,13 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
     for (int ii = threadIdx.x; ii < SI; ii += kBT) sBL[ii] = gb[(int64_t)(L - 1) * ld + i0 + ii];
     __syncthreads();
 
-    const int cl = 16 * wid + n16;  // this lane's channel within the slab
     float ctl = 0.f;                // sum over this lane's rows of k 2^(b_L - b) dk~
 #pragma unroll 1
     for (int I = 0; I < NC; ++I) {
       const float aI = sB[16 * I * LS + cl];
-      // this lane's elements of dq~, dX_w, dk~, loaded while the products run
-      float pq[4], px[4], pk[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * I + 4 * grp + e, i = i0 + cl;
-        const bool ok = r < L && i < Kr;
-        const int64_t eo = (t0 + (ok ? r : 0)) * ld + h * D + (ok ? i : 0);
-        pq[e] = ok ? bw.dqt[eo] : 0.f;
-        px[e] = ok ? bw.dXw[eo] : 0.f;
-        pk[e] = ok ? bw.dkt[eo] : 0.f;
-      }
+      // the next block's elements, loaded while this block's products run
+      float nq[4], nx[4], nk[4];
+      if (I + 1 < NC) load_p(i0, I + 1, nq, nx, nk);
       // Q and R of rows 16I + 4grp + e: blocks J < I, then the diagonal block
       f32x4_t aq = zero4(), ar = zero4();
 #pragma unroll 1
@@ -1364,18 +1381,33 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
       // this wave alone reads these rows of its channels again: dB goes over q
 #pragma unroll
       for (int e = 0; e < 4; ++e) sQ[(16 * I + 4 * grp + e) * LS + cl] = dBv[e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pq[e] = nq[e];
+        px[e] = nx[e];
+        pk[e] = nk[e];
+      }
     }
     // b_L's share summed over the rows: the lanes of one channel hold 4 rows each
     ctl += __shfl_xor(ctl, 16);
     ctl += __shfl_xor(ctl, 32);
     if (grp == 0) sCT[cl] = ctl;
     __syncthreads();
-    // per channel: b_L's terms and the reverse cumsum, in place in sQ (which holds dB)
-    if (threadIdx.x < SI) {
-      const int ii = threadIdx.x, i = i0 + ii;
+    // per channel: b_L's terms and the reverse cumsum, in place in sQ (which holds
+    // dB): each channel's rows in NQ quarters, the quarter sums (in sB, free now)
+    // added in row order to the later quarters
+    {
+      constexpr int NQ = kBT / SI, RQ = C / NQ;
+      const int ii = threadIdx.x % SI, q = threadIdx.x / SI, i = i0 + ii;
+      const int r0 = q * RQ, r1 = min(r0 + RQ, L);
+      float part = 0.f;
+      for (int rr = r0; rr < r1; ++rr) part += sQ[rr * LS + ii];
+      sB[q * SI + ii] = part;
+      __syncthreads();
       if (i < Kr) {
         float acc = sCT[ii] + fast_exp2(sBL[ii]) * bw.dlam[((int64_t)lc.gci * p.H + h) * D + i];
-        for (int rr = L - 1; rr >= 0; --rr) {
+        for (int q2 = NQ - 1; q2 > q; --q2) acc += sB[q2 * SI + ii];
+        for (int rr = r1 - 1; rr >= r0; --rr) {
           acc += sQ[rr * LS + ii];
           sQ[rr * LS + ii] = acc;  // gradient of the natural-log decay of token rr
         }
@@ -1384,17 +1416,18 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
     __syncthreads();
     // per element: the gate activation's derivative; thread = (row group, 4 channels)
     {
-      constexpr int CG = SI / 4, RG = kBT / CG;  // channel groups, row groups
-      const int c4 = 4 * (threadIdx.x % CG), rg = threadIdx.x / CG, i = i0 + c4;
+      const int i = i0 + c4;
       float ddt4[4] = {0.f, 0.f, 0.f, 0.f}, dA4 = 0.f;
       f32x4_t dt4 = zero4();
       if (p.dt_bias && i < Kr) dt4 = ld4(p.dt_bias + h * Kr + i);
-      for (int rr = rg; rr < L; rr += RG) {
-        if (i >= Kr) break;
+#pragma unroll
+      for (int m = 0; m < NXR; ++m) {
+        const int rr = rg + RG * m;
+        if (rr >= L || i >= Kr) break;
         const f32x4_t g4 = ld4(sQ + rr * LS + c4);
         f32x4_t out = g4;
         if constexpr (GK == kGateSafe || GK == kGateSoftplus) {
-          const f32x4_t x4 = ld4(p.g + (t0 + rr) * ldk + h * Kr + i);
+          const f32x4_t x4 = xs[m];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float z = x4[e] + dt4[e];
@@ -1418,7 +1451,6 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
     }
     __syncthreads();
     if (threadIdx.x < SI) {
-      constexpr int RG = kBT / (SI / 4);
       const int ii = threadIdx.x, i = i0 + ii;
       float dsum = 0.f, dAcc = 0.f;
       for (int g2 = 0; g2 < RG; ++g2) {
