@@ -5,6 +5,7 @@
 // Grids are sized from capacity; workgroups past the last chunk exit at once,
 // so no launch depends on a host read of cu_seqlens.
 #include "../../include/kda.h"
+#include "chunk_fused_tiles.h"
 #include "chunk_loc.h"
 #include "chunk_tiles.h"
 #include "kda_launch.h"
@@ -316,6 +317,166 @@ __global__ __launch_bounds__(256) void stage_scan_kernel(ChunkParams p) {
   if (p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, NVW>(p.ht + sbase, Vr, col0, Kr, hs, Vr);
 }
 
+// The same scan for bf16 inputs (D <= 128) with one workgroup per (sequence,
+// head): D / 16 waves, wave w holding value columns 16w .. 16w + 15 of the state. The next
+// chunk's w, k, b and u are loaded into registers while the current chunk
+// computes. w goes to LDS as bf16 in the operand order of the product with the
+// state (the contraction map of Mma<bf16_t>), k~ row-major, read for the state
+// update with the transposing LDS load; every store is a wide one.
+template <int C, int D>
+struct ScanBf16Smem {
+  static constexpr int LDT = D + 8;
+  static constexpr size_t w = 0, k = w + 2 * C * LDT, decay = k + 2 * C * LDT;
+  static constexpr size_t total = decay + 4 * D;
+};
+
+// position of channel x in the operand order of Mma<bf16_t> (inverse of kidx)
+__device__ __forceinline__ int bf16_op_pos(int x) {
+  const int w = x & 31;
+  return (x & ~31) + 8 * ((w >> 2) & 3) + ((w >> 4) << 2) + (w & 3);
+}
+
+template <int C, int D>
+struct ScanBf16Regs {
+  static constexpr int NT = 4 * D, VPR = D / 8, NI = C * VPR, II = (NI + NT - 1) / NT;  // k vectors
+  static constexpr int NF = C * D / 4, IF = (NF + NT - 1) / NT;                          // w vectors
+  static_assert(NT % VPR == 0, "one channel vector per thread");
+  u32x4_t k[II], w[IF];
+  f32x4_t b[II][2], bl[2];
+  f32x4_t u[C / 16];  // this wave's value columns of u (C layout)
+
+  __device__ __forceinline__ void load(const ChunkParams &p, int64_t t0, int L, int h, int col0) {
+    const int t = threadIdx.x;
+    const int64_t ld = (int64_t)p.H * D, ldk = (int64_t)p.Hk * p.Kr;
+    const bf16_t *gk = reinterpret_cast<const bf16_t *>(p.k) + t0 * ldk + (h / (p.H / p.Hk)) * p.Kr;
+    const float *gb = p.b + t0 * ld + h * D, *gw = p.w + t0 * ld + h * D;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int it = 0; it < II; ++it) {
+      const int idx = it * NT + t, r = idx / VPR, c = (idx % VPR) * 8;
+      const bool ok = (NI % NT == 0 || idx < NI) && r < L;
+      k[it] = ok && c < p.Kr ? *reinterpret_cast<const u32x4_t *>(gk + r * ldk + c) : z;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[it][j] = ok ? *reinterpret_cast<const f32x4_t *>(gb + r * ld + c + 4 * j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const int c0 = (t % VPR) * 8;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bl[j] = *reinterpret_cast<const f32x4_t *>(gb + (int64_t)(L - 1) * ld + c0 + 4 * j);
+#pragma unroll
+    for (int it = 0; it < IF; ++it) {
+      const int idx = it * NT + t, r = idx / (D / 4), c = (idx % (D / 4)) * 4;
+      w[it] = ((NF % NT == 0 || idx < NF) && r < L) ? *reinterpret_cast<const u32x4_t *>(gw + r * ld + c) : z;
+    }
+    f32x4_t uu[C / 16][1];
+    load_strip<C / 16, 1>(uu, p.u + t0 * ld + h * D, ld, col0, L);
+#pragma unroll
+    for (int i = 0; i < C / 16; ++i) u[i] = uu[i][0];
+  }
+
+  __device__ __forceinline__ void store(char *smem) const {
+    using S = ScanBf16Smem<C, D>;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < II; ++it) {
+      const int idx = it * NT + t, r = idx / VPR, c = (idx % VPR) * 8;
+      if (NI % NT == 0 || idx < NI) {
+        const bf16x8_t k8 = __builtin_bit_cast(bf16x8_t, k[it]);
+        float kt[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kt[e] = static_cast<float>(k8[e]) * fast_exp2(bl[e >> 2][e & 3] - b[it][e >> 2][e & 3]);
+        *reinterpret_cast<bf16x8_t *>(smem + S::k + 2 * (r * S::LDT + c)) = pack_bf16x8(kt);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < IF; ++it) {
+      const int idx = it * NT + t, r = idx / (D / 4), c = (idx % (D / 4)) * 4;
+      if (NF % NT == 0 || idx < NF)
+        *reinterpret_cast<bf16x4_t *>(smem + S::w + 2 * (r * S::LDT + bf16_op_pos(c))) =
+            to_bf16x4(__builtin_bit_cast(f32x4_t, w[it]));
+    }
+    if (t < VPR) {
+      float *sDecay = reinterpret_cast<float *>(smem + S::decay);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sDecay[t * 8 + e] = fast_exp2(bl[e >> 2][e & 3]);
+    }
+  }
+};
+
+template <int C, int D>
+__global__ __launch_bounds__(4 * D) void stage_scan_bf16_kernel(ChunkParams p) {
+  using S = ScanBf16Smem<C, D>;
+  using M = Mma<bf16_t>;
+  constexpr int NT = 4 * D, NC = C / 16, DT = D / 16, LDT = S::LDT;
+  const int nh = blockIdx.x, n = nh / p.H, h = nh % p.H;
+  const int wid = wave_id();
+  const int n16 = tid_opaque() & 15, grp = (tid_opaque() & 63) >> 4;
+  const int col0 = 16 * wid;
+  const SlotRange sr = slot_range(p.cu, n, p.T);
+  const int nch = (sr.len + C - 1) / C;
+  const int cbase = p.cu ? p.chunk_off[n] : n * ((p.T + C - 1) / C);
+  const int Kr = p.Kr, Vr = p.Vr;
+  const int64_t sbase = (int64_t)nh * Kr * Vr;  // states [Kr, Vr]
+  const int64_t ld = (int64_t)p.H * D;
+  extern __shared__ __align__(16) char smem[];
+  const bf16_t *sW = reinterpret_cast<const bf16_t *>(smem + S::w), *sK = reinterpret_cast<const bf16_t *>(smem + S::k);
+  const float *sDecay = reinterpret_cast<const float *>(smem + S::decay);
+
+  f32x4_t hs[DT][1];
+  if (p.h0) {
+    load_strip<DT, 1>(hs, p.h0 + sbase, Vr, col0, Kr, Vr);
+  } else {
+#pragma unroll
+    for (int t = 0; t < DT; ++t) hs[t][0] = zero4();
+  }
+  ScanBf16Regs<C, D> R;
+  if (nch > 0) R.load(p, sr.t0, min(C, sr.len), h, col0);
+  for (int c = 0; c < nch; ++c) {
+    const int64_t t0 = sr.t0 + (int64_t)c * C;
+    const int L = min(C, sr.len - c * C);
+    store_strip<float, DT, 1>(p.hc + ((int64_t)(cbase + c) * p.H + h) * Kr * Vr, Vr, col0, Kr, hs, Vr);
+    R.store(smem);
+    f32x4_t uv[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) uv[i] = R.u[i];
+    __syncthreads();
+    if (c + 1 < nch) R.load(p, t0 + C, min(C, sr.len - (c + 1) * C), h, col0);
+    // v_new = u - w h (w in operand order, h's accumulators as the B operand)
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      f32x4_t col[DT];
+#pragma unroll
+      for (int t = 0; t < DT; ++t) col[t] = hs[t][0];
+      const bf16x8_t fh = acc_frag<bf16_t, DT>(col, s);
+#pragma unroll
+      for (int i = 0; i < NC; ++i)
+        uv[i] = uv[i] - M::mma(*reinterpret_cast<const bf16x8_t *>(sW + (16 * i + n16) * LDT + 32 * s + 8 * grp), fh,
+                               zero4());
+    }
+    {
+      f32x4_t vs[NC][1];
+#pragma unroll
+      for (int i = 0; i < NC; ++i) vs[i][0] = uv[i];
+      store_strip<float, NC, 1>(p.vnew + t0 * ld + h * D, ld, col0, L, vs);
+    }
+    // h <- Diag(2^b_L) h + k~^T v_new (k~ through the transposing load, v_new's accumulators as B)
+    const int lo = cfrag_lane_off(LDT);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const f32x4_t dec = *reinterpret_cast<const f32x4_t *>(sDecay + 16 * t + 4 * grp);
+      hs[t][0] = hs[t][0] * dec;
+    }
+#pragma unroll
+    for (int kb = 0; kb < NC; ++kb) {
+      const bf16x4_t fv = to_bf16x4(uv[kb]);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) hs[t][0] = mma16(load_cfrag_at(sK + 16 * kb * LDT + 16 * t, lo), fv, hs[t][0]);
+    }
+    __syncthreads();
+  }
+  if (p.ht && !(sr.len == 0 && p.ht == p.h0)) store_strip<float, DT, 1>(p.ht + sbase, Vr, col0, Kr, hs, Vr);
+}
+
 // ---- (6) output o = q~ h_c + A_qk v_new, per (chunk, head, 64-column value block) ----
 template <typename Tin, int C, int D>
 __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
@@ -401,7 +562,7 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
 namespace {
 
 template <typename K>
-hipError_t launch_dyn(K kernel, dim3 grid, size_t smem, hipStream_t st, const ChunkParams &p) {
+hipError_t launch_dyn(K kernel, dim3 grid, size_t smem, hipStream_t st, const ChunkParams &p, int threads = kNT) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
@@ -411,7 +572,7 @@ hipError_t launch_dyn(K kernel, dim3 grid, size_t smem, hipStream_t st, const Ch
       return e;
     }
   }
-  hipLaunchKernelGGL(kernel, grid, dim3(kNT), smem, st, p);
+  hipLaunchKernelGGL(kernel, grid, dim3(threads), smem, st, p);
   return hipGetLastError();
 }
 
@@ -504,6 +665,8 @@ hipError_t launch_stage_scan(const ChunkParams &p, hipStream_t st) {
   return dispatch(p, [&]<typename Tin, int C, int D>() {
     using TL = Tile<Tin, C, D>;
     const size_t smem = sizeof(Tin) * (C * TL::LDT + D * TL::LDKT) + sizeof(float) * 2 * D;
+    if constexpr (sizeof(Tin) == 2 && D <= 128)  // 4 D threads: at D = 256 the state would not fit 128 VGPRs
+      return launch_dyn(stage_scan_bf16_kernel<C, D>, dim3(p.N * p.H), ScanBf16Smem<C, D>::total, st, p, 4 * D);
     return launch_dyn(stage_scan_kernel<Tin, C, D>, dim3(p.N * p.H * ((p.Vr + 63) / 64)), smem, st, p);
   });
 }
