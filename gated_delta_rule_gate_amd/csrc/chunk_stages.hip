@@ -80,29 +80,71 @@ __global__ __launch_bounds__(256) void chunk_index_kernel(const int32_t *cu, int
 }
 
 // ---- (1) gate activation + chunk-local cumsum (base 2) ----
+// Persistent workgroups walk (chunk, head) items: thread t owns channel t % D
+// and RPS consecutive rows, the activation and the cumsum run in registers
+// (the row parts' totals meet in LDS), and the next item's gate input is
+// loaded while the current one is summed and stored.
 template <int C, int D, int GK>
-__global__ __launch_bounds__(256) void stage_gate_kernel(ChunkParams p) {
-  ChunkLoc lc;
-  if (!locate_chunk(p, blockIdx.x, lc)) return;
-  const int h = blockIdx.y;
-  using TL = Tile<float, C, D>;
-  extern __shared__ __align__(16) char smem[];
-  float *sB = reinterpret_cast<float *>(smem);
-  float *sBL = sB + C * TL::LDB;
-  float *sSeg = sBL + D;
-  float *sDt = sSeg + kNT;
-  const int64_t ld = (int64_t)p.H * D, ldg = (int64_t)p.H * p.Kr;
-  for (int i = threadIdx.x; i < D; i += kNT) sDt[i] = (p.dt_bias && i < p.Kr) ? p.dt_bias[h * p.Kr + i] : 0.f;
-  load_rows<float, kNT, C, D>(sB, TL::LDB, p.g + lc.t0 * ldg + h * p.Kr, ldg, lc.L, p.Kr);
-  __syncthreads();
-  // a pre-cumsummed log2 gate already is b: it is only restrided from the
-  // caller's K channels per row to the tile width D (channels >= K zero)
-  if constexpr (GK != kGateLog2Cumsum) {
-    gate_activate<kNT, C, D, GK>(sB, TL::LDB, lc.L, sDt, head_expA(p, h), p.lower_bound);
-    __syncthreads();
-    gate_cumsum<kNT, C, D>(sB, TL::LDB, sBL, sSeg);
+__global__ __launch_bounds__(kNT) void stage_gate_items_kernel(ChunkParams p) {
+  constexpr int TPC = kNT / D, RPS = C / TPC;  // threads per channel, rows per thread
+  static_assert(kNT % D == 0 && C % TPC == 0, "whole channels per thread group");
+  __shared__ float sSeg[kNT];
+  const int t = threadIdx.x, ch = t % D, part = t / D;
+  const int total = p.cu ? p.chunk_off[p.N] : p.B * ((p.T + C - 1) / C);
+  const int64_t items = (int64_t)total * p.H;
+  const int ld = p.H * D, ldg = p.H * p.Kr;  // row strides (elements) within a chunk
+  float x[RPS];
+  auto load = [&](int64_t it) {
+    ChunkLoc lc;
+    locate_chunk(p, (int)(it / p.H), lc);
+    const int h = (int)(it % p.H);
+    const float *g = p.g + lc.t0 * (int64_t)ldg + h * p.Kr + ch;
+#pragma unroll
+    for (int i = 0; i < RPS; ++i) {
+      const int r = part * RPS + i;
+      x[i] = (r < lc.L && ch < p.Kr) ? g[r * ldg] : 0.f;
+    }
+  };
+  int64_t it = blockIdx.x;
+  if (it < items) load(it);
+  for (; it < items; it += gridDim.x) {
+    ChunkLoc lc;
+    locate_chunk(p, (int)(it / p.H), lc);
+    const int h = (int)(it % p.H), L = lc.L;
+    float v[RPS];
+    if constexpr (GK == kGateLog2Cumsum) {
+      // a pre-cumsummed log2 gate already is b: only restrided to the tile width
+#pragma unroll
+      for (int i = 0; i < RPS; ++i) v[i] = x[i];
+    } else {
+      const float expA = head_expA(p, h);
+      const float dt = (p.dt_bias && ch < p.Kr) ? p.dt_bias[h * p.Kr + ch] : 0.f;
+#pragma unroll
+      for (int i = 0; i < RPS; ++i) v[i] = (part * RPS + i < L) ? gate_log2(GK, x[i], dt, expA, p.lower_bound) : 0.f;
+    }
+    if (it + gridDim.x < items) load(it + gridDim.x);
+    if constexpr (GK != kGateLog2Cumsum) {
+#pragma unroll
+      for (int i = 1; i < RPS; ++i) v[i] += v[i - 1];
+      if constexpr (TPC > 1) {
+        sSeg[part * D + ch] = v[RPS - 1];
+        __syncthreads();
+        float off = 0.f;
+#pragma unroll
+        for (int q = 0; q < TPC - 1; ++q)
+          if (q < part) off += sSeg[q * D + ch];
+#pragma unroll
+        for (int i = 0; i < RPS; ++i) v[i] += off;
+        __syncthreads();  // sSeg is rewritten by the next item
+      }
+    }
+    float *b = p.b + lc.t0 * (int64_t)ld + h * D + ch;
+#pragma unroll
+    for (int i = 0; i < RPS; ++i) {
+      const int r = part * RPS + i;
+      if (r < L) b[r * ld] = v[i];
+    }
   }
-  store_rows_f32<C, D, TL::LDB>(p.b + lc.t0 * ld + h * D, ld, sB, lc.L);
 }
 
 // ---- (2) intra-chunk grams ----
@@ -625,13 +667,13 @@ hipError_t launch_chunk_index(const ChunkParams &p, hipStream_t st) {
 
 hipError_t launch_stage_gate(const ChunkParams &p, hipStream_t st) {
   return dispatch(p, [&]<typename Tin, int C, int D>() {
-    const size_t smem = sizeof(float) * ((size_t)C * (D + 4) + 2 * D + kNT);
-    const dim3 grid(p.max_chunks, p.H);
+    // persistent workgroups, four per compute unit
+    const dim3 grid((unsigned)std::min<int64_t>((int64_t)p.max_chunks * p.H, 4LL * device_cus()));
     switch (p.gate_kind) {
-      case kGateSafe: return launch_dyn(stage_gate_kernel<C, D, kGateSafe>, grid, smem, st, p);
-      case kGateSoftplus: return launch_dyn(stage_gate_kernel<C, D, kGateSoftplus>, grid, smem, st, p);
-      case kGateLogE: return launch_dyn(stage_gate_kernel<C, D, kGateLogE>, grid, smem, st, p);
-      case kGateLog2Cumsum: return launch_dyn(stage_gate_kernel<C, D, kGateLog2Cumsum>, grid, smem, st, p);
+      case kGateSafe: return launch_dyn(stage_gate_items_kernel<C, D, kGateSafe>, grid, 0, st, p);
+      case kGateSoftplus: return launch_dyn(stage_gate_items_kernel<C, D, kGateSoftplus>, grid, 0, st, p);
+      case kGateLogE: return launch_dyn(stage_gate_items_kernel<C, D, kGateLogE>, grid, 0, st, p);
+      case kGateLog2Cumsum: return launch_dyn(stage_gate_items_kernel<C, D, kGateLog2Cumsum>, grid, 0, st, p);
     }
     return hipErrorInvalidValue;
   });
