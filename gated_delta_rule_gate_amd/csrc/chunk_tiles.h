@@ -3,7 +3,7 @@
 // Shared by the six standalone step kernels (chunk_stages.hip) and the fused
 // persistent kernel (chunk_fused.hip). For one (sequence, head, chunk) of
 // L <= C rows starting from state h:
-//   (1) b    = cumsum(gate) in log2 units, chunk-local          gate_cumsum
+//   (1) b    = cumsum(gate) in log2 units, chunk-local          (stage kernel)
 //   (2) A_kk = beta_r sum_i k_r k_s 2^(b_r-b_s)   (s < r)         grams
 //       A_qk = scale  sum_i q_r k_s 2^(b_r-b_s)   (s <= r)
 //   (3) T    = (I + A_kk)^-1                                       solve
@@ -141,56 +141,9 @@ __device__ __forceinline__ void load_rows_cvt(T *s, int lds, const float *g, int
 }
 
 // ---------------------------------------------------------------------------------------------
-// (1) gate activation, then the chunk-local inclusive cumsum in log2 units.
-// gate_activate: rows [0, L) of sB hold the raw gate input and become the
-// per-token log2 decay; rows >= L become 0 (a zero gate). sDt: [D] dt_bias.
-// gate_cumsum: in-place inclusive cumsum over the C rows; sBL <- b[C-1]
-// (== b[L-1]). sSeg is scratch of NT floats.
+// (1) The chunk-local gate cumsum in log2 units (the staged step runs it in
+// registers, chunk_stages.hip; the fused kernels in gate_cumsum_tables).
 // ---------------------------------------------------------------------------------------------
-template <int NT, int C, int D, int GK>
-__device__ __forceinline__ void gate_activate(float *sB, int ldb, int L, const float *sDt, float expA,
-                                              float lower_bound) {
-  constexpr int VPR = D / 4, NV = C * VPR, IT = NV / NT;
-  static_assert(NV % NT == 0, "tile");
-#pragma unroll 4
-  for (int it = 0; it < IT; ++it) {
-    const int idx = it * NT + tid_opaque();
-    const int r = idx / VPR, c = (idx % VPR) * 4;
-    f32x4_t x = *reinterpret_cast<const f32x4_t *>(sB + r * ldb + c);
-    const f32x4_t dt = *reinterpret_cast<const f32x4_t *>(sDt + c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = (r < L) ? gate_log2(GK, x[e], dt[e], expA, lower_bound) : 0.f;
-    *reinterpret_cast<f32x4_t *>(sB + r * ldb + c) = x;
-  }
-}
-
-template <int NT, int C, int D>
-__device__ __forceinline__ void gate_cumsum(float *sB, int ldb, float *sBL, float *sSeg) {
-  static_assert(NT % D == 0, "thread mapping: whole channels per thread group");
-  constexpr int TPC = NT / D;  // threads per channel, each owning RPS consecutive rows
-  constexpr int RPS = C / TPC;
-  const int tid = tid_opaque(), col = tid % D, seg = tid / D;
-  float vals[RPS];
-#pragma unroll
-  for (int i = 0; i < RPS; ++i) vals[i] = sB[(seg * RPS + i) * ldb + col];
-#pragma unroll
-  for (int i = 1; i < RPS; ++i) vals[i] += vals[i - 1];
-  if constexpr (TPC > 1) {
-    sSeg[seg * D + col] = vals[RPS - 1];
-    __syncthreads();
-    float off = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < TPC - 1; ++s2)
-      if (s2 < seg) off += sSeg[s2 * D + col];
-#pragma unroll
-    for (int i = 0; i < RPS; ++i) vals[i] += off;
-  }
-#pragma unroll
-  for (int i = 0; i < RPS; ++i) sB[(seg * RPS + i) * ldb + col] = vals[i];
-  if (seg == TPC - 1) sBL[col] = vals[RPS - 1];
-  __syncthreads();
-}
-
 // gate_pad: sB already holds the chunk-local cumsum for rows [0, L); rows >= L
 // take row L-1's value (as the cumsum of a zero gate would) and sBL <- b[L-1].
 template <int NT, int C, int D>
