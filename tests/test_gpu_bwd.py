@@ -172,3 +172,15 @@ def test_bwd_widths(K, V):
     need_gpu()
     d = _case(1, 140, 2, K, V, torch.float32, 1830 + K + V, "softplus")
     _compare(_run(d, "softplus", 64), _oracle(d, "softplus"), "fp32")
+
+
+@pytest.mark.parametrize("B,T,H,D,C,gate", [(2, 1000, 32, 128, 64, "safe"), (2, 1000, 64, 64, 32, "safe"),
+                                             (2, 600, 16, 64, 64, "softplus")])
+def test_bwd_many_items(B, T, H, D, C, gate):
+    """More (chunk, head) items than compute units, each sequence ending in a ragged
+    chunk: the contraction and WY kernels' persistent workgroups walk several items
+    with the next item's loads in flight, and at 4096 items the staged gate step's
+    workgroups (four per compute unit) do as well."""
+    need_gpu()
+    d = _case(B, T, H, D, D, torch.bfloat16, 1840 + H + C, gate)
+    _compare(_run(d, gate, C), _oracle(d, gate), "bf16")

@@ -350,3 +350,17 @@ def test_check_offsets(offsets, T, want):
 
     cu = torch.tensor(offsets, dtype=torch.int32, device="cuda")
     assert check_offsets(cu, T) == want
+
+
+@pytest.mark.parametrize("D,C,gate", [(64, 32, "softplus"), (128, 64, "safe")])
+def test_staged_many_items(D, C, gate):
+    """The staged chain with more (chunk, head) items than its gate step's persistent
+    workgroups (four per compute unit), each sequence ending in a ragged chunk; the
+    state scan runs one workgroup per (sequence, head) for bf16 inputs."""
+    need_gpu()
+    H = 4096 // D
+    d = make(2, 1000, H, D, torch.bfloat16, 3300 + D, gate=gate)
+    o, ht = gpu_run(d, gate, "staged", C=C)
+    o_ref, ht_ref = oracle_run(d, gate)
+    parity(o, o_ref, "bf16", "o")
+    parity(ht, ht_ref, "bf16", "ht")
