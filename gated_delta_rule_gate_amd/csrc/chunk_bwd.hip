@@ -1176,6 +1176,70 @@ __global__ __launch_bounds__(kWyThreads) void bwd_wy_kernel(ChunkParams p, BwdPa
 // both exponents non-positive for any decaying gate ("FLA KDA Skill", "Safe
 // gate numerical note"), and run as fp32 MFMA products; diagonal blocks take
 // E_rs per pair. Each wave owns 16 channels of a 64-channel slab.
+// The grams step's operands in registers between their loads and the LDS stores:
+// the two gram gradients of a chunk (loaded with the first slab), and one
+// 64-channel slab of k, q and b (the next slab's loads are issued while the
+// current slab computes).
+template <typename Tin, int C, int SI>
+struct GramSlabRegs {
+  static constexpr int EPV = 16 / (int)sizeof(Tin), VK = SI / EPV, NK = C * VK, IK = (NK + kBT - 1) / kBT;
+  static constexpr int VB = SI / 4, NB = C * VB, IB = (NB + kBT - 1) / kBT;
+  u32x4_t k[IK], q[IK];
+  f32x4_t b[IB];
+  float bl;
+
+  // rows >= L of b repeat row L - 1, so every exponent formed from them stays <= 0
+  __device__ __forceinline__ void load(const ChunkParams &p, int64_t t0, int L, int h, int i0) {
+    const int t = threadIdx.x, Kr = p.Kr;
+    const int64_t ld = (int64_t)p.H * (int64_t)p.D, ldk = (int64_t)p.H * Kr;
+    const Tin *gk = reinterpret_cast<const Tin *>(p.k) + t0 * ldk + h * Kr + i0;
+    const Tin *gq = reinterpret_cast<const Tin *>(p.q) + t0 * ldk + h * Kr + i0;
+    const float *gb = p.b + t0 * ld + h * p.D + i0;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int it = 0; it < IK; ++it) {
+      const int idx = it * kBT + t, r = idx / VK, c = (idx % VK) * EPV;
+      const bool ok = (NK % kBT == 0 || idx < NK) && r < L && c < Kr - i0;
+      k[it] = ok ? *reinterpret_cast<const u32x4_t *>(gk + r * ldk + c) : z;
+      q[it] = ok ? *reinterpret_cast<const u32x4_t *>(gq + r * ldk + c) : z;
+    }
+#pragma unroll
+    for (int it = 0; it < IB; ++it) {
+      const int idx = it * kBT + t, r = idx / VB, c = (idx % VB) * 4;
+      b[it] = (NB % kBT == 0 || idx < NB) ? ld4(gb + (int64_t)min(r, L - 1) * ld + c) : zero4();
+    }
+    if (t < SI) bl = gb[(int64_t)(L - 1) * ld + t];
+  }
+
+  static __device__ __forceinline__ void put(float *s, int lds, int r, int c, u32x4_t raw) {
+    if constexpr (sizeof(Tin) == 4) {
+      *reinterpret_cast<u32x4_t *>(s + r * lds + c) = raw;
+    } else {
+      const bf16x8_t f = __builtin_bit_cast(bf16x8_t, raw);
+      *reinterpret_cast<f32x4_t *>(s + r * lds + c) = f32x4_t{(float)f[0], (float)f[1], (float)f[2], (float)f[3]};
+      *reinterpret_cast<f32x4_t *>(s + r * lds + c + 4) = f32x4_t{(float)f[4], (float)f[5], (float)f[6], (float)f[7]};
+    }
+  }
+
+  __device__ __forceinline__ void store(float *sK, float *sQ, float *sB, float *sBL, int lds) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < IK; ++it) {
+      const int idx = it * kBT + t, r = idx / VK, c = (idx % VK) * EPV;
+      if (NK % kBT == 0 || idx < NK) {
+        put(sK, lds, r, c, k[it]);
+        put(sQ, lds, r, c, q[it]);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < IB; ++it) {
+      const int idx = it * kBT + t, r = idx / VB, c = (idx % VB) * 4;
+      if (NB % kBT == 0 || idx < NB) *reinterpret_cast<f32x4_t *>(sB + r * lds + c) = b[it];
+    }
+    if (t < SI) sBL[t] = bl;
+  }
+};
+
 template <typename Tin, int C, int D, int GK>
 __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams bw) {
   ChunkLoc lc;
@@ -1205,14 +1269,37 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
   const float scale = p.scale;
   const float expA = (GK == kGateSafe || GK == kGateSoftplus) ? fast_exp2(p.A_log[h] * kLog2e) : 0.f;
 
-  tile_f32<float, C, C>(sDAg, LA, bw.dAkk + t0 * ldc + h * C, ldc, L, C, [](int r, int c, float *v) {
+  // the gram gradients and the first slab's operands, loaded together
+  constexpr int NA = C * C / 4, IA = (NA + kBT - 1) / kBT;
+  f32x4_t akk[IA], aqk[IA];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (c + e < r) ? v[e] : 0.f;
-  });
+  for (int it = 0; it < IA; ++it) {
+    const int idx = it * kBT + threadIdx.x, r = idx / (C / 4), c = (idx % (C / 4)) * 4;
+    const bool ok = (NA % kBT == 0 || idx < NA) && r < L;
+    akk[it] = ok ? ld4(bw.dAkk + (t0 + r) * ldc + h * C + c) : zero4();
+    aqk[it] = ok ? ld4(bw.dAqk + (t0 + r) * ldc + h * C + c) : zero4();
+  }
+  GramSlabRegs<Tin, C, SI> slab;
+  slab.load(p, t0, L, h, 0);
+#pragma unroll
+  for (int it = 0; it < IA; ++it) {
+    const int idx = it * kBT + threadIdx.x, r = idx / (C / 4), c = (idx % (C / 4)) * 4;
+    if (NA % kBT == 0 || idx < NA) {
+      f32x4_t v = akk[it];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (c + e < r) ? v[e] : 0.f;
+      *reinterpret_cast<f32x4_t *>(sDAg + r * LA + c) = v;
+    }
+  }
   __syncthreads();  // the upper triangle and the diagonal are zero before dA_qk goes in
-  for (int idx = threadIdx.x; idx < C * C; idx += kBT) {
-    const int r = idx / C, c = idx % C;  // coalesced rows of dA_qk, written transposed
-    if (c <= r && r < L) sDAg[c * LA + r] = bw.dAqk[(t0 + r) * ldc + h * C + c];
+#pragma unroll
+  for (int it = 0; it < IA; ++it) {
+    const int idx = it * kBT + threadIdx.x, r = idx / (C / 4), c = (idx % (C / 4)) * 4;
+    if (NA % kBT == 0 || idx < NA) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c + e <= r) sDAg[(c + e) * LA + r] = aqk[it][e];  // dA_qk written transposed
+    }
   }
   for (int r = threadIdx.x; r < C; r += kBT) sBeta[r] = r < L ? beta_at(p, t0 + r, h) : 0.f;
   for (int idx = threadIdx.x; idx < NW * C; idx += kBT) sDbw[idx] = 0.f;
@@ -1246,15 +1333,8 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
       xs[m] = ((GK == kGateSafe || GK == kGateSoftplus) && rr < L && i < Kr)
                   ? ld4(p.g + (t0 + rr) * ldk + h * Kr + i) : zero4();
     }
-    tile_f32<Tin, C, SI>(sK, LS, gk + t0 * ldk + h * Kr + i0, ldk, L, Kr - i0);
-    tile_f32<Tin, C, SI>(sQ, LS, gq + t0 * ldk + h * Kr + i0, ldk, L, Kr - i0);
-    tile_f32<float, C, SI>(sB, LS, gb + i0, ld, L, SI, [&](int r, int c, float *v) {
-      if (r < L) return;
-      const f32x4_t bl = ld4(gb + (int64_t)(L - 1) * ld + i0 + c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = bl[e];
-    });
-    for (int ii = threadIdx.x; ii < SI; ii += kBT) sBL[ii] = gb[(int64_t)(L - 1) * ld + i0 + ii];
+    slab.store(sK, sQ, sB, sBL, LS);
+    if (i0 + SI < Kr) slab.load(p, t0, L, h, i0 + SI);  // the next slab, during this one's products
     __syncthreads();
 
     float ctl = 0.f;                // sum over this lane's rows of k 2^(b_L - b) dk~
