@@ -1479,17 +1479,25 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
     {
       constexpr int NQ = kBT / SI, RQ = C / NQ;
       const int ii = threadIdx.x % SI, q = threadIdx.x / SI, i = i0 + ii;
-      const int r0 = q * RQ, r1 = min(r0 + RQ, L);
+      const int r0 = q * RQ;
+      // the quarter's rows in registers (rows past L hold zeros: dB is zero there)
+      float vq[RQ];
+#pragma unroll
+      for (int e = 0; e < RQ; ++e) vq[e] = sQ[(r0 + e) * LS + ii];
       float part = 0.f;
-      for (int rr = r0; rr < r1; ++rr) part += sQ[rr * LS + ii];
+#pragma unroll
+      for (int e = 0; e < RQ; ++e) part += vq[e];
       sB[q * SI + ii] = part;
       __syncthreads();
       if (i < Kr) {
         float acc = sCT[ii] + fast_exp2(sBL[ii]) * bw.dlam[((int64_t)lc.gci * p.H + h) * D + i];
-        for (int q2 = NQ - 1; q2 > q; --q2) acc += sB[q2 * SI + ii];
-        for (int rr = r1 - 1; rr >= r0; --rr) {
-          acc += sQ[rr * LS + ii];
-          sQ[rr * LS + ii] = acc;  // gradient of the natural-log decay of token rr
+#pragma unroll
+        for (int q2 = NQ - 1; q2 > 0; --q2)
+          if (q2 > q) acc += sB[q2 * SI + ii];
+#pragma unroll
+        for (int e = RQ - 1; e >= 0; --e) {
+          acc += vq[e];
+          if (r0 + e < L) sQ[(r0 + e) * LS + ii] = acc;  // gradient of the natural-log decay of token r0 + e
         }
       }
     }
