@@ -1039,16 +1039,27 @@ __global__ __launch_bounds__(kWyThreads) void bwd_wy_kernel(ChunkParams p, BwdPa
     const int L = lc.L;
     const int64_t t0 = lc.t0;
     R.store(smem, L);
-    // v of this wave's dX_u elements (rows 16 rt + 4 g + e, column 16 ct + n16), for the beta gradient
+    // v of this wave's dX_u elements (rows 16 rt + 4 g + e, column 16 ct + n16), for the beta
+    // gradient: range-checked buffer loads (rows past L read zeros), issued together, used last
     float vv[NDW][4];
+    {
+      const rsrc_t rv = store_rsrc(const_cast<Tin *>(reinterpret_cast<const Tin *>(p.v)) + t0 * ldv + h * p.Vr,
+                                   (uint32_t)((L - 1) * ldv + p.Vr) * (uint32_t)sizeof(Tin));
 #pragma unroll
-    for (int t = 0; t < NDW; ++t) {
-      const int tile = wid * NDW + t, rt = tile / DT, ct = tile % DT;
-      const int j = 16 * ct + n16;
+      for (int t = 0; t < NDW; ++t) {
+        const int tile = wid * NDW + t, rt = tile / DT, ct = tile % DT;
+        const int j = 16 * ct + n16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + tile_row(e);
-        vv[t][e] = (r < L && j < p.Vr) ? to_f32(reinterpret_cast<const Tin *>(p.v)[(t0 + r) * ldv + h * p.Vr + j]) : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off = (uint32_t)((16 * rt + tile_row(e)) * ldv + j) * (uint32_t)sizeof(Tin);
+          float x;
+          if constexpr (sizeof(Tin) == 4) {
+            x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (int)off, 0, 0));
+          } else {
+            x = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, (int)off, 0, 0) << 16);
+          }
+          vv[t][e] = j < p.Vr ? x : 0.f;
+        }
       }
     }
     __syncthreads();
