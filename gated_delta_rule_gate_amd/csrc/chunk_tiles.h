@@ -91,22 +91,35 @@ struct Tile {
   static_assert(D == 64 || D == 128 || D == 256, "head width");
 };
 
-// Copies L rows of COLS elements (global row stride ldg elements) into an LDS
-// tile of row stride lds; rows L..ROWS-1 are zero-filled. 16-byte accesses,
-// all loads of a thread issued before its first LDS write.
+// Range-checked loads through a raw buffer resource over [base, base + bytes):
+// an offset at or past `bytes` reads zeros and touches no memory. The masked
+// tile loads below are written with them, branch-free: a load behind a
+// per-lane condition compiles to a branch around each load that waits for its
+// data before the next one issues, which serialises the whole tile fetch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOffNone = 0x80000000u;  // offset of an element to read as zero
+__device__ __forceinline__ u32x4_t tile_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Copies L rows of COLS elements (global row stride ldg elements, L - 1 rows
+// of it well below 2 GiB) into an LDS tile of row stride lds; columns >= ncol
+// (a multiple of the vector width) and rows L..ROWS-1 are zero-filled.
+// 16-byte accesses, all loads of a thread issued before its first LDS write.
 template <typename T, int NT, int ROWS, int COLS>
 __device__ __forceinline__ void load_rows(T *s, int lds, const T *g, int64_t ldg, int L, int ncol = COLS) {
   constexpr int EPV = 16 / (int)sizeof(T);
   constexpr int VPR = COLS / EPV, NV = ROWS * VPR, IT = (NV + NT - 1) / NT;
+  const auto rs = tile_rsrc(g, L > 0 ? (uint32_t)(((int64_t)(L - 1) * ldg + ncol) * (int64_t)sizeof(T)) : 0u);
   u32x4_t buf[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int idx = it * NT + tid_opaque();
     const int r = idx / VPR, c = (idx % VPR) * EPV;
-    buf[it] = u32x4_t{0u, 0u, 0u, 0u};
-    // columns >= ncol read as zeros (ncol is a multiple of the vector width)
-    if ((NV % NT == 0 || idx < NV) && r < L && c < ncol)
-      buf[it] = *reinterpret_cast<const u32x4_t *>(g + (int64_t)r * ldg + c);
+    const bool ok = (NV % NT == 0 || idx < NV) && r < L && c < ncol;
+    buf[it] = tile_load16(rs, ok ? (uint32_t)(((int64_t)r * ldg + c) * (int64_t)sizeof(T)) : kOffNone);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -121,13 +134,14 @@ __device__ __forceinline__ void load_rows(T *s, int lds, const T *g, int64_t ldg
 template <typename T, int NT, int ROWS, int COLS>
 __device__ __forceinline__ void load_rows_cvt(T *s, int lds, const float *g, int64_t ldg, int L) {
   constexpr int VPR = COLS / 4, NV = ROWS * VPR, IT = (NV + NT - 1) / NT;
+  const auto rs = tile_rsrc(g, L > 0 ? (uint32_t)(((int64_t)(L - 1) * ldg + COLS) * 4) : 0u);
   f32x4_t buf[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int idx = it * NT + tid_opaque();
     const int r = idx / VPR, c = (idx % VPR) * 4;
-    buf[it] = zero4();
-    if ((NV % NT == 0 || idx < NV) && r < L) buf[it] = *reinterpret_cast<const f32x4_t *>(g + (int64_t)r * ldg + c);
+    const bool ok = (NV % NT == 0 || idx < NV) && r < L;
+    buf[it] = __builtin_bit_cast(f32x4_t, tile_load16(rs, ok ? (uint32_t)(((int64_t)r * ldg + c) * 4) : kOffNone));
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
