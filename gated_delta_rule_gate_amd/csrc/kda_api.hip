@@ -27,6 +27,11 @@ bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr
 // Widths of q/k (K) and v (V): multiples of 8 up to 256, so every row of a
 // 16-byte aligned tensor starts 16-byte aligned. The kernels run at the tile
 // width pad_width(max(K, V)) and mask the rest.
+// Heads per call: one chunk's 64 rows of a [*, H, 256] fp32 tensor then span under
+// 2^28 bytes, so the kernels' 32-bit in-chunk offsets and their out-of-range
+// sentinels (2^30 and above) never meet.
+constexpr int kMaxHeads = 4096;
+
 bool width_ok(int d) { return d >= 8 && d <= 256 && d % 8 == 0; }
 int pad_width(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
 
@@ -34,7 +39,7 @@ int pad_width(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
 kda_status check_common(const kda_args *a, const void *q, const void *k, const void *v, const float *g,
                         const float *beta, const float *h0, const void *o, const float *ht, bool recurrent) {
   if (!a) return KDA_ERR_NULL;
-  if (a->B < 1 || a->T < 0 || a->H < 1 || a->N < 0) return KDA_ERR_SHAPE;
+  if (a->B < 1 || a->T < 0 || a->H < 1 || a->H > kMaxHeads || a->N < 0) return KDA_ERR_SHAPE;
   if (a->q_l2norm != 0 && a->q_l2norm != 1) return KDA_ERR_SHAPE;
   if (a->beta_logits != 0 && a->beta_logits != 1) return KDA_ERR_SHAPE;
   if (a->Hk < 0 || (a->Hk > 0 && a->H % a->Hk != 0)) return KDA_ERR_SHAPE;
@@ -113,7 +118,7 @@ extern "C" kda_status kda_check_offsets(const int32_t *cu_seqlens, int N, int T,
 extern "C" kda_status kda_gate_cumsum(const kda_args *a, const float *g_in, const int32_t *cu_seqlens,
                                       int chunk_size, float *g_out, void *stream) {
   if (!a) return KDA_ERR_NULL;
-  if (a->B < 1 || a->T < 0 || a->H < 1 || a->N < 0 || a->K < 1) return KDA_ERR_SHAPE;
+  if (a->B < 1 || a->T < 0 || a->H < 1 || a->H > kMaxHeads || a->N < 0 || a->K < 1) return KDA_ERR_SHAPE;
   if (a->T > 0 && (!g_in || !g_out)) return KDA_ERR_NULL;
   if (!aligned16(g_in) || !aligned16(g_out)) return KDA_ERR_ALIGN;
   if (chunk_size != 1 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_CHUNK;
@@ -198,7 +203,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool chunk_shape_ok(const kda_args *a) {
   if (!a) return false;
-  if (a->B < 1 || a->T < 0 || a->H < 1 || a->N < 0) return false;
+  if (a->B < 1 || a->T < 0 || a->H < 1 || a->H > kMaxHeads || a->N < 0) return false;
   if (!width_ok(a->K) || !width_ok(a->V)) return false;
   if (a->chunk_size != 32 && a->chunk_size != 64) return false;
   return true;

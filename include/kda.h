@@ -101,7 +101,8 @@ typedef enum {
 
 typedef struct {
   int B, T, H, K, V;       /* dense: tensors [B, T, H, *] (q, k: [B, T, Hk, K]); packed: B == 1,
-                              T = capacity                                                    */
+                              T = capacity. 1 <= H <= 4096 (else KDA_ERR_SHAPE): the kernels
+                              address one chunk's rows of a head with 32-bit byte offsets   */
   int N;                   /* sequences (slots); cu_seqlens has N + 1 entries (dense: N == B)   */
   int chunk_size;          /* chunk path: 32 or 64 (sub-chunk fixed at 16 rows)                 */
   kda_dtype dtype;         /* dtype of q, k, v and o                                            */

@@ -74,6 +74,7 @@ FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fail
     (dict(q_l2norm=2), 2),             # the q_l2norm flag is 0 or 1
     (dict(beta_logits=-1), 2),         # so is beta_logits
     (dict(H=3, Hk=2), 2),              # value heads must be a multiple of the q/k heads
+    (dict(H=4097), 2),                 # at most 4096 heads per call
 ])
 def test_recurrent_rejects(kda_lib, kw, code):
     a = _args(**kw)
@@ -106,6 +107,7 @@ FAKE2 = ctypes.c_void_p(0x40000000)  # a second aligned address far from FAKE (n
     (dict(gate_kind=2), 64, 5),                 # SOFTPLUS without A_log
     (dict(gate_kind=0, K=44), 64, 8),
     (dict(gate_kind=0, B=2, N=1), 64, 2),
+    (dict(gate_kind=0, H=4097), 64, 2),        # at most 4096 heads per call
 ])
 def test_gate_cumsum_rejects(kda_lib, kw, chunk, code):
     a = _args(**kw)
@@ -125,6 +127,7 @@ def test_gate_cumsum_rejects_overlap_and_null(kda_lib):
     (dict(gate_kind=0, chunk_size=16), 4),
     (dict(gate_kind=0, V=12), 8),              # widths are multiples of 8
     (dict(gate_kind=0, K=52, V=48), 8),
+    (dict(gate_kind=0, H=4097), 2),            # at most 4096 heads per call
 ])
 def test_chunk_rejects(kda_lib, kw, code):
     a = _args(**kw)
