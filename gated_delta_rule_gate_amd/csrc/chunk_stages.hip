@@ -162,10 +162,16 @@ __global__ __launch_bounds__(256) void stage_grams_kernel(ChunkParams p) {
   float *sBeta = sBL + D;
   const int64_t ld = (int64_t)p.H * D, ldc = (int64_t)p.H * C, ldk = (int64_t)p.Hk * p.Kr;
   const int64_t off = lc.t0 * ld + h * D, offk = lc.t0 * ldk + (h / (p.H / p.Hk)) * p.Kr;
-  load_rows<Tin, kNT, C, D>(sQ, TL::LDT, reinterpret_cast<const Tin *>(p.q) + offk, ldk, lc.L, p.Kr);
-  load_rows<Tin, kNT, C, D>(sK, TL::LDT, reinterpret_cast<const Tin *>(p.k) + offk, ldk, lc.L, p.Kr);
-  load_rows<float, kNT, C, D>(sB, TL::LDB, p.b + off, ld, lc.L);
+  // every tile's loads in flight before the first LDS write
+  RowsFetch<Tin, kNT, C, D> fq, fk;
+  RowsFetch<float, kNT, C, D> fb;
+  fq.fetch(reinterpret_cast<const Tin *>(p.q) + offk, ldk, lc.L, p.Kr);
+  fk.fetch(reinterpret_cast<const Tin *>(p.k) + offk, ldk, lc.L, p.Kr);
+  fb.fetch(p.b + off, ld, lc.L);
   load_beta<C>(sBeta, p, lc.t0, h, lc.L);
+  fq.put(sQ, TL::LDT);
+  fk.put(sK, TL::LDT);
+  fb.put(sB, TL::LDB);
   __syncthreads();
   pad_cumsum<kNT, C, D>(sB, TL::LDB, sBL, lc.L);
   __syncthreads();
@@ -231,10 +237,16 @@ __global__ __launch_bounds__(256) void stage_wy_kernel(ChunkParams p) {
   };
   f32x4_t bv[GB];
   if constexpr (IB <= 8) load_b(bv, 0);
-  load_rows<float, kNT, C, C>(sT, TL::LDA, p.Tm + lc.t0 * ldc + h * C, ldc, L);
-  load_rows<Tin, kNT, C, D>(sK, LDT, reinterpret_cast<const Tin *>(p.k) + offk, ldk, L, p.Kr);
-  load_rows<Tin, kNT, C, D>(sV, LDT, reinterpret_cast<const Tin *>(p.v) + lc.t0 * ldv + h * p.Vr, ldv, L, p.Vr);
+  // every tile's loads in flight before the first LDS write
+  RowsFetch<float, kNT, C, C> ft;
+  RowsFetch<Tin, kNT, C, D> fk, fv;
+  ft.fetch(p.Tm + lc.t0 * ldc + h * C, ldc, L);
+  fk.fetch(reinterpret_cast<const Tin *>(p.k) + offk, ldk, L, p.Kr);
+  fv.fetch(reinterpret_cast<const Tin *>(p.v) + lc.t0 * ldv + h * p.Vr, ldv, L, p.Vr);
   load_beta<C>(sBeta, p, lc.t0, h, L);
+  ft.put(sT, TL::LDA);
+  fk.put(sK, LDT);
+  fv.put(sV, LDT);
   __syncthreads();
   // beta k 2^b in place of k; rows past L stay zero
   if constexpr (IB <= 8) {
@@ -561,8 +573,17 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
   };
   f32x4_t bv[GB];
   if constexpr (IB <= 8) load_b(bv, 0);
-  load_rows<Tin, kNT, C, D>(sQ, LDT, reinterpret_cast<const Tin *>(p.q) + offk, ldk, L, p.Kr);
-  load_rows<float, kNT, C, C>(sAqk, TL::LDA, p.Aqk + lc.t0 * ldc + h * C, ldc, L);
+  // every tile's loads, and this wave's state and v_new strips, in flight before
+  // the first LDS write
+  RowsFetch<Tin, kNT, C, D> fq;
+  RowsFetch<float, kNT, C, C> fa;
+  fq.fetch(reinterpret_cast<const Tin *>(p.q) + offk, ldk, L, p.Kr);
+  fa.fetch(p.Aqk + lc.t0 * ldc + h * C, ldc, L);
+  f32x4_t hs[DT][NVW], vn[NC][NVW], o[NC][NVW];
+  load_strip<DT, NVW>(hs, p.hc + ((int64_t)lc.gci * p.H + h) * p.Kr * p.Vr, p.Vr, col0, p.Kr, p.Vr);
+  load_strip<NC, NVW>(vn, p.vnew + off, ld, col0, lc.L);
+  fq.put(sQ, LDT);
+  fa.put(sAqk, TL::LDA);
   __syncthreads();
   if (p.q_l2norm && threadIdx.x < C) {  // raw q: o is linear in each q row
     float ss = 0.f;
@@ -582,9 +603,6 @@ __global__ __launch_bounds__(256) void stage_output_kernel(ChunkParams p) {
       scale_q(bv, j0);
     }
   }
-  f32x4_t hs[DT][NVW], vn[NC][NVW], o[NC][NVW];
-  load_strip<DT, NVW>(hs, p.hc + ((int64_t)lc.gci * p.H + h) * p.Kr * p.Vr, p.Vr, col0, p.Kr, p.Vr);
-  load_strip<NC, NVW>(vn, p.vnew + off, ld, col0, lc.L);
 #pragma unroll
   for (int i = 0; i < NC; ++i) o[i][0] = zero4();
   __syncthreads();

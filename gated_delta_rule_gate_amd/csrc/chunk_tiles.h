@@ -104,29 +104,45 @@ __device__ __forceinline__ u32x4_t tile_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// Copies L rows of COLS elements (global row stride ldg elements, L - 1 rows
-// of it well below 2 GiB) into an LDS tile of row stride lds; columns >= ncol
-// (a multiple of the vector width) and rows L..ROWS-1 are zero-filled.
-// 16-byte accesses, all loads of a thread issued before its first LDS write.
+// L rows of COLS elements (global row stride ldg elements, L - 1 rows of it
+// well below 2 GiB) fetched into registers, then written to an LDS tile of row
+// stride lds; columns >= ncol (a multiple of the vector width) and rows
+// L..ROWS-1 come out zero. 16-byte accesses. A kernel that fills several tiles
+// fetches them all before the first put, so their loads are in flight
+// together: a put waits for its own loads, which would otherwise hold back the
+// next tile's.
+template <typename T, int NT, int ROWS, int COLS>
+struct RowsFetch {
+  static constexpr int EPV = 16 / (int)sizeof(T);
+  static constexpr int VPR = COLS / EPV, NV = ROWS * VPR, IT = (NV + NT - 1) / NT;
+  u32x4_t buf[IT];
+
+  __device__ __forceinline__ void fetch(const T *g, int64_t ldg, int L, int ncol = COLS) {
+    const auto rs = tile_rsrc(g, L > 0 ? (uint32_t)(((int64_t)(L - 1) * ldg + ncol) * (int64_t)sizeof(T)) : 0u);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NT + tid_opaque();
+      const int r = idx / VPR, c = (idx % VPR) * EPV;
+      const bool ok = (NV % NT == 0 || idx < NV) && r < L && c < ncol;
+      buf[it] = tile_load16(rs, ok ? (uint32_t)(((int64_t)r * ldg + c) * (int64_t)sizeof(T)) : kOffNone);
+    }
+  }
+  __device__ __forceinline__ void put(T *s, int lds) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NT + tid_opaque();
+      const int r = idx / VPR, c = (idx % VPR) * EPV;
+      if (NV % NT == 0 || idx < NV) *reinterpret_cast<u32x4_t *>(s + r * lds + c) = buf[it];
+    }
+  }
+};
+
+// One tile on its own: fetch, then put.
 template <typename T, int NT, int ROWS, int COLS>
 __device__ __forceinline__ void load_rows(T *s, int lds, const T *g, int64_t ldg, int L, int ncol = COLS) {
-  constexpr int EPV = 16 / (int)sizeof(T);
-  constexpr int VPR = COLS / EPV, NV = ROWS * VPR, IT = (NV + NT - 1) / NT;
-  const auto rs = tile_rsrc(g, L > 0 ? (uint32_t)(((int64_t)(L - 1) * ldg + ncol) * (int64_t)sizeof(T)) : 0u);
-  u32x4_t buf[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = it * NT + tid_opaque();
-    const int r = idx / VPR, c = (idx % VPR) * EPV;
-    const bool ok = (NV % NT == 0 || idx < NV) && r < L && c < ncol;
-    buf[it] = tile_load16(rs, ok ? (uint32_t)(((int64_t)r * ldg + c) * (int64_t)sizeof(T)) : kOffNone);
-  }
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = it * NT + tid_opaque();
-    const int r = idx / VPR, c = (idx % VPR) * EPV;
-    if (NV % NT == 0 || idx < NV) *reinterpret_cast<u32x4_t *>(s + r * lds + c) = buf[it];
-  }
+  RowsFetch<T, NT, ROWS, COLS> f;
+  f.fetch(g, ldg, L, ncol);
+  f.put(s, lds);
 }
 
 // Same, converting fp32 global rows to the tile type T (used for the fp32
@@ -523,6 +539,10 @@ __device__ __forceinline__ void load_strip(f32x4_t (&x)[RT][NVW], const float *g
                                            int ncol = 1 << 30) {
   const int lane = tid_opaque() & 63;
   const int n16 = lane & 15, grp = lane >> 4;
+  // range-checked and branch-free (kOffNone and rows past L read zeros), so the
+  // loads are issued back to back
+  const int cend = ncol < col0 + 16 * NVW ? ncol : col0 + 16 * NVW;
+  const auto rs = tile_rsrc(g, L > 0 && cend > 0 ? (uint32_t)(((int64_t)(L - 1) * ld + cend) * 4) : 0u);
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -530,7 +550,8 @@ __device__ __forceinline__ void load_strip(f32x4_t (&x)[RT][NVW], const float *g
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * t + 4 * grp + e, c = col0 + 16 * v + n16;
-        x[t][v][e] = (r < L && c < ncol) ? g[(int64_t)r * ld + c] : 0.f;
+        const uint32_t off = (r < L && c < ncol) ? (uint32_t)(((int64_t)r * ld + c) * 4) : kOffNone;
+        x[t][v][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 0));
       }
 }
 
