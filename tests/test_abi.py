@@ -186,6 +186,10 @@ def test_chunk_bwd_rejects(kda_lib):
     assert _bwd(kda_lib, _args(gate_kind=0, chunk_size=16)) == 4
     assert kda_lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_args(gate_kind=0, K=256, V=256))) == 0
     assert kda_lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_args(gate_kind=0))) > 0
+    # more heads than one call takes: no workspace size, and the call itself is refused
+    assert kda_lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_args(gate_kind=0, H=4097))) == 0
+    assert kda_lib.kda_chunk_workspace_bytes(ctypes.byref(_args(gate_kind=0, H=4097))) == 0
+    assert _bwd(kda_lib, _args(gate_kind=0, H=4097)) == 2
 
 
 def test_split_schedule_limits_and_workspace(kda_lib):
