@@ -103,6 +103,26 @@ __device__ __forceinline__ float beta_at(const ChunkParams &p, int64_t row, int 
   return p.beta_logits ? sigmoid_f32(b) : b;
 }
 
+// Sums over aligned groups of 8 or 16 lanes through DPP (two quad permutes,
+// then the half-row and the row mirror), every lane of a group left with the
+// group's sum. Each step adds the same pair of partial sums as a lane shuffle by
+// xor 1, 2, 4, 8 would, so the results are the same; the operands move on the
+// VALU's own crossbar instead of the LDS permute network.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lanes8_sum(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror: lane i and 7 - i of each half-row
+  return x;
+}
+__device__ __forceinline__ float lanes16_sum(float x) {
+  x = lanes8_sum(x);
+  return x + dpp_mov<0x140>(x);  // row_mirror: lane i and 15 - i of each row
+}
+
 // Raw buffer stores: offsets at or past `bytes` are dropped, so the masked rows
 // and channels of a tile need no branches.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -683,9 +703,8 @@ struct ContractRegs {
         put(smem, S::dhH, S::dhL, i, c, y);
         part = x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
       }
-#pragma unroll
-      for (int m = 1; m < SJ / 4; m <<= 1) part += __shfl_xor(part, m);
-      dlam[it] += part;
+      static_assert(SJ / 4 == 8, "a row's partial products on 8 adjacent lanes");
+      dlam[it] += lanes8_sum(part);
     }
   }
 };
@@ -1159,9 +1178,7 @@ __global__ __launch_bounds__(kWyThreads) void bwd_wy_kernel(ChunkParams p, BwdPa
 #pragma unroll
         for (int e = 0; e < 4; ++e) rs[e] += dbp[t][e];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) rs[e] += __shfl_xor(rs[e], m);
+      for (int e = 0; e < 4; ++e) rs[e] = lanes16_sum(rs[e]);
       const int rt = (wid * NDW) / DT, part = ((wid * NDW) % DT) / NDW;
       if (n16 == 0)
 #pragma unroll
@@ -1465,8 +1482,7 @@ __global__ __launch_bounds__(kBT) void bwd_grams_kernel(ChunkParams p, BwdParams
         }
         dBv[e] = dB;
         ctl += ct;
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) dbp += __shfl_xor(dbp, m);
+        dbp = lanes16_sum(dbp);
         if (n16 == 0) sDbw[wid * C + r] += dbp;
       }
       // this wave alone reads these rows of its channels again: dB goes over q
