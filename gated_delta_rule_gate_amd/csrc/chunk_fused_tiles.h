@@ -181,9 +181,9 @@ __device__ __forceinline__ void diag_inverse16(const float *Ablk, int lda, bf16_
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = mine ? z[e] : x[e];
     if (k == 3) break;
-    float y[4];  // group k's finished rows of this column
+    float y[4];  // group k's finished rows of this column, in every group
 #pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = __int_as_float(__builtin_amdgcn_ds_bpermute((16 * k + c) * 4, __float_as_int(x[e])));
+    for (int e = 0; e < 4; ++e) y[e] = k == 0 ? row_bcast<0>(x[e]) : (k == 1 ? row_bcast<1>(x[e]) : row_bcast<2>(x[e]));
     const bool later = (g > k);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

@@ -58,6 +58,21 @@ __device__ __forceinline__ int tid_opaque() {
   return t;
 }
 
+// Row K (lanes 16K .. 16K + 15) of x, in every row at the same position within
+// the row: a v_permlane16_swap of x with itself leaves rows (0, 0, 2, 2) in its
+// first result and (1, 1, 3, 3) in its second, and a v_permlane32_swap of one
+// of those with itself leaves its first half-wave's row in the first result and
+// its second's in the second. Two VALU permutes instead of an LDS permute.
+template <int K>
+__device__ __forceinline__ float row_bcast(float x) {
+  static_assert(K >= 0 && K < 4, "four rows of 16 lanes");
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned h = (K & 1) ? r[1] : r[0];
+  const auto t = __builtin_amdgcn_permlane32_swap(h, h, false, false);
+  return __uint_as_float((K & 2) ? t[1] : t[0]);
+}
+
 // The wave's index within the workgroup as a wave-uniform (scalar) value.
 // Branches on it are scalar branches; a branch on a per-lane value would
 // instead run both sides under an EXEC mask, and MFMA instructions do not
