@@ -188,17 +188,18 @@ __device__ __forceinline__ void key_gate(const f32x2_t (&xr)[16], const float (&
         P[r][e] = (r == 0) ? sg : P[r - 1][e] + sg;
       }
   }
-  // the four blocks' totals of the same channels (rows of 16 lanes, broadcast
-  // to every row), the exclusive offset of block blk and b_L (the last row's
-  // total plus its offset, summed in the same order)
-  float off[2], bL[2], m[2], a[2];
+  // inclusive scan of the block totals over blk, the exclusive offset, b_L
+  float inc[2], off[2], bL[2], m[2], a[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const float t0 = row_bcast<0>(P[15][e]), t1 = row_bcast<1>(P[15][e]);
-    const float t2 = row_bcast<2>(P[15][e]), t3 = row_bcast<3>(P[15][e]);
-    const float o2 = t0 + t1, o3 = o2 + t2;
-    off[e] = blk == 0 ? 0.f : (blk == 1 ? t0 : (blk == 2 ? o2 : o3));
-    bL[e] = c2 * (t3 + o3);
+    inc[e] = P[15][e];
+    float y = __shfl_up(inc[e], 16);
+    if (blk >= 1) inc[e] += y;
+    y = __shfl_up(inc[e], 32);
+    if (blk >= 2) inc[e] += y;
+    y = __shfl_up(inc[e], 16);
+    off[e] = (blk >= 1) ? y : 0.f;
+    bL[e] = c2 * __shfl(inc[e], pr + 48);
     a[e] = c2 * (P[0][e] + off[e]);  // b at the block's first row
     m[e] = c2 * (P[8][e] + off[e]);  // b at its midpoint row
   }
@@ -220,8 +221,7 @@ __device__ __forceinline__ void key_gate(const f32x2_t (&xr)[16], const float (&
   put(S::t0, blk, fast_exp2(m[0] - a[0]), fast_exp2(m[1] - a[1]));
 #pragma unroll
   for (int ip = 1; ip < kNC; ++ip) {
-    const float ap0 = ip == 1 ? row_bcast<1>(a[0]) : (ip == 2 ? row_bcast<2>(a[0]) : row_bcast<3>(a[0]));
-    const float ap1 = ip == 1 ? row_bcast<1>(a[1]) : (ip == 2 ? row_bcast<2>(a[1]) : row_bcast<3>(a[1]));
+    const float ap0 = __shfl(a[0], pr + 16 * ip), ap1 = __shfl(a[1], pr + 16 * ip);
     if (ip > blk) put(S::te, pair_index(ip, blk), fast_exp2(ap0 - m[0]), fast_exp2(ap1 - m[1]));
   }
   if (blk == kNC - 1) put(S::lam, cpar, fast_exp2(bL[0]), fast_exp2(bL[1]));
