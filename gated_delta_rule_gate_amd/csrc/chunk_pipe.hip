@@ -497,9 +497,9 @@ __device__ __forceinline__ void key_side(const ChunkParams &p, char *smem, int i
       if (tt < kC) reinterpret_cast<float *>(smem + S::beta)[tt] = (p.beta_logits && tt < L) ? sigmoid_f32(br) : br;
     }
     __syncthreads();
-    // ---- P2: row operands of block i (the two heaviest key waves issue first)
+    // ---- P2: row operands of block i (the state waves' column operands take
+    // the issue slots first: the key side's grams wait on them)
     wait_vmem();
-    if (i >= 2) __builtin_amdgcn_s_setprio(2);
     float ss = 0.f;
     switch (i) {
       case 0: key_row_operands<0, QN>(qr, kr, smem, fQd, fKd, fQo, fKo, ss); break;
@@ -507,7 +507,6 @@ __device__ __forceinline__ void key_side(const ChunkParams &p, char *smem, int i
       case 2: key_row_operands<2, QN>(qr, kr, smem, fQd, fKd, fQo, fKo, ss); break;
       default: key_row_operands<3, QN>(qr, kr, smem, fQd, fKd, fQo, fKo, ss); break;
     }
-    __builtin_amdgcn_s_setprio(0);
     {
       // output row scale: the query scale, times 1/|q_r| for raw q
       const int lane = tid_opaque() & 63, n16 = lane & 15, grp = lane >> 4;
@@ -642,11 +641,12 @@ __device__ __forceinline__ void state_side(const ChunkParams &p, char *smem, int
     if (c > 0) tail(t0p, Lp);
     __syncthreads();
     // ---- P2: column operands of block sidx (k~ into this chunk's parity buffer);
-    // the two heaviest state waves (blocks 0 and 1: the most exports) issue first.
+    // the state waves issue first in this period (measured: 1.5% shorter chunks
+    // than giving the first slots to the heavier wave of each role).
     // This chunk's k and v loads came before the previous chunk's eight o stores
     // (P1), and vector memory operations retire in order: wait for all but those.
     __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-    if (sidx <= 1) __builtin_amdgcn_s_setprio(2);
+    __builtin_amdgcn_s_setprio(2);
     switch (sidx) {
       case 0: state_col_operands<0>(kr, smem, c & 1); break;
       case 1: state_col_operands<1>(kr, smem, c & 1); break;
